@@ -1,0 +1,389 @@
+"""Plain, slow, obviously correct CPU oracle for the W4A16 group-quantized projection.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): the product path never
+imports this module.
+
+What the method computes
+------------------------
+``y[m, n] = sum_k x[m, k] * w[n, k]``, a projection ("quantized linear") of bf16
+activations ``x [M, K]`` by 4-bit affine-quantized weights, where
+``w[n, k] = s[n, g] * q[n, k] + b[n, g]`` with ``g = k // 128``.
+
+Sources on the pages:
+
+* tiny-llm book, "Week 2 Day 6: SIMD-Matrix Prefill", opening scope list:
+  weights have four bits and group size 128; activations, quantization
+  parameters (scale and bias) and the output are BF16; matrix accumulators
+  are FP32.
+* same page, "Task 3: Hoist Quantization Parameters": one scale and one bias
+  cover 128 reduction values of one output column.
+* same page, "Task 4: Project Only Required Logits": ``logits_to_keep`` slices
+  the last rows *before* the projection.
+* "Route affine qmv_wide by bit-width and batch size #5", description:
+  affine quantized matvec in which a group of weights is dequantized
+  (``scale * q + bias``) and reused across the input rows.
+
+Readings where the pages are silent (each one is also listed in the design doc):
+
+* R1 nibble order: element ``8*j + i`` of a weight row sits in bits
+  ``4*i .. 4*i+3`` of 32-bit word ``j`` (low nibble first).
+* R2 ``Wq`` is ``uint32 [N, K/8]`` row-major: one contiguous run of K codes
+  per output column ``n``.
+* R3 scales and biases are bf16 ``[N, K/128]`` row-major, indexed ``[n, k // 128]``.
+* R4 dequantization is evaluated in fp32 with two roundings,
+  ``f32(f32(s * q) + b)``.  ``s * q`` is exact in fp32 (8-bit by 4-bit
+  significands), so a fused multiply-add gives the same value.
+* R5 the reference accumulates in fp64.  Every product ``x * w`` is exact in
+  fp64 (8 + 24 significand bits), so only the final sum is rounded.
+* R6 per-element parity tolerance:
+  ``|y - y_ref| <= 2^-8 * |y_ref| + 2^-10 * sum_k |x[m,k] * w[n,k]|``;
+  NaN or Inf in ``y`` always fails.
+* R7 the input quantizer (how test weights are made, not part of the method):
+  per (n, g) in fp32, ``scale = (max - min) / 15``, ``bias = min``, both rounded
+  to bf16 (nearest, ties to even); ``q = clamp(rint((W - b) / s), 0, 15)``
+  computed from the *rounded* s and b, ties to even; a group with ``s == 0``
+  gets ``q = 0``.
+"""
+
+from __future__ import annotations
+
+import math
+import struct
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "GROUP",
+    "TOL_REL",
+    "TOL_MASS",
+    "bf16_to_f32",
+    "bf16_to_f64",
+    "f32_to_bf16_rne",
+    "unpack_q",
+    "dequant_f32",
+    "reference",
+    "CheckResult",
+    "check",
+    "quantize_w4g128",
+    "pack_q",
+    "brute_force",
+    "keep_last_rows",
+    "silu_f64",
+    "swiglu_reference",
+    "check_swiglu",
+]
+
+GROUP = 128
+TOL_REL = 2.0 ** -8
+TOL_MASS = 2.0 ** -10
+
+
+# --------------------------------------------------------------------------- bf16
+
+
+def bf16_to_f32(bits) -> np.ndarray:
+    """bf16 bit patterns -> float32, exactly.
+
+    A bf16 value is the upper half of the fp32 pattern with the same sign,
+    exponent and leading seven mantissa bits, so widening is a 16-bit shift.
+    """
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> float64 (exact)."""
+    return bf16_to_f32(bits).astype(np.float64)
+
+
+def f32_to_bf16_rne(values) -> np.ndarray:
+    """float32 -> bf16 bit pattern, round to nearest with ties to even, by definition.
+
+    For a finite value the two bf16 candidates are its truncation toward zero
+    and the next bf16 away from zero.  The nearer one is chosen, measured in
+    exact float64 arithmetic; on a tie the candidate whose lowest mantissa bit
+    is 0 wins.  The step past the largest finite bf16 is the infinity, which
+    takes part in the comparison as the value 2^128, as IEEE 754 overflow
+    rounding prescribes.  NaN maps to a quiet NaN with the same sign.
+    """
+    v = np.asarray(values, dtype=np.float32)
+    u = v.view(np.uint32)
+    sign = u & np.uint32(0x80000000)
+    lo_bits = (u & np.uint32(0xFFFF0000)).astype(np.uint32)
+    hi_bits = (lo_bits + np.uint32(0x10000)).astype(np.uint32)  # next away from zero, same sign
+    mag = np.abs(v.astype(np.float64))
+    lo_mag = np.abs(lo_bits.view(np.float32).astype(np.float64))
+    hi_is_inf = (hi_bits & np.uint32(0x7FFFFFFF)) == np.uint32(0x7F800000)
+    with np.errstate(over="ignore", invalid="ignore"):
+        hi_mag = np.where(hi_is_inf, 2.0 ** 128, np.abs(hi_bits.view(np.float32).astype(np.float64)))
+    with np.errstate(invalid="ignore"):  # inf - inf on infinite inputs; those are replaced below
+        d_lo = mag - lo_mag
+        d_hi = hi_mag - mag
+    lo_even = ((lo_bits >> np.uint32(16)) & np.uint32(1)) == 0
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ~lo_even)
+    out = np.where(take_hi, hi_bits, lo_bits) >> np.uint32(16)
+    finite = np.isfinite(v)
+    is_inf = np.isinf(v)
+    out = np.where(is_inf, (sign >> np.uint32(16)) | np.uint32(0x7F80), out)
+    out = np.where(~finite & ~is_inf, (sign >> np.uint32(16)) | np.uint32(0x7FC0), out)
+    return out.astype(np.uint16)
+
+
+# --------------------------------------------------------------------------- format
+
+
+def unpack_q(wq, K: int) -> np.ndarray:
+    """Packed words ``uint32 [N, K/8]`` -> codes ``uint8 [N, K]`` (readings R1, R2)."""
+    w = np.asarray(wq, dtype=np.uint32)
+    n_rows, n_words = w.shape
+    if n_words * 8 != K:
+        raise ValueError(f"Wq has {n_words} words per row; K={K} needs {K // 8}")
+    q = np.empty((n_rows, K), dtype=np.uint8)
+    for i in range(8):
+        # element 8*j + i of every row comes from bits 4i..4i+3 of word j
+        q[:, i::8] = (w >> np.uint32(4 * i)) & np.uint32(0xF)
+    return q
+
+
+def dequant_f32(wq, scales, biases, K: int, group: int = GROUP) -> np.ndarray:
+    """Dequantized weights ``w[n, k] = f32(f32(s[n,g] * q[n,k]) + b[n,g])`` (reading R4).
+
+    Follows the affine form of "Route affine qmv_wide by bit-width and batch
+    size #5" and the per-group scale/bias of "Week 2 Day 6: SIMD-Matrix
+    Prefill", Task 3.
+    """
+    q = unpack_q(wq, K).astype(np.float32)
+    s = bf16_to_f32(scales)
+    b = bf16_to_f32(biases)
+    if s.shape != (q.shape[0], K // group) or b.shape != s.shape:
+        raise ValueError(f"scales/biases must be [{q.shape[0]}, {K // group}], got {s.shape} / {b.shape}")
+    g_of_k = np.arange(K) // group
+    s_k = s[:, g_of_k]
+    b_k = b[:, g_of_k]
+    prod = np.multiply(s_k, q, dtype=np.float32)
+    return np.add(prod, b_k, dtype=np.float32)
+
+
+def reference(x_bits, wq, scales, biases, group: int = GROUP, columns=None, col_chunk: int = 8192):
+    """Reference output and absolute mass, both fp64 ``[M, N']`` (readings R4, R5).
+
+    ``y_ref = x64 @ w64ᵀ`` and ``A = |x64| @ |w64|ᵀ``, where ``x64`` is the exact
+    widening of the bf16 activations and ``w64`` of the fp32 dequantized
+    weights.  ``columns`` (optional index array) restricts the output columns;
+    the weights are dequantized ``col_chunk`` columns at a time so that large
+    vocabularies fit in memory.
+    """
+    x64 = bf16_to_f64(x_bits)
+    if x64.ndim != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x64.shape
+    wq = np.asarray(wq)
+    scales = np.asarray(scales)
+    biases = np.asarray(biases)
+    cols = np.arange(wq.shape[0]) if columns is None else np.asarray(columns)
+    y = np.empty((M, cols.size), dtype=np.float64)
+    A = np.empty((M, cols.size), dtype=np.float64)
+    ax = np.abs(x64)
+    for c0 in range(0, cols.size, col_chunk):
+        sel = cols[c0:c0 + col_chunk]
+        w64 = dequant_f32(wq[sel], scales[sel], biases[sel], K, group).astype(np.float64)
+        y[:, c0:c0 + sel.size] = x64 @ w64.T
+        A[:, c0:c0 + sel.size] = ax @ np.abs(w64).T
+    return y, A
+
+
+@dataclass
+class CheckResult:
+    ok: bool
+    max_ratio: float       # max over elements of |err| / bound (inf for NaN/Inf or err > 0 = bound)
+    worst: tuple           # (m, n) of the worst element
+    n_bad: int
+    n_total: int
+
+    def __str__(self) -> str:
+        return (f"ok={self.ok} max_err/bound={self.max_ratio:.4g} at {self.worst} "
+                f"bad={self.n_bad}/{self.n_total}")
+
+
+def check(y_bits, y_ref, A, rel: float = TOL_REL, mass: float = TOL_MASS) -> CheckResult:
+    """Per-element parity test of a bf16 result against the fp64 reference (reading R6)."""
+    y = bf16_to_f64(y_bits)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    if y.shape != y_ref.shape or A.shape != y_ref.shape:
+        raise ValueError(f"shape mismatch: y {y.shape}, y_ref {y_ref.shape}, A {A.shape}")
+    finite = np.isfinite(y)
+    with np.errstate(invalid="ignore"):
+        err = np.abs(y - y_ref)
+    bound = rel * np.abs(y_ref) + mass * A
+    good = finite & (err <= bound)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / bound, np.where(err == 0, 0.0, np.inf))
+    ratio = np.where(finite, ratio, np.inf)
+    if ratio.size == 0:
+        return CheckResult(True, 0.0, (), 0, 0)
+    flat = int(np.argmax(ratio))
+    worst = tuple(int(i) for i in np.unravel_index(flat, ratio.shape))
+    return CheckResult(bool(good.all()), float(ratio.flat[flat]), worst,
+                       int((~good).sum()), int(good.size))
+
+
+# --------------------------------------------------------------------------- quantizer (R7)
+
+
+def pack_q(q) -> np.ndarray:
+    """Codes ``[N, K]`` (0..15) -> words ``uint32 [N, K/8]``: word j holds element 8j+i at bits 4i (R1)."""
+    q = np.asarray(q, dtype=np.uint32)
+    n_rows, K = q.shape
+    words = np.zeros((n_rows, K // 8), dtype=np.uint32)
+    for j in range(K // 8):
+        acc = np.zeros(n_rows, dtype=np.uint32)
+        for i in range(8):
+            acc |= (q[:, 8 * j + i] & np.uint32(0xF)) << np.uint32(4 * i)
+        words[:, j] = acc
+    return words
+
+
+def quantize_w4g128(W, group: int = GROUP):
+    """Reference quantizer for the input recipe (reading R7), one group at a time.
+
+    Returns ``(wq uint32 [N, K/8], scales bf16-bits [N, G], biases bf16-bits [N, G])``.
+    """
+    W = np.asarray(W, dtype=np.float32)
+    n_rows, K = W.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    G = K // group
+    q = np.zeros((n_rows, K), dtype=np.uint8)
+    s_bits = np.zeros((n_rows, G), dtype=np.uint16)
+    b_bits = np.zeros((n_rows, G), dtype=np.uint16)
+    fifteen = np.float32(15.0)
+    for n in range(n_rows):
+        for g in range(G):
+            blk = W[n, g * group:(g + 1) * group]
+            mn = np.float32(blk.min())
+            mx = np.float32(blk.max())
+            scale = np.float32(np.float32(mx - mn) / fifteen)
+            sb = f32_to_bf16_rne(np.array([scale], dtype=np.float32))[0]
+            bb = f32_to_bf16_rne(np.array([mn], dtype=np.float32))[0]
+            s_bits[n, g] = sb
+            b_bits[n, g] = bb
+            s32 = bf16_to_f32(np.array([sb]))[0]
+            b32 = bf16_to_f32(np.array([bb]))[0]
+            if s32 == 0:
+                continue  # degenerate group: every code is 0, so w = b
+            t = np.divide(np.subtract(blk, b32, dtype=np.float32), s32, dtype=np.float32)
+            q[n, g * group:(g + 1) * group] = np.clip(np.rint(t), 0, 15).astype(np.uint8)
+    return pack_q(q), s_bits, b_bits
+
+
+# --------------------------------------------------------------------------- brute force
+
+
+def _f32_round(v: float) -> float:
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def _bf16_scalar(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+def brute_force(x_bits, wq, scales, biases, group: int = GROUP):
+    """Pure-Python loops over (m, n, k); small inputs only.
+
+    Every weight is decoded from its word by explicit shifts, dequantized with
+    two fp32 roundings, and each output is the correctly rounded fp64 sum
+    (``math.fsum``) of the exact products.  Returns ``(y, A)`` as fp64 arrays.
+    """
+    x_bits = np.asarray(x_bits)
+    wq = np.asarray(wq)
+    M, K = x_bits.shape
+    N = wq.shape[0]
+    xs = [[_bf16_scalar(x_bits[m, k]) for k in range(K)] for m in range(M)]
+    ws = []
+    for n in range(N):
+        row = []
+        for k in range(K):
+            word = int(wq[n, k // 8])
+            code = (word >> (4 * (k % 8))) & 0xF
+            s = _bf16_scalar(scales[n, k // group])
+            b = _bf16_scalar(biases[n, k // group])
+            row.append(_f32_round(_f32_round(s * code) + b))
+        ws.append(row)
+    y = np.empty((M, N))
+    A = np.empty((M, N))
+    for m in range(M):
+        xm = xs[m]
+        for n in range(N):
+            prods = [xm[k] * ws[n][k] for k in range(K)]
+            y[m, n] = math.fsum(prods)
+            A[m, n] = math.fsum(abs(p) for p in prods)
+    return y, A
+
+
+# --------------------------------------------------------------------------- logits_to_keep
+
+
+def keep_last_rows(M: int, keep: int) -> slice:
+    """Rows a projection sees under ``logits_to_keep`` ("Week 2 Day 6", Task 4).
+
+    ``keep > 0`` selects the last ``keep`` rows, ``keep == 0`` selects every row
+    (prompt scoring), anything else is an error.
+    """
+    if keep < 0 or keep > M:
+        raise ValueError(f"logits_to_keep={keep} must be in [0, M={M}]")
+    return slice(0, M) if keep == 0 else slice(M - keep, M)
+
+
+# --------------------------------------------------------------------------- fused gate/up + SwiGLU
+
+
+def silu_f64(z):
+    """SiLU ``z * sigmoid(z) = z / (1 + exp(-z))`` in fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_reference(x_bits, gate, up, group: int = GROUP, columns=None):
+    """Reference for the gate/up projection pair followed by SwiGLU, all fp64.
+
+    ``gate`` and ``up`` are ``(wq, scales, biases)`` triples of one shape.  The
+    fused step is named by "Feature Request: Metal prefill speedup (~68%) on
+    M5 Max" (feature list: SwiGLU fused into the mat-mat; related work: gate
+    and up rows interleaved with the GLU in the mat-mat epilogue).  Returns
+    ``(h_ref, g_ref, A_g, u_ref, A_u)`` with ``h = silu(g) * u``.
+    """
+    g_ref, A_g = reference(x_bits, *gate, group=group, columns=columns)
+    u_ref, A_u = reference(x_bits, *up, group=group, columns=columns)
+    return silu_f64(g_ref) * u_ref, g_ref, A_g, u_ref, A_u
+
+
+def check_swiglu(h_bits, g_ref, A_g, u_ref, A_u, rel: float = TOL_REL, mass: float = TOL_MASS) -> CheckResult:
+    """Per-element test of a fused SwiGLU result.
+
+    The two projections carry the R6 error ``e_g <= rel*|g| + mass*A_g`` and
+    ``e_u`` likewise.  ``|d silu/dz| <= 1.1`` everywhere, so the product
+    ``silu(g) * u`` may move by ``1.1*e_g*(|u| + e_u) + |silu(g)|*e_u``; the
+    final bf16 rounding adds ``rel*|h|``.
+    """
+    g_ref = np.asarray(g_ref, np.float64)
+    u_ref = np.asarray(u_ref, np.float64)
+    e_g = rel * np.abs(g_ref) + mass * np.asarray(A_g, np.float64)
+    e_u = rel * np.abs(u_ref) + mass * np.asarray(A_u, np.float64)
+    h_ref = silu_f64(g_ref) * u_ref
+    bound = 1.1 * e_g * (np.abs(u_ref) + e_u) + np.abs(silu_f64(g_ref)) * e_u + rel * np.abs(h_ref)
+    h = bf16_to_f64(h_bits)
+    finite = np.isfinite(h)
+    with np.errstate(invalid="ignore"):
+        err = np.abs(h - h_ref)
+    good = finite & (err <= bound)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / bound, np.where(err == 0, 0.0, np.inf))
+    ratio = np.where(finite, ratio, np.inf)
+    if ratio.size == 0:
+        return CheckResult(True, 0.0, (), 0, 0)
+    flat = int(np.argmax(ratio))
+    worst = tuple(int(i) for i in np.unravel_index(flat, ratio.shape))
+    return CheckResult(bool(good.all()), float(ratio.flat[flat]), worst, int((~good).sum()), int(good.size))

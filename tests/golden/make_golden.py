@@ -1,0 +1,65 @@
+"""Writes ``worked_example_w4g128.json``: a tiny worked example whose expected
+outputs are computed here with exact rational arithmetic (``fractions``), from
+the format definition only.  The pages print no worked example, so this fixture
+is a closed-form pin: its values come from neither the oracle nor the HIP path.
+
+Format (the reading the oracle states): element ``8j+i`` of weight row ``n`` is
+bits ``4i..4i+3`` of word ``j``; ``w[n,k] = s[n,k//128] * q[n,k] + b[n,k//128]``;
+``y[m,n] = sum_k x[m,k] * w[n,k]``.  All chosen values are dyadic rationals
+exactly representable in bf16, and every ``s*q + b`` is exact in fp32, so the
+fp32 dequantization rounds nothing and the fp64 reference must equal the
+rational result to within its final rounding.
+
+Run: ``python tests/golden/make_golden.py`` (rewrites the JSON next to it).
+"""
+
+import json
+import os
+import struct
+from fractions import Fraction
+
+M, K, N, GROUP = 3, 256, 4, 128
+
+
+def bf16_bits(v: Fraction) -> int:
+    f = float(v)
+    bits = struct.unpack("<I", struct.pack("<f", f))[0]
+    assert bits & 0xFFFF == 0 and Fraction(f) == v, f"{v} not exact in bf16"
+    return bits >> 16
+
+
+def main():
+    # codes: a closed form that varies with n and k and spans 0..15
+    q = [[(3 * n + 5 * k + (k // 128)) % 16 for k in range(K)] for n in range(N)]
+    words = [[sum(q[n][8 * j + i] << (4 * i) for i in range(8)) for j in range(K // 8)] for n in range(N)]
+    s = [[Fraction(1, 2 ** (4 + n + g)) for g in range(K // GROUP)] for n in range(N)]
+    b = [[Fraction(-(n + 1) * (g + 3), 2 ** 5) for g in range(K // GROUP)] for n in range(N)]
+    # activations: small dyadic values with a pattern per row
+    x = [[Fraction(((m + 1) * (k % 7) - 3), 2 ** (1 + m)) for k in range(K)] for m in range(M)]
+    y = [[sum(x[m][k] * (s[n][k // GROUP] * q[n][k] + b[n][k // GROUP]) for k in range(K))
+          for n in range(N)] for m in range(M)]
+    A = [[sum(abs(x[m][k] * (s[n][k // GROUP] * q[n][k] + b[n][k // GROUP])) for k in range(K))
+          for n in range(N)] for m in range(M)]
+    out = {
+        "citation": ("No page prints a worked example. Closed-form values computed with exact "
+                     "rationals from the affine W4 group-128 format (tiny-llm 'Week 2 Day 6: "
+                     "SIMD-Matrix Prefill', scope list and Task 3) under the oracle's readings "
+                     "R1-R4 (low-nibble-first packing, [N,K/8] words, [N,K/128] scale/bias)."),
+        "M": M, "K": K, "N": N, "group": GROUP,
+        "x_bf16": [[bf16_bits(v) for v in row] for row in x],
+        "wq_u32": words,
+        "scales_bf16": [[bf16_bits(v) for v in row] for row in s],
+        "biases_bf16": [[bf16_bits(v) for v in row] for row in b],
+        "codes": q,
+        "y_exact": [[f"{v.numerator}/{v.denominator}" for v in row] for row in y],
+        "abs_mass_exact": [[f"{v.numerator}/{v.denominator}" for v in row] for row in A],
+    }
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "worked_example_w4g128.json")
+    with open(path, "w") as f:
+        json.dump(out, f)
+        f.write("\n")
+    print("wrote", path)
+
+
+if __name__ == "__main__":
+    main()

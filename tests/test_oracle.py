@@ -1,0 +1,425 @@
+"""Pins for the CPU oracle (``-m "not gpu"``).
+
+Each test fixes the oracle to something other than itself: a library routine
+(torch's bf16 conversions), a closed form (identity activations, all-zero
+codes, power-of-two affine parameters, a rational worked example), an exact
+brute force on tiny inputs, a mathematical bound (the quantization round
+trip) or an invariant (scaling by 2).  ``test_pins_catch_planted_mistakes``
+plants plausible mistakes in copies of the oracle and shows that every one of
+them fails at least one pin.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from w4a16_group_quantized_qmv_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example_w4g128.json")
+
+
+# ----------------------------------------------------------------------------- bf16 conversions
+
+def test_bf16_widening_matches_torch_on_every_pattern():
+    torch = pytest.importorskip("torch")
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = O.bf16_to_f32(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _rne_cases():
+    rng = np.random.default_rng(7)
+    r = rng.standard_normal(200000).astype(np.float32) * np.float32(3.0) ** rng.integers(-40, 40, 200000).astype(np.float32)
+    u = rng.integers(0, 2 ** 32, 100000, dtype=np.uint64).astype(np.uint32)
+    ties = ((u & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)  # exact halfway cases
+    edge = np.array([0.0, -0.0, 1.0, -1.0, 3.3895314e38, 3.4028235e38, -3.4028235e38, 1e-45, -1e-45,
+                     1.1754942e-38, np.inf, -np.inf], dtype=np.float32)
+    near_max = np.array([0x7F7F7FFF, 0x7F7F8000, 0x7F7F8001, 0xFF7F8000], dtype=np.uint32).view(np.float32)
+    allv = np.concatenate([r, u.view(np.float32), ties, edge, near_max])
+    return allv[~np.isnan(allv)]
+
+
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    v = _rne_cases()
+    ours = O.f32_to_bf16_rne(v)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_rounding_of_nan_is_quiet_nan():
+    v = np.array([np.nan, -np.nan], dtype=np.float32)
+    out = O.f32_to_bf16_rne(v)
+    assert np.all(np.isnan(O.bf16_to_f32(out)))
+
+
+def test_generator_rounding_agrees_with_oracle_rounding():
+    v = _rne_cases()
+    v = v[np.isfinite(v)]
+    assert np.array_equal(synth.to_bf16_bits(v), O.f32_to_bf16_rne(v))
+
+
+# ----------------------------------------------------------------------------- unpacking
+
+def test_nibble_order_literal_words():
+    # element 8j+i of a row is bits 4i..4i+3 of word j: the hex digits read right to left
+    words = np.array([[0x76543210, 0xFEDCBA98, 0x0000000F, 0xF0000000]], dtype=np.uint32)
+    q = O.unpack_q(words, 32)
+    assert q[0, :8].tolist() == [0, 1, 2, 3, 4, 5, 6, 7]
+    assert q[0, 8:16].tolist() == [8, 9, 10, 11, 12, 13, 14, 15]
+    assert q[0, 16:24].tolist() == [15, 0, 0, 0, 0, 0, 0, 0]
+    assert q[0, 24:32].tolist() == [0, 0, 0, 0, 0, 0, 0, 15]
+
+
+def test_unpack_inverts_the_generator_packer():
+    rng = np.random.default_rng(3)
+    q = rng.integers(0, 16, (37, 256)).astype(np.uint8)
+    assert np.array_equal(O.unpack_q(synth.pack_codes(q), 256), q)
+    assert np.array_equal(O.pack_q(q), synth.pack_codes(q))
+
+
+# ----------------------------------------------------------------------------- closed forms (pin battery)
+
+def _load_golden():
+    with open(GOLDEN) as f:
+        d = json.load(f)
+    arr = {k: np.array(d[k]) for k in ("x_bf16", "scales_bf16", "biases_bf16")}
+    wq = np.array(d["wq_u32"], dtype=np.uint64).astype(np.uint32)
+    y = [[Fraction(v) for v in row] for row in d["y_exact"]]
+    A = [[Fraction(v) for v in row] for row in d["abs_mass_exact"]]
+    return (arr["x_bf16"].astype(np.uint16), wq, arr["scales_bf16"].astype(np.uint16),
+            arr["biases_bf16"].astype(np.uint16), y, A, np.array(d["codes"]))
+
+
+def pin_worked_example(ref_fn):
+    """Rational worked example: every value is dyadic and every sum exact in fp64."""
+    x, wq, s, b, y_exact, A_exact, _ = _load_golden()
+    y, A = ref_fn(x, wq, s, b)
+    ok_y = all(Fraction(float(y[m, n])) == y_exact[m][n] for m in range(y.shape[0]) for n in range(y.shape[1]))
+    ok_A = all(Fraction(float(A[m, n])) == A_exact[m][n] for m in range(A.shape[0]) for n in range(A.shape[1]))
+    return ok_y and ok_A
+
+
+def pin_identity(ref_fn):
+    """x = identity, s = 1, b = 0: y[m, n] = q[n, m] exactly."""
+    rng = np.random.default_rng(11)
+    K, N = 256, 40
+    q = rng.integers(0, 16, (N, K))
+    wq = synth.pack_codes(q)
+    x = np.where(np.eye(K, dtype=bool), synth.const_bf16(1.0, (K, K)), np.uint16(0))
+    y, _ = ref_fn(x, wq, synth.const_bf16(1.0, (N, K // 128)), synth.const_bf16(0.0, (N, K // 128)))
+    return np.array_equal(y, q.T.astype(np.float64))
+
+
+def pin_all_zero_codes(ref_fn):
+    """q = 0 everywhere: y[m, n] = sum_g b[n, g] * sum_{k in g} x[m, k]."""
+    rng = np.random.default_rng(12)
+    M, K, N = 5, 384, 7
+    G = K // 128
+    x = synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    s = synth.to_bf16_bits(rng.uniform(0.001, 0.01, (N, G)).astype(np.float32))
+    b = synth.to_bf16_bits(rng.standard_normal((N, G)).astype(np.float32))
+    wq = np.zeros((N, K // 8), dtype=np.uint32)
+    y, A = ref_fn(x, wq, s, b)
+    xf = synth.from_bf16_bits(x).astype(np.float64)
+    bf = synth.from_bf16_bits(b).astype(np.float64)
+    ok = True
+    for m in range(M):
+        for n in range(N):
+            terms = [bf[n, g] * xf[m, k] for g in range(G) for k in range(128 * g, 128 * (g + 1))]
+            exact = math.fsum(terms)
+            ok &= abs(y[m, n] - exact) <= 2.0 ** -45 * math.fsum(abs(t) for t in terms)
+            ok &= abs(A[m, n] - math.fsum(abs(t) for t in terms)) <= 2.0 ** -45 * A[m, n]
+    return bool(ok)
+
+
+def pin_power_of_two_affine(ref_fn):
+    """s = 2^-6, b = -8 * 2^-6 gives w = (q - 8) / 64; integer x makes y an exact multiple of 1/64."""
+    rng = np.random.default_rng(13)
+    M, K, N = 6, 256, 9
+    q = rng.integers(0, 16, (N, K))
+    xi = rng.integers(-4, 5, (M, K))
+    x = synth.to_bf16_bits(xi.astype(np.float32))
+    G = K // 128
+    y, _ = ref_fn(x, synth.pack_codes(q), synth.const_bf16(2.0 ** -6, (N, G)), synth.const_bf16(-8 * 2.0 ** -6, (N, G)))
+    exact = (xi @ (q - 8).T) / 64.0
+    return np.array_equal(y, exact)
+
+
+def pin_group_scales_differ(ref_fn):
+    """Each group has its own scale: one-hot x at k picks column k's group scale."""
+    K, N = 512, 3
+    G = K // 128
+    q = np.ones((N, K), dtype=np.int64)
+    s_vals = np.array([[2.0 ** -(g + 1 + n) for g in range(G)] for n in range(N)], dtype=np.float32)
+    b_vals = np.array([[(g + 1) * 2.0 ** -3 * (n + 1) for g in range(G)] for n in range(N)], dtype=np.float32)
+    x = np.where(np.eye(K, dtype=bool), synth.const_bf16(1.0, (K, K)), np.uint16(0))
+    y, _ = ref_fn(x, synth.pack_codes(q), synth.to_bf16_bits(s_vals), synth.to_bf16_bits(b_vals))
+    expect = np.array([[s_vals[n, k // 128] + b_vals[n, k // 128] for n in range(N)] for k in range(K)], dtype=np.float64)
+    return np.array_equal(y, expect)
+
+
+def pin_fp32_dequant(ref_fn):
+    """Dequantization keeps fp32 precision (reading R4): with x = identity, y = w exactly, and the
+    chosen s*q + b needs up to 18 significand bits: exact in fp32, not representable in bf16."""
+    K, N = 256, 6
+    G = K // 128
+    rng = np.random.default_rng(14)
+    q = rng.integers(0, 16, (N, K))
+    s_vals = np.array([[1 + 2.0 ** -7 * (1 + n + g) for g in range(G)] for n in range(N)], dtype=np.float32)
+    b_vals = np.array([[2.0 ** -10 * (2 * n + 1) * (g + 1) for g in range(G)] for n in range(N)], dtype=np.float32)
+    s_bits, b_bits = synth.to_bf16_bits(s_vals), synth.to_bf16_bits(b_vals)
+    assert np.array_equal(synth.from_bf16_bits(s_bits), s_vals) and np.array_equal(synth.from_bf16_bits(b_bits), b_vals)
+    x = np.where(np.eye(K, dtype=bool), synth.const_bf16(1.0, (K, K)), np.uint16(0))
+    y, _ = ref_fn(x, synth.pack_codes(q), s_bits, b_bits)
+    expect = [[Fraction(float(s_vals[n, k // 128])) * int(q[n, k]) + Fraction(float(b_vals[n, k // 128]))
+               for n in range(N)] for k in range(K)]
+    return all(Fraction(float(y[k, n])) == expect[k][n] for k in range(K) for n in range(N))
+
+
+PIN_BATTERY = [pin_worked_example, pin_identity, pin_all_zero_codes, pin_power_of_two_affine, pin_group_scales_differ,
+               pin_fp32_dequant]
+
+
+def oracle_ref(x, wq, s, b):
+    return O.reference(x, wq, s, b)
+
+
+@pytest.mark.parametrize("pin", PIN_BATTERY, ids=lambda p: p.__name__)
+def test_oracle_passes_pin(pin):
+    assert pin(oracle_ref)
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+
+def _mutant(kind):
+    def unpack(wq, K):
+        w = np.asarray(wq, dtype=np.uint32)
+        q = np.empty((w.shape[0], K), dtype=np.uint8)
+        for i in range(8):
+            shift = 4 * (7 - i) if kind == "high_nibble_first" else 4 * i
+            q[:, i::8] = (w >> np.uint32(shift)) & np.uint32(0xF)
+        if kind == "codes_off_by_one_word":
+            q = np.roll(q, 8, axis=1)
+        return q
+
+    def ref(x, wq, s, b):
+        x64 = O.bf16_to_f64(x)
+        K = x64.shape[1]
+        q = unpack(wq, K).astype(np.float32)
+        sf = O.bf16_to_f32(s)
+        bf = O.bf16_to_f32(b)
+        gk = np.arange(K) // 128
+        if kind == "group_of_64":
+            gk = np.minimum(np.arange(K) // 64, sf.shape[1] - 1)
+        if kind == "group_index_modulo":
+            gk = np.arange(K) % sf.shape[1]
+        if kind == "first_group_only":
+            gk = np.zeros(K, dtype=np.int64)
+        sk, bk = sf[:, gk], bf[:, gk]
+        if kind == "scale_bias_swapped":
+            sk, bk = bk, sk
+        w = np.multiply(sk, q, dtype=np.float32)
+        if kind == "bias_dropped":
+            pass
+        elif kind == "bias_sign_flipped":
+            w = w - bk
+        else:
+            w = w + bk
+        if kind == "dequant_in_bf16":
+            w = O.bf16_to_f32(O.f32_to_bf16_rne(w))
+        if kind == "x_bits_read_as_fp16":
+            x64 = np.asarray(x, dtype=np.uint16).view(np.float16).astype(np.float64)
+        w64 = w.astype(np.float64)
+        if kind == "accumulate_fp32":
+            y = (x64.astype(np.float32) @ w.T).astype(np.float64)
+        elif kind == "k_reversed_for_x":
+            y = x64[:, ::-1] @ w64.T
+        else:
+            y = x64 @ w64.T
+        return y, np.abs(x64) @ np.abs(w64).T
+    return ref
+
+
+MUTANTS = ["high_nibble_first", "codes_off_by_one_word", "group_of_64", "group_index_modulo", "first_group_only",
+           "scale_bias_swapped", "bias_dropped", "bias_sign_flipped", "dequant_in_bf16",
+           "x_bits_read_as_fp16", "accumulate_fp32", "k_reversed_for_x"]
+
+
+def test_mutation_harness_is_faithful():
+    # the unmutated harness reproduces the oracle, so failures below come from the planted mistake
+    x, wq, s, b, *_ = _load_golden()
+    y0, A0 = O.reference(x, wq, s, b)
+    y1, A1 = _mutant("none")(x, wq, s, b)
+    assert np.array_equal(y0, y1) and np.array_equal(A0, A1)
+
+
+@pytest.mark.parametrize("kind", MUTANTS)
+def test_pins_catch_planted_mistakes(kind):
+    failed = [p.__name__ for p in PIN_BATTERY if not p(_mutant(kind))]
+    assert failed, f"planted mistake {kind!r} passed every pin"
+
+
+# ----------------------------------------------------------------------------- brute force
+
+def test_brute_force_tiny_config():
+    """Brute force with exact products and fsum on the 33x256 -> 96 workload."""
+    p = synth.problem(1, "tiny")
+    y, A = O.reference(p["x"], p["wq"], p["scales"], p["biases"])
+    yb, Ab = O.brute_force(p["x"], p["wq"], p["scales"], p["biases"])
+    assert np.all(np.abs(y - yb) <= 2.0 ** -40 * Ab)
+    assert np.all(np.abs(A - Ab) <= 2.0 ** -40 * Ab)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (3, 128, 5), (2, 384, 3)])
+def test_brute_force_ragged_small(M, K, N):
+    p = synth.random_problem(100 + M * 7 + N, M, N, K)
+    y, A = O.reference(p["x"], p["wq"], p["scales"], p["biases"])
+    yb, Ab = O.brute_force(p["x"], p["wq"], p["scales"], p["biases"])
+    assert np.all(np.abs(y - yb) <= 2.0 ** -40 * Ab)
+
+
+def test_column_chunking_does_not_change_the_result():
+    p = synth.random_problem(5, 4, 300, 256)
+    y1, A1 = O.reference(p["x"], p["wq"], p["scales"], p["biases"], col_chunk=7)
+    y2, A2 = O.reference(p["x"], p["wq"], p["scales"], p["biases"])
+    assert np.array_equal(y1, y2) and np.array_equal(A1, A2)
+    cols = np.array([299, 0, 17])
+    y3, _ = O.reference(p["x"], p["wq"], p["scales"], p["biases"], columns=cols)
+    assert np.array_equal(y3, y2[:, cols])
+
+
+# ----------------------------------------------------------------------------- invariants
+
+def test_scaling_by_two_is_exact():
+    p = synth.random_problem(21, 7, 33, 256)
+    x2 = synth.to_bf16_bits(2 * synth.from_bf16_bits(p["x"]))
+    y1, _ = O.reference(p["x"], p["wq"], p["scales"], p["biases"])
+    y2, _ = O.reference(x2, p["wq"], p["scales"], p["biases"])
+    assert np.array_equal(y2, 2 * y1)
+
+
+def test_first_rows_of_a_longer_draw_match():
+    a = synth.activations(4, 0, 512, 2560)
+    b = synth.activations(4, 0, 509, 2560)
+    assert np.array_equal(a[:509], b)
+
+
+# ----------------------------------------------------------------------------- quantizer
+
+def test_quantizer_implementations_agree_bit_exactly():
+    rng = np.random.default_rng(31)
+    W = (0.02 * rng.standard_normal((24, 512))).astype(np.float32)
+    W[3, :128] = 0.125            # degenerate group: scale 0
+    W[5, 128:256] = -1.5          # degenerate group, negative
+    W[7, :] *= 1e4                # large range
+    W[8, :] *= 1e-30              # subnormal-range scales
+    a = O.quantize_w4g128(W)
+    b = synth.quantize(W)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def _roundtrip_bound(W, s_bits, b_bits):
+    G = s_bits.shape[1]
+    Wg = W.reshape(W.shape[0], G, 128).astype(np.float64)
+    mn, mx = Wg.min(axis=2), Wg.max(axis=2)
+    s = O.bf16_to_f64(s_bits)
+    mag = np.maximum(np.abs(mn), np.abs(mx))
+    # s/2 from rounding to the nearest code; 2^-9 (|min| + (max-min)) covers the grid ends moved by
+    # rounding s and b to bf16; 2^-20 (...) covers the fp32 roundings of (W - b) / s and of s*q + b.
+    return s / 2 + 2.0 ** -9 * (np.abs(mn) + (mx - mn)) + 2.0 ** -20 * (mag + s)
+
+
+@pytest.mark.parametrize("cfg,shape", [(1, "tiny"), (2, "decode0"), (3, "k"), (4, "down")])
+def test_quantization_round_trip_bound(cfg, shape):
+    idx = synth.shape_index(cfg, shape)
+    _, K, N, _ = synth.CONFIGS[cfg]["runs"][idx]
+    N = min(N, 512)
+    W = np.float32(synth.W_STD) * synth.rng(cfg, idx, synth.ROLE_W, 0).standard_normal((N, K), dtype=np.float32)
+    wq, s, b = synth.quantize(W)
+    w_hat = O.dequant_f32(wq, s, b, K).astype(np.float64)
+    err = np.abs(W.astype(np.float64) - w_hat).reshape(N, K // 128, 128)
+    bound = _roundtrip_bound(W, s, b)[:, :, None]
+    assert np.all(err <= bound)
+    # and the plain scale/2 bound holds for the overwhelming majority of weights
+    assert np.mean(err <= O.bf16_to_f64(s)[:, :, None] / 2 * (1 + 2.0 ** -18)) > 0.99
+
+
+# ----------------------------------------------------------------------------- tolerance check
+
+def test_check_accepts_inside_and_rejects_outside_the_bound():
+    y_bits = synth.to_bf16_bits(np.array([[1.0, -2.0, 0.0, 4.0]], dtype=np.float32))
+    y = synth.from_bf16_bits(y_bits).astype(np.float64)
+    A = np.array([[10.0, 10.0, 10.0, 10.0]])
+    bound = lambda yr: O.TOL_REL * np.abs(yr) + O.TOL_MASS * A
+    # choose y_ref so that |y - y_ref| = 0.99 * bound (solve for a reference above y)
+    d_in = 0.99 * O.TOL_MASS * A / (1 - 0.99 * O.TOL_REL) + 0.99 * O.TOL_REL * np.abs(y) / (1 - 0.99 * O.TOL_REL)
+    assert O.check(y_bits, y + d_in, A).ok
+    d_out = 1.01 * (O.TOL_MASS * A + O.TOL_REL * np.abs(y)) / (1 - 1.01 * O.TOL_REL)
+    r = O.check(y_bits, y + d_out, A)
+    assert not r.ok and r.n_bad == 4 and r.max_ratio > 1.0
+    assert np.all(np.abs(y - (y + d_in)) <= bound(y + d_in))
+
+
+def test_check_rejects_nan_and_inf():
+    y_ref = np.zeros((1, 3))
+    A = np.ones((1, 3))
+    bits = np.array([[0x7FC0, 0x7F80, 0x0000]], dtype=np.uint16)
+    r = O.check(bits, y_ref, A)
+    assert not r.ok and r.n_bad == 2
+
+
+def test_check_exact_zero_bound():
+    y_ref = np.zeros((1, 2))
+    A = np.zeros((1, 2))
+    assert O.check(np.array([[0, 0x8000]], dtype=np.uint16), y_ref, A).ok   # +0 and -0
+    assert not O.check(np.array([[0x0001, 0]], dtype=np.uint16), y_ref, A).ok
+
+
+# ----------------------------------------------------------------------------- logits_to_keep
+
+def test_keep_last_rows():
+    assert O.keep_last_rows(10, 1) == slice(9, 10)
+    assert O.keep_last_rows(10, 0) == slice(0, 10)
+    assert O.keep_last_rows(10, 10) == slice(0, 10)
+    for bad in (-1, 11):
+        with pytest.raises(ValueError):
+            O.keep_last_rows(10, bad)
+
+
+# ----------------------------------------------------------------------------- SwiGLU
+
+def test_silu_closed_forms():
+    z = np.array([-30.0, -2.0, -0.5, 0.0, 0.5, 2.0, 30.0])
+    s = O.silu_f64(z)
+    assert s[3] == 0.0
+    assert abs(s[-1] - 30.0) < 1e-11 and abs(s[0]) < 1e-11
+    # silu(-z) = silu(z) - z
+    assert np.allclose(O.silu_f64(-z), s - z, rtol=0, atol=1e-13)
+    # sigmoid(0) = 1/2: derivative of silu at 0 is 1/2
+    h = 1e-6
+    assert abs((O.silu_f64(h) - O.silu_f64(-h)) / (2 * h) - 0.5) < 1e-9
+
+
+def test_swiglu_reference_composes_two_projections():
+    p = synth.random_problem(41, 3, 16, 256)
+    q = synth.random_problem(42, 3, 16, 256)
+    h, g, Ag, u, Au = O.swiglu_reference(p["x"], (p["wq"], p["scales"], p["biases"]), (q["wq"], q["scales"], q["biases"]))
+    g2, _ = O.reference(p["x"], p["wq"], p["scales"], p["biases"])
+    u2, _ = O.reference(p["x"], q["wq"], q["scales"], q["biases"])
+    assert np.array_equal(g, g2) and np.array_equal(u, u2)
+    assert np.allclose(h, g2 / (1 + np.exp(-g2)) * u2, rtol=1e-15, atol=0)
+    # the fused check accepts the correctly rounded result and rejects a planted 3% error
+    good = O.f32_to_bf16_rne(h.astype(np.float32))
+    assert O.check_swiglu(good, g, Ag, u, Au).ok
+    bad = O.f32_to_bf16_rne((h * 1.03 + 0.01).astype(np.float32))
+    assert not O.check_swiglu(bad, g, Ag, u, Au).ok
