@@ -1,0 +1,142 @@
+/*
+ * w4a16.h -- C ABI of libw4a16.so, the MI355X (gfx950) W4A16 group-quantized projection.
+ *
+ * Operation (every compute entry point):
+ *
+ *     y[m, n] = bf16( sum_k x[m, k] * w[n, k] ),   w[n, k] = s[n, k/128] * q[n, k] + b[n, k/128]
+ *
+ * a "quantized linear" projection of bf16 activations by 4-bit affine weights with one bf16
+ * scale and one bf16 bias per 128 reduction values of each output column, fp32 accumulation,
+ * and one rounding of the result to bf16.  Sources: tiny-llm book, "Week 2 Day 6: SIMD-Matrix
+ * Prefill" -- opening scope list (four-bit weights, group size 128, BF16 activations,
+ * quantization parameters and output, FP32 matrix accumulators), Task 1 (matvec for M <= 8,
+ * tiled matrix kernel for M > 8, 16-bit result dtype), Task 3 (one scale and bias per 128
+ * reduction values, cast once at the final store); "Route affine qmv_wide by bit-width and
+ * batch size #5" (affine group dequantization reused across the M input rows).
+ *
+ * Layouts (all row-major, contiguous; the pages leave these open and this library fixes them):
+ *   x       bf16  [M, K]      bit patterns passed as uint16_t
+ *   wq      u32   [N, K/8]    code q[n, 8j+i] in bits 4i..4i+3 of wq[n, j] (low nibble first)
+ *   scales  bf16  [N, K/128]
+ *   biases  bf16  [N, K/128]
+ *   y       bf16  [M, N]      overwritten, never accumulated into
+ *
+ * Ownership: every pointer is caller-owned device memory (for example torch tensors).  The
+ * library allocates nothing on the compute paths, keeps no pointer after a call returns and
+ * only enqueues work on `stream` (a hipStream_t; NULL = the null stream).  Buffers must stay
+ * alive until that work completes; y must not overlap any input.  Calls are asynchronous:
+ * a fault during execution surfaces when the caller synchronizes the stream.
+ *
+ * Preconditions checked on the host (a violation returns an error status, never launches):
+ *   M, N, K >= 1;  K % 128 == 0;  group == 128;  x, wq, workspace 16-byte aligned;
+ *   scales, biases, y 2-byte aligned.
+ *
+ * Errors are returned as status codes (never exceptions); w4a16_status_string() names them.
+ * Thread safety: stateless apart from a per-device cache of the compute-unit count.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_ABI_VERSION 1
+#define W4A16_GROUP 128
+
+enum w4a16_status {
+    W4A16_OK = 0,
+    W4A16_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+    W4A16_ERR_SHAPE = 2,       /* M, N or K < 1, K % 128 != 0, or a size overflows int32 rows */
+    W4A16_ERR_GROUP = 3,       /* group != 128                                                */
+    W4A16_ERR_ALIGN = 4,       /* a pointer violates the alignment stated above               */
+    W4A16_ERR_WORKSPACE = 5,   /* a forced split_k > 1 has too little workspace               */
+    W4A16_ERR_UNSUPPORTED = 6, /* valid arguments this entry point does not serve (qmv, M > 8)*/
+    W4A16_ERR_LAUNCH = 7,      /* the HIP runtime rejected a launch                           */
+    W4A16_ERR_DEVICE = 8       /* the device could not be queried                             */
+};
+
+enum w4a16_path {
+    W4A16_PATH_AUTO = 0,       /* dispatch: M <= 8 -> qmv, M > 8 -> qmm ("Week 2 Day 6", Task 1) */
+    W4A16_PATH_QMV = 1,        /* wavefront matvec for decode rows                                */
+    W4A16_PATH_QMM = 2         /* MFMA-tiled matrix path for prefill rows                         */
+};
+
+/* Launch plan chosen by the dispatch policy (filled by w4a16_plan). */
+typedef struct w4a16_plan {
+    int32_t path;              /* W4A16_PATH_QMV or W4A16_PATH_QMM                         */
+    int32_t tile_m;            /* rows per workgroup tile (qmm) or MFMA rows (qmv = 16)    */
+    int32_t tile_n;            /* output columns per workgroup                              */
+    int32_t tile_k;            /* reduction values per pipeline step (one group = 128)     */
+    int32_t grid_x;            /* workgroups along N                                        */
+    int32_t grid_y;            /* workgroups along M                                        */
+    int32_t grid_z;            /* split-K slices (qmm) or 1                                 */
+    int32_t block_threads;     /* threads per workgroup                                     */
+    int32_t split_k;           /* S: number of K slices (1 = unsplit)                       */
+    int32_t k_waves;           /* qmv: waves of one workgroup that split K (1 = none)       */
+    int32_t num_cus;           /* compute units the plan was made for                       */
+    int32_t variant;           /* kernel instance index (diagnostic)                        */
+    uint64_t workspace_bytes;  /* fp32 partials needed when split_k > 1 (S * M * N * 4)    */
+} w4a16_plan_t;
+
+/* ABI version of the loaded library (W4A16_ABI_VERSION). */
+int w4a16_abi_version(void);
+
+/* Static, NUL-terminated name of a status code ("W4A16_OK", ...); unknown codes give "unknown". */
+const char* w4a16_status_string(int status);
+
+/*
+ * Dispatch policy ("Week 2 Day 6", Task 1 for the M threshold; Task 5 and "Benchmark Analysis:
+ * Identify Under-Filled Prefill Shapes" for splitting K only when the tile grid under-fills the
+ * GPU).  path: W4A16_PATH_AUTO / _QMV / _QMM.  split_k: 0 = policy, 1 = never split, S > 1 =
+ * exactly S slices (clamped to the number of groups).  num_cus: compute units to plan for;
+ * 0 = query the current device.  Pure host arithmetic; `out` is caller-owned.
+ * Returns W4A16_OK, _ERR_NULL, _ERR_SHAPE, _ERR_GROUP, _ERR_UNSUPPORTED (qmv with M > 8) or
+ * _ERR_DEVICE.
+ */
+int w4a16_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, int32_t split_k,
+               int32_t num_cus, w4a16_plan_t* out);
+
+/*
+ * Workspace bytes w4a16_linear needs for this shape under the policy (0 when the policy does
+ * not split K).  num_cus as in w4a16_plan.  Returns 0 for invalid shapes.
+ */
+uint64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t num_cus);
+
+/*
+ * Decode-row matvec, 1 <= M <= 8 ("Week 2 Day 6", Task 1: the Day 3 matvec serves M <= 8;
+ * "Route affine qmv_wide ...": a dequantized group is reused across the M rows).  Needs no
+ * workspace.  M > 8 returns W4A16_ERR_UNSUPPORTED.
+ */
+int qmv_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+              uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, void* stream);
+
+/*
+ * Tiled matrix path for any M >= 1 ("Week 2 Day 6", "From a Matvec to a Cooperative Tile",
+ * Tasks 2 and 3), with optional split-K (Task 5: a temporary buffer and a second launch).
+ * split_k: 0 = policy, 1 = off, S > 1 = forced (clamped to the number of groups).  When the
+ * plan splits, `workspace` must hold S * M * N fp32 partials (w4a16_plan().workspace_bytes);
+ * the slices are summed in slice order, so results are deterministic.  Under the policy, a
+ * missing or short workspace quietly falls back to S = 1; a forced S > 1 with too little
+ * workspace returns W4A16_ERR_WORKSPACE.
+ */
+int qmm_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+              uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The quantized-linear entry point: dispatch by M (qmv for M <= 8, qmm with the policy's
+ * split otherwise).  Same arguments and errors as qmm_w4a16 with split_k = 0.
+ */
+int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                 uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

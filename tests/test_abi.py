@@ -1,0 +1,153 @@
+"""Host-side tests of the C ABI (``-m "not gpu"``): the library loads, exports every
+declared symbol, and its policy and validation behave as documented.  Compute entry points
+are only called with arguments that fail validation before any HIP call.
+"""
+
+import ctypes
+
+import pytest
+
+import w4a16_group_quantized_qmv_amd as w4
+
+CUS = 256  # MI355X compute units; passed explicitly so no device is queried
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return w4.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = w4.declared_symbols()
+    assert set(names) >= {"w4a16_abi_version", "w4a16_status_string", "w4a16_plan", "w4a16_workspace_bytes",
+                          "qmv_w4a16", "qmm_w4a16", "w4a16_linear"}
+    for name in names:
+        assert hasattr(lib, name), f"libw4a16.so does not export {name}"
+
+
+def test_abi_version_and_status_strings():
+    assert w4.w4a16_abi_version() == 1
+    expect = ["W4A16_OK", "W4A16_ERR_NULL", "W4A16_ERR_SHAPE", "W4A16_ERR_GROUP", "W4A16_ERR_ALIGN",
+              "W4A16_ERR_WORKSPACE", "W4A16_ERR_UNSUPPORTED", "W4A16_ERR_LAUNCH", "W4A16_ERR_DEVICE"]
+    assert [w4.w4a16_status_string(i) for i in range(9)] == expect
+    assert w4.w4a16_status_string(99) == "unknown"
+
+
+# ------------------------------------------------------------------------------ dispatch policy
+
+def plan(M, N, K, path=0, split_k=0):
+    return w4.w4a16_plan(M, N, K, 128, path, split_k, CUS)
+
+
+def test_matvec_threshold_is_eight_rows():
+    # "Week 2 Day 6: SIMD-Matrix Prefill", Task 1: M <= 8 -> matvec, M > 8 -> matrix kernel
+    for M in range(1, 9):
+        assert plan(M, 4096, 2560)["path"] == w4.PATH_QMV
+    for M in (9, 16, 33, 128, 512, 4096):
+        assert plan(M, 4096, 2560)["path"] == w4.PATH_QMM
+
+
+def test_forced_paths():
+    assert plan(4, 1024, 256, path=w4.PATH_QMM)["path"] == w4.PATH_QMM
+    with pytest.raises(NotImplementedError):
+        plan(9, 1024, 256, path=w4.PATH_QMV)
+    with pytest.raises(NotImplementedError):
+        plan(9, 1024, 256, path=7)
+
+
+def test_grid_covers_the_output():
+    for M, N, K in [(33, 96, 256), (509, 9728, 2560), (128, 1024, 2560), (4096, 151936, 2560), (1, 151936, 2560)]:
+        p = plan(M, N, K)
+        assert p["grid_x"] * p["tile_n"] >= N and (p["grid_x"] - 1) * p["tile_n"] < N
+        if p["path"] == w4.PATH_QMM:
+            assert p["grid_y"] * p["tile_m"] >= M and (p["grid_y"] - 1) * p["tile_m"] < M
+        assert p["tile_k"] == 128 and p["num_cus"] == CUS
+
+
+def test_split_k_only_for_under_filled_grids():
+    # "Benchmark Analysis: Identify Under-Filled Prefill Shapes": the short, narrow K/V
+    # projection (32 rows, N = 1024) has too few tiles and gains from split-K ...
+    short = plan(32, 1024, 2560)
+    assert short["split_k"] > 1
+    # ... while a long, occupied grid (2048 rows) is left unsplit (split-K "neutral" at long M)
+    assert plan(2048, 9728, 2560)["split_k"] == 1
+    assert plan(2048, 2560, 9728)["split_k"] == 1
+    # the pages' own geometry: 32 x 32 tiles give the unsplit 32-row K projection 32 groups
+    assert -(-32 // 32) * -(-1024 // 32) == 32
+
+
+def test_split_k_slices_keep_several_groups():
+    for M, N, K in [(128, 1024, 2560), (128, 2560, 9728), (512, 2560, 9728), (64, 96, 1024), (16, 128, 4096)]:
+        p = plan(M, N, K)
+        G = K // 128
+        tiles = p["grid_x"] * p["grid_y"]
+        assert p["grid_z"] == p["split_k"]
+        if p["split_k"] > 1:
+            assert tiles < CUS
+            assert G // p["split_k"] >= 4
+            assert p["workspace_bytes"] == p["split_k"] * M * N * 4
+        else:
+            assert p["workspace_bytes"] == 0
+
+
+def test_forced_split_is_clamped_to_the_group_count():
+    assert plan(128, 1024, 256, path=w4.PATH_QMM, split_k=64)["split_k"] == 2
+    assert plan(128, 1024, 2560, path=w4.PATH_QMM, split_k=3)["split_k"] == 3
+    assert plan(128, 1024, 2560, path=w4.PATH_QMM, split_k=1)["split_k"] == 1
+
+
+def test_long_k_down_projection_splits_at_512_rows():
+    # 512-row down projection (K = 9728, 76 groups) has fewer tiles than compute units
+    p = plan(512, 2560, 9728)
+    assert p["split_k"] > 1 and p["grid_x"] * p["grid_y"] * p["split_k"] >= CUS
+
+
+def test_workspace_bytes_matches_plan():
+    for M, N, K in [(1, 9728, 2560), (128, 1024, 2560), (512, 2560, 9728), (4096, 9728, 2560)]:
+        assert w4.w4a16_workspace_bytes(M, N, K, 128, CUS) == plan(M, N, K)["workspace_bytes"]
+    assert w4.w4a16_workspace_bytes(0, 10, 128, 128, CUS) == 0
+    assert w4.w4a16_workspace_bytes(4, 10, 100, 128, CUS) == 0
+
+
+@pytest.mark.parametrize("args,err", [
+    ((0, 10, 128, 128), ValueError), ((4, 0, 128, 128), ValueError), ((4, 10, 0, 128), ValueError),
+    ((4, 10, 100, 128), ValueError), ((4, 10, 256, 64), ValueError), ((4, 10, 2 ** 31, 128), ValueError),
+])
+def test_plan_rejects_invalid_shapes(args, err):
+    with pytest.raises(err):
+        w4.w4a16_plan(*args, 0, 0, CUS)
+
+
+def test_plan_rejects_null_output(lib):
+    assert lib.w4a16_plan(4, 10, 128, 128, 0, 0, CUS, None) == 1
+    assert lib.w4a16_plan(4, 10, 128, 128, 0, -1, CUS, ctypes.byref(w4.Plan())) == 2
+
+
+# ------------------------------------------------------------------------------ validation before launch
+
+A16 = 0x10000      # fake, 16-byte aligned addresses: validation fails before they could be used
+ODD = 0x10008
+
+
+@pytest.mark.parametrize("fn", ["qmv", "qmm", "linear"])
+def test_compute_entry_points_validate_before_launch(lib, fn):
+    def call(x=A16, wq=A16, s=A16, b=A16, y=A16, M=4, N=16, K=256, group=128):
+        if fn == "qmv":
+            return lib.qmv_w4a16(x, wq, s, b, y, M, N, K, group, None)
+        if fn == "qmm":
+            return lib.qmm_w4a16(x, wq, s, b, y, M, N, K, group, 1, None, 0, None)
+        return lib.w4a16_linear(x, wq, s, b, y, M, N, K, group, None, 0, None)
+
+    assert call(x=None) == 1 and call(wq=None) == 1 and call(s=None) == 1 and call(b=None) == 1 and call(y=None) == 1
+    assert call(M=0) == 2 and call(N=-1) == 2 and call(K=100) == 2 and call(K=0) == 2
+    assert call(group=64) == 3
+    assert call(x=ODD) == 4 and call(wq=ODD) == 4
+    assert call(s=A16 + 1) == 4 and call(y=A16 + 1) == 4
+
+
+def test_qmv_rejects_more_than_eight_rows(lib):
+    assert lib.qmv_w4a16(A16, A16, A16, A16, A16, 9, 16, 256, 128, None) == 6
+
+
+def test_negative_split_is_a_shape_error(lib):
+    assert lib.qmm_w4a16(A16, A16, A16, A16, A16, 16, 16, 256, 128, -2, None, 0, None) == 2

@@ -1,0 +1,303 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by element.
+
+Bar: integer / closed-form cases bit-exact; random cases within the per-element tolerance
+``|y - y_ref| <= 2^-8 |y_ref| + 2^-10 sum_k |x w|`` with no NaN/Inf.  Sizes span several tiles
+with ragged tails; the full workload sizes are checked on sampled rows (all columns) or on
+every element where the oracle is fast enough.
+"""
+
+import numpy as np
+import pytest
+
+import oracle as O
+from w4a16_group_quantized_qmv_amd import synth
+
+from gpu_helpers import announce, bf16_from_bits, bits, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def run(lib, p, path, split_k=None, dev=None):
+    """Run one path on problem p; returns y bits.  path: 'linear' | 'qmv' | 'qmm'."""
+    import torch
+    announce(f"{path} M={p['M']} N={p['N']} K={p['K']} split={split_k}")
+    x, wq, s, b = dev if dev is not None else to_device(p)
+    if path == "linear":
+        y = lib.w4a16_linear(x, wq, s, b)
+    elif path == "qmv":
+        y = lib.qmv_w4a16(x, wq, s, b)
+    else:
+        y = lib.qmm_w4a16(x, wq, s, b, split_k=split_k or 0)
+    torch.cuda.synchronize()
+    return bits(y)
+
+
+def assert_parity(y_bits, p, rows=None, cols=None):
+    x = p["x"] if rows is None else p["x"][rows]
+    y_ref, A = O.reference(x, p["wq"], p["scales"], p["biases"], columns=cols)
+    got = y_bits if rows is None else y_bits[rows]
+    if cols is not None:
+        got = got[:, cols]
+    r = O.check(got, y_ref, A)
+    assert r.ok, str(r)
+    return r
+
+
+# ---------------------------------------------------------------------------------- tiny config
+
+@pytest.mark.parametrize("path,split", [("linear", None), ("qmm", 1), ("qmm", 2), ("qmm", 0)])
+def test_tiny_config_all_paths(lib, path, split):
+    p = synth.problem(1, "tiny")          # M=33, K=256, N=96: ragged in M and N
+    assert_parity(run(lib, p, path, split), p)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_tiny_config_qmv_rows(lib, M):
+    p = dict(synth.problem(1, "tiny"))
+    p["x"] = p["x"][:M]
+    p["M"] = M
+    y_qmv = run(lib, p, "qmv")
+    assert_parity(y_qmv, p)
+    assert_parity(run(lib, p, "qmm", 1), p)
+
+
+# ---------------------------------------------------------------------------------- bit-exact pins
+
+def identity_problem(K=256, N=96, seed=5):
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, (N, K))
+    x = np.where(np.eye(K, dtype=bool), synth.const_bf16(1.0, (K, K)), np.uint16(0))
+    G = K // 128
+    return q, {"x": x, "wq": synth.pack_codes(q), "scales": synth.const_bf16(1.0, (N, G)),
+               "biases": synth.const_bf16(0.0, (N, G)), "M": K, "N": N, "K": K}
+
+
+@pytest.mark.parametrize("split", [1, 2])
+def test_identity_unpack_is_bit_exact_qmm(lib, split):
+    q, p = identity_problem()
+    y = run(lib, p, "qmm", split)
+    expect = synth.to_bf16_bits(q.T.astype(np.float32))
+    assert np.array_equal(y, expect), "nibble order / indexing mismatch on the matrix path"
+
+
+def test_identity_unpack_is_bit_exact_qmv(lib):
+    q, p = identity_problem()
+    expect = synth.to_bf16_bits(q.T.astype(np.float32))
+    for r0 in range(0, 256, 8):       # one-hot rows, eight at a time
+        sub = dict(p, x=p["x"][r0:r0 + 8], M=8)
+        y = run(lib, sub, "qmv")
+        assert np.array_equal(y, expect[r0:r0 + 8]), f"rows {r0}..{r0 + 7}"
+
+
+@pytest.mark.parametrize("path", ["qmv", "qmm"])
+def test_small_integer_sums_are_exact(lib, path):
+    rng = np.random.default_rng(8)
+    M = 8 if path == "qmv" else 40
+    K, N = 512, 160
+    q = rng.integers(0, 16, (N, K))
+    xi = np.zeros((M, K), dtype=np.int64)
+    for m in range(M):                 # at most 17 ones per row keeps every sum <= 255
+        xi[m, rng.choice(K, size=rng.integers(0, 18), replace=False)] = 1
+    G = K // 128
+    p = {"x": synth.to_bf16_bits(xi.astype(np.float32)), "wq": synth.pack_codes(q),
+         "scales": synth.const_bf16(1.0, (N, G)), "biases": synth.const_bf16(0.0, (N, G)), "M": M, "N": N, "K": K}
+    y = run(lib, p, path, 1)
+    assert np.array_equal(y, synth.to_bf16_bits((xi @ q.T).astype(np.float32)))
+
+
+@pytest.mark.parametrize("path", ["qmv", "qmm"])
+def test_power_of_two_affine_is_exact(lib, path):
+    rng = np.random.default_rng(9)
+    M = 8 if path == "qmv" else 24
+    K, N = 384, 48
+    q = rng.integers(0, 16, (N, K))
+    xi = np.zeros((M, K), dtype=np.int64)
+    for m in range(M):                 # <= 32 entries of +-1: |sum x (q - 8)| <= 256, exact in bf16 / 64
+        idx = rng.choice(K, size=32, replace=False)
+        xi[m, idx] = rng.choice([-1, 1], size=32)
+    G = K // 128
+    p = {"x": synth.to_bf16_bits(xi.astype(np.float32)), "wq": synth.pack_codes(q),
+         "scales": synth.const_bf16(2.0 ** -6, (N, G)), "biases": synth.const_bf16(-8 * 2.0 ** -6, (N, G)),
+         "M": M, "N": N, "K": K}
+    y = run(lib, p, path, 1)
+    assert np.array_equal(y, synth.to_bf16_bits(((xi @ (q - 8).T) / 64.0).astype(np.float32)))
+
+
+@pytest.mark.parametrize("path", ["qmv", "qmm"])
+def test_all_zero_codes(lib, path):
+    rng = np.random.default_rng(10)
+    M = 5 if path == "qmv" else 70
+    K, N = 1024, 200
+    G = K // 128
+    p = {"x": synth.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32)),
+         "wq": np.zeros((N, K // 8), dtype=np.uint32),
+         "scales": synth.to_bf16_bits(rng.uniform(0.001, 0.01, (N, G)).astype(np.float32)),
+         "biases": synth.to_bf16_bits((0.02 * rng.standard_normal((N, G))).astype(np.float32)),
+         "M": M, "N": N, "K": K}
+    assert_parity(run(lib, p, path, 1), p)
+
+
+@pytest.mark.parametrize("path,split", [("qmv", None), ("qmm", 1), ("qmm", 3)])
+def test_scaling_by_two_is_bit_exact(lib, path, split):
+    p = synth.random_problem(77, 8 if path == "qmv" else 100, 300, 768)
+    y1 = run(lib, p, path, split)
+    p2 = dict(p, x=synth.to_bf16_bits(2 * synth.from_bf16_bits(p["x"])))
+    y2 = run(lib, p2, path, split)
+    assert np.array_equal(synth.from_bf16_bits(y2), 2 * synth.from_bf16_bits(y1))
+
+
+# ---------------------------------------------------------------------------------- decode config
+
+@pytest.mark.parametrize("shape", ["decode0", "decode1", "decode2", "decode3"])
+@pytest.mark.parametrize("M", [1, 4])
+def test_decode_config(lib, shape, M):
+    p = synth.problem(2, shape, M)
+    dev = to_device(p)
+    y = run(lib, p, "linear", dev=dev)
+    assert_parity(y, p)
+    y_qmv = run(lib, p, "qmv", dev=dev)
+    assert np.array_equal(y, y_qmv)          # linear dispatches M <= 8 to qmv
+
+
+# ---------------------------------------------------------------------------------- prefill configs
+
+@pytest.mark.parametrize("shape", list(synth.LAYER_SHAPES))
+def test_prefill128_config(lib, shape):
+    p = synth.problem(3, shape, 128)
+    dev = to_device(p)
+    assert_parity(run(lib, p, "linear", dev=dev), p)
+    assert_parity(run(lib, p, "qmm", 1, dev=dev), p)
+
+
+def sample_rows(M, n=48, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(M, size=min(n, M), replace=False).tolist()) | {0, M - 1}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("shape", list(synth.LAYER_SHAPES))
+def test_prefill512_config_and_ragged_prefix(lib, shape):
+    p512 = synth.problem(4, shape, 512)
+    y512 = run(lib, p512, "linear")
+    assert_parity(y512, p512, rows=sample_rows(512))
+    p509 = synth.problem(4, shape, 509)
+    assert np.array_equal(p509["x"], p512["x"][:509])
+    y509 = run(lib, p509, "linear")
+    assert_parity(y509, p509, rows=sample_rows(509, seed=1))
+    # same tiles and split for 509 and 512 rows: the shared rows agree bit for bit
+    assert np.array_equal(y509, y512[:509])
+
+
+@pytest.mark.parametrize("split", [1, 2, 4, 19, 0])
+def test_split_k_down_projection(lib, split):
+    p = synth.problem(4, "down", 512)       # K = 9728: 76 groups
+    dev = to_device(p)
+    y = run(lib, p, "qmm", split, dev=dev)
+    assert_parity(y, p, rows=sample_rows(512, 32))
+    again = run(lib, p, "qmm", split, dev=dev)
+    assert np.array_equal(y, again)          # fixed-order reduction: deterministic
+
+
+# ---------------------------------------------------------------------------------- long prefill + vocab
+
+@pytest.mark.parametrize("shape", ["gate", "up", "down"])
+def test_prefill4096_config(lib, shape):
+    p = synth.problem(5, shape, 4096)
+    assert_parity(run(lib, p, "linear"), p, rows=sample_rows(4096, 24))
+
+
+@pytest.fixture(scope="module")
+def vocab():
+    announce("generating vocab head inputs (2560 -> 151936)")
+    return synth.problem(5, "vocab", 4096)
+
+
+@pytest.mark.timeout(900)
+def test_vocab_logits_to_keep(lib, vocab):
+    import torch
+    p = vocab
+    x, wq, s, b = to_device(p)
+    announce("vocab keep=1")
+    last = bits(lib.linear(x, wq, s, b, logits_to_keep=1))
+    assert last.shape == (1, p["N"])
+    one = dict(p, x=p["x"][-1:], M=1)
+    assert_parity(last, one)                                  # every column of the last row
+    announce("vocab all rows")
+    full = bits(lib.linear(x, wq, s, b, logits_to_keep=0))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    cols = np.unique(np.concatenate([rng.choice(p["N"], 4096, replace=False), [0, p["N"] - 1]]))
+    assert_parity(full, p, rows=sample_rows(4096, 8), cols=cols)
+    # the sliced projection and the last row of the full projection both match the oracle
+    assert_parity(full[-1:], one, cols=cols)
+    keep3 = bits(lib.linear(x, wq, s, b, logits_to_keep=3))
+    assert np.array_equal(keep3, bits(lib.linear(x[-3:], wq, s, b)))
+
+
+# ---------------------------------------------------------------------------------- memory safety
+
+SENTINEL = 0x7FA5   # a NaN pattern the kernels never produce
+
+
+@pytest.mark.parametrize("path,M,N,K,split", [("qmv", 3, 96, 256, None), ("qmm", 33, 96, 256, 1),
+                                              ("qmm", 509, 200, 1024, 1), ("qmm", 509, 200, 1024, 3),
+                                              ("qmv", 8, 1000, 384, None), ("qmm", 130, 4000, 256, 2)])
+def test_guard_rows_and_poisoned_output(lib, path, M, N, K, split):
+    import torch
+    p = synth.random_problem(M * 31 + N, M, N, K)
+    x, wq, s, b = to_device(p)
+    big = bf16_from_bits(np.full((M + 2, N), SENTINEL, dtype=np.uint16))
+    y = big[1:M + 1]
+    announce(f"guard {path} M={M} N={N} K={K} split={split}")
+    if path == "qmv":
+        lib.qmv_w4a16(x, wq, s, b, y=y)
+    else:
+        lib.qmm_w4a16(x, wq, s, b, y=y, split_k=split)
+    torch.cuda.synchronize()
+    out = bits(big)
+    assert np.all(out[0] == SENTINEL) and np.all(out[-1] == SENTINEL), "write outside [M, N]"
+    assert not np.any(out[1:-1] == SENTINEL), "element of y left unwritten"
+    assert_parity(out[1:-1], p)
+
+
+def test_repeated_runs_are_bit_identical(lib):
+    p = synth.random_problem(4242, 300, 1000, 2560)
+    dev = to_device(p)
+    for path, split in [("qmm", 0), ("qmm", 5)]:
+        first = run(lib, p, path, split, dev=dev)
+        for _ in range(9):
+            assert np.array_equal(first, run(lib, p, path, split, dev=dev))
+    q = dict(p, x=p["x"][:7], M=7)
+    devq = to_device(q)
+    first = run(lib, q, "qmv", dev=devq)
+    for _ in range(9):
+        assert np.array_equal(first, run(lib, q, "qmv", dev=devq))
+
+
+# ---------------------------------------------------------------------------------- error paths on the device
+
+def test_forced_split_without_workspace_is_rejected(lib):
+    import ctypes
+    p = synth.random_problem(1, 64, 128, 1024)
+    x, wq, s, b = to_device(p)
+    y = bf16_from_bits(np.zeros((64, 128), dtype=np.uint16))
+    L = lib.load()
+    st = L.qmm_w4a16(x.data_ptr(), wq.data_ptr(), s.data_ptr(), b.data_ptr(), y.data_ptr(), 64, 128, 1024, 128, 4,
+                     None, 0, None)
+    assert st == 5
+    st = L.qmm_w4a16(x.data_ptr(), wq.data_ptr(), s.data_ptr(), b.data_ptr(), y.data_ptr(), 64, 128, 1024, 128, 4,
+                     ctypes.c_void_p(x.data_ptr()), 16, None)
+    assert st == 5
+
+
+def test_policy_split_without_workspace_falls_back(lib):
+    import torch
+    p = synth.random_problem(2, 64, 128, 2048)     # few tiles: the policy would split
+    assert lib.w4a16_plan(64, 128, 2048)["split_k"] > 1
+    x, wq, s, b = to_device(p)
+    y = bf16_from_bits(np.zeros((64, 128), dtype=np.uint16))
+    st = lib.load().w4a16_linear(x.data_ptr(), wq.data_ptr(), s.data_ptr(), b.data_ptr(), y.data_ptr(),
+                                 64, 128, 2048, 128, None, 0, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert_parity(bits(y), p)

@@ -1,1 +1,243 @@
-"""MI355X-native W4A16 group-quantized projection (qmv / qmm) — Python binding."""
+"""MI355X-native W4A16 group-quantized projection: Python binding of ``libw4a16.so``.
+
+The functions below have the names of the C ABI (``include/w4a16.h``) and only marshal
+arguments: tensor checks, pointers, the current HIP stream, and output / workspace
+allocation through torch.  Every step of the projection runs in the library's HIP kernels.
+There is no fallback: if the library is not built, every compute call raises.
+
+Tensor conventions (all on the GPU, contiguous):
+    x        torch.bfloat16 [M, K]
+    wq       torch.int32    [N, K/8]   packed codes, read as uint32 (low nibble first)
+    scales   torch.bfloat16 [N, K/128]
+    biases   torch.bfloat16 [N, K/128]
+    y        torch.bfloat16 [M, N]
+
+``linear(..., logits_to_keep=k)`` is the model-level entry: it projects only the last ``k``
+rows (a view, no copy) before the projection, as tiny-llm's "Week 2 Day 6: SIMD-Matrix
+Prefill", Task 4 does before the vocabulary head; ``k = 0`` projects every row.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = [
+    "W4A16_OK", "PATH_AUTO", "PATH_QMV", "PATH_QMM", "GROUP",
+    "load", "lib_path", "w4a16_abi_version", "w4a16_status_string", "w4a16_plan", "w4a16_workspace_bytes",
+    "qmv_w4a16", "qmm_w4a16", "w4a16_linear", "linear", "W4A16Error", "declared_symbols",
+]
+
+GROUP = 128
+W4A16_OK = 0
+PATH_AUTO, PATH_QMV, PATH_QMM = 0, 1, 2
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_HEADER = os.path.join(os.path.dirname(_PKG_DIR), "include", "w4a16.h")
+_LIB = None
+
+
+class W4A16Error(RuntimeError):
+    pass
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "path", "tile_m", "tile_n", "tile_k", "grid_x", "grid_y", "grid_z", "block_threads",
+        "split_k", "k_waves", "num_cus", "variant")] + [("workspace_bytes", ctypes.c_uint64)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+def lib_path() -> str:
+    return os.environ.get("W4A16_LIB", os.path.join(_PKG_DIR, "libw4a16.so"))
+
+
+def load():
+    """Load ``libw4a16.so`` (built in-tree) and declare its C signatures; raises if missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise W4A16Error(f"{path} is not built; run `python -m w4a16_group_quantized_qmv_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, u16p, u32p = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p
+    lib.w4a16_abi_version.restype = ctypes.c_int
+    lib.w4a16_abi_version.argtypes = []
+    lib.w4a16_status_string.restype = ctypes.c_char_p
+    lib.w4a16_status_string.argtypes = [ctypes.c_int]
+    lib.w4a16_plan.restype = ctypes.c_int
+    lib.w4a16_plan.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(Plan)]
+    lib.w4a16_workspace_bytes.restype = ctypes.c_uint64
+    lib.w4a16_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    lib.qmv_w4a16.restype = ctypes.c_int
+    lib.qmv_w4a16.argtypes = [u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, vp]
+    lib.qmm_w4a16.restype = ctypes.c_int
+    lib.qmm_w4a16.argtypes = [u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.w4a16_linear.restype = ctypes.c_int
+    lib.w4a16_linear.argtypes = [u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, vp, ctypes.c_size_t, vp]
+    _LIB = lib
+    return lib
+
+
+def declared_symbols() -> list[str]:
+    """Function names declared in include/w4a16.h."""
+    with open(_HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+# ------------------------------------------------------------------------------------ status
+
+
+def w4a16_abi_version() -> int:
+    return load().w4a16_abi_version()
+
+
+def w4a16_status_string(status: int) -> str:
+    return load().w4a16_status_string(status).decode()
+
+
+def _raise_for(status: int, what: str):
+    if status == W4A16_OK:
+        return
+    msg = f"{what}: {w4a16_status_string(status)}"
+    if status in (1, 2, 3, 4, 5):
+        raise ValueError(msg)
+    if status == 6:
+        raise NotImplementedError(msg)
+    raise W4A16Error(msg)
+
+
+# ------------------------------------------------------------------------------------ planning
+
+
+def w4a16_plan(M: int, N: int, K: int, group: int = GROUP, path: int = PATH_AUTO, split_k: int = 0,
+               num_cus: int = 0) -> dict:
+    p = Plan()
+    _raise_for(load().w4a16_plan(M, N, K, group, path, split_k, num_cus, ctypes.byref(p)), "w4a16_plan")
+    return p.as_dict()
+
+
+def w4a16_workspace_bytes(M: int, N: int, K: int, group: int = GROUP, num_cus: int = 0) -> int:
+    return int(load().w4a16_workspace_bytes(M, N, K, group, num_cus))
+
+
+# ------------------------------------------------------------------------------------ tensors
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(t, name, dtype, shape):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _operands(x, wq, scales, biases, y):
+    torch = _torch()
+    if x.dim() != 2 or wq.dim() != 2:
+        raise ValueError("x and wq must be 2-D")
+    M, K = x.shape
+    N = wq.shape[0]
+    if K % GROUP:
+        raise ValueError(f"K={K} must be a multiple of {GROUP}")
+    _check(x, "x", torch.bfloat16, (M, K))
+    _check(wq, "wq", torch.int32, (N, K // 8))
+    _check(scales, "scales", torch.bfloat16, (N, K // GROUP))
+    _check(biases, "biases", torch.bfloat16, (N, K // GROUP))
+    devs = {t.device for t in (x, wq, scales, biases)}
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(y, "y", torch.bfloat16, (M, N))
+    devs.add(y.device)
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one device, got {devs}")
+    return M, N, K, y
+
+
+def _stream(stream, device):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(workspace, nbytes, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def qmv_w4a16(x, wq, scales, biases, y=None, stream=None):
+    """Decode-row matvec (1 <= M <= 8); returns y."""
+    M, N, K, y = _operands(x, wq, scales, biases, y)
+    st = load().qmv_w4a16(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(),
+                          M, N, K, GROUP, _stream(stream, x.device))
+    _raise_for(st, "qmv_w4a16")
+    return y
+
+
+def qmm_w4a16(x, wq, scales, biases, y=None, split_k: int = 0, workspace=None, stream=None):
+    """Tiled matrix path for any M; split_k 0 = policy, 1 = off, S > 1 forced.  Returns y."""
+    M, N, K, y = _operands(x, wq, scales, biases, y)
+    need = w4a16_plan(M, N, K, GROUP, PATH_QMM, split_k)["workspace_bytes"]
+    ws, ws_bytes = _workspace(workspace, need, x.device)
+    st = load().qmm_w4a16(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(),
+                          M, N, K, GROUP, split_k, None if ws is None else ws.data_ptr(), ws_bytes,
+                          _stream(stream, x.device))
+    _raise_for(st, "qmm_w4a16")
+    return y
+
+
+def w4a16_linear(x, wq, scales, biases, y=None, workspace=None, stream=None):
+    """Dispatching entry point (qmv for M <= 8, qmm with the policy's split otherwise).  Returns y."""
+    M, N, K, y = _operands(x, wq, scales, biases, y)
+    ws, ws_bytes = _workspace(workspace, w4a16_workspace_bytes(M, N, K), x.device)
+    st = load().w4a16_linear(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(),
+                             M, N, K, GROUP, None if ws is None else ws.data_ptr(), ws_bytes,
+                             _stream(stream, x.device))
+    _raise_for(st, "w4a16_linear")
+    return y
+
+
+def linear(x, wq, scales, biases, logits_to_keep: int = 0, path: str | None = None, split_k: int | None = None):
+    """Quantized linear layer ``y = x · dequant(Wq)ᵀ`` with the ``logits_to_keep`` row slice.
+
+    ``logits_to_keep = k > 0`` projects only the last ``k`` rows (for generation, the final
+    prompt row before the vocabulary head); ``0`` projects every row (prompt scoring).
+    ``path`` ("qmv" / "qmm") and ``split_k`` force a path or split for tests and benchmarks.
+    """
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M = x.shape[0]
+    if logits_to_keep < 0 or logits_to_keep > M:
+        raise ValueError(f"logits_to_keep={logits_to_keep} must be in [0, M={M}]")
+    if logits_to_keep:
+        x = x[M - logits_to_keep:]          # trailing rows of a row-major matrix: still contiguous
+    if path is None and split_k is None:
+        return w4a16_linear(x, wq, scales, biases)
+    if path == "qmv":
+        return qmv_w4a16(x, wq, scales, biases)
+    if path in (None, "qmm"):
+        return qmm_w4a16(x, wq, scales, biases, split_k=split_k or 0)
+    raise ValueError(f"unknown path {path!r}")

@@ -1,0 +1,245 @@
+// C ABI of libw4a16.so: argument validation, the dispatch / split-K policy and the entry
+// points declared in include/w4a16.h.  Every compute call only enqueues kernels on the
+// caller's stream; nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stdint.h>
+
+#include "internal.h"
+#include "w4a16.h"
+
+namespace {
+
+using namespace w4a16;
+
+// Policy constants.
+constexpr int64_t kQmvMaxRows = 8;        // decode rows served by qmv ("Week 2 Day 6", Task 1)
+constexpr int kSplitMinGroups = 4;        // fewest groups one split-K slice may own
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+
+std::atomic<int> g_cu_cache[64];
+
+int query_num_cus(int32_t* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_DEVICE;
+    if (dev >= 0 && dev < 64) {
+        const int cached = g_cu_cache[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            *out = cached;
+            return W4A16_OK;
+        }
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return W4A16_ERR_DEVICE;
+    if (dev >= 0 && dev < 64) g_cu_cache[dev].store(cus, std::memory_order_relaxed);
+    *out = cus;
+    return W4A16_OK;
+}
+
+int check_shape(int64_t M, int64_t N, int64_t K, int32_t group) {
+    if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return W4A16_ERR_SHAPE;
+    if (group != W4A16_GROUP) return W4A16_ERR_GROUP;
+    if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
+    return W4A16_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_buffers(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b, const uint16_t* y) {
+    if (!x || !wq || !s || !b || !y) return W4A16_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(s, 2) || !aligned(b, 2) || !aligned(y, 2))
+        return W4A16_ERR_ALIGN;
+    return W4A16_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
+    const int64_t G = K / W4A16_GROUP;
+    const int64_t col_blocks = ceil_div(N, 16);
+    int variant;
+    const QmvShape& wide = kQmvVariants[0];
+    if (ceil_div(N, int64_t{wide.cb} * wide.wn * 16) >= cus) {
+        variant = 0;  // enough workgroups without splitting K inside a workgroup
+    } else {
+        // narrow: 16 columns per workgroup, kw waves share K; aim at one wave per SIMD (4 per CU)
+        // while leaving every wave at least two groups
+        const int64_t want = 4 * static_cast<int64_t>(cus);
+        variant = 1;  // kw = 4
+        if (col_blocks * 4 < want && G >= 16) variant = 2;   // kw = 8
+        if (col_blocks * 8 < want && G >= 32) variant = 3;   // kw = 16
+    }
+    const QmvShape& v = kQmvVariants[variant];
+    p->path = W4A16_PATH_QMV;
+    p->tile_m = 16;
+    p->tile_n = v.cb * v.wn * 16;
+    p->tile_k = W4A16_GROUP;
+    p->grid_x = static_cast<int32_t>(ceil_div(N, p->tile_n));
+    p->grid_y = 1;
+    p->grid_z = 1;
+    p->block_threads = 64 * v.wn * v.kw;
+    p->split_k = 1;
+    p->k_waves = v.kw;
+    p->variant = variant;
+    p->workspace_bytes = 0;
+    (void)M;
+}
+
+void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p) {
+    const int64_t G = K / W4A16_GROUP;
+    int variant;
+    if (M <= 64) {
+        variant = 2;
+    } else {
+        const QmmShape& big = kQmmVariants[0];
+        const int64_t big_tiles = ceil_div(M, big.bm) * ceil_div(N, int64_t{big.nwaves} * big.nb * 16);
+        variant = big_tiles >= cus ? 0 : 1;
+    }
+    const QmmShape& v = kQmmVariants[variant];
+    const int64_t tile_n = int64_t{v.nwaves} * v.nb * 16;
+    const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, tile_n);
+    int64_t S = 1;
+    if (split_k == 0) {
+        // split only an under-filled grid, and only when every slice keeps several groups
+        if (tiles < cus && G >= 2 * kSplitMinGroups) {
+            S = ceil_div(cus, tiles);
+            if (S > G / kSplitMinGroups) S = G / kSplitMinGroups;
+            if (S < 2) S = 1;
+        }
+    } else {
+        S = split_k < 1 ? 1 : split_k;
+        if (S > G) S = G;
+    }
+    p->path = W4A16_PATH_QMM;
+    p->tile_m = v.bm;
+    p->tile_n = static_cast<int32_t>(tile_n);
+    p->tile_k = W4A16_GROUP;
+    p->grid_x = static_cast<int32_t>(ceil_div(N, tile_n));
+    p->grid_y = static_cast<int32_t>(ceil_div(M, v.bm));
+    p->grid_z = static_cast<int32_t>(S);
+    p->block_threads = 64 * v.nwaves;
+    p->split_k = static_cast<int32_t>(S);
+    p->k_waves = 1;
+    p->variant = variant;
+    p->workspace_bytes = S > 1 ? static_cast<uint64_t>(S) * M * N * sizeof(float) : 0;
+}
+
+int make_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, int32_t split_k, int32_t num_cus,
+              w4a16_plan_t* out) {
+    if (!out) return W4A16_ERR_NULL;
+    int st = check_shape(M, N, K, group);
+    if (st != W4A16_OK) return st;
+    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_QMV && path != W4A16_PATH_QMM) return W4A16_ERR_UNSUPPORTED;
+    if (split_k < 0) return W4A16_ERR_SHAPE;
+    int32_t cus = num_cus;
+    if (cus <= 0) {
+        st = query_num_cus(&cus);
+        if (st != W4A16_OK) return st;
+    }
+    if (path == W4A16_PATH_AUTO) path = M <= kQmvMaxRows ? W4A16_PATH_QMV : W4A16_PATH_QMM;
+    if (path == W4A16_PATH_QMV) {
+        if (M > kQmvMaxRows) return W4A16_ERR_UNSUPPORTED;
+        plan_qmv(M, N, K, cus, out);
+    } else {
+        plan_qmm(M, N, K, split_k, cus, out);
+    }
+    out->num_cus = cus;
+    return W4A16_OK;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
+
+int run_plan(const w4a16_plan_t& p, const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+             uint16_t* y, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream) {
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    if (p.path == W4A16_PATH_QMV) return to_status(launch_qmv(p.variant, x, wq, s, b, y, m, n, k, stream));
+    float* ws = static_cast<float*>(workspace);
+    hipError_t e = launch_qmm(p.variant, x, wq, s, b, y, ws, m, n, k, p.split_k, stream);
+    if (e != hipSuccess || p.split_k == 1) return to_status(e);
+    return to_status(launch_splitk_reduce(ws, y, M * N, p.split_k, stream));
+}
+
+int run_qmm(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b, uint16_t* y, int64_t M,
+            int64_t N, int64_t K, int32_t group, int32_t path, int32_t split_k, void* workspace, size_t ws_bytes,
+            void* stream) {
+    int st = check_shape(M, N, K, group);
+    if (st != W4A16_OK) return st;
+    st = check_buffers(x, wq, s, b, y);
+    if (st != W4A16_OK) return st;
+    if (split_k < 0) return W4A16_ERR_SHAPE;
+    w4a16_plan_t p;
+    st = make_plan(M, N, K, group, path, split_k, 0, &p);
+    if (st != W4A16_OK) return st;
+    if (p.path == W4A16_PATH_QMM && p.split_k > 1) {
+        const bool ws_ok = workspace != nullptr && aligned(workspace, 16) && ws_bytes >= p.workspace_bytes;
+        if (!ws_ok) {
+            if (split_k > 1) return workspace != nullptr && !aligned(workspace, 16) ? W4A16_ERR_ALIGN
+                                                                                     : W4A16_ERR_WORKSPACE;
+            // policy split without a usable workspace: the unsplit plan computes the same result
+            plan_qmm(M, N, K, 1, p.num_cus, &p);
+        }
+    }
+    return run_plan(p, x, wq, s, b, y, M, N, K, workspace, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+const char* w4a16_status_string(int status) {
+    switch (status) {
+        case W4A16_OK: return "W4A16_OK";
+        case W4A16_ERR_NULL: return "W4A16_ERR_NULL";
+        case W4A16_ERR_SHAPE: return "W4A16_ERR_SHAPE";
+        case W4A16_ERR_GROUP: return "W4A16_ERR_GROUP";
+        case W4A16_ERR_ALIGN: return "W4A16_ERR_ALIGN";
+        case W4A16_ERR_WORKSPACE: return "W4A16_ERR_WORKSPACE";
+        case W4A16_ERR_UNSUPPORTED: return "W4A16_ERR_UNSUPPORTED";
+        case W4A16_ERR_LAUNCH: return "W4A16_ERR_LAUNCH";
+        case W4A16_ERR_DEVICE: return "W4A16_ERR_DEVICE";
+        default: return "unknown";
+    }
+}
+
+int w4a16_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, int32_t split_k, int32_t num_cus,
+               w4a16_plan_t* out) {
+    return make_plan(M, N, K, group, path, split_k, num_cus, out);
+}
+
+uint64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t num_cus) {
+    w4a16_plan_t p;
+    if (make_plan(M, N, K, group, W4A16_PATH_AUTO, 0, num_cus, &p) != W4A16_OK) return 0;
+    return p.workspace_bytes;
+}
+
+int qmv_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, uint16_t* y,
+              int64_t M, int64_t N, int64_t K, int32_t group, void* stream) {
+    int st = check_shape(M, N, K, group);
+    if (st != W4A16_OK) return st;
+    st = check_buffers(x, wq, scales, biases, y);
+    if (st != W4A16_OK) return st;
+    if (M > kQmvMaxRows) return W4A16_ERR_UNSUPPORTED;
+    w4a16_plan_t p;
+    st = make_plan(M, N, K, group, W4A16_PATH_QMV, 1, 0, &p);
+    if (st != W4A16_OK) return st;
+    return run_plan(p, x, wq, scales, biases, y, M, N, K, nullptr, static_cast<hipStream_t>(stream));
+}
+
+int qmm_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, uint16_t* y,
+              int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, void* workspace,
+              size_t workspace_bytes, void* stream) {
+    return run_qmm(x, wq, scales, biases, y, M, N, K, group, W4A16_PATH_QMM, split_k, workspace, workspace_bytes,
+                   stream);
+}
+
+int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, uint16_t* y,
+                 int64_t M, int64_t N, int64_t K, int32_t group, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    return run_qmm(x, wq, scales, biases, y, M, N, K, group, W4A16_PATH_AUTO, 0, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
