@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 group-quantized projection hot path on one MI355X.
+
+One step is one 512-token prefill pass through the projections of one decoder layer
+(hidden 2560, 32 query heads and 8 key/value heads of dimension 128, MLP 9728: q, k, v, o,
+gate, up, down at M = 512, where the down projection's K = 9728 exercises split-K), followed
+by the vocabulary head (2560 -> 151936) applied to the last row only (logits_to_keep = 1,
+which dispatches to the matvec path).  These are the per-projection prefill shapes that
+tiny-llm's "Week 2 Day 6: SIMD-Matrix Prefill" benchmarks in Task 5 and its Benchmark
+Analysis, with Task 4's last-row slice before the vocabulary projection.  Inputs are seeded
+synthetic data (the pages' Qwen3-4B weights are not available): x ~ N(0, 1) in bf16,
+W ~ N(0, 0.02) quantized to 4-bit affine groups of 128.
+
+All inputs are resident in HBM before the timed region.  Weight sets rotate over several
+device copies so that weight reads miss the 256 MB last-level cache.  Output: one JSON line.
+
+    python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 qmm TFLOP/s + % roofline at M=128/512 prefill; qmv GB/s at M=1"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+M_PREFILL = 512
+LAYER = ["q", "k", "v", "o", "gate", "up", "down"]
+DOMINANT = ("gate", "up")     # largest projections: the roofline kernel
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qmm_prefill512_gate_up_traffic.json")
+KERNEL_SOURCES = ["w4a16_group_quantized_qmv_amd/csrc/qmm.hip", "w4a16_group_quantized_qmv_amd/csrc/device_common.h"]
+
+
+def flops(M, N, K):
+    return 2.0 * M * N * K
+
+
+def algo_bytes(M, N, K):
+    """Algorithmic bytes: packed codes + bf16 scale and bias per group + x + y."""
+    return N * K / 2 + N * K / 32 + 2.0 * M * K + 2.0 * M * N
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per dominant-kernel launch from the committed counter summary, or None when
+    the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def build_inputs(torch, copies):
+    import numpy as np
+    from w4a16_group_quantized_qmv_amd import synth
+    dev = torch.device("cuda", 0)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    projections = []
+    for name in LAYER:
+        idx = synth.shape_index(4, name)
+        K, N = synth.LAYER_SHAPES[name]
+        wq, s, b = synth.weights(4, idx, N, K)
+        x = synth.activations(4, idx, M_PREFILL, K)
+        projections.append({"name": name, "M": M_PREFILL, "N": N, "K": K, "keep": 0,
+                            "host": {"x": x, "wq": wq, "scales": s, "biases": b},
+                            "x": bf16(x), "w": [(torch.from_numpy(wq.view(np.int32)).to(dev), bf16(s), bf16(b))]})
+    vidx = synth.shape_index(5, "vocab")
+    K, N = synth.VOCAB_SHAPE
+    wq, s, b = synth.weights(5, vidx, N, K)
+    x = synth.activations(5, vidx, M_PREFILL, K)
+    projections.append({"name": "vocab_last_row", "M": 1, "N": N, "K": K, "keep": 1,
+                        "host": {"x": x, "wq": wq, "scales": s, "biases": b},
+                        "x": bf16(x), "w": [(torch.from_numpy(wq.view(np.int32)).to(dev), bf16(s), bf16(b))]})
+    for p in projections:        # extra device copies of every weight set (same values)
+        base = p["w"][0]
+        for _ in range(copies - 1):
+            p["w"].append(tuple(t.clone() for t in base))
+    return projections
+
+
+def cpu_baseline(projections):
+    """The oracle, untuned, on one full step (seven projections at M=512 + the last vocab row)."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    total_flops = 0.0
+    t0 = time.perf_counter()
+    for p in projections:
+        h = p["host"]
+        x = h["x"][-p["keep"]:] if p["keep"] else h["x"]
+        O.reference(x, h["wq"], h["scales"], h["biases"])
+        total_flops += flops(x.shape[0], p["N"], p["K"])
+    dt = time.perf_counter() - t0
+    return {"value": total_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "one full step: the seven 512-row layer projections and the last vocab row, "
+                      "unpack + fp32 dequant + fp64 GEMM (reference() with abs-mass), wall clock",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--copies", type=int, default=3, help="device copies of the weights, rotated per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the projection kernels on a single MI355X "
+              "(column- or row-sharding across GPUs is described in DESIGN.md, not implemented).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import w4a16_group_quantized_qmv_amd as w4
+    w4.load()                                   # raises when the HIP library is not built
+    torch.cuda.set_device(0)
+    t_gen = time.perf_counter()
+    projections = build_inputs(torch, args.copies)
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    # prepared calls: one per (projection, weight copy); y buffers shared across copies
+    calls = []
+    for c in range(args.copies):
+        row = []
+        for p in projections:
+            x = p["x"][-p["keep"]:] if p["keep"] else p["x"]
+            wq, s, b = p["w"][c]
+            prev = calls[0][len(row)].y if calls else None
+            row.append(w4.PreparedLinear(x, wq, s, b, y=prev))
+        calls.append(row)
+    plans = [call.plan for call in calls[0]]
+
+    def step(i, events=None):
+        row = calls[i % args.copies]
+        for j, call in enumerate(row):
+            if events is not None:
+                events[j][0].record()
+            call()
+            if events is not None:
+                events[j][1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    n = len(projections)
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(n)]
+          for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i, ev[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = start.elapsed_time(end)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+
+    per = []
+    for j, p in enumerate(projections):
+        us = sorted(ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e3 for i in range(args.steps))
+        avg = sum(us) / len(us)
+        f, by = flops(p["M"], p["N"], p["K"]), algo_bytes(p["M"], p["N"], p["K"])
+        pl = plans[j]
+        per.append({"name": p["name"], "M": p["M"], "N": p["N"], "K": p["K"], "avg_us": round(avg, 3),
+                    "median_us": round(us[len(us) // 2], 3), "TFLOP/s": round(f / avg / 1e6, 2),
+                    "GB/s": round(by / avg / 1e3, 1),
+                    "path": "qmv" if pl["path"] == 1 else "qmm", "variant": pl["variant"],
+                    "tile": [pl["tile_m"], pl["tile_n"]], "split_k": pl["split_k"]})
+    step_flops = sum(flops(p["M"], p["N"], p["K"]) for p in projections)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    dom = [r for r in per if r["name"] in DOMINANT]
+    dom_flops = flops(M_PREFILL, *synth_shape("gate"))
+    dom_us = sum(r["avg_us"] for r in dom) / len(dom)
+    achieved = dom_flops / dom_us / 1e6
+    traffic = load_traffic()
+    vocab = per[-1]
+    vocab_bytes = algo_bytes(1, vocab["N"], vocab["K"])
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill512_layer_projections+vocab_last_row", "M": M_PREFILL,
+                   "projections": {p["name"]: [p["K"], p["N"]] for p in projections}, "group": 128,
+                   "weight_copies": args.copies, "logits_to_keep": 1},
+        "roofline": {"bound": "mfma", "kernel": f"qmm variant {dom[0]['variant']} (gate/up, M=512, K=2560, N=9728)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "flops_per_launch": dom_flops, "avg_launch_us": round(dom_us, 3)},
+        "qmv_vocab_last_row": {"GB/s": round(vocab_bytes / vocab["avg_us"] / 1e3, 1),
+                               "frac_hbm": round(vocab_bytes / vocab["avg_us"] / 1e3 / PEAK_HBM_GBPS, 4),
+                               "avg_us": vocab["avg_us"], "bytes": vocab_bytes},
+        "breakdown": per,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(projections)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def synth_shape(name):
+    from w4a16_group_quantized_qmv_amd import synth
+    K, N = synth.LAYER_SHAPES[name]
+    return N, K
+
+
+if __name__ == "__main__":
+    main()

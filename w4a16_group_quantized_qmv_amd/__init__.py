@@ -26,7 +26,7 @@ import re
 __all__ = [
     "W4A16_OK", "PATH_AUTO", "PATH_QMV", "PATH_QMM", "GROUP",
     "load", "lib_path", "w4a16_abi_version", "w4a16_status_string", "w4a16_plan", "w4a16_workspace_bytes",
-    "qmv_w4a16", "qmm_w4a16", "w4a16_linear", "linear", "W4A16Error", "declared_symbols",
+    "qmv_w4a16", "qmm_w4a16", "w4a16_linear", "linear", "W4A16Error", "declared_symbols", "PreparedLinear",
 ]
 
 GROUP = 128
@@ -241,3 +241,42 @@ def linear(x, wq, scales, biases, logits_to_keep: int = 0, path: str | None = No
     if path in (None, "qmm"):
         return qmm_w4a16(x, wq, scales, biases, split_k=split_k or 0)
     raise ValueError(f"unknown path {path!r}")
+
+
+class PreparedLinear:
+    """One projection with fixed tensors, validated once; calling it only enqueues the kernels.
+
+    For timing loops and graph capture: the output ``y`` and any split-K workspace are
+    allocated here, and ``__call__`` issues a single C-ABI call (``w4a16_linear``, or
+    ``qmv_w4a16`` / ``qmm_w4a16`` when ``path`` forces one) on the stream current at
+    construction.
+    """
+
+    def __init__(self, x, wq, scales, biases, y=None, path: str | None = None, split_k: int = 0):
+        M, N, K, y = _operands(x, wq, scales, biases, y)
+        self.M, self.N, self.K, self.y = M, N, K, y
+        lib = load()
+        stream = _stream(None, x.device)
+        ptrs = (x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(), M, N, K, GROUP)
+        if path == "qmv":
+            self.plan = w4a16_plan(M, N, K, GROUP, PATH_QMV, 1)
+            self._fn, self._args, self._name = lib.qmv_w4a16, ptrs + (stream,), "qmv_w4a16"
+            self.workspace = None
+        else:
+            forced = path == "qmm" or split_k != 0
+            self.plan = w4a16_plan(M, N, K, GROUP, PATH_QMM if forced else PATH_AUTO, split_k)
+            ws, ws_bytes = _workspace(None, self.plan["workspace_bytes"], x.device)
+            self.workspace = ws
+            wsp = None if ws is None else ws.data_ptr()
+            if forced:
+                self._fn, self._name = lib.qmm_w4a16, "qmm_w4a16"
+                self._args = ptrs + (split_k, wsp, ws_bytes, stream)
+            else:
+                self._fn, self._name = lib.w4a16_linear, "w4a16_linear"
+                self._args = ptrs + (wsp, ws_bytes, stream)
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != W4A16_OK:
+            _raise_for(st, self._name)
+        return self.y
