@@ -89,16 +89,16 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
 
 void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p) {
     const int64_t G = K / W4A16_GROUP;
-    int variant;
-    if (M <= 64) {
-        variant = 2;
-    } else {
-        const QmmShape& big = kQmmVariants[0];
-        const int64_t big_tiles = ceil_div(M, big.bm) * ceil_div(N, int64_t{big.nwaves} * big.nb * 16);
-        variant = big_tiles >= cus ? 0 : 1;
-    }
+    auto tiles_of = [&](int v) {
+        const QmmShape& q = kQmmVariants[v];
+        return ceil_div(M, q.bm) * ceil_div(N, int64_t{q.nwaves} * q.nb * 32);
+    };
+    // Measured on MI355X: 64 x 128 tiles (three waves per SIMD) lead up to about a thousand
+    // rows, where the grid is small; 128 x 128 tiles (two waves per SIMD) lead beyond.
+    int variant = M <= 1024 ? 1 : 0;
+    (void)tiles_of;
     const QmmShape& v = kQmmVariants[variant];
-    const int64_t tile_n = int64_t{v.nwaves} * v.nb * 16;
+    const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
     const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, tile_n);
     int64_t S = 1;
     if (split_k == 0) {

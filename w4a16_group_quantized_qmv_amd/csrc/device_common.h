@@ -1,13 +1,17 @@
 // Device helpers shared by the qmv and qmm kernels (gfx950 / CDNA4 only).
 //
-// Operand layouts of the bf16 MFMA used here, v_mfma_f32_16x16x32_bf16 (checked on the MI355X
-// with an in-bounds probe):
-//   A (16 x 32):  lane l holds A[l % 16][8 * (l / 16) + e],  e = 0..7
-//   B (32 x 16):  lane l holds B[8 * (l / 16) + e][l % 16],  e = 0..7
-//   D (16 x 16):  lane l, register r holds D[4 * (l / 16) + r][l % 16]
+// Operand layouts of the two bf16 MFMA shapes used here (checked on the MI355X with an
+// in-bounds probe):
+//   v_mfma_f32_16x16x32_bf16 (qmv)
+//     A (16 x 32):  lane l holds A[l % 16][8 * (l / 16) + e],  e = 0..7
+//     B (32 x 16):  lane l holds B[8 * (l / 16) + e][l % 16]
+//     D (16 x 16):  lane l, register r holds D[4 * (l / 16) + r][l % 16]
+//   v_mfma_f32_32x32x16_bf16 (qmm; about twice the sustained rate of the 16x16x32 shape)
+//     A (32 x 16):  lane l holds A[l % 32][8 * (l / 32) + e]
+//     B (16 x 32):  lane l holds B[8 * (l / 32) + e][l % 32]
+//     D (32 x 32):  lane l, register r holds D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
 // Any bijection between the MFMA's K index and real reduction indices is allowed as long as A
-// and B use the same one; both kernels give lane group h = l / 16 the 32 consecutive values
-// [32h, 32h + 32) of a 128-wide quantization group and feed them 8 at a time.
+// and B use the same one; the kernels document theirs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,6 +22,7 @@ namespace w4a16 {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -35,6 +40,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
 
 __device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // Four-bit codes as fp8 bytes.  Masking a packed word with 0x0F0F0F0F leaves the even codes

@@ -21,7 +21,7 @@ extern const QmvShape kQmvVariants[kNumQmvVariants];
 hipError_t launch_qmv(int variant, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
                       const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream);
 
-// qmm: workgroup tile of bm rows x (nwaves * nb * 16) columns; every wave owns nb 16-column
+// qmm: workgroup tile of bm rows x (nwaves * nb * 32) columns; every wave owns nb 32-column
 // blocks for all bm rows.
 struct QmmShape {
     int bm;
@@ -29,7 +29,7 @@ struct QmmShape {
     int nwaves;
 };
 
-constexpr int kNumQmmVariants = 3;
+constexpr int kNumQmmVariants = 5;
 extern const QmmShape kQmmVariants[kNumQmmVariants];
 
 // split == 1 writes bf16 y; split > 1 writes fp32 partials ws[z][M][N] for z < split.

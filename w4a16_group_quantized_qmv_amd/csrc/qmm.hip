@@ -8,28 +8,46 @@
 // Analysis: Identify Under-Filled Prefill Shapes" add split-K for grids with too few tiles.
 //
 // MI355X design (not the pages' 32x32x32 / 128-thread Apple tile):
-//  * Workgroup tile BM x BN with NW waves; each wave owns NB 16-column blocks for all BM rows, so
-//    each weight is unpacked and dequantized exactly once per workgroup, in registers, by the
-//    wave that uses it.  Weights never pass through LDS.
+//  * The contraction runs on v_mfma_f32_32x32x16_bf16, the bf16 shape with the higher
+//    sustained rate on gfx950.
+//  * Workgroup tile BM x BN with NW waves; each wave owns NB 32-column blocks for all BM rows,
+//    so each weight is unpacked and dequantized exactly once per workgroup, in registers, by the
+//    wave that consumes it, and every dequantized operand feeds BM / 32 MFMAs.  Weights never
+//    pass through LDS.
 //  * One pipeline step is one 128-value quantization group: the scale and bias of a column are
-//    loaded once per step and serve all four 32-value MFMA sub-steps of the group (the analogue
-//    of the page's four reduction tiles per group).
-//  * Activations (shared by every wave) are staged in LDS, double buffered, with a row stride of
-//    136 bf16 (272 bytes): sixteen lanes reading 16 bytes from sixteen consecutive rows then
-//    touch all 64 banks once.
-//  * Global loads are 16 bytes per lane: a lane group reads 64 contiguous bytes (one group) of
-//    16 consecutive weight columns; the activation tile is read row-contiguously.
-//  * Tile order is XCD-aware: workgroup i runs on XCD i % 8, and the remap below hands each XCD
-//    a contiguous run of tiles in M-fastest order, so the M-tiles that re-read the same weight
-//    columns share one L2.
-//  * Split-K: blockIdx selects one of S contiguous runs of groups (sizes differ by at most one).
-//    Each slice writes fp32 partials; splitk_reduce sums them in slice order (deterministic).
+//    loaded once per step and serve all eight 16-value MFMA sub-steps of the group (the
+//    analogue of the page's four reduction tiles per group).
+//  * K mapping inside a group: lane half h = l / 32 of a wave holds words 8h .. 8h + 7 of its
+//    column's group (64 contiguous codes); MFMA sub-step t takes word 8h + t from half h, so
+//    its 16 reduction values are {64h + 8t + e}.  The activation fragment is read from LDS at
+//    the same offsets.
+//  * Activations (shared by every wave) are staged in LDS, double buffered, by the gfx950
+//    direct global-to-LDS loads (global_load_lds_dwordx4): no registers and almost no VALU
+//    work per staged byte.  One wave instruction writes 1 KB = four 256-byte rows.  Rows are
+//    unpadded; instead the 16-byte chunk position p of row r holds activation chunk
+//    p ^ (r & 7), so eight lanes reading one chunk of eight consecutive rows hit eight
+//    different bank groups (conflict-free 16-byte reads).  Rows past M are loaded from row M-1
+//    (in bounds); they only feed output rows that are never stored.
+//  * One barrier per group: the wave's own direct loads for the next group are waited for
+//    (vmcnt) before the barrier that ends the current group, and the next buffer is refilled
+//    only after that barrier.  The weight registers ping-pong between even and odd groups.
+//  * The dequantization of MFMA sub-step t + 1 is issued next to the MFMAs of sub-step t so the
+//    VALU work hides under the matrix core.
+//  * Global loads are 16 bytes per lane: each column's group is 64 contiguous bytes read by its
+//    two lanes; the activation tile is read row-contiguously.
+//  * Tile order: workgroup i runs on XCD i % 8; the remap below hands each XCD a contiguous run
+//    of work indices, and work indices walk the tile grid in bands of up to 8 M-tiles, N-tile by
+//    N-tile, so the workgroups resident on one XCD share activation rows and weight columns in
+//    its L2.
+//  * Split-K: the work index also selects one of S contiguous runs of groups (sizes differ by at
+//    most one).  Each slice writes fp32 partials; splitk_reduce sums them in slice order, so the
+//    result is deterministic.
 #include "device_common.h"
 #include "internal.h"
 
 namespace w4a16 {
 
-constexpr int kLdsStride = kGroup + 8;  // bf16 elements per staged activation row
+constexpr int kBandM = 8;               // M-tiles per band of the tile order
 
 // Linear workgroup index -> work index such that XCD c (= i % 8) receives the contiguous range
 // of work indices [start_c, start_c + count_c).
@@ -39,24 +57,34 @@ __device__ __forceinline__ int xcd_remap(int i, int total) {
     return c * per + (c < rem ? c : rem) + k;
 }
 
-template <int BM, int NB, int NW>
-__global__ __launch_bounds__(64 * NW) void qmm_kernel(
+// Tile index -> (tm, tn): bands of up to kBandM M-tiles, each band walked N-tile by N-tile.
+__device__ __forceinline__ void band_order(int tile, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int band = tile / (kBandM * tiles_n);
+    const int first = band * kBandM;
+    const int rows = min(kBandM, tiles_m - first);
+    const int in_band = tile - band * kBandM * tiles_n;
+    tm = first + in_band % rows;
+    tn = in_band / rows;
+}
+
+template <int BM, int NB, int NW, int WAVES_PER_SIMD>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD))) void qmm_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N, int K,
     int split, int tiles_m, int tiles_n) {
-    constexpr int BN = NW * NB * 16;
-    constexpr int THREADS = 64 * NW;
-    constexpr int RB = BM / 16;                   // 16-row blocks per wave
-    constexpr int XCHUNKS = BM * 16 / THREADS;    // 16-byte activation chunks per thread per group
-    static_assert(BM * 16 % THREADS == 0, "activation tile must divide evenly among threads");
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kLdsStride];
+    constexpr int BN = NW * NB * 32;
+    constexpr int RB = BM / 32;                   // 32-row blocks per wave
+    constexpr int TILE = BM * kGroup;             // bf16 elements of one staged activation tile
+    constexpr int DMA_PER_WAVE = BM / (4 * NW);   // 1 KB direct loads per wave per group
+    static_assert(BM % (4 * NW) == 0 && BM % 32 == 0, "tile shape");
+    static_assert(NW == 4, "row & 15 of a direct load must not depend on the instruction index");
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2 * TILE];
 
     const int tiles = tiles_m * tiles_n;
     const int work = xcd_remap(blockIdx.x, tiles * split);
     const int z = work / tiles;
-    const int tile = work - z * tiles;
-    const int tm = tile % tiles_m;
-    const int tn = tile / tiles_m;
+    int tm, tn;
+    band_order(work - z * tiles, tiles_m, tiles_n, tm, tn);
 
     const int G = K >> 7;
     const int words_per_row = K >> 3;
@@ -65,111 +93,153 @@ __global__ __launch_bounds__(64 * NW) void qmm_kernel(
     const int m0 = tm * BM;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int kq = lane >> 4;
+    const int half = lane >> 5;
 
     int col[NB];
     bool col_ok[NB];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
-        col[cb] = tn * BN + (wave * NB + cb) * 16 + (lane & 15);
+        col[cb] = tn * BN + (wave * NB + cb) * 32 + (lane & 31);
         col_ok[cb] = col[cb] < N;
     }
 
-    // activation staging: chunk c = tid + i * THREADS covers row c / 16, 16-byte chunk c % 16
-    auto load_x = [&](int g, u32x4_t* xr) {
+    // direct activation loads through a buffer resource based at the tile's first row: reads
+    // past the last row return zeros and cannot fault.  Instruction i of this wave fills rows
+    // 4 * (i * NW + wave) + 0..3; lane l writes chunk position l % 16 of row l / 16 with
+    // activation chunk (l % 16) ^ (row & 15).  Row & 15 does not depend on i (rows advance by
+    // 4 * NW = 16 per instruction), so one 32-bit lane offset serves every instruction and the
+    // group / instruction steps go into the scalar offset.
+    const uint16_t* xtile = x + static_cast<size_t>(m0) * K;
+    const uint64_t tile_bytes = static_cast<uint64_t>(M - m0) * K * 2;
+    const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(xtile), 0, static_cast<int>(tile_bytes > 0x7FFFFFFFull ? 0x7FFFFFFFull : tile_bytes),
+        0x00020000);
+    const int xrow0 = 4 * wave + (lane >> 4);
+    const uint32_t xvoff = static_cast<uint32_t>(xrow0 * K + (((lane & 15) ^ (xrow0 & 15)) << 3)) * 2u;
+    auto stage_x = [&](int g, int buf) {
 #pragma unroll
-        for (int i = 0; i < XCHUNKS; ++i) {
-            const int c = threadIdx.x + i * THREADS;
-            const int r = c >> 4, kc = c & 15;
-            xr[i] = (m0 + r < M) ? load16(x + static_cast<size_t>(m0 + r) * K + g * kGroup + kc * 8)
-                                 : u32x4_t{0u, 0u, 0u, 0u};
+        for (int i = 0; i < DMA_PER_WAVE; ++i) {
+            uint16_t* dst = xs + buf * TILE + __builtin_amdgcn_readfirstlane(4 * (i * NW + wave) * kGroup);
+            const uint32_t soff = static_cast<uint32_t>(g) * (kGroup * 2) + static_cast<uint32_t>(i) * (4 * NW * 2) * K;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, dst, 16, xvoff, soff, 0, 0);
         }
     };
-    auto store_x = [&](int buf, const u32x4_t* xr) {
-#pragma unroll
-        for (int i = 0; i < XCHUNKS; ++i) {
-            const int c = threadIdx.x + i * THREADS;
-            const int r = c >> 4, kc = c & 15;
-            *reinterpret_cast<u32x4_t*>(&xs[buf][r * kLdsStride + kc * 8]) = xr[i];
-        }
-    };
-    auto load_w = [&](int g, u32x4_t* wv, uint16_t* sv, uint16_t* bv) {
+    // weights: lane half h takes words 8h .. 8h + 7 of the group (two 16-byte loads)
+    auto load_w = [&](int g, u32x4_t (*wv)[2], uint16_t* sv, uint16_t* bv) {
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
             if (col_ok[cb]) {
                 const size_t row = static_cast<size_t>(col[cb]);
-                wv[cb] = load16(wq + row * words_per_row + g * kWordsPerGroup + kq * 4);
+                const uint32_t* src = wq + row * words_per_row + g * kWordsPerGroup + half * 8;
+                wv[cb][0] = load16(src);
+                wv[cb][1] = load16(src + 4);
                 sv[cb] = scales[row * G + g];
                 bv[cb] = biases[row * G + g];
             } else {
-                wv[cb] = u32x4_t{0u, 0u, 0u, 0u};
+                wv[cb][0] = u32x4_t{0u, 0u, 0u, 0u};
+                wv[cb][1] = u32x4_t{0u, 0u, 0u, 0u};
                 sv[cb] = 0;
                 bv[cb] = 0;
             }
         }
     };
+    // LDS element offset of the A fragment of sub-step t for this lane (row block 0, buffer 0):
+    // row r = lane % 32, chunk 8 * half + t stored at position (8 * half + t) ^ (r & 15)
+    // = 8 * (half ^ (r >> 3 & 1)) + (t ^ (r & 7)); with the row part a multiple of 128 this is
+    // one lane constant XOR (t << 3).
+    const int arow = lane & 31;
+    const int abase = arow * kGroup + (((half ^ ((arow >> 3) & 1)) << 6) | ((arow & 7) << 3));
 
-    f32x4_t acc[RB][NB];
+    f32x16_t acc[RB][NB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
 
-    u32x4_t xr[XCHUNKS];
-    u32x4_t wcur[NB], wnxt[NB];
-    uint16_t scur[NB], bcur[NB], snxt[NB], bnxt[NB];
-
-    if (g_begin < g_end) {
-        load_x(g_begin, xr);
-        load_w(g_begin, wcur, scur, bcur);
-        store_x(0, xr);
-    }
-    __syncthreads();
-
-    for (int g = g_begin; g < g_end; ++g) {
-        const int buf = (g - g_begin) & 1;
-        const bool more = g + 1 < g_end;
-        if (more) {
-            load_x(g + 1, xr);
-            load_w(g + 1, wnxt, snxt, bnxt);
-        }
+    // One group: eight MFMA sub-steps.  Operands are double buffered by sub-step parity: while
+    // the MFMAs of sub-step t run, the fragment reads and the dequantization of sub-step t + 1
+    // are already issued.  The scheduling barrier at the end of each sub-step bounds the live
+    // registers to two sub-steps' operands.
+    auto compute = [&](int buf, const u32x4_t (*wv)[2], const uint16_t* sv, const uint16_t* bv) {
         float s[NB], b[NB];
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
-            s[cb] = bf16_bits_to_f32(scur[cb]);
-            b[cb] = bf16_bits_to_f32(bcur[cb]);
+            s[cb] = bf16_bits_to_f32(sv[cb]);
+            b[cb] = bf16_bits_to_f32(bv[cb]);
         }
-        const uint16_t* xt = &xs[buf][(lane & 15) * kLdsStride + kq * 32];
+        const uint16_t* xt = xs + buf * TILE;
+        bf16x8_t a[2][RB], bw[2][NB];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            bf16x8_t bw[NB];
+        for (int rb = 0; rb < RB; ++rb) a[0][rb] = *reinterpret_cast<const bf16x8_t*>(xt + abase + rb * 32 * kGroup);
 #pragma unroll
-            for (int cb = 0; cb < NB; ++cb) bw[cb] = dequant_word(wcur[cb][t], s[cb], b[cb]);
+        for (int cb = 0; cb < NB; ++cb) bw[0][cb] = dequant_word(wv[cb][0][0], s[cb], b[cb]);
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(xt + rb * 16 * kLdsStride + t * 8);
+        for (int t = 0; t < 8; ++t) {
+            const int cur = t & 1, nxt = cur ^ 1;
+            if (t < 7) {
 #pragma unroll
-                for (int cb = 0; cb < NB; ++cb) acc[rb][cb] = mfma16x16x32(a, bw[cb], acc[rb][cb]);
+                for (int rb = 0; rb < RB; ++rb)
+                    a[nxt][rb] = *reinterpret_cast<const bf16x8_t*>(xt + (abase ^ ((t + 1) << 3)) + rb * 32 * kGroup);
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb)
+                    bw[nxt][cb] = dequant_word(wv[cb][(t + 1) >> 2][(t + 1) & 3], s[cb], b[cb]);
             }
-        }
-        if (more) {
-            store_x(buf ^ 1, xr);
 #pragma unroll
-            for (int cb = 0; cb < NB; ++cb) {
-                wcur[cb] = wnxt[cb];
-                scur[cb] = snxt[cb];
-                bcur[cb] = bnxt[cb];
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb) acc[rb][cb] = mfma32x32x16(a[cur][rb], bw[cur][cb], acc[rb][cb]);
+            // interleave: each MFMA is followed by a share of the next sub-step's dequantization
+            // (VALU) and fragment reads, so the wave keeps issuing while the matrix core works
+#pragma unroll
+            for (int i = 0; i < RB * NB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, (20 * NB + RB * NB - 1) / (RB * NB), 0);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // LDS read
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+
+    u32x4_t wA[NB][2], wB[NB][2];
+    uint16_t sA[NB], bA[NB], sB[NB], bB[NB];
+
+    if (g_begin < g_end) {
+        stage_x(g_begin, 0);
+        load_w(g_begin, wA, sA, bA);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    for (int g = g_begin; g < g_end; g += 2) {
+        // even step: group g in buffer 0 and wA; prefetch group g + 1 into buffer 1 and wB
+        const bool has1 = g + 1 < g_end;
+        if (has1) {
+            stage_x(g + 1, 1);
+            load_w(g + 1, wB, sB, bB);
+        }
+        compute(0, wA, sA, bA);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (!has1) break;
+        // odd step: group g + 1 in buffer 1 and wB; prefetch group g + 2 into buffer 0 and wA
+        const bool has2 = g + 2 < g_end;
+        if (has2) {
+            stage_x(g + 2, 0);
+            load_w(g + 2, wA, sA, bA);
+        }
+        compute(1, wB, sB, bB);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 
-    // epilogue: D layout puts rows 4 * (lane / 16) + r of column lane % 16 in this lane
+    // epilogue: D layout puts rows 8 * (r / 4) + 4 * half + r % 4 of column lane % 32 in this lane
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = m0 + rb * 16 + 4 * (lane >> 4) + r;
+        for (int r = 0; r < 16; ++r) {
+            const int m = m0 + rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
             if (m >= M) continue;
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
@@ -194,19 +264,21 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 const QmmShape kQmmVariants[kNumQmmVariants] = {
-    {128, 4, 4},  // 0: 128 x 256 tile, 4 waves of 128 x 64
-    {128, 2, 4},  // 1: 128 x 128 tile, 4 waves of 128 x 32
-    {64, 2, 4},   // 2:  64 x 128 tile, 4 waves of  64 x 32
+    {128, 1, 4},  // 0: 128 x 128 tile, 4 waves of 128 x 32, two waves per SIMD
+    {64, 1, 4},   // 1:  64 x 128 tile, 4 waves of  64 x 32, three waves per SIMD
+    {64, 2, 4},   // 2:  64 x 256 tile, 4 waves of  64 x 64, two waves per SIMD
+    {128, 2, 4},  // 3: 128 x 256 tile, 4 waves of 128 x 64, one wave per SIMD
+    {256, 1, 4},  // 4: 256 x 128 tile, 4 waves of 256 x 32, one wave per SIMD
 };
 
-template <int BM, int NB, int NW>
+template <int BM, int NB, int NW, int WAVES_PER_SIMD>
 static hipError_t launch_qmm_t(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                                uint16_t* y, float* ws, int M, int N, int K, int split, hipStream_t stream) {
-    constexpr int BN = NW * NB * 16;
+    constexpr int BN = NW * NB * 32;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const dim3 grid(tiles_m * tiles_n * split);
-    hipLaunchKernelGGL((qmm_kernel<BM, NB, NW>), grid, dim3(64 * NW), 0, stream, x, wq, s, b, y, ws, M, N, K, split,
+    hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WAVES_PER_SIMD>), grid, dim3(64 * NW), 0, stream, x, wq, s, b, y, ws, M, N, K, split,
                        tiles_m, tiles_n);
     return hipGetLastError();
 }
@@ -215,9 +287,11 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint32_t* wq, const 
                       const uint16_t* biases, uint16_t* y, float* ws, int M, int N, int K, int split,
                       hipStream_t stream) {
     switch (variant) {
-        case 0: return launch_qmm_t<128, 4, 4>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 1: return launch_qmm_t<128, 2, 4>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 2: return launch_qmm_t<64, 2, 4>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 0: return launch_qmm_t<128, 1, 4, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 1: return launch_qmm_t<64, 1, 4, 3>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 2: return launch_qmm_t<64, 2, 4, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 3: return launch_qmm_t<128, 2, 4, 1>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 4: return launch_qmm_t<256, 1, 4, 1>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
         default: return hipErrorInvalidValue;
     }
 }
