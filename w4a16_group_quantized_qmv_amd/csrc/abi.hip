@@ -57,20 +57,12 @@ int check_buffers(const uint16_t* x, const uint32_t* wq, const uint16_t* s, cons
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
-    const int64_t G = K / W4A16_GROUP;
-    const int64_t col_blocks = ceil_div(N, 16);
-    int variant;
-    const QmvShape& wide = kQmvVariants[0];
-    if (ceil_div(N, int64_t{wide.cb} * wide.wn * 16) >= cus) {
-        variant = 0;  // enough workgroups without splitting K inside a workgroup
-    } else {
-        // narrow: 16 columns per workgroup, kw waves share K; aim at one wave per SIMD (4 per CU)
-        // while leaving every wave at least two groups
-        const int64_t want = 4 * static_cast<int64_t>(cus);
-        variant = 1;  // kw = 4
-        if (col_blocks * 4 < want && G >= 16) variant = 2;   // kw = 8
-        if (col_blocks * 8 < want && G >= 32) variant = 3;   // kw = 16
-    }
+    // Measured on MI355X: for wide outputs (the 151936-column vocabulary head) 32 columns per
+    // wave and four waves side by side stream best; narrower projections need the parallelism of
+    // 16-column workgroups whose four waves split K.
+    const QmvShape& wide = kQmvVariants[1];
+    const int variant = ceil_div(N, int64_t{wide.cb} * wide.wn * 16) >= 2 * static_cast<int64_t>(cus) ? 1 : 2;
+    (void)K;
     const QmvShape& v = kQmvVariants[variant];
     p->path = W4A16_PATH_QMV;
     p->tile_m = 16;

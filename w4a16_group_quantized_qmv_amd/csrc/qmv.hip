@@ -12,105 +12,193 @@
 // which is sum_{k in g} x[m,k] * (s q + b) regrouped.  The codes enter the MFMA as exact bf16
 // integers (see codes_bf16_permuted), so no weight is rounded before the contraction.
 //
-// Memory: the weights stream once from HBM with 16-byte loads; lane group h = l / 16 of a wave
-// reads 64 contiguous bytes (one 128-value group) of 16 consecutive columns.  Activations are
-// re-read from L2 (they are at most 16 x K bf16).  A workgroup is wn x kw waves: wn waves side
-// by side along N, kw waves splitting the groups of the same columns; the kw partial sums are
-// added in wave order through LDS, so the result does not depend on timing.
+// Memory (the kernel is bound by HBM bandwidth):
+//  * Weights stream once, through the gfx950 direct global-to-LDS buffer loads: no registers
+//    and no VALU work per loaded byte.  One load instruction moves 8 columns x 128 contiguous
+//    bytes (the two groups of a group pair), so every request is a whole 128-byte line; loads
+//    of 16 columns x 64 bytes measured about 20% slower on MI355X.
+//  * The destination slot of each 16-byte chunk is permuted so that the MFMA operand read --
+//    16 lanes, one per column, same group and same 32-value quarter -- touches 16 different
+//    bank groups (conflict free).  Reads past the last column hit the buffer bound and return
+//    zeros; those columns are never stored.
+//  * Each wave owns a private double-buffered LDS region: the next group pair streams in while
+//    the current one is computed, with no workgroup barrier.
+//  * Activations, scales and biases are small and L2-resident; they are prefetched one group
+//    pair ahead in registers.
+// A workgroup is wn x kw waves: wn waves side by side along N, kw waves splitting the group
+// pairs of the same columns; the kw partial sums are added in wave order through LDS, so the
+// result does not depend on timing.
 #include "device_common.h"
 #include "internal.h"
 
 namespace w4a16 {
 
+namespace {
+
+constexpr int kPairBytes = 2048;   // one 16-column block x one group pair of packed codes
+
+// LDS byte offset (within a block's 2 KB) of the 16-byte chunk h of column c, group g (0/1):
+// columns 0..7 fill the first kilobyte, columns 8..15 the second, and within each kilobyte the
+// slot is 16 * h + (c % 8) + 8 * (g or 1 - g) so that c = 0..15 at fixed (g, h) cover all
+// sixteen 16-byte bank groups.
+__device__ __forceinline__ int pair_slot(int c, int g, int h) {
+    return c < 8 ? 16 * (16 * h + c + 8 * g) : 1024 + 16 * (16 * h + (c - 8) + 8 * (1 - g));
+}
+
+}  // namespace
+
 template <int CB, int WN, int KW>
 __global__ __launch_bounds__(64 * WN * KW) void qmv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int N, int K) {
+    // two separate LDS objects (not one array indexed by buffer): the compiler's wait
+    // insertion can then tell that a direct load into one buffer does not feed reads of the other
+    __shared__ __attribute__((aligned(16))) uint8_t wbuf0[WN * KW][CB * kPairBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t wbuf1[WN * KW][CB * kPairBytes];
+
     const int G = K >> 7;
-    const int words_per_row = K >> 3;
+    const int pairs = (G + 1) >> 1;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keeps resources in SGPRs
     const int wn = wave % WN;
     const int wk = wave / WN;
     const int col0 = (blockIdx.x * WN + wn) * (CB * 16);
-    const int g0 = static_cast<int>(static_cast<int64_t>(wk) * G / KW);
-    const int g1 = static_cast<int>(static_cast<int64_t>(wk + 1) * G / KW);
-    const int arow = lane & 15;   // activation row fed by this lane (A operand)
+    const int p0 = static_cast<int>(static_cast<int64_t>(wk) * pairs / KW);
+    const int p1 = static_cast<int>(static_cast<int64_t>(wk + 1) * pairs / KW);
+    const int c = lane & 15;      // column within a 16-column block (B operand / D layout)
     const int kq = lane >> 4;     // 32-value quarter of each group held by this lane
+    const int arow = lane & 15;   // activation row fed by this lane (A operand)
     const bool arow_ok = arow < M;
+    const int row_bytes = K >> 1;
+
+    // weight stream: buffer resource based at this wave's first column; reads past the last
+    // column fall outside the resource and return zeros
+    const uint8_t* wbase = reinterpret_cast<const uint8_t*>(wq) + static_cast<size_t>(col0) * row_bytes;
+    const int64_t wbytes = col0 < N ? static_cast<int64_t>(N - col0) * row_bytes : 0;
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(wbase), 0, static_cast<int>(wbytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : wbytes), 0x00020000);
+    // load lane l fills slot l of each kilobyte: invert pair_slot for its column / group / chunk
+    const int lh = lane >> 4, lr = lane & 15;
+    const uint32_t voff_lo = static_cast<uint32_t>((lr & 7) * row_bytes + (lr >> 3) * 64 + lh * 16);
+    const uint32_t voff_hi = static_cast<uint32_t>((8 + (lr & 7)) * row_bytes + (1 - (lr >> 3)) * 64 + lh * 16);
+    auto stage_w = [&](int pair, int buf) {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            uint8_t* dst = (buf ? &wbuf1[wave][0] : &wbuf0[wave][0]) + cb * kPairBytes;
+            const uint32_t soff = static_cast<uint32_t>(pair) * 128u + static_cast<uint32_t>(cb * 16 * row_bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst, 16, voff_lo, soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst + 1024, 16, voff_hi, soff, 0, 0);
+        }
+    };
+    const int rd0 = pair_slot(c, 0, kq), rd1 = pair_slot(c, 1, kq);
 
     int col[CB];
     bool col_ok[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-        col[cb] = col0 + cb * 16 + (lane & 15);
+        col[cb] = col0 + cb * 16 + c;
         col_ok[cb] = col[cb] < N;
     }
-    const uint16_t* xrow = x + static_cast<size_t>(arow_ok ? arow : 0) * K + kq * 32;
 
-    f32x4_t yacc[CB];
+    // small operands of one group pair -- activations (2 groups x 4 x 16 B), scales, biases --
+    // through buffer loads: rows >= M and columns >= N read as zeros, and every pair issues the
+    // same number of loads (the LDS waits below count them)
+    auto clamp_records = [](int64_t bytes) { return static_cast<int>(bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes); };
+    const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x), 0, clamp_records(static_cast<int64_t>(M) * K * 2), 0x00020000);
+    // scales / biases: resources based at this wave's first column (offsets stay small)
+    const int sb_records = clamp_records(col0 < N ? static_cast<int64_t>(N - col0) * G * 2 : 0);
+    const size_t sb_base = static_cast<size_t>(col0) * G;
+    const __amdgpu_buffer_rsrc_t srsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales + sb_base), 0, sb_records, 0x00020000);
+    const __amdgpu_buffer_rsrc_t brsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(biases + sb_base), 0, sb_records, 0x00020000);
+    const uint32_t xvoff = arow_ok ? static_cast<uint32_t>(arow * K + kq * 32) * 2u : 0x80000000u;
+    uint32_t sboff[CB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) yacc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < CB; ++cb) sboff[cb] = col_ok[cb] ? static_cast<uint32_t>((cb * 16 + c) * G * 2) : 0x80000000u;
+    constexpr int kLoadsPerPair = 2 * CB + 8 + 4 * CB;   // direct + activation + scale/bias loads
 
-    u32x4_t wcur[CB], wnxt[CB], xcur[4], xnxt[4];
-    uint16_t scur[CB], bcur[CB], snxt[CB], bnxt[CB];
-
-    auto load_group = [&](int g, u32x4_t* wv, u32x4_t* xv, uint16_t* sv, uint16_t* bv) {
+    struct Small {
+        u32x4_t xv[2][4];
+        uint16_t s[2][CB], b[2][CB];
+    };
+    auto load_small = [&](int pair, Small& o) {
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            if (col_ok[cb]) {
-                const size_t row = static_cast<size_t>(col[cb]);
-                wv[cb] = load16(wq + row * words_per_row + g * kWordsPerGroup + kq * 4);
-                sv[cb] = scales[row * G + g];
-                bv[cb] = biases[row * G + g];
-            } else {
-                wv[cb] = u32x4_t{0u, 0u, 0u, 0u};
-                sv[cb] = 0;
-                bv[cb] = 0;
+        for (int g2 = 0; g2 < 2; ++g2) {
+            const int g = 2 * pair + g2;   // past the last group only for an odd count; unused then
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                o.xv[g2][t] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xvoff, (g * kGroup + t * 8) * 2, 0));
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                // the empty asm statements keep each load a separate instruction (no merging),
+                // so the per-pair load count used by the LDS waits is exact
+                o.s[g2][cb] = __builtin_amdgcn_raw_buffer_load_b16(srsrc, sboff[cb], g * 2, 0);
+                asm volatile("" ::: "memory");
+                o.b[g2][cb] = __builtin_amdgcn_raw_buffer_load_b16(brsrc, sboff[cb], g * 2, 0);
+                asm volatile("" ::: "memory");
             }
         }
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            xv[t] = arow_ok ? load16(xrow + g * kGroup + t * 8) : u32x4_t{0u, 0u, 0u, 0u};
     };
 
     const bf16x8_t ones = {__bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f),
                            __bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f)};
     const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t yacc[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) yacc[cb] = zero4;
 
-    if (g0 < g1) load_group(g0, wcur, xcur, scur, bcur);
-    for (int g = g0; g < g1; ++g) {
-        if (g + 1 < g1) load_group(g + 1, wnxt, xnxt, snxt, bnxt);
-
-        bf16x8_t a[4];
+    auto compute = [&](int pair, int buf, const Small& o) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) a[t] = permute_like_codes(xcur[t]);
-        // X[m] = sum of the group's activations of row m, by the matrix core (B = ones)
-        f32x4_t xs = mfma16x16x32(a[0], ones, zero4);
+        for (int g2 = 0; g2 < 2; ++g2) {
+            if (2 * pair + g2 >= G) break;  // odd group count: the last pair has one group
+            bf16x8_t a[4];
 #pragma unroll
-        for (int t = 1; t < 4; ++t) xs = mfma16x16x32(a[t], ones, xs);
-
+            for (int t = 0; t < 4; ++t) a[t] = permute_like_codes(o.xv[g2][t]);
+            // X[m] = sum of the group's activations of row m, by the matrix core (B = ones)
+            f32x4_t xs = mfma16x16x32(a[0], ones, zero4);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            f32x4_t p = mfma16x16x32(a[0], codes_bf16_permuted(wcur[cb][0]), zero4);
-#pragma unroll
-            for (int t = 1; t < 4; ++t) p = mfma16x16x32(a[t], codes_bf16_permuted(wcur[cb][t]), p);
-            const float s = bf16_bits_to_f32(scur[cb]);
-            const float b = bf16_bits_to_f32(bcur[cb]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) yacc[cb][r] = __builtin_fmaf(s, p[r], __builtin_fmaf(b, xs[r], yacc[cb][r]));
-        }
-
-        if (g + 1 < g1) {
+            for (int t = 1; t < 4; ++t) xs = mfma16x16x32(a[t], ones, xs);
+            const int rd = g2 == 0 ? rd0 : rd1;
 #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
-                wcur[cb] = wnxt[cb];
-                scur[cb] = snxt[cb];
-                bcur[cb] = bnxt[cb];
-            }
+                const uint8_t* src = (buf ? &wbuf1[wave][0] : &wbuf0[wave][0]) + cb * kPairBytes + rd;
+                const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(src);
+                f32x4_t p = mfma16x16x32(a[0], codes_bf16_permuted(wv[0]), zero4);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) xcur[t] = xnxt[t];
+                for (int t = 1; t < 4; ++t) p = mfma16x16x32(a[t], codes_bf16_permuted(wv[t]), p);
+                const float s = bf16_bits_to_f32(o.s[g2][cb]);
+                const float b = bf16_bits_to_f32(o.b[g2][cb]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yacc[cb][r] = __builtin_fmaf(s, p[r], __builtin_fmaf(b, xs[r], yacc[cb][r]));
+            }
         }
+    };
+
+    // One group pair per step, two steps per iteration with ping-pong buffers (registers and
+    // LDS), so no operand is ever copied.  The next pair's loads are always issued (the last
+    // step re-reads its own pair into the idle buffer): every step has the same load count and
+    // the wait before each compute is exact -- it retires the loads of the pair computed now
+    // while the next pair stays in flight.
+    if (p0 < p1) {
+        Small sa, sb;
+        stage_w(p0, 0);
+        load_small(p0, sa);
+        for (int p = p0;; p += 2) {
+            stage_w(p + 1 < p1 ? p + 1 : p, 1);
+            load_small(p + 1 < p1 ? p + 1 : p, sb);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerPair) : "memory");
+            compute(p, 0, sa);
+            if (p + 1 >= p1) break;
+            stage_w(p + 2 < p1 ? p + 2 : p + 1, 0);
+            load_small(p + 2 < p1 ? p + 2 : p + 1, sa);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerPair) : "memory");
+            compute(p + 1, 1, sb);
+            if (p + 2 >= p1) break;
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no direct load may outlive the wave
     }
 
     if constexpr (KW > 1) {
@@ -146,11 +234,11 @@ __global__ __launch_bounds__(64 * WN * KW) void qmv_kernel(
 }
 
 const QmvShape kQmvVariants[kNumQmvVariants] = {
-    {4, 4, 1},   // 0: wide N, one wave per 64 columns, no K split
-    {1, 1, 4},   // 1: 16 columns per workgroup, 4 waves split K
-    {1, 1, 8},   // 2: 16 columns per workgroup, 8 waves split K
-    {1, 1, 16},  // 3: 16 columns per workgroup, 16 waves split K
-    {2, 2, 2},   // 4: 64 columns per workgroup, 2 waves split K
+    {4, 4, 1},   // 0: wide N: 64 columns per wave, no K split
+    {2, 4, 1},   // 1: wide N: 32 columns per wave, no K split
+    {1, 1, 4},   // 2: 16 columns per workgroup, 4 waves split K
+    {1, 1, 8},   // 3: 16 columns per workgroup, 8 waves split K
+    {2, 2, 4},   // 4: 64 columns per workgroup, 4 waves split K
 };
 
 template <int CB, int WN, int KW>
@@ -166,10 +254,10 @@ hipError_t launch_qmv(int variant, const uint16_t* x, const uint32_t* wq, const 
                       const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream) {
     switch (variant) {
         case 0: return launch_qmv_t<4, 4, 1>(x, wq, scales, biases, y, M, N, K, stream);
-        case 1: return launch_qmv_t<1, 1, 4>(x, wq, scales, biases, y, M, N, K, stream);
-        case 2: return launch_qmv_t<1, 1, 8>(x, wq, scales, biases, y, M, N, K, stream);
-        case 3: return launch_qmv_t<1, 1, 16>(x, wq, scales, biases, y, M, N, K, stream);
-        case 4: return launch_qmv_t<2, 2, 2>(x, wq, scales, biases, y, M, N, K, stream);
+        case 1: return launch_qmv_t<2, 4, 1>(x, wq, scales, biases, y, M, N, K, stream);
+        case 2: return launch_qmv_t<1, 1, 4>(x, wq, scales, biases, y, M, N, K, stream);
+        case 3: return launch_qmv_t<1, 1, 8>(x, wq, scales, biases, y, M, N, K, stream);
+        case 4: return launch_qmv_t<2, 2, 4>(x, wq, scales, biases, y, M, N, K, stream);
         default: return hipErrorInvalidValue;
     }
 }
