@@ -28,8 +28,8 @@
  * a fault during execution surfaces when the caller synchronizes the stream.
  *
  * Preconditions checked on the host (a violation returns an error status, never launches):
- *   M, N, K >= 1;  K % 128 == 0;  group == 128;  x, wq, workspace 16-byte aligned;
- *   scales, biases, y 2-byte aligned.
+ *   1 <= M, N <= 2^31 - 1;  1 <= K <= 2^20;  K % 128 == 0;  group == 128;
+ *   x, wq, workspace 16-byte aligned;  scales, biases, y 2-byte aligned.
  *
  * Errors are returned as status codes (never exceptions); w4a16_status_string() names them.
  * Thread safety: stateless apart from a per-device cache of the compute-unit count.
@@ -50,7 +50,7 @@ extern "C" {
 enum w4a16_status {
     W4A16_OK = 0,
     W4A16_ERR_NULL = 1,        /* a required pointer is NULL                                  */
-    W4A16_ERR_SHAPE = 2,       /* M, N or K < 1, K % 128 != 0, or a size overflows int32 rows */
+    W4A16_ERR_SHAPE = 2,       /* a size outside the limits above, or K % 128 != 0           */
     W4A16_ERR_GROUP = 3,       /* group != 128                                                */
     W4A16_ERR_ALIGN = 4,       /* a pointer violates the alignment stated above               */
     W4A16_ERR_WORKSPACE = 5,   /* a forced split_k > 1 has too little workspace               */

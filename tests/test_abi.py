@@ -58,6 +58,12 @@ def test_forced_paths():
 def test_grid_covers_the_output():
     for M, N, K in [(33, 96, 256), (509, 9728, 2560), (128, 1024, 2560), (4096, 151936, 2560), (1, 151936, 2560)]:
         p = plan(M, N, K)
+        if p["path"] == w4.PATH_QMV and p["grid_x"] * p["tile_n"] < N:
+            # persistent wide matvec: resident workgroups whose waves loop over 16-column blocks
+            waves_per_wg = p["block_threads"] // 64
+            assert p["tile_n"] == 16 and p["k_waves"] == 1
+            assert p["grid_x"] == min(-(-N // (16 * waves_per_wg)), 8 * CUS)
+            continue
         assert p["grid_x"] * p["tile_n"] >= N and (p["grid_x"] - 1) * p["tile_n"] < N
         if p["path"] == w4.PATH_QMM:
             assert p["grid_y"] * p["tile_m"] >= M and (p["grid_y"] - 1) * p["tile_m"] < M
@@ -112,6 +118,7 @@ def test_workspace_bytes_matches_plan():
 @pytest.mark.parametrize("args,err", [
     ((0, 10, 128, 128), ValueError), ((4, 0, 128, 128), ValueError), ((4, 10, 0, 128), ValueError),
     ((4, 10, 100, 128), ValueError), ((4, 10, 256, 64), ValueError), ((4, 10, 2 ** 31, 128), ValueError),
+    ((4, 10, 2 ** 20 + 128, 128), ValueError),
 ])
 def test_plan_rejects_invalid_shapes(args, err):
     with pytest.raises(err):

@@ -80,8 +80,9 @@ def test_identity_unpack_is_bit_exact_qmm(lib, split):
     assert np.array_equal(y, expect), "nibble order / indexing mismatch on the matrix path"
 
 
-def test_identity_unpack_is_bit_exact_qmv(lib):
-    q, p = identity_problem()
+@pytest.mark.parametrize("N", [96, 24600])        # 16-column K-split kernel / persistent wide kernel
+def test_identity_unpack_is_bit_exact_qmv(lib, N):
+    q, p = identity_problem(N=N)
     expect = synth.to_bf16_bits(q.T.astype(np.float32))
     for r0 in range(0, 256, 8):       # one-hot rows, eight at a time
         sub = dict(p, x=p["x"][r0:r0 + 8], M=8)
@@ -89,11 +90,11 @@ def test_identity_unpack_is_bit_exact_qmv(lib):
         assert np.array_equal(y, expect[r0:r0 + 8]), f"rows {r0}..{r0 + 7}"
 
 
-@pytest.mark.parametrize("path", ["qmv", "qmm"])
-def test_small_integer_sums_are_exact(lib, path):
+@pytest.mark.parametrize("path,N", [("qmv", 160), ("qmv", 6150), ("qmv", 8200), ("qmv", 24600), ("qmm", 160)])
+def test_small_integer_sums_are_exact(lib, path, N):
     rng = np.random.default_rng(8)
     M = 8 if path == "qmv" else 40
-    K, N = 512, 160
+    K = 512
     q = rng.integers(0, 16, (N, K))
     xi = np.zeros((M, K), dtype=np.int64)
     for m in range(M):                 # at most 17 ones per row keeps every sum <= 255
@@ -105,11 +106,11 @@ def test_small_integer_sums_are_exact(lib, path):
     assert np.array_equal(y, synth.to_bf16_bits((xi @ q.T).astype(np.float32)))
 
 
-@pytest.mark.parametrize("path", ["qmv", "qmm"])
-def test_power_of_two_affine_is_exact(lib, path):
+@pytest.mark.parametrize("path,N", [("qmv", 48), ("qmv", 24600), ("qmm", 48)])
+def test_power_of_two_affine_is_exact(lib, path, N):
     rng = np.random.default_rng(9)
     M = 8 if path == "qmv" else 24
-    K, N = 384, 48
+    K = 384
     q = rng.integers(0, 16, (N, K))
     xi = np.zeros((M, K), dtype=np.int64)
     for m in range(M):                 # <= 32 entries of +-1: |sum x (q - 8)| <= 256, exact in bf16 / 64
@@ -135,6 +136,33 @@ def test_all_zero_codes(lib, path):
          "biases": synth.to_bf16_bits((0.02 * rng.standard_normal((N, G))).astype(np.float32)),
          "M": M, "N": N, "K": K}
     assert_parity(run(lib, p, path, 1), p)
+
+
+# ---------------------------------------------------------------------------------- qmv families
+
+# (N, K, M, kernel the policy picks): 0 = 16-column workgroups splitting K four ways, 1 = 32-column
+# workgroups, 2 = 64-column workgroups, 3 = persistent wide kernel (activations and their group
+# sums staged in LDS once, one wave per 16-column block)
+QMV_FAMILY_CASES = [
+    (4000, 256, 3, 0),       # ragged N
+    (6150, 384, 1, 1),       # odd group count, ragged N
+    (8200, 384, 8, 2),
+    (24600, 256, 1, 3),      # one group pair per block: every step ends a block
+    (24600, 512, 5, 3),      # ragged N and M
+    (30010, 1024, 8, 3),     # eight rows
+    (24600, 384, 2, 2),      # odd group count: the wide kernel does not apply
+    (9728, 4096, 4, 3),      # wide from 512 blocks once K >= 4096
+    (24600, 9728, 8, 2),     # activations too large for the wide kernel's LDS
+]
+
+
+@pytest.mark.parametrize("N,K,M,variant", QMV_FAMILY_CASES)
+def test_qmv_kernel_families(lib, N, K, M, variant):
+    assert lib.w4a16_plan(M, N, K, 128, lib.PATH_QMV)["variant"] == variant
+    p = synth.random_problem(11, M, N, K)
+    y = run(lib, p, "qmv")
+    assert_parity(y, p)
+    assert np.array_equal(run(lib, p, "qmv"), y), "repeat run differs"
 
 
 @pytest.mark.parametrize("path,split", [("qmv", None), ("qmm", 1), ("qmm", 3)])

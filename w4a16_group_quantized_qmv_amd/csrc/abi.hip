@@ -3,6 +3,7 @@
 // caller's stream; nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <stdint.h>
 
@@ -17,6 +18,9 @@ using namespace w4a16;
 constexpr int64_t kQmvMaxRows = 8;        // decode rows served by qmv ("Week 2 Day 6", Task 1)
 constexpr int kSplitMinGroups = 4;        // fewest groups one split-K slice may own
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+// Largest K: keeps every per-lane buffer offset of the kernels (at most 256 K bytes past a
+// wave's base) inside 32 bits.
+constexpr int64_t kMaxK = int64_t{1} << 20;
 
 std::atomic<int> g_cu_cache[64];
 
@@ -39,7 +43,7 @@ int query_num_cus(int32_t* out) {
 }
 
 int check_shape(int64_t M, int64_t N, int64_t K, int32_t group) {
-    if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return W4A16_ERR_SHAPE;
+    if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxK) return W4A16_ERR_SHAPE;
     if (group != W4A16_GROUP) return W4A16_ERR_GROUP;
     if (K % W4A16_GROUP != 0) return W4A16_ERR_SHAPE;
     return W4A16_OK;
@@ -57,18 +61,34 @@ int check_buffers(const uint16_t* x, const uint32_t* wq, const uint16_t* s, cons
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
-    // Measured on MI355X: for wide outputs (the 151936-column vocabulary head) 32 columns per
-    // wave and four waves side by side stream best; narrower projections need the parallelism of
-    // 16-column workgroups whose four waves split K.
-    const QmvShape& wide = kQmvVariants[1];
-    const int variant = ceil_div(N, int64_t{wide.cb} * wide.wn * 16) >= 2 * static_cast<int64_t>(cus) ? 1 : 2;
-    (void)K;
+    // Measured on MI355X (K = 2560 and 4096, M = 1 and 4): up to 4096 columns the 16-column
+    // workgroups whose four waves split K are fastest; 32-column ones around 6144 columns and
+    // 64-column ones up to about 16k; from 24k columns (or 9728 at K = 4096) the persistent wide
+    // kernel, which streams whole blocks per wave, wins by 1.4x on the 151936-column head.
+    const int64_t blocks16 = ceil_div(N, 16);
+    const int64_t G = K / W4A16_GROUP;
+    int variant;
+    if (qmv_wide_fits(static_cast<int>(M), static_cast<int>(K)) && (blocks16 >= 1536 || (blocks16 >= 512 && G >= 32)))
+        variant = kQmvWideVariant;
+    else if (blocks16 >= 512)
+        variant = 2;
+    else if (blocks16 >= 384)
+        variant = 1;
+    else
+        variant = 0;
     const QmvShape& v = kQmvVariants[variant];
     p->path = W4A16_PATH_QMV;
     p->tile_m = 16;
     p->tile_n = v.cb * v.wn * 16;
     p->tile_k = W4A16_GROUP;
-    p->grid_x = static_cast<int32_t>(ceil_div(N, p->tile_n));
+    if (variant == kQmvWideVariant) {
+        // persistent: at most as many workgroups as are resident at once (the launch asks the
+        // runtime how many fit per compute unit; 8 is the register limit of this instance)
+        p->tile_n = 16;
+        p->grid_x = static_cast<int32_t>(std::min<int64_t>(ceil_div(blocks16, v.wn), int64_t{8} * cus));
+    } else {
+        p->grid_x = static_cast<int32_t>(ceil_div(N, p->tile_n));
+    }
     p->grid_y = 1;
     p->grid_z = 1;
     p->block_threads = 64 * v.wn * v.kw;

@@ -15,8 +15,27 @@ struct QmvShape {
 };
 
 // Kernel instances compiled for qmv (index = plan variant).
-constexpr int kNumQmvVariants = 5;
+constexpr int kNumQmvVariants = 4;
 extern const QmvShape kQmvVariants[kNumQmvVariants];
+
+// The wide (persistent) qmv instance: 16-column blocks, 4-wave workgroups, 2 LDS stages.
+constexpr int kQmvWideVariant = 3;
+constexpr int kQmvWideStages = 2;
+// Its LDS: per wave and stage one 2 KB block of codes plus 512 bytes of scales and biases
+// (with 1 KB allowed for the kernel's small placeholder objects); dynamically the permuted
+// activations (whole 1 KB units of 64 chunks of 16 bytes) and the per-group activation sums
+// (16 fp32 per group).
+constexpr size_t kQmvWideStaticLds = 4 * (2048 + 512) * kQmvWideStages + 1024;
+inline size_t qmv_wide_x_bytes_host(int M, int K) {
+    const size_t chunks = static_cast<size_t>(M) * (K / 8);
+    return (chunks + 63) / 64 * 1024;
+}
+inline size_t qmv_wide_lds_bytes(int M, int K) { return qmv_wide_x_bytes_host(M, K) + static_cast<size_t>(K / 128) * 64; }
+// The wide kernel needs an even group count, at most 16 rows and its LDS within a workgroup's
+// 160 KB.
+inline bool qmv_wide_fits(int M, int K) {
+    return (K / 128) % 2 == 0 && M >= 1 && M <= 16 && kQmvWideStaticLds + qmv_wide_lds_bytes(M, K) <= 160 * 1024;
+}
 
 hipError_t launch_qmv(int variant, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
                       const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream);

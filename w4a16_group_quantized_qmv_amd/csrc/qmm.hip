@@ -107,8 +107,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     // past the last row return zeros and cannot fault.  Instruction i of this wave fills rows
     // 4 * (i * NW + wave) + 0..3; lane l writes chunk position l % 16 of row l / 16 with
     // activation chunk (l % 16) ^ (row & 15).  Row & 15 does not depend on i (rows advance by
-    // 4 * NW = 16 per instruction), so one 32-bit lane offset serves every instruction and the
-    // group / instruction steps go into the scalar offset.
+    // 4 * NW = 16 per instruction), so one lane offset plus a row step serves every
+    // instruction.  The row step stays in the per-lane offset, which the range check always
+    // covers; only the group step (inside a valid row) goes into the scalar offset.
     const uint16_t* xtile = x + static_cast<size_t>(m0) * K;
     const uint64_t tile_bytes = static_cast<uint64_t>(M - m0) * K * 2;
     const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -120,8 +121,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; ++i) {
             uint16_t* dst = xs + buf * TILE + __builtin_amdgcn_readfirstlane(4 * (i * NW + wave) * kGroup);
-            const uint32_t soff = static_cast<uint32_t>(g) * (kGroup * 2) + static_cast<uint32_t>(i) * (4 * NW * 2) * K;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, dst, 16, xvoff, soff, 0, 0);
+            const uint32_t soff = static_cast<uint32_t>(g) * (kGroup * 2);
+            const uint32_t voff = xvoff + static_cast<uint32_t>(i) * (4 * NW * 2) * static_cast<uint32_t>(K);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, dst, 16, voff, soff, 0, 0);
         }
     };
     // weights: lane half h takes words 8h .. 8h + 7 of the group (two 16-byte loads)

@@ -31,11 +31,17 @@
 #include "device_common.h"
 #include "internal.h"
 
+#include <algorithm>
+#include <type_traits>
+
 namespace w4a16 {
 
 namespace {
 
 constexpr int kPairBytes = 2048;   // one 16-column block x one group pair of packed codes
+
+// bytes of permuted activations in the wide kernel's dynamic LDS (whole 1 KB units)
+__device__ __forceinline__ int qmv_wide_x_bytes(int M, int K) { return (M * (K >> 3) + 63) / 64 * 1024; }
 
 // LDS byte offset (within a block's 2 KB) of the 16-byte chunk h of column c, group g (0/1):
 // columns 0..7 fill the first kilobyte, columns 8..15 the second, and within each kilobyte the
@@ -81,13 +87,15 @@ __global__ __launch_bounds__(64 * WN * KW) void qmv_kernel(
     const int lh = lane >> 4, lr = lane & 15;
     const uint32_t voff_lo = static_cast<uint32_t>((lr & 7) * row_bytes + (lr >> 3) * 64 + lh * 16);
     const uint32_t voff_hi = static_cast<uint32_t>((8 + (lr & 7)) * row_bytes + (1 - (lr >> 3)) * 64 + lh * 16);
+    // every byte offset that can cross the last column goes into the per-lane offset, which the
+    // range check always covers; the scalar offset stays zero
     auto stage_w = [&](int pair, int buf) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             uint8_t* dst = (buf ? &wbuf1[wave][0] : &wbuf0[wave][0]) + cb * kPairBytes;
-            const uint32_t soff = static_cast<uint32_t>(pair) * 128u + static_cast<uint32_t>(cb * 16 * row_bytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst, 16, voff_lo, soff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst + 1024, 16, voff_hi, soff, 0, 0);
+            const uint32_t step = static_cast<uint32_t>(pair) * 128u + static_cast<uint32_t>(cb * 16 * row_bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst, 16, voff_lo + step, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst + 1024, 16, voff_hi + step, 0, 0, 0);
         }
     };
     const int rd0 = pair_slot(c, 0, kq), rd1 = pair_slot(c, 1, kq);
@@ -126,7 +134,7 @@ __global__ __launch_bounds__(64 * WN * KW) void qmv_kernel(
     auto load_small = [&](int pair, Small& o) {
 #pragma unroll
         for (int g2 = 0; g2 < 2; ++g2) {
-            const int g = 2 * pair + g2;   // past the last group only for an odd count; unused then
+            const int g = min(2 * pair + g2, G - 1);   // an odd count repeats the last group (unused)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
                 o.xv[g2][t] = __builtin_bit_cast(
@@ -233,12 +241,248 @@ __global__ __launch_bounds__(64 * WN * KW) void qmv_kernel(
     }
 }
 
+// Wide form (many output columns, e.g. the vocabulary head): a persistent grid of
+// workgroups of W waves, as many as fit on the chip at once.
+//  * Prologue, once per workgroup: the activations (all M rows, the whole K) go into LDS already
+//    permuted into the MFMA A-operand order, and the per-group activation sums X[m, g] are
+//    formed once (matrix core, B = ones) and kept in LDS.  The steady state then issues no
+//    activation loads and no MFMA for X.
+//  * Each wave then works alone: it takes the 16*CB-column blocks w, w + total waves, ... and
+//    walks the (block, group pair) steps of all of them in one flat sequence with D LDS stages,
+//    keeping D - 1 steps of loads in flight across block boundaries.
+//  * One step is 2*CB direct loads of weights (whole 128-byte lines) plus one direct 4-byte load
+//    of scales and one of biases (the two groups of a pair are adjacent in memory).
+// A block's sums are stored when its last pair is done.  Needs an even group count.
+template <int CB, int D, int W>
+__global__ __launch_bounds__(64 * W) void qmv_wide_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int N, int K) {
+    static_assert(D >= 2 && D <= 6, "stage count");
+    static_assert(CB >= 1 && CB <= 4, "one scale load serves at most 64 columns");
+    constexpr int kSbOff = CB * kPairBytes;         // scales of the stage, then biases at +256
+    constexpr int kStage = kSbOff + 512;
+    // one LDS object per stage: the compiler's wait insertion can then tell that a direct load
+    // into one stage does not feed reads of another
+    __shared__ __attribute__((aligned(16))) uint8_t st0[W][kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[W][kStage];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[W][D > 2 ? kStage : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[W][D > 3 ? kStage : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st4[W][D > 4 ? kStage : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st5[W][D > 5 ? kStage : 16];
+    // dynamic LDS: permuted activations (qmv_wide_x_bytes), then X[g][16 rows] as fp32
+    extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
+
+    const int G = K >> 7;
+    const int pairs = G >> 1;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row_bytes = K >> 1;
+    const int kq = lane >> 4;
+    const int arow = lane & 15;
+    const bool arow_ok = arow < M;
+    float* const xsum = reinterpret_cast<float*>(xl + qmv_wide_x_bytes(M, K));
+    auto clamp_records = [](int64_t bytes) { return static_cast<int>(bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes); };
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    const u32x4_t zero_u4 = {0u, 0u, 0u, 0u};
+    // the A operand of MFMA step t of group g for this lane (row arow, quarter kq); rows >= M
+    // are zero and never stored.  Chunk ((4 g + t) * 4 + kq) * M + m holds row m.
+    auto read_a = [&](int g, int t) -> u32x4_t {
+        const int chunk = ((4 * g + t) * 4 + kq) * M + arow;
+        return arow_ok ? *reinterpret_cast<const u32x4_t*>(xl + chunk * 16) : zero_u4;
+    };
+
+    // ---- prologue 1: activations into LDS in A-operand order, permuted like the codes
+    {
+        const int chunks = M * (K >> 3);
+        const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(x), 0, clamp_records(static_cast<int64_t>(M) * K * 2), 0x00020000);
+        for (int i = wave; i * 64 < chunks; i += W) {
+            const int d = i * 64 + lane;
+            uint32_t voff = 0x80000000u;            // past the end: out of range, reads zeros
+            if (d < chunks) {
+                const int m = d % M;
+                int r = d / M;
+                const int q = r & 3;
+                r >>= 2;
+                const int t = r & 3;
+                const int g = r >> 2;
+                voff = static_cast<uint32_t>(m * K + g * kGroup + q * 32 + t * 8) * 2u;
+            }
+            const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, voff, 0, 0));
+            *reinterpret_cast<bf16x8_t*>(xl + i * 1024 + lane * 16) = permute_like_codes(v);
+        }
+        __syncthreads();
+    }
+    // ---- prologue 2: X[m, g] = sum of the group's activations of row m, by the matrix core
+    {
+        const bf16x8_t ones = {__bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f),
+                               __bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f)};
+        for (int g = wave; g < G; g += W) {
+            f32x4_t xs = zero4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xs = mfma16x16x32(__builtin_bit_cast(bf16x8_t, read_a(g, t)), ones, xs);
+            // D layout: lane (c, q) holds rows 4q .. 4q + 3, the same for every column c
+            if ((lane & 15) == 0) *reinterpret_cast<f32x4_t*>(xsum + g * 16 + 4 * kq) = xs;
+        }
+        __syncthreads();
+    }
+
+    const int waves = gridDim.x * W;
+    const int gw = blockIdx.x * W + wave;
+    const int blocks = (N + CB * 16 - 1) / (CB * 16);
+    const int my_blocks = gw < blocks ? (blocks - gw + waves - 1) / waves : 0;
+    const int T = my_blocks * pairs;
+    if (T == 0) return;
+
+    const int c = lane & 15;
+    const int lh = lane >> 4, lr = lane & 15;
+    const uint32_t voff_lo = static_cast<uint32_t>((lr & 7) * row_bytes + (lr >> 3) * 64 + lh * 16);
+    const uint32_t voff_hi = static_cast<uint32_t>((8 + (lr & 7)) * row_bytes + (1 - (lr >> 3)) * 64 + lh * 16);
+    const uint32_t sb_voff = lane < 16 * CB ? static_cast<uint32_t>(lane * G * 2) : 0x80000000u;
+    const int rd0 = pair_slot(c, 0, kq), rd1 = pair_slot(c, 1, kq);
+
+    auto stage = [&](auto ic) -> uint8_t* {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i == 0) return &st0[wave][0];
+        else if constexpr (i == 1) return &st1[wave][0];
+        else if constexpr (i == 2) return &st2[wave][0];
+        else if constexpr (i == 3) return &st3[wave][0];
+        else if constexpr (i == 4) return &st4[wave][0];
+        else return &st5[wave][0];
+    };
+
+    // issue side: the next step to load is pair ip of block ib.  The block's buffer resources
+    // are rebuilt when ib changes; past this wave's last block they have zero records, so the
+    // remaining loads fetch nothing but keep the per-step load count the waits rely on.
+    int ib = gw, ip = 0;
+    __amdgpu_buffer_rsrc_t wrsrc, srsrc, brsrc;
+    auto set_block = [&]() {
+        const bool live = ib < blocks;
+        const int col0 = live ? ib * (CB * 16) : 0;
+        const int64_t cols = live ? static_cast<int64_t>(N - col0) : 0;
+        wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + static_cast<size_t>(col0) * row_bytes), 0,
+            clamp_records(cols * row_bytes), 0x00020000);
+        const size_t sb_base = static_cast<size_t>(col0) * G;
+        const int sb_records = clamp_records(cols * G * 2);
+        srsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales + sb_base), 0, sb_records, 0x00020000);
+        brsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(biases + sb_base), 0, sb_records, 0x00020000);
+    };
+    set_block();
+    constexpr int kLoadsPerStep = 2 * CB + 2;
+    auto issue = [&](auto ic) {
+        uint8_t* dst = stage(ic);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const uint32_t step = static_cast<uint32_t>(ip) * 128u + static_cast<uint32_t>(cb * 16 * row_bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst + cb * kPairBytes, 16, voff_lo + step, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst + cb * kPairBytes + 1024, 16, voff_hi + step, 0, 0, 0);
+        }
+        const uint32_t sbo = sb_voff + static_cast<uint32_t>(ip) * 4u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, dst + kSbOff, 4, sbo, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(brsrc, dst + kSbOff + 256, 4, sbo, 0, 0, 0);
+        if (++ip == pairs) {
+            ip = 0;
+            ib += waves;
+            set_block();
+        }
+    };
+
+    f32x4_t yacc[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) yacc[cb] = zero4;
+
+    // compute side: step (block cbk, pair cp)
+    int done = 0, cbk = gw, cp = 0;
+    auto compute = [&](auto ic) {
+        const uint8_t* src = stage(ic);
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+            const int g = 2 * cp + g2;
+            bf16x8_t a[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) a[t] = __builtin_bit_cast(bf16x8_t, read_a(g, t));
+            const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(xsum + g * 16 + 4 * kq);
+            const int rd = g2 == 0 ? rd0 : rd1;
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const u32x4_t wv = *reinterpret_cast<const u32x4_t*>(src + cb * kPairBytes + rd);
+                f32x4_t p = mfma16x16x32(a[0], codes_bf16_permuted(wv[0]), zero4);
+#pragma unroll
+                for (int t = 1; t < 4; ++t) p = mfma16x16x32(a[t], codes_bf16_permuted(wv[t]), p);
+                const int so = kSbOff + 4 * (cb * 16 + c) + 2 * g2;
+                const float s = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(src + so));
+                const float b = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(src + so + 256));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yacc[cb][r] = __builtin_fmaf(s, p[r], __builtin_fmaf(b, xs[r], yacc[cb][r]));
+            }
+        }
+        if (++cp == pairs) {   // block finished: store it, start the next one
+            const int col0 = cbk * (CB * 16);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const int col = col0 + cb * 16 + c;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 4 * kq + r;
+                    if (m < M && col < N) y[static_cast<size_t>(m) * N + col] = f32_to_bf16_bits(yacc[cb][r]);
+                }
+                yacc[cb] = zero4;
+            }
+            cp = 0;
+            cbk += waves;
+        }
+        ++done;
+    };
+
+    // D-stage pipeline over steps t = -(D - 1), ..., T - 1: position d of the D-fold unrolled
+    // body loads step t + D - 1 into stage d, waits until only the newest D - 1 steps of loads
+    // are outstanding (so step t has landed) and computes step t from stage (d + 1) % D.  The
+    // stage being loaded was computed one position earlier; its LDS reads have all returned
+    // (their values fed the MFMAs).  The first D - 1 positions only load.  Keeping the fill
+    // inside the loop (no peeled prologue) lets the compiler see that each stage's reads
+    // depend on that stage's loads alone.
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    using C0 = std::integral_constant<int, 1 % D>;
+    using C1 = std::integral_constant<int, 2 % D>;
+    using C2 = std::integral_constant<int, 3 % D>;
+    using C3 = std::integral_constant<int, 4 % D>;
+    using C4 = std::integral_constant<int, 5 % D>;
+    using C5 = std::integral_constant<int, 6 % D>;
+    int t = -(D - 1);
+    asm volatile("" : "+s"(t));   // opaque start: the fill iterations are not peeled off the loop
+#define W4A16_WIDE_STEP(d, I, C)                                                          \
+    if constexpr (D > d) {                                                                \
+        issue(I{});                                                                       \
+        if (t >= 0) {                                                                     \
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((D - 1) * kLoadsPerStep) : "memory"); \
+            compute(C{});                                                                 \
+            if (done >= T) break;                                                         \
+        }                                                                                 \
+        ++t;                                                                              \
+    }
+    for (;;) {
+        W4A16_WIDE_STEP(0, I0, C0)
+        W4A16_WIDE_STEP(1, I1, C1)
+        W4A16_WIDE_STEP(2, I2, C2)
+        W4A16_WIDE_STEP(3, I3, C3)
+        W4A16_WIDE_STEP(4, I4, C4)
+        W4A16_WIDE_STEP(5, I5, C5)
+    }
+#undef W4A16_WIDE_STEP
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no direct load may outlive the wave
+}
+
 const QmvShape kQmvVariants[kNumQmvVariants] = {
-    {4, 4, 1},   // 0: wide N: 64 columns per wave, no K split
-    {2, 4, 1},   // 1: wide N: 32 columns per wave, no K split
-    {1, 1, 4},   // 2: 16 columns per workgroup, 4 waves split K
-    {1, 1, 8},   // 3: 16 columns per workgroup, 8 waves split K
-    {2, 2, 4},   // 4: 64 columns per workgroup, 4 waves split K
+    {1, 1, 4},   // 0: 16 columns per workgroup, 4 waves split K
+    {1, 2, 2},   // 1: 32 columns per workgroup, 2 waves split K
+    {2, 2, 2},   // 2: 64 columns per workgroup, 2 waves split K
+    {1, 4, 1},   // 3: wide: persistent, 16-column blocks, 4-wave workgroups, 2 LDS stages
 };
 
 template <int CB, int WN, int KW>
@@ -250,14 +494,37 @@ static hipError_t launch_qmv_t(const uint16_t* x, const uint32_t* wq, const uint
     return hipGetLastError();
 }
 
+template <int CB, int D, int W>
+static hipError_t launch_qmv_wide_t(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                                    uint16_t* y, int M, int N, int K, hipStream_t stream) {
+    static_assert(CB == 1 && W == 4 && D == kQmvWideStages, "qmv_wide_fits describes this instance");
+    if (!qmv_wide_fits(M, K)) return hipErrorInvalidValue;
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int blocks = (N + CB * 16 - 1) / (CB * 16);
+    const size_t xbytes = qmv_wide_lds_bytes(M, K);
+    auto kern = qmv_wide_kernel<CB, D, W>;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(xbytes));
+    if (e != hipSuccess) return e;
+    int per_cu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * W, xbytes);
+    if (e != hipSuccess) return e;
+    const int wgs = std::min(std::max(per_cu, 1) * cus, (blocks + W - 1) / W);
+    hipLaunchKernelGGL(kern, dim3(wgs), dim3(64 * W), xbytes, stream, x, wq, s, b, y, M, N, K);
+    return hipGetLastError();
+}
+
 hipError_t launch_qmv(int variant, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
                       const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream) {
     switch (variant) {
-        case 0: return launch_qmv_t<4, 4, 1>(x, wq, scales, biases, y, M, N, K, stream);
-        case 1: return launch_qmv_t<2, 4, 1>(x, wq, scales, biases, y, M, N, K, stream);
-        case 2: return launch_qmv_t<1, 1, 4>(x, wq, scales, biases, y, M, N, K, stream);
-        case 3: return launch_qmv_t<1, 1, 8>(x, wq, scales, biases, y, M, N, K, stream);
-        case 4: return launch_qmv_t<2, 2, 4>(x, wq, scales, biases, y, M, N, K, stream);
+        case 0: return launch_qmv_t<1, 1, 4>(x, wq, scales, biases, y, M, N, K, stream);
+        case 1: return launch_qmv_t<1, 2, 2>(x, wq, scales, biases, y, M, N, K, stream);
+        case 2: return launch_qmv_t<2, 2, 2>(x, wq, scales, biases, y, M, N, K, stream);
+        case kQmvWideVariant: return launch_qmv_wide_t<1, kQmvWideStages, 4>(x, wq, scales, biases, y, M, N, K, stream);
         default: return hipErrorInvalidValue;
     }
 }
