@@ -114,9 +114,12 @@ void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a
     const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, tile_n);
     int64_t S = 1;
     if (split_k == 0) {
-        // split only an under-filled grid, and only when every slice keeps several groups
+        // split only an under-filled grid, and only when every slice keeps several groups.
+        // Measured on MI355X (M = 128 and 512 for the 2560-wide layer's projections): one slice
+        // more than just filling the compute units wins for the K/V, O and down projections
+        // (e.g. S = 3 for 160 tiles), because a compute unit holds several workgroups.
         if (tiles < cus && G >= 2 * kSplitMinGroups) {
-            S = ceil_div(cus, tiles);
+            S = ceil_div(cus, tiles) + 1;
             if (S > G / kSplitMinGroups) S = G / kSplitMinGroups;
             if (S < 2) S = 1;
         }

@@ -46,9 +46,10 @@ struct QmmShape {
     int bm;
     int nb;
     int nwaves;
+    int stages;   // groups in flight: LDS activation tiles and weight register sets
 };
 
-constexpr int kNumQmmVariants = 5;
+constexpr int kNumQmmVariants = 3;
 extern const QmmShape kQmmVariants[kNumQmmVariants];
 
 // split == 1 writes bf16 y; split > 1 writes fp32 partials ws[z][M][N] for z < split.

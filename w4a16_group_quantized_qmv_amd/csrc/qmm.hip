@@ -45,6 +45,8 @@
 #include "device_common.h"
 #include "internal.h"
 
+#include <type_traits>
+
 namespace w4a16 {
 
 constexpr int kBandM = 8;               // M-tiles per band of the tile order
@@ -67,7 +69,7 @@ __device__ __forceinline__ void band_order(int tile, int tiles_m, int tiles_n, i
     tn = in_band / rows;
 }
 
-template <int BM, int NB, int NW, int WAVES_PER_SIMD>
+template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD))) void qmm_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N, int K,
@@ -78,7 +80,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     constexpr int DMA_PER_WAVE = BM / (4 * NW);   // 1 KB direct loads per wave per group
     static_assert(BM % (4 * NW) == 0 && BM % 32 == 0, "tile shape");
     static_assert(NW == 4, "row & 15 of a direct load must not depend on the instruction index");
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2 * TILE];
+    static_assert(STAGES >= 2 && STAGES <= 3, "stage count");
+    // one LDS object per stage: the compiler's wait insertion can then tell that a direct load
+    // into one stage does not feed fragment reads of another
+    __shared__ __attribute__((aligned(16))) uint16_t xs0[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t xs1[TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t xs2[STAGES > 2 ? TILE : 8];
 
     const int tiles = tiles_m * tiles_n;
     const int work = xcd_remap(blockIdx.x, tiles * split);
@@ -87,65 +94,96 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     band_order(work - z * tiles, tiles_m, tiles_n, tm, tn);
 
     const int G = K >> 7;
-    const int words_per_row = K >> 3;
+    const int row_bytes = K >> 1;
     const int g_begin = static_cast<int>(static_cast<int64_t>(z) * G / split);
     const int g_end = static_cast<int>(static_cast<int64_t>(z + 1) * G / split);
+    const int groups = g_end - g_begin;
     const int m0 = tm * BM;
+    const int n0 = tn * BN;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = lane >> 5;
+    auto clamp_records = [](int64_t bytes) { return static_cast<int>(bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes); };
+    auto stage = [&](auto ic) -> uint16_t* {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i == 0) return xs0;
+        else if constexpr (i == 1) return xs1;
+        else return xs2;
+    };
 
-    int col[NB];
-    bool col_ok[NB];
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-        col[cb] = tn * BN + (wave * NB + cb) * 32 + (lane & 31);
-        col_ok[cb] = col[cb] < N;
-    }
-
-    // direct activation loads through a buffer resource based at the tile's first row: reads
-    // past the last row return zeros and cannot fault.  Instruction i of this wave fills rows
-    // 4 * (i * NW + wave) + 0..3; lane l writes chunk position l % 16 of row l / 16 with
+    // Every load goes through a buffer resource.  Loads for groups past this slice use
+    // resources with zero records: they fetch nothing, write zeros, and keep the per-group load
+    // count that the waits rely on.  Reads past the last row or column are out of range and
+    // return zeros; only byte offsets inside a valid row go into scalar offsets.
+    //
+    // Activations: resource based at the tile's first row.  Instruction i of this wave fills
+    // rows 4 * (i * NW + wave) + 0..3; lane l writes chunk position l % 16 of row l / 16 with
     // activation chunk (l % 16) ^ (row & 15).  Row & 15 does not depend on i (rows advance by
-    // 4 * NW = 16 per instruction), so one lane offset plus a row step serves every
-    // instruction.  The row step stays in the per-lane offset, which the range check always
-    // covers; only the group step (inside a valid row) goes into the scalar offset.
-    const uint16_t* xtile = x + static_cast<size_t>(m0) * K;
-    const uint64_t tile_bytes = static_cast<uint64_t>(M - m0) * K * 2;
+    // 4 * NW = 16 per instruction), so one lane offset plus a row step serves every instruction.
     const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(xtile), 0, static_cast<int>(tile_bytes > 0x7FFFFFFFull ? 0x7FFFFFFFull : tile_bytes),
-        0x00020000);
+        const_cast<uint16_t*>(x + static_cast<size_t>(m0) * K), 0,
+        clamp_records(static_cast<int64_t>(M - m0) * K * 2), 0x00020000);
     const int xrow0 = 4 * wave + (lane >> 4);
     const uint32_t xvoff = static_cast<uint32_t>(xrow0 * K + (((lane & 15) ^ (xrow0 & 15)) << 3)) * 2u;
-    auto stage_x = [&](int g, int buf) {
+    // Weights, scales, biases: resources based at the workgroup's first column.  Lane half h of
+    // column block cb takes words 8h .. 8h + 7 of its column's group (two 16-byte loads).
+    const int64_t cols_left = static_cast<int64_t>(N - n0);
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + static_cast<size_t>(n0) * row_bytes), 0,
+        clamp_records(cols_left * row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(scales + static_cast<size_t>(n0) * G), 0, clamp_records(cols_left * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(biases + static_cast<size_t>(n0) * G), 0, clamp_records(cols_left * G * 2), 0x00020000);
+    auto dead = [&](__amdgpu_buffer_rsrc_t r) {
+        (void)r;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, 0, 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t none = dead(xrsrc);
+    uint32_t wvoff[NB], sbvoff[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        const int c = (wave * NB + cb) * 32 + (lane & 31);     // column within the tile
+        wvoff[cb] = static_cast<uint32_t>(c * row_bytes + half * 32);
+        sbvoff[cb] = static_cast<uint32_t>(c * G * 2);
+    }
+
+    struct Slot {
+        u32x4_t w[NB][2];
+        uint16_t s[NB], b[NB];
+    };
+    constexpr int kLoadsPerGroup = DMA_PER_WAVE + 4 * NB;
+    // all loads of group g (relative index j = g - g_begin) into stage / slot ic
+    auto issue = [&](int j, auto ic, Slot& o) {
+        const bool live = j < groups;
+        const int g = g_begin + (live ? j : 0);
+        const __amdgpu_buffer_rsrc_t xr = live ? xrsrc : none;
+        const __amdgpu_buffer_rsrc_t wr = live ? wrsrc : none;
+        const __amdgpu_buffer_rsrc_t sr = live ? srsrc : none;
+        const __amdgpu_buffer_rsrc_t br = live ? brsrc : none;
+        uint16_t* xt = stage(ic);
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; ++i) {
-            uint16_t* dst = xs + buf * TILE + __builtin_amdgcn_readfirstlane(4 * (i * NW + wave) * kGroup);
-            const uint32_t soff = static_cast<uint32_t>(g) * (kGroup * 2);
+            uint16_t* dst = xt + __builtin_amdgcn_readfirstlane(4 * (i * NW + wave) * kGroup);
             const uint32_t voff = xvoff + static_cast<uint32_t>(i) * (4 * NW * 2) * static_cast<uint32_t>(K);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xrsrc, dst, 16, voff, soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, voff, static_cast<uint32_t>(g) * (kGroup * 2), 0, 0);
         }
-    };
-    // weights: lane half h takes words 8h .. 8h + 7 of the group (two 16-byte loads)
-    auto load_w = [&](int g, u32x4_t (*wv)[2], uint16_t* sv, uint16_t* bv) {
+        // the empty asm statements keep every load a separate instruction, so the per-group
+        // count used by the waits is exact
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
-            if (col_ok[cb]) {
-                const size_t row = static_cast<size_t>(col[cb]);
-                const uint32_t* src = wq + row * words_per_row + g * kWordsPerGroup + half * 8;
-                wv[cb][0] = load16(src);
-                wv[cb][1] = load16(src + 4);
-                sv[cb] = scales[row * G + g];
-                bv[cb] = biases[row * G + g];
-            } else {
-                wv[cb][0] = u32x4_t{0u, 0u, 0u, 0u};
-                wv[cb][1] = u32x4_t{0u, 0u, 0u, 0u};
-                sv[cb] = 0;
-                bv[cb] = 0;
-            }
+            o.w[cb][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff[cb], g * 64, 0));
+            asm volatile("" ::: "memory");
+            o.w[cb][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff[cb], g * 64 + 16, 0));
+            asm volatile("" ::: "memory");
+            o.s[cb] = __builtin_amdgcn_raw_buffer_load_b16(sr, sbvoff[cb], g * 2, 0);
+            asm volatile("" ::: "memory");
+            o.b[cb] = __builtin_amdgcn_raw_buffer_load_b16(br, sbvoff[cb], g * 2, 0);
+            asm volatile("" ::: "memory");
         }
     };
-    // LDS element offset of the A fragment of sub-step t for this lane (row block 0, buffer 0):
+
+    // LDS element offset of the A fragment of sub-step t for this lane (row block 0):
     // row r = lane % 32, chunk 8 * half + t stored at position (8 * half + t) ^ (r & 15)
     // = 8 * (half ^ (r >> 3 & 1)) + (t ^ (r & 7)); with the row part a multiple of 128 this is
     // one lane constant XOR (t << 3).
@@ -164,19 +202,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     // the MFMAs of sub-step t run, the fragment reads and the dequantization of sub-step t + 1
     // are already issued.  The scheduling barrier at the end of each sub-step bounds the live
     // registers to two sub-steps' operands.
-    auto compute = [&](int buf, const u32x4_t (*wv)[2], const uint16_t* sv, const uint16_t* bv) {
+    auto compute = [&](auto ic, const Slot& o) {
         float s[NB], b[NB];
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
-            s[cb] = bf16_bits_to_f32(sv[cb]);
-            b[cb] = bf16_bits_to_f32(bv[cb]);
+            s[cb] = bf16_bits_to_f32(o.s[cb]);
+            b[cb] = bf16_bits_to_f32(o.b[cb]);
         }
-        const uint16_t* xt = xs + buf * TILE;
+        const uint16_t* xt = stage(ic);
         bf16x8_t a[2][RB], bw[2][NB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) a[0][rb] = *reinterpret_cast<const bf16x8_t*>(xt + abase + rb * 32 * kGroup);
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) bw[0][cb] = dequant_word(wv[cb][0][0], s[cb], b[cb]);
+        for (int cb = 0; cb < NB; ++cb) bw[0][cb] = dequant_word(o.w[cb][0][0], s[cb], b[cb]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int cur = t & 1, nxt = cur ^ 1;
@@ -186,7 +224,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
                     a[nxt][rb] = *reinterpret_cast<const bf16x8_t*>(xt + (abase ^ ((t + 1) << 3)) + rb * 32 * kGroup);
 #pragma unroll
                 for (int cb = 0; cb < NB; ++cb)
-                    bw[nxt][cb] = dequant_word(wv[cb][(t + 1) >> 2][(t + 1) & 3], s[cb], b[cb]);
+                    bw[nxt][cb] = dequant_word(o.w[cb][(t + 1) >> 2][(t + 1) & 3], s[cb], b[cb]);
             }
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
@@ -204,37 +242,46 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
         }
     };
 
-    u32x4_t wA[NB][2], wB[NB][2];
-    uint16_t sA[NB], bA[NB], sB[NB], bB[NB];
-
-    if (g_begin < g_end) {
-        stage_x(g_begin, 0);
-        load_w(g_begin, wA, sA, bA);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    for (int g = g_begin; g < g_end; g += 2) {
-        // even step: group g in buffer 0 and wA; prefetch group g + 1 into buffer 1 and wB
-        const bool has1 = g + 1 < g_end;
-        if (has1) {
-            stage_x(g + 1, 1);
-            load_w(g + 1, wB, sB, bB);
+    // STAGES-deep pipeline over relative groups t = -(STAGES - 1), ..., groups - 1.  Position d
+    // of the STAGES-fold unrolled body handles t = d - (STAGES - 1) (mod STAGES): it waits until
+    // only the newest STAGES - 2 groups of loads are outstanding (group t has landed for this
+    // wave), meets the other waves at the barrier (group t has landed for all of them, and all
+    // have finished reading the stage of group t - 1), refills that stage with group
+    // t + STAGES - 1, and computes group t from stage (d + 1) % STAGES.  Positions with t < 0
+    // only load.  Keeping the fill inside the loop (no peeled prologue) lets the compiler see
+    // that each stage's reads depend on that stage's loads alone.
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using C0 = std::integral_constant<int, 1 % STAGES>;
+    using C1 = std::integral_constant<int, 2 % STAGES>;
+    using C2 = std::integral_constant<int, 3 % STAGES>;
+    Slot slot0, slot1, slot2;
+    int t = -(STAGES - 1);
+    asm volatile("" : "+s"(t));   // opaque start: the fill iterations are not peeled off the loop
+    if (groups > 0) {
+#define W4A16_QMM_STEP(d, I, C, SLOT_IN, SLOT_C)                                                   \
+        if constexpr (STAGES > d) {                                                              \
+            if (t >= 0) {                                                                        \
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((STAGES - 2) * kLoadsPerGroup) : "memory"); \
+                __builtin_amdgcn_s_barrier();                                                    \
+                asm volatile("" ::: "memory");                                                   \
+            }                                                                                    \
+            issue(t + STAGES - 1, I{}, SLOT_IN);                                                 \
+            if (t >= 0) {                                                                        \
+                compute(C{}, SLOT_C);                                                            \
+                if (t + 1 >= groups) break;                                                      \
+            }                                                                                    \
+            ++t;                                                                                 \
         }
-        compute(0, wA, sA, bA);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (!has1) break;
-        // odd step: group g + 1 in buffer 1 and wB; prefetch group g + 2 into buffer 0 and wA
-        const bool has2 = g + 2 < g_end;
-        if (has2) {
-            stage_x(g + 2, 0);
-            load_w(g + 2, wA, sA, bA);
+        for (;;) {
+            W4A16_QMM_STEP(0, I0, C0, slot0, (STAGES == 3 ? slot1 : slot1))
+            W4A16_QMM_STEP(1, I1, C1, slot1, (STAGES == 3 ? slot2 : slot0))
+            W4A16_QMM_STEP(2, I2, C2, slot2, slot0)
         }
-        compute(1, wB, sB, bB);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+#undef W4A16_QMM_STEP
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no direct load may outlive the wave
 
     // epilogue: D layout puts rows 8 * (r / 4) + 4 * half + r % 4 of column lane % 32 in this lane
 #pragma unroll
@@ -245,8 +292,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
             if (m >= M) continue;
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
-                if (!col_ok[cb]) continue;
-                const size_t idx = static_cast<size_t>(m) * N + col[cb];
+                const int col = n0 + (wave * NB + cb) * 32 + (lane & 31);
+                if (col >= N) continue;
+                const size_t idx = static_cast<size_t>(m) * N + col;
                 if (split == 1)
                     y[idx] = f32_to_bf16_bits(acc[rb][cb][r]);
                 else
@@ -266,22 +314,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 const QmmShape kQmmVariants[kNumQmmVariants] = {
-    {128, 1, 4},  // 0: 128 x 128 tile, 4 waves of 128 x 32, two waves per SIMD
-    {64, 1, 4},   // 1:  64 x 128 tile, 4 waves of  64 x 32, three waves per SIMD
-    {64, 2, 4},   // 2:  64 x 256 tile, 4 waves of  64 x 64, two waves per SIMD
-    {128, 2, 4},  // 3: 128 x 256 tile, 4 waves of 128 x 64, one wave per SIMD
-    {256, 1, 4},  // 4: 256 x 128 tile, 4 waves of 256 x 32, one wave per SIMD
+    {128, 1, 4, 2},  // 0: 128 x 128 tile, 4 waves of 128 x 32, two waves per SIMD, 2 stages
+    {64, 1, 4, 2},   // 1:  64 x 128 tile, 4 waves of  64 x 32, three waves per SIMD, 2 stages
+    {64, 1, 4, 3},   // 2:  64 x 128 tile, two waves per SIMD, 3 stages
 };
 
-template <int BM, int NB, int NW, int WAVES_PER_SIMD>
+template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES>
 static hipError_t launch_qmm_t(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                                uint16_t* y, float* ws, int M, int N, int K, int split, hipStream_t stream) {
     constexpr int BN = NW * NB * 32;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const dim3 grid(tiles_m * tiles_n * split);
-    hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WAVES_PER_SIMD>), grid, dim3(64 * NW), 0, stream, x, wq, s, b, y, ws, M, N, K, split,
-                       tiles_m, tiles_n);
+    hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WAVES_PER_SIMD, STAGES>), grid, dim3(64 * NW), 0, stream, x, wq, s, b, y,
+                       ws, M, N, K, split, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -289,11 +335,9 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint32_t* wq, const 
                       const uint16_t* biases, uint16_t* y, float* ws, int M, int N, int K, int split,
                       hipStream_t stream) {
     switch (variant) {
-        case 0: return launch_qmm_t<128, 1, 4, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 1: return launch_qmm_t<64, 1, 4, 3>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 2: return launch_qmm_t<64, 2, 4, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 3: return launch_qmm_t<128, 2, 4, 1>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 4: return launch_qmm_t<256, 1, 4, 1>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 0: return launch_qmm_t<128, 1, 4, 2, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 1: return launch_qmm_t<64, 1, 4, 3, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 2: return launch_qmm_t<64, 1, 4, 2, 3>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
         default: return hipErrorInvalidValue;
     }
 }

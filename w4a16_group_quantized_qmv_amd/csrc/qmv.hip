@@ -32,6 +32,7 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace w4a16 {
@@ -494,26 +495,53 @@ static hipError_t launch_qmv_t(const uint16_t* x, const uint32_t* wq, const uint
     return hipGetLastError();
 }
 
+namespace {
+constexpr int kMaxDevices = 64;
+struct WideLaunchCache {
+    std::atomic<bool> ready{false};
+    std::atomic<int> cus{0};
+    std::atomic<uint64_t> occupancy{0};
+};
+WideLaunchCache g_wide_cache[kMaxDevices];
+}  // namespace
+
 template <int CB, int D, int W>
 static hipError_t launch_qmv_wide_t(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                                     uint16_t* y, int M, int N, int K, hipStream_t stream) {
     static_assert(CB == 1 && W == 4 && D == kQmvWideStages, "qmv_wide_fits describes this instance");
     if (!qmv_wide_fits(M, K)) return hipErrorInvalidValue;
-    int dev = 0, cus = 0;
+    int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     const int blocks = (N + CB * 16 - 1) / (CB * 16);
     const size_t xbytes = qmv_wide_lds_bytes(M, K);
     auto kern = qmv_wide_kernel<CB, D, W>;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(xbytes));
-    if (e != hipSuccess) return e;
-    int per_cu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * W, xbytes);
-    if (e != hipSuccess) return e;
-    const int wgs = std::min(std::max(per_cu, 1) * cus, (blocks + W - 1) / W);
+    // Per device, once: the compute-unit count, and permission for the largest dynamic LDS the
+    // fit check admits.  Per activation size: resident workgroups per compute unit (cached for
+    // the last size asked; a race only repeats the query).
+    WideLaunchCache& cache = g_wide_cache[dev];
+    if (!cache.ready.load(std::memory_order_acquire)) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(160 * 1024 - kQmvWideStaticLds));
+        if (e != hipSuccess) return e;
+        cache.cus.store(cus, std::memory_order_relaxed);
+        cache.ready.store(true, std::memory_order_release);
+    }
+    const int cus = cache.cus.load(std::memory_order_relaxed);
+    const uint64_t packed = cache.occupancy.load(std::memory_order_relaxed);   // xbytes << 8 | per_cu
+    int per_cu = (packed >> 8) == xbytes ? static_cast<int>(packed & 0xFF) : 0;
+    if (per_cu == 0) {
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * W, xbytes);
+        if (e != hipSuccess) return e;
+        per_cu = std::max(1, std::min(per_cu, 255));
+        cache.occupancy.store((static_cast<uint64_t>(xbytes) << 8) | static_cast<uint64_t>(per_cu),
+                              std::memory_order_relaxed);
+    }
+    const int wgs = std::min(per_cu * cus, (blocks + W - 1) / W);
     hipLaunchKernelGGL(kern, dim3(wgs), dim3(64 * W), xbytes, stream, x, wq, s, b, y, M, N, K);
     return hipGetLastError();
 }
