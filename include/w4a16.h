@@ -60,15 +60,21 @@ enum w4a16_status {
 };
 
 enum w4a16_path {
-    W4A16_PATH_AUTO = 0,       /* dispatch: M <= 8 -> qmv, M > 8 -> qmm ("Week 2 Day 6", Task 1) */
+    W4A16_PATH_AUTO = 0,       /* dispatch: M <= 8 -> qmv ("Week 2 Day 6", Task 1), 8 < M <= 32
+                                  -> skinny, M > 32 -> qmm                                       */
     W4A16_PATH_QMV = 1,        /* wavefront matvec for decode rows                                */
-    W4A16_PATH_QMM = 2         /* MFMA-tiled matrix path for prefill rows                         */
+    W4A16_PATH_QMM = 2,        /* MFMA-tiled matrix path for prefill rows                         */
+    W4A16_PATH_SKINNY = 3      /* 8 < M <= 32 under AUTO (any M <= 32 when asked for): the matvec
+                                  kernels up to 16 rows, 32-row MFMA tiles with deterministic
+                                  split-K above (the small-batch regime 8 < rows <= 32 that
+                                  "Feature Request: Metal prefill speedup (~68%) on M5 Max",
+                                  Related work, names for skinny tiles + deterministic split-K)  */
 };
 
 /* Launch plan chosen by the dispatch policy (filled by w4a16_plan). */
 typedef struct w4a16_plan {
-    int32_t path;              /* W4A16_PATH_QMV or W4A16_PATH_QMM                         */
-    int32_t tile_m;            /* rows per workgroup tile (qmm) or MFMA rows (qmv = 16)    */
+    int32_t path;              /* W4A16_PATH_QMV, _QMM or _SKINNY                          */
+    int32_t tile_m;            /* rows per workgroup tile, or 16 for the matvec kernels     */
     int32_t tile_n;            /* output columns per workgroup                              */
     int32_t tile_k;            /* reduction values per pipeline step (one group = 128)     */
     int32_t grid_x;            /* workgroups along N                                        */
@@ -91,11 +97,11 @@ const char* w4a16_status_string(int status);
 /*
  * Dispatch policy ("Week 2 Day 6", Task 1 for the M threshold; Task 5 and "Benchmark Analysis:
  * Identify Under-Filled Prefill Shapes" for splitting K only when the tile grid under-fills the
- * GPU).  path: W4A16_PATH_AUTO / _QMV / _QMM.  split_k: 0 = policy, 1 = never split, S > 1 =
+ * GPU).  path: W4A16_PATH_AUTO / _QMV / _QMM / _SKINNY.  split_k: 0 = policy, 1 = never split, S > 1 =
  * exactly S slices (clamped to the number of groups).  num_cus: compute units to plan for;
  * 0 = query the current device.  Pure host arithmetic; `out` is caller-owned.
- * Returns W4A16_OK, _ERR_NULL, _ERR_SHAPE, _ERR_GROUP, _ERR_UNSUPPORTED (qmv with M > 8) or
- * _ERR_DEVICE.
+ * Returns W4A16_OK, _ERR_NULL, _ERR_SHAPE, _ERR_GROUP, _ERR_UNSUPPORTED (qmv with M > 8,
+ * skinny with M > 32, unknown path) or _ERR_DEVICE.
  */
 int w4a16_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, int32_t split_k,
                int32_t num_cus, w4a16_plan_t* out);
@@ -128,8 +134,9 @@ int qmm_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, con
               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * The quantized-linear entry point: dispatch by M (qmv for M <= 8, qmm with the policy's
- * split otherwise).  Same arguments and errors as qmm_w4a16 with split_k = 0.
+ * The quantized-linear entry point: dispatch by M (qmv for M <= 8, the skinny path for
+ * 8 < M <= 32, qmm beyond, each with the policy's split).  Same arguments and errors as
+ * qmm_w4a16 with split_k = 0.
  */
 int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                  uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group,

@@ -40,11 +40,40 @@ def plan(M, N, K, path=0, split_k=0):
 
 
 def test_matvec_threshold_is_eight_rows():
-    # "Week 2 Day 6: SIMD-Matrix Prefill", Task 1: M <= 8 -> matvec, M > 8 -> matrix kernel
+    # "Week 2 Day 6: SIMD-Matrix Prefill", Task 1: M <= 8 -> matvec, M > 8 -> matrix kernels;
+    # 8 < M <= 32 is the skinny regime (small-batch tiles with deterministic split-K)
     for M in range(1, 9):
         assert plan(M, 4096, 2560)["path"] == w4.PATH_QMV
-    for M in (9, 16, 33, 128, 512, 4096):
+    for M in (9, 16, 17, 32):
+        assert plan(M, 4096, 2560)["path"] == w4.PATH_SKINNY
+    for M in (33, 128, 512, 4096):
         assert plan(M, 4096, 2560)["path"] == w4.PATH_QMM
+
+
+def test_skinny_plans():
+    # up to 16 rows: the matvec kernels (tile_m = 16, no split); above: 32-row tiles
+    for M in (9, 12, 16):
+        p = plan(M, 4096, 2560)
+        assert p["tile_m"] == 16 and p["split_k"] == 1 and p["workspace_bytes"] == 0
+    for M in (17, 24, 32):
+        p = plan(M, 4096, 2560)
+        assert p["tile_m"] == 32 and p["grid_y"] == 1
+    # skinny split: about one work unit per compute unit, at most 8 slices of >= 2 groups
+    assert plan(32, 9728, 2560)["split_k"] == CUS // 76          # 76 tiles of 32 x 128
+    assert plan(32, 2560, 9728)["split_k"] == 8                  # 20 tiles, K = 9728
+    assert plan(32, 1024, 256)["split_k"] == 1                   # two groups: nothing to split
+    assert plan(32, 151936, 2560)["split_k"] == 1                # 1187 tiles fill the GPU
+    # a 16-row wide head would leave one workgroup per compute unit: 32-row tiles instead
+    assert plan(16, 151936, 2560)["tile_m"] == 32
+    assert plan(9, 151936, 2560)["tile_m"] == 16
+    # the forced skinny path serves any M <= 32 and nothing above
+    assert plan(4, 4096, 2560, path=w4.PATH_SKINNY)["path"] == w4.PATH_SKINNY
+    with pytest.raises(NotImplementedError):
+        plan(33, 4096, 2560, path=w4.PATH_SKINNY)
+    # workspace sizing follows the skinny split
+    p = plan(32, 2560, 9728)
+    assert p["workspace_bytes"] == 8 * 32 * 2560 * 4
+    assert w4.w4a16_workspace_bytes(32, 2560, 9728, 128, CUS) == p["workspace_bytes"]
 
 
 def test_forced_paths():

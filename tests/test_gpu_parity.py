@@ -165,6 +165,50 @@ def test_qmv_kernel_families(lib, N, K, M, variant):
     assert np.array_equal(run(lib, p, "qmv"), y), "repeat run differs"
 
 
+# ---------------------------------------------------------------------------------- skinny rows
+
+# (M, N, K, tile_m the policy picks): 8 < M <= 16 runs the matvec kernels (tile_m 16), above
+# that 32-row MFMA tiles with split-K (tile_m 32)
+SKINNY_CASES = [
+    (9, 4000, 256, 16),        # 16-column K-split matvec, ragged N
+    (16, 8200, 384, 16),       # 64-column K-split matvec, odd group count
+    (12, 24600, 512, 16),      # wide matvec at 12 rows
+    (16, 24600, 2048, 32),     # the wide matvec's activation tile would be too large: tiles
+    (17, 1000, 2560, 32),      # ragged N, split-K (8 tiles)
+    (24, 2560, 9728, 32),      # long K: 8 slices
+    (32, 9728, 2560, 32),      # gate projection shape, 3 slices
+    (32, 4096, 384, 32),       # odd group count, split limited to one slice per group pair
+]
+
+
+@pytest.mark.parametrize("M,N,K,tile_m", SKINNY_CASES)
+def test_skinny_rows(lib, M, N, K, tile_m):
+    pl = lib.w4a16_plan(M, N, K, 128, lib.PATH_AUTO)
+    assert pl["path"] == lib.PATH_SKINNY and pl["tile_m"] == tile_m
+    p = synth.random_problem(12, M, N, K)
+    y = run(lib, p, "linear")
+    assert_parity(y, p)
+    assert np.array_equal(run(lib, p, "linear"), y), "repeat run differs"
+
+
+def test_skinny_matches_tiled_path_on_integer_sums(lib):
+    # exact integer sums: the skinny kernels and the 64-row tiles must agree bit for bit
+    rng = np.random.default_rng(13)
+    for M in (9, 16, 20, 32):
+        K, N = 512, 1100
+        q = rng.integers(0, 16, (N, K))
+        xi = np.zeros((M, K), dtype=np.int64)
+        for m in range(M):
+            xi[m, rng.choice(K, size=rng.integers(0, 18), replace=False)] = 1
+        G = K // 128
+        p = {"x": synth.to_bf16_bits(xi.astype(np.float32)), "wq": synth.pack_codes(q),
+             "scales": synth.const_bf16(1.0, (N, G)), "biases": synth.const_bf16(0.0, (N, G)),
+             "M": M, "N": N, "K": K}
+        expect = synth.to_bf16_bits((xi @ q.T).astype(np.float32))
+        assert np.array_equal(run(lib, p, "linear"), expect), f"skinny M={M}"
+        assert np.array_equal(run(lib, p, "qmm", 1), expect), f"tiled M={M}"
+
+
 @pytest.mark.parametrize("path,split", [("qmv", None), ("qmm", 1), ("qmm", 3)])
 def test_scaling_by_two_is_bit_exact(lib, path, split):
     p = synth.random_problem(77, 8 if path == "qmv" else 100, 300, 768)

@@ -24,14 +24,14 @@ import os
 import re
 
 __all__ = [
-    "W4A16_OK", "PATH_AUTO", "PATH_QMV", "PATH_QMM", "GROUP",
+    "W4A16_OK", "PATH_AUTO", "PATH_QMV", "PATH_QMM", "PATH_SKINNY", "GROUP",
     "load", "lib_path", "w4a16_abi_version", "w4a16_status_string", "w4a16_plan", "w4a16_workspace_bytes",
     "qmv_w4a16", "qmm_w4a16", "w4a16_linear", "linear", "W4A16Error", "declared_symbols", "PreparedLinear",
 ]
 
 GROUP = 128
 W4A16_OK = 0
-PATH_AUTO, PATH_QMV, PATH_QMM = 0, 1, 2
+PATH_AUTO, PATH_QMV, PATH_QMM, PATH_SKINNY = 0, 1, 2, 3
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG_DIR), "include", "w4a16.h")
@@ -210,7 +210,8 @@ def qmm_w4a16(x, wq, scales, biases, y=None, split_k: int = 0, workspace=None, s
 
 
 def w4a16_linear(x, wq, scales, biases, y=None, workspace=None, stream=None):
-    """Dispatching entry point (qmv for M <= 8, qmm with the policy's split otherwise).  Returns y."""
+    """Dispatching entry point (qmv for M <= 8, the skinny path for 8 < M <= 32, qmm beyond, each
+    with the policy's split).  Returns y."""
     M, N, K, y = _operands(x, wq, scales, biases, y)
     ws, ws_bytes = _workspace(workspace, w4a16_workspace_bytes(M, N, K), x.device)
     st = load().w4a16_linear(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(),

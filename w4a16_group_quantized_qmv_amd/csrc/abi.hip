@@ -16,6 +16,10 @@ using namespace w4a16;
 
 // Policy constants.
 constexpr int64_t kQmvMaxRows = 8;        // decode rows served by qmv ("Week 2 Day 6", Task 1)
+constexpr int64_t kSkinnyMaxRows = 32;    // rows served by the skinny path
+constexpr int64_t kQmvKernelRows = 16;    // rows one matvec MFMA operand covers
+// LDS a wide-kernel workgroup may use on the skinny path (two workgroups per compute unit)
+constexpr size_t kQmvWideSkinnyLds = 80 * 1024;
 constexpr int kSplitMinGroups = 4;        // fewest groups one split-K slice may own
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 // Largest K: keeps every per-lane buffer offset of the kernels (at most 256 K bytes past a
@@ -99,26 +103,33 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
     (void)M;
 }
 
-void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p) {
+// skinny: 32-row tiles and the skinny split rule (rows 17..32, or a wide head at 9..16 rows)
+void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p,
+              bool skinny = false) {
     const int64_t G = K / W4A16_GROUP;
-    auto tiles_of = [&](int v) {
-        const QmmShape& q = kQmmVariants[v];
-        return ceil_div(M, q.bm) * ceil_div(N, int64_t{q.nwaves} * q.nb * 32);
-    };
     // Measured on MI355X: 64 x 128 tiles (three waves per SIMD) lead up to about a thousand
-    // rows, where the grid is small; 128 x 128 tiles (two waves per SIMD) lead beyond.
-    int variant = M <= 1024 ? 1 : 0;
-    (void)tiles_of;
+    // rows, where the grid is small; 128 x 128 tiles (two waves per SIMD) lead beyond.  For at
+    // most 32 rows, 32 x 128 tiles (four waves per SIMD, three stages) lead on every layer shape
+    // and on the vocabulary head.
+    const int variant = skinny ? kQmmSkinnyVariant : (M <= 1024 ? 1 : 0);
     const QmmShape& v = kQmmVariants[variant];
     const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
     const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, tile_n);
     int64_t S = 1;
     if (split_k == 0) {
-        // split only an under-filled grid, and only when every slice keeps several groups.
-        // Measured on MI355X (M = 128 and 512 for the 2560-wide layer's projections): one slice
-        // more than just filling the compute units wins for the K/V, O and down projections
-        // (e.g. S = 3 for 160 tiles), because a compute unit holds several workgroups.
-        if (tiles < cus && G >= 2 * kSplitMinGroups) {
+        if (skinny) {
+            // skinny tiles: about one work unit per compute unit (measured best: gate S = 3 for
+            // 76 tiles, q S = 4..8 for 32, down / o / k,v S = 8), at most 8 slices of >= 2 groups
+            if (tiles < cus) {
+                S = std::min<int64_t>({cus / tiles, 8, G / 2});
+                if (S < 2) S = 1;
+            }
+        } else if (tiles < cus && G >= 2 * kSplitMinGroups) {
+            // split only an under-filled grid, and only when every slice keeps several groups.
+            // Measured on MI355X (M = 128 and 512 for the 2560-wide layer's projections): one
+            // slice more than just filling the compute units wins for the K/V, O and down
+            // projections (e.g. S = 3 for 160 tiles), because a compute unit holds several
+            // workgroups.
             S = ceil_div(cus, tiles) + 1;
             if (S > G / kSplitMinGroups) S = G / kSplitMinGroups;
             if (S < 2) S = 1;
@@ -127,7 +138,7 @@ void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a
         S = split_k < 1 ? 1 : split_k;
         if (S > G) S = G;
     }
-    p->path = W4A16_PATH_QMM;
+    p->path = skinny ? W4A16_PATH_SKINNY : W4A16_PATH_QMM;
     p->tile_m = v.bm;
     p->tile_n = static_cast<int32_t>(tile_n);
     p->tile_k = W4A16_GROUP;
@@ -141,22 +152,45 @@ void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a
     p->workspace_bytes = S > 1 ? static_cast<uint64_t>(S) * M * N * sizeof(float) : 0;
 }
 
+// Skinny rows (at most 32): up to 16 rows the matvec kernels (their 16-row MFMA operand covers
+// them; measured 1.1-1.7x faster than tiles at 9..16 rows), except where the wide kernel's
+// activation tile would leave fewer than two workgroups per compute unit; above 16 rows the
+// 32-row MFMA tiles with split-K.
+void plan_skinny(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p) {
+    if (M <= kQmvKernelRows) {
+        plan_qmv(M, N, K, cus, p);
+        const bool wide_too_big = p->variant == kQmvWideVariant &&
+                                  kQmvWideStaticLds + qmv_wide_lds_bytes(static_cast<int>(M), static_cast<int>(K)) >
+                                      kQmvWideSkinnyLds;
+        if (!wide_too_big) {
+            p->path = W4A16_PATH_SKINNY;
+            return;
+        }
+    }
+    plan_qmm(M, N, K, split_k, cus, p, true);
+}
+
 int make_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, int32_t split_k, int32_t num_cus,
               w4a16_plan_t* out) {
     if (!out) return W4A16_ERR_NULL;
     int st = check_shape(M, N, K, group);
     if (st != W4A16_OK) return st;
-    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_QMV && path != W4A16_PATH_QMM) return W4A16_ERR_UNSUPPORTED;
+    if (path != W4A16_PATH_AUTO && path != W4A16_PATH_QMV && path != W4A16_PATH_QMM && path != W4A16_PATH_SKINNY)
+        return W4A16_ERR_UNSUPPORTED;
     if (split_k < 0) return W4A16_ERR_SHAPE;
     int32_t cus = num_cus;
     if (cus <= 0) {
         st = query_num_cus(&cus);
         if (st != W4A16_OK) return st;
     }
-    if (path == W4A16_PATH_AUTO) path = M <= kQmvMaxRows ? W4A16_PATH_QMV : W4A16_PATH_QMM;
+    if (path == W4A16_PATH_AUTO)
+        path = M <= kQmvMaxRows ? W4A16_PATH_QMV : (M <= kSkinnyMaxRows ? W4A16_PATH_SKINNY : W4A16_PATH_QMM);
     if (path == W4A16_PATH_QMV) {
         if (M > kQmvMaxRows) return W4A16_ERR_UNSUPPORTED;
         plan_qmv(M, N, K, cus, out);
+    } else if (path == W4A16_PATH_SKINNY) {
+        if (M > kSkinnyMaxRows) return W4A16_ERR_UNSUPPORTED;
+        plan_skinny(M, N, K, split_k, cus, out);
     } else {
         plan_qmm(M, N, K, split_k, cus, out);
     }
@@ -166,10 +200,15 @@ int make_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, int3
 
 int to_status(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH; }
 
+// a skinny plan of at most 16 rows runs the matvec kernels (tile_m = 16); otherwise tiles
+bool uses_qmv_kernels(const w4a16_plan_t& p) {
+    return p.path == W4A16_PATH_QMV || (p.path == W4A16_PATH_SKINNY && p.tile_m == kQmvKernelRows);
+}
+
 int run_plan(const w4a16_plan_t& p, const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
              uint16_t* y, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream) {
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-    if (p.path == W4A16_PATH_QMV) return to_status(launch_qmv(p.variant, x, wq, s, b, y, m, n, k, stream));
+    if (uses_qmv_kernels(p)) return to_status(launch_qmv(p.variant, x, wq, s, b, y, m, n, k, stream));
     float* ws = static_cast<float*>(workspace);
     hipError_t e = launch_qmm(p.variant, x, wq, s, b, y, ws, m, n, k, p.split_k, stream);
     if (e != hipSuccess || p.split_k == 1) return to_status(e);
@@ -187,13 +226,13 @@ int run_qmm(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint
     w4a16_plan_t p;
     st = make_plan(M, N, K, group, path, split_k, 0, &p);
     if (st != W4A16_OK) return st;
-    if (p.path == W4A16_PATH_QMM && p.split_k > 1) {
+    if (!uses_qmv_kernels(p) && p.split_k > 1) {
         const bool ws_ok = workspace != nullptr && aligned(workspace, 16) && ws_bytes >= p.workspace_bytes;
         if (!ws_ok) {
             if (split_k > 1) return workspace != nullptr && !aligned(workspace, 16) ? W4A16_ERR_ALIGN
                                                                                      : W4A16_ERR_WORKSPACE;
             // policy split without a usable workspace: the unsplit plan computes the same result
-            plan_qmm(M, N, K, 1, p.num_cus, &p);
+            plan_qmm(M, N, K, 1, p.num_cus, &p, p.path == W4A16_PATH_SKINNY);
         }
     }
     return run_plan(p, x, wq, s, b, y, M, N, K, workspace, static_cast<hipStream_t>(stream));

@@ -49,7 +49,8 @@ struct QmmShape {
     int stages;   // groups in flight: LDS activation tiles and weight register sets
 };
 
-constexpr int kNumQmmVariants = 3;
+constexpr int kNumQmmVariants = 5;
+constexpr int kQmmSkinnyVariant = 4;   // 32 x 128 tiles, three stages: at most 32 rows
 extern const QmmShape kQmmVariants[kNumQmmVariants];
 
 // split == 1 writes bf16 y; split > 1 writes fp32 partials ws[z][M][N] for z < split.

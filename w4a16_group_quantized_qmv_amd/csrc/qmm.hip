@@ -317,6 +317,8 @@ const QmmShape kQmmVariants[kNumQmmVariants] = {
     {128, 1, 4, 2},  // 0: 128 x 128 tile, 4 waves of 128 x 32, two waves per SIMD, 2 stages
     {64, 1, 4, 2},   // 1:  64 x 128 tile, 4 waves of  64 x 32, three waves per SIMD, 2 stages
     {64, 1, 4, 3},   // 2:  64 x 128 tile, two waves per SIMD, 3 stages
+    {32, 1, 4, 2},   // 3:  32 x 128 tile, 4 waves of 32 x 32, four waves per SIMD, 2 stages (skinny M)
+    {32, 1, 4, 3},   // 4:  32 x 128 tile, four waves per SIMD, 3 stages (skinny M)
 };
 
 template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES>
@@ -338,6 +340,8 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint32_t* wq, const 
         case 0: return launch_qmm_t<128, 1, 4, 2, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
         case 1: return launch_qmm_t<64, 1, 4, 3, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
         case 2: return launch_qmm_t<64, 1, 4, 2, 3>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 3: return launch_qmm_t<32, 1, 4, 4, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 4: return launch_qmm_t<32, 1, 4, 4, 3>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
         default: return hipErrorInvalidValue;
     }
 }
