@@ -64,11 +64,12 @@ enum w4a16_path {
                                   -> skinny, M > 32 -> qmm                                       */
     W4A16_PATH_QMV = 1,        /* wavefront matvec for decode rows                                */
     W4A16_PATH_QMM = 2,        /* MFMA-tiled matrix path for prefill rows                         */
-    W4A16_PATH_SKINNY = 3      /* 8 < M <= 32 under AUTO (any M <= 32 when asked for): the matvec
+    W4A16_PATH_SKINNY = 3,     /* 8 < M <= 32 under AUTO (any M <= 32 when asked for): the matvec
                                   kernels up to 16 rows, 32-row MFMA tiles with deterministic
                                   split-K above (the small-batch regime 8 < rows <= 32 that
                                   "Feature Request: Metal prefill speedup (~68%) on M5 Max",
                                   Related work, names for skinny tiles + deterministic split-K)  */
+    W4A16_PATH_GATE_UP = 4     /* reported by w4a16_gate_up_plan only: the fused gate / up tiles  */
 };
 
 /* Launch plan chosen by the dispatch policy (filled by w4a16_plan). */
@@ -141,6 +142,35 @@ int qmm_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, con
 int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                  uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Fused gate / up projection pair with SwiGLU (the SwiGLU fused into the mat-mat, and gate / up
+ * computed together with the GLU in the mat-mat epilogue, named by "Feature Request: Metal
+ * prefill speedup (~68%) on M5 Max": feature list and Related work):
+ *
+ *     h[m, n] = bf16( silu(g[m, n]) * u[m, n] ),   silu(z) = z / (1 + e^-z),
+ *     g = x . dequant(Wq_gate)^T,  u = x . dequant(Wq_up)^T   (fp32, never rounded to bf16)
+ *
+ * One tile kernel reads each activation fragment once for both projections and writes only h.
+ * Both weight sets have the layouts above with the same N and K; h is bf16 [M, N].  Any M >= 1
+ * (32-row tiles up to 32 rows, 64-row up to ~1k, 128-row beyond).  split_k as for qmm_w4a16;
+ * a split plan needs `workspace` of 2 * S * M * N fp32 (w4a16_gate_up_plan().workspace_bytes:
+ * gate partials, then up partials), summed in slice order before the SiLU, so results are
+ * deterministic.  Same preconditions, ownership and errors as qmm_w4a16 (every pointer
+ * checked, h must not overlap an input).
+ */
+int w4a16_gate_up_swiglu(const uint16_t* x, const uint32_t* wq_gate, const uint16_t* scales_gate,
+                         const uint16_t* biases_gate, const uint32_t* wq_up, const uint16_t* scales_up,
+                         const uint16_t* biases_up, uint16_t* h, int64_t M, int64_t N, int64_t K, int32_t group,
+                         int32_t split_k, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Launch plan of w4a16_gate_up_swiglu (path = W4A16_PATH_GATE_UP): tiles, split and workspace
+ * bytes.  split_k and num_cus as in w4a16_plan.  Pure host arithmetic.  Returns W4A16_OK,
+ * _ERR_NULL, _ERR_SHAPE, _ERR_GROUP or _ERR_DEVICE.
+ */
+int w4a16_gate_up_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, int32_t num_cus,
+                       w4a16_plan_t* out);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ def lib():
 def test_library_exports_every_declared_symbol(lib):
     names = w4.declared_symbols()
     assert set(names) >= {"w4a16_abi_version", "w4a16_status_string", "w4a16_plan", "w4a16_workspace_bytes",
-                          "qmv_w4a16", "qmm_w4a16", "w4a16_linear"}
+                          "qmv_w4a16", "qmm_w4a16", "w4a16_linear", "w4a16_gate_up_plan", "w4a16_gate_up_swiglu"}
     for name in names:
         assert hasattr(lib, name), f"libw4a16.so does not export {name}"
 
@@ -187,3 +187,38 @@ def test_qmv_rejects_more_than_eight_rows(lib):
 
 def test_negative_split_is_a_shape_error(lib):
     assert lib.qmm_w4a16(A16, A16, A16, A16, A16, 16, 16, 256, 128, -2, None, 0, None) == 2
+
+
+# ------------------------------------------------------------------------------ fused gate / up + SwiGLU
+
+def gate_up_plan(M, N, K, split_k=0):
+    return w4.w4a16_gate_up_plan(M, N, K, 128, split_k, CUS)
+
+
+def test_gate_up_plan_tiles_and_workspace():
+    # tile rows as for the projection: 32 up to 32 rows, 64 up to ~1k, 128 beyond
+    for M, tile_m in [(1, 32), (32, 32), (33, 64), (512, 64), (1024, 64), (1025, 128), (4096, 128)]:
+        p = gate_up_plan(M, 9728, 2560)
+        assert p["path"] == w4.PATH_GATE_UP and p["tile_m"] == tile_m and p["tile_n"] == 128
+        assert p["grid_x"] == -(-9728 // 128) and p["grid_y"] == -(-M // tile_m)
+        # the workspace holds gate and up partials
+        assert p["workspace_bytes"] == (2 * p["split_k"] * M * 9728 * 4 if p["split_k"] > 1 else 0)
+    # the split follows the projection's rule on the same tile grid
+    for M, N, K in [(128, 9728, 2560), (512, 9728, 2560), (512, 2560, 9728), (16, 1024, 2560)]:
+        g, q = gate_up_plan(M, N, K), plan(M, N, K, path=w4.PATH_QMM if M > 32 else w4.PATH_SKINNY)
+        assert g["split_k"] == q["split_k"] or M <= 16       # 9..16 rows: the skinny plan is a matvec
+    assert gate_up_plan(128, 1024, 2560, split_k=3)["split_k"] == 3
+    assert gate_up_plan(128, 1024, 256, split_k=64)["split_k"] == 2
+
+
+def test_gate_up_validates_before_launch(lib):
+    def call(x=A16, wg=A16, sg=A16, bg=A16, wu=A16, su=A16, bu=A16, h=A16, M=4, N=16, K=256, group=128, split=1):
+        return lib.w4a16_gate_up_swiglu(x, wg, sg, bg, wu, su, bu, h, M, N, K, group, split, None, 0, None)
+
+    for kw in ("x", "wg", "sg", "bg", "wu", "su", "bu", "h"):
+        assert call(**{kw: None}) == 1, kw
+    assert call(M=0) == 2 and call(K=100) == 2 and call(split=-1) == 2
+    assert call(group=64) == 3
+    assert call(wu=ODD) == 4 and call(su=A16 + 1) == 4 and call(h=A16 + 1) == 4
+    with pytest.raises(ValueError):
+        w4.w4a16_gate_up_plan(4, 16, 100, 128, 0, CUS)

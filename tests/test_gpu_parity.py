@@ -373,3 +373,101 @@ def test_policy_split_without_workspace_falls_back(lib):
     assert st == 0
     torch.cuda.synchronize()
     assert_parity(bits(y), p)
+
+
+# ---------------------------------------------------------------------------------- fused gate / up
+
+def gate_up_problem(seed, M, N, K):
+    """x, gate and up weights of one shape from the seeded recipe (gate and up differ)."""
+    g = synth.random_problem(seed, M, N, K)
+    u = synth.random_problem(seed + 1000, M, N, K)
+    return g["x"], (g["wq"], g["scales"], g["biases"]), (u["wq"], u["scales"], u["biases"])
+
+
+def run_gate_up(lib, x, gate, up, split_k=0, workspace="auto"):
+    import torch
+    announce(f"gate_up M={x.shape[0]} N={gate[0].shape[0]} K={x.shape[1]} split={split_k}")
+    M, K = x.shape
+    xd = to_device({"x": x, "wq": gate[0], "scales": gate[1], "biases": gate[2]})
+    ud = to_device({"x": x, "wq": up[0], "scales": up[1], "biases": up[2]})
+    if workspace == "auto":
+        h = lib.w4a16_gate_up_swiglu(xd[0], xd[1:], ud[1:], split_k=split_k)
+    else:   # call the C ABI directly with the given workspace (None = no workspace)
+        N = gate[0].shape[0]
+        h = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+        st = lib.load().w4a16_gate_up_swiglu(xd[0].data_ptr(), xd[1].data_ptr(), xd[2].data_ptr(), xd[3].data_ptr(),
+                                             ud[1].data_ptr(), ud[2].data_ptr(), ud[3].data_ptr(), h.data_ptr(),
+                                             M, N, K, 128, split_k, None, 0, None)
+        if st != 0:
+            return st
+    torch.cuda.synchronize()
+    return bits(h)
+
+
+def assert_swiglu_parity(h_bits, x, gate, up, rows=None):
+    xs = x if rows is None else x[rows]
+    h_ref, g_ref, A_g, u_ref, A_u = O.swiglu_reference(xs, gate, up)
+    got = h_bits if rows is None else h_bits[rows]
+    r = O.check_swiglu(got, g_ref, A_g, u_ref, A_u)
+    assert r.ok, str(r)
+    return r
+
+
+@pytest.mark.parametrize("M,N,K,split", [
+    (33, 96, 256, 0),          # ragged M and N, 64-row tiles
+    (1, 1000, 2560, 0),        # one row: 32-row tiles, policy split
+    (20, 1000, 2560, 0),       # skinny rows, ragged N
+    (128, 9728, 2560, 0),      # the 128-row gate / up shape, policy split (3 slices)
+    (128, 2000, 1024, 1),      # forced: unsplit
+    (70, 1100, 1024, 2),       # forced: two slices
+    (70, 1100, 1024, 5),       # forced: five slices of 1 or 2 groups
+    (1500, 512, 384, 0),       # 128-row tiles, odd group count
+])
+def test_gate_up_swiglu_matches_oracle(lib, M, N, K, split):
+    x, gate, up = gate_up_problem(21, M, N, K)
+    h = run_gate_up(lib, x, gate, up, split)
+    assert_swiglu_parity(h, x, gate, up)
+    assert np.array_equal(run_gate_up(lib, x, gate, up, split), h), "repeat run differs"
+
+
+def test_gate_up_swiglu_prefill512_sampled_rows(lib):
+    # the 512-row layer shape (2560 -> 9728): every column of a row sample, rows across all tiles
+    x, gate, up = gate_up_problem(22, 512, 9728, 2560)
+    h = run_gate_up(lib, x, gate, up)
+    assert_swiglu_parity(h, x, gate, up, rows=np.arange(0, 512, 37))
+
+
+def test_gate_up_swiglu_saturation_closed_form(lib):
+    # all-zero codes and x = 1: g[n] = 128 * sum_g b_gate[n, g], u[n] = 128 * sum_g b_up[n, g].
+    # Gate sums of -256, 0 and +256 hit silu's exp overflow (silu -> -0), its zero and its
+    # identity tail (silu(256) = 256 in fp32); every product is exact in bf16.
+    M, N, K = 3, 96, 256
+    G = K // 128
+    x = synth.const_bf16(1.0, (M, K))
+    bg_vals = np.array([-1.0, 0.0, 1.0])[np.arange(N) % 3]
+    bg = np.repeat(bg_vals[:, None], G, axis=1).astype(np.float32)
+    bu = synth.const_bf16(2.0 ** -7, (N, G))                  # u = 128 * 2^-7 * G = G
+    zero = np.zeros((N, K // 8), dtype=np.uint32)
+    gate = (zero, synth.const_bf16(1.0, (N, G)), synth.to_bf16_bits(bg))
+    up = (zero, synth.const_bf16(1.0, (N, G)), bu)
+    h = run_gate_up(lib, x, gate, up)
+    g = 128.0 * G * bg_vals
+    expect = np.where(g > 0, g * G, 0.0)
+    got = synth.from_bf16_bits(h)
+    assert np.array_equal(got, np.broadcast_to(expect, (M, N)).astype(got.dtype)), got[0, :6]
+    assert_swiglu_parity(h, x, gate, up)
+
+
+def test_gate_up_forced_split_without_workspace_is_rejected(lib):
+    x, gate, up = gate_up_problem(23, 64, 256, 1024)
+    assert run_gate_up(lib, x, gate, up, split_k=4, workspace=None) == 5      # W4A16_ERR_WORKSPACE
+
+
+def test_gate_up_policy_split_without_workspace_falls_back(lib):
+    # the policy splits this grid; without a workspace the unsplit plan runs and gives the
+    # forced-unsplit result bit for bit
+    x, gate, up = gate_up_problem(24, 32, 2048, 2560)
+    assert lib.w4a16_gate_up_plan(32, 2048, 2560)["split_k"] > 1
+    h = run_gate_up(lib, x, gate, up, split_k=0, workspace=None)
+    assert np.array_equal(h, run_gate_up(lib, x, gate, up, split_k=1))
+    assert_swiglu_parity(h, x, gate, up)

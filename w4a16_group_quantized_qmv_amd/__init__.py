@@ -24,14 +24,15 @@ import os
 import re
 
 __all__ = [
-    "W4A16_OK", "PATH_AUTO", "PATH_QMV", "PATH_QMM", "PATH_SKINNY", "GROUP",
+    "W4A16_OK", "PATH_AUTO", "PATH_QMV", "PATH_QMM", "PATH_SKINNY", "PATH_GATE_UP", "GROUP",
     "load", "lib_path", "w4a16_abi_version", "w4a16_status_string", "w4a16_plan", "w4a16_workspace_bytes",
     "qmv_w4a16", "qmm_w4a16", "w4a16_linear", "linear", "W4A16Error", "declared_symbols", "PreparedLinear",
+    "w4a16_gate_up_plan", "w4a16_gate_up_swiglu", "PreparedGateUp",
 ]
 
 GROUP = 128
 W4A16_OK = 0
-PATH_AUTO, PATH_QMV, PATH_QMM, PATH_SKINNY = 0, 1, 2, 3
+PATH_AUTO, PATH_QMV, PATH_QMM, PATH_SKINNY, PATH_GATE_UP = 0, 1, 2, 3, 4
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG_DIR), "include", "w4a16.h")
@@ -79,6 +80,11 @@ def load():
     lib.qmm_w4a16.argtypes = [u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, i32, vp, ctypes.c_size_t, vp]
     lib.w4a16_linear.restype = ctypes.c_int
     lib.w4a16_linear.argtypes = [u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, vp, ctypes.c_size_t, vp]
+    lib.w4a16_gate_up_plan.restype = ctypes.c_int
+    lib.w4a16_gate_up_plan.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(Plan)]
+    lib.w4a16_gate_up_swiglu.restype = ctypes.c_int
+    lib.w4a16_gate_up_swiglu.argtypes = [u16p, u32p, u16p, u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, i32,
+                                         vp, ctypes.c_size_t, vp]
     _LIB = lib
     return lib
 
@@ -124,6 +130,12 @@ def w4a16_plan(M: int, N: int, K: int, group: int = GROUP, path: int = PATH_AUTO
 
 def w4a16_workspace_bytes(M: int, N: int, K: int, group: int = GROUP, num_cus: int = 0) -> int:
     return int(load().w4a16_workspace_bytes(M, N, K, group, num_cus))
+
+
+def w4a16_gate_up_plan(M: int, N: int, K: int, group: int = GROUP, split_k: int = 0, num_cus: int = 0) -> dict:
+    p = Plan()
+    _raise_for(load().w4a16_gate_up_plan(M, N, K, group, split_k, num_cus, ctypes.byref(p)), "w4a16_gate_up_plan")
+    return p.as_dict()
 
 
 # ------------------------------------------------------------------------------------ tensors
@@ -221,6 +233,23 @@ def w4a16_linear(x, wq, scales, biases, y=None, workspace=None, stream=None):
     return y
 
 
+def w4a16_gate_up_swiglu(x, gate, up, h=None, split_k: int = 0, workspace=None, stream=None):
+    """Fused gate / up projections with SwiGLU: ``h = silu(x . Wg^T) * (x . Wu^T)`` in one tile
+    kernel.  ``gate`` and ``up`` are ``(wq, scales, biases)`` triples of one shape.  Returns h."""
+    (wg, sg, bg), (wu, su, bu) = gate, up
+    M, N, K, h = _operands(x, wg, sg, bg, h)
+    if tuple(wu.shape) != tuple(wg.shape) or tuple(su.shape) != tuple(sg.shape) or tuple(bu.shape) != tuple(bg.shape):
+        raise ValueError("gate and up weights must have the same shapes")
+    _operands(x, wu, su, bu, h)                      # same dtype / device / contiguity checks for up
+    need = w4a16_gate_up_plan(M, N, K, GROUP, split_k)["workspace_bytes"]
+    ws, ws_bytes = _workspace(workspace, need, x.device)
+    st = load().w4a16_gate_up_swiglu(x.data_ptr(), wg.data_ptr(), sg.data_ptr(), bg.data_ptr(), wu.data_ptr(),
+                                     su.data_ptr(), bu.data_ptr(), h.data_ptr(), M, N, K, GROUP, split_k,
+                                     None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream, x.device))
+    _raise_for(st, "w4a16_gate_up_swiglu")
+    return h
+
+
 def linear(x, wq, scales, biases, logits_to_keep: int = 0, path: str | None = None, split_k: int | None = None):
     """Quantized linear layer ``y = x · dequant(Wq)ᵀ`` with the ``logits_to_keep`` row slice.
 
@@ -281,3 +310,31 @@ class PreparedLinear:
         if st != W4A16_OK:
             _raise_for(st, self._name)
         return self.y
+
+
+class PreparedGateUp:
+    """The fused gate / up + SwiGLU call with fixed tensors, validated once (see PreparedLinear):
+    ``h`` and any split-K workspace are allocated here; ``__call__`` issues one C-ABI call
+    (``w4a16_gate_up_swiglu``) on the stream current at construction."""
+
+    def __init__(self, x, gate, up, h=None, split_k: int = 0):
+        (wg, sg, bg), (wu, su, bu) = gate, up
+        M, N, K, h = _operands(x, wg, sg, bg, h)
+        if tuple(wu.shape) != tuple(wg.shape):
+            raise ValueError("gate and up weights must have the same shapes")
+        _operands(x, wu, su, bu, h)
+        self.M, self.N, self.K, self.h = M, N, K, h
+        lib = load()
+        self.plan = w4a16_gate_up_plan(M, N, K, GROUP, split_k)
+        ws, ws_bytes = _workspace(None, self.plan["workspace_bytes"], x.device)
+        self.workspace = ws
+        self._fn = lib.w4a16_gate_up_swiglu
+        self._args = (x.data_ptr(), wg.data_ptr(), sg.data_ptr(), bg.data_ptr(), wu.data_ptr(), su.data_ptr(),
+                      bu.data_ptr(), h.data_ptr(), M, N, K, GROUP, split_k, None if ws is None else ws.data_ptr(),
+                      ws_bytes, _stream(None, x.device))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != W4A16_OK:
+            _raise_for(st, "w4a16_gate_up_swiglu")
+        return self.h

@@ -238,6 +238,71 @@ int run_qmm(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint
     return run_plan(p, x, wq, s, b, y, M, N, K, workspace, static_cast<hipStream_t>(stream));
 }
 
+// Gate / up pair with SwiGLU: one tile kernel computes both projections of the same columns.
+// Tile rows as for qmm (32 up to 32 rows, 64 up to ~1k, 128 beyond); the split follows the
+// matching qmm rule; the workspace holds the gate and up partials (2 * S * M * N fp32).
+void plan_gate_up(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p) {
+    plan_qmm(M, N, K, split_k, cus, p, M <= kSkinnyMaxRows);
+    const int variant = M <= kSkinnyMaxRows ? 0 : (M <= 1024 ? 1 : 2);
+    const QmmShape& v = kGateUpVariants[variant];
+    const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
+    if (v.bm != p->tile_m || tile_n != p->tile_n) {   // same tile grid as the qmm rule it follows
+        p->tile_m = v.bm;
+        p->tile_n = static_cast<int32_t>(tile_n);
+        p->grid_x = static_cast<int32_t>(ceil_div(N, tile_n));
+        p->grid_y = static_cast<int32_t>(ceil_div(M, v.bm));
+    }
+    p->path = W4A16_PATH_GATE_UP;
+    p->block_threads = 64 * v.nwaves;
+    p->variant = variant;
+    p->workspace_bytes = p->split_k > 1 ? 2ull * static_cast<uint64_t>(p->split_k) * M * N * sizeof(float) : 0;
+}
+
+int make_gate_up_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, int32_t num_cus,
+                      w4a16_plan_t* out) {
+    if (!out) return W4A16_ERR_NULL;
+    int st = check_shape(M, N, K, group);
+    if (st != W4A16_OK) return st;
+    if (split_k < 0) return W4A16_ERR_SHAPE;
+    int32_t cus = num_cus;
+    if (cus <= 0) {
+        st = query_num_cus(&cus);
+        if (st != W4A16_OK) return st;
+    }
+    plan_gate_up(M, N, K, split_k, cus, out);
+    out->num_cus = cus;
+    return W4A16_OK;
+}
+
+int run_gate_up(const uint16_t* x, const uint32_t* wq_g, const uint16_t* s_g, const uint16_t* b_g,
+                const uint32_t* wq_u, const uint16_t* s_u, const uint16_t* b_u, uint16_t* h, int64_t M, int64_t N,
+                int64_t K, int32_t group, int32_t split_k, void* workspace, size_t ws_bytes, void* stream) {
+    int st = check_shape(M, N, K, group);
+    if (st != W4A16_OK) return st;
+    st = check_buffers(x, wq_g, s_g, b_g, h);
+    if (st != W4A16_OK) return st;
+    st = check_buffers(x, wq_u, s_u, b_u, h);
+    if (st != W4A16_OK) return st;
+    if (split_k < 0) return W4A16_ERR_SHAPE;
+    w4a16_plan_t p;
+    st = make_gate_up_plan(M, N, K, group, split_k, 0, &p);
+    if (st != W4A16_OK) return st;
+    if (p.split_k > 1) {
+        const bool ws_ok = workspace != nullptr && aligned(workspace, 16) && ws_bytes >= p.workspace_bytes;
+        if (!ws_ok) {
+            if (split_k > 1) return workspace != nullptr && !aligned(workspace, 16) ? W4A16_ERR_ALIGN
+                                                                                     : W4A16_ERR_WORKSPACE;
+            plan_gate_up(M, N, K, 1, p.num_cus, &p);   // the unsplit plan computes the same result
+        }
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    float* ws = static_cast<float*>(workspace);
+    hipError_t e = launch_gate_up(p.variant, x, wq_g, s_g, b_g, wq_u, s_u, b_u, h, ws, static_cast<int>(M),
+                                  static_cast<int>(N), static_cast<int>(K), p.split_k, s);
+    if (e != hipSuccess || p.split_k == 1) return to_status(e);
+    return to_status(launch_splitk_reduce_glu(ws, h, M * N, p.split_k, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -294,6 +359,19 @@ int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, 
                  int64_t M, int64_t N, int64_t K, int32_t group, void* workspace, size_t workspace_bytes,
                  void* stream) {
     return run_qmm(x, wq, scales, biases, y, M, N, K, group, W4A16_PATH_AUTO, 0, workspace, workspace_bytes, stream);
+}
+
+int w4a16_gate_up_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, int32_t num_cus,
+                       w4a16_plan_t* out) {
+    return make_gate_up_plan(M, N, K, group, split_k, num_cus, out);
+}
+
+int w4a16_gate_up_swiglu(const uint16_t* x, const uint32_t* wq_gate, const uint16_t* scales_gate,
+                         const uint16_t* biases_gate, const uint32_t* wq_up, const uint16_t* scales_up,
+                         const uint16_t* biases_up, uint16_t* h, int64_t M, int64_t N, int64_t K, int32_t group,
+                         int32_t split_k, void* workspace, size_t workspace_bytes, void* stream) {
+    return run_gate_up(x, wq_gate, scales_gate, biases_gate, wq_up, scales_up, biases_up, h, M, N, K, group, split_k,
+                       workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

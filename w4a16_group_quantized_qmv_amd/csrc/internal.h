@@ -58,6 +58,16 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint32_t* wq, const 
                       const uint16_t* biases, uint16_t* y, float* ws, int M, int N, int K, int split,
                       hipStream_t stream);
 
+// Gate / up pair with SwiGLU: h = bf16(silu(x . gate^T) * (x . up^T)), one tile kernel for both
+// projections.  split > 1 writes fp32 partials ws[0][z][M][N] (gate) and ws[1][z][M][N] (up).
+constexpr int kNumGateUpVariants = 3;
+extern const QmmShape kGateUpVariants[kNumGateUpVariants];
+hipError_t launch_gate_up(int variant, const uint16_t* x, const uint32_t* wq_gate, const uint16_t* s_gate,
+                          const uint16_t* b_gate, const uint32_t* wq_up, const uint16_t* s_up, const uint16_t* b_up,
+                          uint16_t* h, float* ws, int M, int N, int K, int split, hipStream_t stream);
+// h[i] = bf16(silu(sum_z ws[0][z][i]) * sum_z ws[1][z][i]), slices summed in order.
+hipError_t launch_splitk_reduce_glu(const float* ws, uint16_t* h, int64_t MN, int split, hipStream_t stream);
+
 // y[i] = bf16(sum_{z < split} ws[z][i]) summed in slice order.
 hipError_t launch_splitk_reduce(const float* ws, uint16_t* y, int64_t MN, int split, hipStream_t stream);
 

@@ -69,12 +69,23 @@ __device__ __forceinline__ void band_order(int tile, int tiles_m, int tiles_n, i
     tn = in_band / rows;
 }
 
-template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES>
+// SiLU in fp32: z * sigmoid(z) = z / (1 + e^-z); e^-z overflows to inf for z < -88 and the
+// quotient is then -0, the limit.
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.f + expf(-z)); }
+
+// NP weight sets share every activation fragment: NP = 1 is the projection; NP = 2 is the
+// gate / up pair with h = silu(gate) * up formed from the fp32 accumulators in the epilogue
+// (the SwiGLU fused into the mat-mat of "Feature Request: Metal prefill speedup (~68%) on M5
+// Max").  Weight set p of column block cb is block j = p * NB + cb.
+template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES, int NP = 1>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD))) void qmm_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
-    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N, int K,
+    const uint16_t* __restrict__ biases, const uint32_t* __restrict__ wq2, const uint16_t* __restrict__ scales2,
+    const uint16_t* __restrict__ biases2, uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N, int K,
     int split, int tiles_m, int tiles_n) {
-    constexpr int BN = NW * NB * 32;
+    constexpr int BN = NW * NB * 32;              // output columns of the tile (per weight set)
+    constexpr int J = NP * NB;                    // weight blocks per wave
+    static_assert(NP == 1 || NP == 2, "one projection or the gate / up pair");
     constexpr int RB = BM / 32;                   // 32-row blocks per wave
     constexpr int TILE = BM * kGroup;             // bf16 elements of one staged activation tile
     constexpr int DMA_PER_WAVE = BM / (4 * NW);   // 1 KB direct loads per wave per group
@@ -128,13 +139,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     // Weights, scales, biases: resources based at the workgroup's first column.  Lane half h of
     // column block cb takes words 8h .. 8h + 7 of its column's group (two 16-byte loads).
     const int64_t cols_left = static_cast<int64_t>(N - n0);
-    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + static_cast<size_t>(n0) * row_bytes), 0,
-        clamp_records(cols_left * row_bytes), 0x00020000);
-    const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(scales + static_cast<size_t>(n0) * G), 0, clamp_records(cols_left * G * 2), 0x00020000);
-    const __amdgpu_buffer_rsrc_t brsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(biases + static_cast<size_t>(n0) * G), 0, clamp_records(cols_left * G * 2), 0x00020000);
+    __amdgpu_buffer_rsrc_t wrsrc[NP], srsrc[NP], brsrc[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const uint32_t* wp = p == 0 ? wq : wq2;
+        const uint16_t* sp = p == 0 ? scales : scales2;
+        const uint16_t* bp = p == 0 ? biases : biases2;
+        wrsrc[p] = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wp) + static_cast<size_t>(n0) * row_bytes), 0,
+            clamp_records(cols_left * row_bytes), 0x00020000);
+        srsrc[p] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(sp + static_cast<size_t>(n0) * G), 0,
+                                                     clamp_records(cols_left * G * 2), 0x00020000);
+        brsrc[p] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(bp + static_cast<size_t>(n0) * G), 0,
+                                                     clamp_records(cols_left * G * 2), 0x00020000);
+    }
     auto dead = [&](__amdgpu_buffer_rsrc_t r) {
         (void)r;
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, 0, 0x00020000);
@@ -149,18 +167,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     }
 
     struct Slot {
-        u32x4_t w[NB][2];
-        uint16_t s[NB], b[NB];
+        u32x4_t w[J][2];
+        uint16_t s[J], b[J];
     };
-    constexpr int kLoadsPerGroup = DMA_PER_WAVE + 4 * NB;
+    constexpr int kLoadsPerGroup = DMA_PER_WAVE + 4 * J;
     // all loads of group g (relative index j = g - g_begin) into stage / slot ic
     auto issue = [&](int j, auto ic, Slot& o) {
         const bool live = j < groups;
         const int g = g_begin + (live ? j : 0);
         const __amdgpu_buffer_rsrc_t xr = live ? xrsrc : none;
-        const __amdgpu_buffer_rsrc_t wr = live ? wrsrc : none;
-        const __amdgpu_buffer_rsrc_t sr = live ? srsrc : none;
-        const __amdgpu_buffer_rsrc_t br = live ? brsrc : none;
         uint16_t* xt = stage(ic);
 #pragma unroll
         for (int i = 0; i < DMA_PER_WAVE; ++i) {
@@ -171,14 +186,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
         // the empty asm statements keep every load a separate instruction, so the per-group
         // count used by the waits is exact
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) {
-            o.w[cb][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff[cb], g * 64, 0));
+        for (int j = 0; j < J; ++j) {
+            const int p = j / NB, cb = j % NB;
+            const __amdgpu_buffer_rsrc_t wr = live ? wrsrc[p] : none;
+            const __amdgpu_buffer_rsrc_t sr = live ? srsrc[p] : none;
+            const __amdgpu_buffer_rsrc_t br = live ? brsrc[p] : none;
+            o.w[j][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff[cb], g * 64, 0));
             asm volatile("" ::: "memory");
-            o.w[cb][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff[cb], g * 64 + 16, 0));
+            o.w[j][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff[cb], g * 64 + 16, 0));
             asm volatile("" ::: "memory");
-            o.s[cb] = __builtin_amdgcn_raw_buffer_load_b16(sr, sbvoff[cb], g * 2, 0);
+            o.s[j] = __builtin_amdgcn_raw_buffer_load_b16(sr, sbvoff[cb], g * 2, 0);
             asm volatile("" ::: "memory");
-            o.b[cb] = __builtin_amdgcn_raw_buffer_load_b16(br, sbvoff[cb], g * 2, 0);
+            o.b[j] = __builtin_amdgcn_raw_buffer_load_b16(br, sbvoff[cb], g * 2, 0);
             asm volatile("" ::: "memory");
         }
     };
@@ -190,31 +209,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     const int arow = lane & 31;
     const int abase = arow * kGroup + (((half ^ ((arow >> 3) & 1)) << 6) | ((arow & 7) << 3));
 
-    f32x16_t acc[RB][NB];
+    f32x16_t acc[RB][J];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb)
+        for (int j = 0; j < J; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+            for (int r = 0; r < 16; ++r) acc[rb][j][r] = 0.f;
 
     // One group: eight MFMA sub-steps.  Operands are double buffered by sub-step parity: while
     // the MFMAs of sub-step t run, the fragment reads and the dequantization of sub-step t + 1
     // are already issued.  The scheduling barrier at the end of each sub-step bounds the live
     // registers to two sub-steps' operands.
     auto compute = [&](auto ic, const Slot& o) {
-        float s[NB], b[NB];
+        float s[J], b[J];
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) {
-            s[cb] = bf16_bits_to_f32(o.s[cb]);
-            b[cb] = bf16_bits_to_f32(o.b[cb]);
+        for (int j = 0; j < J; ++j) {
+            s[j] = bf16_bits_to_f32(o.s[j]);
+            b[j] = bf16_bits_to_f32(o.b[j]);
         }
         const uint16_t* xt = stage(ic);
-        bf16x8_t a[2][RB], bw[2][NB];
+        bf16x8_t a[2][RB], bw[2][J];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) a[0][rb] = *reinterpret_cast<const bf16x8_t*>(xt + abase + rb * 32 * kGroup);
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) bw[0][cb] = dequant_word(o.w[cb][0][0], s[cb], b[cb]);
+        for (int j = 0; j < J; ++j) bw[0][j] = dequant_word(o.w[j][0][0], s[j], b[j]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int cur = t & 1, nxt = cur ^ 1;
@@ -223,19 +242,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
                 for (int rb = 0; rb < RB; ++rb)
                     a[nxt][rb] = *reinterpret_cast<const bf16x8_t*>(xt + (abase ^ ((t + 1) << 3)) + rb * 32 * kGroup);
 #pragma unroll
-                for (int cb = 0; cb < NB; ++cb)
-                    bw[nxt][cb] = dequant_word(o.w[cb][(t + 1) >> 2][(t + 1) & 3], s[cb], b[cb]);
+                for (int j = 0; j < J; ++j)
+                    bw[nxt][j] = dequant_word(o.w[j][(t + 1) >> 2][(t + 1) & 3], s[j], b[j]);
             }
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int cb = 0; cb < NB; ++cb) acc[rb][cb] = mfma32x32x16(a[cur][rb], bw[cur][cb], acc[rb][cb]);
+                for (int j = 0; j < J; ++j) acc[rb][j] = mfma32x32x16(a[cur][rb], bw[cur][j], acc[rb][j]);
             // interleave: each MFMA is followed by a share of the next sub-step's dequantization
             // (VALU) and fragment reads, so the wave keeps issuing while the matrix core works
 #pragma unroll
-            for (int i = 0; i < RB * NB; ++i) {
+            for (int i = 0; i < RB * J; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, (20 * NB + RB * NB - 1) / (RB * NB), 0);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x002, (20 * J + RB * J - 1) / (RB * J), 0);  // VALU
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // LDS read
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -295,13 +314,37 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
                 const int col = n0 + (wave * NB + cb) * 32 + (lane & 31);
                 if (col >= N) continue;
                 const size_t idx = static_cast<size_t>(m) * N + col;
-                if (split == 1)
-                    y[idx] = f32_to_bf16_bits(acc[rb][cb][r]);
-                else
-                    ws[static_cast<size_t>(z) * M * N + idx] = acc[rb][cb][r];
+                if constexpr (NP == 1) {
+                    if (split == 1)
+                        y[idx] = f32_to_bf16_bits(acc[rb][cb][r]);
+                    else
+                        ws[static_cast<size_t>(z) * M * N + idx] = acc[rb][cb][r];
+                } else {
+                    // gate partials in plane 0, up partials in plane 1 (each [split][M][N])
+                    const float gv = acc[rb][cb][r], uv = acc[rb][NB + cb][r];
+                    if (split == 1) {
+                        y[idx] = f32_to_bf16_bits(silu_f32(gv) * uv);
+                    } else {
+                        ws[static_cast<size_t>(z) * M * N + idx] = gv;
+                        ws[(static_cast<size_t>(split) + z) * M * N + idx] = uv;
+                    }
+                }
             }
         }
     }
+}
+
+// gate / up pair: h = bf16(silu(sum_z gate partial) * sum_z up partial), slices in order
+__global__ __launch_bounds__(256) void splitk_reduce_glu_kernel(const float* __restrict__ ws, uint16_t* __restrict__ h,
+                                                                int64_t MN, int split) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= MN) return;
+    float g = ws[i], u = ws[split * MN + i];
+    for (int z = 1; z < split; ++z) {
+        g += ws[z * MN + i];
+        u += ws[(split + z) * MN + i];
+    }
+    h[i] = f32_to_bf16_bits(silu_f32(g) * u);
 }
 
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ y,
@@ -328,8 +371,21 @@ static hipError_t launch_qmm_t(const uint16_t* x, const uint32_t* wq, const uint
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const dim3 grid(tiles_m * tiles_n * split);
-    hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WAVES_PER_SIMD, STAGES>), grid, dim3(64 * NW), 0, stream, x, wq, s, b, y,
-                       ws, M, N, K, split, tiles_m, tiles_n);
+    hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WAVES_PER_SIMD, STAGES>), grid, dim3(64 * NW), 0, stream, x, wq, s, b,
+                       nullptr, nullptr, nullptr, y, ws, M, N, K, split, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+template <int BM, int WAVES_PER_SIMD, int STAGES>
+static hipError_t launch_gate_up_t(const uint16_t* x, const uint32_t* wg, const uint16_t* sg, const uint16_t* bg,
+                                   const uint32_t* wu, const uint16_t* su, const uint16_t* bu, uint16_t* h, float* ws,
+                                   int M, int N, int K, int split, hipStream_t stream) {
+    constexpr int BN = 4 * 32;
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    const dim3 grid(tiles_m * tiles_n * split);
+    hipLaunchKernelGGL((qmm_kernel<BM, 1, 4, WAVES_PER_SIMD, STAGES, 2>), grid, dim3(256), 0, stream, x, wg, sg, bg,
+                       wu, su, bu, h, ws, M, N, K, split, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -344,6 +400,30 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint32_t* wq, const 
         case 4: return launch_qmm_t<32, 1, 4, 4, 3>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+const QmmShape kGateUpVariants[kNumGateUpVariants] = {
+    {32, 1, 4, 2},   // 0:  32 x 128 tile of h (gate and up: 2 x 32 columns per wave), three waves per SIMD
+    {64, 1, 4, 2},   // 1:  64 x 128 tile of h, two waves per SIMD
+    {128, 1, 4, 2},  // 2: 128 x 128 tile of h, one wave per SIMD
+};
+
+hipError_t launch_gate_up(int variant, const uint16_t* x, const uint32_t* wq_gate, const uint16_t* s_gate,
+                          const uint16_t* b_gate, const uint32_t* wq_up, const uint16_t* s_up, const uint16_t* b_up,
+                          uint16_t* h, float* ws, int M, int N, int K, int split, hipStream_t stream) {
+    switch (variant) {
+        case 0: return launch_gate_up_t<32, 3, 2>(x, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K, split, stream);
+        case 1: return launch_gate_up_t<64, 2, 2>(x, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K, split, stream);
+        case 2: return launch_gate_up_t<128, 1, 2>(x, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K, split, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_splitk_reduce_glu(const float* ws, uint16_t* h, int64_t MN, int split, hipStream_t stream) {
+    const int64_t blocks = (MN + 255) / 256;
+    hipLaunchKernelGGL(splitk_reduce_glu_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, ws, h, MN,
+                       split);
+    return hipGetLastError();
 }
 
 hipError_t launch_splitk_reduce(const float* ws, uint16_t* y, int64_t MN, int split, hipStream_t stream) {
