@@ -258,12 +258,75 @@ def main():
         "breakdown": per,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
+    result["next_rows"] = next_rows(torch, w4, projections, args.copies)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(projections)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def time_call(torch, fns, reps):
+    """Average microseconds of one call, rotating over the prepared calls in ``fns`` (one per
+    weight copy), with HIP events on the launch stream around each call."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record()
+        fns[i % len(fns)]()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) * 1e3 / reps
+
+
+def next_rows(torch, w4, projections, copies, reps=20):
+    """Measurements of the rows beyond the step: the fused gate/up + SwiGLU pair at the step's
+    512 rows against the two separate projections, and the skinny path (16 and 32 rows) against
+    the 64-row tiles, on the layer's gate and down shapes."""
+    by = {p["name"]: p for p in projections}
+    gate, up = by["gate"], by["up"]
+    x = gate["x"]
+    M, N, K = gate["M"], gate["N"], gate["K"]
+    fused = [w4.PreparedGateUp(x, gate["w"][c], up["w"][c]) for c in range(copies)]
+    sep_g = [w4.PreparedLinear(x, *gate["w"][c]) for c in range(copies)]
+    sep_u = [w4.PreparedLinear(x, *up["w"][c], y=torch.empty_like(sep_g[0].y)) for c in range(copies)]
+    g_out, u_out = sep_g[0].y, sep_u[0].y
+
+    def glu():      # the unfused epilogue as a framework runs it: bf16 SiLU, then the product
+        return torch.nn.functional.silu(g_out).mul_(u_out)
+
+    def unfused(c):
+        return lambda: (sep_g[c](), sep_u[c](), glu())
+
+    t_fused = time_call(torch, fused, reps)
+    t_sep = time_call(torch, sep_g, reps) + time_call(torch, sep_u, reps)
+    t_unfused = time_call(torch, [unfused(c) for c in range(copies)], reps)
+    f2 = 2 * flops(M, N, K)
+    out = {"fused_gate_up_swiglu": {
+        "M": M, "N": N, "K": K, "plan": {k: fused[0].plan[k] for k in ("tile_m", "tile_n", "split_k", "variant")},
+        "fused_us": round(t_fused, 3), "gate_plus_up_us": round(t_sep, 3),
+        "unfused_gate_up_silu_mul_us": round(t_unfused, 3),
+        "speedup_vs_unfused": round(t_unfused / t_fused, 3), "TFLOP/s": round(f2 / t_fused / 1e6, 2),
+        "frac_mfma": round(f2 / t_fused / 1e6 / PEAK_BF16_TFLOPS, 4)}}
+    skinny = []
+    for name in ("gate", "down"):
+        p = by[name]
+        for m in (16, 32):
+            xs = p["x"][:m]
+            auto = [w4.PreparedLinear(xs, *p["w"][c]) for c in range(copies)]
+            tiled = [w4.PreparedLinear(xs, *p["w"][c], path="qmm") for c in range(copies)]
+            t_a, t_t = time_call(torch, auto, reps), time_call(torch, tiled, reps)
+            b = algo_bytes(m, p["N"], p["K"])
+            skinny.append({"name": name, "M": m, "N": p["N"], "K": p["K"], "tile_m": auto[0].plan["tile_m"],
+                           "split_k": auto[0].plan["split_k"], "skinny_us": round(t_a, 3),
+                           "tiled64_us": round(t_t, 3), "GB/s": round(b / t_a / 1e3, 1),
+                           "frac_hbm": round(b / t_a / 1e3 / PEAK_HBM_GBPS, 4)})
+    out["skinny"] = skinny
+    out["timing"] = "HIP events around each call, rotating weight copies, after the timed region"
+    return out
 
 
 def synth_shape(name):
