@@ -107,7 +107,7 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
 void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p,
               bool skinny = false) {
     const int64_t G = K / W4A16_GROUP;
-    // Measured on MI355X: 64 x 128 tiles (three waves per SIMD) lead up to about a thousand
+    // Measured on MI355X: 64 x 128 tiles (four waves per SIMD) lead up to about a thousand
     // rows, where the grid is small; 128 x 128 tiles (two waves per SIMD) lead beyond.  For at
     // most 32 rows, 32 x 128 tiles (four waves per SIMD, three stages) lead on every layer shape
     // and on the vocabulary head.

@@ -173,7 +173,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     constexpr int kLoadsPerGroup = DMA_PER_WAVE + 4 * J;
     // all loads of group g (relative index j = g - g_begin) into stage / slot ic
     auto issue = [&](int j, auto ic, Slot& o) {
-        const bool live = j < groups;
+        const bool live = j >= 0 && j < groups;
         const int g = g_begin + (live ? j : 0);
         const __amdgpu_buffer_rsrc_t xr = live ? xrsrc : none;
         uint16_t* xt = stage(ic);
@@ -261,14 +261,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
         }
     };
 
-    // STAGES-deep pipeline over relative groups t = -(STAGES - 1), ..., groups - 1.  Position d
-    // of the STAGES-fold unrolled body handles t = d - (STAGES - 1) (mod STAGES): it waits until
-    // only the newest STAGES - 2 groups of loads are outstanding (group t has landed for this
-    // wave), meets the other waves at the barrier (group t has landed for all of them, and all
-    // have finished reading the stage of group t - 1), refills that stage with group
-    // t + STAGES - 1, and computes group t from stage (d + 1) % STAGES.  Positions with t < 0
-    // only load.  Keeping the fill inside the loop (no peeled prologue) lets the compiler see
-    // that each stage's reads depend on that stage's loads alone.
+    // STAGES-deep pipeline over positions P = 0, 1, ...: position P loads group
+    // t + STAGES - 1 into stage P % STAGES and computes group t = P - pad - (STAGES - 1) from
+    // stage (P + 1) % STAGES, where pad < STAGES makes the position count a multiple of
+    // STAGES, so the loop has one exit, at the end of its unrolled body (a mid-body exit made
+    // the compiler copy the accumulators at every back-edge).  Before computing, a position
+    // waits until only the newest STAGES - 2 groups of loads are outstanding (group t has landed
+    // for this wave) and meets the other waves at the barrier (group t has landed for all of
+    // them, and all have finished reading the stage about to be refilled).  Positions with
+    // t < 0 only load (group indices below 0 are dead loads).  Keeping the fill inside the loop
+    // (no peeled prologue) lets the compiler see that each stage's reads depend on that stage's
+    // loads alone.
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
@@ -276,7 +279,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     using C1 = std::integral_constant<int, 2 % STAGES>;
     using C2 = std::integral_constant<int, 3 % STAGES>;
     Slot slot0, slot1, slot2;
-    int t = -(STAGES - 1);
+    const int pad = (STAGES - (groups + STAGES - 1) % STAGES) % STAGES;
+    int t = -(STAGES - 1) - pad;
     asm volatile("" : "+s"(t));   // opaque start: the fill iterations are not peeled off the loop
     if (groups > 0) {
 #define W4A16_QMM_STEP(d, I, C, SLOT_IN, SLOT_C)                                                   \
@@ -287,16 +291,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
                 asm volatile("" ::: "memory");                                                   \
             }                                                                                    \
             issue(t + STAGES - 1, I{}, SLOT_IN);                                                 \
-            if (t >= 0) {                                                                        \
-                compute(C{}, SLOT_C);                                                            \
-                if (t + 1 >= groups) break;                                                      \
-            }                                                                                    \
+            if (t >= 0) compute(C{}, SLOT_C);                                                    \
             ++t;                                                                                 \
         }
         for (;;) {
             W4A16_QMM_STEP(0, I0, C0, slot0, (STAGES == 3 ? slot1 : slot1))
             W4A16_QMM_STEP(1, I1, C1, slot1, (STAGES == 3 ? slot2 : slot0))
             W4A16_QMM_STEP(2, I2, C2, slot2, slot0)
+            if (t >= groups) break;
         }
 #undef W4A16_QMM_STEP
     }
@@ -358,9 +360,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 const QmmShape kQmmVariants[kNumQmmVariants] = {
     {128, 1, 4, 2},  // 0: 128 x 128 tile, 4 waves of 128 x 32, two waves per SIMD, 2 stages
-    {64, 1, 4, 2},   // 1:  64 x 128 tile, 4 waves of  64 x 32, three waves per SIMD, 2 stages
+    {64, 1, 4, 2},   // 1:  64 x 128 tile, 4 waves of  64 x 32, four waves per SIMD, 2 stages
     {64, 1, 4, 3},   // 2:  64 x 128 tile, two waves per SIMD, 3 stages
-    {32, 1, 4, 2},   // 3:  32 x 128 tile, 4 waves of 32 x 32, four waves per SIMD, 2 stages (skinny M)
+    {32, 1, 4, 2},   // 3:  32 x 128 tile, 4 waves of 32 x 32, four waves per SIMD, 2 stages
     {32, 1, 4, 3},   // 4:  32 x 128 tile, four waves per SIMD, 3 stages (skinny M)
 };
 
@@ -394,7 +396,7 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint32_t* wq, const 
                       hipStream_t stream) {
     switch (variant) {
         case 0: return launch_qmm_t<128, 1, 4, 2, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 1: return launch_qmm_t<64, 1, 4, 3, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 1: return launch_qmm_t<64, 1, 4, 4, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
         case 2: return launch_qmm_t<64, 1, 4, 2, 3>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
         case 3: return launch_qmm_t<32, 1, 4, 4, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
         case 4: return launch_qmm_t<32, 1, 4, 4, 3>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
@@ -403,8 +405,8 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint32_t* wq, const 
 }
 
 const QmmShape kGateUpVariants[kNumGateUpVariants] = {
-    {32, 1, 4, 2},   // 0:  32 x 128 tile of h (gate and up: 2 x 32 columns per wave), three waves per SIMD
-    {64, 1, 4, 2},   // 1:  64 x 128 tile of h, two waves per SIMD
+    {32, 1, 4, 2},   // 0:  32 x 128 tile of h (gate and up: 2 x 32 columns per wave), four waves per SIMD
+    {64, 1, 4, 2},   // 1:  64 x 128 tile of h, three waves per SIMD
     {128, 1, 4, 2},  // 2: 128 x 128 tile of h, one wave per SIMD
 };
 
@@ -412,8 +414,8 @@ hipError_t launch_gate_up(int variant, const uint16_t* x, const uint32_t* wq_gat
                           const uint16_t* b_gate, const uint32_t* wq_up, const uint16_t* s_up, const uint16_t* b_up,
                           uint16_t* h, float* ws, int M, int N, int K, int split, hipStream_t stream) {
     switch (variant) {
-        case 0: return launch_gate_up_t<32, 3, 2>(x, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K, split, stream);
-        case 1: return launch_gate_up_t<64, 2, 2>(x, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K, split, stream);
+        case 0: return launch_gate_up_t<32, 4, 2>(x, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K, split, stream);
+        case 1: return launch_gate_up_t<64, 3, 2>(x, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K, split, stream);
         case 2: return launch_gate_up_t<128, 1, 2>(x, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K, split, stream);
         default: return hipErrorInvalidValue;
     }
