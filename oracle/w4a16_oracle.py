@@ -43,6 +43,14 @@ Readings where the pages are silent (each one is also listed in the design doc):
   to bf16 (nearest, ties to even); ``q = clamp(rint((W - b) / s), 0, 15)``
   computed from the *rounded* s and b, ties to even; a group with ``s == 0``
   gets ``q = 0``.
+* R8 other bit widths ("Route affine qmv_wide by bit-width and batch size #5"
+  routes affine matvecs by bit width, naming 1- and 2-bit weights; the page
+  gives no format): for ``bits`` in {1, 2, 4, 8} a 32-bit word holds
+  ``32 / bits`` codes, element ``(32/bits)*j + i`` of a row in bits
+  ``bits*i .. bits*i + bits - 1`` of word ``j`` (low first, as R1), ``Wq`` is
+  ``uint32 [N, K*bits/32]``, and the group, scale, bias and R4-R7 are
+  unchanged with ``2**bits - 1`` in place of 15.  ``s * q`` stays exact in
+  fp32 (at most 8 + 8 significand bits).
 """
 
 from __future__ import annotations
@@ -66,7 +74,9 @@ __all__ = [
     "CheckResult",
     "check",
     "quantize_w4g128",
+    "quantize_affine",
     "pack_q",
+    "BITS",
     "brute_force",
     "keep_last_rows",
     "silu_f64",
@@ -75,6 +85,7 @@ __all__ = [
 ]
 
 GROUP = 128
+BITS = (1, 2, 4, 8)          # code widths of reading R8 (4 is the W4 format of R1)
 TOL_REL = 2.0 ** -8
 TOL_MASS = 2.0 ** -10
 
@@ -133,27 +144,35 @@ def f32_to_bf16_rne(values) -> np.ndarray:
 # --------------------------------------------------------------------------- format
 
 
-def unpack_q(wq, K: int) -> np.ndarray:
-    """Packed words ``uint32 [N, K/8]`` -> codes ``uint8 [N, K]`` (readings R1, R2)."""
+def _codes_per_word(bits: int) -> int:
+    if bits not in BITS:
+        raise ValueError(f"bits={bits} is not one of {BITS}")
+    return 32 // bits
+
+
+def unpack_q(wq, K: int, bits: int = 4) -> np.ndarray:
+    """Packed words ``uint32 [N, K*bits/32]`` -> codes ``uint8 [N, K]`` (readings R1, R2, R8)."""
+    per = _codes_per_word(bits)
     w = np.asarray(wq, dtype=np.uint32)
     n_rows, n_words = w.shape
-    if n_words * 8 != K:
-        raise ValueError(f"Wq has {n_words} words per row; K={K} needs {K // 8}")
+    if n_words * per != K:
+        raise ValueError(f"Wq has {n_words} words per row; K={K} at {bits} bits needs {K // per}")
     q = np.empty((n_rows, K), dtype=np.uint8)
-    for i in range(8):
-        # element 8*j + i of every row comes from bits 4i..4i+3 of word j
-        q[:, i::8] = (w >> np.uint32(4 * i)) & np.uint32(0xF)
+    mask = np.uint32((1 << bits) - 1)
+    for i in range(per):
+        # element per*j + i of every row comes from bits bits*i .. bits*i + bits - 1 of word j
+        q[:, i::per] = (w >> np.uint32(bits * i)) & mask
     return q
 
 
-def dequant_f32(wq, scales, biases, K: int, group: int = GROUP) -> np.ndarray:
+def dequant_f32(wq, scales, biases, K: int, group: int = GROUP, bits: int = 4) -> np.ndarray:
     """Dequantized weights ``w[n, k] = f32(f32(s[n,g] * q[n,k]) + b[n,g])`` (reading R4).
 
     Follows the affine form of "Route affine qmv_wide by bit-width and batch
     size #5" and the per-group scale/bias of "Week 2 Day 6: SIMD-Matrix
     Prefill", Task 3.
     """
-    q = unpack_q(wq, K).astype(np.float32)
+    q = unpack_q(wq, K, bits).astype(np.float32)
     s = bf16_to_f32(scales)
     b = bf16_to_f32(biases)
     if s.shape != (q.shape[0], K // group) or b.shape != s.shape:
@@ -165,7 +184,8 @@ def dequant_f32(wq, scales, biases, K: int, group: int = GROUP) -> np.ndarray:
     return np.add(prod, b_k, dtype=np.float32)
 
 
-def reference(x_bits, wq, scales, biases, group: int = GROUP, columns=None, col_chunk: int = 8192):
+def reference(x_bits, wq, scales, biases, group: int = GROUP, columns=None, col_chunk: int = 8192,
+              bits: int = 4):
     """Reference output and absolute mass, both fp64 ``[M, N']`` (readings R4, R5).
 
     ``y_ref = x64 @ w64ᵀ`` and ``A = |x64| @ |w64|ᵀ``, where ``x64`` is the exact
@@ -187,7 +207,7 @@ def reference(x_bits, wq, scales, biases, group: int = GROUP, columns=None, col_
     ax = np.abs(x64)
     for c0 in range(0, cols.size, col_chunk):
         sel = cols[c0:c0 + col_chunk]
-        w64 = dequant_f32(wq[sel], scales[sel], biases[sel], K, group).astype(np.float64)
+        w64 = dequant_f32(wq[sel], scales[sel], biases[sel], K, group, bits).astype(np.float64)
         y[:, c0:c0 + sel.size] = x64 @ w64.T
         A[:, c0:c0 + sel.size] = ax @ np.abs(w64).T
     return y, A
@@ -232,15 +252,18 @@ def check(y_bits, y_ref, A, rel: float = TOL_REL, mass: float = TOL_MASS) -> Che
 # --------------------------------------------------------------------------- quantizer (R7)
 
 
-def pack_q(q) -> np.ndarray:
-    """Codes ``[N, K]`` (0..15) -> words ``uint32 [N, K/8]``: word j holds element 8j+i at bits 4i (R1)."""
+def pack_q(q, bits: int = 4) -> np.ndarray:
+    """Codes ``[N, K]`` (0 .. 2**bits - 1) -> words ``uint32 [N, K*bits/32]``: word j holds
+    element per*j + i at bits bits*i, per = 32 / bits (R1, R8)."""
+    per = _codes_per_word(bits)
     q = np.asarray(q, dtype=np.uint32)
     n_rows, K = q.shape
-    words = np.zeros((n_rows, K // 8), dtype=np.uint32)
-    for j in range(K // 8):
+    mask = np.uint32((1 << bits) - 1)
+    words = np.zeros((n_rows, K // per), dtype=np.uint32)
+    for j in range(K // per):
         acc = np.zeros(n_rows, dtype=np.uint32)
-        for i in range(8):
-            acc |= (q[:, 8 * j + i] & np.uint32(0xF)) << np.uint32(4 * i)
+        for i in range(per):
+            acc |= (q[:, per * j + i] & mask) << np.uint32(bits * i)
         words[:, j] = acc
     return words
 
@@ -250,6 +273,15 @@ def quantize_w4g128(W, group: int = GROUP):
 
     Returns ``(wq uint32 [N, K/8], scales bf16-bits [N, G], biases bf16-bits [N, G])``.
     """
+    return quantize_affine(W, 4, group)
+
+
+def quantize_affine(W, bits: int = 4, group: int = GROUP):
+    """The R7 quantizer at ``bits`` per code (R8): ``2**bits - 1`` levels per group.
+
+    Returns ``(wq uint32 [N, K*bits/32], scales bf16-bits [N, G], biases bf16-bits [N, G])``.
+    """
+    _codes_per_word(bits)
     W = np.asarray(W, dtype=np.float32)
     n_rows, K = W.shape
     if K % group:
@@ -258,13 +290,13 @@ def quantize_w4g128(W, group: int = GROUP):
     q = np.zeros((n_rows, K), dtype=np.uint8)
     s_bits = np.zeros((n_rows, G), dtype=np.uint16)
     b_bits = np.zeros((n_rows, G), dtype=np.uint16)
-    fifteen = np.float32(15.0)
+    levels = np.float32((1 << bits) - 1)
     for n in range(n_rows):
         for g in range(G):
             blk = W[n, g * group:(g + 1) * group]
             mn = np.float32(blk.min())
             mx = np.float32(blk.max())
-            scale = np.float32(np.float32(mx - mn) / fifteen)
+            scale = np.float32(np.float32(mx - mn) / levels)
             sb = f32_to_bf16_rne(np.array([scale], dtype=np.float32))[0]
             bb = f32_to_bf16_rne(np.array([mn], dtype=np.float32))[0]
             s_bits[n, g] = sb
@@ -274,8 +306,8 @@ def quantize_w4g128(W, group: int = GROUP):
             if s32 == 0:
                 continue  # degenerate group: every code is 0, so w = b
             t = np.divide(np.subtract(blk, b32, dtype=np.float32), s32, dtype=np.float32)
-            q[n, g * group:(g + 1) * group] = np.clip(np.rint(t), 0, 15).astype(np.uint8)
-    return pack_q(q), s_bits, b_bits
+            q[n, g * group:(g + 1) * group] = np.clip(np.rint(t), 0, levels).astype(np.uint8)
+    return pack_q(q, bits), s_bits, b_bits
 
 
 # --------------------------------------------------------------------------- brute force
@@ -289,7 +321,7 @@ def _bf16_scalar(bits: int) -> float:
     return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
 
 
-def brute_force(x_bits, wq, scales, biases, group: int = GROUP):
+def brute_force(x_bits, wq, scales, biases, group: int = GROUP, bits: int = 4):
     """Pure-Python loops over (m, n, k); small inputs only.
 
     Every weight is decoded from its word by explicit shifts, dequantized with
@@ -302,11 +334,12 @@ def brute_force(x_bits, wq, scales, biases, group: int = GROUP):
     N = wq.shape[0]
     xs = [[_bf16_scalar(x_bits[m, k]) for k in range(K)] for m in range(M)]
     ws = []
+    per = 32 // bits
     for n in range(N):
         row = []
         for k in range(K):
-            word = int(wq[n, k // 8])
-            code = (word >> (4 * (k % 8))) & 0xF
+            word = int(wq[n, k // per])
+            code = (word >> (bits * (k % per))) & ((1 << bits) - 1)
             s = _bf16_scalar(scales[n, k // group])
             b = _bf16_scalar(biases[n, k // group])
             row.append(_f32_round(_f32_round(s * code) + b))

@@ -10,7 +10,11 @@ exactly representable in bf16, and every ``s*q + b`` is exact in fp32, so the
 fp32 dequantization rounds nothing and the fp64 reference must equal the
 rational result to within its final rounding.
 
-Run: ``python tests/golden/make_golden.py`` (rewrites the JSON next to it).
+It also writes ``worked_example_w{1,2,8}g128.json``: the same construction at the other
+code widths (element ``(32/b)j + i`` of a row in bits ``b*i .. b*i + b - 1`` of word ``j``,
+codes in ``0 .. 2**b - 1``), again from exact rationals only.
+
+Run: ``python tests/golden/make_golden.py`` (rewrites the JSON files next to it).
 """
 
 import json
@@ -28,10 +32,12 @@ def bf16_bits(v: Fraction) -> int:
     return bits >> 16
 
 
-def main():
-    # codes: a closed form that varies with n and k and spans 0..15
-    q = [[(3 * n + 5 * k + (k // 128)) % 16 for k in range(K)] for n in range(N)]
-    words = [[sum(q[n][8 * j + i] << (4 * i) for i in range(8)) for j in range(K // 8)] for n in range(N)]
+def write(bits):
+    per = 32 // bits
+    levels = 1 << bits
+    # codes: a closed form that varies with n and k and spans 0 .. 2**bits - 1
+    q = [[(3 * n + 5 * k + (k // 128)) % levels for k in range(K)] for n in range(N)]
+    words = [[sum(q[n][per * j + i] << (bits * i) for i in range(per)) for j in range(K // per)] for n in range(N)]
     s = [[Fraction(1, 2 ** (4 + n + g)) for g in range(K // GROUP)] for n in range(N)]
     b = [[Fraction(-(n + 1) * (g + 3), 2 ** 5) for g in range(K // GROUP)] for n in range(N)]
     # activations: small dyadic values with a pattern per row
@@ -40,12 +46,19 @@ def main():
           for n in range(N)] for m in range(M)]
     A = [[sum(abs(x[m][k] * (s[n][k // GROUP] * q[n][k] + b[n][k // GROUP])) for k in range(K))
           for n in range(N)] for m in range(M)]
+    if bits == 4:
+        citation = ("No page prints a worked example. Closed-form values computed with exact "
+                    "rationals from the affine W4 group-128 format (tiny-llm 'Week 2 Day 6: "
+                    "SIMD-Matrix Prefill', scope list and Task 3) under the oracle's readings "
+                    "R1-R4 (low-nibble-first packing, [N,K/8] words, [N,K/128] scale/bias).")
+    else:
+        citation = (f"No page prints a worked example. Closed-form values computed with exact "
+                    f"rationals for {bits}-bit affine codes ('Route affine qmv_wide by bit-width and "
+                    f"batch size #5' routes 1- and 2-bit affine matvecs) under the oracle's reading R8 "
+                    f"({per} codes per word, lowest bits first) and R3-R4.")
     out = {
-        "citation": ("No page prints a worked example. Closed-form values computed with exact "
-                     "rationals from the affine W4 group-128 format (tiny-llm 'Week 2 Day 6: "
-                     "SIMD-Matrix Prefill', scope list and Task 3) under the oracle's readings "
-                     "R1-R4 (low-nibble-first packing, [N,K/8] words, [N,K/128] scale/bias)."),
-        "M": M, "K": K, "N": N, "group": GROUP,
+        "citation": citation,
+        "M": M, "K": K, "N": N, "group": GROUP, "bits": bits,
         "x_bf16": [[bf16_bits(v) for v in row] for row in x],
         "wq_u32": words,
         "scales_bf16": [[bf16_bits(v) for v in row] for row in s],
@@ -54,11 +67,16 @@ def main():
         "y_exact": [[f"{v.numerator}/{v.denominator}" for v in row] for row in y],
         "abs_mass_exact": [[f"{v.numerator}/{v.denominator}" for v in row] for row in A],
     }
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "worked_example_w4g128.json")
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), f"worked_example_w{bits}g128.json")
     with open(path, "w") as f:
         json.dump(out, f)
         f.write("\n")
     print("wrote", path)
+
+
+def main():
+    for bits in (4, 1, 2, 8):
+        write(bits)
 
 
 if __name__ == "__main__":

@@ -423,3 +423,167 @@ def test_swiglu_reference_composes_two_projections():
     assert O.check_swiglu(good, g, Ag, u, Au).ok
     bad = O.f32_to_bf16_rne((h * 1.03 + 0.01).astype(np.float32))
     assert not O.check_swiglu(bad, g, Ag, u, Au).ok
+
+
+# ----------------------------------------------------------------------------- other code widths (R8)
+
+def _load_golden_bits(bits):
+    path = os.path.join(os.path.dirname(__file__), "golden", f"worked_example_w{bits}g128.json")
+    with open(path) as f:
+        d = json.load(f)
+    assert d["bits"] == bits
+    x = np.array(d["x_bf16"]).astype(np.uint16)
+    wq = np.array(d["wq_u32"], dtype=np.uint64).astype(np.uint32)
+    s = np.array(d["scales_bf16"]).astype(np.uint16)
+    b = np.array(d["biases_bf16"]).astype(np.uint16)
+    y = [[Fraction(v) for v in row] for row in d["y_exact"]]
+    A = [[Fraction(v) for v in row] for row in d["abs_mass_exact"]]
+    return x, wq, s, b, y, A, np.array(d["codes"])
+
+
+def _bits_pin_worked_example(ref_fn, bits):
+    x, wq, s, b, y_exact, A_exact, _ = _load_golden_bits(bits)
+    try:
+        y, A = ref_fn(x, wq, s, b, bits)
+    except ValueError:
+        return False
+    return (all(Fraction(float(y[m, n])) == y_exact[m][n] for m in range(y.shape[0]) for n in range(y.shape[1]))
+            and all(Fraction(float(A[m, n])) == A_exact[m][n] for m in range(A.shape[0]) for n in range(A.shape[1])))
+
+
+def _bits_pin_identity(ref_fn, bits):
+    """x = identity, s = 1, b = 0: y[m, n] = q[n, m] exactly."""
+    rng = np.random.default_rng(40 + bits)
+    K, N = 256, 24
+    q = rng.integers(0, 1 << bits, (N, K))
+    x = np.where(np.eye(K, dtype=bool), synth.const_bf16(1.0, (K, K)), np.uint16(0))
+    try:
+        y, _ = ref_fn(x, synth.pack_codes(q, bits), synth.const_bf16(1.0, (N, 2)), synth.const_bf16(0.0, (N, 2)), bits)
+    except ValueError:
+        return False
+    return np.array_equal(y, q.T.astype(np.float64))
+
+
+def _bits_pin_max_codes(ref_fn, bits):
+    """Every code 2**bits - 1: y[m, n] = sum_g (s (2**bits - 1) + b) * sum_{k in g} x[m, k]."""
+    rng = np.random.default_rng(50 + bits)
+    M, K, N = 3, 384, 5
+    G = K // 128
+    q = np.full((N, K), (1 << bits) - 1)
+    xi = rng.integers(-4, 5, (M, K))
+    s = (2.0 ** -rng.integers(3, 8, (N, G))).astype(np.float32)
+    b = (-(2.0 ** -rng.integers(2, 6, (N, G)))).astype(np.float32)
+    try:
+        y, _ = ref_fn(synth.to_bf16_bits(xi.astype(np.float32)), synth.pack_codes(q, bits), synth.to_bf16_bits(s),
+                      synth.to_bf16_bits(b), bits)
+    except ValueError:
+        return False
+    X = xi.reshape(M, G, 128).sum(axis=2).astype(np.float64)          # [M, G]
+    expect = X @ (s.astype(np.float64) * ((1 << bits) - 1) + b.astype(np.float64)).T
+    return np.array_equal(y, expect)
+
+
+BITS_PINS = [_bits_pin_worked_example, _bits_pin_identity, _bits_pin_max_codes]
+
+
+def _oracle_bits(x, wq, s, b, bits):
+    return O.reference(x, wq, s, b, bits=bits)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 8])
+@pytest.mark.parametrize("pin", BITS_PINS, ids=lambda p: p.__name__)
+def test_oracle_passes_bits_pin(pin, bits):
+    assert pin(_oracle_bits, bits)
+
+
+def test_unpack_literal_words_other_widths():
+    # 8-bit: bytes low first
+    assert O.unpack_q(np.array([[0x04030201, 0xFF00807F]], dtype=np.uint32), 8, bits=8).tolist() == \
+        [[1, 2, 3, 4, 0x7F, 0x80, 0x00, 0xFF]]
+    # 2-bit: 0b11_10_01_00 repeated = 0xE4E4E4E4 -> 0, 1, 2, 3, 0, 1, 2, 3, ...
+    assert O.unpack_q(np.array([[0xE4E4E4E4]], dtype=np.uint32), 16, bits=2).tolist() == [[0, 1, 2, 3] * 4]
+    # 1-bit: bit i is element i
+    q1 = O.unpack_q(np.array([[0x80000005]], dtype=np.uint32), 32, bits=1)[0].tolist()
+    assert q1 == [1, 0, 1] + [0] * 28 + [1]
+    # 4-bit keeps reading R1
+    assert O.unpack_q(np.array([[0x76543210]], dtype=np.uint32), 8).tolist() == [[0, 1, 2, 3, 4, 5, 6, 7]]
+    with pytest.raises(ValueError):
+        O.unpack_q(np.zeros((1, 4), dtype=np.uint32), 32, bits=3)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 8])
+def test_pack_and_unpack_are_inverse_and_match_the_input_generator(bits):
+    rng = np.random.default_rng(60 + bits)
+    q = rng.integers(0, 1 << bits, (7, 256))
+    w = O.pack_q(q, bits)
+    assert np.array_equal(w, synth.pack_codes(q, bits))
+    assert np.array_equal(O.unpack_q(w, 256, bits), q)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 8])
+def test_reference_matches_brute_force_other_widths(bits):
+    p = synth.random_problem(70 + bits, 3, 5, 256, bits=bits)
+    y, A = O.reference(p["x"], p["wq"], p["scales"], p["biases"], bits=bits)
+    yb, Ab = O.brute_force(p["x"], p["wq"], p["scales"], p["biases"], bits=bits)
+    assert np.allclose(y, yb, rtol=0, atol=1e-12 * max(1.0, float(np.abs(Ab).max())))
+    assert np.allclose(A, Ab, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 8])
+def test_quantization_round_trip_bound_other_widths(bits):
+    rng = np.random.default_rng(80 + bits)
+    N, K = 64, 512
+    W = np.float32(synth.W_STD) * rng.standard_normal((N, K)).astype(np.float32)
+    wq, s, b = synth.quantize(W, bits=bits)
+    wq_o, s_o, b_o = O.quantize_affine(W, bits)           # the oracle's own loop quantizer agrees
+    assert np.array_equal(wq, wq_o) and np.array_equal(s, s_o) and np.array_equal(b, b_o)
+    w_hat = O.dequant_f32(wq, s, b, K, bits=bits).astype(np.float64)
+    err = np.abs(W.astype(np.float64) - w_hat).reshape(N, K // 128, 128)
+    assert np.all(err <= _roundtrip_bound(W, s, b)[:, :, None])
+
+
+def _bits_mutant(kind):
+    """A copy of the oracle's width-generic unpack with one plausible mistake."""
+    def unpack(wq, K, bits):
+        per = 32 // bits
+        w = np.asarray(wq, dtype=np.uint32)
+        if kind == "fixed_eight_per_word":
+            per = 8
+        if w.shape[1] * per != K:
+            raise ValueError("shape")
+        q = np.empty((w.shape[0], K), dtype=np.uint8)
+        mask = (1 << bits) - 1 if kind != "four_bit_mask" else 0xF
+        for i in range(per):
+            shift = bits * i if kind != "high_bits_first" else 32 - bits * (i + 1)
+            if kind == "nibble_stride":
+                shift = (4 * i) % 32
+            q[:, i::per] = (w >> np.uint32(shift)) & np.uint32(mask)
+        return q
+
+    def ref(x, wq, s, b, bits):
+        K = np.asarray(x).shape[1]
+        q = unpack(wq, K, bits).astype(np.float32)
+        g = np.arange(K) // 128
+        w = (O.bf16_to_f32(s)[:, g] * q + O.bf16_to_f32(b)[:, g]).astype(np.float64)
+        x64 = O.bf16_to_f64(x)
+        return x64 @ w.T, np.abs(x64) @ np.abs(w).T
+    return ref
+
+
+BITS_MUTANTS = ["fixed_eight_per_word", "four_bit_mask", "high_bits_first", "nibble_stride"]
+
+
+@pytest.mark.parametrize("bits", [1, 2, 8])
+@pytest.mark.parametrize("kind", BITS_MUTANTS)
+def test_bits_pins_catch_planted_mistakes(kind, bits):
+    if kind == "four_bit_mask" and bits == 4:
+        pytest.skip("not a mistake at 4 bits")
+    failed = [p.__name__ for p in BITS_PINS if not p(_bits_mutant(kind), bits)]
+    assert failed, f"planted mistake {kind!r} at {bits} bits passed every pin"
+
+
+def test_bits_mutant_copy_is_faithful_without_a_mistake():
+    # the mutant harness itself, with no mistake planted, passes every pin (so failures above
+    # come from the planted mistakes)
+    for bits in (1, 2, 8):
+        assert all(p(_bits_mutant("none"), bits) for p in BITS_PINS)

@@ -88,21 +88,26 @@ def from_bf16_bits(bits) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def pack_codes(q) -> np.ndarray:
-    """Codes ``[N, K]`` in 0..15 -> ``uint32 [N, K/8]``, low nibble first."""
+def pack_codes(q, bits: int = 4) -> np.ndarray:
+    """Codes ``[N, K]`` in 0 .. 2**bits - 1 -> ``uint32 [N, K*bits/32]``, lowest bits first
+    (``bits`` in 1, 2, 4, 8)."""
+    if bits not in (1, 2, 4, 8):
+        raise ValueError(f"bits={bits} is not one of 1, 2, 4, 8")
+    per = 32 // bits
     q = np.asarray(q, dtype=np.uint32)
     n_rows, K = q.shape
-    if K % 8:
-        raise ValueError("K must be a multiple of 8")
-    q8 = q.reshape(n_rows, K // 8, 8)
-    shifts = (np.arange(8, dtype=np.uint32) * np.uint32(4))[None, None, :]
-    return np.bitwise_or.reduce(q8 << shifts, axis=2).astype(np.uint32)
+    if K % per:
+        raise ValueError(f"K must be a multiple of {per}")
+    qw = q.reshape(n_rows, K // per, per)
+    shifts = (np.arange(per, dtype=np.uint32) * np.uint32(bits))[None, None, :]
+    return np.bitwise_or.reduce(qw << shifts, axis=2).astype(np.uint32)
 
 
-def quantize(W, group: int = GROUP):
-    """Quantize fp32 weights ``[N, K]`` with the recipe above (vectorized over groups).
+def quantize(W, group: int = GROUP, bits: int = 4):
+    """Quantize fp32 weights ``[N, K]`` with the recipe above (vectorized over groups), with
+    ``2**bits - 1`` levels per group.
 
-    Returns ``(wq uint32 [N, K/8], scales uint16 [N, K/group], biases uint16 [N, K/group])``.
+    Returns ``(wq uint32 [N, K*bits/32], scales uint16 [N, K/group], biases uint16 [N, K/group])``.
     """
     W = np.ascontiguousarray(W, dtype=np.float32)
     n_rows, K = W.shape
@@ -111,7 +116,8 @@ def quantize(W, group: int = GROUP):
     Wg = W.reshape(n_rows, K // group, group)
     mn = Wg.min(axis=2)
     mx = Wg.max(axis=2)
-    scale = np.divide(np.subtract(mx, mn, dtype=np.float32), np.float32(15.0), dtype=np.float32)
+    levels = (1 << bits) - 1
+    scale = np.divide(np.subtract(mx, mn, dtype=np.float32), np.float32(levels), dtype=np.float32)
     s_bits = to_bf16_bits(scale)
     b_bits = to_bf16_bits(mn)
     s = from_bf16_bits(s_bits)[:, :, None]
@@ -119,8 +125,8 @@ def quantize(W, group: int = GROUP):
     with np.errstate(divide="ignore", invalid="ignore"):
         t = np.divide(np.subtract(Wg, b, dtype=np.float32), s, dtype=np.float32)
     t = np.where(s == 0, np.float32(0), t)
-    q = np.clip(np.rint(t), 0, 15).astype(np.uint8).reshape(n_rows, K)
-    return pack_codes(q), s_bits, b_bits
+    q = np.clip(np.rint(t), 0, levels).astype(np.uint8).reshape(n_rows, K)
+    return pack_codes(q, bits), s_bits, b_bits
 
 
 def weights(cfg: int, shape: int, N: int, K: int, group: int = GROUP):
@@ -154,17 +160,18 @@ def problem(cfg: int, shape_name: str, M: int | None = None):
     return {"x": x, "wq": wq, "scales": s, "biases": b, "M": M, "N": N, "K": K}
 
 
-def random_problem(seed: int, M: int, N: int, K: int, group: int = GROUP):
-    """Inputs of an arbitrary shape from the same recipe, for tests (stream ``[0, seed, role, chunk]``)."""
-    wq = np.empty((N, K // 8), dtype=np.uint32)
+def random_problem(seed: int, M: int, N: int, K: int, group: int = GROUP, bits: int = 4):
+    """Inputs of an arbitrary shape from the same recipe, for tests (stream ``[0, seed, role, chunk]``);
+    ``bits`` per code (1, 2, 4, 8)."""
+    wq = np.empty((N, K * bits // 32), dtype=np.uint32)
     s = np.empty((N, K // group), dtype=np.uint16)
     b = np.empty((N, K // group), dtype=np.uint16)
     for chunk, r0 in enumerate(range(0, N, ROW_CHUNK)):
         r1 = min(N, r0 + ROW_CHUNK)
         W = np.float32(W_STD) * rng(0, seed, ROLE_W, chunk).standard_normal((r1 - r0, K), dtype=np.float32)
-        wq[r0:r1], s[r0:r1], b[r0:r1] = quantize(W, group)
+        wq[r0:r1], s[r0:r1], b[r0:r1] = quantize(W, group, bits)
     x = to_bf16_bits(rng(0, seed, ROLE_X).standard_normal((M, K), dtype=np.float32))
-    return {"x": x, "wq": wq, "scales": s, "biases": b, "M": M, "N": N, "K": K}
+    return {"x": x, "wq": wq, "scales": s, "biases": b, "M": M, "N": N, "K": K, "bits": bits}
 
 
 def const_bf16(value: float, shape) -> np.ndarray:
