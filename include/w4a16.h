@@ -172,6 +172,39 @@ int w4a16_gate_up_swiglu(const uint16_t* x, const uint32_t* wq_gate, const uint1
 int w4a16_gate_up_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, int32_t num_cus,
                        w4a16_plan_t* out);
 
+/* Kernel choice of qmv_affine ("Route affine qmv_wide by bit-width and batch size #5"). */
+enum w4a16_qmv_mode {
+    W4A16_QMV_POLICY = 0,      /* route by (bits, M) as measured on MI355X                         */
+    W4A16_QMV_AMORTIZED = 1,   /* row-amortized: one unpacked group feeds all M rows (matrix core)  */
+    W4A16_QMV_PER_ROW = 2,     /* per-row dot products, M <= 2                                      */
+    W4A16_QMV_FAMILIES = 3     /* bits = 4 only: the kernel families and policy of qmv_w4a16        */
+};
+
+/*
+ * Affine matvec for decode rows (1 <= M <= 8) at bits = 1, 2, 4 or 8 per code, routed by
+ * (bits, M) between a per-row kernel and a row-amortized one ("Route affine qmv_wide by
+ * bit-width and batch size #5" routes 1-bit and small M per row and larger M row-amortized).
+ * Measured on MI355X the row-amortized kernel leads at every width and M, so the policy takes
+ * it, and at bits = 4 the policy is qmv_w4a16's.  Layouts as above with wq uint32 [N, K * bits / 32]:
+ * element (32/bits)*j + i of a row in bits bits*i .. bits*i + bits - 1 of word j (lowest bits
+ * first); scales and biases bf16 [N, K/128]; w = s * q + b.  mode: enum w4a16_qmv_mode.  Needs no
+ * workspace.  Same preconditions, ownership and errors as qmv_w4a16; bits outside {1, 2, 4, 8},
+ * M > 8, an unknown mode, the per-row mode with M > 2, or W4A16_QMV_FAMILIES with bits != 4 return
+ * W4A16_ERR_UNSUPPORTED.
+ */
+int qmv_affine(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+               uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, int32_t mode,
+               void* stream);
+
+/*
+ * Plan of qmv_affine (path = W4A16_PATH_QMV; variant = the chosen enum w4a16_qmv_mode; with
+ * W4A16_QMV_FAMILIES the tile and grid fields are those of w4a16_plan's matvec plan).  num_cus
+ * as in w4a16_plan.  Pure host arithmetic.  Errors as qmv_affine, plus W4A16_ERR_NULL for `out`;
+ * W4A16_QMV_FAMILIES with bits != 4 returns W4A16_ERR_UNSUPPORTED.
+ */
+int qmv_affine_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, int32_t mode,
+                    int32_t num_cus, w4a16_plan_t* out);
+
 #ifdef __cplusplus
 }
 #endif

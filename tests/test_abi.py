@@ -222,3 +222,48 @@ def test_gate_up_validates_before_launch(lib):
     assert call(wu=ODD) == 4 and call(su=A16 + 1) == 4 and call(h=A16 + 1) == 4
     with pytest.raises(ValueError):
         w4.w4a16_gate_up_plan(4, 16, 100, 128, 0, CUS)
+
+
+# ------------------------------------------------------------------------------ width-generic matvec
+
+def test_qmv_affine_plans():
+    # measured routing: the row-amortized kernel at 1, 2 and 8 bits; qmv_w4a16's policy at 4 bits
+    for bits in w4.BITS:
+        for M in range(1, 9):
+            for N, K in [(4000, 2560), (151936, 2560), (2560, 9728)]:
+                p = w4.qmv_affine_plan(M, N, K, bits, w4.QMV_POLICY, 128, CUS)
+                assert p["path"] == w4.PATH_QMV and p["workspace_bytes"] == 0
+                if bits == 4:
+                    q = plan(M, N, K, path=w4.PATH_QMV)
+                    assert p["variant"] == w4.QMV_FAMILIES
+                    assert (p["tile_n"], p["grid_x"], p["k_waves"]) == (q["tile_n"], q["grid_x"], q["k_waves"])
+                else:
+                    assert p["variant"] == w4.QMV_AMORTIZED
+                    assert p["tile_n"] == 16 and p["grid_x"] == -(-N // 16)
+        for mode in (w4.QMV_AMORTIZED, w4.QMV_PER_ROW):
+            assert w4.qmv_affine_plan(2, 4000, 2560, bits, mode, 128, CUS)["variant"] == mode
+
+
+@pytest.mark.parametrize("args", [
+    (1, 16, 256, 3, 0), (1, 16, 256, 16, 0), (1, 16, 256, 0, 0),   # widths outside {1, 2, 4, 8}
+    (9, 16, 256, 4, 0),                                            # more than eight rows
+    (3, 16, 256, 4, w4.QMV_PER_ROW),                               # per-row kernel: M <= 2
+    (1, 16, 256, 2, w4.QMV_FAMILIES),                              # the 4-bit families: bits = 4
+    (1, 16, 256, 4, 4), (1, 16, 256, 4, -1),                       # unknown mode
+])
+def test_qmv_affine_rejects_unsupported(lib, args):
+    M, N, K, bits, mode = args
+    with pytest.raises(NotImplementedError):
+        w4.qmv_affine_plan(M, N, K, bits, mode, 128, CUS)
+    assert lib.qmv_affine(A16, A16, A16, A16, A16, M, N, K, 128, bits, mode, None) == 6
+
+
+def test_qmv_affine_validates_before_launch(lib):
+    def call(x=A16, wq=A16, s=A16, b=A16, y=A16, M=2, N=16, K=256, group=128, bits=2, mode=0):
+        return lib.qmv_affine(x, wq, s, b, y, M, N, K, group, bits, mode, None)
+
+    assert call(x=None) == 1 and call(wq=None) == 1 and call(s=None) == 1 and call(b=None) == 1 and call(y=None) == 1
+    assert call(M=0) == 2 and call(N=-1) == 2 and call(K=100) == 2 and call(K=2 ** 20 + 128) == 2
+    assert call(group=64) == 3
+    assert call(x=ODD) == 4 and call(wq=ODD) == 4 and call(s=A16 + 1) == 4 and call(y=A16 + 1) == 4
+    assert lib.qmv_affine_plan(1, 16, 256, 128, 4, 0, CUS, None) == 1

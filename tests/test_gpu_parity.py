@@ -80,7 +80,7 @@ def test_identity_unpack_is_bit_exact_qmm(lib, split):
     assert np.array_equal(y, expect), "nibble order / indexing mismatch on the matrix path"
 
 
-@pytest.mark.parametrize("N", [96, 24600])        # 16-column K-split kernel / persistent wide kernel
+@pytest.mark.parametrize("N", [96, 24600])        # row-amortized kernel / persistent wide kernel
 def test_identity_unpack_is_bit_exact_qmv(lib, N):
     q, p = identity_problem(N=N)
     expect = synth.to_bf16_bits(q.T.astype(np.float32))
@@ -90,11 +90,12 @@ def test_identity_unpack_is_bit_exact_qmv(lib, N):
         assert np.array_equal(y, expect[r0:r0 + 8]), f"rows {r0}..{r0 + 7}"
 
 
-@pytest.mark.parametrize("path,N", [("qmv", 160), ("qmv", 6150), ("qmv", 8200), ("qmv", 24600), ("qmm", 160)])
-def test_small_integer_sums_are_exact(lib, path, N):
+@pytest.mark.parametrize("path,N,K", [("qmv", 160, 512), ("qmv", 6150, 512), ("qmv", 300, 8192), ("qmv", 16400, 512),
+                                      ("qmv", 24600, 512), ("qmm", 160, 512)])
+def test_small_integer_sums_are_exact(lib, path, N, K):
+    # qmv cases cover the row-amortized, dequantizing K-split, 64-column and wide kernels
     rng = np.random.default_rng(8)
     M = 8 if path == "qmv" else 40
-    K = 512
     q = rng.integers(0, 16, (N, K))
     xi = np.zeros((M, K), dtype=np.int64)
     for m in range(M):                 # at most 17 ones per row keeps every sum <= 255
@@ -140,19 +141,23 @@ def test_all_zero_codes(lib, path):
 
 # ---------------------------------------------------------------------------------- qmv families
 
-# (N, K, M, kernel the policy picks): 0 = 16-column workgroups splitting K four ways, 1 = 32-column
-# workgroups, 2 = 64-column workgroups, 3 = persistent wide kernel (activations and their group
-# sums staged in LDS once, one wave per 16-column block)
+# (N, K, M, kernel the policy picks): 0 = 16-column dequantizing workgroups splitting K four ways,
+# 1 = 64-column workgroups, 2 = persistent wide kernel (activations and their group sums staged
+# in LDS once, one wave per 16-column block), 3 = row-amortized 16-column workgroups (exact codes
+# on the matrix core, s * P + b * X per group)
 QMV_FAMILY_CASES = [
-    (4000, 256, 3, 0),       # ragged N
-    (6150, 384, 1, 1),       # odd group count, ragged N
-    (8200, 384, 8, 2),
-    (24600, 256, 1, 3),      # one group pair per block: every step ends a block
-    (24600, 512, 5, 3),      # ragged N and M
-    (30010, 1024, 8, 3),     # eight rows
-    (24600, 384, 2, 2),      # odd group count: the wide kernel does not apply
-    (9728, 4096, 4, 3),      # wide from 512 blocks once K >= 4096
-    (24600, 9728, 8, 2),     # activations too large for the wide kernel's LDS
+    (4000, 256, 3, 3),       # ragged N
+    (6150, 384, 1, 3),       # odd group count, ragged N
+    (2600, 8192, 3, 0),      # 64 groups: the dequantizing K-split kernel
+    (1000, 9728, 8, 0),      # long K, ragged N
+    (16390, 384, 8, 1),      # 1025 blocks, odd group count
+    (24600, 256, 1, 2),      # one group pair per block: every step ends a block
+    (24600, 512, 5, 2),      # ragged N and M
+    (30010, 1024, 8, 2),     # eight rows
+    (24600, 384, 2, 1),      # odd group count: the wide kernel does not apply
+    (16400, 4096, 4, 2),     # wide from 1024 blocks once K >= 4096
+    (9728, 4096, 4, 3),      # 608 blocks at K = 4096: row-amortized
+    (24600, 9728, 8, 1),     # activations too large for the wide kernel's LDS
 ]
 
 
@@ -170,8 +175,10 @@ def test_qmv_kernel_families(lib, N, K, M, variant):
 # (M, N, K, tile_m the policy picks): 8 < M <= 16 runs the matvec kernels (tile_m 16), above
 # that 32-row MFMA tiles with split-K (tile_m 32)
 SKINNY_CASES = [
-    (9, 4000, 256, 16),        # 16-column K-split matvec, ragged N
-    (16, 8200, 384, 16),       # 64-column K-split matvec, odd group count
+    (9, 4000, 256, 16),        # row-amortized matvec, ragged N
+    (16, 8200, 384, 16),       # row-amortized matvec, odd group count
+    (12, 2600, 8192, 16),      # long K above eight rows: row-amortized
+    (10, 16400, 384, 16),      # 64-column matvec
     (12, 24600, 512, 16),      # wide matvec at 12 rows
     (16, 24600, 2048, 32),     # the wide matvec's activation tile would be too large: tiles
     (17, 1000, 2560, 32),      # ragged N, split-K (8 tiles)

@@ -12,6 +12,8 @@ Tensor conventions (all on the GPU, contiguous):
     biases   torch.bfloat16 [N, K/128]
     y        torch.bfloat16 [M, N]
 
+``qmv_affine`` takes codes of 1, 2, 4 or 8 bits: ``wq`` int32 [N, K*bits/32], lowest bits first.
+
 ``linear(..., logits_to_keep=k)`` is the model-level entry: it projects only the last ``k``
 rows (a view, no copy) before the projection, as tiny-llm's "Week 2 Day 6: SIMD-Matrix
 Prefill", Task 4 does before the vocabulary head; ``k = 0`` projects every row.
@@ -28,11 +30,14 @@ __all__ = [
     "load", "lib_path", "w4a16_abi_version", "w4a16_status_string", "w4a16_plan", "w4a16_workspace_bytes",
     "qmv_w4a16", "qmm_w4a16", "w4a16_linear", "linear", "W4A16Error", "declared_symbols", "PreparedLinear",
     "w4a16_gate_up_plan", "w4a16_gate_up_swiglu", "PreparedGateUp",
+    "qmv_affine", "qmv_affine_plan", "QMV_POLICY", "QMV_AMORTIZED", "QMV_PER_ROW", "QMV_FAMILIES", "BITS",
 ]
 
 GROUP = 128
 W4A16_OK = 0
 PATH_AUTO, PATH_QMV, PATH_QMM, PATH_SKINNY, PATH_GATE_UP = 0, 1, 2, 3, 4
+QMV_POLICY, QMV_AMORTIZED, QMV_PER_ROW, QMV_FAMILIES = 0, 1, 2, 3
+BITS = (1, 2, 4, 8)
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG_DIR), "include", "w4a16.h")
@@ -85,6 +90,10 @@ def load():
     lib.w4a16_gate_up_swiglu.restype = ctypes.c_int
     lib.w4a16_gate_up_swiglu.argtypes = [u16p, u32p, u16p, u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, i32,
                                          vp, ctypes.c_size_t, vp]
+    lib.qmv_affine_plan.restype = ctypes.c_int
+    lib.qmv_affine_plan.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(Plan)]
+    lib.qmv_affine.restype = ctypes.c_int
+    lib.qmv_affine.argtypes = [u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, i32, i32, vp]
     _LIB = lib
     return lib
 
@@ -138,6 +147,13 @@ def w4a16_gate_up_plan(M: int, N: int, K: int, group: int = GROUP, split_k: int 
     return p.as_dict()
 
 
+def qmv_affine_plan(M: int, N: int, K: int, bits: int, mode: int = QMV_POLICY, group: int = GROUP,
+                    num_cus: int = 0) -> dict:
+    p = Plan()
+    _raise_for(load().qmv_affine_plan(M, N, K, group, bits, mode, num_cus, ctypes.byref(p)), "qmv_affine_plan")
+    return p.as_dict()
+
+
 # ------------------------------------------------------------------------------------ tensors
 
 
@@ -160,7 +176,7 @@ def _check(t, name, dtype, shape):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _operands(x, wq, scales, biases, y):
+def _operands(x, wq, scales, biases, y, bits: int = 4):
     torch = _torch()
     if x.dim() != 2 or wq.dim() != 2:
         raise ValueError("x and wq must be 2-D")
@@ -169,7 +185,7 @@ def _operands(x, wq, scales, biases, y):
     if K % GROUP:
         raise ValueError(f"K={K} must be a multiple of {GROUP}")
     _check(x, "x", torch.bfloat16, (M, K))
-    _check(wq, "wq", torch.int32, (N, K // 8))
+    _check(wq, "wq", torch.int32, (N, K * bits // 32))
     _check(scales, "scales", torch.bfloat16, (N, K // GROUP))
     _check(biases, "biases", torch.bfloat16, (N, K // GROUP))
     devs = {t.device for t in (x, wq, scales, biases)}
@@ -206,6 +222,19 @@ def qmv_w4a16(x, wq, scales, biases, y=None, stream=None):
     st = load().qmv_w4a16(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(),
                           M, N, K, GROUP, _stream(stream, x.device))
     _raise_for(st, "qmv_w4a16")
+    return y
+
+
+def qmv_affine(x, wq, scales, biases, bits: int, y=None, mode: int = QMV_POLICY, stream=None):
+    """Decode-row matvec (1 <= M <= 8) over ``bits``-bit affine codes (1, 2, 4 or 8; ``wq`` int32
+    ``[N, K * bits / 32]``, lowest bits first), routed by (bits, M) unless ``mode`` forces the
+    row-amortized or the per-row kernel.  Returns y."""
+    if bits not in BITS:
+        raise ValueError(f"bits={bits} must be one of {BITS}")
+    M, N, K, y = _operands(x, wq, scales, biases, y, bits)
+    st = load().qmv_affine(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(),
+                           M, N, K, GROUP, bits, mode, _stream(stream, x.device))
+    _raise_for(st, "qmv_affine")
     return y
 
 

@@ -20,6 +20,8 @@ constexpr int64_t kSkinnyMaxRows = 32;    // rows served by the skinny path
 constexpr int64_t kQmvKernelRows = 16;    // rows one matvec MFMA operand covers
 // LDS a wide-kernel workgroup may use on the skinny path (two workgroups per compute unit)
 constexpr size_t kQmvWideSkinnyLds = 80 * 1024;
+constexpr int64_t kQmvPerRowMaxRows = 2;   // rows the per-row width-generic kernel serves
+constexpr int kQmvBitsWaves = 4;           // waves splitting K in the width-generic kernels
 constexpr int kSplitMinGroups = 4;        // fewest groups one split-K slice may own
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
 // Largest K: keeps every per-lane buffer offset of the kernels (at most 256 K bytes past a
@@ -65,21 +67,23 @@ int check_buffers(const uint16_t* x, const uint32_t* wq, const uint16_t* s, cons
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
-    // Measured on MI355X (K = 2560 and 4096, M = 1 and 4): up to 4096 columns the 16-column
-    // workgroups whose four waves split K are fastest; 32-column ones around 6144 columns and
-    // 64-column ones up to about 16k; from 24k columns (or 9728 at K = 4096) the persistent wide
+    // Measured on MI355X (K = 1024 .. 9728, N = 1024 .. 151936, M = 1 .. 16, random data): below
+    // 16k columns the row-amortized kernel (exact codes on the matrix core, s * P + b * X per
+    // group) leads by 5-22%, except for long K (64 groups or more) at up to 8 rows, where the
+    // 16-column dequantizing kernel whose four waves split K leads by 5-20%; around 16k columns
+    // the 64-column kernel leads; from 24k columns (16k at 32 groups or more) the persistent wide
     // kernel, which streams whole blocks per wave, wins by 1.4x on the 151936-column head.
     const int64_t blocks16 = ceil_div(N, 16);
     const int64_t G = K / W4A16_GROUP;
     int variant;
-    if (qmv_wide_fits(static_cast<int>(M), static_cast<int>(K)) && (blocks16 >= 1536 || (blocks16 >= 512 && G >= 32)))
+    if (qmv_wide_fits(static_cast<int>(M), static_cast<int>(K)) && (blocks16 >= 1536 || (blocks16 >= 1024 && G >= 32)))
         variant = kQmvWideVariant;
-    else if (blocks16 >= 512)
-        variant = 2;
-    else if (blocks16 >= 384)
+    else if (blocks16 >= 1024)
         variant = 1;
-    else
+    else if (G >= 64 && M <= kQmvMaxRows)
         variant = 0;
+    else
+        variant = kQmvAmortizedVariant;
     const QmvShape& v = kQmvVariants[variant];
     p->path = W4A16_PATH_QMV;
     p->tile_m = 16;
@@ -100,7 +104,6 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
     p->k_waves = v.kw;
     p->variant = variant;
     p->workspace_bytes = 0;
-    (void)M;
 }
 
 // skinny: 32-row tiles and the skinny split rule (rows 17..32, or a wide head at 9..16 rows)
@@ -303,6 +306,69 @@ int run_gate_up(const uint16_t* x, const uint32_t* wq_g, const uint16_t* s_g, co
     return to_status(launch_splitk_reduce_glu(ws, h, M * N, p.split_k, s));
 }
 
+// Width-generic matvec: bits in {1, 2, 4, 8}, M <= 8.  Routing by (bits, M), measured on
+// MI355X (K = 2560 .. 9728, N = 1024 .. 151936, M = 1 .. 8, random data): the row-amortized
+// kernel is never more than 7% behind the per-row one and up to 35% ahead of it (the 151936-
+// column head), at every width and row count, so the policy takes it; at 4 bits the policy is
+// that of qmv_w4a16, whose kernel families include the same row-amortized kernel.
+bool bits_ok(int32_t bits) { return bits == 1 || bits == 2 || bits == 4 || bits == 8; }
+
+int plan_qmv_affine(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, int32_t mode, int32_t num_cus,
+                    w4a16_plan_t* p) {
+    if (!p) return W4A16_ERR_NULL;
+    int st = check_shape(M, N, K, group);
+    if (st != W4A16_OK) return st;
+    if (!bits_ok(bits) || M > kQmvMaxRows || mode < W4A16_QMV_POLICY || mode > W4A16_QMV_FAMILIES)
+        return W4A16_ERR_UNSUPPORTED;
+    if (mode == W4A16_QMV_PER_ROW && M > kQmvPerRowMaxRows) return W4A16_ERR_UNSUPPORTED;
+    if (mode == W4A16_QMV_FAMILIES && bits != 4) return W4A16_ERR_UNSUPPORTED;
+    int32_t cus = num_cus;
+    if (cus <= 0) {
+        st = query_num_cus(&cus);
+        if (st != W4A16_OK) return st;
+    }
+    if (mode == W4A16_QMV_POLICY) mode = bits == 4 ? W4A16_QMV_FAMILIES : W4A16_QMV_AMORTIZED;
+    if (mode == W4A16_QMV_FAMILIES) {
+        plan_qmv(M, N, K, cus, p);
+        p->num_cus = cus;
+        p->variant = mode;
+        return W4A16_OK;
+    }
+    p->path = W4A16_PATH_QMV;
+    p->tile_m = mode == W4A16_QMV_PER_ROW ? static_cast<int32_t>(kQmvPerRowMaxRows) : static_cast<int32_t>(kQmvKernelRows);
+    p->tile_n = 16;
+    p->tile_k = W4A16_GROUP;
+    p->grid_x = static_cast<int32_t>(ceil_div(N, 16));
+    p->grid_y = 1;
+    p->grid_z = 1;
+    p->block_threads = 64 * kQmvBitsWaves;
+    p->split_k = 1;
+    p->k_waves = kQmvBitsWaves;
+    p->num_cus = cus;
+    p->variant = mode;
+    p->workspace_bytes = 0;
+    return W4A16_OK;
+}
+
+int run_qmv_affine(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b, uint16_t* y,
+                   int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, int32_t mode, void* stream) {
+    int st = check_shape(M, N, K, group);
+    if (st != W4A16_OK) return st;
+    st = check_buffers(x, wq, s, b, y);
+    if (st != W4A16_OK) return st;
+    w4a16_plan_t p;
+    st = plan_qmv_affine(M, N, K, group, bits, mode, 0, &p);
+    if (st != W4A16_OK) return st;
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (p.variant == W4A16_QMV_FAMILIES) {
+        plan_qmv(M, N, K, p.num_cus, &p);
+        return to_status(launch_qmv(p.variant, x, wq, s, b, y, m, n, k, hs));
+    }
+    return to_status(launch_qmv_bits(bits, p.variant == W4A16_QMV_PER_ROW ? kQmvBitsRows : kQmvBitsMatrix, x, wq, s,
+                                     b, y, m, n, k, hs));
+}
+
 }  // namespace
 
 extern "C" {
@@ -359,6 +425,16 @@ int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, 
                  int64_t M, int64_t N, int64_t K, int32_t group, void* workspace, size_t workspace_bytes,
                  void* stream) {
     return run_qmm(x, wq, scales, biases, y, M, N, K, group, W4A16_PATH_AUTO, 0, workspace, workspace_bytes, stream);
+}
+
+int qmv_affine_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, int32_t mode, int32_t num_cus,
+                    w4a16_plan_t* out) {
+    return plan_qmv_affine(M, N, K, group, bits, mode, num_cus, out);
+}
+
+int qmv_affine(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, uint16_t* y,
+               int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, int32_t mode, void* stream) {
+    return run_qmv_affine(x, wq, scales, biases, y, M, N, K, group, bits, mode, stream);
 }
 
 int w4a16_gate_up_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, int32_t num_cus,

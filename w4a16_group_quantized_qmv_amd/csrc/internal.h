@@ -19,7 +19,10 @@ constexpr int kNumQmvVariants = 4;
 extern const QmvShape kQmvVariants[kNumQmvVariants];
 
 // The wide (persistent) qmv instance: 16-column blocks, 4-wave workgroups, 2 LDS stages.
-constexpr int kQmvWideVariant = 3;
+constexpr int kQmvWideVariant = 2;
+// The row-amortized kernel of the width-generic matvec at 4 bits (16 columns, 4 waves split K):
+// exact integer codes on the matrix core and y += s * P + b * X per group.
+constexpr int kQmvAmortizedVariant = 3;
 constexpr int kQmvWideStages = 2;
 // Its LDS: per wave and stage one 2 KB block of codes plus 512 bytes of scales and biases
 // (with 1 KB allowed for the kernel's small placeholder objects); dynamically the permuted
@@ -67,6 +70,12 @@ hipError_t launch_gate_up(int variant, const uint16_t* x, const uint32_t* wq_gat
                           uint16_t* h, float* ws, int M, int N, int K, int split, hipStream_t stream);
 // h[i] = bf16(silu(sum_z ws[0][z][i]) * sum_z ws[1][z][i]), slices summed in order.
 hipError_t launch_splitk_reduce_glu(const float* ws, uint16_t* h, int64_t MN, int split, hipStream_t stream);
+
+// Width-generic affine matvec (1, 2, 4 or 8 bits per code, M <= 8): row-amortized on the
+// matrix core (mode kQmvBitsMatrix) or per row with dot products (kQmvBitsRows, M <= 2).
+constexpr int kQmvBitsMatrix = 0, kQmvBitsRows = 1;
+hipError_t launch_qmv_bits(int bits, int mode, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                           const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream);
 
 // y[i] = bf16(sum_{z < split} ws[z][i]) summed in slice order.
 hipError_t launch_splitk_reduce(const float* ws, uint16_t* y, int64_t MN, int split, hipStream_t stream);

@@ -481,9 +481,9 @@ __global__ __launch_bounds__(64 * W) void qmv_wide_kernel(
 
 const QmvShape kQmvVariants[kNumQmvVariants] = {
     {1, 1, 4},   // 0: 16 columns per workgroup, 4 waves split K
-    {1, 2, 2},   // 1: 32 columns per workgroup, 2 waves split K
-    {2, 2, 2},   // 2: 64 columns per workgroup, 2 waves split K
-    {1, 4, 1},   // 3: wide: persistent, 16-column blocks, 4-wave workgroups, 2 LDS stages
+    {2, 2, 2},   // 1: 64 columns per workgroup, 2 waves split K
+    {1, 4, 1},   // 2: wide: persistent, 16-column blocks, 4-wave workgroups, 2 LDS stages
+    {1, 1, 4},   // 3: row-amortized (width-generic kernel at 4 bits), 16 columns, 4 waves split K
 };
 
 template <int CB, int WN, int KW>
@@ -550,9 +550,9 @@ hipError_t launch_qmv(int variant, const uint16_t* x, const uint32_t* wq, const 
                       const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream) {
     switch (variant) {
         case 0: return launch_qmv_t<1, 1, 4>(x, wq, scales, biases, y, M, N, K, stream);
-        case 1: return launch_qmv_t<1, 2, 2>(x, wq, scales, biases, y, M, N, K, stream);
-        case 2: return launch_qmv_t<2, 2, 2>(x, wq, scales, biases, y, M, N, K, stream);
+        case 1: return launch_qmv_t<2, 2, 2>(x, wq, scales, biases, y, M, N, K, stream);
         case kQmvWideVariant: return launch_qmv_wide_t<1, kQmvWideStages, 4>(x, wq, scales, biases, y, M, N, K, stream);
+        case kQmvAmortizedVariant: return launch_qmv_bits(4, kQmvBitsMatrix, x, wq, scales, biases, y, M, N, K, stream);
         default: return hipErrorInvalidValue;
     }
 }

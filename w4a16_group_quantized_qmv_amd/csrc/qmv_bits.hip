@@ -1,0 +1,347 @@
+// qmv_bits: affine matvec for decode rows (M <= 8) at 1, 2, 4 or 8 bits per code.
+//
+// "Route affine qmv_wide by bit-width and batch size #5" routes affine quantized matvecs by
+// code width and row count between a per-row kernel and a row-amortized kernel that
+// dequantizes a group once and reuses it across the M rows.  Both exist here for every width,
+// sharing the load and unpack code; the dispatch policy picks one from measurements.
+//
+// Format (the width-generic reading of the W4 layout): at BITS bits a 32-bit word holds
+// 32 / BITS codes, element (32/BITS)*j + i of a column's row in bits BITS*i .. BITS*i + BITS - 1
+// of word j; one bf16 scale and bias per 128 reduction values; w = s * q + b.
+//
+// Lane layout, per 128-value group of one 16-column block: lane l holds column c = l % 16 and
+// the 32 consecutive reduction values kq*32 .. kq*32 + 31 of the group, kq = l / 16 -- the B
+// operand of v_mfma_f32_16x16x32_bf16.  Its codes are 4*BITS contiguous bytes of the column's
+// row, loaded with one buffer load (two at 8 bits).  They become exact bf16 integers:
+//   * 1, 2 and 4 bits: masked words hold one code per byte; a byte 0..15 read as an OCP e4m3
+//     value is q * 2^-9, so the scaled converter with scale 2^9 gives q exactly, two per
+//     instruction (the same identity the 4-bit kernels use);
+//   * 8 bits: v_cvt_f32_ubyte* then a bf16 pack (integers up to 255 are exact in bf16).
+// The unpack order is not the natural one (except at 8 bits), so the activations are put in the
+// same order with v_perm_b32 (CodeOrder below); any bijection of the reduction index works as
+// long as codes and activations agree.
+//
+// Modes:
+//   * kMatrix (row-amortized): the M rows (zero-padded to 16) are the A operand; per group
+//     P = sum x*q and X = sum x come from the matrix core and y += s*P + b*X.
+//   * kRows (per-row): for each row, P and X from v_dot2_f32_bf16 on (activation, code) pairs;
+//     rows are not amortized.  Serves M <= 2.
+// A workgroup is KW waves on one 16-column block, splitting its groups; the partial sums are
+// added in wave order through LDS, so results do not depend on timing.  Every load goes through
+// a buffer resource: columns past N and rows past M read zeros, and byte offsets that can pass
+// the end of a buffer are in the per-lane (range-checked) offset.
+#include "device_common.h"
+#include "internal.h"
+
+namespace w4a16 {
+
+namespace {
+
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Reduction offset (0..31 within the lane's 32 values) of B-operand element 8t + e.
+template <int BITS>
+struct CodeOrder;
+template <>
+struct CodeOrder<8> {
+    static constexpr int at(int i) { return i; }
+};
+template <>
+struct CodeOrder<4> {   // per word t: [q0, q2, q1, q3, q4, q6, q5, q7]
+    static constexpr int at(int i) {
+        constexpr int w[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+        return 8 * (i / 8) + w[i % 8];
+    }
+};
+template <>
+struct CodeOrder<2> {   // operand t: word t/2, shifts 2*i0 and 2*(i0+1), i0 = 2*(t%2)
+    static constexpr int at(int i) {
+        const int t = i / 8, e = i % 8, i0 = 2 * (t % 2) + e / 4, pos = e % 4;
+        return 16 * (t / 2) + i0 + 4 * pos;
+    }
+};
+template <>
+struct CodeOrder<1> {   // operand t: shifts 2t and 2t + 1
+    static constexpr int at(int i) {
+        const int t = i / 8, e = i % 8, sh = 2 * t + e / 4, pos = e % 4;
+        return sh + 8 * pos;
+    }
+};
+
+// The lane's 32 codes (BITS words: 4*BITS bytes) as four B operands of exact bf16 integers,
+// element 8t + e holding reduction offset CodeOrder<BITS>::at(8t + e).
+template <int BITS>
+__device__ __forceinline__ void codes_to_bf16(const uint32_t (&w)[BITS], u32x4_t (&bop)[4]) {
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t v = w[2 * t + h];
+                const bf16x2_t lo = {static_cast<__bf16>(static_cast<float>(v & 0xFFu)),
+                                     static_cast<__bf16>(static_cast<float>((v >> 8) & 0xFFu))};
+                const bf16x2_t hi = {static_cast<__bf16>(static_cast<float>((v >> 16) & 0xFFu)),
+                                     static_cast<__bf16>(static_cast<float>(v >> 24))};
+                bop[t][2 * h] = __builtin_bit_cast(uint32_t, lo);
+                bop[t][2 * h + 1] = __builtin_bit_cast(uint32_t, hi);
+            }
+        }
+    } else if constexpr (BITS == 4) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bop[t] = __builtin_bit_cast(u32x4_t, codes_bf16_permuted(w[t]));
+    } else {
+        constexpr uint32_t mask = BITS == 2 ? 0x03030303u : 0x01010101u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t v = BITS == 2 ? w[t / 2] : w[0];
+            const int s0 = BITS == 2 ? 2 * (2 * (t % 2)) : 2 * t;     // shift of the first masked word
+            const uint32_t m0 = (v >> s0) & mask, m1 = (v >> (s0 + BITS)) & mask;
+            bop[t][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m0, 512.0f, false));
+            bop[t][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m0, 512.0f, true));
+            bop[t][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m1, 512.0f, false));
+            bop[t][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m1, 512.0f, true));
+        }
+    }
+}
+
+// Activation pair (a, b) of the lane's 32 values (xv: natural order, dword d = values 2d, 2d+1)
+// as one dword: a in the low half, b in the high half.
+template <int A, int B>
+__device__ __forceinline__ uint32_t act_pair(const u32x4_t (&xv)[4]) {
+    constexpr uint32_t sel = (2u * (A % 2)) | ((2u * (A % 2) + 1u) << 8) | ((4u + 2u * (B % 2)) << 16) |
+                             ((5u + 2u * (B % 2)) << 24);
+    return __builtin_amdgcn_perm(xv[(B / 2) / 4][(B / 2) % 4], xv[(A / 2) / 4][(A / 2) % 4], sel);
+}
+
+template <int BITS, int T, int E2>
+__device__ __forceinline__ uint32_t act_dword(const u32x4_t (&xv)[4]) {
+    return act_pair<CodeOrder<BITS>::at(8 * T + 2 * E2), CodeOrder<BITS>::at(8 * T + 2 * E2 + 1)>(xv);
+}
+
+// The activations in the codes' order, as four operands.
+template <int BITS>
+__device__ __forceinline__ void acts_in_code_order(const u32x4_t (&xv)[4], u32x4_t (&aop)[4]) {
+    if constexpr (BITS == 8) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) aop[t] = xv[t];
+    } else {
+        aop[0] = u32x4_t{act_dword<BITS, 0, 0>(xv), act_dword<BITS, 0, 1>(xv), act_dword<BITS, 0, 2>(xv),
+                         act_dword<BITS, 0, 3>(xv)};
+        aop[1] = u32x4_t{act_dword<BITS, 1, 0>(xv), act_dword<BITS, 1, 1>(xv), act_dword<BITS, 1, 2>(xv),
+                         act_dword<BITS, 1, 3>(xv)};
+        aop[2] = u32x4_t{act_dword<BITS, 2, 0>(xv), act_dword<BITS, 2, 1>(xv), act_dword<BITS, 2, 2>(xv),
+                         act_dword<BITS, 2, 3>(xv)};
+        aop[3] = u32x4_t{act_dword<BITS, 3, 0>(xv), act_dword<BITS, 3, 1>(xv), act_dword<BITS, 3, 2>(xv),
+                         act_dword<BITS, 3, 3>(xv)};
+    }
+}
+
+template <int BITS>
+__device__ __forceinline__ void load_codes(const __amdgpu_buffer_rsrc_t& r, uint32_t voff, uint32_t soff,
+                                           uint32_t (&w)[BITS]) {
+    if constexpr (BITS == 1) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+    } else if constexpr (BITS == 2) {
+        const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+        w[0] = v[0];
+        w[1] = v[1];
+    } else {
+#pragma unroll
+        for (int h = 0; h < BITS / 4; ++h) {
+            const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16 * h, 0));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[4 * h + i] = v[i];
+        }
+    }
+}
+
+}  // namespace
+
+constexpr int kMatrix = kQmvBitsMatrix, kRows = kQmvBitsRows;
+
+template <int BITS, int KW, int MODE>
+__global__ __launch_bounds__(64 * KW) void qmv_bits_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int N, int K) {
+    constexpr int MR = MODE == kRows ? 2 : 1;   // rows held per lane in the per-row mode
+    const int G = K >> 7;
+    const int lane = threadIdx.x & 63;
+    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col0 = blockIdx.x * 16;
+    const int g0 = static_cast<int>(static_cast<int64_t>(wk) * G / KW);
+    const int g1 = static_cast<int>(static_cast<int64_t>(wk + 1) * G / KW);
+    const int c = lane & 15, kq = lane >> 4;
+    const int row_bytes = K / 8 * BITS;
+    auto clamp_records = [](int64_t bytes) { return static_cast<int>(bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes); };
+
+    const int64_t cols = static_cast<int64_t>(N - col0);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + static_cast<size_t>(col0) * row_bytes), 0,
+        clamp_records(cols * row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(scales + static_cast<size_t>(col0) * G), 0, clamp_records(cols * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(biases + static_cast<size_t>(col0) * G), 0, clamp_records(cols * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x), 0, clamp_records(static_cast<int64_t>(M) * K * 2), 0x00020000);
+    const uint32_t wvoff = static_cast<uint32_t>(c * row_bytes + kq * 4 * BITS);
+    const uint32_t sbvoff = static_cast<uint32_t>(c * G * 2);
+
+    // one group's operands: codes, scale, bias, activations of the lane's rows
+    struct Step {
+        uint32_t w[BITS];
+        uint16_t s, b;
+        u32x4_t xv[MR][4];
+    };
+    auto load_step = [&](int g, Step& o) {
+        load_codes<BITS>(wr, wvoff, static_cast<uint32_t>(g * 16 * BITS), o.w);
+        o.s = __builtin_amdgcn_raw_buffer_load_b16(sr, sbvoff, g * 2, 0);
+        o.b = __builtin_amdgcn_raw_buffer_load_b16(br, sbvoff, g * 2, 0);
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            // matrix mode: lane row l % 16; per-row mode: rows 0 and 1 (broadcast over columns)
+            const int row = MODE == kMatrix ? (lane & 15) : r;
+            const uint32_t xvoff = row < M ? static_cast<uint32_t>(row * K + kq * 32) * 2u : 0x80000000u;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                o.xv[r][t] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, xvoff, (g * kGroup + t * 8) * 2, 0));
+        }
+    };
+
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    const bf16x8_t ones = {__bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f),
+                           __bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f)};
+    const bf16x2_t ones2 = {__bf16(1.f), __bf16(1.f)};
+    f32x4_t yacc = zero4;          // matrix mode: rows 4*kq + r of column c
+    float racc[MR] = {};           // per-row mode: partial sums of rows 0..MR-1 over this lane's values
+
+    auto compute = [&](const Step& o) {
+        u32x4_t bop[4];
+        codes_to_bf16<BITS>(o.w, bop);
+        const float s = bf16_bits_to_f32(o.s), b = bf16_bits_to_f32(o.b);
+        if constexpr (MODE == kMatrix) {
+            u32x4_t aop[4];
+            acts_in_code_order<BITS>(o.xv[0], aop);
+            f32x4_t xs = zero4, p = zero4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, aop[t]);
+                xs = mfma16x16x32(a, ones, xs);
+                p = mfma16x16x32(a, __builtin_bit_cast(bf16x8_t, bop[t]), p);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, p[r], __builtin_fmaf(b, xs[r], yacc[r]));
+        } else {
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+                if (r >= M) break;
+                u32x4_t aop[4];
+                acts_in_code_order<BITS>(o.xv[r], aop);
+                float p = 0.f, xs = 0.f;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        // elements are copied out before the bit cast: a cast applied to the
+                        // vector element itself reads element 0
+                        const uint32_t a = aop[t][d], q = bop[t][d], xn = o.xv[r][t][d];
+                        p = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                                           __builtin_bit_cast(bf16x2_t, q), p, false);
+                        xs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xn), ones2, xs, false);
+                    }
+                racc[r] = __builtin_fmaf(s, p, __builtin_fmaf(b, xs, racc[r]));
+            }
+        }
+    };
+
+    // one group in flight ahead of the one computed, in ping-pong register sets
+    if (g0 < g1) {
+        Step sa, sb;
+        load_step(g0, sa);
+        for (int g = g0;; g += 2) {
+            if (g + 1 < g1) load_step(g + 1, sb);
+            compute(sa);
+            if (g + 1 >= g1) break;
+            if (g + 2 < g1) load_step(g + 2, sa);
+            compute(sb);
+            if (g + 2 >= g1) break;
+        }
+    }
+
+    // per-row mode: the four lanes of a column (kq = 0..3) hold quarters of the sums
+    if constexpr (MODE == kRows) {
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+            racc[r] += __shfl_xor(racc[r], 16);
+            racc[r] += __shfl_xor(racc[r], 32);
+        }
+    }
+
+    if constexpr (KW > 1) {
+        __shared__ float red[KW - 1][4][64];
+        if (wk > 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[wk - 1][r][lane] = MODE == kMatrix ? yacc[r] : (r < MR ? racc[r < MR ? r : 0] : 0.f);
+        }
+        __syncthreads();
+        if (wk == 0) {
+#pragma unroll
+            for (int j = 0; j < KW - 1; ++j) {
+                if constexpr (MODE == kMatrix) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) yacc[r] += red[j][r][lane];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < MR; ++r) racc[r] += red[j][r][lane];
+                }
+            }
+        }
+    }
+
+    if (wk == 0) {
+        const int col = col0 + c;
+        if (col < N) {
+            if constexpr (MODE == kMatrix) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = 4 * kq + r;
+                    if (m < M) y[static_cast<size_t>(m) * N + col] = f32_to_bf16_bits(yacc[r]);
+                }
+            } else if (kq == 0) {
+#pragma unroll
+                for (int r = 0; r < MR; ++r)
+                    if (r < M) y[static_cast<size_t>(r) * N + col] = f32_to_bf16_bits(racc[r]);
+            }
+        }
+    }
+}
+
+template <int BITS, int KW, int MODE>
+static hipError_t launch_qmv_bits_t(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                                    uint16_t* y, int M, int N, int K, hipStream_t stream) {
+    if (M < 1 || M > (MODE == kRows ? 2 : 16)) return hipErrorInvalidValue;   // rows one operand holds
+    hipLaunchKernelGGL((qmv_bits_kernel<BITS, KW, MODE>), dim3((N + 15) / 16), dim3(64 * KW), 0, stream, x, wq, s, b,
+                       y, M, N, K);
+    return hipGetLastError();
+}
+
+// variant = 2 * width index (1, 2, 4, 8 bits -> 0..3) + mode; four waves split K
+hipError_t launch_qmv_bits(int bits, int mode, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                           const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream) {
+    const bool rows = mode == kQmvBitsRows;
+    switch (bits) {
+        case 1: return rows ? launch_qmv_bits_t<1, 4, kRows>(x, wq, scales, biases, y, M, N, K, stream)
+                            : launch_qmv_bits_t<1, 4, kMatrix>(x, wq, scales, biases, y, M, N, K, stream);
+        case 2: return rows ? launch_qmv_bits_t<2, 4, kRows>(x, wq, scales, biases, y, M, N, K, stream)
+                            : launch_qmv_bits_t<2, 4, kMatrix>(x, wq, scales, biases, y, M, N, K, stream);
+        case 4: return rows ? launch_qmv_bits_t<4, 4, kRows>(x, wq, scales, biases, y, M, N, K, stream)
+                            : launch_qmv_bits_t<4, 4, kMatrix>(x, wq, scales, biases, y, M, N, K, stream);
+        case 8: return rows ? launch_qmv_bits_t<8, 4, kRows>(x, wq, scales, biases, y, M, N, K, stream)
+                            : launch_qmv_bits_t<8, 4, kMatrix>(x, wq, scales, biases, y, M, N, K, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace w4a16
