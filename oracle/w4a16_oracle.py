@@ -51,6 +51,14 @@ Readings where the pages are silent (each one is also listed in the design doc):
   ``uint32 [N, K*bits/32]``, and the group, scale, bias and R4-R7 are
   unchanged with ``2**bits - 1`` in place of 15.  ``s * q`` stays exact in
   fp32 (at most 8 + 8 significand bits).
+* R9 int8 activations (W4A8; "Feature Request: Metal prefill speedup (~68%)
+  on M5 Max" lists an int8 mat-mat for large batches after oMLX's int8 prefill,
+  with no recipe): each activation row is quantized symmetrically to int8 with
+  one fp32 scale, all in fp32: ``a = max_k |x[m, k]|``, ``inv = 127 / a`` and
+  ``sx = a / 127`` (each a correctly rounded division; a zero row has
+  ``inv = sx = 0``), ``xq = clamp(rint(x * inv), -127, 127)`` with the product
+  rounded to fp32 and ties to even.  The projection then uses ``sx * xq`` in
+  place of ``x``; weights as R1-R4.
 """
 
 from __future__ import annotations
@@ -82,6 +90,9 @@ __all__ = [
     "silu_f64",
     "swiglu_reference",
     "check_swiglu",
+    "quantize_rows_int8",
+    "reference_w4a8",
+    "brute_force_w4a8",
 ]
 
 GROUP = 128
@@ -197,6 +208,11 @@ def reference(x_bits, wq, scales, biases, group: int = GROUP, columns=None, col_
     x64 = bf16_to_f64(x_bits)
     if x64.ndim != 2:
         raise ValueError("x must be 2-D [M, K]")
+    return _project(x64, wq, scales, biases, group, columns, col_chunk, bits)
+
+
+def _project(x64, wq, scales, biases, group, columns, col_chunk, bits):
+    """``(x64 @ w64ᵀ, |x64| @ |w64|ᵀ)`` for fp64 activations (shared by both references)."""
     M, K = x64.shape
     wq = np.asarray(wq)
     scales = np.asarray(scales)
@@ -333,9 +349,14 @@ def brute_force(x_bits, wq, scales, biases, group: int = GROUP, bits: int = 4):
     M, K = x_bits.shape
     N = wq.shape[0]
     xs = [[_bf16_scalar(x_bits[m, k]) for k in range(K)] for m in range(M)]
+    return _brute_sums(xs, _brute_weights(wq, scales, biases, K, group, bits))
+
+
+def _brute_weights(wq, scales, biases, K, group, bits):
+    """Every weight decoded from its word by explicit shifts, dequantized with two fp32 roundings."""
     ws = []
     per = 32 // bits
-    for n in range(N):
+    for n in range(wq.shape[0]):
         row = []
         for k in range(K):
             word = int(wq[n, k // per])
@@ -344,6 +365,12 @@ def brute_force(x_bits, wq, scales, biases, group: int = GROUP, bits: int = 4):
             b = _bf16_scalar(biases[n, k // group])
             row.append(_f32_round(_f32_round(s * code) + b))
         ws.append(row)
+    return ws
+
+
+def _brute_sums(xs, ws):
+    """Correctly rounded fp64 sums of the exact products, with their absolute mass."""
+    M, N, K = len(xs), len(ws), len(xs[0]) if xs else 0
     y = np.empty((M, N))
     A = np.empty((M, N))
     for m in range(M):
@@ -420,3 +447,57 @@ def check_swiglu(h_bits, g_ref, A_g, u_ref, A_u, rel: float = TOL_REL, mass: flo
     flat = int(np.argmax(ratio))
     worst = tuple(int(i) for i in np.unravel_index(flat, ratio.shape))
     return CheckResult(bool(good.all()), float(ratio.flat[flat]), worst, int((~good).sum()), int(good.size))
+
+
+# --------------------------------------------------------------------------- W4A8 (R9)
+
+
+def quantize_rows_int8(x_bits):
+    """Per-row symmetric int8 quantizer of the activations (reading R9).
+
+    Returns ``(xq, sx)``: int8 codes ``[M, K]`` and the fp32 row scales ``[M]``,
+    so that ``sx[m] * xq[m, k]`` approximates ``x[m, k]`` within ``sx[m] / 2``
+    (plus fp32 rounding of the scale).
+    """
+    x = bf16_to_f32(x_bits)
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    a = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(a > 0, np.float32(127) / a, np.float32(0)).astype(np.float32)
+    sx = (a / np.float32(127)).astype(np.float32)
+    prod = (x * inv[:, None]).astype(np.float32)
+    xq = np.clip(np.rint(prod), -127, 127).astype(np.int8)
+    return xq, sx
+
+
+def reference_w4a8(x_bits, wq, scales, biases, group: int = GROUP, columns=None, col_chunk: int = 8192):
+    """Reference of the W4A8 projection and its absolute mass, fp64 ``[M, N']``.
+
+    The activations are replaced by their int8 reconstruction ``sx * xq``
+    (exact in fp64: an fp32 scale times an integer below 2^7) and projected by
+    the dequantized 4-bit weights as in ``reference``.
+    """
+    xq, sx = quantize_rows_int8(x_bits)
+    x64 = sx.astype(np.float64)[:, None] * xq.astype(np.float64)
+    return _project(x64, wq, scales, biases, group, columns, col_chunk, 4)
+
+
+def brute_force_w4a8(x_bits, wq, scales, biases, group: int = GROUP):
+    """Pure-Python loops for the W4A8 projection; small inputs only.
+
+    The quantizer works on Python floats: a division or product of two fp32
+    values evaluated in fp64 and rounded once to fp32 is the correctly rounded
+    fp32 result, and ``round`` breaks ties to even.
+    """
+    x_bits = np.asarray(x_bits)
+    M, K = x_bits.shape
+    xs = []
+    for m in range(M):
+        row = [_bf16_scalar(x_bits[m, k]) for k in range(K)]
+        a = max((abs(v) for v in row), default=0.0)
+        inv = _f32_round(127.0 / a) if a > 0 else 0.0
+        sx = _f32_round(a / 127.0)
+        codes = [max(-127, min(127, round(_f32_round(v * inv)))) for v in row]
+        xs.append([sx * c for c in codes])
+    return _brute_sums(xs, _brute_weights(np.asarray(wq), scales, biases, K, group, 4))

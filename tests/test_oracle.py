@@ -587,3 +587,148 @@ def test_bits_mutant_copy_is_faithful_without_a_mistake():
     # come from the planted mistakes)
     for bits in (1, 2, 8):
         assert all(p(_bits_mutant("none"), bits) for p in BITS_PINS)
+
+
+# ----------------------------------------------------------------------------- W4A8 quantizer (R9)
+#
+# Pins of the per-row int8 activation quantizer, each independent of the oracle's numpy code:
+# rows on an exact int8 grid, exact rounding ties, the zero row, the absmax element, the
+# round-trip bound, and a pure-Python quantizer.  Each pin takes a quantizer (x_bits -> (xq, sx))
+# so that planted mistakes can be shown to fail at least one of them.
+
+def _grid_rows(rng, M, K):
+    """Rows x = c * j with integer j in [-127, 127], |j| = 127 somewhere, c a power of two."""
+    j = rng.integers(-127, 128, (M, K))
+    j[np.arange(M), rng.integers(0, K, M)] = rng.choice([-127, 127], M)
+    c = 2.0 ** rng.integers(-12, 4, M)
+    return j, c, synth.to_bf16_bits((j * c[:, None]).astype(np.float32))
+
+
+def _a8_pin_grid(qf):
+    j, c, x = _grid_rows(np.random.default_rng(60), 6, 384)
+    xq, sx = qf(x)
+    return np.array_equal(np.asarray(xq, np.int64), j) and np.array_equal(np.asarray(sx, np.float64), c)
+
+
+def _a8_pin_ties(qf):
+    """x = c * (j + 1/2) next to an element 127 c: x * inv is an exact tie, broken to even."""
+    rng = np.random.default_rng(61)
+    M, K = 4, 256
+    j = rng.integers(-126, 126, (M, K))
+    v = (j + 0.5).astype(np.float64)
+    v[:, 0] = 127.0
+    c = 2.0 ** rng.integers(-8, 2, M)
+    xq, _ = qf(synth.to_bf16_bits((v * c[:, None]).astype(np.float32)))
+    expect = np.rint(v).astype(np.int64)          # numpy rint: ties to even, exact here
+    return np.array_equal(np.asarray(xq, np.int64), expect)
+
+
+def _a8_pin_zero_row(qf):
+    x = synth.to_bf16_bits(np.random.default_rng(62).standard_normal((3, 256)).astype(np.float32))
+    x[1] = 0
+    xq, sx = qf(x)
+    return float(sx[1]) == 0.0 and not np.any(np.asarray(xq)[1]) and float(sx[0]) > 0
+
+
+def _a8_pin_absmax_and_bound(qf):
+    """Random rows: the largest |x| maps to +-127 and |x - sx xq| <= sx / 2 + 2^-22 max|x|."""
+    rng = np.random.default_rng(63)
+    x = synth.to_bf16_bits((rng.standard_normal((8, 640)) * 2.0 ** rng.integers(-6, 6, (8, 1))).astype(np.float32))
+    xq, sx = qf(x)
+    xf = O.bf16_to_f64(x)
+    a = np.max(np.abs(xf), axis=1)
+    xq = np.asarray(xq, np.float64)
+    sx = np.asarray(sx, np.float64)
+    top = np.abs(xq[np.arange(8), np.argmax(np.abs(xf), axis=1)])
+    err = np.abs(xf - sx[:, None] * xq)
+    return (np.all(top == 127) and np.all(np.abs(xq) <= 127)
+            and np.all(err <= (sx / 2 + 2.0 ** -22 * a)[:, None]))
+
+
+def _a8_pin_python_loops(qf):
+    """Against a quantizer written with Python floats and loops (fp64 then one fp32 rounding)."""
+    rng = np.random.default_rng(64)
+    x = synth.to_bf16_bits(rng.standard_normal((3, 200)).astype(np.float32))
+    xq, sx = qf(x)
+    for m in range(3):
+        row = [O.bf16_to_f64(x[m, k:k + 1])[0] for k in range(200)]
+        a = max(abs(v) for v in row)
+        inv = _f32(127.0 / a)
+        if float(sx[m]) != _f32(a / 127.0):
+            return False
+        if [int(q) for q in xq[m]] != [max(-127, min(127, round(_f32(v * inv)))) for v in row]:
+            return False
+    return True
+
+
+def _f32(v):
+    return float(np.float32(v))
+
+
+A8_PINS = [_a8_pin_grid, _a8_pin_ties, _a8_pin_zero_row, _a8_pin_absmax_and_bound, _a8_pin_python_loops]
+
+
+@pytest.mark.parametrize("pin", A8_PINS, ids=lambda p: p.__name__)
+def test_int8_quantizer_passes_pin(pin):
+    assert pin(O.quantize_rows_int8)
+
+
+def _a8_mutant(kind):
+    """A copy of the oracle's quantizer with one plausible mistake."""
+    def qf(x_bits):
+        x = O.bf16_to_f32(x_bits)
+        a = np.max(np.abs(x), axis=1)
+        if kind == "per_tensor_scale":
+            a = np.full_like(a, np.max(a))
+        top = np.float32(128 if kind == "scale_128" else 127)
+        with np.errstate(divide="ignore"):
+            inv = np.where(a > 0, top / a, np.float32(0)).astype(np.float32)
+        sx = (a / top).astype(np.float32)
+        prod = (x * inv[:, None]).astype(np.float32)
+        if kind == "truncate":
+            r = np.trunc(prod)
+        elif kind == "ties_away":
+            r = np.sign(prod) * np.floor(np.abs(prod) + 0.5)
+        else:
+            r = np.rint(prod)
+        return np.clip(r, -127, 127).astype(np.int8), sx
+    return qf
+
+
+A8_MUTANTS = ["per_tensor_scale", "scale_128", "truncate", "ties_away"]
+
+
+@pytest.mark.parametrize("kind", A8_MUTANTS)
+def test_int8_quantizer_pins_catch_planted_mistakes(kind):
+    failed = [p.__name__ for p in A8_PINS if not p(_a8_mutant(kind))]
+    assert failed, f"planted mistake {kind!r} passed every pin"
+
+
+def test_int8_mutant_copy_is_faithful_without_a_mistake():
+    assert all(p(_a8_mutant("none")) for p in A8_PINS)
+
+
+def test_w4a8_reference_equals_w4a16_reference_on_grid_rows():
+    # on rows that the int8 grid represents exactly, sx * xq == x and the two references agree bit for bit
+    rng = np.random.default_rng(65)
+    _, _, x = _grid_rows(rng, 5, 512)
+    p = synth.random_problem(66, 5, 40, 512)
+    y8, A8 = O.reference_w4a8(x, p["wq"], p["scales"], p["biases"])
+    y16, A16 = O.reference(x, p["wq"], p["scales"], p["biases"])
+    assert np.array_equal(y8, y16) and np.array_equal(A8, A16)
+
+
+@pytest.mark.parametrize("M,K,N", [(3, 256, 5), (2, 384, 7)])
+def test_w4a8_reference_matches_brute_force(M, K, N):
+    p = synth.random_problem(67 + M, M, N, K)
+    y, A = O.reference_w4a8(p["x"], p["wq"], p["scales"], p["biases"])
+    yb, Ab = O.brute_force_w4a8(p["x"], p["wq"], p["scales"], p["biases"])
+    assert np.allclose(y, yb, rtol=0, atol=1e-12 * np.max(Ab)) and np.allclose(A, Ab, rtol=1e-12, atol=0)
+
+
+def test_w4a8_zero_row_projects_to_zero():
+    p = synth.random_problem(68, 3, 9, 256)
+    x = p["x"].copy()
+    x[2] = 0
+    y, A = O.reference_w4a8(x, p["wq"], p["scales"], p["biases"])
+    assert not np.any(y[2]) and not np.any(A[2])
