@@ -29,6 +29,27 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kGroup = 128;          // reduction values per scale/bias pair
 constexpr int kWordsPerGroup = 16;   // 128 four-bit codes in sixteen 32-bit words
 
+// Tile order of the tiled kernels (qmm and the int8 path).
+constexpr int kBandM = 8;               // M-tiles per band of the tile order
+
+// Linear workgroup index -> work index such that XCD c (= i % 8) receives the contiguous range
+// of work indices [start_c, start_c + count_c).
+__device__ __forceinline__ int xcd_remap(int i, int total) {
+    const int per = total >> 3, rem = total & 7;
+    const int c = i & 7, k = i >> 3;
+    return c * per + (c < rem ? c : rem) + k;
+}
+
+// Tile index -> (tm, tn): bands of up to kBandM M-tiles, each band walked N-tile by N-tile.
+__device__ __forceinline__ void band_order(int tile, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int band = tile / (kBandM * tiles_n);
+    const int first = band * kBandM;
+    const int rows = min(kBandM, tiles_m - first);
+    const int in_band = tile - band * kBandM * tiles_n;
+    tm = first + in_band % rows;
+    tn = in_band / rows;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }

@@ -49,26 +49,6 @@
 
 namespace w4a16 {
 
-constexpr int kBandM = 8;               // M-tiles per band of the tile order
-
-// Linear workgroup index -> work index such that XCD c (= i % 8) receives the contiguous range
-// of work indices [start_c, start_c + count_c).
-__device__ __forceinline__ int xcd_remap(int i, int total) {
-    const int per = total >> 3, rem = total & 7;
-    const int c = i & 7, k = i >> 3;
-    return c * per + (c < rem ? c : rem) + k;
-}
-
-// Tile index -> (tm, tn): bands of up to kBandM M-tiles, each band walked N-tile by N-tile.
-__device__ __forceinline__ void band_order(int tile, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int band = tile / (kBandM * tiles_n);
-    const int first = band * kBandM;
-    const int rows = min(kBandM, tiles_m - first);
-    const int in_band = tile - band * kBandM * tiles_n;
-    tm = first + in_band % rows;
-    tn = in_band / rows;
-}
-
 // SiLU in fp32: z * sigmoid(z) = z / (1 + e^-z); e^-z overflows to inf for z < -88 and the
 // quotient is then -0, the limit.
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.f + expf(-z)); }
