@@ -69,7 +69,8 @@ enum w4a16_path {
                                   split-K above (the small-batch regime 8 < rows <= 32 that
                                   "Feature Request: Metal prefill speedup (~68%) on M5 Max",
                                   Related work, names for skinny tiles + deterministic split-K)  */
-    W4A16_PATH_GATE_UP = 4     /* reported by w4a16_gate_up_plan only: the fused gate / up tiles  */
+    W4A16_PATH_GATE_UP = 4,    /* reported by w4a16_gate_up_plan only: the fused gate / up tiles  */
+    W4A16_PATH_W4A8 = 5        /* reported by w4a8_plan only: int8-activation tiles               */
 };
 
 /* Launch plan chosen by the dispatch policy (filled by w4a16_plan). */
@@ -204,6 +205,66 @@ int qmv_affine(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, co
  */
 int qmv_affine_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, int32_t mode,
                     int32_t num_cus, w4a16_plan_t* out);
+
+/*
+ * W4A8: the same 4-bit affine weights with int8 activations on the int8 matrix cores (the int8
+ * mat-mat for large batches that "Feature Request: Metal prefill speedup (~68%) on M5 Max (NAX /
+ * tensor API kernels)" lists in its feature list and Related work; the page gives no recipe).
+ * Reading taken: each activation row m is quantized symmetrically, all in fp32,
+ *
+ *     a = max_k |x[m, k]|,  inv = 127 / a,  sx[m] = a / 127   (correctly rounded; a = 0 gives 0),
+ *     xq[m, k] = clamp(rint(x[m, k] * inv), -127, 127)         (product rounded to fp32, ties even),
+ *
+ * and the projection uses sx * xq in place of x:  y[m, n] = bf16( sum_k sx[m] xq[m, k] w[n, k] ),
+ * computed as sx[m] * (sum_g s[n, g] P[m, n, g] + sum_g b[n, g] X[m, g]) with the exact integer
+ * group products P = sum_{k in g} xq q and group sums X = sum_{k in g} xq.  Inputs must be finite.
+ *
+ * Activation buffers (made by w4a8_quantize_rows, read by qmm_w4a8; caller-owned device memory):
+ *   xq    int8 [M, K], 16-byte aligned: each aligned run of 8 values k0..k7 is stored in the
+ *         order k0 k2 k4 k6 k1 k3 k5 k7 (the order of the kernel's code operand)
+ *   sx    fp32 [M], 4-byte aligned
+ *   xsum  bf16 [M, w4a8_xsum_cols(K)], 16-byte aligned: xsum[m, 2g] + xsum[m, 2g + 1] = X[m, g]
+ *         exactly (the multiple of 128 and the remainder 0..127), zeros beyond 2G
+ */
+
+/* Columns of xsum for a given K: 2 * K / 128 rounded up to a multiple of 16 (0 for invalid K). */
+int64_t w4a8_xsum_cols(int64_t K);
+
+/*
+ * Quantize the rows of x (bf16 [M, K]) into xq, sx and xsum as described above.  One launch on
+ * `stream`.  Errors: W4A16_ERR_NULL, _ERR_SHAPE (M < 1, K outside the limits), _ERR_GROUP,
+ * _ERR_ALIGN, _ERR_LAUNCH.
+ */
+int w4a8_quantize_rows(const uint16_t* x, int8_t* xq, float* sx, uint16_t* xsum, int64_t M, int64_t K, int32_t group,
+                       void* stream);
+
+/*
+ * Launch plan of qmm_w4a8 (path = W4A16_PATH_W4A8): 32-row tiles up to 32 rows, 64 up to ~1k,
+ * 128 beyond; the split rule of qmm_w4a16.  workspace_bytes = the fp32 partials (S * M * N * 4)
+ * when the plan splits.  split_k and num_cus as in w4a16_plan.  Pure host arithmetic.
+ */
+int w4a8_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, int32_t num_cus, w4a16_plan_t* out);
+
+/*
+ * int8-activation tile path for any M >= 1 over buffers from w4a8_quantize_rows; weights, y,
+ * split_k, workspace and errors as for qmm_w4a16 (the slices are summed in slice order).
+ */
+int qmm_w4a8(const int8_t* xq, const float* sx, const uint16_t* xsum, const uint32_t* wq, const uint16_t* scales,
+             const uint16_t* biases, uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of w4a8_linear: the three activation buffers plus the policy's partials. */
+uint64_t w4a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t num_cus);
+
+/*
+ * One-call W4A8 projection of bf16 x: w4a8_quantize_rows into the start of `workspace` (256-byte
+ * aligned, at least w4a8_linear_workspace_bytes), then qmm_w4a8 under the policy with the rest
+ * of the workspace for partials (a policy split without room falls back to S = 1).  Same
+ * preconditions and errors as qmm_w4a16; a missing or short workspace returns
+ * W4A16_ERR_WORKSPACE, a misaligned one W4A16_ERR_ALIGN.
+ */
+int w4a8_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, uint16_t* y,
+                int64_t M, int64_t N, int64_t K, int32_t group, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

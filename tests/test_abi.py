@@ -267,3 +267,54 @@ def test_qmv_affine_validates_before_launch(lib):
     assert call(group=64) == 3
     assert call(x=ODD) == 4 and call(wq=ODD) == 4 and call(s=A16 + 1) == 4 and call(y=A16 + 1) == 4
     assert lib.qmv_affine_plan(1, 16, 256, 128, 4, 0, CUS, None) == 1
+
+
+# ------------------------------------------------------------------------------ W4A8
+
+def test_w4a8_plan_tiles_split_and_workspace():
+    for M, tile_m in [(1, 32), (32, 32), (33, 64), (512, 64), (1024, 64), (1025, 128), (4096, 128)]:
+        p = w4.w4a8_plan(M, 9728, 2560, 128, 0, CUS)
+        assert p["path"] == w4.PATH_W4A8 and p["tile_m"] == tile_m and p["tile_n"] == 128
+        assert p["grid_x"] == -(-9728 // 128) and p["grid_y"] == -(-M // tile_m)
+        assert p["workspace_bytes"] == (p["split_k"] * M * 9728 * 4 if p["split_k"] > 1 else 0)
+    # the split rule of the W4A16 tiles: only under-filled grids with enough groups
+    assert w4.w4a8_plan(4096, 9728, 2560, 128, 0, CUS)["split_k"] == 1
+    assert w4.w4a8_plan(512, 2560, 9728, 128, 0, CUS)["split_k"] > 1
+    assert w4.w4a8_plan(33, 96, 256, 128, 0, CUS)["split_k"] == 1          # G = 2: never split
+    assert w4.w4a8_plan(128, 1024, 2560, 128, 3, CUS)["split_k"] == 3
+    assert w4.w4a8_plan(128, 1024, 256, 128, 64, CUS)["split_k"] == 2       # clamped to G
+
+
+def test_w4a8_xsum_columns_and_linear_workspace():
+    # two bf16 halves per group, rounded up to the 16-value MFMA step
+    for K, cols in [(128, 16), (256, 16), (1024, 16), (1152, 32), (2560, 48), (4096, 64), (9728, 160)]:
+        assert w4.w4a8_xsum_cols(K) == cols
+    assert w4.w4a8_xsum_cols(100) == 0 and w4.w4a8_xsum_cols(0) == 0
+    r256 = lambda v: -(-v // 256) * 256
+    for M, N, K in [(33, 96, 256), (512, 9728, 2560), (512, 2560, 9728)]:
+        act = r256(M * K) + r256(M * 4) + r256(M * w4.w4a8_xsum_cols(K) * 2)
+        assert w4.w4a8_linear_workspace_bytes(M, N, K, 128, CUS) == act + w4.w4a8_plan(M, N, K, 128, 0, CUS)[
+            "workspace_bytes"]
+
+
+def test_w4a8_entry_points_validate_before_launch(lib):
+    def quant(x=A16, xq=A16, sx=A16, xs=A16, M=4, K=256, group=128):
+        return lib.w4a8_quantize_rows(x, xq, sx, xs, M, K, group, None)
+
+    assert quant(x=None) == 1 and quant(xq=None) == 1 and quant(sx=None) == 1 and quant(xs=None) == 1
+    assert quant(M=0) == 2 and quant(K=100) == 2 and quant(group=64) == 3
+    assert quant(x=ODD) == 4 and quant(xq=ODD) == 4 and quant(xs=ODD) == 4 and quant(sx=A16 + 2) == 4
+
+    def qmm(xq=A16, sx=A16, xs=A16, wq=A16, s=A16, b=A16, y=A16, M=4, N=16, K=256, group=128, split=1):
+        return lib.qmm_w4a8(xq, sx, xs, wq, s, b, y, M, N, K, group, split, None, 0, None)
+
+    for kw in ("xq", "sx", "xs", "wq", "s", "b", "y"):
+        assert qmm(**{kw: None}) == 1, kw
+    assert qmm(M=0) == 2 and qmm(K=100) == 2 and qmm(split=-1) == 2 and qmm(group=64) == 3
+    assert qmm(xq=ODD) == 4 and qmm(wq=ODD) == 4 and qmm(y=A16 + 1) == 4
+
+    def linear(x=A16, wq=A16, s=A16, b=A16, y=A16, M=4, N=16, K=256, ws=A16 * 16, nbytes=1 << 20):
+        return lib.w4a8_linear(x, wq, s, b, y, M, N, K, 128, ws, nbytes, None)
+
+    assert linear(x=None) == 1 and linear(M=0) == 2 and linear(x=ODD) == 4
+    assert linear(ws=None) == 5 and linear(nbytes=100) == 5 and linear(ws=A16 * 16 + 16) == 4

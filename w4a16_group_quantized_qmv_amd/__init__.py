@@ -31,11 +31,13 @@ __all__ = [
     "qmv_w4a16", "qmm_w4a16", "w4a16_linear", "linear", "W4A16Error", "declared_symbols", "PreparedLinear",
     "w4a16_gate_up_plan", "w4a16_gate_up_swiglu", "PreparedGateUp",
     "qmv_affine", "qmv_affine_plan", "QMV_POLICY", "QMV_AMORTIZED", "QMV_PER_ROW", "QMV_FAMILIES", "BITS",
+    "PATH_W4A8", "w4a8_xsum_cols", "w4a8_quantize_rows", "w4a8_plan", "qmm_w4a8", "w4a8_linear_workspace_bytes",
+    "w4a8_linear", "PreparedW4A8",
 ]
 
 GROUP = 128
 W4A16_OK = 0
-PATH_AUTO, PATH_QMV, PATH_QMM, PATH_SKINNY, PATH_GATE_UP = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_QMV, PATH_QMM, PATH_SKINNY, PATH_GATE_UP, PATH_W4A8 = 0, 1, 2, 3, 4, 5
 QMV_POLICY, QMV_AMORTIZED, QMV_PER_ROW, QMV_FAMILIES = 0, 1, 2, 3
 BITS = (1, 2, 4, 8)
 
@@ -94,6 +96,18 @@ def load():
     lib.qmv_affine_plan.argtypes = [i64, i64, i64, i32, i32, i32, i32, ctypes.POINTER(Plan)]
     lib.qmv_affine.restype = ctypes.c_int
     lib.qmv_affine.argtypes = [u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, i32, i32, vp]
+    lib.w4a8_xsum_cols.restype = i64
+    lib.w4a8_xsum_cols.argtypes = [i64]
+    lib.w4a8_quantize_rows.restype = ctypes.c_int
+    lib.w4a8_quantize_rows.argtypes = [u16p, vp, vp, u16p, i64, i64, i32, vp]
+    lib.w4a8_plan.restype = ctypes.c_int
+    lib.w4a8_plan.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(Plan)]
+    lib.qmm_w4a8.restype = ctypes.c_int
+    lib.qmm_w4a8.argtypes = [vp, vp, u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.w4a8_linear_workspace_bytes.restype = ctypes.c_uint64
+    lib.w4a8_linear_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    lib.w4a8_linear.restype = ctypes.c_int
+    lib.w4a8_linear.argtypes = [u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, vp, ctypes.c_size_t, vp]
     _LIB = lib
     return lib
 
@@ -152,6 +166,20 @@ def qmv_affine_plan(M: int, N: int, K: int, bits: int, mode: int = QMV_POLICY, g
     p = Plan()
     _raise_for(load().qmv_affine_plan(M, N, K, group, bits, mode, num_cus, ctypes.byref(p)), "qmv_affine_plan")
     return p.as_dict()
+
+
+def w4a8_plan(M: int, N: int, K: int, group: int = GROUP, split_k: int = 0, num_cus: int = 0) -> dict:
+    p = Plan()
+    _raise_for(load().w4a8_plan(M, N, K, group, split_k, num_cus, ctypes.byref(p)), "w4a8_plan")
+    return p.as_dict()
+
+
+def w4a8_xsum_cols(K: int) -> int:
+    return int(load().w4a8_xsum_cols(K))
+
+
+def w4a8_linear_workspace_bytes(M: int, N: int, K: int, group: int = GROUP, num_cus: int = 0) -> int:
+    return int(load().w4a8_linear_workspace_bytes(M, N, K, group, num_cus))
 
 
 # ------------------------------------------------------------------------------------ tensors
@@ -279,6 +307,70 @@ def w4a16_gate_up_swiglu(x, gate, up, h=None, split_k: int = 0, workspace=None, 
     return h
 
 
+def w4a8_quantize_rows(x, xq=None, sx=None, xsum=None, stream=None):
+    """Per-row int8 quantization of bf16 ``x [M, K]`` for the W4A8 path; returns ``(xq, sx, xsum)``:
+    ``xq`` int8 ``[M, K]`` (each run of 8 values stored as k0 k2 k4 k6 k1 k3 k5 k7), ``sx`` fp32
+    ``[M]`` and ``xsum`` bf16 ``[M, w4a8_xsum_cols(K)]`` (exact per-group code sums as hi / lo)."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    _check(x, "x", torch.bfloat16, (M, K))
+    KB = w4a8_xsum_cols(K)
+    if KB == 0:
+        raise ValueError(f"K={K} must be a positive multiple of {GROUP}")
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device) if xq is None else xq
+    sx = torch.empty((M,), dtype=torch.float32, device=x.device) if sx is None else sx
+    xsum = torch.empty((M, KB), dtype=torch.bfloat16, device=x.device) if xsum is None else xsum
+    _check(xq, "xq", torch.int8, (M, K))
+    _check(sx, "sx", torch.float32, (M,))
+    _check(xsum, "xsum", torch.bfloat16, (M, KB))
+    st = load().w4a8_quantize_rows(x.data_ptr(), xq.data_ptr(), sx.data_ptr(), xsum.data_ptr(), M, K, GROUP,
+                                   _stream(stream, x.device))
+    _raise_for(st, "w4a8_quantize_rows")
+    return xq, sx, xsum
+
+
+def qmm_w4a8(xq, sx, xsum, wq, scales, biases, y=None, split_k: int = 0, workspace=None, stream=None):
+    """int8-activation tile path over the buffers of ``w4a8_quantize_rows``; split_k as for
+    ``qmm_w4a16``.  Returns y (bf16 ``[M, N]``)."""
+    torch = _torch()
+    if xq.dim() != 2 or wq.dim() != 2:
+        raise ValueError("xq and wq must be 2-D")
+    M, K = xq.shape
+    N = wq.shape[0]
+    if K % GROUP:
+        raise ValueError(f"K={K} must be a multiple of {GROUP}")
+    _check(xq, "xq", torch.int8, (M, K))
+    _check(sx, "sx", torch.float32, (M,))
+    _check(xsum, "xsum", torch.bfloat16, (M, w4a8_xsum_cols(K)))
+    _check(wq, "wq", torch.int32, (N, K // 8))
+    _check(scales, "scales", torch.bfloat16, (N, K // GROUP))
+    _check(biases, "biases", torch.bfloat16, (N, K // GROUP))
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _check(y, "y", torch.bfloat16, (M, N))
+    need = w4a8_plan(M, N, K, GROUP, split_k)["workspace_bytes"]
+    ws, ws_bytes = _workspace(workspace, need, xq.device)
+    st = load().qmm_w4a8(xq.data_ptr(), sx.data_ptr(), xsum.data_ptr(), wq.data_ptr(), scales.data_ptr(),
+                         biases.data_ptr(), y.data_ptr(), M, N, K, GROUP, split_k,
+                         None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream, xq.device))
+    _raise_for(st, "qmm_w4a8")
+    return y
+
+
+def w4a8_linear(x, wq, scales, biases, y=None, workspace=None, stream=None):
+    """One-call W4A8 projection of bf16 ``x``: per-row int8 quantization into the workspace, then
+    the int8 tile path under the policy.  Returns y."""
+    M, N, K, y = _operands(x, wq, scales, biases, y)
+    ws, ws_bytes = _workspace(workspace, w4a8_linear_workspace_bytes(M, N, K), x.device)
+    st = load().w4a8_linear(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(),
+                            M, N, K, GROUP, None if ws is None else ws.data_ptr(), ws_bytes,
+                            _stream(stream, x.device))
+    _raise_for(st, "w4a8_linear")
+    return y
+
+
 def linear(x, wq, scales, biases, logits_to_keep: int = 0, path: str | None = None, split_k: int | None = None):
     """Quantized linear layer ``y = x · dequant(Wq)ᵀ`` with the ``logits_to_keep`` row slice.
 
@@ -367,3 +459,26 @@ class PreparedGateUp:
         if st != W4A16_OK:
             _raise_for(st, "w4a16_gate_up_swiglu")
         return self.h
+
+
+class PreparedW4A8:
+    """The one-call W4A8 projection with fixed tensors, validated once (see PreparedLinear): ``y``
+    and the workspace (activation buffers plus partials) are allocated here; ``__call__`` issues
+    one C-ABI call (``w4a8_linear``) on the stream current at construction."""
+
+    def __init__(self, x, wq, scales, biases, y=None):
+        M, N, K, y = _operands(x, wq, scales, biases, y)
+        self.M, self.N, self.K, self.y = M, N, K, y
+        lib = load()
+        self.plan = w4a8_plan(M, N, K, GROUP, 0)
+        ws, ws_bytes = _workspace(None, w4a8_linear_workspace_bytes(M, N, K), x.device)
+        self.workspace = ws
+        self._fn = lib.w4a8_linear
+        self._args = (x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(), M, N, K,
+                      GROUP, ws.data_ptr(), ws_bytes, _stream(None, x.device))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != W4A16_OK:
+            _raise_for(st, "w4a8_linear")
+        return self.y

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libw4a16.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["abi.hip", "qmv.hip", "qmv_bits.hip", "qmm.hip"]
+SOURCES = ["abi.hip", "qmv.hip", "qmv_bits.hip", "qmm.hip", "w4a8.hip"]
 ARCH = "gfx950"
 
 

@@ -369,6 +369,116 @@ int run_qmv_affine(const uint16_t* x, const uint32_t* wq, const uint16_t* s, con
                                      b, y, m, n, k, hs));
 }
 
+// W4A8 (int8 activations, "Feature Request: Metal prefill speedup (~68%) on M5 Max", feature
+// list and Related work): tiles of 32 rows up to 32 rows, 64 up to ~1k, 128 beyond; the split
+// rule of the W4A16 tiles.  workspace_bytes covers the fp32 partials only.
+void plan_w4a8(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p) {
+    plan_qmm(M, N, K, split_k, cus, p, M <= kSkinnyMaxRows);
+    const int variant = M <= kSkinnyMaxRows ? 0 : (M <= 1024 ? 1 : 2);
+    const QmmShape& v = kW4A8Variants[variant];
+    const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
+    if (v.bm != p->tile_m || tile_n != p->tile_n) {
+        p->tile_m = v.bm;
+        p->tile_n = static_cast<int32_t>(tile_n);
+        p->grid_x = static_cast<int32_t>(ceil_div(N, tile_n));
+        p->grid_y = static_cast<int32_t>(ceil_div(M, v.bm));
+    }
+    p->path = W4A16_PATH_W4A8;
+    p->block_threads = 64 * v.nwaves;
+    p->variant = variant;
+    p->workspace_bytes = p->split_k > 1 ? static_cast<uint64_t>(p->split_k) * M * N * sizeof(float) : 0;
+}
+
+int make_w4a8_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, int32_t num_cus,
+                   w4a16_plan_t* out) {
+    if (!out) return W4A16_ERR_NULL;
+    int st = check_shape(M, N, K, group);
+    if (st != W4A16_OK) return st;
+    if (split_k < 0) return W4A16_ERR_SHAPE;
+    int32_t cus = num_cus;
+    if (cus <= 0) {
+        st = query_num_cus(&cus);
+        if (st != W4A16_OK) return st;
+    }
+    plan_w4a8(M, N, K, split_k, cus, out);
+    out->num_cus = cus;
+    return W4A16_OK;
+}
+
+uint64_t round256(uint64_t v) { return (v + 255) / 256 * 256; }
+
+// Byte sizes of the activation buffers that w4a8_linear carves from its workspace.
+struct W4A8Act {
+    uint64_t xq, sx, xsum, total;
+};
+W4A8Act w4a8_act_bytes(int64_t M, int64_t K) {
+    W4A8Act a;
+    a.xq = round256(static_cast<uint64_t>(M) * K);
+    a.sx = round256(static_cast<uint64_t>(M) * sizeof(float));
+    a.xsum = round256(static_cast<uint64_t>(M) * w4a8_xsum_cols(static_cast<int>(K)) * 2);
+    a.total = a.xq + a.sx + a.xsum;
+    return a;
+}
+
+int run_quantize_rows(const uint16_t* x, int8_t* xq, float* sx, uint16_t* xsum, int64_t M, int64_t K,
+                      int32_t group, void* stream) {
+    int st = check_shape(M, 1, K, group);
+    if (st != W4A16_OK) return st;
+    if (!x || !xq || !sx || !xsum) return W4A16_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(sx, 4) || !aligned(xsum, 16)) return W4A16_ERR_ALIGN;
+    return to_status(launch_quantize_rows_int8(x, xq, sx, xsum, static_cast<int>(M), static_cast<int>(K),
+                                               w4a8_xsum_cols(static_cast<int>(K)), static_cast<hipStream_t>(stream)));
+}
+
+int run_w4a8(const int8_t* xq, const float* sx, const uint16_t* xsum, const uint32_t* wq, const uint16_t* s,
+             const uint16_t* b, uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k,
+             void* workspace, size_t ws_bytes, void* stream) {
+    int st = check_shape(M, N, K, group);
+    if (st != W4A16_OK) return st;
+    if (!xq || !sx || !xsum || !wq || !s || !b || !y) return W4A16_ERR_NULL;
+    if (!aligned(xq, 16) || !aligned(sx, 4) || !aligned(xsum, 16) || !aligned(wq, 16) || !aligned(s, 2) ||
+        !aligned(b, 2) || !aligned(y, 2))
+        return W4A16_ERR_ALIGN;
+    if (split_k < 0) return W4A16_ERR_SHAPE;
+    w4a16_plan_t p;
+    st = make_w4a8_plan(M, N, K, group, split_k, 0, &p);
+    if (st != W4A16_OK) return st;
+    if (p.split_k > 1) {
+        const bool ws_ok = workspace != nullptr && aligned(workspace, 16) && ws_bytes >= p.workspace_bytes;
+        if (!ws_ok) {
+            if (split_k > 1) return workspace != nullptr && !aligned(workspace, 16) ? W4A16_ERR_ALIGN
+                                                                                     : W4A16_ERR_WORKSPACE;
+            plan_w4a8(M, N, K, 1, p.num_cus, &p);   // the unsplit plan computes the same result
+        }
+    }
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    float* ws = static_cast<float*>(workspace);
+    const int k = static_cast<int>(K);
+    hipError_t e = launch_qmm_w4a8(p.variant, xq, sx, xsum, wq, s, b, y, ws, static_cast<int>(M), static_cast<int>(N),
+                                   k, w4a8_xsum_cols(k), p.split_k, hs);
+    if (e != hipSuccess || p.split_k == 1) return to_status(e);
+    return to_status(launch_splitk_reduce(ws, y, M * N, p.split_k, hs));
+}
+
+int run_w4a8_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b, uint16_t* y,
+                    int64_t M, int64_t N, int64_t K, int32_t group, void* workspace, size_t ws_bytes, void* stream) {
+    int st = check_shape(M, N, K, group);
+    if (st != W4A16_OK) return st;
+    st = check_buffers(x, wq, s, b, y);
+    if (st != W4A16_OK) return st;
+    if (!workspace) return W4A16_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return W4A16_ERR_ALIGN;
+    const W4A8Act a = w4a8_act_bytes(M, K);
+    if (ws_bytes < a.total) return W4A16_ERR_WORKSPACE;
+    uint8_t* base = static_cast<uint8_t*>(workspace);
+    int8_t* xq = reinterpret_cast<int8_t*>(base);
+    float* sx = reinterpret_cast<float*>(base + a.xq);
+    uint16_t* xsum = reinterpret_cast<uint16_t*>(base + a.xq + a.sx);
+    st = run_quantize_rows(x, xq, sx, xsum, M, K, group, stream);
+    if (st != W4A16_OK) return st;
+    return run_w4a8(xq, sx, xsum, wq, s, b, y, M, N, K, group, 0, base + a.total, ws_bytes - a.total, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -448,6 +558,37 @@ int w4a16_gate_up_swiglu(const uint16_t* x, const uint32_t* wq_gate, const uint1
                          int32_t split_k, void* workspace, size_t workspace_bytes, void* stream) {
     return run_gate_up(x, wq_gate, scales_gate, biases_gate, wq_up, scales_up, biases_up, h, M, N, K, group, split_k,
                        workspace, workspace_bytes, stream);
+}
+
+int64_t w4a8_xsum_cols(int64_t K) {
+    if (K < 1 || K > kMaxK || K % W4A16_GROUP != 0) return 0;
+    return w4a8_xsum_cols(static_cast<int>(K));
+}
+
+int w4a8_quantize_rows(const uint16_t* x, int8_t* xq, float* sx, uint16_t* xsum, int64_t M, int64_t K, int32_t group,
+                       void* stream) {
+    return run_quantize_rows(x, xq, sx, xsum, M, K, group, stream);
+}
+
+int w4a8_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, int32_t num_cus, w4a16_plan_t* out) {
+    return make_w4a8_plan(M, N, K, group, split_k, num_cus, out);
+}
+
+int qmm_w4a8(const int8_t* xq, const float* sx, const uint16_t* xsum, const uint32_t* wq, const uint16_t* scales,
+             const uint16_t* biases, uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k,
+             void* workspace, size_t workspace_bytes, void* stream) {
+    return run_w4a8(xq, sx, xsum, wq, scales, biases, y, M, N, K, group, split_k, workspace, workspace_bytes, stream);
+}
+
+uint64_t w4a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t num_cus) {
+    w4a16_plan_t p;
+    if (make_w4a8_plan(M, N, K, group, 0, num_cus, &p) != W4A16_OK) return 0;
+    return w4a8_act_bytes(M, K).total + p.workspace_bytes;
+}
+
+int w4a8_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, uint16_t* y,
+                int64_t M, int64_t N, int64_t K, int32_t group, void* workspace, size_t workspace_bytes, void* stream) {
+    return run_w4a8_linear(x, wq, scales, biases, y, M, N, K, group, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

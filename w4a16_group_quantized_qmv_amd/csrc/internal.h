@@ -77,6 +77,18 @@ constexpr int kQmvBitsMatrix = 0, kQmvBitsRows = 1;
 hipError_t launch_qmv_bits(int bits, int mode, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
                            const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream);
 
+// W4A8: per-row int8 activations (codes stored in the int8 kernel's operand order, one fp32
+// scale per row, exact per-group code sums as bf16 hi / lo pairs in xsum [M, KB]) and the int8
+// tile kernel.  split > 1 writes fp32 partials ws[z][M][N], summed by launch_splitk_reduce.
+inline int w4a8_xsum_cols(int K) { return ((2 * (K / 128) + 15) / 16) * 16; }
+hipError_t launch_quantize_rows_int8(const uint16_t* x, int8_t* xq, float* sx, uint16_t* xsum, int M, int K, int KB,
+                                     hipStream_t stream);
+constexpr int kNumW4A8Variants = 3;
+extern const QmmShape kW4A8Variants[kNumW4A8Variants];
+hipError_t launch_qmm_w4a8(int variant, const int8_t* xq, const float* sx, const uint16_t* xsum, const uint32_t* wq,
+                           const uint16_t* scales, const uint16_t* biases, uint16_t* y, float* ws, int M, int N,
+                           int K, int KB, int split, hipStream_t stream);
+
 // y[i] = bf16(sum_{z < split} ws[z][i]) summed in slice order.
 hipError_t launch_splitk_reduce(const float* ws, uint16_t* y, int64_t MN, int split, hipStream_t stream);
 
