@@ -318,3 +318,23 @@ def test_w4a8_entry_points_validate_before_launch(lib):
 
     assert linear(x=None) == 1 and linear(M=0) == 2 and linear(x=ODD) == 4
     assert linear(ws=None) == 5 and linear(nbytes=100) == 5 and linear(ws=A16 * 16 + 16) == 4
+
+
+def test_exact_code_mode_plans():
+    # above 1024 rows the 128-row tiles run the exact-code mode: the plan reports the tile
+    # variant + 10 and the workspace starts with the activations' group sums (bf16 [M, KB])
+    r256 = lambda v: -(-v // 256) * 256
+    for M, N, K in [(1025, 9728, 2560), (4096, 2560, 9728), (4096, 151936, 2560), (2048, 1024, 256)]:
+        p = plan(M, N, K)
+        assert p["path"] == w4.PATH_QMM and p["tile_m"] == 128 and p["variant"] >= 10
+        sums = r256(M * w4.w4a8_xsum_cols(K) * 2)
+        parts = p["split_k"] * M * N * 4 if p["split_k"] > 1 else 0
+        assert p["workspace_bytes"] == sums + parts
+        assert w4.w4a16_workspace_bytes(M, N, K, 128, CUS) == p["workspace_bytes"]
+    # 1024 rows and fewer dequantize in registers (no group sums)
+    for M in (33, 512, 1024):
+        p = plan(M, 9728, 2560)
+        assert p["variant"] < 10
+        assert p["workspace_bytes"] == (p["split_k"] * M * 9728 * 4 if p["split_k"] > 1 else 0)
+    # the fused gate / up pair always dequantizes
+    assert gate_up_plan(4096, 9728, 2560)["variant"] < 10

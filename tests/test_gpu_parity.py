@@ -478,3 +478,69 @@ def test_gate_up_policy_split_without_workspace_falls_back(lib):
     h = run_gate_up(lib, x, gate, up, split_k=0, workspace=None)
     assert np.array_equal(h, run_gate_up(lib, x, gate, up, split_k=1))
     assert_swiglu_parity(h, x, gate, up)
+
+
+# ---------------------------------------------------------------------------------- exact-code mode
+# Above 1024 rows the 128-row tiles multiply the raw codes on the matrix core and scale each
+# group's fp32 product once (acc += s * P), adding sum_g b X from the activations' group sums;
+# without workspace for those sums the plan falls back to dequantizing in registers.
+
+def exact_code_plan(lib, M, N, K, split=0):
+    p = lib.w4a16_plan(M, N, K, 128, lib.PATH_QMM if split else lib.PATH_AUTO, split)
+    assert p["variant"] >= 10, "expected the exact-code mode"
+    return p
+
+
+def test_exact_code_mode_identity_is_bit_exact(lib):
+    q, p = identity_problem(K=1152, N=96, seed=31)      # M = K = 1152 > 1024 rows
+    exact_code_plan(lib, 1152, 96, 1152)
+    y = run(lib, p, "linear")
+    assert np.array_equal(y, synth.to_bf16_bits(q.T.astype(np.float32))), "exact-code unpack / indexing mismatch"
+
+
+def test_exact_code_mode_power_of_two_affine_is_bit_exact(lib):
+    # x = I, s = 2^-6, b = -8 * 2^-6: y[k, n] = (q[n, k] - 8) / 64 exactly (the bias term b * X
+    # with X = 1 for the group holding k)
+    K, N = 1280, 160
+    q, p = identity_problem(K=K, N=N, seed=32)
+    G = K // 128
+    p["scales"], p["biases"] = synth.const_bf16(2.0 ** -6, (N, G)), synth.const_bf16(-8.0 * 2.0 ** -6, (N, G))
+    exact_code_plan(lib, K, N, K)
+    y = run(lib, p, "linear")
+    assert np.array_equal(y, synth.to_bf16_bits(((q.T - 8) / 64.0).astype(np.float32)))
+
+
+@pytest.mark.parametrize("split", [0, 2])
+def test_exact_code_mode_bias_term_is_exact(lib, split):
+    # s = 0 and small-integer activations: y = sum_g b[n, g] X[m, g] with exact group sums
+    M, N, K = 1100, 130, 2560
+    G = K // 128
+    rng = np.random.default_rng(33)
+    xv = rng.integers(-3, 4, (M, K)).astype(np.float32)
+    bias = (((np.arange(N)[:, None] % 7) - 3) / 4.0 * np.where(np.arange(G)[None, :] % 2, -1.0, 1.0)).astype(np.float32)
+    p = {"x": synth.to_bf16_bits(xv), "wq": synth.pack_codes(rng.integers(0, 16, (N, K))),
+         "scales": synth.const_bf16(0.0, (N, G)), "biases": synth.to_bf16_bits(bias), "M": M, "N": N, "K": K}
+    if split:
+        exact_code_plan(lib, M, N, K, split)
+    y = run(lib, p, "qmm" if split else "linear", split or None)
+    X = xv.reshape(M, G, 128).sum(axis=2)
+    assert np.array_equal(y, synth.to_bf16_bits((X @ bias.T).astype(np.float32)))
+
+
+def test_exact_code_and_dequantizing_forms_match_the_oracle(lib):
+    import torch
+    p = synth.random_problem(34, 1500, 640, 2560)
+    exact_code_plan(lib, 1500, 640, 2560)
+    x, wq, s, b = to_device(p)
+    announce("exact-code vs dequantizing form M=1500 N=640 K=2560")
+    y_codes = lib.w4a16_linear(x, wq, s, b)
+    y_deq = torch.empty_like(y_codes)
+    st = lib.load().w4a16_linear(x.data_ptr(), wq.data_ptr(), s.data_ptr(), b.data_ptr(), y_deq.data_ptr(),
+                                 1500, 640, 2560, 128, None, 0, None)   # no workspace: dequantizing form
+    assert st == 0
+    torch.cuda.synchronize()
+    yc, yd = bits(y_codes), bits(y_deq)
+    assert not np.array_equal(yc, yd), "both calls ran the same form"
+    rows = sample_rows(1500, 16)
+    rc, rd = assert_parity(yc, p, rows=rows), assert_parity(yd, p, rows=rows)
+    announce(f"exact-code {rc}; dequantizing {rd}")

@@ -106,9 +106,18 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
     p->workspace_bytes = 0;
 }
 
-// skinny: 32-row tiles and the skinny split rule (rows 17..32, or a wide head at 9..16 rows)
+uint64_t round256(uint64_t v) { return (v + 255) / 256 * 256; }
+
+// Bytes of the activations' group sums (exact-code mode), at the start of the workspace.
+uint64_t group_sum_bytes(int64_t M, int64_t K) {
+    return round256(static_cast<uint64_t>(M) * group_sum_cols(static_cast<int>(K)) * 2);
+}
+
+// skinny: 32-row tiles and the skinny split rule (rows 17..32, or a wide head at 9..16 rows).
+// codes: the exact-code mode (codes on the matrix core, per-group scaling, bias from the group
+// sums of the activations), which needs the group sums in the workspace.
 void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p,
-              bool skinny = false) {
+              bool skinny = false, bool codes = true) {
     const int64_t G = K / W4A16_GROUP;
     // Measured on MI355X: 64 x 128 tiles (four waves per SIMD) lead up to about a thousand
     // rows, where the grid is small; 128 x 128 tiles (two waves per SIMD) lead beyond.  For at
@@ -151,9 +160,14 @@ void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a
     p->block_threads = 64 * v.nwaves;
     p->split_k = static_cast<int32_t>(S);
     p->k_waves = 1;
-    p->variant = variant;
-    p->workspace_bytes = S > 1 ? static_cast<uint64_t>(S) * M * N * sizeof(float) : 0;
+    codes = codes && variant == kQmmCodesTileVariant;
+    p->variant = variant + (codes ? kQmmCodesVariantOffset : 0);
+    p->workspace_bytes = (codes ? group_sum_bytes(M, K) : 0) +
+                         (S > 1 ? static_cast<uint64_t>(S) * M * N * sizeof(float) : 0);
 }
+
+bool plan_codes(const w4a16_plan_t& p) { return p.variant >= kQmmCodesVariantOffset; }
+int plan_tile_variant(const w4a16_plan_t& p) { return p.variant % kQmmCodesVariantOffset; }
 
 // Skinny rows (at most 32): up to 16 rows the matvec kernels (their 16-row MFMA operand covers
 // them; measured 1.1-1.7x faster than tiles at 9..16 rows), except where the wide kernel's
@@ -212,10 +226,39 @@ int run_plan(const w4a16_plan_t& p, const uint16_t* x, const uint32_t* wq, const
              uint16_t* y, int64_t M, int64_t N, int64_t K, void* workspace, hipStream_t stream) {
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     if (uses_qmv_kernels(p)) return to_status(launch_qmv(p.variant, x, wq, s, b, y, m, n, k, stream));
-    float* ws = static_cast<float*>(workspace);
-    hipError_t e = launch_qmm(p.variant, x, wq, s, b, y, ws, m, n, k, p.split_k, stream);
+    // workspace: [group sums (exact-code mode)][fp32 split-K partials]
+    uint16_t* xsum = nullptr;
+    uint8_t* rest = static_cast<uint8_t*>(workspace);
+    if (plan_codes(p)) {
+        xsum = static_cast<uint16_t*>(workspace);
+        rest += group_sum_bytes(M, K);
+        const hipError_t e0 = launch_act_group_sums(x, xsum, m, k, group_sum_cols(k), stream);
+        if (e0 != hipSuccess) return to_status(e0);
+    }
+    float* ws = reinterpret_cast<float*>(rest);
+    hipError_t e = launch_qmm(plan_tile_variant(p), x, xsum, wq, s, b, y, ws, m, n, k, p.split_k, stream);
     if (e != hipSuccess || p.split_k == 1) return to_status(e);
     return to_status(launch_splitk_reduce(ws, y, M * N, p.split_k, stream));
+}
+
+// Fit a tile plan to the caller's workspace: the exact-code mode needs the group sums, a split
+// needs the partials.  Without room the plan drops the exact-code mode (same result within the
+// tolerance), then, under the policy, the split (the unsplit plan computes the same result); a
+// forced split with too little room for its partials is an error.
+template <typename Replan>
+int fit_workspace(w4a16_plan_t& p, int32_t split_k, void* workspace, size_t ws_bytes, Replan replan) {
+    auto fits = [&](const w4a16_plan_t& q) {
+        return q.workspace_bytes == 0 || (workspace != nullptr && aligned(workspace, 16) && ws_bytes >= q.workspace_bytes);
+    };
+    if (fits(p)) return W4A16_OK;
+    if (plan_codes(p)) {
+        replan(p.split_k, false);
+        if (fits(p)) return W4A16_OK;
+    }
+    if (split_k > 1)
+        return workspace != nullptr && !aligned(workspace, 16) ? W4A16_ERR_ALIGN : W4A16_ERR_WORKSPACE;
+    replan(1, false);
+    return W4A16_OK;
 }
 
 int run_qmm(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b, uint16_t* y, int64_t M,
@@ -229,14 +272,14 @@ int run_qmm(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint
     w4a16_plan_t p;
     st = make_plan(M, N, K, group, path, split_k, 0, &p);
     if (st != W4A16_OK) return st;
-    if (!uses_qmv_kernels(p) && p.split_k > 1) {
-        const bool ws_ok = workspace != nullptr && aligned(workspace, 16) && ws_bytes >= p.workspace_bytes;
-        if (!ws_ok) {
-            if (split_k > 1) return workspace != nullptr && !aligned(workspace, 16) ? W4A16_ERR_ALIGN
-                                                                                     : W4A16_ERR_WORKSPACE;
-            // policy split without a usable workspace: the unsplit plan computes the same result
-            plan_qmm(M, N, K, 1, p.num_cus, &p, p.path == W4A16_PATH_SKINNY);
-        }
+    if (!uses_qmv_kernels(p)) {
+        const bool skinny = p.path == W4A16_PATH_SKINNY;
+        const int32_t cus = p.num_cus;
+        st = fit_workspace(p, split_k, workspace, ws_bytes, [&](int32_t S, bool codes) {
+            plan_qmm(M, N, K, S, cus, &p, skinny, codes);
+            p.num_cus = cus;
+        });
+        if (st != W4A16_OK) return st;
     }
     return run_plan(p, x, wq, s, b, y, M, N, K, workspace, static_cast<hipStream_t>(stream));
 }
@@ -244,8 +287,9 @@ int run_qmm(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint
 // Gate / up pair with SwiGLU: one tile kernel computes both projections of the same columns.
 // Tile rows as for qmm (32 up to 32 rows, 64 up to ~1k, 128 beyond); the split follows the
 // matching qmm rule; the workspace holds the gate and up partials (2 * S * M * N fp32).
+// The pair always dequantizes (its exact-code form needs twice the P registers and spills).
 void plan_gate_up(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p) {
-    plan_qmm(M, N, K, split_k, cus, p, M <= kSkinnyMaxRows);
+    plan_qmm(M, N, K, split_k, cus, p, M <= kSkinnyMaxRows, false);
     const int variant = M <= kSkinnyMaxRows ? 0 : (M <= 1024 ? 1 : 2);
     const QmmShape& v = kGateUpVariants[variant];
     const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
@@ -290,18 +334,16 @@ int run_gate_up(const uint16_t* x, const uint32_t* wq_g, const uint16_t* s_g, co
     w4a16_plan_t p;
     st = make_gate_up_plan(M, N, K, group, split_k, 0, &p);
     if (st != W4A16_OK) return st;
-    if (p.split_k > 1) {
-        const bool ws_ok = workspace != nullptr && aligned(workspace, 16) && ws_bytes >= p.workspace_bytes;
-        if (!ws_ok) {
-            if (split_k > 1) return workspace != nullptr && !aligned(workspace, 16) ? W4A16_ERR_ALIGN
-                                                                                     : W4A16_ERR_WORKSPACE;
-            plan_gate_up(M, N, K, 1, p.num_cus, &p);   // the unsplit plan computes the same result
-        }
-    }
+    const int32_t cus = p.num_cus;
+    st = fit_workspace(p, split_k, workspace, ws_bytes, [&](int32_t S, bool) {
+        plan_gate_up(M, N, K, S, cus, &p);
+        p.num_cus = cus;
+    });
+    if (st != W4A16_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     float* ws = static_cast<float*>(workspace);
-    hipError_t e = launch_gate_up(p.variant, x, wq_g, s_g, b_g, wq_u, s_u, b_u, h, ws, static_cast<int>(M),
-                                  static_cast<int>(N), static_cast<int>(K), p.split_k, s);
+    hipError_t e = launch_gate_up(p.variant, x, nullptr, wq_g, s_g, b_g, wq_u, s_u, b_u, h, ws,
+                                  static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), p.split_k, s);
     if (e != hipSuccess || p.split_k == 1) return to_status(e);
     return to_status(launch_splitk_reduce_glu(ws, h, M * N, p.split_k, s));
 }
@@ -373,7 +415,7 @@ int run_qmv_affine(const uint16_t* x, const uint32_t* wq, const uint16_t* s, con
 // list and Related work): tiles of 32 rows up to 32 rows, 64 up to ~1k, 128 beyond; the split
 // rule of the W4A16 tiles.  workspace_bytes covers the fp32 partials only.
 void plan_w4a8(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p) {
-    plan_qmm(M, N, K, split_k, cus, p, M <= kSkinnyMaxRows);
+    plan_qmm(M, N, K, split_k, cus, p, M <= kSkinnyMaxRows, false);
     const int variant = M <= kSkinnyMaxRows ? 0 : (M <= 1024 ? 1 : 2);
     const QmmShape& v = kW4A8Variants[variant];
     const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
@@ -404,8 +446,6 @@ int make_w4a8_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t split
     out->num_cus = cus;
     return W4A16_OK;
 }
-
-uint64_t round256(uint64_t v) { return (v + 255) / 256 * 256; }
 
 // Byte sizes of the activation buffers that w4a8_linear carves from its workspace.
 struct W4A8Act {

@@ -56,8 +56,21 @@ constexpr int kNumQmmVariants = 5;
 constexpr int kQmmSkinnyVariant = 4;   // 32 x 128 tiles, three stages: at most 32 rows
 extern const QmmShape kQmmVariants[kNumQmmVariants];
 
-// split == 1 writes bf16 y; split > 1 writes fp32 partials ws[z][M][N] for z < split.
-hipError_t launch_qmm(int variant, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+// Columns of a per-row group-sum buffer: two bf16 halves per 128-value group, rounded up to the
+// 16-value MFMA step.
+inline int group_sum_cols(int K) { return ((2 * (K / 128) + 15) / 16) * 16; }
+// Exact-code mode of the tile kernels needs the activations' group sums: xsum [M, KB] bf16,
+// columns 2g / 2g + 1 = hi / lo of the fp32 sum of group g, zeros beyond 2G.
+hipError_t launch_act_group_sums(const uint16_t* x, uint16_t* xsum, int M, int K, int KB, hipStream_t stream);
+// Plans report the exact-code mode as the tile variant plus this offset.  It is compiled for the
+// 128-row tiles (variant kQmmCodesTileVariant), where it measured faster than dequantizing.
+constexpr int kQmmCodesVariantOffset = 10;
+constexpr int kQmmCodesTileVariant = 0;
+
+// split == 1 writes bf16 y; split > 1 writes fp32 partials ws[z][M][N] for z < split.  xsum != nullptr
+// selects the exact-code mode (codes on the matrix core, y = sum_g s P + sum_g b X), else weights are
+// dequantized to bf16 in registers.
+hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, const uint32_t* wq, const uint16_t* scales,
                       const uint16_t* biases, uint16_t* y, float* ws, int M, int N, int K, int split,
                       hipStream_t stream);
 
@@ -65,9 +78,10 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint32_t* wq, const 
 // projections.  split > 1 writes fp32 partials ws[0][z][M][N] (gate) and ws[1][z][M][N] (up).
 constexpr int kNumGateUpVariants = 3;
 extern const QmmShape kGateUpVariants[kNumGateUpVariants];
-hipError_t launch_gate_up(int variant, const uint16_t* x, const uint32_t* wq_gate, const uint16_t* s_gate,
-                          const uint16_t* b_gate, const uint32_t* wq_up, const uint16_t* s_up, const uint16_t* b_up,
-                          uint16_t* h, float* ws, int M, int N, int K, int split, hipStream_t stream);
+hipError_t launch_gate_up(int variant, const uint16_t* x, const uint16_t* xsum, const uint32_t* wq_gate,
+                          const uint16_t* s_gate, const uint16_t* b_gate, const uint32_t* wq_up, const uint16_t* s_up,
+                          const uint16_t* b_up, uint16_t* h, float* ws, int M, int N, int K, int split,
+                          hipStream_t stream);
 // h[i] = bf16(silu(sum_z ws[0][z][i]) * sum_z ws[1][z][i]), slices summed in order.
 hipError_t launch_splitk_reduce_glu(const float* ws, uint16_t* h, int64_t MN, int split, hipStream_t stream);
 
@@ -80,7 +94,7 @@ hipError_t launch_qmv_bits(int bits, int mode, const uint16_t* x, const uint32_t
 // W4A8: per-row int8 activations (codes stored in the int8 kernel's operand order, one fp32
 // scale per row, exact per-group code sums as bf16 hi / lo pairs in xsum [M, KB]) and the int8
 // tile kernel.  split > 1 writes fp32 partials ws[z][M][N], summed by launch_splitk_reduce.
-inline int w4a8_xsum_cols(int K) { return ((2 * (K / 128) + 15) / 16) * 16; }
+inline int w4a8_xsum_cols(int K) { return group_sum_cols(K); }
 hipError_t launch_quantize_rows_int8(const uint16_t* x, int8_t* xq, float* sx, uint16_t* xsum, int M, int K, int KB,
                                      hipStream_t stream);
 constexpr int kNumW4A8Variants = 3;

@@ -57,12 +57,12 @@ __device__ __forceinline__ float silu_f32(float z) { return z / (1.f + expf(-z))
 // gate / up pair with h = silu(gate) * up formed from the fp32 accumulators in the epilogue
 // (the SwiGLU fused into the mat-mat of "Feature Request: Metal prefill speedup (~68%) on M5
 // Max").  Weight set p of column block cb is block j = p * NB + cb.
-template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES, int NP = 1>
+template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES, int NP = 1, int CODES = 0>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD))) void qmm_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const uint32_t* __restrict__ wq2, const uint16_t* __restrict__ scales2,
     const uint16_t* __restrict__ biases2, uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N, int K,
-    int split, int tiles_m, int tiles_n) {
+    int split, int tiles_m, int tiles_n, const uint16_t* __restrict__ xsum, int KB) {
     constexpr int BN = NW * NB * 32;              // output columns of the tile (per weight set)
     constexpr int J = NP * NB;                    // weight blocks per wave
     static_assert(NP == 1 || NP == 2, "one projection or the gate / up pair");
@@ -150,7 +150,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
         u32x4_t w[J][2];
         uint16_t s[J], b[J];
     };
-    constexpr int kLoadsPerGroup = DMA_PER_WAVE + 4 * J;
+    // exact-code mode reads the biases once, in the epilogue
+    constexpr int kLoadsPerGroup = DMA_PER_WAVE + (CODES > 0 ? 3 : 4) * J;
     // all loads of group g (relative index j = g - g_begin) into stage / slot ic
     auto issue = [&](int j, auto ic, Slot& o) {
         const bool live = j >= 0 && j < groups;
@@ -177,8 +178,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
             asm volatile("" ::: "memory");
             o.s[j] = __builtin_amdgcn_raw_buffer_load_b16(sr, sbvoff[cb], g * 2, 0);
             asm volatile("" ::: "memory");
-            o.b[j] = __builtin_amdgcn_raw_buffer_load_b16(br, sbvoff[cb], g * 2, 0);
-            asm volatile("" ::: "memory");
+            if constexpr (CODES == 0) {
+                o.b[j] = __builtin_amdgcn_raw_buffer_load_b16(br, sbvoff[cb], g * 2, 0);
+                asm volatile("" ::: "memory");
+            } else {
+                (void)br;
+                o.b[j] = 0;
+            }
         }
     };
 
@@ -201,6 +207,84 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     // the MFMAs of sub-step t run, the fragment reads and the dequantization of sub-step t + 1
     // are already issued.  The scheduling barrier at the end of each sub-step bounds the live
     // registers to two sub-steps' operands.
+    // Exact-code mode (CODES > 0): the matrix core multiplies the raw codes (exact bf16
+    // integers), giving the group's P = sum_k x q in fp32, which is scaled into the accumulators,
+    // acc += s * P.  CODES == 1 scales right after the group's last MFMA (one P set; other waves
+    // cover the wait); CODES == 2 spreads the scaling of group t over the MFMAs of group t + 1
+    // (a ring of STAGES P sets, one per pipeline position).  The bias term sum_g b X is added
+    // once per tile from the group sums of the activations.
+    constexpr int PSETS = CODES == 2 ? STAGES : 1;
+    f32x16_t Pr[PSETS][RB][J];
+    float s_last[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) s_last[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < PSETS; ++i)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) Pr[i][rb][j][r] = 0.f;
+    auto compute_codes = [&](auto ic, const Slot& o, auto pc) {
+        constexpr int PC = PSETS == 1 ? 0 : decltype(pc)::value;
+        constexpr int PP = PSETS == 1 ? 0 : (PC + STAGES - 1) % STAGES;
+        const uint16_t* xt = stage(ic);
+        bf16x8_t a[2][RB], bw[2][J];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) a[0][rb] = *reinterpret_cast<const bf16x8_t*>(xt + abase + rb * 32 * kGroup);
+#pragma unroll
+        for (int j = 0; j < J; ++j) bw[0][j] = codes_bf16_natural(o.w[j][0][0]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int cur = t & 1, nxt = cur ^ 1;
+            if (t < 7) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    a[nxt][rb] = *reinterpret_cast<const bf16x8_t*>(xt + (abase ^ ((t + 1) << 3)) + rb * 32 * kGroup);
+#pragma unroll
+                for (int j = 0; j < J; ++j) bw[nxt][j] = codes_bf16_natural(o.w[j][(t + 1) >> 2][(t + 1) & 3]);
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    const f32x16_t zero = {};
+                    Pr[PC][rb][j] = mfma32x32x16(a[cur][rb], bw[cur][j], t == 0 ? zero : Pr[PC][rb][j]);
+                }
+            if constexpr (PSETS > 1) {
+                // an eighth of the previous group's scaling per sub-step
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int j = 0; j < J; ++j)
+#pragma unroll
+                        for (int r = 2 * t; r < 2 * t + 2; ++r)
+                            acc[rb][j][r] = __builtin_fmaf(s_last[j], Pr[PP][rb][j][r], acc[rb][j][r]);
+            }
+#pragma unroll
+            for (int i = 0; i < RB * J; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, (11 * J + 2 * RB * J + RB * J - 1) / (RB * J), 0);  // VALU
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              // LDS read
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (PSETS == 1) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    const float sj = bf16_bits_to_f32(o.s[j]);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[rb][j][r] = __builtin_fmaf(sj, Pr[0][rb][j][r], acc[rb][j][r]);
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < J; ++j) s_last[j] = bf16_bits_to_f32(o.s[j]);
+        }
+    };
+
     auto compute = [&](auto ic, const Slot& o) {
         float s[J], b[J];
 #pragma unroll
@@ -271,7 +355,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
                 asm volatile("" ::: "memory");                                                   \
             }                                                                                    \
             issue(t + STAGES - 1, I{}, SLOT_IN);                                                 \
-            if (t >= 0) compute(C{}, SLOT_C);                                                    \
+            if (t >= 0) {                                                                        \
+                if constexpr (CODES > 0) compute_codes(C{}, SLOT_C, I{});                        \
+                else compute(C{}, SLOT_C);                                                       \
+            }                                                                                    \
             ++t;                                                                                 \
         }
         for (;;) {
@@ -283,6 +370,51 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
 #undef W4A16_QMM_STEP
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no direct load may outlive the wave
+
+    if constexpr (CODES > 0) {
+        if constexpr (PSETS > 1) {
+            // the last group computed sits in the P set of the body's last position
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int j = 0; j < J; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        acc[rb][j][r] = __builtin_fmaf(s_last[j], Pr[STAGES - 1][rb][j][r], acc[rb][j][r]);
+        }
+        // bias term, once per output (slice 0): acc += xsum . baug^T over KB / 16 sub-steps, with
+        // baug[n, k'] = b[n, k' / 2] (zero for k' / 2 >= G) against the hi / lo halves of X
+        if (z == 0) {
+            const __amdgpu_buffer_rsrc_t xsr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(xsum + static_cast<size_t>(m0) * KB), 0,
+                clamp_records(static_cast<int64_t>(M - m0) * KB * 2), 0x00020000);
+            for (int u = 0; u < KB / 16; ++u) {
+                const int g0 = 8 * u + 4 * half;
+                bf16x8_t bfrag[J];
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    const int p = j / NB, cb = j % NB;
+                    uint32_t bb[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t off = sbvoff[cb] + static_cast<uint32_t>(g0 + i < G ? g0 + i : 0) * 2u;
+                        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b16(brsrc[p], off, 0, 0);
+                        bb[i] = g0 + i < G ? v : 0u;
+                    }
+                    bfrag[j] = __builtin_bit_cast(bf16x8_t, u32x4_t{bb[0] | (bb[0] << 16), bb[1] | (bb[1] << 16),
+                                                                    bb[2] | (bb[2] << 16), bb[3] | (bb[3] << 16)});
+                }
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const uint32_t off = static_cast<uint32_t>(((rb * 32 + arow) * KB + 16 * u + 8 * half) * 2);
+                    const bf16x8_t afrag =
+                        __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(xsr, off, 0, 0));
+#pragma unroll
+                    for (int j = 0; j < J; ++j) acc[rb][j] = mfma32x32x16(afrag, bfrag[j], acc[rb][j]);
+                }
+            }
+        }
+    }
 
     // epilogue: D layout puts rows 8 * (r / 4) + 4 * half + r % 4 of column lane % 32 in this lane
 #pragma unroll
@@ -316,6 +448,44 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     }
 }
 
+// Group sums of the activations for the exact-code mode: one workgroup per row; X[m, g] is the
+// fp32 sum of the group's 128 values (each lane adds 8, then a fixed xor tree over the 16 lanes
+// of the group), stored as hi = bf16(X) and lo = bf16(X - hi) at columns 2g and 2g + 1 of xsum
+// [M, KB]; columns 2G .. KB - 1 are zero.
+__global__ __launch_bounds__(256) void act_group_sums_kernel(const uint16_t* __restrict__ x,
+                                                             uint16_t* __restrict__ xsum, int K, int KB) {
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int chunks = K >> 3;
+    const uint16_t* xr = x + static_cast<size_t>(m) * K;
+    uint16_t* out = xsum + static_cast<size_t>(m) * KB;
+    const int iters = (chunks + 255) >> 8;
+    for (int it = 0; it < iters; ++it) {
+        const int c = tid + 256 * it;
+        const bool valid = c < chunks;     // uniform over each 16-lane group (chunks % 16 == 0)
+        float v = 0.f;
+        if (valid) {
+            const u32x4_t q = load16(xr + 8 * c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v += __uint_as_float(q[i] << 16) + __uint_as_float(q[i] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+        if (valid && (tid & 15) == 0) {
+            const int g = c >> 4;
+            const uint16_t hi = f32_to_bf16_bits(v);
+            out[2 * g] = hi;
+            out[2 * g + 1] = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+        }
+    }
+    for (int k = 2 * (K >> 7) + tid; k < KB; k += 256) out[k] = 0;
+}
+
+hipError_t launch_act_group_sums(const uint16_t* x, uint16_t* xsum, int M, int K, int KB, hipStream_t stream) {
+    hipLaunchKernelGGL(act_group_sums_kernel, dim3(M), dim3(256), 0, stream, x, xsum, K, KB);
+    return hipGetLastError();
+}
+
 // gate / up pair: h = bf16(silu(sum_z gate partial) * sum_z up partial), slices in order
 __global__ __launch_bounds__(256) void splitk_reduce_glu_kernel(const float* __restrict__ ws, uint16_t* __restrict__ h,
                                                                 int64_t MN, int split) {
@@ -346,40 +516,60 @@ const QmmShape kQmmVariants[kNumQmmVariants] = {
     {32, 1, 4, 3},   // 4:  32 x 128 tile, four waves per SIMD, 3 stages (skinny M)
 };
 
-template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES>
-static hipError_t launch_qmm_t(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
-                               uint16_t* y, float* ws, int M, int N, int K, int split, hipStream_t stream) {
+template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES, int CM = 0, int CODES_WPS = WAVES_PER_SIMD>
+static hipError_t launch_qmm_t(const uint16_t* x, const uint16_t* xsum, int KB, const uint32_t* wq, const uint16_t* s,
+                               const uint16_t* b, uint16_t* y, float* ws, int M, int N, int K, int split,
+                               hipStream_t stream) {
     constexpr int BN = NW * NB * 32;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const dim3 grid(tiles_m * tiles_n * split);
-    hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WAVES_PER_SIMD, STAGES>), grid, dim3(64 * NW), 0, stream, x, wq, s, b,
-                       nullptr, nullptr, nullptr, y, ws, M, N, K, split, tiles_m, tiles_n);
+    if constexpr (CM > 0) {
+        if (xsum) {
+            hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, CODES_WPS, STAGES, 1, CM>), grid, dim3(64 * NW), 0, stream, x,
+                               wq, s, b, nullptr, nullptr, nullptr, y, ws, M, N, K, split, tiles_m, tiles_n, xsum, KB);
+            return hipGetLastError();
+        }
+    }
+        hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WAVES_PER_SIMD, STAGES>), grid, dim3(64 * NW), 0, stream, x, wq, s,
+                           b, nullptr, nullptr, nullptr, y, ws, M, N, K, split, tiles_m, tiles_n, nullptr, 0);
     return hipGetLastError();
 }
 
-template <int BM, int WAVES_PER_SIMD, int STAGES>
-static hipError_t launch_gate_up_t(const uint16_t* x, const uint32_t* wg, const uint16_t* sg, const uint16_t* bg,
-                                   const uint32_t* wu, const uint16_t* su, const uint16_t* bu, uint16_t* h, float* ws,
-                                   int M, int N, int K, int split, hipStream_t stream) {
+template <int BM, int WAVES_PER_SIMD, int STAGES, int CM = 0, int CODES_WPS = WAVES_PER_SIMD>
+static hipError_t launch_gate_up_t(const uint16_t* x, const uint16_t* xsum, int KB, const uint32_t* wg,
+                                   const uint16_t* sg, const uint16_t* bg, const uint32_t* wu, const uint16_t* su,
+                                   const uint16_t* bu, uint16_t* h, float* ws, int M, int N, int K, int split,
+                                   hipStream_t stream) {
     constexpr int BN = 4 * 32;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const dim3 grid(tiles_m * tiles_n * split);
-    hipLaunchKernelGGL((qmm_kernel<BM, 1, 4, WAVES_PER_SIMD, STAGES, 2>), grid, dim3(256), 0, stream, x, wg, sg, bg,
-                       wu, su, bu, h, ws, M, N, K, split, tiles_m, tiles_n);
+    if constexpr (CM > 0) {
+        if (xsum) {
+            hipLaunchKernelGGL((qmm_kernel<BM, 1, 4, CODES_WPS, STAGES, 2, CM>), grid, dim3(256), 0, stream, x, wg,
+                               sg, bg, wu, su, bu, h, ws, M, N, K, split, tiles_m, tiles_n, xsum, KB);
+            return hipGetLastError();
+        }
+    }
+    if (xsum) return hipErrorInvalidValue;   // the gate / up pair runs the dequantizing form
+    hipLaunchKernelGGL((qmm_kernel<BM, 1, 4, WAVES_PER_SIMD, STAGES, 2>), grid, dim3(256), 0, stream, x, wg, sg,
+                           bg, wu, su, bu, h, ws, M, N, K, split, tiles_m, tiles_n, nullptr, 0);
     return hipGetLastError();
 }
 
-hipError_t launch_qmm(int variant, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, const uint32_t* wq, const uint16_t* scales,
                       const uint16_t* biases, uint16_t* y, float* ws, int M, int N, int K, int split,
                       hipStream_t stream) {
+    const int KB = group_sum_cols(K);
+    // the exact-code mode is compiled for the 128-row tiles, where it measured faster
+    if (xsum && variant != kQmmCodesTileVariant) return hipErrorInvalidValue;
     switch (variant) {
-        case 0: return launch_qmm_t<128, 1, 4, 2, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 1: return launch_qmm_t<64, 1, 4, 4, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 2: return launch_qmm_t<64, 1, 4, 2, 3>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 3: return launch_qmm_t<32, 1, 4, 4, 2>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 4: return launch_qmm_t<32, 1, 4, 4, 3>(x, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 0: return launch_qmm_t<128, 1, 4, 2, 2, 2>(x, xsum, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 1: return launch_qmm_t<64, 1, 4, 4, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 2: return launch_qmm_t<64, 1, 4, 2, 3>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 3: return launch_qmm_t<32, 1, 4, 4, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 4: return launch_qmm_t<32, 1, 4, 4, 3>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -390,13 +580,18 @@ const QmmShape kGateUpVariants[kNumGateUpVariants] = {
     {128, 1, 4, 2},  // 2: 128 x 128 tile of h, one wave per SIMD
 };
 
-hipError_t launch_gate_up(int variant, const uint16_t* x, const uint32_t* wq_gate, const uint16_t* s_gate,
-                          const uint16_t* b_gate, const uint32_t* wq_up, const uint16_t* s_up, const uint16_t* b_up,
-                          uint16_t* h, float* ws, int M, int N, int K, int split, hipStream_t stream) {
+hipError_t launch_gate_up(int variant, const uint16_t* x, const uint16_t* xsum, const uint32_t* wq_gate,
+                          const uint16_t* s_gate, const uint16_t* b_gate, const uint32_t* wq_up, const uint16_t* s_up,
+                          const uint16_t* b_up, uint16_t* h, float* ws, int M, int N, int K, int split,
+                          hipStream_t stream) {
+    const int KB = group_sum_cols(K);
     switch (variant) {
-        case 0: return launch_gate_up_t<32, 4, 2>(x, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K, split, stream);
-        case 1: return launch_gate_up_t<64, 3, 2>(x, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K, split, stream);
-        case 2: return launch_gate_up_t<128, 1, 2>(x, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K, split, stream);
+        case 0: return launch_gate_up_t<32, 4, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K,
+                                                  split, stream);
+        case 1: return launch_gate_up_t<64, 3, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K,
+                                                  split, stream);
+        case 2: return launch_gate_up_t<128, 1, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N,
+                                                   K, split, stream);
         default: return hipErrorInvalidValue;
     }
 }
