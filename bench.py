@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A16 qmm TFLOP/s + % roofline at M=128/512 prefill; qmv GB/s at M=1"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA
 M_PREFILL = 512
 LAYER = ["q", "k", "v", "o", "gate", "up", "down"]
 DOMINANT = ("gate", "up")     # largest projections: the roofline kernel
@@ -258,7 +259,9 @@ def main():
         "breakdown": per,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
-    result["next_rows"] = next_rows(torch, w4, projections, args.copies)
+    gs = torch.cuda.Stream()             # graph capture needs a stream other than the null stream
+    with torch.cuda.stream(gs):
+        result["next_rows"] = next_rows(torch, w4, projections, args.copies)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(projections)
@@ -267,65 +270,193 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def time_call(torch, fns, reps):
-    """Average microseconds of one call, rotating over the prepared calls in ``fns`` (one per
-    weight copy), with HIP events on the launch stream around each call."""
+def time_call(torch, fns, reps, trials=5):
+    """Microseconds per call on the GPU: ``reps`` calls (rotating over ``fns``, one per weight
+    copy) are captured in one HIP graph on the current stream (the calls must have been prepared
+    on it) and replayed ``trials`` times between HIP events on that stream; the median replay
+    divided by ``reps``.  Replaying a graph removes the host's launch cost between calls, so short
+    kernels are timed back to back as a model's decode step would issue them."""
+    stream = torch.cuda.current_stream()
     for f in fns:
         f()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for i in range(reps):
-        ev[i][0].record()
-        fns[i % len(fns)]()
-        ev[i][1].record()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(reps):
+            fns[i % len(fns)]()
+    g.replay()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) * 1e3 / reps
+    per = []
+    for _ in range(trials):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        b.synchronize()
+        per.append(a.elapsed_time(b) * 1e3 / reps)
+    del g
+    return sorted(per)[len(per) // 2]
+
+
+ROTATE_BYTES = 600 << 20   # weight bytes cycled per timed case: over twice the 256 MB last-level cache
+
+
+def rotation(w, min_bytes=ROTATE_BYTES):
+    """The weight set ``w`` (wq, scales, biases) and enough device clones of it that one pass over
+    them reads at least ``min_bytes``, so every call's weights come from HBM."""
+    nbytes = sum(t.numel() * t.element_size() for t in w)
+    n = max(2, -(-min_bytes // nbytes))
+    return [w] + [tuple(t.clone() for t in w) for _ in range(n - 1)]
+
+
+def ws_for(torch, nbytes, device):
+    return torch.empty((nbytes + 3) // 4, dtype=torch.float32, device=device) if nbytes else None
 
 
 def next_rows(torch, w4, projections, copies, reps=20):
-    """Measurements of the rows beyond the step: the fused gate/up + SwiGLU pair at the step's
-    512 rows against the two separate projections, and the skinny path (16 and 32 rows) against
-    the 64-row tiles, on the layer's gate and down shapes."""
+    """Measurements of the rows beyond the step, each case timed alone on the current (side)
+    stream from a HIP graph over a weight rotation of more than 512 MB:
+      * the fused gate/up + SwiGLU pair at the step's 512 rows against the two projections and
+        against gate, up, then a framework-style bf16 SiLU and product;
+      * the skinny path (16 and 32 rows) against the 64-row tiles on the gate and down shapes;
+      * W4A8 (int8 activations) against W4A16 on the step's seven projections;
+      * the 4096-row prefill of gate / up / down and the vocabulary head over all rows;
+      * decode rows (M = 1, 4) on the four decode shapes, and the width-generic matvec at
+        1, 2, 4 and 8 bits."""
+    from w4a16_group_quantized_qmv_amd import synth
     by = {p["name"]: p for p in projections}
+    dev = by["gate"]["x"].device
+    out = {}
+
+    def timed(fns):
+        return time_call(torch, fns, max(reps, len(fns)))
+
+    # fused gate / up + SwiGLU
     gate, up = by["gate"], by["up"]
     x = gate["x"]
     M, N, K = gate["M"], gate["N"], gate["K"]
-    fused = [w4.PreparedGateUp(x, gate["w"][c], up["w"][c]) for c in range(copies)]
-    sep_g = [w4.PreparedLinear(x, *gate["w"][c]) for c in range(copies)]
-    sep_u = [w4.PreparedLinear(x, *up["w"][c], y=torch.empty_like(sep_g[0].y)) for c in range(copies)]
-    g_out, u_out = sep_g[0].y, sep_u[0].y
+    rot_g, rot_u = rotation(gate["w"][0]), rotation(up["w"][0])
+    n = min(len(rot_g), len(rot_u))
+    h = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    fused = [w4.PreparedGateUp(x, rot_g[c], rot_u[c], h=h) for c in range(n)]
+    g_out, u_out = torch.empty_like(h), torch.empty_like(h)
+    sep_g = [w4.PreparedLinear(x, *rot_g[c], y=g_out) for c in range(n)]
+    sep_u = [w4.PreparedLinear(x, *rot_u[c], y=u_out) for c in range(n)]
 
-    def glu():      # the unfused epilogue as a framework runs it: bf16 SiLU, then the product
-        return torch.nn.functional.silu(g_out).mul_(u_out)
+    def unfused(c):       # the unfused epilogue as a framework runs it: bf16 SiLU, then the product
+        return lambda: (sep_g[c](), sep_u[c](), torch.nn.functional.silu(g_out).mul_(u_out))
 
-    def unfused(c):
-        return lambda: (sep_g[c](), sep_u[c](), glu())
-
-    t_fused = time_call(torch, fused, reps)
-    t_sep = time_call(torch, sep_g, reps) + time_call(torch, sep_u, reps)
-    t_unfused = time_call(torch, [unfused(c) for c in range(copies)], reps)
+    t_fused = timed(fused)
+    t_sep = timed([(lambda c=c: (sep_g[c](), sep_u[c]())) for c in range(n)])
+    t_unfused = timed([unfused(c) for c in range(n)])
     f2 = 2 * flops(M, N, K)
-    out = {"fused_gate_up_swiglu": {
+    out["fused_gate_up_swiglu"] = {
         "M": M, "N": N, "K": K, "plan": {k: fused[0].plan[k] for k in ("tile_m", "tile_n", "split_k", "variant")},
         "fused_us": round(t_fused, 3), "gate_plus_up_us": round(t_sep, 3),
         "unfused_gate_up_silu_mul_us": round(t_unfused, 3),
         "speedup_vs_unfused": round(t_unfused / t_fused, 3), "TFLOP/s": round(f2 / t_fused / 1e6, 2),
-        "frac_mfma": round(f2 / t_fused / 1e6 / PEAK_BF16_TFLOPS, 4)}}
+        "frac_mfma": round(f2 / t_fused / 1e6 / PEAK_BF16_TFLOPS, 4)}
+    del fused, sep_g, sep_u, rot_g, rot_u
+
+    # skinny rows
     skinny = []
     for name in ("gate", "down"):
         p = by[name]
+        rot = rotation(p["w"][0])
         for m in (16, 32):
             xs = p["x"][:m]
-            auto = [w4.PreparedLinear(xs, *p["w"][c]) for c in range(copies)]
-            tiled = [w4.PreparedLinear(xs, *p["w"][c], path="qmm") for c in range(copies)]
-            t_a, t_t = time_call(torch, auto, reps), time_call(torch, tiled, reps)
+            y = torch.empty((m, p["N"]), dtype=torch.bfloat16, device=dev)
+            pa = w4.w4a16_plan(m, p["N"], p["K"], 128, w4.PATH_AUTO, 0)
+            pt = w4.w4a16_plan(m, p["N"], p["K"], 128, w4.PATH_QMM, 0)
+            wa, wt = ws_for(torch, pa["workspace_bytes"], dev), ws_for(torch, pt["workspace_bytes"], dev)
+            auto = [w4.PreparedLinear(xs, *w, y=y, workspace=wa) for w in rot]
+            tiled = [w4.PreparedLinear(xs, *w, y=y, path="qmm", workspace=wt) for w in rot]
+            t_a, t_t = timed(auto), timed(tiled)
             b = algo_bytes(m, p["N"], p["K"])
-            skinny.append({"name": name, "M": m, "N": p["N"], "K": p["K"], "tile_m": auto[0].plan["tile_m"],
-                           "split_k": auto[0].plan["split_k"], "skinny_us": round(t_a, 3),
+            skinny.append({"name": name, "M": m, "N": p["N"], "K": p["K"], "tile_m": pa["tile_m"],
+                           "split_k": pa["split_k"], "skinny_us": round(t_a, 3),
                            "tiled64_us": round(t_t, 3), "GB/s": round(b / t_a / 1e3, 1),
                            "frac_hbm": round(b / t_a / 1e3 / PEAK_HBM_GBPS, 4)})
+        del rot
     out["skinny"] = skinny
-    out["timing"] = "HIP events around each call, rotating weight copies, after the timed region"
+
+    # W4A8 against W4A16 on the step's projections
+    w4a8 = []
+    for name in LAYER:
+        p = by[name]
+        rot = rotation(p["w"][0])
+        y = torch.empty((p["M"], p["N"]), dtype=torch.bfloat16, device=dev)
+        w8 = ws_for(torch, w4.w4a8_linear_workspace_bytes(p["M"], p["N"], p["K"]), dev)
+        w16 = ws_for(torch, w4.w4a16_workspace_bytes(p["M"], p["N"], p["K"]), dev)
+        t8 = timed([w4.PreparedW4A8(p["x"], *w, y=y, workspace=w8) for w in rot])
+        t16 = timed([w4.PreparedLinear(p["x"], *w, y=y, workspace=w16) for w in rot])
+        f = flops(p["M"], p["N"], p["K"])
+        w4a8.append({"name": name, "M": p["M"], "N": p["N"], "K": p["K"],
+                     "split_k": w4.w4a8_plan(p["M"], p["N"], p["K"])["split_k"],
+                     "w4a8_us": round(t8, 3), "w4a16_us": round(t16, 3), "w4a8_TOP/s": round(f / t8 / 1e6, 2),
+                     "frac_int8_mfma": round(f / t8 / 1e6 / PEAK_INT8_TOPS, 4)})
+        del rot
+    out["w4a8"] = w4a8
+
+    # 4096-row prefill: gate / up / down and the vocabulary head over all rows
+    long_rows = []
+    for name, src in (("gate", "gate"), ("up", "up"), ("down", "down"), ("vocab_all_rows", "vocab_last_row")):
+        p = by[src]
+        sname = "vocab" if src == "vocab_last_row" else src
+        xl = torch.from_numpy(synth.activations(5, synth.shape_index(5, sname), 4096, p["K"]).view("int16"))
+        xl = xl.view(torch.bfloat16).to(dev)
+        rot = rotation(p["w"][0])
+        pl = w4.w4a16_plan(4096, p["N"], p["K"])
+        y = torch.empty((4096, p["N"]), dtype=torch.bfloat16, device=dev)
+        wsb = ws_for(torch, pl["workspace_bytes"], dev)
+        fns = [w4.PreparedLinear(xl, *w, y=y, workspace=wsb) for w in rot]
+        t = time_call(torch, fns, max(len(fns), 4 if src == "vocab_last_row" else reps))
+        f = flops(4096, p["N"], p["K"])
+        long_rows.append({"name": name, "M": 4096, "N": p["N"], "K": p["K"], "tile_m": pl["tile_m"],
+                          "exact_codes": pl["variant"] >= 10, "avg_us": round(t, 3),
+                          "TFLOP/s": round(f / t / 1e6, 2), "frac_mfma": round(f / t / 1e6 / PEAK_BF16_TFLOPS, 4)})
+        del fns, rot, y, xl
+    out["prefill4096"] = long_rows
+
+    # decode rows on the four decode shapes
+    decode = []
+    for i, (K, N) in enumerate(synth.DECODE_SHAPES):
+        wq, sc, bi = synth.weights(2, i, N, K)
+        w0 = (torch.from_numpy(wq.view("int32")).to(dev), torch.from_numpy(sc.view("int16")).view(torch.bfloat16).to(dev),
+              torch.from_numpy(bi.view("int16")).view(torch.bfloat16).to(dev))
+        rot = rotation(w0)
+        for m in (1, 4):
+            xd = torch.from_numpy(synth.activations(2, i, m, K).view("int16")).view(torch.bfloat16).to(dev)
+            y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+            pl = w4.w4a16_plan(m, N, K)
+            t = timed([w4.PreparedLinear(xd, *w, y=y) for w in rot])
+            b = algo_bytes(m, N, K)
+            decode.append({"K": K, "N": N, "M": m, "variant": pl["variant"], "avg_us": round(t, 3),
+                           "GB/s": round(b / t / 1e3, 1), "frac_hbm": round(b / t / 1e3 / PEAK_HBM_GBPS, 4)})
+        del rot
+    out["decode"] = decode
+
+    # width-generic matvec on the 2560 -> 9728 shape
+    bits_rows = []
+    K, N = synth.DECODE_SHAPES[0]
+    for bits in (1, 2, 4, 8):
+        pr = synth.random_problem(40 + bits, 4, N, K, bits=bits)
+        w0 = (torch.from_numpy(pr["wq"].view("int32")).to(dev),
+              torch.from_numpy(pr["scales"].view("int16")).view(torch.bfloat16).to(dev),
+              torch.from_numpy(pr["biases"].view("int16")).view(torch.bfloat16).to(dev))
+        rot = rotation(w0)
+        xb = torch.from_numpy(pr["x"].view("int16")).view(torch.bfloat16).to(dev)
+        for m in (1, 4):
+            y = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+            xm = xb[:m]
+            t = timed([(lambda w=w: w4.qmv_affine(xm, *w, bits=bits, y=y)) for w in rot])
+            b = N * K * bits / 8 + N * K / 32 + 2.0 * m * K + 2.0 * m * N
+            bits_rows.append({"bits": bits, "K": K, "N": N, "M": m, "avg_us": round(t, 3),
+                              "GB/s": round(b / t / 1e3, 1), "frac_hbm": round(b / t / 1e3 / PEAK_HBM_GBPS, 4)})
+        del rot
+    out["qmv_affine_bits"] = bits_rows
+    out["timing"] = ("after the timed region: each case alone, its calls over a weight rotation of more than "
+                     "512 MB replayed from a HIP graph on a side stream, median of 5 replays")
     return out
 
 

@@ -397,13 +397,14 @@ def linear(x, wq, scales, biases, logits_to_keep: int = 0, path: str | None = No
 class PreparedLinear:
     """One projection with fixed tensors, validated once; calling it only enqueues the kernels.
 
-    For timing loops and graph capture: the output ``y`` and any split-K workspace are
-    allocated here, and ``__call__`` issues a single C-ABI call (``w4a16_linear``, or
+    For timing loops and graph capture: the output ``y`` and any workspace are allocated here
+    (or passed in: ``y`` and ``workspace`` may be shared by calls that do not overlap), and
+    ``__call__`` issues a single C-ABI call (``w4a16_linear``, or
     ``qmv_w4a16`` / ``qmm_w4a16`` when ``path`` forces one) on the stream current at
     construction.
     """
 
-    def __init__(self, x, wq, scales, biases, y=None, path: str | None = None, split_k: int = 0):
+    def __init__(self, x, wq, scales, biases, y=None, path: str | None = None, split_k: int = 0, workspace=None):
         M, N, K, y = _operands(x, wq, scales, biases, y)
         self.M, self.N, self.K, self.y = M, N, K, y
         lib = load()
@@ -416,7 +417,7 @@ class PreparedLinear:
         else:
             forced = path == "qmm" or split_k != 0
             self.plan = w4a16_plan(M, N, K, GROUP, PATH_QMM if forced else PATH_AUTO, split_k)
-            ws, ws_bytes = _workspace(None, self.plan["workspace_bytes"], x.device)
+            ws, ws_bytes = _workspace(workspace, self.plan["workspace_bytes"], x.device)
             self.workspace = ws
             wsp = None if ws is None else ws.data_ptr()
             if forced:
@@ -438,7 +439,7 @@ class PreparedGateUp:
     ``h`` and any split-K workspace are allocated here; ``__call__`` issues one C-ABI call
     (``w4a16_gate_up_swiglu``) on the stream current at construction."""
 
-    def __init__(self, x, gate, up, h=None, split_k: int = 0):
+    def __init__(self, x, gate, up, h=None, split_k: int = 0, workspace=None):
         (wg, sg, bg), (wu, su, bu) = gate, up
         M, N, K, h = _operands(x, wg, sg, bg, h)
         if tuple(wu.shape) != tuple(wg.shape):
@@ -447,7 +448,7 @@ class PreparedGateUp:
         self.M, self.N, self.K, self.h = M, N, K, h
         lib = load()
         self.plan = w4a16_gate_up_plan(M, N, K, GROUP, split_k)
-        ws, ws_bytes = _workspace(None, self.plan["workspace_bytes"], x.device)
+        ws, ws_bytes = _workspace(workspace, self.plan["workspace_bytes"], x.device)
         self.workspace = ws
         self._fn = lib.w4a16_gate_up_swiglu
         self._args = (x.data_ptr(), wg.data_ptr(), sg.data_ptr(), bg.data_ptr(), wu.data_ptr(), su.data_ptr(),
@@ -466,12 +467,12 @@ class PreparedW4A8:
     and the workspace (activation buffers plus partials) are allocated here; ``__call__`` issues
     one C-ABI call (``w4a8_linear``) on the stream current at construction."""
 
-    def __init__(self, x, wq, scales, biases, y=None):
+    def __init__(self, x, wq, scales, biases, y=None, workspace=None):
         M, N, K, y = _operands(x, wq, scales, biases, y)
         self.M, self.N, self.K, self.y = M, N, K, y
         lib = load()
         self.plan = w4a8_plan(M, N, K, GROUP, 0)
-        ws, ws_bytes = _workspace(None, w4a8_linear_workspace_bytes(M, N, K), x.device)
+        ws, ws_bytes = _workspace(workspace, w4a8_linear_workspace_bytes(M, N, K), x.device)
         self.workspace = ws
         self._fn = lib.w4a8_linear
         self._args = (x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(), M, N, K,
