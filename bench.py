@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--copies", type=int, default=3, help="device copies of the weights, rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the measurements beyond the step (for profiler runs of the step alone)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before the timed region, copy a 256 MiB buffer three times (reference for counter scaling)")
     args = ap.parse_args()
@@ -259,9 +261,10 @@ def main():
         "breakdown": per,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
-    gs = torch.cuda.Stream()             # graph capture needs a stream other than the null stream
-    with torch.cuda.stream(gs):
-        result["next_rows"] = next_rows(torch, w4, projections, args.copies)
+    if not args.no_next_rows:
+        gs = torch.cuda.Stream()         # graph capture needs a stream other than the null stream
+        with torch.cuda.stream(gs):
+            result["next_rows"] = next_rows(torch, w4, projections, args.copies)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(projections)
