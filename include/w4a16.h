@@ -86,8 +86,10 @@ typedef struct w4a16_plan {
     int32_t split_k;           /* S: number of K slices (1 = unsplit)                       */
     int32_t k_waves;           /* qmv: waves of one workgroup that split K (1 = none)       */
     int32_t num_cus;           /* compute units the plan was made for                       */
-    int32_t variant;           /* kernel instance index (diagnostic)                        */
-    uint64_t workspace_bytes;  /* fp32 partials needed when split_k > 1 (S * M * N * 4)    */
+    int32_t variant;           /* kernel instance index (diagnostic); qmm plans add 10 when
+                                  they run the exact-code form (see qmm_w4a16)                */
+    uint64_t workspace_bytes;  /* the exact-code form's activation group sums, then the fp32
+                                  partials when split_k > 1 (S * M * N * 4)                   */
 } w4a16_plan_t;
 
 /* ABI version of the loaded library (W4A16_ABI_VERSION). */
@@ -109,8 +111,8 @@ int w4a16_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t path, int
                int32_t num_cus, w4a16_plan_t* out);
 
 /*
- * Workspace bytes w4a16_linear needs for this shape under the policy (0 when the policy does
- * not split K).  num_cus as in w4a16_plan.  Returns 0 for invalid shapes.
+ * Workspace bytes w4a16_linear needs for this shape under the policy (0 when the plan needs
+ * neither group sums nor partials).  num_cus as in w4a16_plan.  Returns 0 for invalid shapes.
  */
 uint64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t num_cus);
 
@@ -125,11 +127,20 @@ int qmv_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, con
 /*
  * Tiled matrix path for any M >= 1 ("Week 2 Day 6", "From a Matvec to a Cooperative Tile",
  * Tasks 2 and 3), with optional split-K (Task 5: a temporary buffer and a second launch).
- * split_k: 0 = policy, 1 = off, S > 1 = forced (clamped to the number of groups).  When the
- * plan splits, `workspace` must hold S * M * N fp32 partials (w4a16_plan().workspace_bytes);
- * the slices are summed in slice order, so results are deterministic.  Under the policy, a
- * missing or short workspace quietly falls back to S = 1; a forced S > 1 with too little
- * workspace returns W4A16_ERR_WORKSPACE.
+ * split_k: 0 = policy, 1 = off, S > 1 = forced (clamped to the number of groups).
+ *
+ * Two forms of the same product (both within the parity tolerance, integer cases identical):
+ * tiles of up to 64 rows (M <= 1024) dequantize each weight to bf16 in registers; the 128-row
+ * tiles (M > 1024) multiply the raw codes on the matrix core, scale each group's fp32 product
+ * once and add sum_g b * X from the activations' per-group sums, which a first launch writes
+ * to the start of `workspace` (bf16 [M, 2G rounded up to 16], padded to 256 bytes).
+ *
+ * `workspace` (16-byte aligned) holds, in order, those group sums (exact-code form only) and,
+ * when the plan splits, S * M * N fp32 partials; w4a16_plan().workspace_bytes is the total.
+ * The slices are summed in slice order, so results are deterministic.  With too little
+ * workspace the call drops the exact-code form, then (under the policy) the split, both of
+ * which compute the same result; a forced S > 1 without room for its partials returns
+ * W4A16_ERR_WORKSPACE.
  */
 int qmm_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
               uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k,

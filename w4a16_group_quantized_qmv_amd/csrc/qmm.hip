@@ -14,6 +14,12 @@
 //    so each weight is unpacked and dequantized exactly once per workgroup, in registers, by the
 //    wave that consumes it, and every dequantized operand feeds BM / 32 MFMAs.  Weights never
 //    pass through LDS.
+//  * Exact-code form (template CODES > 0, used for the 128-row tiles): instead of dequantizing,
+//    the wave feeds the raw codes as exact bf16 integers, the matrix core returns each group's
+//    P = sum_k x q in fp32, and the accumulators take acc += s * P once per group; the bias term
+//    sum_g b * X (X = the activations' group sums, from act_group_sums_kernel) is one small MFMA
+//    contraction per tile in the epilogue.  Fewer VALU instructions per MFMA, and no weight is
+//    rounded to bf16.
 //  * One pipeline step is one 128-value quantization group: the scale and bias of a column are
 //    loaded once per step and serve all eight 16-value MFMA sub-steps of the group (the
 //    analogue of the page's four reduction tiles per group).
