@@ -83,6 +83,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     __shared__ __attribute__((aligned(16))) uint16_t xs0[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t xs1[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t xs2[STAGES > 2 ? TILE : 8];
+    // codes of one group, per stage: each wave's J blocks of 32 columns x 64 bytes
+    constexpr int CODES_BYTES = NW * J * 2048;
+    __shared__ __attribute__((aligned(16))) uint8_t cs0[CODES_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t cs1[CODES_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t cs2[STAGES > 2 ? CODES_BYTES : 16];
 
     const int tiles = tiles_m * tiles_n;
     const int work = xcd_remap(blockIdx.x, tiles * split);
@@ -106,6 +111,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
         if constexpr (i == 0) return xs0;
         else if constexpr (i == 1) return xs1;
         else return xs2;
+    };
+    auto cstage = [&](auto ic) -> uint8_t* {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i == 0) return cs0;
+        else if constexpr (i == 1) return cs1;
+        else return cs2;
     };
 
     // Every load goes through a buffer resource.  Loads for groups past this slice use
@@ -144,16 +155,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, 0, 0x00020000);
     };
     const __amdgpu_buffer_rsrc_t none = dead(xrsrc);
-    uint32_t wvoff[NB], sbvoff[NB];
+    // Codes go through LDS by direct loads that read whole 64-byte column groups: instruction i
+    // of block cb fills 16 columns, lane l taking column 16 i + l / 4 and writing its 16 bytes to
+    // slot l % 4 of that column's 64 bytes.  Slot p holds chunk p ^ ((column / 4) & 3), so the 16
+    // lanes that later read one chunk of 16 consecutive columns hit 16 different bank groups.
+    // (column / 4) & 3 = (l / 16) & 3 for both instructions.
+    uint32_t cvoff[NB], sbvoff[NB];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
         const int c = (wave * NB + cb) * 32 + (lane & 31);     // column within the tile
-        wvoff[cb] = static_cast<uint32_t>(c * row_bytes + half * 32);
+        cvoff[cb] = static_cast<uint32_t>(((wave * NB + cb) * 32 + (lane >> 2)) * row_bytes +
+                                          16 * ((lane & 3) ^ ((lane >> 4) & 3)));
         sbvoff[cb] = static_cast<uint32_t>(c * G * 2);
     }
+    // this lane's two chunks (2 half, 2 half + 1) of its column's group in a stage's code block
+    const int ccol = lane & 31;
+    const int cread0 = ccol * 64 + 16 * ((2 * half) ^ ((ccol >> 2) & 3));
+    const int cread1 = ccol * 64 + 16 * ((2 * half + 1) ^ ((ccol >> 2) & 3));
 
     struct Slot {
-        u32x4_t w[J][2];
         uint16_t s[J], b[J];
     };
     // exact-code mode reads the biases once, in the epilogue
@@ -178,9 +198,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
             const __amdgpu_buffer_rsrc_t wr = live ? wrsrc[p] : none;
             const __amdgpu_buffer_rsrc_t sr = live ? srsrc[p] : none;
             const __amdgpu_buffer_rsrc_t br = live ? brsrc[p] : none;
-            o.w[j][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff[cb], g * 64, 0));
-            asm volatile("" ::: "memory");
-            o.w[j][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff[cb], g * 64 + 16, 0));
+            uint8_t* cdst = cstage(ic) + (wave * J + j) * 2048;
+            // (offsets go through locals: an array element as a builtin operand made the host pass
+            // drop the kernel's launch stub)
+            const uint32_t co = cvoff[cb], cg = static_cast<uint32_t>(g) * 64u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst, 16, co, cg, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst + 1024, 16, co + 16u * static_cast<uint32_t>(row_bytes), cg, 0, 0);
             asm volatile("" ::: "memory");
             o.s[j] = __builtin_amdgcn_raw_buffer_load_b16(sr, sbvoff[cb], g * 2, 0);
             asm volatile("" ::: "memory");
@@ -232,15 +255,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
             for (int j = 0; j < J; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) Pr[i][rb][j][r] = 0.f;
+    // this lane's eight code words of block j (words 8 half .. 8 half + 7 of its column's group)
+    auto read_codes = [&](auto ic, u32x4_t (&w)[J][2]) {
+        const uint8_t* cb = cstage(ic) + wave * J * 2048;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            w[j][0] = *reinterpret_cast<const u32x4_t*>(cb + j * 2048 + cread0);
+            w[j][1] = *reinterpret_cast<const u32x4_t*>(cb + j * 2048 + cread1);
+        }
+    };
+
     auto compute_codes = [&](auto ic, const Slot& o, auto pc) {
         constexpr int PC = PSETS == 1 ? 0 : decltype(pc)::value;
         constexpr int PP = PSETS == 1 ? 0 : (PC + STAGES - 1) % STAGES;
         const uint16_t* xt = stage(ic);
+        u32x4_t ow[J][2];
+        read_codes(ic, ow);
         bf16x8_t a[2][RB], bw[2][J];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) a[0][rb] = *reinterpret_cast<const bf16x8_t*>(xt + abase + rb * 32 * kGroup);
 #pragma unroll
-        for (int j = 0; j < J; ++j) bw[0][j] = codes_bf16_natural(o.w[j][0][0]);
+        for (int j = 0; j < J; ++j) bw[0][j] = codes_bf16_natural(ow[j][0][0]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int cur = t & 1, nxt = cur ^ 1;
@@ -249,7 +284,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
                 for (int rb = 0; rb < RB; ++rb)
                     a[nxt][rb] = *reinterpret_cast<const bf16x8_t*>(xt + (abase ^ ((t + 1) << 3)) + rb * 32 * kGroup);
 #pragma unroll
-                for (int j = 0; j < J; ++j) bw[nxt][j] = codes_bf16_natural(o.w[j][(t + 1) >> 2][(t + 1) & 3]);
+                for (int j = 0; j < J; ++j) bw[nxt][j] = codes_bf16_natural(ow[j][(t + 1) >> 2][(t + 1) & 3]);
             }
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
@@ -292,6 +327,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     };
 
     auto compute = [&](auto ic, const Slot& o) {
+        u32x4_t ow[J][2];
+        read_codes(ic, ow);
         float s[J], b[J];
 #pragma unroll
         for (int j = 0; j < J; ++j) {
@@ -303,7 +340,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) a[0][rb] = *reinterpret_cast<const bf16x8_t*>(xt + abase + rb * 32 * kGroup);
 #pragma unroll
-        for (int j = 0; j < J; ++j) bw[0][j] = dequant_word(o.w[j][0][0], s[j], b[j]);
+        for (int j = 0; j < J; ++j) bw[0][j] = dequant_word(ow[j][0][0], s[j], b[j]);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int cur = t & 1, nxt = cur ^ 1;
@@ -313,7 +350,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
                     a[nxt][rb] = *reinterpret_cast<const bf16x8_t*>(xt + (abase ^ ((t + 1) << 3)) + rb * 32 * kGroup);
 #pragma unroll
                 for (int j = 0; j < J; ++j)
-                    bw[nxt][j] = dequant_word(o.w[j][(t + 1) >> 2][(t + 1) & 3], s[j], b[j]);
+                    bw[nxt][j] = dequant_word(ow[j][(t + 1) >> 2][(t + 1) & 3], s[j], b[j]);
             }
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
