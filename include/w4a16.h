@@ -86,10 +86,11 @@ typedef struct w4a16_plan {
     int32_t split_k;           /* S: number of K slices (1 = unsplit)                       */
     int32_t k_waves;           /* qmv: waves of one workgroup that split K (1 = none)       */
     int32_t num_cus;           /* compute units the plan was made for                       */
-    int32_t variant;           /* kernel instance index (diagnostic); qmm plans add 10 when
-                                  they run the exact-code form (see qmm_w4a16)                */
+    int32_t variant;           /* kernel instance index (diagnostic); qmm and gate / up plans
+                                  add 10 when they run the exact-code form (see qmm_w4a16)    */
     uint64_t workspace_bytes;  /* the exact-code form's activation group sums, then the fp32
-                                  partials when split_k > 1 (S * M * N * 4)                   */
+                                  partials when split_k > 1 (S * M * N * 4; twice that for
+                                  the gate / up pair)                                         */
 } w4a16_plan_t;
 
 /* ABI version of the loaded library (W4A16_ABI_VERSION). */
@@ -164,12 +165,15 @@ int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, 
  *     g = x . dequant(Wq_gate)^T,  u = x . dequant(Wq_up)^T   (fp32, never rounded to bf16)
  *
  * One tile kernel reads each activation fragment once for both projections and writes only h.
- * Both weight sets have the layouts above with the same N and K; h is bf16 [M, N].  Any M >= 1
- * (32-row tiles up to 32 rows, 64-row up to ~1k, 128-row beyond).  split_k as for qmm_w4a16;
- * a split plan needs `workspace` of 2 * S * M * N fp32 (w4a16_gate_up_plan().workspace_bytes:
- * gate partials, then up partials), summed in slice order before the SiLU, so results are
- * deterministic.  Same preconditions, ownership and errors as qmm_w4a16 (every pointer
- * checked, h must not overlap an input).
+ * Both weight sets have the layouts above with the same N and K; h is bf16 [M, N].  Any M >= 1:
+ * 32-row tiles up to 32 rows; above, 64-row tiles in the exact-code form described at
+ * qmm_w4a16 (codes on the matrix core, the bias term from the activations' group sums), or,
+ * when the workspace has no room for the group sums, dequantizing tiles (64 rows up to ~1k,
+ * 128 beyond; same result within the tolerance).  split_k as for qmm_w4a16.  Workspace
+ * (w4a16_gate_up_plan().workspace_bytes): [group sums, exact-code form][gate partials][up
+ * partials], the partials 2 * S * M * N fp32 of a split plan, summed in slice order before the
+ * SiLU, so results are deterministic.  Same preconditions, ownership and errors as qmm_w4a16
+ * (every pointer checked, h must not overlap an input).
  */
 int w4a16_gate_up_swiglu(const uint16_t* x, const uint32_t* wq_gate, const uint16_t* scales_gate,
                          const uint16_t* biases_gate, const uint32_t* wq_up, const uint16_t* scales_up,

@@ -196,13 +196,16 @@ def gate_up_plan(M, N, K, split_k=0):
 
 
 def test_gate_up_plan_tiles_and_workspace():
-    # tile rows as for the projection: 32 up to 32 rows, 64 up to ~1k, 128 beyond
-    for M, tile_m in [(1, 32), (32, 32), (33, 64), (512, 64), (1024, 64), (1025, 128), (4096, 128)]:
+    # 32-row tiles up to 32 rows (dequantizing); above, 64-row tiles in the exact-code form
+    r256 = lambda v: -(-v // 256) * 256
+    for M, tile_m in [(1, 32), (32, 32), (33, 64), (512, 64), (1024, 64), (1025, 64), (4096, 64)]:
         p = gate_up_plan(M, 9728, 2560)
         assert p["path"] == w4.PATH_GATE_UP and p["tile_m"] == tile_m and p["tile_n"] == 128
         assert p["grid_x"] == -(-9728 // 128) and p["grid_y"] == -(-M // tile_m)
-        # the workspace holds gate and up partials
-        assert p["workspace_bytes"] == (2 * p["split_k"] * M * 9728 * 4 if p["split_k"] > 1 else 0)
+        assert (p["variant"] >= 10) == (M > 32)
+        # the workspace holds the group sums (exact-code form), then gate and up partials
+        sums = r256(M * w4.w4a8_xsum_cols(2560) * 2) if M > 32 else 0
+        assert p["workspace_bytes"] == sums + (2 * p["split_k"] * M * 9728 * 4 if p["split_k"] > 1 else 0)
     # the split follows the projection's rule on the same tile grid
     for M, N, K in [(128, 9728, 2560), (512, 9728, 2560), (512, 2560, 9728), (16, 1024, 2560)]:
         g, q = gate_up_plan(M, N, K), plan(M, N, K, path=w4.PATH_QMM if M > 32 else w4.PATH_SKINNY)
@@ -336,5 +339,6 @@ def test_exact_code_mode_plans():
         p = plan(M, 9728, 2560)
         assert p["variant"] < 10
         assert p["workspace_bytes"] == (p["split_k"] * M * 9728 * 4 if p["split_k"] > 1 else 0)
-    # the fused gate / up pair always dequantizes
-    assert gate_up_plan(4096, 9728, 2560)["variant"] < 10
+    # the fused gate / up pair runs the exact-code form on its 64-row tiles above 32 rows
+    assert gate_up_plan(4096, 9728, 2560)["variant"] == 11 and gate_up_plan(512, 9728, 2560)["variant"] == 11
+    assert gate_up_plan(32, 9728, 2560)["variant"] < 10

@@ -421,14 +421,14 @@ def assert_swiglu_parity(h_bits, x, gate, up, rows=None):
 
 
 @pytest.mark.parametrize("M,N,K,split", [
-    (33, 96, 256, 0),          # ragged M and N, 64-row tiles
+    (33, 96, 256, 0),          # ragged M and N, 64-row exact-code tiles
     (1, 1000, 2560, 0),        # one row: 32-row tiles, policy split
     (20, 1000, 2560, 0),       # skinny rows, ragged N
     (128, 9728, 2560, 0),      # the 128-row gate / up shape, policy split (3 slices)
     (128, 2000, 1024, 1),      # forced: unsplit
     (70, 1100, 1024, 2),       # forced: two slices
     (70, 1100, 1024, 5),       # forced: five slices of 1 or 2 groups
-    (1500, 512, 384, 0),       # 128-row tiles, odd group count
+    (1500, 512, 384, 0),       # beyond 1024 rows, odd group count
 ])
 def test_gate_up_swiglu_matches_oracle(lib, M, N, K, split):
     x, gate, up = gate_up_problem(21, M, N, K)
@@ -444,11 +444,12 @@ def test_gate_up_swiglu_prefill512_sampled_rows(lib):
     assert_swiglu_parity(h, x, gate, up, rows=np.arange(0, 512, 37))
 
 
-def test_gate_up_swiglu_saturation_closed_form(lib):
+@pytest.mark.parametrize("M", [3, 40])     # 32-row dequantizing tiles; 64-row exact-code tiles
+def test_gate_up_swiglu_saturation_closed_form(lib, M):
     # all-zero codes and x = 1: g[n] = 128 * sum_g b_gate[n, g], u[n] = 128 * sum_g b_up[n, g].
     # Gate sums of -256, 0 and +256 hit silu's exp overflow (silu -> -0), its zero and its
     # identity tail (silu(256) = 256 in fp32); every product is exact in bf16.
-    M, N, K = 3, 96, 256
+    N, K = 96, 256
     G = K // 128
     x = synth.const_bf16(1.0, (M, K))
     bg_vals = np.array([-1.0, 0.0, 1.0])[np.arange(N) % 3]
@@ -463,6 +464,24 @@ def test_gate_up_swiglu_saturation_closed_form(lib):
     got = synth.from_bf16_bits(h)
     assert np.array_equal(got, np.broadcast_to(expect, (M, N)).astype(got.dtype)), got[0, :6]
     assert_swiglu_parity(h, x, gate, up)
+
+
+def test_gate_up_exact_code_and_dequantizing_forms(lib):
+    # above 32 rows the plan runs the exact-code form; a call without workspace (no room for the
+    # activations' group sums) runs the dequantizing tiles instead: both within the tolerance
+    x, gate, up = gate_up_problem(25, 200, 1100, 2560)
+    assert lib.w4a16_gate_up_plan(200, 1100, 2560, split_k=1)["variant"] >= 10
+    h_codes = run_gate_up(lib, x, gate, up, split_k=1)
+    h_deq = run_gate_up(lib, x, gate, up, split_k=1, workspace=None)
+    assert_swiglu_parity(h_codes, x, gate, up)
+    assert_swiglu_parity(h_deq, x, gate, up)
+
+
+def test_gate_up_long_prefill_sampled_rows(lib):
+    # 4096 rows of the 2560 -> 9728 pair (exact-code tiles): every column of sampled rows
+    x, gate, up = gate_up_problem(26, 4096, 9728, 2560)
+    h = run_gate_up(lib, x, gate, up)
+    assert_swiglu_parity(h, x, gate, up, rows=np.r_[0, 63, 64, 2047, 4032, 4095])
 
 
 def test_gate_up_forced_split_without_workspace_is_rejected(lib):

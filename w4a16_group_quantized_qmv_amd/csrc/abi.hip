@@ -113,20 +113,9 @@ uint64_t group_sum_bytes(int64_t M, int64_t K) {
     return round256(static_cast<uint64_t>(M) * group_sum_cols(static_cast<int>(K)) * 2);
 }
 
-// skinny: 32-row tiles and the skinny split rule (rows 17..32, or a wide head at 9..16 rows).
-// codes: the exact-code mode (codes on the matrix core, per-group scaling, bias from the group
-// sums of the activations), which needs the group sums in the workspace.
-void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p,
-              bool skinny = false, bool codes = true) {
-    const int64_t G = K / W4A16_GROUP;
-    // Measured on MI355X: 64 x 128 tiles (four waves per SIMD) lead up to about a thousand
-    // rows, where the grid is small; 128 x 128 tiles (two waves per SIMD) lead beyond.  For at
-    // most 32 rows, 32 x 128 tiles (four waves per SIMD, three stages) lead on every layer shape
-    // and on the vocabulary head.
-    const int variant = skinny ? kQmmSkinnyVariant : (M <= 1024 ? 1 : 0);
-    const QmmShape& v = kQmmVariants[variant];
-    const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
-    const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, tile_n);
+// Split-K slices for a grid of `tiles` output tiles over G groups: the caller's split_k if
+// nonzero (at most G), else the policy's (skinny: the rule of the 32-row tiles).
+int64_t tile_split(int64_t tiles, int64_t G, int32_t split_k, int32_t cus, bool skinny) {
     int64_t S = 1;
     if (split_k == 0) {
         if (skinny) {
@@ -150,6 +139,24 @@ void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a
         S = split_k < 1 ? 1 : split_k;
         if (S > G) S = G;
     }
+    return S;
+}
+
+// skinny: 32-row tiles and the skinny split rule (rows 17..32, or a wide head at 9..16 rows).
+// codes: the exact-code mode (codes on the matrix core, per-group scaling, bias from the group
+// sums of the activations), which needs the group sums in the workspace.
+void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p,
+              bool skinny = false, bool codes = true) {
+    const int64_t G = K / W4A16_GROUP;
+    // Measured on MI355X: 64 x 128 tiles (four waves per SIMD) lead up to about a thousand
+    // rows, where the grid is small; 128 x 128 tiles (two waves per SIMD) lead beyond.  For at
+    // most 32 rows, 32 x 128 tiles (four waves per SIMD, three stages) lead on every layer shape
+    // and on the vocabulary head.
+    const int variant = skinny ? kQmmSkinnyVariant : (M <= 1024 ? 1 : 0);
+    const QmmShape& v = kQmmVariants[variant];
+    const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
+    const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, tile_n);
+    const int64_t S = tile_split(tiles, G, split_k, cus, skinny);
     p->path = skinny ? W4A16_PATH_SKINNY : W4A16_PATH_QMM;
     p->tile_m = v.bm;
     p->tile_n = static_cast<int32_t>(tile_n);
@@ -285,24 +292,33 @@ int run_qmm(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint
 }
 
 // Gate / up pair with SwiGLU: one tile kernel computes both projections of the same columns.
-// Tile rows as for qmm (32 up to 32 rows, 64 up to ~1k, 128 beyond); the split follows the
-// matching qmm rule; the workspace holds the gate and up partials (2 * S * M * N fp32).
-// The pair always dequantizes (its exact-code form needs twice the P registers and spills).
-void plan_gate_up(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p) {
-    plan_qmm(M, N, K, split_k, cus, p, M <= kSkinnyMaxRows, false);
-    const int variant = M <= kSkinnyMaxRows ? 0 : (M <= 1024 ? 1 : 2);
+// Tiles: 32 rows up to 32 rows; above, 64-row tiles in the exact-code mode (measured on MI355X
+// against the dequantizing 64- and 128-row tiles: 87 vs 98 us at 512 rows and 497 vs 560 us at
+// 4096 rows, K = 2560, N = 9728); without the exact-code mode 64 rows up to ~1k and 128 beyond.
+// The split follows the qmm rule on the same tile grid.  Workspace: [group sums (exact-code
+// mode)][gate partials][up partials], the partials 2 * S * M * N fp32.
+void plan_gate_up(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p,
+                  bool codes = true) {
+    const bool skinny = M <= kSkinnyMaxRows;
+    codes = codes && !skinny;
+    const int variant = skinny ? 0 : (codes ? kGateUpCodesTileVariant : (M <= 1024 ? 1 : 2));
     const QmmShape& v = kGateUpVariants[variant];
     const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
-    if (v.bm != p->tile_m || tile_n != p->tile_n) {   // same tile grid as the qmm rule it follows
-        p->tile_m = v.bm;
-        p->tile_n = static_cast<int32_t>(tile_n);
-        p->grid_x = static_cast<int32_t>(ceil_div(N, tile_n));
-        p->grid_y = static_cast<int32_t>(ceil_div(M, v.bm));
-    }
+    const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, tile_n);
+    const int64_t S = tile_split(tiles, K / W4A16_GROUP, split_k, cus, skinny);
     p->path = W4A16_PATH_GATE_UP;
+    p->tile_m = v.bm;
+    p->tile_n = static_cast<int32_t>(tile_n);
+    p->tile_k = W4A16_GROUP;
+    p->grid_x = static_cast<int32_t>(ceil_div(N, tile_n));
+    p->grid_y = static_cast<int32_t>(ceil_div(M, v.bm));
+    p->grid_z = static_cast<int32_t>(S);
     p->block_threads = 64 * v.nwaves;
-    p->variant = variant;
-    p->workspace_bytes = p->split_k > 1 ? 2ull * static_cast<uint64_t>(p->split_k) * M * N * sizeof(float) : 0;
+    p->split_k = static_cast<int32_t>(S);
+    p->k_waves = 1;
+    p->variant = variant + (codes ? kQmmCodesVariantOffset : 0);
+    p->workspace_bytes = (codes ? group_sum_bytes(M, K) : 0) +
+                         (S > 1 ? 2ull * static_cast<uint64_t>(S) * M * N * sizeof(float) : 0);
 }
 
 int make_gate_up_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, int32_t num_cus,
@@ -335,15 +351,24 @@ int run_gate_up(const uint16_t* x, const uint32_t* wq_g, const uint16_t* s_g, co
     st = make_gate_up_plan(M, N, K, group, split_k, 0, &p);
     if (st != W4A16_OK) return st;
     const int32_t cus = p.num_cus;
-    st = fit_workspace(p, split_k, workspace, ws_bytes, [&](int32_t S, bool) {
-        plan_gate_up(M, N, K, S, cus, &p);
+    st = fit_workspace(p, split_k, workspace, ws_bytes, [&](int32_t S, bool codes) {
+        plan_gate_up(M, N, K, S, cus, &p, codes);
         p.num_cus = cus;
     });
     if (st != W4A16_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    float* ws = static_cast<float*>(workspace);
-    hipError_t e = launch_gate_up(p.variant, x, nullptr, wq_g, s_g, b_g, wq_u, s_u, b_u, h, ws,
-                                  static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), p.split_k, s);
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    uint16_t* xsum = nullptr;
+    uint8_t* rest = static_cast<uint8_t*>(workspace);
+    if (plan_codes(p)) {
+        xsum = static_cast<uint16_t*>(workspace);
+        rest += group_sum_bytes(M, K);
+        const hipError_t e0 = launch_act_group_sums(x, xsum, m, k, group_sum_cols(k), s);
+        if (e0 != hipSuccess) return to_status(e0);
+    }
+    float* ws = reinterpret_cast<float*>(rest);
+    hipError_t e = launch_gate_up(plan_tile_variant(p), x, xsum, wq_g, s_g, b_g, wq_u, s_u, b_u, h, ws, m, n, k,
+                                  p.split_k, s);
     if (e != hipSuccess || p.split_k == 1) return to_status(e);
     return to_status(launch_splitk_reduce_glu(ws, h, M * N, p.split_k, s));
 }

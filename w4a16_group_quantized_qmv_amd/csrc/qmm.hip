@@ -619,7 +619,7 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, cons
 
 const QmmShape kGateUpVariants[kNumGateUpVariants] = {
     {32, 1, 4, 2},   // 0:  32 x 128 tile of h (gate and up: 2 x 32 columns per wave), four waves per SIMD
-    {64, 1, 4, 2},   // 1:  64 x 128 tile of h, three waves per SIMD
+    {64, 1, 4, 2},   // 1:  64 x 128 tile of h, three waves per SIMD (two in the exact-code mode)
     {128, 1, 4, 2},  // 2: 128 x 128 tile of h, one wave per SIMD
 };
 
@@ -628,10 +628,11 @@ hipError_t launch_gate_up(int variant, const uint16_t* x, const uint16_t* xsum, 
                           const uint16_t* b_up, uint16_t* h, float* ws, int M, int N, int K, int split,
                           hipStream_t stream) {
     const int KB = group_sum_cols(K);
+    if (xsum && variant != kGateUpCodesTileVariant) return hipErrorInvalidValue;
     switch (variant) {
         case 0: return launch_gate_up_t<32, 4, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K,
                                                   split, stream);
-        case 1: return launch_gate_up_t<64, 3, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K,
+        case 1: return launch_gate_up_t<64, 3, 2, 1, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K,
                                                   split, stream);
         case 2: return launch_gate_up_t<128, 1, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N,
                                                    K, split, stream);
