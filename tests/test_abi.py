@@ -90,8 +90,9 @@ def test_grid_covers_the_output():
         if p["path"] == w4.PATH_QMV and p["grid_x"] * p["tile_n"] < N:
             # persistent wide matvec: resident workgroups whose waves loop over 16-column blocks
             waves_per_wg = p["block_threads"] // 64
+            assert waves_per_wg == (8 if M <= 4 else 4)      # eight-wave workgroups up to 4 rows
             assert p["tile_n"] == 16 and p["k_waves"] == 1
-            assert p["grid_x"] == min(-(-N // (16 * waves_per_wg)), 8 * CUS)
+            assert p["grid_x"] == min(-(-N // (16 * waves_per_wg)), 32 // waves_per_wg * CUS)
             continue
         assert p["grid_x"] * p["tile_n"] >= N and (p["grid_x"] - 1) * p["tile_n"] < N
         if p["path"] == w4.PATH_QMM:

@@ -89,17 +89,19 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
     p->tile_m = 16;
     p->tile_n = v.cb * v.wn * 16;
     p->tile_k = W4A16_GROUP;
+    int waves = v.wn * v.kw;
     if (variant == kQmvWideVariant) {
         // persistent: at most as many workgroups as are resident at once (the launch asks the
-        // runtime how many fit per compute unit; 8 is the register limit of this instance)
+        // runtime how many fit per compute unit; 32 waves per compute unit is the register limit)
+        waves = qmv_wide_waves(static_cast<int>(M));
         p->tile_n = 16;
-        p->grid_x = static_cast<int32_t>(std::min<int64_t>(ceil_div(blocks16, v.wn), int64_t{8} * cus));
+        p->grid_x = static_cast<int32_t>(std::min<int64_t>(ceil_div(blocks16, waves), int64_t{32 / waves} * cus));
     } else {
         p->grid_x = static_cast<int32_t>(ceil_div(N, p->tile_n));
     }
     p->grid_y = 1;
     p->grid_z = 1;
-    p->block_threads = 64 * v.wn * v.kw;
+    p->block_threads = 64 * waves;
     p->split_k = 1;
     p->k_waves = v.kw;
     p->variant = variant;
@@ -184,7 +186,7 @@ void plan_skinny(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, 
     if (M <= kQmvKernelRows) {
         plan_qmv(M, N, K, cus, p);
         const bool wide_too_big = p->variant == kQmvWideVariant &&
-                                  kQmvWideStaticLds + qmv_wide_lds_bytes(static_cast<int>(M), static_cast<int>(K)) >
+                                  qmv_wide_static_lds(static_cast<int>(M)) + qmv_wide_lds_bytes(static_cast<int>(M), static_cast<int>(K)) >
                                       kQmvWideSkinnyLds;
         if (!wide_too_big) {
             p->path = W4A16_PATH_SKINNY;

@@ -18,7 +18,8 @@ struct QmvShape {
 constexpr int kNumQmvVariants = 4;
 extern const QmvShape kQmvVariants[kNumQmvVariants];
 
-// The wide (persistent) qmv instance: 16-column blocks, 4-wave workgroups, 2 LDS stages.
+// The wide (persistent) qmv instances: 16-column blocks, 2 LDS stages, workgroups of
+// qmv_wide_waves(M) waves.
 constexpr int kQmvWideVariant = 2;
 // The row-amortized kernel of the width-generic matvec at 4 bits (16 columns, 4 waves split K):
 // exact integer codes on the matrix core and y += s * P + b * X per group.
@@ -26,18 +27,28 @@ constexpr int kQmvAmortizedVariant = 3;
 constexpr int kQmvWideStages = 2;
 // Its LDS: per wave and stage one 2 KB block of codes plus 512 bytes of scales and biases
 // (with 1 KB allowed for the kernel's small placeholder objects); dynamically the permuted
-// activations (whole 1 KB units of 64 chunks of 16 bytes) and the per-group activation sums
-// (16 fp32 per group).
-constexpr size_t kQmvWideStaticLds = 4 * (2048 + 512) * kQmvWideStages + 1024;
+// activations (whole 1 KB units of 64 chunks of 16 bytes), the per-group activation sums
+// (16 fp32 per group) and a zero area that the operand reads of padding rows (M..15) address
+// (four sub-step strides of 64 M bytes).
+// Eight waves per workgroup up to 4 rows (half the activation copies per compute unit: on the
+// 151936-column vocabulary head at M = 1 measured 41-42 us against 44-47 us with four), four
+// beyond, where the activation tile grows.
+inline int qmv_wide_waves(int M) { return M <= 4 ? 8 : 4; }
+inline size_t qmv_wide_static_lds(int M) {
+    return static_cast<size_t>(qmv_wide_waves(M)) * (2048 + 512) * kQmvWideStages + 1024;
+}
 inline size_t qmv_wide_x_bytes_host(int M, int K) {
     const size_t chunks = static_cast<size_t>(M) * (K / 8);
     return (chunks + 63) / 64 * 1024;
 }
-inline size_t qmv_wide_lds_bytes(int M, int K) { return qmv_wide_x_bytes_host(M, K) + static_cast<size_t>(K / 128) * 64; }
+inline size_t qmv_wide_zero_bytes(int M) { return static_cast<size_t>(192 * M + 16); }
+inline size_t qmv_wide_lds_bytes(int M, int K) {
+    return qmv_wide_x_bytes_host(M, K) + static_cast<size_t>(K / 128) * 64 + qmv_wide_zero_bytes(M);
+}
 // The wide kernel needs an even group count, at most 16 rows and its LDS within a workgroup's
 // 160 KB.
 inline bool qmv_wide_fits(int M, int K) {
-    return (K / 128) % 2 == 0 && M >= 1 && M <= 16 && kQmvWideStaticLds + qmv_wide_lds_bytes(M, K) <= 160 * 1024;
+    return (K / 128) % 2 == 0 && M >= 1 && M <= 16 && qmv_wide_static_lds(M) + qmv_wide_lds_bytes(M, K) <= 160 * 1024;
 }
 
 hipError_t launch_qmv(int variant, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,

@@ -270,7 +270,8 @@ __global__ __launch_bounds__(64 * W) void qmv_wide_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t st3[W][D > 3 ? kStage : 16];
     __shared__ __attribute__((aligned(16))) uint8_t st4[W][D > 4 ? kStage : 16];
     __shared__ __attribute__((aligned(16))) uint8_t st5[W][D > 5 ? kStage : 16];
-    // dynamic LDS: permuted activations (qmv_wide_x_bytes), then X[g][16 rows] as fp32
+    // dynamic LDS: permuted activations (qmv_wide_x_bytes), then X[g][16 rows] as fp32, then
+    // 192 M + 16 bytes of zeros
     extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
 
     const int G = K >> 7;
@@ -282,6 +283,7 @@ __global__ __launch_bounds__(64 * W) void qmv_wide_kernel(
     const int arow = lane & 15;
     const bool arow_ok = arow < M;
     float* const xsum = reinterpret_cast<float*>(xl + qmv_wide_x_bytes(M, K));
+    const int zero_off = qmv_wide_x_bytes(M, K) + G * 64;
     auto clamp_records = [](int64_t bytes) { return static_cast<int>(bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes); };
     const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
     const u32x4_t zero_u4 = {0u, 0u, 0u, 0u};
@@ -292,48 +294,11 @@ __global__ __launch_bounds__(64 * W) void qmv_wide_kernel(
         return arow_ok ? *reinterpret_cast<const u32x4_t*>(xl + chunk * 16) : zero_u4;
     };
 
-    // ---- prologue 1: activations into LDS in A-operand order, permuted like the codes
-    {
-        const int chunks = M * (K >> 3);
-        const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(x), 0, clamp_records(static_cast<int64_t>(M) * K * 2), 0x00020000);
-        for (int i = wave; i * 64 < chunks; i += W) {
-            const int d = i * 64 + lane;
-            uint32_t voff = 0x80000000u;            // past the end: out of range, reads zeros
-            if (d < chunks) {
-                const int m = d % M;
-                int r = d / M;
-                const int q = r & 3;
-                r >>= 2;
-                const int t = r & 3;
-                const int g = r >> 2;
-                voff = static_cast<uint32_t>(m * K + g * kGroup + q * 32 + t * 8) * 2u;
-            }
-            const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, voff, 0, 0));
-            *reinterpret_cast<bf16x8_t*>(xl + i * 1024 + lane * 16) = permute_like_codes(v);
-        }
-        __syncthreads();
-    }
-    // ---- prologue 2: X[m, g] = sum of the group's activations of row m, by the matrix core
-    {
-        const bf16x8_t ones = {__bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f),
-                               __bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f)};
-        for (int g = wave; g < G; g += W) {
-            f32x4_t xs = zero4;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) xs = mfma16x16x32(__builtin_bit_cast(bf16x8_t, read_a(g, t)), ones, xs);
-            // D layout: lane (c, q) holds rows 4q .. 4q + 3, the same for every column c
-            if ((lane & 15) == 0) *reinterpret_cast<f32x4_t*>(xsum + g * 16 + 4 * kq) = xs;
-        }
-        __syncthreads();
-    }
-
     const int waves = gridDim.x * W;
     const int gw = blockIdx.x * W + wave;
     const int blocks = (N + CB * 16 - 1) / (CB * 16);
     const int my_blocks = gw < blocks ? (blocks - gw + waves - 1) / waves : 0;
     const int T = my_blocks * pairs;
-    if (T == 0) return;
 
     const int c = lane & 15;
     const int lh = lane >> 4, lr = lane & 15;
@@ -341,6 +306,11 @@ __global__ __launch_bounds__(64 * W) void qmv_wide_kernel(
     const uint32_t voff_hi = static_cast<uint32_t>((8 + (lr & 7)) * row_bytes + (1 - (lr >> 3)) * 64 + lh * 16);
     const uint32_t sb_voff = lane < 16 * CB ? static_cast<uint32_t>(lane * G * 2) : 0x80000000u;
     const int rd0 = pair_slot(c, 0, kq), rd1 = pair_slot(c, 1, kq);
+    // steady-state operand reads without branches: lanes of padding rows read the zero area at
+    // the same sub-step strides (their group stride is 0)
+    const int a_base = arow_ok ? (kq * M + arow) * 16 : zero_off;
+    const int a_gstride = arow_ok ? 256 * M : 0;
+    const int a_tstride = 64 * M;
 
     auto stage = [&](auto ic) -> uint8_t* {
         constexpr int i = decltype(ic)::value;
@@ -389,6 +359,57 @@ __global__ __launch_bounds__(64 * W) void qmv_wide_kernel(
         }
     };
 
+    // The first D - 1 steps of weights go out before the activations are staged, so the weight
+    // stream's first memory latency overlaps the prologue (whose waits on its own loads also
+    // cover these; the loop below skips its fill loads).
+    if (T > 0) {
+        issue(std::integral_constant<int, 0>{});
+        if constexpr (D > 2) issue(std::integral_constant<int, 1>{});
+        if constexpr (D > 3) issue(std::integral_constant<int, 2>{});
+        if constexpr (D > 4) issue(std::integral_constant<int, 3>{});
+        if constexpr (D > 5) issue(std::integral_constant<int, 4>{});
+    }
+
+    // ---- prologue 1: activations into LDS in A-operand order, permuted like the codes
+    {
+        const int chunks = M * (K >> 3);
+        const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(x), 0, clamp_records(static_cast<int64_t>(M) * K * 2), 0x00020000);
+        for (int i = wave; i * 64 < chunks; i += W) {
+            const int d = i * 64 + lane;
+            uint32_t voff = 0x80000000u;            // past the end: out of range, reads zeros
+            if (d < chunks) {
+                const int m = d % M;
+                int r = d / M;
+                const int q = r & 3;
+                r >>= 2;
+                const int t = r & 3;
+                const int g = r >> 2;
+                voff = static_cast<uint32_t>(m * K + g * kGroup + q * 32 + t * 8) * 2u;
+            }
+            const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, voff, 0, 0));
+            *reinterpret_cast<bf16x8_t*>(xl + i * 1024 + lane * 16) = permute_like_codes(v);
+        }
+        for (int i = threadIdx.x; i * 16 < 192 * M + 16; i += 64 * W)
+            *reinterpret_cast<u32x4_t*>(xl + zero_off + i * 16) = zero_u4;
+        __syncthreads();
+    }
+    // ---- prologue 2: X[m, g] = sum of the group's activations of row m, by the matrix core
+    {
+        const bf16x8_t ones = {__bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f),
+                               __bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f)};
+        for (int g = wave; g < G; g += W) {
+            f32x4_t xs = zero4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xs = mfma16x16x32(__builtin_bit_cast(bf16x8_t, read_a(g, t)), ones, xs);
+            // D layout: lane (c, q) holds rows 4q .. 4q + 3, the same for every column c
+            if ((lane & 15) == 0) *reinterpret_cast<f32x4_t*>(xsum + g * 16 + 4 * kq) = xs;
+        }
+        __syncthreads();
+    }
+
+    if (T == 0) return;
+
     f32x4_t yacc[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) yacc[cb] = zero4;
@@ -401,8 +422,9 @@ __global__ __launch_bounds__(64 * W) void qmv_wide_kernel(
         for (int g2 = 0; g2 < 2; ++g2) {
             const int g = 2 * cp + g2;
             bf16x8_t a[4];
+            const uint8_t* ab = xl + a_base + g * a_gstride;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) a[t] = __builtin_bit_cast(bf16x8_t, read_a(g, t));
+            for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const bf16x8_t*>(ab + t * a_tstride);
             const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(xsum + g * 16 + 4 * kq);
             const int rd = g2 == 0 ? rd0 : rd1;
 #pragma unroll
@@ -440,7 +462,8 @@ __global__ __launch_bounds__(64 * W) void qmv_wide_kernel(
     // body loads step t + D - 1 into stage d, waits until only the newest D - 1 steps of loads
     // are outstanding (so step t has landed) and computes step t from stage (d + 1) % D.  The
     // stage being loaded was computed one position earlier; its LDS reads have all returned
-    // (their values fed the MFMAs).  The first D - 1 positions only load.  Keeping the fill
+    // (their values fed the MFMAs).  The first D - 1 positions (the fill, loaded before the
+    // prologue) do nothing.  Keeping the fill
     // inside the loop (no peeled prologue) lets the compiler see that each stage's reads
     // depend on that stage's loads alone.
     using I0 = std::integral_constant<int, 0>;
@@ -459,7 +482,7 @@ __global__ __launch_bounds__(64 * W) void qmv_wide_kernel(
     asm volatile("" : "+s"(t));   // opaque start: the fill iterations are not peeled off the loop
 #define W4A16_WIDE_STEP(d, I, C)                                                          \
     if constexpr (D > d) {                                                                \
-        issue(I{});                                                                       \
+        if (t >= 0) issue(I{});                                                           \
         if (t >= 0) {                                                                     \
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"((D - 1) * kLoadsPerStep) : "memory"); \
             compute(C{});                                                                 \
@@ -482,7 +505,7 @@ __global__ __launch_bounds__(64 * W) void qmv_wide_kernel(
 const QmvShape kQmvVariants[kNumQmvVariants] = {
     {1, 1, 4},   // 0: 16 columns per workgroup, 4 waves split K
     {2, 2, 2},   // 1: 64 columns per workgroup, 2 waves split K
-    {1, 4, 1},   // 2: wide: persistent, 16-column blocks, 4-wave workgroups, 2 LDS stages
+    {1, 4, 1},   // 2: wide: persistent, 16-column blocks, 8-wave (M <= 4) or 4-wave workgroups, 2 LDS stages
     {1, 1, 4},   // 3: row-amortized (width-generic kernel at 4 bits), 16 columns, 4 waves split K
 };
 
@@ -502,14 +525,13 @@ struct WideLaunchCache {
     std::atomic<int> cus{0};
     std::atomic<uint64_t> occupancy{0};
 };
-WideLaunchCache g_wide_cache[kMaxDevices];
 }  // namespace
 
 template <int CB, int D, int W>
 static hipError_t launch_qmv_wide_t(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                                     uint16_t* y, int M, int N, int K, hipStream_t stream) {
-    static_assert(CB == 1 && W == 4 && D == kQmvWideStages, "qmv_wide_fits describes this instance");
-    if (!qmv_wide_fits(M, K)) return hipErrorInvalidValue;
+    static_assert(CB == 1 && D == kQmvWideStages, "qmv_wide_fits describes this instance");
+    if (!qmv_wide_fits(M, K) || W != qmv_wide_waves(M)) return hipErrorInvalidValue;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -520,13 +542,14 @@ static hipError_t launch_qmv_wide_t(const uint16_t* x, const uint32_t* wq, const
     // Per device, once: the compute-unit count, and permission for the largest dynamic LDS the
     // fit check admits.  Per activation size: resident workgroups per compute unit (cached for
     // the last size asked; a race only repeats the query).
-    WideLaunchCache& cache = g_wide_cache[dev];
+    static WideLaunchCache caches[kMaxDevices];   // per instance
+    WideLaunchCache& cache = caches[dev];
     if (!cache.ready.load(std::memory_order_acquire)) {
         int cus = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                static_cast<int>(160 * 1024 - kQmvWideStaticLds));
+                                static_cast<int>(160 * 1024 - qmv_wide_static_lds(M)));
         if (e != hipSuccess) return e;
         cache.cus.store(cus, std::memory_order_relaxed);
         cache.ready.store(true, std::memory_order_release);
@@ -551,7 +574,10 @@ hipError_t launch_qmv(int variant, const uint16_t* x, const uint32_t* wq, const 
     switch (variant) {
         case 0: return launch_qmv_t<1, 1, 4>(x, wq, scales, biases, y, M, N, K, stream);
         case 1: return launch_qmv_t<2, 2, 2>(x, wq, scales, biases, y, M, N, K, stream);
-        case kQmvWideVariant: return launch_qmv_wide_t<1, kQmvWideStages, 4>(x, wq, scales, biases, y, M, N, K, stream);
+        case kQmvWideVariant:
+            return qmv_wide_waves(M) == 8
+                       ? launch_qmv_wide_t<1, kQmvWideStages, 8>(x, wq, scales, biases, y, M, N, K, stream)
+                       : launch_qmv_wide_t<1, kQmvWideStages, 4>(x, wq, scales, biases, y, M, N, K, stream);
         case kQmvAmortizedVariant: return launch_qmv_bits(4, kQmvBitsMatrix, x, wq, scales, biases, y, M, N, K, stream);
         default: return hipErrorInvalidValue;
     }
