@@ -424,7 +424,8 @@ def assert_swiglu_parity(h_bits, x, gate, up, rows=None):
     (33, 96, 256, 0),          # ragged M and N, 64-row exact-code tiles
     (1, 1000, 2560, 0),        # one row: 32-row tiles, policy split
     (20, 1000, 2560, 0),       # skinny rows, ragged N
-    (128, 9728, 2560, 0),      # the 128-row gate / up shape, policy split (3 slices)
+    (128, 9728, 2560, 0),      # the 128-row gate / up shape (152 tiles: unsplit)
+    (128, 2560, 4096, 0),      # 40 tiles of 32 groups: policy split (6 slices)
     (128, 2000, 1024, 1),      # forced: unsplit
     (70, 1100, 1024, 2),       # forced: two slices
     (70, 1100, 1024, 5),       # forced: five slices of 1 or 2 groups

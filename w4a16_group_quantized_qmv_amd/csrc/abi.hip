@@ -115,9 +115,10 @@ uint64_t group_sum_bytes(int64_t M, int64_t K) {
     return round256(static_cast<uint64_t>(M) * group_sum_cols(static_cast<int>(K)) * 2);
 }
 
-// Split-K slices for a grid of `tiles` output tiles over G groups: the caller's split_k if
-// nonzero (at most G), else the policy's (skinny: the rule of the 32-row tiles).
-int64_t tile_split(int64_t tiles, int64_t G, int32_t split_k, int32_t cus, bool skinny) {
+// Split-K slices for a grid of `tiles` output tiles (of an M x N output) over G groups: the
+// caller's split_k if nonzero (at most G), else the policy's (skinny: the rule of the 32-row
+// tiles).
+int64_t tile_split(int64_t tiles, int64_t M, int64_t N, int64_t G, int32_t split_k, int32_t cus, bool skinny) {
     int64_t S = 1;
     if (split_k == 0) {
         if (skinny) {
@@ -128,14 +129,23 @@ int64_t tile_split(int64_t tiles, int64_t G, int32_t split_k, int32_t cus, bool 
                 if (S < 2) S = 1;
             }
         } else if (tiles < cus && G >= 2 * kSplitMinGroups) {
-            // split only an under-filled grid, and only when every slice keeps several groups.
-            // Measured on MI355X (M = 128 and 512 for the 2560-wide layer's projections): one
-            // slice more than just filling the compute units wins for the K/V, O and down
-            // projections (e.g. S = 3 for 160 tiles), because a compute unit holds several
-            // workgroups.
-            S = ceil_div(cus, tiles) + 1;
-            if (S > G / kSplitMinGroups) S = G / kSplitMinGroups;
-            if (S < 2) S = 1;
+            // Split only an under-filled grid, by a cost model fitted to sweeps of S = 1..8 on
+            // MI355X (64 x 128 tiles; M = 128 and 512; the q, k/v, o, gate and down shapes of
+            // the 2560-wide layer): rounds of one work unit per compute unit x groups per
+            // slice x 0.75 us, plus 2 us and 0.3 us per MB of fp32 partials for a split.  It
+            // picks the measured best S (or one within 0.7 us) on every swept shape, e.g.
+            // S = 3 for 160 tiles of K = 4096 or 9728, S = 1 for 152 tiles of K = 2560; every
+            // slice keeps at least kSplitMinGroups groups.
+            double best = 0.0;
+            const int64_t s_max = std::min<int64_t>(8, G / kSplitMinGroups);
+            for (int64_t s = 1; s <= s_max; ++s) {
+                double t = static_cast<double>(ceil_div(tiles * s, cus)) * static_cast<double>(ceil_div(G, s)) * 0.75;
+                if (s > 1) t += 2.0 + 0.3 * static_cast<double>(s * M * N) * 4.0 / 1e6;
+                if (s == 1 || t < best) {
+                    best = t;
+                    S = s;
+                }
+            }
         }
     } else {
         S = split_k < 1 ? 1 : split_k;
@@ -158,7 +168,7 @@ void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a
     const QmmShape& v = kQmmVariants[variant];
     const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
     const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, tile_n);
-    const int64_t S = tile_split(tiles, G, split_k, cus, skinny);
+    const int64_t S = tile_split(tiles, M, N, G, split_k, cus, skinny);
     p->path = skinny ? W4A16_PATH_SKINNY : W4A16_PATH_QMM;
     p->tile_m = v.bm;
     p->tile_n = static_cast<int32_t>(tile_n);
@@ -307,7 +317,7 @@ void plan_gate_up(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus,
     const QmmShape& v = kGateUpVariants[variant];
     const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
     const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, tile_n);
-    const int64_t S = tile_split(tiles, K / W4A16_GROUP, split_k, cus, skinny);
+    const int64_t S = tile_split(tiles, M, N, K / W4A16_GROUP, split_k, cus, skinny);
     p->path = W4A16_PATH_GATE_UP;
     p->tile_m = v.bm;
     p->tile_n = static_cast<int32_t>(tile_n);
