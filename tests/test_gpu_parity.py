@@ -313,6 +313,45 @@ def test_vocab_logits_to_keep(lib, vocab):
     assert np.array_equal(keep3, bits(lib.linear(x[-3:], wq, s, b)))
 
 
+# ---------------------------------------------------------------------------------- scale alignment
+# The ABI requires 2-byte aligned scales and biases.  The tile kernels read them four groups per
+# 8-byte load only when both arrays are 8-byte aligned (and G % 4 == 0), and the wide matvec a
+# group pair per 4-byte load only when they are 4-byte aligned; otherwise the per-group forms run.
+
+def offset_by_one(t):
+    """The same bf16 values in a buffer that starts 2 bytes past an aligned allocation."""
+    import torch
+    flat = torch.zeros(t.numel() + 1, dtype=t.dtype, device=t.device)
+    flat[1:] = t.reshape(-1)
+    return flat[1:].view(t.shape)
+
+
+def test_tile_scales_at_two_byte_offsets_match_aligned(lib):
+    # G = 20: the aligned call reads scales four groups per load, the offset one per group; the
+    # per-group arithmetic is the same, so the results agree bit for bit
+    import torch
+    p = synth.random_problem(41, 200, 1024, 2560)
+    announce("qmm scales at 2-byte offsets M=200 N=1024 K=2560")
+    x, wq, s, b = to_device(p)
+    so, bo = offset_by_one(s), offset_by_one(b)
+    assert so.data_ptr() % 8 == 2 and bo.data_ptr() % 8 == 2
+    y_al = bits(lib.linear(x, wq, s, b, path="qmm", split_k=1))
+    y_off = bits(lib.linear(x, wq, so, bo, path="qmm", split_k=1))
+    assert np.array_equal(y_al, y_off)
+    assert_parity(y_off, p, rows=np.r_[0, 63, 64, 199])
+
+
+def test_wide_matvec_scales_at_two_byte_offsets(lib):
+    # 24576 columns route one row to the persistent wide kernel; offset scales take the 64-column
+    # kernel instead; both within the tolerance
+    p = synth.random_problem(42, 1, 24576, 256)
+    assert lib.w4a16_plan(1, 24576, 256)["variant"] == 2
+    announce("wide qmv scales at 2-byte offsets M=1 N=24576 K=256")
+    x, wq, s, b = to_device(p)
+    assert_parity(bits(lib.linear(x, wq, s, b)), p)
+    assert_parity(bits(lib.linear(x, wq, offset_by_one(s), offset_by_one(b))), p)
+
+
 # ---------------------------------------------------------------------------------- memory safety
 
 SENTINEL = 0x7FA5   # a NaN pattern the kernels never produce

@@ -575,6 +575,9 @@ hipError_t launch_qmv(int variant, const uint16_t* x, const uint32_t* wq, const 
         case 0: return launch_qmv_t<1, 1, 4>(x, wq, scales, biases, y, M, N, K, stream);
         case 1: return launch_qmv_t<2, 2, 2>(x, wq, scales, biases, y, M, N, K, stream);
         case kQmvWideVariant:
+            // the wide kernel loads the scales (biases) of a group pair as one 4-byte word
+            if (reinterpret_cast<uintptr_t>(scales) % 4 != 0 || reinterpret_cast<uintptr_t>(biases) % 4 != 0)
+                return launch_qmv_t<2, 2, 2>(x, wq, scales, biases, y, M, N, K, stream);
             return qmv_wide_waves(M) == 8
                        ? launch_qmv_wide_t<1, kQmvWideStages, 8>(x, wq, scales, biases, y, M, N, K, stream)
                        : launch_qmv_wide_t<1, kQmvWideStages, 4>(x, wq, scales, biases, y, M, N, K, stream);
