@@ -84,7 +84,8 @@ typedef struct w4a16_plan {
     int32_t grid_z;            /* split-K slices (qmm) or 1                                 */
     int32_t block_threads;     /* threads per workgroup                                     */
     int32_t split_k;           /* S: number of K slices (1 = unsplit)                       */
-    int32_t k_waves;           /* qmv: waves of one workgroup that split K (1 = none)       */
+    int32_t k_waves;           /* waves of one workgroup that split K (1 = none): qmv waves
+                                  over groups; qmm tiles with two waves per column strip  */
     int32_t num_cus;           /* compute units the plan was made for                       */
     int32_t variant;           /* kernel instance index (diagnostic); qmm and gate / up plans
                                   add 10 when they run the exact-code form (see qmm_w4a16)    */

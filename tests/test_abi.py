@@ -100,6 +100,18 @@ def test_grid_covers_the_output():
         assert p["tile_k"] == 128 and p["num_cus"] == CUS
 
 
+def test_k_split_waves_for_small_grids():
+    # at most one work unit per compute unit: the 64 x 128 tiles run with two waves per column
+    # strip (k_waves = 2, 8-wave workgroups); larger grids keep four waves
+    q = plan(512, 4096, 2560)                      # 256 tiles, unsplit
+    assert (q["tile_m"], q["tile_n"], q["k_waves"], q["block_threads"]) == (64, 128, 2, 512)
+    k = plan(512, 1024, 2560)                      # 64 tiles x 4 slices
+    assert k["k_waves"] == 2 and k["grid_x"] * k["grid_y"] * k["split_k"] <= CUS
+    for M, N, K in [(512, 9728, 2560), (512, 2560, 4096), (2048, 9728, 2560), (32, 9728, 2560)]:
+        p = plan(M, N, K)
+        assert p["k_waves"] == 1 and p["block_threads"] == 256, (M, N, K)
+
+
 def test_split_k_only_for_under_filled_grids():
     # "Benchmark Analysis: Identify Under-Filled Prefill Shapes": the short, narrow K/V
     # projection (32 rows, N = 1024) has too few tiles and gains from split-K ...

@@ -164,11 +164,15 @@ void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a
     // rows, where the grid is small; 128 x 128 tiles (two waves per SIMD) lead beyond.  For at
     // most 32 rows, 32 x 128 tiles (four waves per SIMD, three stages) lead on every layer shape
     // and on the vocabulary head.
-    const int variant = skinny ? kQmmSkinnyVariant : (M <= 1024 ? 1 : 0);
-    const QmmShape& v = kQmmVariants[variant];
-    const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
-    const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, tile_n);
+    int variant = skinny ? kQmmSkinnyVariant : (M <= 1024 ? 1 : 0);
+    const int64_t tile_n = kQmmVariants[variant].tile_n();
+    const int64_t tiles = ceil_div(M, kQmmVariants[variant].bm) * ceil_div(N, tile_n);
     const int64_t S = tile_split(tiles, M, N, G, split_k, cus, skinny);
+    // At most one work unit per compute unit: the same tiles with two waves per column strip
+    // (measured on MI355X: 512-row q 23.6 -> 21.4 us, k/v 16.4 -> 15.0 us, 128-row gate 22.6 ->
+    // 21.7 us; with more units per compute unit it measured 0-6% slower).
+    if (variant == 1 && tiles * S <= cus) variant = kQmmKSplitVariant;
+    const QmmShape& v = kQmmVariants[variant];
     p->path = skinny ? W4A16_PATH_SKINNY : W4A16_PATH_QMM;
     p->tile_m = v.bm;
     p->tile_n = static_cast<int32_t>(tile_n);
@@ -178,7 +182,7 @@ void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a
     p->grid_z = static_cast<int32_t>(S);
     p->block_threads = 64 * v.nwaves;
     p->split_k = static_cast<int32_t>(S);
-    p->k_waves = 1;
+    p->k_waves = v.ksplit;
     codes = codes && variant == kQmmCodesTileVariant;
     p->variant = variant + (codes ? kQmmCodesVariantOffset : 0);
     p->workspace_bytes = (codes ? group_sum_bytes(M, K) : 0) +
@@ -315,7 +319,7 @@ void plan_gate_up(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus,
     codes = codes && !skinny;
     const int variant = skinny ? 0 : (codes ? kGateUpCodesTileVariant : (M <= 1024 ? 1 : 2));
     const QmmShape& v = kGateUpVariants[variant];
-    const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
+    const int64_t tile_n = v.tile_n();
     const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, tile_n);
     const int64_t S = tile_split(tiles, M, N, K / W4A16_GROUP, split_k, cus, skinny);
     p->path = W4A16_PATH_GATE_UP;
@@ -455,7 +459,7 @@ void plan_w4a8(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4
     plan_qmm(M, N, K, split_k, cus, p, M <= kSkinnyMaxRows, false);
     const int variant = M <= kSkinnyMaxRows ? 0 : (M <= 1024 ? 1 : 2);
     const QmmShape& v = kW4A8Variants[variant];
-    const int64_t tile_n = int64_t{v.nwaves} * v.nb * 32;
+    const int64_t tile_n = v.tile_n();
     if (v.bm != p->tile_m || tile_n != p->tile_n) {
         p->tile_m = v.bm;
         p->tile_n = static_cast<int32_t>(tile_n);
@@ -464,6 +468,7 @@ void plan_w4a8(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4
     }
     p->path = W4A16_PATH_W4A8;
     p->block_threads = 64 * v.nwaves;
+    p->k_waves = 1;
     p->variant = variant;
     p->workspace_bytes = p->split_k > 1 ? static_cast<uint64_t>(p->split_k) * M * N * sizeof(float) : 0;
 }

@@ -60,10 +60,15 @@ struct QmmShape {
     int bm;
     int nb;
     int nwaves;
-    int stages;   // groups in flight: LDS activation tiles and weight register sets
+    int stages;       // groups in flight: LDS activation tiles and weight register sets
+    int ksplit = 1;   // waves per 32-column strip, splitting each group's MFMA sub-steps
+    int tile_n() const { return nwaves / ksplit * nb * 32; }
 };
 
-constexpr int kNumQmmVariants = 5;
+constexpr int kNumQmmVariants = 6;
+// 64 x 128 tiles with two waves per column strip: for grids of at most one work unit per
+// compute unit (twice the waves per tile)
+constexpr int kQmmKSplitVariant = 5;
 constexpr int kQmmSkinnyVariant = 4;   // 32 x 128 tiles, three stages: at most 32 rows
 extern const QmmShape kQmmVariants[kNumQmmVariants];
 

@@ -63,20 +63,25 @@ __device__ __forceinline__ float silu_f32(float z) { return z / (1.f + expf(-z))
 // gate / up pair with h = silu(gate) * up formed from the fp32 accumulators in the epilogue
 // (the SwiGLU fused into the mat-mat of "Feature Request: Metal prefill speedup (~68%) on M5
 // Max").  Weight set p of column block cb is block j = p * NB + cb.
-template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES, int NP = 1, int CODES = 0, int SBQ = 1>
+template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES, int NP = 1, int CODES = 0, int SBQ = 1, int KS = 1>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD))) void qmm_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const uint32_t* __restrict__ wq2, const uint16_t* __restrict__ scales2,
     const uint16_t* __restrict__ biases2, uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N, int K,
     int split, int tiles_m, int tiles_n, const uint16_t* __restrict__ xsum, int KB) {
-    constexpr int BN = NW * NB * 32;              // output columns of the tile (per weight set)
+    // KS = 2: two waves share each column strip, one taking sub-steps 0..3 of every group and
+    // the other 4..7; their partial accumulators are added through LDS at the end
+    static_assert(KS == 1 || (KS == 2 && NP == 1), "K-split waves: single projections");
+    constexpr int WN = NW / KS;                   // waves across the tile's columns
+    constexpr int TSUB = 8 / KS;                  // MFMA sub-steps per group and wave
+    constexpr int BN = WN * NB * 32;              // output columns of the tile (per weight set)
     constexpr int J = NP * NB;                    // weight blocks per wave
     static_assert(NP == 1 || NP == 2, "one projection or the gate / up pair");
     constexpr int RB = BM / 32;                   // 32-row blocks per wave
     constexpr int TILE = BM * kGroup;             // bf16 elements of one staged activation tile
     constexpr int DMA_PER_WAVE = BM / (4 * NW);   // 1 KB direct loads per wave per group
     static_assert(BM % (4 * NW) == 0 && BM % 32 == 0, "tile shape");
-    static_assert(NW == 4, "row & 15 of a direct load must not depend on the instruction index");
+    static_assert(WN == 4 && NW % 4 == 0, "row & 15 of a direct load must not depend on the instruction index");
     static_assert(STAGES >= 2 && STAGES <= 3, "stage count");
     // one LDS object per stage: the compiler's wait insertion can then tell that a direct load
     // into one stage does not feed fragment reads of another
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     __shared__ __attribute__((aligned(16))) uint16_t xs1[TILE];
     __shared__ __attribute__((aligned(16))) uint16_t xs2[STAGES > 2 ? TILE : 8];
     // codes of one group, per stage: each wave's J blocks of 32 columns x 64 bytes
-    constexpr int CODES_BYTES = NW * J * 2048;
+    constexpr int CODES_BYTES = WN * J * 2048;
     __shared__ __attribute__((aligned(16))) uint8_t cs0[CODES_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t cs1[CODES_BYTES];
     __shared__ __attribute__((aligned(16))) uint8_t cs2[STAGES > 2 ? CODES_BYTES : 16];
@@ -108,6 +113,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     const int n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kh = wave / WN, wn = wave % WN;     // K half (KS = 2) and column strip of this wave
     const int half = lane >> 5;
     auto clamp_records = [](int64_t bytes) { return static_cast<int>(bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes); };
     auto stage = [&](auto ic) -> uint16_t* {
@@ -167,8 +173,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     uint32_t cvoff[NB], sbvoff[NB];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
-        const int c = (wave * NB + cb) * 32 + (lane & 31);     // column within the tile
-        cvoff[cb] = static_cast<uint32_t>(((wave * NB + cb) * 32 + (lane >> 2)) * row_bytes +
+        const int c = (wn * NB + cb) * 32 + (lane & 31);       // column within the tile
+        cvoff[cb] = static_cast<uint32_t>(((wn * NB + cb) * 32 + (lane >> 2)) * row_bytes +
                                           16 * ((lane & 3) ^ ((lane >> 4) & 3)));
         sbvoff[cb] = static_cast<uint32_t>(c * G * 2);
     }
@@ -194,7 +200,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     // exact-code mode reads the biases once, in the epilogue.  With SBQ = 4 only the first group
     // of each four loads scales and biases (the wait before each group is vmcnt(0) with two
     // stages, so the count may vary); the others copy them from the previous group's slot.
-    constexpr int kLoadsPerGroup = DMA_PER_WAVE + (CODES > 0 ? 3 : 4) * J;
+    constexpr int kLoadsPerGroup = DMA_PER_WAVE + (2 / KS) * J + (CODES > 0 ? 1 : 2) * J;
     // all loads of group g (relative index j = g - g_begin) into stage / slot ic; prev is the
     // slot of group j - 1
     auto issue = [&](int j, auto ic, Slot& o, const Slot& prev, auto quad) {
@@ -216,12 +222,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
             const __amdgpu_buffer_rsrc_t wr = live ? wrsrc[p] : none;
             const __amdgpu_buffer_rsrc_t sr = live ? srsrc[p] : none;
             const __amdgpu_buffer_rsrc_t br = live ? brsrc[p] : none;
-            uint8_t* cdst = cstage(ic) + (wave * J + j) * 2048;
+            uint8_t* cdst = cstage(ic) + (wn * J + j) * 2048;
             // (offsets go through locals: an array element as a builtin operand made the host pass
             // drop the kernel's launch stub)
             const uint32_t co = cvoff[cb], cg = static_cast<uint32_t>(g) * 64u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst, 16, co, cg, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst + 1024, 16, co + 16u * static_cast<uint32_t>(row_bytes), cg, 0, 0);
+            if constexpr (KS == 1) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst, 16, co, cg, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst + 1024, 16, co + 16u * static_cast<uint32_t>(row_bytes),
+                                                         cg, 0, 0);
+            } else {   // the two waves of a strip load one half of its columns each
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wr, cdst + __builtin_amdgcn_readfirstlane(kh * 1024), 16,
+                    co + 16u * static_cast<uint32_t>(kh) * static_cast<uint32_t>(row_bytes), cg, 0, 0);
+            }
             asm volatile("" ::: "memory");
             if constexpr (SBQ == 1) {
                 (void)prev;
@@ -257,7 +270,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     // = 8 * (half ^ (r >> 3 & 1)) + (t ^ (r & 7)); with the row part a multiple of 128 this is
     // one lane constant XOR (t << 3).
     const int arow = lane & 31;
-    const int abase = arow * kGroup + (((half ^ ((arow >> 3) & 1)) << 6) | ((arow & 7) << 3));
+    // (with KS = 2 this wave's sub-steps start at 4 kh: chunk 8 half + 4 kh + tt)
+    const int abase = (arow * kGroup + (((half ^ ((arow >> 3) & 1)) << 6) | ((arow & 7) << 3))) ^ (kh << 5);
 
     f32x16_t acc[RB][J];
 #pragma unroll
@@ -290,13 +304,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
             for (int j = 0; j < J; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) Pr[i][rb][j][r] = 0.f;
-    // this lane's eight code words of block j (words 8 half .. 8 half + 7 of its column's group)
-    auto read_codes = [&](auto ic, u32x4_t (&w)[J][2]) {
-        const uint8_t* cb = cstage(ic) + wave * J * 2048;
+    // this lane's code words of block j: words 8 half .. 8 half + 7 of its column's group
+    // (KS = 2: the four of this wave's sub-steps, 8 half + 4 kh ..)
+    constexpr int WCH = 2 / KS;   // 16-byte chunks per lane and block
+    const int cread_k = kh ? cread1 : cread0;
+    auto read_codes = [&](auto ic, u32x4_t (&w)[J][WCH]) {
+        const uint8_t* cb = cstage(ic) + wn * J * 2048;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            w[j][0] = *reinterpret_cast<const u32x4_t*>(cb + j * 2048 + cread0);
-            w[j][1] = *reinterpret_cast<const u32x4_t*>(cb + j * 2048 + cread1);
+            if constexpr (KS == 1) {
+                w[j][0] = *reinterpret_cast<const u32x4_t*>(cb + j * 2048 + cread0);
+                w[j][1] = *reinterpret_cast<const u32x4_t*>(cb + j * 2048 + cread1);
+            } else {
+                w[j][0] = *reinterpret_cast<const u32x4_t*>(cb + j * 2048 + cread_k);
+            }
         }
     };
 
@@ -304,7 +325,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
         constexpr int PC = PSETS == 1 ? 0 : decltype(pc)::value;
         constexpr int PP = PSETS == 1 ? 0 : (PC + STAGES - 1) % STAGES;
         const uint16_t* xt = stage(ic);
-        u32x4_t ow[J][2];
+        u32x4_t ow[J][WCH];
         read_codes(ic, ow);
         bf16x8_t a[2][RB], bw[2][J];
 #pragma unroll
@@ -312,9 +333,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
 #pragma unroll
         for (int j = 0; j < J; ++j) bw[0][j] = codes_bf16_natural(ow[j][0][0]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < TSUB; ++t) {
             const int cur = t & 1, nxt = cur ^ 1;
-            if (t < 7) {
+            if (t < TSUB - 1) {
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
                     a[nxt][rb] = *reinterpret_cast<const bf16x8_t*>(xt + (abase ^ ((t + 1) << 3)) + rb * 32 * kGroup);
@@ -329,13 +350,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
                     Pr[PC][rb][j] = mfma32x32x16(a[cur][rb], bw[cur][j], t == 0 ? zero : Pr[PC][rb][j]);
                 }
             if constexpr (PSETS > 1) {
-                // an eighth of the previous group's scaling per sub-step
+                // a TSUB-th of the previous group's scaling per sub-step
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int j = 0; j < J; ++j)
 #pragma unroll
-                        for (int r = 2 * t; r < 2 * t + 2; ++r)
+                        for (int r = 2 * KS * t; r < 2 * KS * (t + 1); ++r)
                             acc[rb][j][r] = __builtin_fmaf(s_last[j], Pr[PP][rb][j][r], acc[rb][j][r]);
             }
 #pragma unroll
@@ -362,7 +383,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     };
 
     auto compute = [&](auto ic, const Slot& o, int r) {
-        u32x4_t ow[J][2];
+        u32x4_t ow[J][WCH];
         read_codes(ic, ow);
         float s[J], b[J];
 #pragma unroll
@@ -377,9 +398,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
 #pragma unroll
         for (int j = 0; j < J; ++j) bw[0][j] = dequant_word(ow[j][0][0], s[j], b[j]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
+        for (int t = 0; t < TSUB; ++t) {
             const int cur = t & 1, nxt = cur ^ 1;
-            if (t < 7) {
+            if (t < TSUB - 1) {
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
                     a[nxt][rb] = *reinterpret_cast<const bf16x8_t*>(xt + (abase ^ ((t + 1) << 3)) + rb * 32 * kGroup);
@@ -475,9 +496,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
                     for (int r = 0; r < 16; ++r)
                         acc[rb][j][r] = __builtin_fmaf(s_last[j], Pr[STAGES - 1][rb][j][r], acc[rb][j][r]);
         }
-        // bias term, once per output (slice 0): acc += xsum . baug^T over KB / 16 sub-steps, with
-        // baug[n, k'] = b[n, k' / 2] (zero for k' / 2 >= G) against the hi / lo halves of X
-        if (z == 0) {
+        // bias term, once per output (slice 0, K half 0): acc += xsum . baug^T over KB / 16
+        // sub-steps, with baug[n, k'] = b[n, k' / 2] (zero for k' / 2 >= G) against the hi / lo
+        // halves of X
+        if (z == 0 && kh == 0) {
             const __amdgpu_buffer_rsrc_t xsr = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t*>(xsum + static_cast<size_t>(m0) * KB), 0,
                 clamp_records(static_cast<int64_t>(M - m0) * KB * 2), 0x00020000);
@@ -509,16 +531,51 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
         }
     }
 
+    // KS = 2: the two waves of a strip add their partial sums.  Of the RB * 16 accumulator
+    // elements e = 16 rb + r, K half 0 finishes e < 8 RB and K half 1 the rest; each writes the
+    // other's elements to the activation stage of its own K half, and reads its partner's.
+    if constexpr (KS == 2) {
+        __syncthreads();   // every wave is done with the stages
+        constexpr int HALF = RB * 8;
+        static_assert(WN * HALF * J * 64 * 4 <= TILE * 2, "partial sums fit one activation stage");
+        float* mine = reinterpret_cast<float*>(kh == 0 ? xs0 : xs1) + wn * HALF * J * 64;
+        const float* theirs = reinterpret_cast<const float*>(kh == 0 ? xs1 : xs0) + wn * HALF * J * 64;
+        // element indices stay compile-time constants (a runtime index would move acc to scratch)
+        auto exchange = [&](auto khc) {
+            constexpr int KH = decltype(khc)::value;
+#pragma unroll
+            for (int e = 0; e < HALF; ++e) {
+                constexpr int off = KH == 0 ? HALF : 0;   // the partner's elements
+#pragma unroll
+                for (int j = 0; j < J; ++j) mine[(e * J + j) * 64 + lane] = acc[(e + off) >> 4][j][(e + off) & 15];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < HALF; ++e) {
+                constexpr int off = KH == 0 ? 0 : HALF;   // this wave's elements
+#pragma unroll
+                for (int j = 0; j < J; ++j) acc[(e + off) >> 4][j][(e + off) & 15] += theirs[(e * J + j) * 64 + lane];
+            }
+        };
+        if (kh == 0)
+            exchange(std::integral_constant<int, 0>{});
+        else
+            exchange(std::integral_constant<int, 1>{});
+    }
+
     // epilogue: D layout puts rows 8 * (r / 4) + 4 * half + r % 4 of column lane % 32 in this lane
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+            if constexpr (KS == 2) {
+                if ((16 * rb + r < RB * 8) != (kh == 0)) continue;
+            }
             const int m = m0 + rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
             if (m >= M) continue;
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
-                const int col = n0 + (wave * NB + cb) * 32 + (lane & 31);
+                const int col = n0 + (wn * NB + cb) * 32 + (lane & 31);
                 if (col >= N) continue;
                 const size_t idx = static_cast<size_t>(m) * N + col;
                 if constexpr (NP == 1) {
@@ -607,6 +664,8 @@ const QmmShape kQmmVariants[kNumQmmVariants] = {
     {64, 1, 4, 3},   // 2:  64 x 128 tile, two waves per SIMD, 3 stages
     {32, 1, 4, 2},   // 3:  32 x 128 tile, 4 waves of 32 x 32, four waves per SIMD, 2 stages
     {32, 1, 4, 3},   // 4:  32 x 128 tile, four waves per SIMD, 3 stages (skinny M)
+    {64, 1, 8, 2, 2},  // 5:  64 x 128 tile, 8 waves: two per 32-column strip, each taking half of
+                       //     every group's sub-steps; six waves per SIMD
 };
 
 // Scales and biases four groups per load (two-stage instances) when the group count is a
@@ -619,17 +678,18 @@ static bool quad_scales(int K, int split, const uint16_t* s, const uint16_t* b) 
            reinterpret_cast<uintptr_t>(b) % 8 == 0;
 }
 
-template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES, int CM = 0, int CODES_WPS = WAVES_PER_SIMD>
+template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES, int CM = 0, int CODES_WPS = WAVES_PER_SIMD,
+          int KS = 1>
 static hipError_t launch_qmm_t(const uint16_t* x, const uint16_t* xsum, int KB, const uint32_t* wq, const uint16_t* s,
                                const uint16_t* b, uint16_t* y, float* ws, int M, int N, int K, int split,
                                hipStream_t stream) {
-    constexpr int BN = NW * NB * 32;
+    constexpr int BN = NW / KS * NB * 32;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const dim3 grid(tiles_m * tiles_n * split);
     const bool quad = STAGES == 2 && quad_scales(K, split, s, b);
 #define W4A16_LAUNCH_QMM(WPS, CODES, SBQ, XS)                                                                  \
-    hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WPS, STAGES, 1, CODES, SBQ>), grid, dim3(64 * NW), 0, stream, x, wq, \
+    hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WPS, STAGES, 1, CODES, SBQ, KS>), grid, dim3(64 * NW), 0, stream, x, wq, \
                        s, b, nullptr, nullptr, nullptr, y, ws, M, N, K, split, tiles_m, tiles_n, XS, KB)
     if constexpr (CM > 0) {
         if (xsum) {
@@ -703,6 +763,8 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, cons
         case 2: return launch_qmm_t<64, 1, 4, 2, 3>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
         case 3: return launch_qmm_t<32, 1, 4, 4, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
         case 4: return launch_qmm_t<32, 1, 4, 4, 3>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 5: return launch_qmm_t<64, 1, 8, 6, 2, 0, 6, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split,
+                                                           stream);
         default: return hipErrorInvalidValue;
     }
 }
