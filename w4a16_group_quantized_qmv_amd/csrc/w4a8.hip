@@ -134,6 +134,9 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
     static_assert(BM % 32 == 0 && DMA_PER_WAVE >= 1, "tile shape");
     __shared__ __attribute__((aligned(16))) int8_t xs0[TILE];
     __shared__ __attribute__((aligned(16))) int8_t xs1[TILE];
+    // codes of one group, per stage: each wave's 32 columns x 64 bytes
+    __shared__ __attribute__((aligned(16))) uint8_t cs0[NW * 2048];
+    __shared__ __attribute__((aligned(16))) uint8_t cs1[NW * 2048];
 
     const int tiles = tiles_m * tiles_n;
     const int work = xcd_remap(blockIdx.x, tiles * split);
@@ -169,16 +172,26 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
     const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(scales + static_cast<size_t>(n0) * G), 0, clamp_records(cols_left * G * 2), 0x00020000);
     const int col = wave * 32 + (lane & 31);           // column within the tile
-    const uint32_t wvoff = static_cast<uint32_t>(col * row_bytes + half * 32);
     const uint32_t svoff = static_cast<uint32_t>(col * G * 2);
+    // Codes go through LDS by direct loads that read whole 64-byte column groups (the layout of
+    // the W4A16 tile kernel): instruction i fills columns 16 i + l / 4, lane l writing its 16
+    // bytes to slot l % 4 of the column's 64, slot p holding chunk p ^ ((column / 4) & 3).
+    const uint32_t cvoff = static_cast<uint32_t>((wave * 32 + (lane >> 2)) * row_bytes +
+                                                 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+    const int ccol = lane & 31;
+    const int cread0 = ccol * 64 + 16 * ((2 * half) ^ ((ccol >> 2) & 3));
+    const int cread1 = ccol * 64 + 16 * ((2 * half + 1) ^ ((ccol >> 2) & 3));
 
     struct Slot {
-        u32x4_t w[2];
         uint16_t s;
     };
     auto stage = [&](auto ic) -> int8_t* {
         if constexpr (decltype(ic)::value == 0) return xs0;
         else return xs1;
+    };
+    auto cstage = [&](auto ic) -> uint8_t* {
+        if constexpr (decltype(ic)::value == 0) return cs0 + wave * 2048;
+        else return cs1 + wave * 2048;
     };
     auto issue = [&](int j, auto ic, Slot& o) {
         const bool live = j >= 0 && j < groups;
@@ -193,9 +206,11 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
         }
         const __amdgpu_buffer_rsrc_t wr = live ? wrsrc : none;
         const __amdgpu_buffer_rsrc_t sr = live ? srsrc : none;
-        o.w[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff, g * 64, 0));
-        asm volatile("" ::: "memory");
-        o.w[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, wvoff, g * 64 + 16, 0));
+        uint8_t* cdst = cstage(ic);
+        const uint32_t cg = static_cast<uint32_t>(g) * 64u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst, 16, cvoff, cg, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst + 1024, 16, cvoff + 16u * static_cast<uint32_t>(row_bytes),
+                                                 cg, 0, 0);
         asm volatile("" ::: "memory");
         o.s = __builtin_amdgcn_raw_buffer_load_b16(sr, svoff, g * 2, 0);
         asm volatile("" ::: "memory");
@@ -223,10 +238,14 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
     // Pp (scale s_last) spread between them.
     auto compute = [&](auto ic, const Slot& o, i32x16_t (&Pc)[RB], const i32x16_t (&Pp)[RB]) {
         const int8_t* xt = stage(ic);
+        // this lane's eight code words (words 8 half .. 8 half + 7 of its column's group)
+        const uint8_t* cb = cstage(ic);
+        const u32x4_t ow[2] = {*reinterpret_cast<const u32x4_t*>(cb + cread0),
+                               *reinterpret_cast<const u32x4_t*>(cb + cread1)};
         i32x4_t a[2][RB];
         i32x4_t bq[2];
         auto codes = [&](int t) {
-            const uint32_t w0 = o.w[t >> 1][(t & 1) * 2], w1 = o.w[t >> 1][(t & 1) * 2 + 1];
+            const uint32_t w0 = ow[t >> 1][(t & 1) * 2], w1 = ow[t >> 1][(t & 1) * 2 + 1];
             return i32x4_t{static_cast<int>(even_codes(w0)), static_cast<int>(odd_codes(w0)),
                            static_cast<int>(even_codes(w1)), static_cast<int>(odd_codes(w1))};
         };
