@@ -301,6 +301,15 @@ def test_w4a8_plan_tiles_split_and_workspace():
     assert w4.w4a8_plan(128, 1024, 256, 128, 64, CUS)["split_k"] == 2       # clamped to G
 
 
+def test_w4a8_k_split_waves_for_small_grids():
+    # at most one work unit per compute unit: 64-row tiles with two waves per column block
+    q = w4.w4a8_plan(512, 4096, 2560, 128, 0, CUS)                 # 256 tiles, unsplit
+    assert (q["tile_m"], q["tile_n"], q["k_waves"], q["block_threads"]) == (64, 128, 2, 512)
+    for M, N in [(512, 9728), (2048, 9728), (32, 9728)]:
+        p = w4.w4a8_plan(M, N, 2560, 128, 0, CUS)
+        assert p["k_waves"] == 1 and p["block_threads"] == 256, (M, N)
+
+
 def test_w4a8_xsum_columns_and_linear_workspace():
     # two bf16 halves per group, rounded up to the 16-value MFMA step
     for K, cols in [(128, 16), (256, 16), (1024, 16), (1152, 32), (2560, 48), (4096, 64), (9728, 160)]:

@@ -457,7 +457,9 @@ int run_qmv_affine(const uint16_t* x, const uint32_t* wq, const uint16_t* s, con
 // rule of the W4A16 tiles.  workspace_bytes covers the fp32 partials only.
 void plan_w4a8(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p) {
     plan_qmm(M, N, K, split_k, cus, p, M <= kSkinnyMaxRows, false);
-    const int variant = M <= kSkinnyMaxRows ? 0 : (M <= 1024 ? 1 : 2);
+    int variant = M <= kSkinnyMaxRows ? 0 : (M <= 1024 ? 1 : 2);
+    // at most one work unit per compute unit: two waves per column block, as for the W4A16 tiles
+    if (variant == 1 && ceil_div(M, 64) * ceil_div(N, 128) * p->split_k <= cus) variant = kW4A8KSplitVariant;
     const QmmShape& v = kW4A8Variants[variant];
     const int64_t tile_n = v.tile_n();
     if (v.bm != p->tile_m || tile_n != p->tile_n) {
@@ -468,7 +470,7 @@ void plan_w4a8(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4
     }
     p->path = W4A16_PATH_W4A8;
     p->block_threads = 64 * v.nwaves;
-    p->k_waves = 1;
+    p->k_waves = v.ksplit;
     p->variant = variant;
     p->workspace_bytes = p->split_k > 1 ? static_cast<uint64_t>(p->split_k) * M * N * sizeof(float) : 0;
 }

@@ -116,7 +116,8 @@ hipError_t launch_qmv_bits(int bits, int mode, const uint16_t* x, const uint32_t
 inline int w4a8_xsum_cols(int K) { return group_sum_cols(K); }
 hipError_t launch_quantize_rows_int8(const uint16_t* x, int8_t* xq, float* sx, uint16_t* xsum, int M, int K, int KB,
                                      hipStream_t stream);
-constexpr int kNumW4A8Variants = 3;
+constexpr int kNumW4A8Variants = 4;
+constexpr int kW4A8KSplitVariant = 3;   // 64 x 128 tiles, two waves per column block
 extern const QmmShape kW4A8Variants[kNumW4A8Variants];
 hipError_t launch_qmm_w4a8(int variant, const int8_t* xq, const float* sx, const uint16_t* xsum, const uint32_t* wq,
                            const uint16_t* scales, const uint16_t* biases, uint16_t* y, float* ws, int M, int N,

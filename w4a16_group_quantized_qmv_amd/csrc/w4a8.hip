@@ -120,14 +120,18 @@ __global__ __launch_bounds__(256) void quantize_rows_int8_kernel(const uint16_t*
 // Activations are staged by direct global-to-LDS loads into unpadded 128-byte rows (one wave
 // instruction writes 8 rows); chunk c of tile row r sits at slot c ^ ((r >> 1) & 7), so 16
 // lanes reading one chunk of 16 consecutive rows hit 16 different 16-byte bank groups.
-template <int BM, int WAVES_PER_SIMD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD))) void
+// KS = 2: two waves per column block, one taking sub-steps 0-1 and the other 2-3 of every group;
+// their partial sums are added through the activation stages at the end.
+template <int BM, int WAVES_PER_SIMD, int KS = 1>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD))) void
 qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, const uint16_t* __restrict__ xsum,
                 const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
                 const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N,
                 int K, int KB, int split, int tiles_m, int tiles_n) {
-    constexpr int NW = 4;
-    constexpr int BN = NW * 32;
+    constexpr int WN = 4;                           // waves across the tile's columns
+    constexpr int NW = WN * KS;
+    constexpr int TSUB = 4 / KS;                    // int8 MFMA sub-steps per group and wave
+    constexpr int BN = WN * 32;
     constexpr int RB = BM / 32;
     constexpr int TILE = BM * kGroup;               // bytes of one staged activation tile
     constexpr int DMA_PER_WAVE = BM / (8 * NW);     // 1 KB direct loads per wave per group
@@ -135,8 +139,8 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
     __shared__ __attribute__((aligned(16))) int8_t xs0[TILE];
     __shared__ __attribute__((aligned(16))) int8_t xs1[TILE];
     // codes of one group, per stage: each wave's 32 columns x 64 bytes
-    __shared__ __attribute__((aligned(16))) uint8_t cs0[NW * 2048];
-    __shared__ __attribute__((aligned(16))) uint8_t cs1[NW * 2048];
+    __shared__ __attribute__((aligned(16))) uint8_t cs0[WN * 2048];
+    __shared__ __attribute__((aligned(16))) uint8_t cs1[WN * 2048];
 
     const int tiles = tiles_m * tiles_n;
     const int work = xcd_remap(blockIdx.x, tiles * split);
@@ -153,6 +157,7 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
     const int n0 = tn * BN;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kh = wave / WN, wn = wave % WN;      // K half (KS = 2) and column block
     const int half = lane >> 5;
     auto clamp_records = [](int64_t bytes) { return static_cast<int>(bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes); };
 
@@ -171,12 +176,12 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
         clamp_records(cols_left * row_bytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(scales + static_cast<size_t>(n0) * G), 0, clamp_records(cols_left * G * 2), 0x00020000);
-    const int col = wave * 32 + (lane & 31);           // column within the tile
+    const int col = wn * 32 + (lane & 31);             // column within the tile
     const uint32_t svoff = static_cast<uint32_t>(col * G * 2);
     // Codes go through LDS by direct loads that read whole 64-byte column groups (the layout of
     // the W4A16 tile kernel): instruction i fills columns 16 i + l / 4, lane l writing its 16
     // bytes to slot l % 4 of the column's 64, slot p holding chunk p ^ ((column / 4) & 3).
-    const uint32_t cvoff = static_cast<uint32_t>((wave * 32 + (lane >> 2)) * row_bytes +
+    const uint32_t cvoff = static_cast<uint32_t>((wn * 32 + (lane >> 2)) * row_bytes +
                                                  16 * ((lane & 3) ^ ((lane >> 4) & 3)));
     const int ccol = lane & 31;
     const int cread0 = ccol * 64 + 16 * ((2 * half) ^ ((ccol >> 2) & 3));
@@ -190,8 +195,8 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
         else return xs1;
     };
     auto cstage = [&](auto ic) -> uint8_t* {
-        if constexpr (decltype(ic)::value == 0) return cs0 + wave * 2048;
-        else return cs1 + wave * 2048;
+        if constexpr (decltype(ic)::value == 0) return cs0 + wn * 2048;
+        else return cs1 + wn * 2048;
     };
     auto issue = [&](int j, auto ic, Slot& o) {
         const bool live = j >= 0 && j < groups;
@@ -208,9 +213,15 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
         const __amdgpu_buffer_rsrc_t sr = live ? srsrc : none;
         uint8_t* cdst = cstage(ic);
         const uint32_t cg = static_cast<uint32_t>(g) * 64u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst, 16, cvoff, cg, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst + 1024, 16, cvoff + 16u * static_cast<uint32_t>(row_bytes),
-                                                 cg, 0, 0);
+        if constexpr (KS == 1) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst, 16, cvoff, cg, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst + 1024, 16, cvoff + 16u * static_cast<uint32_t>(row_bytes),
+                                                     cg, 0, 0);
+        } else {   // the two waves of a column block load one half of its columns each
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, cdst + __builtin_amdgcn_readfirstlane(kh * 1024), 16,
+                                                     cvoff + 16u * static_cast<uint32_t>(kh) * static_cast<uint32_t>(row_bytes),
+                                                     cg, 0, 0);
+        }
         asm volatile("" ::: "memory");
         o.s = __builtin_amdgcn_raw_buffer_load_b16(sr, svoff, g * 2, 0);
         asm volatile("" ::: "memory");
@@ -220,7 +231,8 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
     // r = lane % 32, chunk 4 * half + t at slot (4 * half + t) ^ ((r >> 1) & 7).
     const int arow = lane & 31;
     const int asw = (arow >> 1) & 7;
-    auto a_off = [&](int t) { return arow * kGroup + ((((half << 2) | t) ^ asw) << 4); };
+    // (KS = 2: this wave's sub-step tt is t = 2 kh + tt)
+    auto a_off = [&](int tt) { return arow * kGroup + ((((half << 2) | (TSUB * kh + tt)) ^ asw) << 4); };
 
     f32x16_t acc[RB];
     i32x16_t P0[RB], P1[RB];
@@ -240,8 +252,14 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
         const int8_t* xt = stage(ic);
         // this lane's eight code words (words 8 half .. 8 half + 7 of its column's group)
         const uint8_t* cb = cstage(ic);
-        const u32x4_t ow[2] = {*reinterpret_cast<const u32x4_t*>(cb + cread0),
-                               *reinterpret_cast<const u32x4_t*>(cb + cread1)};
+        u32x4_t ow[2];
+        if constexpr (KS == 1) {
+            ow[0] = *reinterpret_cast<const u32x4_t*>(cb + cread0);
+            ow[1] = *reinterpret_cast<const u32x4_t*>(cb + cread1);
+        } else {   // sub-steps 2 kh, 2 kh + 1 use chunk kh
+            ow[0] = *reinterpret_cast<const u32x4_t*>(cb + (kh ? cread1 : cread0));
+            ow[1] = ow[0];
+        }
         i32x4_t a[2][RB];
         i32x4_t bq[2];
         auto codes = [&](int t) {
@@ -255,9 +273,9 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
         bq[0] = codes(0);
         const float sp = s_last;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < TSUB; ++t) {
             const int cur = t & 1, nxt = cur ^ 1;
-            if (t < 3) {
+            if (t < TSUB - 1) {
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
                     a[nxt][rb] = *reinterpret_cast<const i32x4_t*>(xt + a_off(t + 1) + rb * 32 * kGroup);
@@ -272,7 +290,7 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int r = 4 * t; r < 4 * t + 4; ++r)
+                for (int r = 4 * KS * t; r < 4 * KS * (t + 1); ++r)
                     acc[rb][r] = __builtin_fmaf(sp, static_cast<float>(Pp[rb][r]), acc[rb][r]);
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
@@ -322,9 +340,10 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[rb][r] = __builtin_fmaf(s_last, static_cast<float>(P0[rb][r]), acc[rb][r]);
 
-    // Bias term, once per output (slice 0): acc += xsum . baug^T over KB / 16 bf16 sub-steps,
-    // with baug[n, k'] = b[n, k' / 2] (zero for k' / 2 >= G) against xsum's hi / lo halves.
-    if (z == 0) {
+    // Bias term, once per output (slice 0, K half 0): acc += xsum . baug^T over KB / 16 bf16
+    // sub-steps, with baug[n, k'] = b[n, k' / 2] (zero for k' / 2 >= G) against xsum's hi / lo
+    // halves.
+    if (z == 0 && kh == 0) {
         const __amdgpu_buffer_rsrc_t xsr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(xsum + static_cast<size_t>(m0) * KB), 0,
             clamp_records(static_cast<int64_t>(M - m0) * KB * 2), 0x00020000);
@@ -353,6 +372,41 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
         }
     }
 
+    // KS = 2: the two waves of a column block add their partial sums; K half 0 finishes the
+    // elements e = 16 rb + r < 8 RB, K half 1 the rest.  Each writes the elements it hands over to
+    // the activation and code stages of its own K half (first and second half of them) and reads
+    // its partner's.
+    if constexpr (KS == 2) {
+        __syncthreads();   // every wave is done with the stages
+        constexpr int HALF = RB * 8;
+        constexpr int CH = HALF / 2;
+        static_assert(WN * CH * 64 * 4 <= TILE && WN * CH * 64 * 4 <= WN * 2048, "partial sums fit the stages");
+        float* mine0 = reinterpret_cast<float*>(kh == 0 ? xs0 : xs1) + wn * CH * 64;
+        float* mine1 = reinterpret_cast<float*>(kh == 0 ? cs0 : cs1) + wn * CH * 64;
+        const float* theirs0 = reinterpret_cast<const float*>(kh == 0 ? xs1 : xs0) + wn * CH * 64;
+        const float* theirs1 = reinterpret_cast<const float*>(kh == 0 ? cs1 : cs0) + wn * CH * 64;
+        // element indices stay compile-time constants (a runtime index would move acc to scratch)
+        auto exchange = [&](auto khc) {
+            constexpr int KH = decltype(khc)::value;
+            constexpr int give = KH == 0 ? HALF : 0, keep = KH == 0 ? 0 : HALF;
+#pragma unroll
+            for (int e = 0; e < HALF; ++e) {
+                float* dst = e < CH ? mine0 : mine1;
+                dst[(e % CH) * 64 + lane] = acc[(e + give) >> 4][(e + give) & 15];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < HALF; ++e) {
+                const float* src = e < CH ? theirs0 : theirs1;
+                acc[(e + keep) >> 4][(e + keep) & 15] += src[(e % CH) * 64 + lane];
+            }
+        };
+        if (kh == 0)
+            exchange(std::integral_constant<int, 0>{});
+        else
+            exchange(std::integral_constant<int, 1>{});
+    }
+
     // epilogue: y = sx[m] * acc; D layout puts rows 8 (r / 4) + 4 half + r % 4 of column
     // lane % 32 in this lane
     const int n = n0 + col;
@@ -360,6 +414,9 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+            if constexpr (KS == 2) {
+                if ((16 * rb + r < RB * 8) != (kh == 0)) continue;
+            }
             const int m = m0 + rb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
             if (m >= M || n >= N) continue;
             const float v = sx[m] * acc[rb][r];
@@ -376,6 +433,7 @@ const QmmShape kW4A8Variants[kNumW4A8Variants] = {
     {32, 1, 4, 2},    // 0:  32 x 128 tile, four waves per SIMD
     {64, 1, 4, 2},    // 1:  64 x 128 tile, three waves per SIMD
     {128, 1, 4, 2},   // 2: 128 x 128 tile, two waves per SIMD
+    {64, 1, 8, 2, 2},  // 3:  64 x 128 tile, 8 waves: two per column block splitting each group
 };
 
 hipError_t launch_quantize_rows_int8(const uint16_t* x, int8_t* xq, float* sx, uint16_t* xsum, int M, int K, int KB,
@@ -384,14 +442,14 @@ hipError_t launch_quantize_rows_int8(const uint16_t* x, int8_t* xq, float* sx, u
     return hipGetLastError();
 }
 
-template <int BM, int WPS>
+template <int BM, int WPS, int KS = 1>
 static hipError_t launch_w4a8_t(const int8_t* xq, const float* sx, const uint16_t* xsum, const uint32_t* wq,
                                 const uint16_t* s, const uint16_t* b, uint16_t* y, float* ws, int M, int N, int K,
                                 int KB, int split, hipStream_t stream) {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + 127) / 128;
-    hipLaunchKernelGGL((qmm_w4a8_kernel<BM, WPS>), dim3(tiles_m * tiles_n * split), dim3(256), 0, stream, xq, sx,
-                       xsum, wq, s, b, y, ws, M, N, K, KB, split, tiles_m, tiles_n);
+    hipLaunchKernelGGL((qmm_w4a8_kernel<BM, WPS, KS>), dim3(tiles_m * tiles_n * split), dim3(256 * KS), 0, stream,
+                       xq, sx, xsum, wq, s, b, y, ws, M, N, K, KB, split, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
@@ -402,6 +460,7 @@ hipError_t launch_qmm_w4a8(int variant, const int8_t* xq, const float* sx, const
         case 0: return launch_w4a8_t<32, 4>(xq, sx, xsum, wq, scales, biases, y, ws, M, N, K, KB, split, stream);
         case 1: return launch_w4a8_t<64, 3>(xq, sx, xsum, wq, scales, biases, y, ws, M, N, K, KB, split, stream);
         case 2: return launch_w4a8_t<128, 2>(xq, sx, xsum, wq, scales, biases, y, ws, M, N, K, KB, split, stream);
+        case 3: return launch_w4a8_t<64, 4, 2>(xq, sx, xsum, wq, scales, biases, y, ws, M, N, K, KB, split, stream);
         default: return hipErrorInvalidValue;
     }
 }
