@@ -45,10 +45,14 @@ Readings where the pages are silent (each one is also listed in the design doc):
   gets ``q = 0``.
 * R8 other bit widths ("Route affine qmv_wide by bit-width and batch size #5"
   routes affine matvecs by bit width, naming 1- and 2-bit weights; the page
-  gives no format): for ``bits`` in {1, 2, 4, 8} a 32-bit word holds
-  ``32 / bits`` codes, element ``(32/bits)*j + i`` of a row in bits
-  ``bits*i .. bits*i + bits - 1`` of word ``j`` (low first, as R1), ``Wq`` is
-  ``uint32 [N, K*bits/32]``, and the group, scale, bias and R4-R7 are
+  gives no format): for ``bits`` in {1, 2, 3, 4, 8} the words of a row form one
+  bit stream, lowest bits first (stream bit ``t`` is bit ``t % 32`` of word
+  ``t // 32``), and element ``k`` of the row is stream bits
+  ``bits*k .. bits*k + bits - 1``; ``Wq`` is ``uint32 [N, K*bits/32]``.  At 1,
+  2, 4 and 8 bits no code crosses a word, so element ``(32/bits)*j + i`` sits
+  in bits ``bits*i .. bits*i + bits - 1`` of word ``j`` (R1 at 4 bits); at 3
+  bits every 32 codes fill three words and two of them (elements 10 and 21 of
+  the run) straddle a word boundary.  The group, scale, bias and R4-R7 are
   unchanged with ``2**bits - 1`` in place of 15.  ``s * q`` stays exact in
   fp32 (at most 8 + 8 significand bits).
 * R9 int8 activations (W4A8; "Feature Request: Metal prefill speedup (~68%)
@@ -96,7 +100,7 @@ __all__ = [
 ]
 
 GROUP = 128
-BITS = (1, 2, 4, 8)          # code widths of reading R8 (4 is the W4 format of R1)
+BITS = (1, 2, 3, 4, 8)       # code widths of reading R8 (4 is the W4 format of R1)
 TOL_REL = 2.0 ** -8
 TOL_MASS = 2.0 ** -10
 
@@ -155,24 +159,36 @@ def f32_to_bf16_rne(values) -> np.ndarray:
 # --------------------------------------------------------------------------- format
 
 
-def _codes_per_word(bits: int) -> int:
+def _stream_period(bits: int) -> tuple[int, int]:
+    """(codes, words) of the shortest run of whole words that holds whole codes: (32/bits, 1)
+    when bits divides 32, (32, 3) at 3 bits (reading R8)."""
     if bits not in BITS:
         raise ValueError(f"bits={bits} is not one of {BITS}")
-    return 32 // bits
+    codes = 32 // math.gcd(32, bits)
+    return codes, codes * bits // 32
 
 
 def unpack_q(wq, K: int, bits: int = 4) -> np.ndarray:
-    """Packed words ``uint32 [N, K*bits/32]`` -> codes ``uint8 [N, K]`` (readings R1, R2, R8)."""
-    per = _codes_per_word(bits)
+    """Packed words ``uint32 [N, K*bits/32]`` -> codes ``uint8 [N, K]`` (readings R1, R2, R8).
+
+    Element ``k`` of a row is stream bits ``bits*k ..``: bits ``sh ..`` of word ``j`` and, when
+    it crosses the word, the low bits of word ``j + 1``, with ``j, sh = divmod(bits*k, 32)``.
+    """
+    per, wpp = _stream_period(bits)
     w = np.asarray(wq, dtype=np.uint32)
     n_rows, n_words = w.shape
-    if n_words * per != K:
-        raise ValueError(f"Wq has {n_words} words per row; K={K} at {bits} bits needs {K // per}")
+    if n_words * 32 != K * bits:
+        raise ValueError(f"Wq has {n_words} words per row; K={K} at {bits} bits needs {K * bits // 32}")
+    # each word next to its successor as one 64-bit window (a zero word after the last)
+    w64 = np.concatenate([w, np.zeros((n_rows, 1), dtype=np.uint32)], axis=1).astype(np.uint64)
+    mask = np.uint64((1 << bits) - 1)
     q = np.empty((n_rows, K), dtype=np.uint8)
-    mask = np.uint32((1 << bits) - 1)
     for i in range(per):
-        # element per*j + i of every row comes from bits bits*i .. bits*i + bits - 1 of word j
-        q[:, i::per] = (w >> np.uint32(bits * i)) & mask
+        # element per*r + i of every row, for every run r of wpp words
+        j, sh = divmod(bits * i, 32)
+        lo = w64[:, j:n_words:wpp]
+        hi = w64[:, j + 1:n_words + 1:wpp]
+        q[:, i::per] = ((lo | (hi << np.uint64(32))) >> np.uint64(sh)) & mask
     return q
 
 
@@ -269,19 +285,22 @@ def check(y_bits, y_ref, A, rel: float = TOL_REL, mass: float = TOL_MASS) -> Che
 
 
 def pack_q(q, bits: int = 4) -> np.ndarray:
-    """Codes ``[N, K]`` (0 .. 2**bits - 1) -> words ``uint32 [N, K*bits/32]``: word j holds
-    element per*j + i at bits bits*i, per = 32 / bits (R1, R8)."""
-    per = _codes_per_word(bits)
-    q = np.asarray(q, dtype=np.uint32)
+    """Codes ``[N, K]`` (0 .. 2**bits - 1) -> words ``uint32 [N, K*bits/32]``: element k at stream
+    bits bits*k .., lowest bits first (R1, R8)."""
+    per, wpp = _stream_period(bits)
+    q = np.asarray(q, dtype=np.uint64)
     n_rows, K = q.shape
-    mask = np.uint32((1 << bits) - 1)
-    words = np.zeros((n_rows, K // per), dtype=np.uint32)
-    for j in range(K // per):
-        acc = np.zeros(n_rows, dtype=np.uint32)
-        for i in range(per):
-            acc |= (q[:, per * j + i] & mask) << np.uint32(bits * i)
-        words[:, j] = acc
-    return words
+    if K % per:
+        raise ValueError(f"K={K} is not a multiple of {per} at {bits} bits")
+    n_words = K * bits // 32
+    mask = np.uint64((1 << bits) - 1)
+    words = np.zeros((n_rows, n_words + 1), dtype=np.uint64)   # one spare word for the carry
+    for i in range(per):
+        j, sh = divmod(bits * i, 32)
+        v = (q[:, i::per] & mask) << np.uint64(sh)
+        words[:, j:n_words:wpp] |= v & np.uint64(0xFFFFFFFF)
+        words[:, j + 1:n_words + 1:wpp] |= v >> np.uint64(32)
+    return words[:, :n_words].astype(np.uint32)
 
 
 def quantize_w4g128(W, group: int = GROUP):
@@ -297,7 +316,7 @@ def quantize_affine(W, bits: int = 4, group: int = GROUP):
 
     Returns ``(wq uint32 [N, K*bits/32], scales bf16-bits [N, G], biases bf16-bits [N, G])``.
     """
-    _codes_per_word(bits)
+    _stream_period(bits)
     W = np.asarray(W, dtype=np.float32)
     n_rows, K = W.shape
     if K % group:

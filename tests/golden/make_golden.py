@@ -10,9 +10,11 @@ exactly representable in bf16, and every ``s*q + b`` is exact in fp32, so the
 fp32 dequantization rounds nothing and the fp64 reference must equal the
 rational result to within its final rounding.
 
-It also writes ``worked_example_w{1,2,8}g128.json``: the same construction at the other
-code widths (element ``(32/b)j + i`` of a row in bits ``b*i .. b*i + b - 1`` of word ``j``,
-codes in ``0 .. 2**b - 1``), again from exact rationals only.
+It also writes ``worked_example_w{1,2,3,8}g128.json``: the same construction at the other
+code widths (a row's codes as one bit stream, lowest bits first: element ``k`` in stream bits
+``b*k .. b*k + b - 1``, stream bit ``t`` in bit ``t % 32`` of word ``t // 32``; codes in
+``0 .. 2**b - 1``), again from exact rationals only.  At 1, 2, 4 and 8 bits that is element
+``(32/b)j + i`` in bits ``b*i ..`` of word ``j``.
 
 Run: ``python tests/golden/make_golden.py`` (rewrites the JSON files next to it).
 """
@@ -33,11 +35,12 @@ def bf16_bits(v: Fraction) -> int:
 
 
 def write(bits):
-    per = 32 // bits
     levels = 1 << bits
     # codes: a closed form that varies with n and k and spans 0 .. 2**bits - 1
     q = [[(3 * n + 5 * k + (k // 128)) % levels for k in range(K)] for n in range(N)]
-    words = [[sum(q[n][per * j + i] << (bits * i) for i in range(per)) for j in range(K // per)] for n in range(N)]
+    # each row as one integer bit stream, cut into 32-bit words
+    streams = [sum(q[n][k] << (bits * k) for k in range(K)) for n in range(N)]
+    words = [[(streams[n] >> (32 * j)) & 0xFFFFFFFF for j in range(K * bits // 32)] for n in range(N)]
     s = [[Fraction(1, 2 ** (4 + n + g)) for g in range(K // GROUP)] for n in range(N)]
     b = [[Fraction(-(n + 1) * (g + 3), 2 ** 5) for g in range(K // GROUP)] for n in range(N)]
     # activations: small dyadic values with a pattern per row
@@ -55,7 +58,7 @@ def write(bits):
         citation = (f"No page prints a worked example. Closed-form values computed with exact "
                     f"rationals for {bits}-bit affine codes ('Route affine qmv_wide by bit-width and "
                     f"batch size #5' routes 1- and 2-bit affine matvecs) under the oracle's reading R8 "
-                    f"({per} codes per word, lowest bits first) and R3-R4.")
+                    f"(a row's codes as one bit stream, lowest bits first) and R3-R4.")
     out = {
         "citation": citation,
         "M": M, "K": K, "N": N, "group": GROUP, "bits": bits,
@@ -75,7 +78,7 @@ def write(bits):
 
 
 def main():
-    for bits in (4, 1, 2, 8):
+    for bits in (4, 1, 2, 3, 8):
         write(bits)
 
 

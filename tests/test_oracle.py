@@ -490,7 +490,7 @@ def _oracle_bits(x, wq, s, b, bits):
     return O.reference(x, wq, s, b, bits=bits)
 
 
-@pytest.mark.parametrize("bits", [1, 2, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 8])
 @pytest.mark.parametrize("pin", BITS_PINS, ids=lambda p: p.__name__)
 def test_oracle_passes_bits_pin(pin, bits):
     assert pin(_oracle_bits, bits)
@@ -508,10 +508,29 @@ def test_unpack_literal_words_other_widths():
     # 4-bit keeps reading R1
     assert O.unpack_q(np.array([[0x76543210]], dtype=np.uint32), 8).tolist() == [[0, 1, 2, 3, 4, 5, 6, 7]]
     with pytest.raises(ValueError):
+        O.unpack_q(np.zeros((1, 5), dtype=np.uint32), 32, bits=5)
+
+
+def test_unpack_literal_words_three_bits():
+    # eight 3-bit codes fill 24 stream bits and read as the octal digits right to left:
+    # 1, 2, ..., 7, 0 is 0o07654321 = 0x1F58D1; four such runs fill three words
+    w = np.array([[0xD11F58D1, 0x58D11F58, 0x1F58D11F]], dtype=np.uint32)
+    assert O.unpack_q(w, 32, bits=3).tolist() == [[1, 2, 3, 4, 5, 6, 7, 0] * 4]
+    # the codes that straddle a word: element 10 is bits 30, 31 of word 0 and bit 0 of word 1,
+    # element 21 is bit 31 of word 1 and bits 0, 1 of word 2
+    q = O.unpack_q(np.array([[0xC0000000, 0x00000001, 0x0]], dtype=np.uint32), 32, bits=3)[0]
+    assert q.tolist() == [0] * 10 + [7] + [0] * 21
+    q = O.unpack_q(np.array([[0x0, 0x80000000, 0x00000002]], dtype=np.uint32), 32, bits=3)[0]
+    assert q.tolist() == [0] * 21 + [5] + [0] * 10
+    # runs meet at a word boundary: bit 31 of word 2 is the top bit of element 31, bits 0, 1 of
+    # word 3 the low bits of element 32
+    q = O.unpack_q(np.array([[0, 0, 0x80000000, 0x00000003, 0, 0]], dtype=np.uint32), 64, bits=3)[0]
+    assert q.tolist() == [0] * 31 + [4, 3] + [0] * 31
+    with pytest.raises(ValueError):
         O.unpack_q(np.zeros((1, 4), dtype=np.uint32), 32, bits=3)
 
 
-@pytest.mark.parametrize("bits", [1, 2, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 8])
 def test_pack_and_unpack_are_inverse_and_match_the_input_generator(bits):
     rng = np.random.default_rng(60 + bits)
     q = rng.integers(0, 1 << bits, (7, 256))

@@ -89,18 +89,25 @@ def from_bf16_bits(bits) -> np.ndarray:
 
 
 def pack_codes(q, bits: int = 4) -> np.ndarray:
-    """Codes ``[N, K]`` in 0 .. 2**bits - 1 -> ``uint32 [N, K*bits/32]``, lowest bits first
-    (``bits`` in 1, 2, 4, 8)."""
-    if bits not in (1, 2, 4, 8):
-        raise ValueError(f"bits={bits} is not one of 1, 2, 4, 8")
-    per = 32 // bits
+    """Codes ``[N, K]`` in 0 .. 2**bits - 1 -> ``uint32 [N, K*bits/32]``: a row's codes as one bit
+    stream, lowest bits first (``bits`` in 1, 2, 3, 4, 8; at 1, 2, 4 and 8 no code crosses a
+    word)."""
+    if bits not in (1, 2, 3, 4, 8):
+        raise ValueError(f"bits={bits} is not one of 1, 2, 3, 4, 8")
     q = np.asarray(q, dtype=np.uint32)
     n_rows, K = q.shape
-    if K % per:
-        raise ValueError(f"K must be a multiple of {per}")
-    qw = q.reshape(n_rows, K // per, per)
-    shifts = (np.arange(per, dtype=np.uint32) * np.uint32(bits))[None, None, :]
-    return np.bitwise_or.reduce(qw << shifts, axis=2).astype(np.uint32)
+    if (K * bits) % 32:
+        raise ValueError(f"K * bits must be a multiple of 32")
+    if 32 % bits == 0:
+        per = 32 // bits
+        qw = q.reshape(n_rows, K // per, per)
+        shifts = (np.arange(per, dtype=np.uint32) * np.uint32(bits))[None, None, :]
+        return np.bitwise_or.reduce(qw << shifts, axis=2).astype(np.uint32)
+    # codes that may cross words: spell out the stream bit by bit, then gather 32 bits per word
+    stream = ((q[:, :, None] >> np.arange(bits, dtype=np.uint32)[None, None, :]) & 1).astype(np.uint32)
+    stream = stream.reshape(n_rows, K * bits // 32, 32)
+    weights = (np.uint32(1) << np.arange(32, dtype=np.uint32))[None, None, :]
+    return (stream * weights).sum(axis=2, dtype=np.uint64).astype(np.uint32)
 
 
 def quantize(W, group: int = GROUP, bits: int = 4):
@@ -162,7 +169,7 @@ def problem(cfg: int, shape_name: str, M: int | None = None):
 
 def random_problem(seed: int, M: int, N: int, K: int, group: int = GROUP, bits: int = 4):
     """Inputs of an arbitrary shape from the same recipe, for tests (stream ``[0, seed, role, chunk]``);
-    ``bits`` per code (1, 2, 4, 8)."""
+    ``bits`` per code (1, 2, 3, 4, 8)."""
     wq = np.empty((N, K * bits // 32), dtype=np.uint32)
     s = np.empty((N, K // group), dtype=np.uint16)
     b = np.empty((N, K // group), dtype=np.uint16)
