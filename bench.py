@@ -325,7 +325,7 @@ def next_rows(torch, w4, projections, copies, reps=20):
       * W4A8 (int8 activations) against W4A16 on the step's seven projections;
       * the 4096-row prefill of gate / up / down and the vocabulary head over all rows;
       * decode rows (M = 1, 4) on the four decode shapes, and the width-generic matvec at
-        1, 2, 4 and 8 bits."""
+        1, 2, 3, 4 and 8 bits."""
     from w4a16_group_quantized_qmv_amd import synth
     by = {p["name"]: p for p in projections}
     dev = by["gate"]["x"].device
@@ -442,7 +442,7 @@ def next_rows(torch, w4, projections, copies, reps=20):
     # width-generic matvec on the 2560 -> 9728 shape
     bits_rows = []
     K, N = synth.DECODE_SHAPES[0]
-    for bits in (1, 2, 4, 8):
+    for bits in (1, 2, 3, 4, 8):
         pr = synth.random_problem(40 + bits, 4, N, K, bits=bits)
         w0 = (torch.from_numpy(pr["wq"].view("int32")).to(dev),
               torch.from_numpy(pr["scales"].view("int16")).view(torch.bfloat16).to(dev),

@@ -198,14 +198,16 @@ enum w4a16_qmv_mode {
 };
 
 /*
- * Affine matvec for decode rows (1 <= M <= 8) at bits = 1, 2, 4 or 8 per code, routed by
+ * Affine matvec for decode rows (1 <= M <= 8) at bits = 1, 2, 3, 4 or 8 per code, routed by
  * (bits, M) between a per-row kernel and a row-amortized one ("Route affine qmv_wide by
  * bit-width and batch size #5" routes 1-bit and small M per row and larger M row-amortized).
  * Measured on MI355X the row-amortized kernel leads at every width and M, so the policy takes
  * it, and at bits = 4 the policy is qmv_w4a16's.  Layouts as above with wq uint32 [N, K * bits / 32]:
- * element (32/bits)*j + i of a row in bits bits*i .. bits*i + bits - 1 of word j (lowest bits
- * first); scales and biases bf16 [N, K/128]; w = s * q + b.  mode: enum w4a16_qmv_mode.  Needs no
- * workspace.  Same preconditions, ownership and errors as qmv_w4a16; bits outside {1, 2, 4, 8},
+ * a row's words are one bit stream, lowest bits first (stream bit t = bit t % 32 of word t / 32),
+ * element k in stream bits bits*k .. bits*k + bits - 1 -- at 1, 2, 4 and 8 bits element
+ * (32/bits)*j + i in bits bits*i .. of word j, at 3 bits codes 10 and 21 of every 32 straddle a
+ * word; scales and biases bf16 [N, K/128]; w = s * q + b.  mode: enum w4a16_qmv_mode.  Needs no
+ * workspace.  Same preconditions, ownership and errors as qmv_w4a16; bits outside {1, 2, 3, 4, 8},
  * M > 8, an unknown mode, the per-row mode with M > 2, or W4A16_QMV_FAMILIES with bits != 4 return
  * W4A16_ERR_UNSUPPORTED.
  */

@@ -261,7 +261,7 @@ def test_qmv_affine_plans():
 
 
 @pytest.mark.parametrize("args", [
-    (1, 16, 256, 3, 0), (1, 16, 256, 16, 0), (1, 16, 256, 0, 0),   # widths outside {1, 2, 4, 8}
+    (1, 16, 256, 5, 0), (1, 16, 256, 16, 0), (1, 16, 256, 0, 0),   # widths outside {1, 2, 3, 4, 8}
     (9, 16, 256, 4, 0),                                            # more than eight rows
     (3, 16, 256, 4, w4.QMV_PER_ROW),                               # per-row kernel: M <= 2
     (1, 16, 256, 2, w4.QMV_FAMILIES),                              # the 4-bit families: bits = 4

@@ -1,4 +1,4 @@
-"""GPU parity of the width-generic affine matvec (``qmv_affine``: 1, 2, 4 and 8 bits per code,
+"""GPU parity of the width-generic affine matvec (``qmv_affine``: 1, 2, 3, 4 and 8 bits per code,
 M <= 8) against the oracle, through the C ABI.
 
 Both kernels (row-amortized and per-row) and the policy are checked at every width on ragged
@@ -20,7 +20,7 @@ from gpu_helpers import announce, bits as to_bits, to_device
 
 pytestmark = pytest.mark.gpu
 
-WIDTHS = (1, 2, 4, 8)
+WIDTHS = (1, 2, 3, 4, 8)
 MODES = {"policy": 0, "amortized": 1, "per_row": 2}
 
 

@@ -12,7 +12,8 @@ Tensor conventions (all on the GPU, contiguous):
     biases   torch.bfloat16 [N, K/128]
     y        torch.bfloat16 [M, N]
 
-``qmv_affine`` takes codes of 1, 2, 4 or 8 bits: ``wq`` int32 [N, K*bits/32], lowest bits first.
+``qmv_affine`` takes codes of 1, 2, 3, 4 or 8 bits: ``wq`` int32 [N, K*bits/32], a row's words one
+bit stream, lowest bits first.
 
 ``linear(..., logits_to_keep=k)`` is the model-level entry: it projects only the last ``k``
 rows (a view, no copy) before the projection, as tiny-llm's "Week 2 Day 6: SIMD-Matrix
@@ -39,7 +40,7 @@ GROUP = 128
 W4A16_OK = 0
 PATH_AUTO, PATH_QMV, PATH_QMM, PATH_SKINNY, PATH_GATE_UP, PATH_W4A8 = 0, 1, 2, 3, 4, 5
 QMV_POLICY, QMV_AMORTIZED, QMV_PER_ROW, QMV_FAMILIES = 0, 1, 2, 3
-BITS = (1, 2, 4, 8)
+BITS = (1, 2, 3, 4, 8)
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _HEADER = os.path.join(os.path.dirname(_PKG_DIR), "include", "w4a16.h")
@@ -254,7 +255,7 @@ def qmv_w4a16(x, wq, scales, biases, y=None, stream=None):
 
 
 def qmv_affine(x, wq, scales, biases, bits: int, y=None, mode: int = QMV_POLICY, stream=None):
-    """Decode-row matvec (1 <= M <= 8) over ``bits``-bit affine codes (1, 2, 4 or 8; ``wq`` int32
+    """Decode-row matvec (1 <= M <= 8) over ``bits``-bit affine codes (1, 2, 3, 4 or 8; ``wq`` int32
     ``[N, K * bits / 32]``, lowest bits first), routed by (bits, M) unless ``mode`` forces the
     row-amortized or the per-row kernel.  Returns y."""
     if bits not in BITS:

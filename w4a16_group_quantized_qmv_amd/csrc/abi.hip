@@ -389,12 +389,12 @@ int run_gate_up(const uint16_t* x, const uint32_t* wq_g, const uint16_t* s_g, co
     return to_status(launch_splitk_reduce_glu(ws, h, M * N, p.split_k, s));
 }
 
-// Width-generic matvec: bits in {1, 2, 4, 8}, M <= 8.  Routing by (bits, M), measured on
+// Width-generic matvec: bits in {1, 2, 3, 4, 8}, M <= 8.  Routing by (bits, M), measured on
 // MI355X (K = 2560 .. 9728, N = 1024 .. 151936, M = 1 .. 8, random data): the row-amortized
 // kernel is never more than 7% behind the per-row one and up to 35% ahead of it (the 151936-
 // column head), at every width and row count, so the policy takes it; at 4 bits the policy is
 // that of qmv_w4a16, whose kernel families include the same row-amortized kernel.
-bool bits_ok(int32_t bits) { return bits == 1 || bits == 2 || bits == 4 || bits == 8; }
+bool bits_ok(int32_t bits) { return bits == 1 || bits == 2 || bits == 3 || bits == 4 || bits == 8; }
 
 int plan_qmv_affine(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, int32_t mode, int32_t num_cus,
                     w4a16_plan_t* p) {

@@ -104,7 +104,7 @@ hipError_t launch_gate_up(int variant, const uint16_t* x, const uint16_t* xsum, 
 // h[i] = bf16(silu(sum_z ws[0][z][i]) * sum_z ws[1][z][i]), slices summed in order.
 hipError_t launch_splitk_reduce_glu(const float* ws, uint16_t* h, int64_t MN, int split, hipStream_t stream);
 
-// Width-generic affine matvec (1, 2, 4 or 8 bits per code, M <= 8): row-amortized on the
+// Width-generic affine matvec (1, 2, 3, 4 or 8 bits per code, M <= 8): row-amortized on the
 // matrix core (mode kQmvBitsMatrix) or per row with dot products (kQmvBitsRows, M <= 2).
 constexpr int kQmvBitsMatrix = 0, kQmvBitsRows = 1;
 hipError_t launch_qmv_bits(int bits, int mode, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,

@@ -1,13 +1,15 @@
-// qmv_bits: affine matvec for decode rows (M <= 8) at 1, 2, 4 or 8 bits per code.
+// qmv_bits: affine matvec for decode rows (M <= 8) at 1, 2, 3, 4 or 8 bits per code.
 //
 // "Route affine qmv_wide by bit-width and batch size #5" routes affine quantized matvecs by
 // code width and row count between a per-row kernel and a row-amortized kernel that
 // dequantizes a group once and reuses it across the M rows.  Both exist here for every width,
 // sharing the load and unpack code; the dispatch policy picks one from measurements.
 //
-// Format (the width-generic reading of the W4 layout): at BITS bits a 32-bit word holds
-// 32 / BITS codes, element (32/BITS)*j + i of a column's row in bits BITS*i .. BITS*i + BITS - 1
-// of word j; one bf16 scale and bias per 128 reduction values; w = s * q + b.
+// Format (the width-generic reading of the W4 layout): a column's row of words is one bit
+// stream, lowest bits first, element k in stream bits BITS*k .. BITS*k + BITS - 1; at 1, 2, 4
+// and 8 bits that is element (32/BITS)*j + i in bits BITS*i .. of word j, at 3 bits every 32
+// codes fill three words and two of them straddle a word.  One bf16 scale and bias per 128
+// reduction values; w = s * q + b.
 //
 // Lane layout, per 128-value group of one 16-column block: lane l holds column c = l % 16 and
 // the 32 consecutive reduction values kq*32 .. kq*32 + 31 of the group, kq = l / 16 -- the B
@@ -16,6 +18,9 @@
 //   * 1, 2 and 4 bits: masked words hold one code per byte; a byte 0..15 read as an OCP e4m3
 //     value is q * 2^-9, so the scaled converter with scale 2^9 gives q exactly, two per
 //     instruction (the same identity the 4-bit kernels use);
+//   * 3 bits: each 24 stream bits (8 codes) are spread in two bit-field inserts to one pair
+//     of codes per byte (codes 2i, 2i + 1 in bits 0..2, 3..5 of byte i), then masked into
+//     one code per byte and converted as above;
 //   * 8 bits: v_cvt_f32_ubyte* then a bf16 pack (integers up to 255 are exact in bf16).
 // The unpack order is not the natural one (except at 8 bits), so the activations are put in the
 // same order with v_perm_b32 (CodeOrder below); any bijection of the reduction index works as
@@ -38,6 +43,7 @@ namespace w4a16 {
 namespace {
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
 
 // Reduction offset (0..31 within the lane's 32 values) of B-operand element 8t + e.
 template <int BITS>
@@ -51,6 +57,13 @@ struct CodeOrder<4> {   // per word t: [q0, q2, q1, q3, q4, q6, q5, q7]
     static constexpr int at(int i) {
         constexpr int w[8] = {0, 2, 1, 3, 4, 6, 5, 7};
         return 8 * (i / 8) + w[i % 8];
+    }
+};
+template <>
+struct CodeOrder<3> {   // operand t: codes 8t + [0, 2, 4, 6, 1, 3, 5, 7]
+    static constexpr int at(int i) {
+        const int e = i % 8;
+        return 8 * (i / 8) + 2 * (e % 4) + e / 4;
     }
 };
 template <>
@@ -89,6 +102,23 @@ __device__ __forceinline__ void codes_to_bf16(const uint32_t (&w)[BITS], u32x4_t
     } else if constexpr (BITS == 4) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) bop[t] = __builtin_bit_cast(u32x4_t, codes_bf16_permuted(w[t]));
+    } else if constexpr (BITS == 3) {
+        // operand t: stream bits 24t .. 24t + 23 (low 24 bits of the chunk; the rest is ignored)
+        const uint32_t chunk[4] = {w[0], __builtin_amdgcn_alignbit(w[1], w[0], 24),
+                                   __builtin_amdgcn_alignbit(w[2], w[1], 16), w[2] >> 8};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            uint32_t u = chunk[t];
+            // codes 4..7 to bits 16..27 (bits 12..15 and 28..31 are left over, never read)
+            u = (u & 0x00000FFFu) | ((u << 4) & ~0x00000FFFu);
+            // codes 2, 3 and 6, 7 to bytes 1 and 3: byte i holds codes 2i, 2i + 1 in bits 0..5
+            u = (u & 0x003F003Fu) | ((u << 2) & ~0x003F003Fu);
+            const uint32_t m0 = u & 0x07070707u, m1 = (u >> 3) & 0x07070707u;
+            bop[t][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m0, 512.0f, false));
+            bop[t][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m0, 512.0f, true));
+            bop[t][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m1, 512.0f, false));
+            bop[t][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(m1, 512.0f, true));
+        }
     } else {
         constexpr uint32_t mask = BITS == 2 ? 0x03030303u : 0x01010101u;
 #pragma unroll
@@ -145,6 +175,11 @@ __device__ __forceinline__ void load_codes(const __amdgpu_buffer_rsrc_t& r, uint
         const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
         w[0] = v[0];
         w[1] = v[1];
+    } else if constexpr (BITS == 3) {
+        const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+        w[0] = v[0];
+        w[1] = v[1];
+        w[2] = v[2];
     } else {
 #pragma unroll
         for (int h = 0; h < BITS / 4; ++h) {
@@ -327,7 +362,7 @@ static hipError_t launch_qmv_bits_t(const uint16_t* x, const uint32_t* wq, const
     return hipGetLastError();
 }
 
-// variant = 2 * width index (1, 2, 4, 8 bits -> 0..3) + mode; four waves split K
+// four waves split K
 hipError_t launch_qmv_bits(int bits, int mode, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
                            const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream) {
     const bool rows = mode == kQmvBitsRows;
@@ -336,6 +371,8 @@ hipError_t launch_qmv_bits(int bits, int mode, const uint16_t* x, const uint32_t
                             : launch_qmv_bits_t<1, 4, kMatrix>(x, wq, scales, biases, y, M, N, K, stream);
         case 2: return rows ? launch_qmv_bits_t<2, 4, kRows>(x, wq, scales, biases, y, M, N, K, stream)
                             : launch_qmv_bits_t<2, 4, kMatrix>(x, wq, scales, biases, y, M, N, K, stream);
+        case 3: return rows ? launch_qmv_bits_t<3, 4, kRows>(x, wq, scales, biases, y, M, N, K, stream)
+                            : launch_qmv_bits_t<3, 4, kMatrix>(x, wq, scales, biases, y, M, N, K, stream);
         case 4: return rows ? launch_qmv_bits_t<4, 4, kRows>(x, wq, scales, biases, y, M, N, K, stream)
                             : launch_qmv_bits_t<4, 4, kMatrix>(x, wq, scales, biases, y, M, N, K, stream);
         case 8: return rows ? launch_qmv_bits_t<8, 4, kRows>(x, wq, scales, biases, y, M, N, K, stream)
