@@ -392,6 +392,72 @@ def test_repeated_runs_are_bit_identical(lib):
         assert np.array_equal(first, run(lib, q, "qmv", dev=devq))
 
 
+# ---------------------------------------------------------------------------------- split-K workspace reuse
+# A split launch writes every fp32 partial it later sums, so the workspace's earlier contents do
+# not matter, and a captured split call replays like an eager one (no memset in the path).
+
+def split_call(lib, p, split, ws, dev):
+    import torch
+    x, wq, s, b = dev
+    y = torch.empty((p["M"], p["N"]), dtype=torch.bfloat16, device=x.device)
+    lib.qmm_w4a16(x, wq, s, b, y=y, split_k=split, workspace=ws)
+    return y
+
+
+def test_split_ignores_stale_workspace_and_reuses_it(lib):
+    import torch
+    M, N, K, split = 100, 700, 4096, 5
+    p = synth.random_problem(31, M, N, K)
+    dev = to_device(p)
+    plan = lib.w4a16_plan(M, N, K, path=lib.PATH_QMM, split_k=split)
+    assert plan["split_k"] == split
+    nbytes = plan["workspace_bytes"]
+    announce(f"split workspace reuse M={M} N={N} K={K} split={split} workspace={nbytes}")
+    zeroed = torch.zeros(nbytes // 4 + 1, dtype=torch.int32, device="cuda:0")
+    y0 = bits(split_call(lib, p, split, zeroed, dev))
+    torch.cuda.synchronize()
+    assert_parity(y0, p)
+    # arbitrary bytes everywhere (seeded; as a fresh allocation may hold), then the same
+    # workspace call after call, and another split of the same shape on it
+    noise = torch.from_numpy(np.random.default_rng(7).integers(-2 ** 31, 2 ** 31, nbytes // 4 + 1,
+                                                               dtype=np.int64).astype(np.int32)).to("cuda:0")
+    for _ in range(4):
+        assert np.array_equal(bits(split_call(lib, p, split, noise, dev)), y0)
+    assert_parity(bits(split_call(lib, p, 3, noise, dev)), p)
+
+
+def test_split_call_in_a_graph_replays(lib):
+    """A captured split call (tile kernel, then the slice reduction) replays like the eager call;
+    replays alternate with eager calls on the same workspace."""
+    import torch
+    M, N, K, split = 64, 1000, 2560, 4
+    p = synth.random_problem(32, M, N, K)
+    x, wq, s, b = to_device(p)
+    plan = lib.w4a16_plan(M, N, K, path=lib.PATH_QMM, split_k=split)
+    ws = torch.zeros(plan["workspace_bytes"] // 4 + 1, dtype=torch.int32, device="cuda:0")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    announce(f"split graph replay M={M} N={N} K={K} split={split}")
+    lib.qmm_w4a16(x, wq, s, b, y=y, split_k=split, workspace=ws)
+    torch.cuda.synchronize()
+    ref = bits(y)
+    assert_parity(ref, p)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            lib.qmm_w4a16(x, wq, s, b, y=y, split_k=split, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(y), ref), f"replay {i}"
+        y2 = torch.empty_like(y)
+        lib.qmm_w4a16(x, wq, s, b, y=y2, split_k=split, workspace=ws)     # eager, same workspace
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(y2), ref), f"eager call after replay {i}"
+
+
 # ---------------------------------------------------------------------------------- error paths on the device
 
 def test_forced_split_without_workspace_is_rejected(lib):
