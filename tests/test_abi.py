@@ -107,9 +107,26 @@ def test_k_split_waves_for_small_grids():
     assert (q["tile_m"], q["tile_n"], q["k_waves"], q["block_threads"]) == (64, 128, 2, 512)
     k = plan(512, 1024, 2560)                      # 64 tiles x 4 slices
     assert k["k_waves"] == 2 and k["grid_x"] * k["grid_y"] * k["split_k"] <= CUS
-    for M, N, K in [(512, 9728, 2560), (512, 2560, 4096), (2048, 9728, 2560), (32, 9728, 2560)]:
+    for M, N, K in [(512, 2560, 4096), (2048, 9728, 2560), (32, 9728, 2560), (384, 9728, 2560)]:
         p = plan(M, N, K)
         assert p["k_waves"] == 1 and p["block_threads"] == 256, (M, N, K)
+
+
+def test_96_row_tiles_when_they_need_fewer_rounds():
+    # unsplit grids: 96 x 128 tiles with two waves per strip (two resident per compute unit) when
+    # their rounds of tiles per compute unit are fewer than the 64-row tiles' and at most two
+    def rounds(M, N, bm):
+        return -(-(-(-M // bm) * -(-N // 128)) // CUS)
+
+    for M, N in [(512, 9728), (509, 9728), (256, 9728), (192, 16384)]:
+        p = plan(M, N, 2560)
+        assert rounds(M, N, 96) < rounds(M, N, 64) and rounds(M, N, 96) <= 2, (M, N)
+        assert (p["tile_m"], p["tile_n"], p["k_waves"], p["block_threads"], p["split_k"]) == (96, 128, 2, 512, 1)
+        assert p["grid_y"] == -(-M // 96) and p["grid_x"] == -(-N // 128)
+    # as many rounds (384 rows), more than two (1024 rows), split grids and one tile per unit: 64 rows
+    for M, N, K in [(384, 9728, 2560), (1024, 9728, 2560), (512, 12288, 2560), (512, 2560, 9728),
+                    (512, 4096, 2560), (128, 9728, 2560)]:
+        assert plan(M, N, K)["tile_m"] == 64, (M, N, K)
 
 
 def test_split_k_only_for_under_filled_grids():

@@ -267,6 +267,18 @@ def test_prefill512_config_and_ragged_prefix(lib, shape):
     assert np.array_equal(y509, y512[:509])
 
 
+@pytest.mark.parametrize("M,N,K", [(192, 16384, 256), (250, 9728, 384), (90, 40000, 1280)])
+def test_96_row_tiles_match_oracle(lib, M, N, K):
+    # shapes the policy gives 96 x 128 tiles (fewer rounds per compute unit than 64-row tiles):
+    # ragged rows (250 = 2 x 96 + 58, 90 < 96) and columns (40000 = 312 x 128 + 64)
+    plan = lib.w4a16_plan(M, N, K)
+    assert (plan["tile_m"], plan["k_waves"], plan["split_k"]) == (96, 2, 1)
+    p = synth.random_problem(96, M, N, K)
+    y = run(lib, p, "linear")
+    assert_parity(y, p)
+    assert np.array_equal(y, run(lib, p, "qmm", 1))      # the forced-unsplit plan is the same plan
+
+
 @pytest.mark.parametrize("split", [1, 2, 4, 19, 0])
 def test_split_k_down_projection(lib, split):
     p = synth.problem(4, "down", 512)       # K = 9728: 76 groups

@@ -172,6 +172,16 @@ void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a
     // (measured on MI355X: 512-row q 23.6 -> 21.4 us, k/v 16.4 -> 15.0 us, 128-row gate 22.6 ->
     // 21.7 us; with more units per compute unit it measured 0-6% slower).
     if (variant == 1 && tiles * S <= cus) variant = kQmmKSplitVariant;
+    // Unsplit grids of more than one tile per compute unit: 96-row tiles with two waves per
+    // column strip (two resident per compute unit) when they need fewer rounds of tiles per
+    // compute unit, and at most two (measured on MI355X at 512 rows, K = 2560, N = 9728: 456
+    // tiles in 38.0 us against 608 64-row tiles in 43.0 us; with as many rounds, as for the
+    // 4096-wide q or the split o and down, they measured 4-13% slower).
+    if (variant == 1 && S == 1) {
+        const int64_t tiles96 = ceil_div(M, kQmmVariants[kQmmRows96Variant].bm) * ceil_div(N, tile_n);
+        const int64_t rounds64 = ceil_div(tiles, cus), rounds96 = ceil_div(tiles96, cus);
+        if (rounds96 < rounds64 && rounds96 <= 2) variant = kQmmRows96Variant;
+    }
     const QmmShape& v = kQmmVariants[variant];
     p->path = skinny ? W4A16_PATH_SKINNY : W4A16_PATH_QMM;
     p->tile_m = v.bm;

@@ -65,10 +65,13 @@ struct QmmShape {
     int tile_n() const { return nwaves / ksplit * nb * 32; }
 };
 
-constexpr int kNumQmmVariants = 6;
+constexpr int kNumQmmVariants = 7;
 // 64 x 128 tiles with two waves per column strip: for grids of at most one work unit per
 // compute unit (twice the waves per tile)
 constexpr int kQmmKSplitVariant = 5;
+// 96 x 128 tiles with two waves per column strip: when they need fewer rounds of tiles per
+// compute unit than the 64-row tiles, at most two
+constexpr int kQmmRows96Variant = 6;
 constexpr int kQmmSkinnyVariant = 4;   // 32 x 128 tiles, three stages: at most 32 rows
 extern const QmmShape kQmmVariants[kNumQmmVariants];
 

@@ -666,6 +666,7 @@ const QmmShape kQmmVariants[kNumQmmVariants] = {
     {32, 1, 4, 3},   // 4:  32 x 128 tile, four waves per SIMD, 3 stages (skinny M)
     {64, 1, 8, 2, 2},  // 5:  64 x 128 tile, 8 waves: two per 32-column strip, each taking half of
                        //     every group's sub-steps; six waves per SIMD
+    {96, 1, 8, 2, 2},  // 6:  96 x 128 tile, 8 waves as variant 5; four waves per SIMD (two tiles)
 };
 
 // Scales and biases four groups per load (two-stage instances) when the group count is a
@@ -764,6 +765,8 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, cons
         case 3: return launch_qmm_t<32, 1, 4, 4, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
         case 4: return launch_qmm_t<32, 1, 4, 4, 3>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
         case 5: return launch_qmm_t<64, 1, 8, 6, 2, 0, 6, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split,
+                                                           stream);
+        case 6: return launch_qmm_t<96, 1, 8, 4, 2, 0, 4, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split,
                                                            stream);
         default: return hipErrorInvalidValue;
     }
