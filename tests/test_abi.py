@@ -226,16 +226,21 @@ def gate_up_plan(M, N, K, split_k=0):
 
 
 def test_gate_up_plan_tiles_and_workspace():
-    # 32-row tiles up to 32 rows (dequantizing); above, 64-row tiles in the exact-code form
+    # 32-row tiles up to 32 rows (dequantizing); above, 64-row tiles in the exact-code form, except
+    # unsplit grids that dequantizing 96-row tiles cover in fewer rounds per compute unit (<= 2)
     r256 = lambda v: -(-v // 256) * 256
-    for M, tile_m in [(1, 32), (32, 32), (33, 64), (512, 64), (1024, 64), (1025, 64), (4096, 64)]:
+    for M, tile_m in [(1, 32), (32, 32), (33, 64), (256, 96), (384, 64), (512, 96), (1024, 64), (1025, 64),
+                      (4096, 64)]:
         p = gate_up_plan(M, 9728, 2560)
-        assert p["path"] == w4.PATH_GATE_UP and p["tile_m"] == tile_m and p["tile_n"] == 128
+        assert p["path"] == w4.PATH_GATE_UP and p["tile_m"] == tile_m and p["tile_n"] == 128, M
         assert p["grid_x"] == -(-9728 // 128) and p["grid_y"] == -(-M // tile_m)
-        assert (p["variant"] >= 10) == (M > 32)
+        codes = M > 32 and tile_m == 64
+        assert (p["variant"] >= 10) == codes
         # the workspace holds the group sums (exact-code form), then gate and up partials
-        sums = r256(M * w4.w4a8_xsum_cols(2560) * 2) if M > 32 else 0
+        sums = r256(M * w4.w4a8_xsum_cols(2560) * 2) if codes else 0
         assert p["workspace_bytes"] == sums + (2 * p["split_k"] * M * 9728 * 4 if p["split_k"] > 1 else 0)
+        if tile_m == 96:
+            assert p["variant"] == 3 and p["split_k"] == 1
     # the split follows the projection's rule on the same tile grid
     for M, N, K in [(128, 9728, 2560), (512, 9728, 2560), (512, 2560, 9728), (16, 1024, 2560)]:
         g, q = gate_up_plan(M, N, K), plan(M, N, K, path=w4.PATH_QMM if M > 32 else w4.PATH_SKINNY)
@@ -379,5 +384,6 @@ def test_exact_code_mode_plans():
         assert p["variant"] < 10
         assert p["workspace_bytes"] == (p["split_k"] * M * 9728 * 4 if p["split_k"] > 1 else 0)
     # the fused gate / up pair runs the exact-code form on its 64-row tiles above 32 rows
-    assert gate_up_plan(4096, 9728, 2560)["variant"] == 11 and gate_up_plan(512, 9728, 2560)["variant"] == 11
+    assert gate_up_plan(4096, 9728, 2560)["variant"] == 11 and gate_up_plan(1024, 9728, 2560)["variant"] == 11
+    assert gate_up_plan(512, 9728, 2560)["variant"] == 3                 # 96-row dequantizing tiles
     assert gate_up_plan(32, 9728, 2560)["variant"] < 10

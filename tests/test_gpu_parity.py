@@ -547,6 +547,8 @@ def assert_swiglu_parity(h_bits, x, gate, up, rows=None):
     (70, 1100, 1024, 2),       # forced: two slices
     (70, 1100, 1024, 5),       # forced: five slices of 1 or 2 groups
     (1500, 512, 384, 0),       # beyond 1024 rows, odd group count
+    (250, 9728, 384, 0),       # 96-row dequantizing tiles (one round against two): ragged rows
+    (90, 40000, 256, 0),       # 96-row tiles, ragged columns (40000 = 312 x 128 + 64)
 ])
 def test_gate_up_swiglu_matches_oracle(lib, M, N, K, split):
     x, gate, up = gate_up_problem(21, M, N, K)

@@ -320,18 +320,32 @@ int run_qmm(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint
 // Gate / up pair with SwiGLU: one tile kernel computes both projections of the same columns.
 // Tiles: 32 rows up to 32 rows; above, 64-row tiles in the exact-code mode (measured on MI355X
 // against the dequantizing 64- and 128-row tiles: 87 vs 98 us at 512 rows and 497 vs 560 us at
-// 4096 rows, K = 2560, N = 9728); without the exact-code mode 64 rows up to ~1k and 128 beyond.
+// 4096 rows, K = 2560, N = 9728); without the exact-code mode 64 rows up to ~1k and 128 beyond;
+// unsplit grids that 96-row tiles cover in fewer rounds per compute unit take those (below).
 // The split follows the qmm rule on the same tile grid.  Workspace: [group sums (exact-code
 // mode)][gate partials][up partials], the partials 2 * S * M * N fp32.
 void plan_gate_up(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p,
                   bool codes = true) {
     const bool skinny = M <= kSkinnyMaxRows;
     codes = codes && !skinny;
-    const int variant = skinny ? 0 : (codes ? kGateUpCodesTileVariant : (M <= 1024 ? 1 : 2));
-    const QmmShape& v = kGateUpVariants[variant];
-    const int64_t tile_n = v.tile_n();
-    const int64_t tiles = ceil_div(M, v.bm) * ceil_div(N, tile_n);
+    int variant = skinny ? 0 : (codes ? kGateUpCodesTileVariant : (M <= 1024 ? 1 : 2));
+    int64_t tile_n = kGateUpVariants[variant].tile_n();
+    int64_t tiles = ceil_div(M, kGateUpVariants[variant].bm) * ceil_div(N, tile_n);
     const int64_t S = tile_split(tiles, M, N, K / W4A16_GROUP, split_k, cus, skinny);
+    // Unsplit 64-row grids of more than one tile per compute unit: dequantizing 96-row tiles when
+    // they need fewer rounds of tiles per compute unit, and at most two (measured on MI355X, K =
+    // 2560, N = 9728: 512 rows 73.5-76.4 us against 86-87 us for the 64-row exact-code tiles,
+    // 256 rows 46 against 55 us; at 1024 rows, four rounds against five, 145 against 141 us).
+    if (!skinny && S == 1) {
+        const int64_t tiles96 = ceil_div(M, kGateUpVariants[kGateUpRows96Variant].bm) * ceil_div(N, tile_n);
+        if (ceil_div(tiles96, cus) < ceil_div(tiles, cus) && ceil_div(tiles96, cus) <= 2) {
+            variant = kGateUpRows96Variant;
+            codes = false;
+            tiles = tiles96;
+        }
+    }
+    const QmmShape& v = kGateUpVariants[variant];
+    tile_n = v.tile_n();
     p->path = W4A16_PATH_GATE_UP;
     p->tile_m = v.bm;
     p->tile_n = static_cast<int32_t>(tile_n);

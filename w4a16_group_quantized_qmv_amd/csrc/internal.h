@@ -97,8 +97,11 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, cons
 // projections.  split > 1 writes fp32 partials ws[0][z][M][N] (gate) and ws[1][z][M][N] (up).
 // xsum != nullptr selects the exact-code mode, compiled for the 64-row tiles
 // (kGateUpCodesTileVariant), where it measured faster than dequantizing at 512 and 4096 rows.
-constexpr int kNumGateUpVariants = 3;
+constexpr int kNumGateUpVariants = 4;
 constexpr int kGateUpCodesTileVariant = 1;
+// 96 x 128 tiles (dequantizing, two resident per compute unit): when they need fewer rounds of
+// tiles per compute unit than the 64-row tiles, at most two
+constexpr int kGateUpRows96Variant = 3;
 extern const QmmShape kGateUpVariants[kNumGateUpVariants];
 hipError_t launch_gate_up(int variant, const uint16_t* x, const uint16_t* xsum, const uint32_t* wq_gate,
                           const uint16_t* s_gate, const uint16_t* b_gate, const uint32_t* wq_up, const uint16_t* s_up,

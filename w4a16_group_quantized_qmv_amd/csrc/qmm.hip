@@ -776,6 +776,7 @@ const QmmShape kGateUpVariants[kNumGateUpVariants] = {
     {32, 1, 4, 2},   // 0:  32 x 128 tile of h (gate and up: 2 x 32 columns per wave), four waves per SIMD
     {64, 1, 4, 2},   // 1:  64 x 128 tile of h, three waves per SIMD (two in the exact-code mode)
     {128, 1, 4, 2},  // 2: 128 x 128 tile of h, one wave per SIMD
+    {96, 1, 4, 2},   // 3:  96 x 128 tile of h, two waves per SIMD
 };
 
 hipError_t launch_gate_up(int variant, const uint16_t* x, const uint16_t* xsum, const uint32_t* wq_gate,
@@ -791,6 +792,8 @@ hipError_t launch_gate_up(int variant, const uint16_t* x, const uint16_t* xsum, 
                                                   split, stream);
         case 2: return launch_gate_up_t<128, 1, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N,
                                                    K, split, stream);
+        case 3: return launch_gate_up_t<96, 2, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N,
+                                                  K, split, stream);
         default: return hipErrorInvalidValue;
     }
 }
