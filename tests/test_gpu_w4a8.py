@@ -152,7 +152,8 @@ def test_tiny_config(lib, split):
 
 @pytest.mark.parametrize("M,N,K,split", [
     (1, 96, 256, 0), (8, 200, 1152, 0), (31, 130, 2560, 0), (64, 1024, 2560, 3), (100, 257, 4096, 0),
-    (129, 384, 1280, 5), (300, 1000, 2560, 0)])
+    (129, 384, 1280, 5), (300, 1000, 2560, 0),
+    (250, 9728, 384, 0), (90, 40000, 256, 0)])     # wide grids: ragged rows, ragged columns
 def test_random_shapes(lib, M, N, K, split):
     p = synth.random_problem(21, M, N, K)
     assert_w4a8_parity(run_w4a8(lib, p, split), p)
