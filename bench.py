@@ -324,6 +324,7 @@ def next_rows(torch, w4, projections, copies, reps=20):
       * the skinny path (16 and 32 rows) against the 64-row tiles on the gate and down shapes;
       * W4A8 (int8 activations) against W4A16 on the step's seven projections;
       * the 4096-row prefill of gate / up / down and the vocabulary head over all rows;
+      * the 128-row prefill of the seven layer projections (and their sum as one layer);
       * decode rows (M = 1, 4) on the four decode shapes, and the width-generic matvec at
         1, 2, 3, 4 and 8 bits."""
     from w4a16_group_quantized_qmv_amd import synth
@@ -420,6 +421,26 @@ def next_rows(torch, w4, projections, copies, reps=20):
                           "TFLOP/s": round(f / t / 1e6, 2), "frac_mfma": round(f / t / 1e6 / PEAK_BF16_TFLOPS, 4)})
         del fns, rot, y, xl
     out["prefill4096"] = long_rows
+
+    # 128-row prefill: the seven layer projections, each alone
+    short_rows = []
+    for name in LAYER:
+        p = by[name]
+        xs = torch.from_numpy(synth.activations(3, synth.shape_index(3, name), 128, p["K"]).view("int16"))
+        xs = xs.view(torch.bfloat16).to(dev)
+        rot = rotation(p["w"][0])
+        pl = w4.w4a16_plan(128, p["N"], p["K"])
+        y = torch.empty((128, p["N"]), dtype=torch.bfloat16, device=dev)
+        wsb = ws_for(torch, pl["workspace_bytes"], dev)
+        t = timed([w4.PreparedLinear(xs, *w, y=y, workspace=wsb) for w in rot])
+        f = flops(128, p["N"], p["K"])
+        short_rows.append({"name": name, "M": 128, "N": p["N"], "K": p["K"], "tile": [pl["tile_m"], pl["tile_n"]],
+                           "split_k": pl["split_k"], "avg_us": round(t, 3), "TFLOP/s": round(f / t / 1e6, 2),
+                           "frac_mfma": round(f / t / 1e6 / PEAK_BF16_TFLOPS, 4)})
+        del rot, y, xs
+    layer_flops = sum(flops(128, r["N"], r["K"]) for r in short_rows)
+    out["prefill128"] = {"projections": short_rows,
+                         "layer_TFLOP/s": round(layer_flops / sum(r["avg_us"] for r in short_rows) / 1e6, 2)}
 
     # decode rows on the four decode shapes
     decode = []
