@@ -142,8 +142,8 @@ def main():
                     help="before the timed region, copy a 256 MiB buffer three times (reference for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the projection kernels on a single MI355X "
-              "(column- or row-sharding across GPUs is described in DESIGN.md, not implemented).", file=sys.stderr)
+        print("bench.py measures one GPU only: the projection kernels run on a single MI355X "
+              "(column- or row-sharding across GPUs is not implemented).", file=sys.stderr)
         sys.exit(2)
 
     import torch
