@@ -132,7 +132,7 @@ int qmv_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, con
  * split_k: 0 = policy, 1 = off, S > 1 = forced (clamped to the number of groups).
  *
  * Two forms of the same product (both within the parity tolerance, integer cases identical):
- * tiles of up to 64 rows (M <= 1024) dequantize each weight to bf16 in registers; the 128-row
+ * tiles of up to 96 rows (M <= 1024) dequantize each weight to bf16 in registers; the 128-row
  * tiles (M > 1024) multiply the raw codes on the matrix core, scale each group's fp32 product
  * once and add sum_g b * X from the activations' per-group sums, which a first launch writes
  * to the start of `workspace` (bf16 [M, 2G rounded up to 16], padded to 256 bytes).
@@ -170,7 +170,8 @@ int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, 
  * 32-row tiles up to 32 rows; above, 64-row tiles in the exact-code form described at
  * qmm_w4a16 (codes on the matrix core, the bias term from the activations' group sums), or,
  * when the workspace has no room for the group sums, dequantizing tiles (64 rows up to ~1k,
- * 128 beyond; same result within the tolerance).  split_k as for qmm_w4a16.  Workspace
+ * 128 beyond; same result within the tolerance).  Unsplit grids that 96-row tiles cover in
+ * fewer rounds of tiles per compute unit (at most two) run dequantizing 96-row tiles.  split_k as for qmm_w4a16.  Workspace
  * (w4a16_gate_up_plan().workspace_bytes): [group sums, exact-code form][gate partials][up
  * partials], the partials 2 * S * M * N fp32 of a split plan, summed in slice order before the
  * SiLU, so results are deterministic.  Same preconditions, ownership and errors as qmm_w4a16
