@@ -259,8 +259,10 @@ int w4a8_quantize_rows(const uint16_t* x, int8_t* xq, float* sx, uint16_t* xsum,
 
 /*
  * Launch plan of qmm_w4a8 (path = W4A16_PATH_W4A8): 32-row tiles up to 32 rows, 64 up to ~1k,
- * 128 beyond; the split rule of qmm_w4a16.  workspace_bytes = the fp32 partials (S * M * N * 4)
- * when the plan splits.  split_k and num_cus as in w4a16_plan.  Pure host arithmetic.
+ * 128 beyond; the split rule of qmm_w4a16.  64-row grids of at most one work unit (tile x
+ * slice) per compute unit run eight waves per tile, two per 32-column block (k_waves = 2,
+ * block_threads = 512).  workspace_bytes = the fp32 partials (S * M * N * 4) when the plan
+ * splits.  split_k and num_cus as in w4a16_plan.  Pure host arithmetic.
  */
 int w4a8_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, int32_t num_cus, w4a16_plan_t* out);
 
