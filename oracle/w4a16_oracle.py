@@ -372,14 +372,20 @@ def brute_force(x_bits, wq, scales, biases, group: int = GROUP, bits: int = 4):
 
 
 def _brute_weights(wq, scales, biases, K, group, bits):
-    """Every weight decoded from its word by explicit shifts, dequantized with two fp32 roundings."""
+    """Every weight decoded from the row's bit stream by explicit shifts (reading R8: element k is
+    stream bits ``bits*k ..``, i.e. bits ``sh ..`` of word ``j`` continued in word ``j + 1`` when
+    the code crosses it, ``j, sh = divmod(bits*k, 32)``), dequantized with two fp32 roundings."""
     ws = []
-    per = 32 // bits
+    mask = (1 << bits) - 1
+    n_words = wq.shape[1]
     for n in range(wq.shape[0]):
         row = []
         for k in range(K):
-            word = int(wq[n, k // per])
-            code = (word >> (bits * (k % per))) & ((1 << bits) - 1)
+            j, sh = divmod(bits * k, 32)
+            window = int(wq[n, j])
+            if j + 1 < n_words:
+                window |= int(wq[n, j + 1]) << 32
+            code = (window >> sh) & mask
             s = _bf16_scalar(scales[n, k // group])
             b = _bf16_scalar(biases[n, k // group])
             row.append(_f32_round(_f32_round(s * code) + b))

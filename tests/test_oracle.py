@@ -425,6 +425,111 @@ def test_swiglu_reference_composes_two_projections():
     assert not O.check_swiglu(bad, g, Ag, u, Au).ok
 
 
+# The SwiGLU bound is derived from R6 by error propagation.  It is pinned against a numerical
+# exploration of what a correct fused kernel may return, not against a copy of its formula:
+#   soundness  every result a kernel could legitimately produce -- gate and up sums anywhere in
+#              their R6 boxes, SiLU and the product in fp32, one rounding to bf16 -- is accepted;
+#   tightness  in a configuration where one term of the bound dominates, the bound (read back
+#              from the check's own error ratio) is within 1.15x of the worst legitimate error (measured:
+#              1.005-1.10x), so the bound sits at the edge of what a correct kernel can return.
+# Planted mistakes (a looser tolerance, a dropped term, a smaller slope constant) each fail one.
+
+SWIGLU_CASES = {
+    # name: (g, u, A_g, A_u, tight)
+    "gate_error_at_steepest_slope": (2.3994, 3.0, 512.0, 0.0, True),    # silu' peaks near z = 2.3994
+    "up_error_at_large_gate": (20.0, 0.01, 0.0, 10.24, True),
+    "both_errors_at_zero": (0.0, 0.0, 51200.0, 1.024, True),            # the cross term alone
+    "rounding_only": (20.0, 1.0, 0.0, 0.0, False),
+    "silu_minimum": (-1.2785, 4.0, 512.0, 0.0, False),                  # the global slope bound is loose here
+    "saturated_negative_gate": (-30.0, 5.0, 64.0, 64.0, False),
+}
+
+
+def _f32(v):
+    return np.float32(v)
+
+
+def _legit_results(g, u, A_g, A_u, n=401):
+    """bf16 results a correct kernel may return: g~, u~ on a grid of their R6 boxes (fp32), then
+    silu(g~) * u~ in fp32 arithmetic and one round-to-nearest-even to bf16."""
+    e_g = O.TOL_REL * abs(g) + O.TOL_MASS * A_g
+    e_u = O.TOL_REL * abs(u) + O.TOL_MASS * A_u
+    gg = np.linspace(g - e_g, g + e_g, n).astype(np.float32)
+    out = []
+    for ut in (u - e_u, u, u + e_u):
+        ut32 = _f32(ut)
+        with np.errstate(over="ignore"):
+            silu = gg / (_f32(1) + np.exp(-gg))        # fp32 throughout
+        out.append(O.f32_to_bf16_rne((silu * ut32).astype(np.float32)))
+    return np.concatenate(out)
+
+
+def _exact_h(g, u):
+    return g / (1.0 + math.exp(-g)) * u if g > -700 else 0.0
+
+
+def _bound_from_ratio(check_fn, g, u, A_g, A_u):
+    """The check's bound at one element, read back from its own error ratio."""
+    h_ref = _exact_h(g, u)
+    probe = O.f32_to_bf16_rne(np.array([[h_ref + 1.0 + abs(h_ref)]], dtype=np.float32))
+    err = abs(float(O.bf16_to_f64(probe)[0, 0]) - h_ref)
+    r = check_fn(probe, np.array([[g]]), np.array([[A_g]]), np.array([[u]]), np.array([[A_u]]))
+    return err / r.max_ratio
+
+
+def _swiglu_pins(check_fn):
+    """Names of the SwiGLU pins that ``check_fn`` fails (empty: it passes all)."""
+    failed = []
+    for name, (g, u, A_g, A_u, tight) in SWIGLU_CASES.items():
+        legit = _legit_results(g, u, A_g, A_u)
+        ones = np.ones((1, legit.size))
+        r = check_fn(legit[None, :], g * ones, A_g * ones, u * ones, A_u * ones)
+        if not r.ok:
+            failed.append(f"sound:{name}")
+        if tight:
+            worst = float(np.max(np.abs(O.bf16_to_f64(legit) - _exact_h(g, u))))
+            if _bound_from_ratio(check_fn, g, u, A_g, A_u) > 1.15 * worst:
+                failed.append(f"tight:{name}")
+    return failed
+
+
+def test_check_swiglu_is_sound_and_tight():
+    assert _swiglu_pins(O.check_swiglu) == []
+
+
+def _swiglu_mutant(kind):
+    def fn(h_bits, g_ref, A_g, u_ref, A_u):
+        if kind == "tolerance_8x_looser":
+            return O.check_swiglu(h_bits, g_ref, A_g, u_ref, A_u, rel=8 * O.TOL_REL, mass=8 * O.TOL_MASS)
+        g_ref, u_ref = np.asarray(g_ref, np.float64), np.asarray(u_ref, np.float64)
+        e_g = O.TOL_REL * np.abs(g_ref) + O.TOL_MASS * np.asarray(A_g, np.float64)
+        e_u = O.TOL_REL * np.abs(u_ref) + O.TOL_MASS * np.asarray(A_u, np.float64)
+        h_ref = O.silu_f64(g_ref) * u_ref
+        slope = 1.0 if kind == "slope_bound_1" else 1.1
+        t_g = slope * e_g * (np.abs(u_ref) + (0 if kind == "cross_term_dropped" else e_u))
+        t_u = 0 if kind == "up_error_term_dropped" else np.abs(O.silu_f64(g_ref)) * e_u
+        t_r = 0 if kind == "rounding_term_dropped" else O.TOL_REL * np.abs(h_ref)
+        bound = t_g + t_u + t_r
+        err = np.abs(O.bf16_to_f64(h_bits) - h_ref)
+        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1), np.where(err == 0, 0.0, np.inf))
+        ok = bool(np.all(np.isfinite(err) & (err <= bound)))
+        return O.CheckResult(ok, float(ratio.max()), (), int((err > bound).sum()), int(err.size))
+    return fn
+
+
+SWIGLU_MUTANTS = ["tolerance_8x_looser", "slope_bound_1", "cross_term_dropped", "up_error_term_dropped",
+                  "rounding_term_dropped"]
+
+
+def test_swiglu_mutant_copy_is_faithful_without_a_mistake():
+    assert _swiglu_pins(_swiglu_mutant("none")) == []
+
+
+@pytest.mark.parametrize("kind", SWIGLU_MUTANTS)
+def test_swiglu_pins_catch_planted_mistakes(kind):
+    assert _swiglu_pins(_swiglu_mutant(kind)), f"planted mistake {kind!r} passed every SwiGLU pin"
+
+
 # ----------------------------------------------------------------------------- other code widths (R8)
 
 def _load_golden_bits(bits):
@@ -539,13 +644,32 @@ def test_pack_and_unpack_are_inverse_and_match_the_input_generator(bits):
     assert np.array_equal(O.unpack_q(w, 256, bits), q)
 
 
-@pytest.mark.parametrize("bits", [1, 2, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 8])
 def test_reference_matches_brute_force_other_widths(bits):
     p = synth.random_problem(70 + bits, 3, 5, 256, bits=bits)
     y, A = O.reference(p["x"], p["wq"], p["scales"], p["biases"], bits=bits)
     yb, Ab = O.brute_force(p["x"], p["wq"], p["scales"], p["biases"], bits=bits)
     assert np.allclose(y, yb, rtol=0, atol=1e-12 * max(1.0, float(np.abs(Ab).max())))
     assert np.allclose(A, Ab, rtol=1e-12, atol=0)
+
+
+def test_brute_force_decodes_straddling_three_bit_codes():
+    # hand-packed 3-bit rows (reading R8): element 10 is bits 30, 31 of word 0 and bit 0 of word 1
+    # (code 7), element 21 is bit 31 of word 1 and bits 0, 1 of word 2 (code 5), and elements 31
+    # and 32 meet at the boundary of two runs (bit 31 of word 2 is the top bit of element 31, bits
+    # 0, 1 of word 3 the low bits of element 32: codes 4 and 3); every other code is 0
+    K = 128
+    words = np.zeros((2, K * 3 // 32), dtype=np.uint32)
+    words[0, 0], words[0, 1] = 0xC0000000, 0x00000001
+    words[1, 1], words[1, 2], words[1, 3] = 0x80000000, 0x80000002, 0x00000003
+    s = synth.const_bf16(1.0, (2, 1))
+    b = synth.const_bf16(0.0, (2, 1))
+    x = np.where(np.eye(K, dtype=bool), synth.const_bf16(1.0, (K, K)), np.uint16(0))   # y = q^T
+    y, _ = O.brute_force(x, words, s, b, bits=3)
+    expect = np.zeros((K, 2))
+    expect[10, 0] = 7
+    expect[21, 1], expect[31, 1], expect[32, 1] = 5, 4, 3
+    assert np.array_equal(y, expect)
 
 
 @pytest.mark.parametrize("bits", [1, 2, 8])
