@@ -29,9 +29,14 @@
  *
  * Preconditions checked on the host (a violation returns an error status, never launches):
  *   1 <= M, N <= 2^31 - 1;  1 <= K <= 2^20;  K % 128 == 0;  group == 128;
- *   x, wq, workspace 16-byte aligned;  scales, biases, y 2-byte aligned.
+ *   x, wq, workspace 16-byte aligned;  scales, biases, y 2-byte aligned;
+ *   the output's bytes disjoint from every input's (by address range; the workspace is not
+ *   compared and must not overlap any other buffer).
  *
  * Errors are returned as status codes (never exceptions); w4a16_status_string() names them.
+ * A case outside what an entry point serves is an error of its own (W4A16_ERR_UNSUPPORTED),
+ * never a silently different computation: the convention of raising NotImplementedError for
+ * unsupported cases in "MLX Metal Kernels v0.20.0", Known limitations (continuation prefill).
  * Thread safety: stateless apart from a per-device cache of the compute-unit count.
  */
 #ifndef W4A16_H
@@ -56,7 +61,8 @@ enum w4a16_status {
     W4A16_ERR_WORKSPACE = 5,   /* a forced split_k > 1 has too little workspace               */
     W4A16_ERR_UNSUPPORTED = 6, /* valid arguments this entry point does not serve (qmv, M > 8)*/
     W4A16_ERR_LAUNCH = 7,      /* the HIP runtime rejected a launch                           */
-    W4A16_ERR_DEVICE = 8       /* the device could not be queried                             */
+    W4A16_ERR_DEVICE = 8,      /* the device could not be queried                             */
+    W4A16_ERR_OVERLAP = 9      /* an output shares bytes with an input                        */
 };
 
 enum w4a16_path {
@@ -175,7 +181,8 @@ int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, 
  * (w4a16_gate_up_plan().workspace_bytes): [group sums, exact-code form][gate partials][up
  * partials], the partials 2 * S * M * N fp32 of a split plan, summed in slice order before the
  * SiLU, so results are deterministic.  Same preconditions, ownership and errors as qmm_w4a16
- * (every pointer checked, h must not overlap an input).
+ * (every pointer checked for null and alignment; h overlapping x or either weight set returns
+ * W4A16_ERR_OVERLAP).
  */
 int w4a16_gate_up_swiglu(const uint16_t* x, const uint32_t* wq_gate, const uint16_t* scales_gate,
                          const uint16_t* biases_gate, const uint32_t* wq_up, const uint16_t* scales_up,

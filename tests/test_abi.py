@@ -28,8 +28,9 @@ def test_library_exports_every_declared_symbol(lib):
 def test_abi_version_and_status_strings():
     assert w4.w4a16_abi_version() == 1
     expect = ["W4A16_OK", "W4A16_ERR_NULL", "W4A16_ERR_SHAPE", "W4A16_ERR_GROUP", "W4A16_ERR_ALIGN",
-              "W4A16_ERR_WORKSPACE", "W4A16_ERR_UNSUPPORTED", "W4A16_ERR_LAUNCH", "W4A16_ERR_DEVICE"]
-    assert [w4.w4a16_status_string(i) for i in range(9)] == expect
+              "W4A16_ERR_WORKSPACE", "W4A16_ERR_UNSUPPORTED", "W4A16_ERR_LAUNCH", "W4A16_ERR_DEVICE",
+              "W4A16_ERR_OVERLAP"]
+    assert [w4.w4a16_status_string(i) for i in range(10)] == expect
     assert w4.w4a16_status_string(99) == "unknown"
 
 
@@ -191,13 +192,16 @@ def test_plan_rejects_null_output(lib):
 
 # ------------------------------------------------------------------------------ validation before launch
 
-A16 = 0x10000      # fake, 16-byte aligned addresses: validation fails before they could be used
-ODD = 0x10008
+# fake, 16-byte aligned addresses 16 MiB apart (one per buffer, so no two overlap): validation
+# fails before they could be used
+X, WQ, S, B, Y, WS = (i << 24 for i in range(1, 7))
+WU, SU, BU = (i << 24 for i in range(7, 10))
+ODD = X + 8
 
 
 @pytest.mark.parametrize("fn", ["qmv", "qmm", "linear"])
 def test_compute_entry_points_validate_before_launch(lib, fn):
-    def call(x=A16, wq=A16, s=A16, b=A16, y=A16, M=4, N=16, K=256, group=128):
+    def call(x=X, wq=WQ, s=S, b=B, y=Y, M=4, N=16, K=256, group=128):
         if fn == "qmv":
             return lib.qmv_w4a16(x, wq, s, b, y, M, N, K, group, None)
         if fn == "qmm":
@@ -207,16 +211,18 @@ def test_compute_entry_points_validate_before_launch(lib, fn):
     assert call(x=None) == 1 and call(wq=None) == 1 and call(s=None) == 1 and call(b=None) == 1 and call(y=None) == 1
     assert call(M=0) == 2 and call(N=-1) == 2 and call(K=100) == 2 and call(K=0) == 2
     assert call(group=64) == 3
-    assert call(x=ODD) == 4 and call(wq=ODD) == 4
-    assert call(s=A16 + 1) == 4 and call(y=A16 + 1) == 4
+    assert call(x=ODD) == 4 and call(wq=WQ + 8) == 4
+    assert call(s=S + 1) == 4 and call(y=Y + 1) == 4
+    # the output may not share a byte with an input (x is 4 x 256 bf16 = 2 KiB; wq 16 x 128 B)
+    assert call(y=X) == 9 and call(y=X + 2046) == 9 and call(y=WQ + 1024) == 9 and call(y=S) == 9 and call(y=B) == 9
 
 
 def test_qmv_rejects_more_than_eight_rows(lib):
-    assert lib.qmv_w4a16(A16, A16, A16, A16, A16, 9, 16, 256, 128, None) == 6
+    assert lib.qmv_w4a16(X, WQ, S, B, Y, 9, 16, 256, 128, None) == 6
 
 
 def test_negative_split_is_a_shape_error(lib):
-    assert lib.qmm_w4a16(A16, A16, A16, A16, A16, 16, 16, 256, 128, -2, None, 0, None) == 2
+    assert lib.qmm_w4a16(X, WQ, S, B, Y, 16, 16, 256, 128, -2, None, 0, None) == 2
 
 
 # ------------------------------------------------------------------------------ fused gate / up + SwiGLU
@@ -250,14 +256,16 @@ def test_gate_up_plan_tiles_and_workspace():
 
 
 def test_gate_up_validates_before_launch(lib):
-    def call(x=A16, wg=A16, sg=A16, bg=A16, wu=A16, su=A16, bu=A16, h=A16, M=4, N=16, K=256, group=128, split=1):
+    def call(x=X, wg=WQ, sg=S, bg=B, wu=WU, su=SU, bu=BU, h=Y, M=4, N=16, K=256, group=128, split=1):
         return lib.w4a16_gate_up_swiglu(x, wg, sg, bg, wu, su, bu, h, M, N, K, group, split, None, 0, None)
 
     for kw in ("x", "wg", "sg", "bg", "wu", "su", "bu", "h"):
         assert call(**{kw: None}) == 1, kw
     assert call(M=0) == 2 and call(K=100) == 2 and call(split=-1) == 2
     assert call(group=64) == 3
-    assert call(wu=ODD) == 4 and call(su=A16 + 1) == 4 and call(h=A16 + 1) == 4
+    assert call(wu=WU + 8) == 4 and call(su=SU + 1) == 4 and call(h=Y + 1) == 4
+    for kw, base in (("x", X), ("wg", WQ), ("sg", S), ("bg", B), ("wu", WU), ("su", SU), ("bu", BU)):
+        assert call(h=base) == 9, kw                                # h may not overlap any input
     with pytest.raises(ValueError):
         w4.w4a16_gate_up_plan(4, 16, 100, 128, 0, CUS)
 
@@ -293,17 +301,19 @@ def test_qmv_affine_rejects_unsupported(lib, args):
     M, N, K, bits, mode = args
     with pytest.raises(NotImplementedError):
         w4.qmv_affine_plan(M, N, K, bits, mode, 128, CUS)
-    assert lib.qmv_affine(A16, A16, A16, A16, A16, M, N, K, 128, bits, mode, None) == 6
+    assert lib.qmv_affine(X, WQ, S, B, Y, M, N, K, 128, bits, mode, None) == 6
 
 
 def test_qmv_affine_validates_before_launch(lib):
-    def call(x=A16, wq=A16, s=A16, b=A16, y=A16, M=2, N=16, K=256, group=128, bits=2, mode=0):
+    def call(x=X, wq=WQ, s=S, b=B, y=Y, M=2, N=16, K=256, group=128, bits=2, mode=0):
         return lib.qmv_affine(x, wq, s, b, y, M, N, K, group, bits, mode, None)
 
     assert call(x=None) == 1 and call(wq=None) == 1 and call(s=None) == 1 and call(b=None) == 1 and call(y=None) == 1
     assert call(M=0) == 2 and call(N=-1) == 2 and call(K=100) == 2 and call(K=2 ** 20 + 128) == 2
     assert call(group=64) == 3
-    assert call(x=ODD) == 4 and call(wq=ODD) == 4 and call(s=A16 + 1) == 4 and call(y=A16 + 1) == 4
+    assert call(x=ODD) == 4 and call(wq=WQ + 8) == 4 and call(s=S + 1) == 4 and call(y=Y + 1) == 4
+    # 2-bit codes: wq is 16 x 64 bytes, so an output at +1000 overlaps it
+    assert call(y=WQ + 1000) == 9
     assert lib.qmv_affine_plan(1, 16, 256, 128, 4, 0, CUS, None) == 1
 
 
@@ -345,26 +355,30 @@ def test_w4a8_xsum_columns_and_linear_workspace():
 
 
 def test_w4a8_entry_points_validate_before_launch(lib):
-    def quant(x=A16, xq=A16, sx=A16, xs=A16, M=4, K=256, group=128):
+    def quant(x=X, xq=WQ, sx=S, xs=B, M=4, K=256, group=128):
         return lib.w4a8_quantize_rows(x, xq, sx, xs, M, K, group, None)
 
     assert quant(x=None) == 1 and quant(xq=None) == 1 and quant(sx=None) == 1 and quant(xs=None) == 1
     assert quant(M=0) == 2 and quant(K=100) == 2 and quant(group=64) == 3
-    assert quant(x=ODD) == 4 and quant(xq=ODD) == 4 and quant(xs=ODD) == 4 and quant(sx=A16 + 2) == 4
+    assert quant(x=ODD) == 4 and quant(xq=WQ + 8) == 4 and quant(xs=B + 8) == 4 and quant(sx=S + 2) == 4
+    assert quant(xq=X + 1024) == 9 and quant(sx=X) == 9 and quant(xs=WQ + 16) == 9 and quant(sx=WQ + 1020) == 9
 
-    def qmm(xq=A16, sx=A16, xs=A16, wq=A16, s=A16, b=A16, y=A16, M=4, N=16, K=256, group=128, split=1):
+    def qmm(xq=X, sx=WS, xs=WU, wq=WQ, s=S, b=B, y=Y, M=4, N=16, K=256, group=128, split=1):
         return lib.qmm_w4a8(xq, sx, xs, wq, s, b, y, M, N, K, group, split, None, 0, None)
 
     for kw in ("xq", "sx", "xs", "wq", "s", "b", "y"):
         assert qmm(**{kw: None}) == 1, kw
     assert qmm(M=0) == 2 and qmm(K=100) == 2 and qmm(split=-1) == 2 and qmm(group=64) == 3
-    assert qmm(xq=ODD) == 4 and qmm(wq=ODD) == 4 and qmm(y=A16 + 1) == 4
+    assert qmm(xq=ODD) == 4 and qmm(wq=WQ + 8) == 4 and qmm(y=Y + 1) == 4
+    for kw, base in (("xq", X), ("sx", WS), ("xs", WU), ("wq", WQ), ("s", S), ("b", B)):
+        assert qmm(y=base) == 9, kw
 
-    def linear(x=A16, wq=A16, s=A16, b=A16, y=A16, M=4, N=16, K=256, ws=A16 * 16, nbytes=1 << 20):
+    def linear(x=X, wq=WQ, s=S, b=B, y=Y, M=4, N=16, K=256, ws=WS, nbytes=1 << 20):
         return lib.w4a8_linear(x, wq, s, b, y, M, N, K, 128, ws, nbytes, None)
 
     assert linear(x=None) == 1 and linear(M=0) == 2 and linear(x=ODD) == 4
-    assert linear(ws=None) == 5 and linear(nbytes=100) == 5 and linear(ws=A16 * 16 + 16) == 4
+    assert linear(ws=None) == 5 and linear(nbytes=100) == 5 and linear(ws=WS + 16) == 4
+    assert linear(y=X + 512) == 9
 
 
 def test_exact_code_mode_plans():

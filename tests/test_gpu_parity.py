@@ -470,6 +470,38 @@ def test_split_call_in_a_graph_replays(lib):
         assert np.array_equal(bits(y2), ref), f"eager call after replay {i}"
 
 
+def test_split_call_on_a_side_stream_keeps_its_workspace(lib):
+    """A split call on the caller's side stream, with output and workspace allocated by the
+    binding on torch's current stream: the side stream is kept busy first, so the call's kernels
+    are still queued when it returns; the current stream then allocates memory of the
+    workspace's size and fills it.  The result must match the oracle (the binding records the
+    side stream on what it allocated, so that memory is not handed out again early)."""
+    import torch
+    M, N, K, split = 64, 2000, 4096, 4
+    p = synth.random_problem(33, M, N, K)
+    x, wq, s, b = to_device(p)
+    nbytes = lib.w4a16_plan(M, N, K, path=lib.PATH_QMM, split_k=split)["workspace_bytes"]
+    busy = torch.randn(4096, 4096, device="cuda:0")
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    ref = None
+    for trial in range(3):
+        announce(f"side-stream split call M={M} N={N} K={K} split={split} trial={trial}")
+        with torch.cuda.stream(side):
+            for _ in range(6):
+                busy = (busy @ busy).mul_(1.0 / 64.0)
+        y = lib.qmm_w4a16(x, wq, s, b, split_k=split, stream=side)
+        junk = torch.empty((nbytes + 3) // 4, dtype=torch.float32, device="cuda:0").fill_(float("nan"))
+        junk2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0").fill_(float("nan"))
+        torch.cuda.synchronize()
+        got = bits(y)
+        assert_parity(got, p)
+        if ref is None:
+            ref = got
+        assert np.array_equal(got, ref), f"trial {trial}"
+        del junk, junk2
+
+
 # ---------------------------------------------------------------------------------- error paths on the device
 
 def test_forced_split_without_workspace_is_rejected(lib):

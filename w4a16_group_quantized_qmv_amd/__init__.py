@@ -135,7 +135,7 @@ def _raise_for(status: int, what: str):
     if status == W4A16_OK:
         return
     msg = f"{what}: {w4a16_status_string(status)}"
-    if status in (1, 2, 3, 4, 5):
+    if status in (1, 2, 3, 4, 5, 9):
         raise ValueError(msg)
     if status == 6:
         raise NotImplementedError(msg)
@@ -227,11 +227,30 @@ def _operands(x, wq, scales, biases, y, bits: int = 4):
     return M, N, K, y
 
 
+def _stream_handle(stream) -> int:
+    """A HIP stream handle from a ``torch.cuda.Stream`` or an integer handle."""
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
 def _stream(stream, device):
     if stream is not None:
-        return ctypes.c_void_p(int(stream))
+        return ctypes.c_void_p(_stream_handle(stream))
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _keep_for_stream(stream, device, *tensors):
+    """Tensors allocated here (on torch's current stream) but used by kernels on the caller's
+    ``stream``: record that stream on them, so torch's caching allocator does not hand their
+    memory to another allocation before the kernels queued there have finished with it."""
+    if stream is None:
+        return
+    torch = _torch()
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(_stream_handle(stream),
+                                                                                      device=device)
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
 
 
 def _workspace(workspace, nbytes, device):
@@ -247,7 +266,9 @@ def _workspace(workspace, nbytes, device):
 
 def qmv_w4a16(x, wq, scales, biases, y=None, stream=None):
     """Decode-row matvec (1 <= M <= 8); returns y."""
+    own_y = y is None
     M, N, K, y = _operands(x, wq, scales, biases, y)
+    _keep_for_stream(stream, x.device, y if own_y else None)
     st = load().qmv_w4a16(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(),
                           M, N, K, GROUP, _stream(stream, x.device))
     _raise_for(st, "qmv_w4a16")
@@ -260,7 +281,9 @@ def qmv_affine(x, wq, scales, biases, bits: int, y=None, mode: int = QMV_POLICY,
     row-amortized or the per-row kernel.  Returns y."""
     if bits not in BITS:
         raise ValueError(f"bits={bits} must be one of {BITS}")
+    own_y = y is None
     M, N, K, y = _operands(x, wq, scales, biases, y, bits)
+    _keep_for_stream(stream, x.device, y if own_y else None)
     st = load().qmv_affine(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(),
                            M, N, K, GROUP, bits, mode, _stream(stream, x.device))
     _raise_for(st, "qmv_affine")
@@ -269,9 +292,11 @@ def qmv_affine(x, wq, scales, biases, bits: int, y=None, mode: int = QMV_POLICY,
 
 def qmm_w4a16(x, wq, scales, biases, y=None, split_k: int = 0, workspace=None, stream=None):
     """Tiled matrix path for any M; split_k 0 = policy, 1 = off, S > 1 forced.  Returns y."""
+    own_y, own_ws = y is None, workspace is None
     M, N, K, y = _operands(x, wq, scales, biases, y)
     need = w4a16_plan(M, N, K, GROUP, PATH_QMM, split_k)["workspace_bytes"]
     ws, ws_bytes = _workspace(workspace, need, x.device)
+    _keep_for_stream(stream, x.device, y if own_y else None, ws if own_ws else None)
     st = load().qmm_w4a16(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(),
                           M, N, K, GROUP, split_k, None if ws is None else ws.data_ptr(), ws_bytes,
                           _stream(stream, x.device))
@@ -282,8 +307,10 @@ def qmm_w4a16(x, wq, scales, biases, y=None, split_k: int = 0, workspace=None, s
 def w4a16_linear(x, wq, scales, biases, y=None, workspace=None, stream=None):
     """Dispatching entry point (qmv for M <= 8, the skinny path for 8 < M <= 32, qmm beyond, each
     with the policy's split).  Returns y."""
+    own_y, own_ws = y is None, workspace is None
     M, N, K, y = _operands(x, wq, scales, biases, y)
     ws, ws_bytes = _workspace(workspace, w4a16_workspace_bytes(M, N, K), x.device)
+    _keep_for_stream(stream, x.device, y if own_y else None, ws if own_ws else None)
     st = load().w4a16_linear(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(),
                              M, N, K, GROUP, None if ws is None else ws.data_ptr(), ws_bytes,
                              _stream(stream, x.device))
@@ -295,12 +322,14 @@ def w4a16_gate_up_swiglu(x, gate, up, h=None, split_k: int = 0, workspace=None, 
     """Fused gate / up projections with SwiGLU: ``h = silu(x . Wg^T) * (x . Wu^T)`` in one tile
     kernel.  ``gate`` and ``up`` are ``(wq, scales, biases)`` triples of one shape.  Returns h."""
     (wg, sg, bg), (wu, su, bu) = gate, up
+    own_h, own_ws = h is None, workspace is None
     M, N, K, h = _operands(x, wg, sg, bg, h)
     if tuple(wu.shape) != tuple(wg.shape) or tuple(su.shape) != tuple(sg.shape) or tuple(bu.shape) != tuple(bg.shape):
         raise ValueError("gate and up weights must have the same shapes")
     _operands(x, wu, su, bu, h)                      # same dtype / device / contiguity checks for up
     need = w4a16_gate_up_plan(M, N, K, GROUP, split_k)["workspace_bytes"]
     ws, ws_bytes = _workspace(workspace, need, x.device)
+    _keep_for_stream(stream, x.device, h if own_h else None, ws if own_ws else None)
     st = load().w4a16_gate_up_swiglu(x.data_ptr(), wg.data_ptr(), sg.data_ptr(), bg.data_ptr(), wu.data_ptr(),
                                      su.data_ptr(), bu.data_ptr(), h.data_ptr(), M, N, K, GROUP, split_k,
                                      None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream, x.device))
@@ -320,12 +349,14 @@ def w4a8_quantize_rows(x, xq=None, sx=None, xsum=None, stream=None):
     KB = w4a8_xsum_cols(K)
     if KB == 0:
         raise ValueError(f"K={K} must be a positive multiple of {GROUP}")
+    own = [t is None for t in (xq, sx, xsum)]
     xq = torch.empty((M, K), dtype=torch.int8, device=x.device) if xq is None else xq
     sx = torch.empty((M,), dtype=torch.float32, device=x.device) if sx is None else sx
     xsum = torch.empty((M, KB), dtype=torch.bfloat16, device=x.device) if xsum is None else xsum
     _check(xq, "xq", torch.int8, (M, K))
     _check(sx, "sx", torch.float32, (M,))
     _check(xsum, "xsum", torch.bfloat16, (M, KB))
+    _keep_for_stream(stream, x.device, *[t for t, o in zip((xq, sx, xsum), own) if o])
     st = load().w4a8_quantize_rows(x.data_ptr(), xq.data_ptr(), sx.data_ptr(), xsum.data_ptr(), M, K, GROUP,
                                    _stream(stream, x.device))
     _raise_for(st, "w4a8_quantize_rows")
@@ -348,11 +379,13 @@ def qmm_w4a8(xq, sx, xsum, wq, scales, biases, y=None, split_k: int = 0, workspa
     _check(wq, "wq", torch.int32, (N, K // 8))
     _check(scales, "scales", torch.bfloat16, (N, K // GROUP))
     _check(biases, "biases", torch.bfloat16, (N, K // GROUP))
+    own_y, own_ws = y is None, workspace is None
     if y is None:
         y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
     _check(y, "y", torch.bfloat16, (M, N))
     need = w4a8_plan(M, N, K, GROUP, split_k)["workspace_bytes"]
     ws, ws_bytes = _workspace(workspace, need, xq.device)
+    _keep_for_stream(stream, xq.device, y if own_y else None, ws if own_ws else None)
     st = load().qmm_w4a8(xq.data_ptr(), sx.data_ptr(), xsum.data_ptr(), wq.data_ptr(), scales.data_ptr(),
                          biases.data_ptr(), y.data_ptr(), M, N, K, GROUP, split_k,
                          None if ws is None else ws.data_ptr(), ws_bytes, _stream(stream, xq.device))
@@ -363,8 +396,10 @@ def qmm_w4a8(xq, sx, xsum, wq, scales, biases, y=None, split_k: int = 0, workspa
 def w4a8_linear(x, wq, scales, biases, y=None, workspace=None, stream=None):
     """One-call W4A8 projection of bf16 ``x``: per-row int8 quantization into the workspace, then
     the int8 tile path under the policy.  Returns y."""
+    own_y, own_ws = y is None, workspace is None
     M, N, K, y = _operands(x, wq, scales, biases, y)
     ws, ws_bytes = _workspace(workspace, w4a8_linear_workspace_bytes(M, N, K), x.device)
+    _keep_for_stream(stream, x.device, y if own_y else None, ws if own_ws else None)
     st = load().w4a8_linear(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(), y.data_ptr(),
                             M, N, K, GROUP, None if ws is None else ws.data_ptr(), ws_bytes,
                             _stream(stream, x.device))

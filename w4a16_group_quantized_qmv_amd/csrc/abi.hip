@@ -57,10 +57,24 @@ int check_shape(int64_t M, int64_t N, int64_t K, int32_t group) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-int check_buffers(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b, const uint16_t* y) {
+// Byte ranges [p, p + n) of two buffers share at least one byte.
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
+}
+
+// Pointer checks of a projection y [M, N] = x [M, K] . dequant(wq [N, K * bits / 32])^T (shape
+// already validated): non-null, aligned, and the output sharing no byte with an input.
+int check_buffers(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b, const uint16_t* y,
+                  int64_t M, int64_t N, int64_t K, int32_t bits = 4) {
     if (!x || !wq || !s || !b || !y) return W4A16_ERR_NULL;
     if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(s, 2) || !aligned(b, 2) || !aligned(y, 2))
         return W4A16_ERR_ALIGN;
+    const uint64_t ny = static_cast<uint64_t>(M) * N * 2, sb = static_cast<uint64_t>(N) * (K / W4A16_GROUP) * 2;
+    if (overlaps(y, ny, x, static_cast<uint64_t>(M) * K * 2) ||
+        overlaps(y, ny, wq, static_cast<uint64_t>(N) * K * bits / 8) || overlaps(y, ny, s, sb) ||
+        overlaps(y, ny, b, sb))
+        return W4A16_ERR_OVERLAP;
     return W4A16_OK;
 }
 
@@ -299,7 +313,7 @@ int run_qmm(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint
             void* stream) {
     int st = check_shape(M, N, K, group);
     if (st != W4A16_OK) return st;
-    st = check_buffers(x, wq, s, b, y);
+    st = check_buffers(x, wq, s, b, y, M, N, K);
     if (st != W4A16_OK) return st;
     if (split_k < 0) return W4A16_ERR_SHAPE;
     w4a16_plan_t p;
@@ -382,9 +396,9 @@ int run_gate_up(const uint16_t* x, const uint32_t* wq_g, const uint16_t* s_g, co
                 int64_t K, int32_t group, int32_t split_k, void* workspace, size_t ws_bytes, void* stream) {
     int st = check_shape(M, N, K, group);
     if (st != W4A16_OK) return st;
-    st = check_buffers(x, wq_g, s_g, b_g, h);
+    st = check_buffers(x, wq_g, s_g, b_g, h, M, N, K);
     if (st != W4A16_OK) return st;
-    st = check_buffers(x, wq_u, s_u, b_u, h);
+    st = check_buffers(x, wq_u, s_u, b_u, h, M, N, K);
     if (st != W4A16_OK) return st;
     if (split_k < 0) return W4A16_ERR_SHAPE;
     w4a16_plan_t p;
@@ -461,7 +475,8 @@ int run_qmv_affine(const uint16_t* x, const uint32_t* wq, const uint16_t* s, con
                    int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, int32_t mode, void* stream) {
     int st = check_shape(M, N, K, group);
     if (st != W4A16_OK) return st;
-    st = check_buffers(x, wq, s, b, y);
+    if (!bits_ok(bits)) return W4A16_ERR_UNSUPPORTED;
+    st = check_buffers(x, wq, s, b, y, M, N, K, bits);
     if (st != W4A16_OK) return st;
     w4a16_plan_t p;
     st = plan_qmv_affine(M, N, K, group, bits, mode, 0, &p);
@@ -534,6 +549,12 @@ int run_quantize_rows(const uint16_t* x, int8_t* xq, float* sx, uint16_t* xsum, 
     if (st != W4A16_OK) return st;
     if (!x || !xq || !sx || !xsum) return W4A16_ERR_NULL;
     if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(sx, 4) || !aligned(xsum, 16)) return W4A16_ERR_ALIGN;
+    const uint64_t nx = static_cast<uint64_t>(M) * K * 2, nq = static_cast<uint64_t>(M) * K,
+                   ns = static_cast<uint64_t>(M) * 4,
+                   nk = static_cast<uint64_t>(M) * w4a8_xsum_cols(static_cast<int>(K)) * 2;
+    if (overlaps(x, nx, xq, nq) || overlaps(x, nx, sx, ns) || overlaps(x, nx, xsum, nk) || overlaps(xq, nq, sx, ns) ||
+        overlaps(xq, nq, xsum, nk) || overlaps(sx, ns, xsum, nk))
+        return W4A16_ERR_OVERLAP;
     return to_status(launch_quantize_rows_int8(x, xq, sx, xsum, static_cast<int>(M), static_cast<int>(K),
                                                w4a8_xsum_cols(static_cast<int>(K)), static_cast<hipStream_t>(stream)));
 }
@@ -547,6 +568,13 @@ int run_w4a8(const int8_t* xq, const float* sx, const uint16_t* xsum, const uint
     if (!aligned(xq, 16) || !aligned(sx, 4) || !aligned(xsum, 16) || !aligned(wq, 16) || !aligned(s, 2) ||
         !aligned(b, 2) || !aligned(y, 2))
         return W4A16_ERR_ALIGN;
+    {
+        const uint64_t ny = static_cast<uint64_t>(M) * N * 2, sb = static_cast<uint64_t>(N) * (K / W4A16_GROUP) * 2;
+        if (overlaps(y, ny, xq, static_cast<uint64_t>(M) * K) || overlaps(y, ny, sx, static_cast<uint64_t>(M) * 4) ||
+            overlaps(y, ny, xsum, static_cast<uint64_t>(M) * w4a8_xsum_cols(static_cast<int>(K)) * 2) ||
+            overlaps(y, ny, wq, static_cast<uint64_t>(N) * K / 2) || overlaps(y, ny, s, sb) || overlaps(y, ny, b, sb))
+            return W4A16_ERR_OVERLAP;
+    }
     if (split_k < 0) return W4A16_ERR_SHAPE;
     w4a16_plan_t p;
     st = make_w4a8_plan(M, N, K, group, split_k, 0, &p);
@@ -572,7 +600,7 @@ int run_w4a8_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* s, co
                     int64_t M, int64_t N, int64_t K, int32_t group, void* workspace, size_t ws_bytes, void* stream) {
     int st = check_shape(M, N, K, group);
     if (st != W4A16_OK) return st;
-    st = check_buffers(x, wq, s, b, y);
+    st = check_buffers(x, wq, s, b, y, M, N, K);
     if (st != W4A16_OK) return st;
     if (!workspace) return W4A16_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return W4A16_ERR_ALIGN;
@@ -604,6 +632,7 @@ const char* w4a16_status_string(int status) {
         case W4A16_ERR_UNSUPPORTED: return "W4A16_ERR_UNSUPPORTED";
         case W4A16_ERR_LAUNCH: return "W4A16_ERR_LAUNCH";
         case W4A16_ERR_DEVICE: return "W4A16_ERR_DEVICE";
+        case W4A16_ERR_OVERLAP: return "W4A16_ERR_OVERLAP";
         default: return "unknown";
     }
 }
@@ -623,7 +652,7 @@ int qmv_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, con
               int64_t M, int64_t N, int64_t K, int32_t group, void* stream) {
     int st = check_shape(M, N, K, group);
     if (st != W4A16_OK) return st;
-    st = check_buffers(x, wq, scales, biases, y);
+    st = check_buffers(x, wq, scales, biases, y, M, N, K);
     if (st != W4A16_OK) return st;
     if (M > kQmvMaxRows) return W4A16_ERR_UNSUPPORTED;
     w4a16_plan_t p;
