@@ -164,6 +164,25 @@ int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, 
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free variant of w4a16_linear, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same dispatch
+ * and arguments as w4a16_linear, without a workspace argument, plus split_k as for qmm_w4a16
+ * (0 = policy, 1 = off, S > 1 = forced).  The split-K partials and the exact-code form's group
+ * sums live in a device array of W4A16_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * kept until the process ends; the call allocates nothing and calls no allocating routine.
+ * Under the policy the plan is fitted to that scratch exactly as w4a16_linear fits it to a short
+ * workspace (same result); a forced split_k whose partials (S * M * N * 4 bytes) exceed it returns
+ * W4A16_ERR_WORKSPACE.  The first call on a device resolves that device's scratch address
+ * (W4A16_ERR_DEVICE if it cannot).  The scratch keeps the last call's contents; every value a
+ * call reads from it is written earlier in the same call, so nothing needs clearing.  Calls that
+ * overlap on one GPU (concurrent streams or host threads) share the scratch and race: the
+ * caller must order them.  Other preconditions and errors as w4a16_linear.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (32u << 20)
+int w4a16_linear_noalloc(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                         uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, void* stream);
+
+/*
  * Fused gate / up projection pair with SwiGLU (the SwiGLU fused into the mat-mat, and gate / up
  * computed together with the GLU in the mat-mat epilogue, named by "Feature Request: Metal
  * prefill speedup (~68%) on M5 Max": feature list and Related work):

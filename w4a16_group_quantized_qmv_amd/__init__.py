@@ -29,7 +29,7 @@ import re
 __all__ = [
     "W4A16_OK", "PATH_AUTO", "PATH_QMV", "PATH_QMM", "PATH_SKINNY", "PATH_GATE_UP", "GROUP",
     "load", "lib_path", "w4a16_abi_version", "w4a16_status_string", "w4a16_plan", "w4a16_workspace_bytes",
-    "qmv_w4a16", "qmm_w4a16", "w4a16_linear", "linear", "W4A16Error", "declared_symbols", "PreparedLinear",
+    "qmv_w4a16", "qmm_w4a16", "w4a16_linear", "w4a16_linear_noalloc", "NOALLOC_SCRATCH_BYTES", "linear", "W4A16Error", "declared_symbols", "PreparedLinear",
     "w4a16_gate_up_plan", "w4a16_gate_up_swiglu", "PreparedGateUp",
     "qmv_affine", "qmv_affine_plan", "QMV_POLICY", "QMV_AMORTIZED", "QMV_PER_ROW", "QMV_FAMILIES", "BITS",
     "PATH_W4A8", "w4a8_xsum_cols", "w4a8_quantize_rows", "w4a8_plan", "qmm_w4a8", "w4a8_linear_workspace_bytes",
@@ -88,6 +88,8 @@ def load():
     lib.qmm_w4a16.argtypes = [u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, i32, vp, ctypes.c_size_t, vp]
     lib.w4a16_linear.restype = ctypes.c_int
     lib.w4a16_linear.argtypes = [u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, vp, ctypes.c_size_t, vp]
+    lib.w4a16_linear_noalloc.restype = ctypes.c_int
+    lib.w4a16_linear_noalloc.argtypes = [u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, i32, vp]
     lib.w4a16_gate_up_plan.restype = ctypes.c_int
     lib.w4a16_gate_up_plan.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.POINTER(Plan)]
     lib.w4a16_gate_up_swiglu.restype = ctypes.c_int
@@ -315,6 +317,22 @@ def w4a16_linear(x, wq, scales, biases, y=None, workspace=None, stream=None):
                              M, N, K, GROUP, None if ws is None else ws.data_ptr(), ws_bytes,
                              _stream(stream, x.device))
     _raise_for(st, "w4a16_linear")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def w4a16_linear_noalloc(x, wq, scales, biases, y, split_k: int = 0, stream=None):
+    """``w4a16_linear`` with its workspace in the library's own device scratch (no allocation in
+    the call; ``y`` must be given).  ``split_k`` as for ``qmm_w4a16``.  Calls that overlap on one
+    GPU share the scratch and must be ordered by the caller.  Returns y."""
+    if y is None:
+        raise ValueError("w4a16_linear_noalloc writes into a caller-provided y")
+    M, N, K, y = _operands(x, wq, scales, biases, y)
+    st = load().w4a16_linear_noalloc(x.data_ptr(), wq.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                                     y.data_ptr(), M, N, K, GROUP, split_k, _stream(stream, x.device))
+    _raise_for(st, "w4a16_linear_noalloc")
     return y
 
 

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 
 #include "internal.h"
@@ -615,6 +616,47 @@ int run_w4a8_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* s, co
     return run_w4a8(xq, sx, xsum, wq, s, b, y, M, N, K, group, 0, base + a.total, ws_bytes - a.total, stream);
 }
 
+// Device scratch of w4a16_linear_noalloc (for callers that cannot allocate): the exact-code
+// form's activation group sums and the split-K partials of its plans.  Every GPU the library runs
+// on holds its own copy until the process ends.  In host code `scratch` only names the symbol;
+// its device address, per device, comes from hipGetSymbolAddress (g_scratch below).
+constexpr size_t kScratchBytes = W4A16_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch[64];   // device address of `scratch` per device, set on the first call there
+
+// The current device's address of `scratch`, resolved once per device with that device current.
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return W4A16_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return W4A16_ERR_DEVICE;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return W4A16_OK;
+}
+
+// w4a16_linear with its workspace in `scratch`: the policy plan is fitted to the scratch (no
+// exact-code form, then no split, when it needs more; same result), a forced split whose
+// partials do not fit is rejected.  Nothing here allocates; every partial and group sum a launch
+// reads is written by an earlier launch of the same call, so the scratch needs no clearing.
+int run_linear_noalloc(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b, uint16_t* y,
+                       int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, void* stream) {
+    int st = check_shape(M, N, K, group);
+    if (st != W4A16_OK) return st;
+    st = check_buffers(x, wq, s, b, y, M, N, K);
+    if (st != W4A16_OK) return st;
+    if (split_k < 0) return W4A16_ERR_SHAPE;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != W4A16_OK) return st;
+    return run_qmm(x, wq, s, b, y, M, N, K, group, W4A16_PATH_AUTO, split_k, ws, kScratchBytes, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -672,6 +714,11 @@ int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, 
                  int64_t M, int64_t N, int64_t K, int32_t group, void* workspace, size_t workspace_bytes,
                  void* stream) {
     return run_qmm(x, wq, scales, biases, y, M, N, K, group, W4A16_PATH_AUTO, 0, workspace, workspace_bytes, stream);
+}
+
+int w4a16_linear_noalloc(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                         uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, void* stream) {
+    return run_linear_noalloc(x, wq, scales, biases, y, M, N, K, group, split_k, stream);
 }
 
 int qmv_affine_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, int32_t mode, int32_t num_cus,
