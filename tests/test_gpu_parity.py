@@ -125,6 +125,43 @@ def test_power_of_two_affine_is_exact(lib, path, N):
     assert np.array_equal(y, synth.to_bf16_bits(((xi @ (q - 8).T) / 64.0).astype(np.float32)))
 
 
+def _exact_case(kind, M, N, K, seed):
+    """Integer inputs whose projection is exact in fp32 and bf16: ``sums`` (s = 1, b = 0, at most 17
+    ones per row: every sum an integer <= 255) or ``pow2`` (s = 2^-6, b = -8 * 2^-6, 32 entries of
+    +-1 per row: every result k / 64 with |k| <= 256)."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, 16, (N, K))
+    xi = np.zeros((M, K), dtype=np.int64)
+    for m in range(M):
+        if kind == "sums":
+            xi[m, rng.choice(K, size=rng.integers(0, 18), replace=False)] = 1
+        else:
+            xi[m, rng.choice(K, size=32, replace=False)] = rng.choice([-1, 1], size=32)
+    G = K // 128
+    s, b = (1.0, 0.0) if kind == "sums" else (2.0 ** -6, -8 * 2.0 ** -6)
+    p = {"x": synth.to_bf16_bits(xi.astype(np.float32)), "wq": synth.pack_codes(q),
+         "scales": synth.const_bf16(s, (N, G)), "biases": synth.const_bf16(b, (N, G)), "M": M, "N": N, "K": K}
+    xf = xi.astype(np.float64)
+    exact = xf @ q.T.astype(np.float64) if kind == "sums" else (xf @ (q - 8).T.astype(np.float64)) / 64.0
+    return p, synth.to_bf16_bits(exact.astype(np.float32))
+
+
+@pytest.mark.parametrize("kind", ["sums", "pow2"])
+@pytest.mark.parametrize("shape", list(synth.LAYER_SHAPES))
+def test_step_tiles_are_bit_exact(lib, shape, kind):
+    """The tiles and splits the 512-row step plans (96 x 128 for gate / up, four-wave 64 x 128 with
+    three slices for o / down, eight-wave 64 x 128 for q and the split k / v) on exact integer and
+    power-of-two cases: the result must equal the exact value bit for bit."""
+    K, N = synth.LAYER_SHAPES[shape]
+    M = 512
+    plan = lib.w4a16_plan(M, N, K)
+    p, expect = _exact_case(kind, M, N, K, seed=1000 + 2 * list(synth.LAYER_SHAPES).index(shape) + (kind == "pow2"))
+    announce(f"step tile {shape} {kind}: plan tile {plan['tile_m']}x{plan['tile_n']} variant {plan['variant']} "
+             f"split {plan['split_k']}")
+    y = run(lib, p, "linear")
+    assert np.array_equal(y, expect), f"{shape} {kind} plan {plan}"
+
+
 @pytest.mark.parametrize("path", ["qmv", "qmm"])
 def test_all_zero_codes(lib, path):
     rng = np.random.default_rng(10)

@@ -10,11 +10,13 @@
 // MI355X design (not the pages' 32x32x32 / 128-thread Apple tile):
 //  * The contraction runs on v_mfma_f32_32x32x16_bf16, the bf16 shape with the higher
 //    sustained rate on gfx950.
-//  * Workgroup tile BM x BN with NW waves; each wave owns NB 32-column blocks for all BM rows,
-//    so each weight is unpacked and dequantized exactly once per workgroup, in registers, by the
-//    wave that consumes it, and every dequantized operand feeds BM / 32 MFMAs.  Weights never
-//    pass through LDS.
-//  * Exact-code form (template CODES > 0, used for the 128-row tiles): instead of dequantizing,
+//  * Workgroup tile BM x BN with NW waves; each wave owns NB 32-column blocks for all BM rows
+//    (with KS = 2 two waves share a strip, each taking half of every group's MFMA sub-steps).
+//    A group's codes for the tile's columns are staged in LDS by direct loads, like the
+//    activations; each wave unpacks and dequantizes only its own columns' codes, in registers,
+//    once per workgroup, and every dequantized operand feeds BM / 32 MFMAs.
+//  * Exact-code form (template CODES > 0, used for the 128-row projection tiles and the 64-row
+//    gate / up tiles): instead of dequantizing,
 //    the wave feeds the raw codes as exact bf16 integers, the matrix core returns each group's
 //    P = sum_k x q in fp32, and the accumulators take acc += s * P once per group; the bias term
 //    sum_g b * X (X = the activations' group sums, from act_group_sums_kernel) is one small MFMA
@@ -39,8 +41,9 @@
 //    only after that barrier.  The weight registers ping-pong between even and odd groups.
 //  * The dequantization of MFMA sub-step t + 1 is issued next to the MFMAs of sub-step t so the
 //    VALU work hides under the matrix core.
-//  * Global loads are 16 bytes per lane: each column's group is 64 contiguous bytes read by its
-//    two lanes; the activation tile is read row-contiguously.
+//  * Code and activation loads are 16 bytes per lane: a column's group is 64 contiguous bytes
+//    read by four lanes, the activation tile row-contiguously.  Scales and biases come as one
+//    bf16 per column and group, or (SBQ = 4) four consecutive groups in one 8-byte load.
 //  * Tile order: workgroup i runs on XCD i % 8; the remap below hands each XCD a contiguous run
 //    of work indices, and work indices walk the tile grid in bands of up to 8 M-tiles, N-tile by
 //    N-tile, so the workgroups resident on one XCD share activation rows and weight columns in
@@ -540,27 +543,32 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
         static_assert(WN * HALF * J * 64 * 4 <= TILE * 2, "partial sums fit one activation stage");
         float* mine = reinterpret_cast<float*>(kh == 0 ? xs0 : xs1) + wn * HALF * J * 64;
         const float* theirs = reinterpret_cast<const float*>(kh == 0 ? xs1 : xs0) + wn * HALF * J * 64;
-        // element indices stay compile-time constants (a runtime index would move acc to scratch)
-        auto exchange = [&](auto khc) {
-            constexpr int KH = decltype(khc)::value;
+        // element indices stay compile-time constants (a runtime index would move acc to scratch);
+        // the barrier between handing over and adding sits outside the K-half branches, so every
+        // wave of the workgroup reaches the same one
+        auto hand_over = [&](auto khc) {
+            constexpr int off = decltype(khc)::value == 0 ? HALF : 0;   // the partner's elements
 #pragma unroll
-            for (int e = 0; e < HALF; ++e) {
-                constexpr int off = KH == 0 ? HALF : 0;   // the partner's elements
+            for (int e = 0; e < HALF; ++e)
 #pragma unroll
                 for (int j = 0; j < J; ++j) mine[(e * J + j) * 64 + lane] = acc[(e + off) >> 4][j][(e + off) & 15];
-            }
-            __syncthreads();
+        };
+        auto add_partner = [&](auto khc) {
+            constexpr int off = decltype(khc)::value == 0 ? 0 : HALF;   // this wave's elements
 #pragma unroll
-            for (int e = 0; e < HALF; ++e) {
-                constexpr int off = KH == 0 ? 0 : HALF;   // this wave's elements
+            for (int e = 0; e < HALF; ++e)
 #pragma unroll
                 for (int j = 0; j < J; ++j) acc[(e + off) >> 4][j][(e + off) & 15] += theirs[(e * J + j) * 64 + lane];
-            }
         };
         if (kh == 0)
-            exchange(std::integral_constant<int, 0>{});
+            hand_over(std::integral_constant<int, 0>{});
         else
-            exchange(std::integral_constant<int, 1>{});
+            hand_over(std::integral_constant<int, 1>{});
+        __syncthreads();
+        if (kh == 0)
+            add_partner(std::integral_constant<int, 0>{});
+        else
+            add_partner(std::integral_constant<int, 1>{});
     }
 
     // epilogue: D layout puts rows 8 * (r / 4) + 4 * half + r % 4 of column lane % 32 in this lane
@@ -660,10 +668,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 
 const QmmShape kQmmVariants[kNumQmmVariants] = {
     {128, 1, 4, 2},  // 0: 128 x 128 tile, 4 waves of 128 x 32, two waves per SIMD, 2 stages
-    {64, 1, 4, 2},   // 1:  64 x 128 tile, 4 waves of  64 x 32, four waves per SIMD, 2 stages
+    {64, 1, 4, 2},   // 1:  64 x 128 tile, 4 waves of  64 x 32, three waves per SIMD (48 KB of LDS
+                     //     per workgroup: three resident per compute unit), 2 stages
     {64, 1, 4, 3},   // 2:  64 x 128 tile, two waves per SIMD, 3 stages
     {32, 1, 4, 2},   // 3:  32 x 128 tile, 4 waves of 32 x 32, four waves per SIMD, 2 stages
-    {32, 1, 4, 3},   // 4:  32 x 128 tile, four waves per SIMD, 3 stages (skinny M)
+    {32, 1, 4, 3},   // 4:  32 x 128 tile, three waves per SIMD (48 KB of LDS), 3 stages (skinny M)
     {64, 1, 8, 2, 2},  // 5:  64 x 128 tile, 8 waves: two per 32-column strip, each taking half of
                        //     every group's sub-steps; six waves per SIMD
     {96, 1, 8, 2, 2},  // 6:  96 x 128 tile, 8 waves as variant 5; four waves per SIMD (two tiles)
@@ -759,11 +768,11 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, cons
     // the exact-code mode is compiled for the 128-row tiles, where it measured faster
     if (xsum && variant != kQmmCodesTileVariant) return hipErrorInvalidValue;
     switch (variant) {
-        case 0: return launch_qmm_t<128, 1, 4, 2, 2, 2>(x, xsum, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 1: return launch_qmm_t<64, 1, 4, 4, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 0: return launch_qmm_t<128, 1, 4, 2, 2, 1>(x, xsum, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 1: return launch_qmm_t<64, 1, 4, 3, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
         case 2: return launch_qmm_t<64, 1, 4, 2, 3>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
         case 3: return launch_qmm_t<32, 1, 4, 4, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 4: return launch_qmm_t<32, 1, 4, 4, 3>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
+        case 4: return launch_qmm_t<32, 1, 4, 3, 3>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
         case 5: return launch_qmm_t<64, 1, 8, 6, 2, 0, 6, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split,
                                                            stream);
         case 6: return launch_qmm_t<96, 1, 8, 4, 2, 0, 4, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split,
@@ -773,8 +782,9 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, cons
 }
 
 const QmmShape kGateUpVariants[kNumGateUpVariants] = {
-    {32, 1, 4, 2},   // 0:  32 x 128 tile of h (gate and up: 2 x 32 columns per wave), four waves per SIMD
-    {64, 1, 4, 2},   // 1:  64 x 128 tile of h, three waves per SIMD (two in the exact-code mode)
+    {32, 1, 4, 2},   // 0:  32 x 128 tile of h (gate and up: 2 x 32 columns per wave), three waves per
+                     //     SIMD (48 KB of LDS per workgroup)
+    {64, 1, 4, 2},   // 1:  64 x 128 tile of h, two waves per SIMD (64 KB of LDS per workgroup)
     {128, 1, 4, 2},  // 2: 128 x 128 tile of h, one wave per SIMD
     {96, 1, 4, 2},   // 3:  96 x 128 tile of h, two waves per SIMD
 };
@@ -786,9 +796,9 @@ hipError_t launch_gate_up(int variant, const uint16_t* x, const uint16_t* xsum, 
     const int KB = group_sum_cols(K);
     if (xsum && variant != kGateUpCodesTileVariant) return hipErrorInvalidValue;
     switch (variant) {
-        case 0: return launch_gate_up_t<32, 4, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K,
+        case 0: return launch_gate_up_t<32, 3, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K,
                                                   split, stream);
-        case 1: return launch_gate_up_t<64, 3, 2, 1, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K,
+        case 1: return launch_gate_up_t<64, 2, 2, 1, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N, K,
                                                   split, stream);
         case 2: return launch_gate_up_t<128, 1, 2>(x, xsum, KB, wq_gate, s_gate, b_gate, wq_up, s_up, b_up, h, ws, M, N,
                                                    K, split, stream);

@@ -385,16 +385,19 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
         float* mine1 = reinterpret_cast<float*>(kh == 0 ? cs0 : cs1) + wn * CH * 64;
         const float* theirs0 = reinterpret_cast<const float*>(kh == 0 ? xs1 : xs0) + wn * CH * 64;
         const float* theirs1 = reinterpret_cast<const float*>(kh == 0 ? cs1 : cs0) + wn * CH * 64;
-        // element indices stay compile-time constants (a runtime index would move acc to scratch)
-        auto exchange = [&](auto khc) {
-            constexpr int KH = decltype(khc)::value;
-            constexpr int give = KH == 0 ? HALF : 0, keep = KH == 0 ? 0 : HALF;
+        // element indices stay compile-time constants (a runtime index would move acc to scratch);
+        // the barrier between handing over and adding sits outside the K-half branches, so every
+        // wave of the workgroup reaches the same one
+        auto hand_over = [&](auto khc) {
+            constexpr int give = decltype(khc)::value == 0 ? HALF : 0;
 #pragma unroll
             for (int e = 0; e < HALF; ++e) {
                 float* dst = e < CH ? mine0 : mine1;
                 dst[(e % CH) * 64 + lane] = acc[(e + give) >> 4][(e + give) & 15];
             }
-            __syncthreads();
+        };
+        auto add_partner = [&](auto khc) {
+            constexpr int keep = decltype(khc)::value == 0 ? 0 : HALF;
 #pragma unroll
             for (int e = 0; e < HALF; ++e) {
                 const float* src = e < CH ? theirs0 : theirs1;
@@ -402,9 +405,14 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
             }
         };
         if (kh == 0)
-            exchange(std::integral_constant<int, 0>{});
+            hand_over(std::integral_constant<int, 0>{});
         else
-            exchange(std::integral_constant<int, 1>{});
+            hand_over(std::integral_constant<int, 1>{});
+        __syncthreads();
+        if (kh == 0)
+            add_partner(std::integral_constant<int, 0>{});
+        else
+            add_partner(std::integral_constant<int, 1>{});
     }
 
     // epilogue: y = sx[m] * acc; D layout puts rows 8 (r / 4) + 4 half + r % 4 of column
