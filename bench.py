@@ -14,7 +14,13 @@ W ~ N(0, 0.02) quantized to 4-bit affine groups of 128.
 All inputs are resident in HBM before the timed region.  Weight sets rotate over several
 device copies so that weight reads miss the 256 MB last-level cache.  Output: one JSON line.
 
-    python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu-baseline] [--no-next-rows]
+
+Besides the step's throughput the line carries: the dominant kernel's roofline (HIP events
+around each of its launches in the timed region), the same run's measured ceilings (torch's
+bf16 GEMM through hipBLASLt on the same shapes, and device copy / read rates), every timed
+shape's fraction of the roof that binds it (min(MFMA peak, arithmetic intensity x HBM
+bandwidth)), and the CPU oracle on a bounded sample of the step.
 """
 
 from __future__ import annotations
@@ -47,6 +53,17 @@ def flops(M, N, K):
 def algo_bytes(M, N, K):
     """Algorithmic bytes: packed codes + bf16 scale and bias per group + x + y."""
     return N * K / 2 + N * K / 32 + 2.0 * M * K + 2.0 * M * N
+
+
+def roof(M, N, K, achieved_tflops):
+    """Roofline of one projection: arithmetic intensity (flop per algorithmic byte), the roof that
+    binds it (MFMA peak or AI x HBM bandwidth, whichever is lower) and the achieved fraction."""
+    ai = flops(M, N, K) / algo_bytes(M, N, K)
+    hbm_roof = ai * PEAK_HBM_GBPS / 1e3          # TFLOP/s that HBM can feed at this intensity
+    bound = "mfma" if PEAK_BF16_TFLOPS <= hbm_roof else "hbm"
+    r = min(PEAK_BF16_TFLOPS, hbm_roof)
+    return {"AI": round(ai, 1), "bound": bound, "roof_TFLOP/s": round(r, 1),
+            "roofline_frac": round(achieved_tflops / r, 4)}
 
 
 def kernel_source_hash() -> str:
@@ -104,29 +121,130 @@ def build_inputs(torch, copies):
 VOCAB_SAMPLE_COLS = 151936 // 4
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(projections):
     """The oracle, untuned, on a bounded sample of one step: the seven 512-row projections in
-    full and the last vocab row over the first quarter of the vocabulary columns."""
+    full and the last vocab row over the first quarter of the vocabulary columns.  Timed: the
+    oracle's definition of the projection -- unpack, fp32 dequantization (``dequant_f32``) and
+    the fp64 GEMM ``x64 @ w64.T`` over the same column chunks as ``reference`` -- without the
+    absolute-mass GEMM that ``reference`` adds for the tolerance, so the rate counts the one
+    GEMM that is timed."""
+    import numpy as np
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        blas_threads = None
+    affinity = len(os.sched_getaffinity(0))
     total_flops = 0.0
     t0 = time.perf_counter()
     for p in projections:
         h = p["host"]
         x = h["x"][-p["keep"]:] if p["keep"] else h["x"]
         n = p["N"] if not p["keep"] else VOCAB_SAMPLE_COLS
-        O.reference(x, h["wq"][:n], h["scales"][:n], h["biases"][:n])
+        x64 = O.bf16_to_f64(x)
+        for c0 in range(0, n, 8192):
+            c1 = min(n, c0 + 8192)
+            w64 = O.dequant_f32(h["wq"][c0:c1], h["scales"][c0:c1], h["biases"][c0:c1], p["K"]).astype(np.float64)
+            _ = x64 @ w64.T
         total_flops += flops(x.shape[0], n, p["K"])
     dt = time.perf_counter() - t0
-    return {"value": total_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": total_flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads or affinity),
+            "kind": "oracle",
             "sample": "the seven 512-row layer projections in full and the last vocab row over the first "
-                      f"{VOCAB_SAMPLE_COLS} of 151936 columns: unpack + fp32 dequant + fp64 GEMM "
-                      "(reference() including the abs-mass), wall clock, rate scaled to the sample's FLOPs",
-            "seconds": dt}
+                      f"{VOCAB_SAMPLE_COLS} of 151936 columns: the oracle's unpack + fp32 dequant + fp64 GEMM "
+                      "(dequant_f32, x64 @ w64.T in 8192-column chunks), wall clock, rate = sample FLOPs / time",
+            "seconds": round(dt, 3), "cpu_model": cpu_model(), "affinity_cores": affinity,
+            "blas_threads": blas_threads}
+
+
+READ_FLOOR_SHAPES = ((1024, 2560), (4096, 2560), (9728, 2560), (151936, 2560))
+
+
+def read_floor_key(N, K):
+    """The measured read floor that stands for a matvec shape (the transposed 13 MB shape shares
+    its partner's)."""
+    return f"read_{max(N, K)}x{min(N, K)}_us" if N * K == 9728 * 2560 else f"read_{N}x{K}_us"
+
+
+def measured_ceilings(torch, reps=50):
+    """This run's own denominators on the same GPU: torch's bf16 GEMM (hipBLASLt) on the gate
+    shape (K = 2560, N = 9728) at 512 and 4096 rows, a 1 GiB device-to-device copy (read +
+    write) and a 1 GiB streaming read (the package's read probe, libw4a16_probe.so: 16-byte
+    non-temporal loads, four in flight per thread, 2048 workgroups)."""
+    import ctypes
+    dev = torch.device("cuda", 0)
+    out = {}
+
+    def timed(fn, n):
+        for _ in range(5):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / n          # us per call
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    for M in (512, 4096):
+        a = torch.randn((M, 2560), generator=g, device=dev).to(torch.bfloat16)
+        w = torch.randn((9728, 2560), generator=g, device=dev).to(torch.bfloat16)
+        us = timed(lambda: torch.nn.functional.linear(a, w), reps)
+        out[f"bf16_gemm_M{M}_TFLOP/s"] = round(flops(M, 9728, 2560) / us / 1e6, 1)
+        del a, w
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    us = timed(lambda: dst.copy_(src), 10)
+    out["copy_GB/s"] = round(2 * (1 << 30) / us / 1e3, 1)
+    probe = ctypes.CDLL(os.path.join(ROOT, "w4a16_group_quantized_qmv_amd", "libw4a16_probe.so"))
+    probe.w4a16_probe_stream_read.restype = ctypes.c_int
+    probe.w4a16_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                              ctypes.c_void_p]
+    blocks = 2048
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    hs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def read():
+        st = probe.w4a16_probe_stream_read(src.data_ptr(), 1 << 30, sink.data_ptr(), blocks, hs)
+        assert st == 0, st
+    us = timed(read, 10)
+    out["read_GB/s"] = round((1 << 30) / us / 1e3, 1)
+    # the same probe over the bytes of each matvec shape (N x K; 2560 x 9728 moves the bytes of
+    # 9728 x 2560 to within 0.1%), each call on the next window of the 1 GiB buffer so that it
+    # comes from HBM, replayed from a HIP graph as the matvec timings are
+    gs = torch.cuda.Stream()
+    with torch.cuda.stream(gs):
+        hg = ctypes.c_void_p(gs.cuda_stream)
+        for name, nbytes in ((f"{N}x{K}", algo_bytes(1, N, K)) for N, K in READ_FLOOR_SHAPES):
+            nb = int(nbytes) // 256 * 256
+            windows = max(2, (1 << 30) // nb)
+            nblk = max(1, min(blocks, -(-nb // (256 * 64))))
+            calls = [lambda off=(i % windows) * nb: probe.w4a16_probe_stream_read(src.data_ptr() + off, nb,
+                                                                                 sink.data_ptr(), nblk, hg)
+                     for i in range(max(20, windows))]
+            us = time_call(torch, calls, len(calls))
+            out[f"read_{name}_us"] = round(us, 3)
+            out[f"read_{name}_GB/s"] = round(nb / us / 1e3, 1)
+    del src, dst, sink
+    torch.cuda.synchronize()
+    out["how"] = ("torch.nn.functional.linear in bf16 (x [M, 2560] by W [9728, 2560]), Tensor.copy_ of 1 GiB, "
+                  "the streaming-read probe over 1 GiB; HIP events, mean over back-to-back calls; read_<size>: the "
+                  "probe over one matvec's algorithmic bytes, graph-replayed over successive windows of 1 GiB")
+    return out
 
 
 def main():
@@ -138,6 +256,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next-rows", action="store_true",
                     help="skip the measurements beyond the step (for profiler runs of the step alone)")
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="only run the decode matvecs (M = 1 and 4 on the four decode shapes, and the vocab "
+                         "head's last row) a few times each with plain launches, for profiler runs, then exit")
+    ap.add_argument("--profile-long", action="store_true",
+                    help="only run the 4096-row gate, up and down projections a few times each with plain "
+                         "launches, for profiler runs, then exit")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured ceilings (torch bf16 GEMM, copy and read rates)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="before the timed region, copy a 256 MiB buffer three times (reference for counter scaling)")
     args = ap.parse_args()
@@ -150,6 +276,12 @@ def main():
     import w4a16_group_quantized_qmv_amd as w4
     w4.load()                                   # raises when the HIP library is not built
     torch.cuda.set_device(0)
+    if args.profile_decode:
+        profile_decode(torch, w4)
+        return
+    if args.profile_long:
+        profile_long(torch, w4)
+        return
     t_gen = time.perf_counter()
     projections = build_inputs(torch, args.copies)
     print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
@@ -169,22 +301,20 @@ def main():
     dom_idx = [j for j, p in enumerate(projections) if p["name"] in DOMINANT]
     assert dom_idx == list(range(dom_idx[0], dom_idx[0] + len(dom_idx))), "dominant projections must be adjacent"
 
-    def step(i, per_call_events=None, dom_events=None):
-        """One pass over the eight projections.  per_call_events brackets every call (breakdown
-        pass); dom_events brackets only the adjacent gate/up launches (timed pass), so the timed
-        stream carries two event records per step instead of sixteen."""
+    def step(i, events=None):
+        """One pass over the eight projections.  ``events`` maps a call's index to its (start,
+        end) HIP events: every call in the breakdown pass, only the gate and up launches in the
+        timed pass."""
         row = calls[i % args.copies]
         for j, call in enumerate(row):
-            if per_call_events is not None:
-                per_call_events[j][0].record()
-            elif dom_events is not None and j == dom_idx[0]:
-                dom_events[0].record()
+            ev = events.get(j) if events is not None else None
+            if ev is not None:
+                ev[0].record()
             call()
-            if per_call_events is not None:
-                per_call_events[j][1].record()
-            elif dom_events is not None and j == dom_idx[-1]:
-                dom_events[1].record()
+            if ev is not None:
+                ev[1].record()
 
+    ceilings = measured_ceilings(torch) if not args.no_ceilings else None
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -196,28 +326,31 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: the steps back to back on one stream, events only around gate/up
+    def event_pair():
+        return [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+
+    # timed region: the steps back to back on one stream, events around each gate and up launch
     n = len(projections)
-    dom_ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
+    dom_ev = [{j: event_pair() for j in dom_idx} for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        step(i, dom_events=dom_ev[i])
+        step(i, dom_ev[i])
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(end)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
-    dom_us = sum(e[0].elapsed_time(e[1]) for e in dom_ev) * 1e3 / (args.steps * len(dom_idx))
+    dom_launch_us = [e[0].elapsed_time(e[1]) * 1e3 for d in dom_ev for e in d.values()]
+    dom_us = sum(dom_launch_us) / len(dom_launch_us)
 
     # breakdown pass (not timed as a whole): events around every call
     bsteps = max(3, min(args.steps, 10))
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(n)]
-          for _ in range(bsteps)]
+    ev = [{j: event_pair() for j in range(n)} for _ in range(bsteps)]
     for i in range(bsteps):
-        step(i, per_call_events=ev[i])
+        step(i, ev[i])
     torch.cuda.synchronize()
     per = []
     for j, p in enumerate(projections):
@@ -229,7 +362,8 @@ def main():
                     "median_us": round(us[len(us) // 2], 3), "TFLOP/s": round(f / avg / 1e6, 2),
                     "GB/s": round(by / avg / 1e3, 1),
                     "path": "qmv" if pl["path"] == 1 else "qmm", "variant": pl["variant"],
-                    "tile": [pl["tile_m"], pl["tile_n"]], "split_k": pl["split_k"]})
+                    "tile": [pl["tile_m"], pl["tile_n"]], "split_k": pl["split_k"],
+                    **roof(p["M"], p["N"], p["K"], f / avg / 1e6)})
     step_flops = sum(flops(p["M"], p["N"], p["K"]) for p in projections)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -252,11 +386,19 @@ def main():
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": dom_flops, "avg_launch_us": round(dom_us, 3),
-                     "timing": "HIP events around the adjacent gate and up launches of every timed step "
-                               "(on the launch stream), divided by the two launches"},
+                     "launches": len(dom_launch_us),
+                     "frac_of_measured_bf16_gemm": (round(achieved / ceilings["bf16_gemm_M512_TFLOP/s"], 4)
+                                                    if ceilings else None),
+                     "timing": "HIP events around each gate and each up launch of every timed step (on the "
+                               "launch stream), mean over those launches"},
+        "measured_ceiling": ceilings,
         "breakdown_timing": "separate pass after the timed region: HIP events around every call",
         "qmv_vocab_last_row": {"GB/s": round(vocab_bytes / vocab["avg_us"] / 1e3, 1),
+                               "frac_of_measured_read_floor": (round(ceilings[read_floor_key(vocab["N"], vocab["K"])]
+                                                                     / vocab["avg_us"], 4) if ceilings else None),
                                "frac_hbm": round(vocab_bytes / vocab["avg_us"] / 1e3 / PEAK_HBM_GBPS, 4),
+                               "frac_of_measured_read": (round(vocab_bytes / vocab["avg_us"] / 1e3 /
+                                                               ceilings["read_GB/s"], 4) if ceilings else None),
                                "avg_us": vocab["avg_us"], "bytes": vocab_bytes},
         "breakdown": per,
         "kernel_source_sha256_16": kernel_source_hash(),
@@ -265,12 +407,75 @@ def main():
         gs = torch.cuda.Stream()         # graph capture needs a stream other than the null stream
         with torch.cuda.stream(gs):
             result["next_rows"] = next_rows(torch, w4, projections, args.copies)
+        if ceilings:
+            for row in result["next_rows"]["decode"]:
+                floor = ceilings.get(read_floor_key(row["N"], row["K"]))
+                row["frac_of_measured_read"] = round(floor / row["avg_us"], 4) if floor else None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(projections)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def profile_decode(torch, w4, calls=5):
+    """The decode matvecs alone, with plain stream launches (no graph), so a profiler attributes
+    kernel durations and counters to each shape by its launch grid: M = 1 and 4 on 2560 -> 9728,
+    9728 -> 2560, 2560 -> 4096, 2560 -> 1024, then the vocabulary head's last row (2560 ->
+    151936, M = 1).  Each shape runs ``calls`` passes over a weight rotation of more than twice
+    the last-level cache, one launch per weight copy, so every launch reads its weights from HBM."""
+    import numpy as np
+    from w4a16_group_quantized_qmv_amd import synth
+    dev = torch.device("cuda", 0)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    cases = [(2, i, K, N) for i, (K, N) in enumerate(synth.DECODE_SHAPES)]
+    cases.append((5, synth.shape_index(5, "vocab"), *synth.VOCAB_SHAPE))
+    for cfg, idx, K, N in cases:
+        wq, s, b = synth.weights(cfg, idx, N, K)
+        rot = rotation((torch.from_numpy(wq.view(np.int32)).to(dev), bf16(s), bf16(b)))
+        for m in ((1, 4) if cfg == 2 else (1,)):
+            x = bf16(synth.activations(cfg, idx, m, K))
+            prepared = [w4.PreparedLinear(x, *w) for w in rot]
+            for _ in range(calls):
+                for call in prepared:
+                    call()
+            torch.cuda.synchronize()
+            plan = prepared[0].plan
+            print(f"[profile-decode] M={m} K={K} N={N} plan variant {plan['variant']} grid {plan['grid_x']} "
+                  f"x {plan['block_threads']} threads, {calls} x {len(rot)} launches", file=sys.stderr, flush=True)
+            del prepared
+        del rot
+        torch.cuda.synchronize()
+
+
+def profile_long(torch, w4, calls=3):
+    """The 4096-row prefill projections alone (gate 2560 -> 9728, up 2560 -> 9728, down 9728 ->
+    2560, the synthetic inputs of the long-prefill workload), each ``calls`` times with plain
+    stream launches, so a profiler attributes kernel durations and counters to each by its grid."""
+    import numpy as np
+    from w4a16_group_quantized_qmv_amd import synth
+    dev = torch.device("cuda", 0)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    for name in ("gate", "up", "down"):
+        idx = synth.shape_index(5, name)
+        K, N = synth.LAYER_SHAPES[name]
+        wq, s, b = synth.weights(5, idx, N, K)
+        x = bf16(synth.activations(5, idx, 4096, K))
+        call = w4.PreparedLinear(x, torch.from_numpy(wq.view(np.int32)).to(dev), bf16(s), bf16(b))
+        for _ in range(calls):
+            call()
+        torch.cuda.synchronize()
+        plan = call.plan
+        print(f"[profile-long] {name} M=4096 K={K} N={N} plan variant {plan['variant']} tile {plan['tile_m']}x"
+              f"{plan['tile_n']} split {plan['split_k']} grid {plan['grid_x']}", file=sys.stderr, flush=True)
+        del call, x
 
 
 def time_call(torch, fns, reps, trials=5):
@@ -418,29 +623,33 @@ def next_rows(torch, w4, projections, copies, reps=20):
         f = flops(4096, p["N"], p["K"])
         long_rows.append({"name": name, "M": 4096, "N": p["N"], "K": p["K"], "tile_m": pl["tile_m"],
                           "exact_codes": pl["variant"] >= 10, "avg_us": round(t, 3),
-                          "TFLOP/s": round(f / t / 1e6, 2), "frac_mfma": round(f / t / 1e6 / PEAK_BF16_TFLOPS, 4)})
+                          "TFLOP/s": round(f / t / 1e6, 2), "frac_mfma": round(f / t / 1e6 / PEAK_BF16_TFLOPS, 4),
+                          **roof(4096, p["N"], p["K"], f / t / 1e6)})
         del fns, rot, y, xl
     out["prefill4096"] = long_rows
 
-    # 128-row prefill: the seven layer projections, each alone
-    short_rows = []
-    for name in LAYER:
-        p = by[name]
-        xs = torch.from_numpy(synth.activations(3, synth.shape_index(3, name), 128, p["K"]).view("int16"))
-        xs = xs.view(torch.bfloat16).to(dev)
-        rot = rotation(p["w"][0])
-        pl = w4.w4a16_plan(128, p["N"], p["K"])
-        y = torch.empty((128, p["N"]), dtype=torch.bfloat16, device=dev)
-        wsb = ws_for(torch, pl["workspace_bytes"], dev)
-        t = timed([w4.PreparedLinear(xs, *w, y=y, workspace=wsb) for w in rot])
-        f = flops(128, p["N"], p["K"])
-        short_rows.append({"name": name, "M": 128, "N": p["N"], "K": p["K"], "tile": [pl["tile_m"], pl["tile_n"]],
-                           "split_k": pl["split_k"], "avg_us": round(t, 3), "TFLOP/s": round(f / t / 1e6, 2),
-                           "frac_mfma": round(f / t / 1e6 / PEAK_BF16_TFLOPS, 4)})
-        del rot, y, xs
-    layer_flops = sum(flops(128, r["N"], r["K"]) for r in short_rows)
-    out["prefill128"] = {"projections": short_rows,
-                         "layer_TFLOP/s": round(layer_flops / sum(r["avg_us"] for r in short_rows) / 1e6, 2)}
+    # 128-row prefill and the ragged 509-row prefill: the seven layer projections, each alone
+    for rows, cfg, key in ((128, 3, "prefill128"), (509, 4, "prefill509")):
+        short_rows = []
+        for name in LAYER:
+            p = by[name]
+            xs = torch.from_numpy(synth.activations(cfg, synth.shape_index(cfg, name), rows, p["K"]).view("int16"))
+            xs = xs.view(torch.bfloat16).to(dev)
+            rot = rotation(p["w"][0])
+            pl = w4.w4a16_plan(rows, p["N"], p["K"])
+            y = torch.empty((rows, p["N"]), dtype=torch.bfloat16, device=dev)
+            wsb = ws_for(torch, pl["workspace_bytes"], dev)
+            t = timed([w4.PreparedLinear(xs, *w, y=y, workspace=wsb) for w in rot])
+            f = flops(rows, p["N"], p["K"])
+            short_rows.append({"name": name, "M": rows, "N": p["N"], "K": p["K"],
+                               "tile": [pl["tile_m"], pl["tile_n"]], "split_k": pl["split_k"],
+                               "avg_us": round(t, 3), "TFLOP/s": round(f / t / 1e6, 2),
+                               "frac_mfma": round(f / t / 1e6 / PEAK_BF16_TFLOPS, 4),
+                               **roof(rows, p["N"], p["K"], f / t / 1e6)})
+            del rot, y, xs
+        layer_flops = sum(flops(rows, r["N"], r["K"]) for r in short_rows)
+        out[key] = {"projections": short_rows,
+                    "layer_TFLOP/s": round(layer_flops / sum(r["avg_us"] for r in short_rows) / 1e6, 2)}
 
     # decode rows on the four decode shapes
     decode = []
@@ -456,7 +665,8 @@ def next_rows(torch, w4, projections, copies, reps=20):
             t = timed([w4.PreparedLinear(xd, *w, y=y) for w in rot])
             b = algo_bytes(m, N, K)
             decode.append({"K": K, "N": N, "M": m, "variant": pl["variant"], "avg_us": round(t, 3),
-                           "GB/s": round(b / t / 1e3, 1), "frac_hbm": round(b / t / 1e3 / PEAK_HBM_GBPS, 4)})
+                           "GB/s": round(b / t / 1e3, 1), "frac_hbm": round(b / t / 1e3 / PEAK_HBM_GBPS, 4),
+                           **roof(m, N, K, flops(m, N, K) / t / 1e6)})
         del rot
     out["decode"] = decode
 

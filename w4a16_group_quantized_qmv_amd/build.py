@@ -40,10 +40,11 @@ def command(out_path: str = LIB_PATH, resource_usage: bool = False) -> list[str]
     return cmd
 
 
-def build(resource_usage: bool = False, verbose: bool = False) -> str:
-    """Compile every HIP source into ``libw4a16.so`` next to this file; returns its path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = command(tmp, resource_usage)
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libw4a16_probe.so")
+PROBE_SOURCES = ["probe.hip"]
+
+
+def _compile(cmd: list[str], tmp: str, out: str, verbose: bool, show: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,9 +52,20 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
     log = "\n".join(line for line in (proc.stdout + proc.stderr).splitlines() if noise not in line)
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{log}")
-    os.replace(tmp, LIB_PATH)
-    if verbose or resource_usage:
+    os.replace(tmp, out)
+    if verbose or show:
         print(log)
+
+
+def build(resource_usage: bool = False, verbose: bool = False) -> str:
+    """Compile every HIP source into ``libw4a16.so`` next to this file, and the benchmark's
+    streaming-read probe into ``libw4a16_probe.so``; returns the library's path."""
+    tmp = LIB_PATH + ".tmp"
+    _compile(command(tmp, resource_usage), tmp, LIB_PATH, verbose, resource_usage)
+    ptmp = PROBE_LIB_PATH + ".tmp"
+    pcmd = command(ptmp)
+    pcmd = pcmd[:pcmd.index(os.path.join(CSRC, SOURCES[0]))] + [os.path.join(CSRC, s) for s in PROBE_SOURCES]
+    _compile(pcmd, ptmp, PROBE_LIB_PATH, verbose, False)
     return LIB_PATH
 
 
