@@ -301,18 +301,18 @@ def main():
     dom_idx = [j for j, p in enumerate(projections) if p["name"] in DOMINANT]
     assert dom_idx == list(range(dom_idx[0], dom_idx[0] + len(dom_idx))), "dominant projections must be adjacent"
 
-    def step(i, events=None):
-        """One pass over the eight projections.  ``events`` maps a call's index to its (start,
-        end) HIP events: every call in the breakdown pass, only the gate and up launches in the
-        timed pass."""
+    def step(i, starts=None, ends=None):
+        """One pass over the eight projections.  ``starts`` / ``ends`` map a call's index to a HIP
+        event recorded just before / after it: every call in the breakdown pass; in the timed pass
+        one event before the gate launch and one after the up launch that follows it, so that no
+        event sits between the two dominant launches."""
         row = calls[i % args.copies]
         for j, call in enumerate(row):
-            ev = events.get(j) if events is not None else None
-            if ev is not None:
-                ev[0].record()
+            if starts is not None and j in starts:
+                starts[j].record()
             call()
-            if ev is not None:
-                ev[1].record()
+            if ends is not None and j in ends:
+                ends[j].record()
 
     ceilings = measured_ceilings(torch) if not args.no_ceilings else None
     if args.calibrate_copy:
@@ -331,26 +331,26 @@ def main():
 
     # timed region: the steps back to back on one stream, events around each gate and up launch
     n = len(projections)
-    dom_ev = [{j: event_pair() for j in dom_idx} for _ in range(args.steps)]
+    dom_ev = [event_pair() for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        step(i, dom_ev[i])
+        step(i, {dom_idx[0]: dom_ev[i][0]}, {dom_idx[-1]: dom_ev[i][1]})
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(end)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
-    dom_launch_us = [e[0].elapsed_time(e[1]) * 1e3 for d in dom_ev for e in d.values()]
+    dom_launch_us = [e[0].elapsed_time(e[1]) * 1e3 / len(dom_idx) for e in dom_ev]
     dom_us = sum(dom_launch_us) / len(dom_launch_us)
 
     # breakdown pass (not timed as a whole): events around every call
     bsteps = max(3, min(args.steps, 10))
     ev = [{j: event_pair() for j in range(n)} for _ in range(bsteps)]
     for i in range(bsteps):
-        step(i, ev[i])
+        step(i, {j: e[0] for j, e in ev[i].items()}, {j: e[1] for j, e in ev[i].items()})
     torch.cuda.synchronize()
     per = []
     for j, p in enumerate(projections):
@@ -386,11 +386,12 @@ def main():
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": dom_flops, "avg_launch_us": round(dom_us, 3),
-                     "launches": len(dom_launch_us),
+                     "launches": len(dom_launch_us) * len(dom_idx),
                      "frac_of_measured_bf16_gemm": (round(achieved / ceilings["bf16_gemm_M512_TFLOP/s"], 4)
                                                     if ceilings else None),
-                     "timing": "HIP events around each gate and each up launch of every timed step (on the "
-                               "launch stream), mean over those launches"},
+                     "timing": "HIP events on the launch stream before each timed step's gate launch and after "
+                               "the up launch that follows it (no event between the two), elapsed / 2, mean over "
+                               "the timed steps"},
         "measured_ceiling": ceilings,
         "breakdown_timing": "separate pass after the timed region: HIP events around every call",
         "qmv_vocab_last_row": {"GB/s": round(vocab_bytes / vocab["avg_us"] / 1e3, 1),
