@@ -3,7 +3,8 @@
 
 One step is one 512-token prefill pass through the projections of one decoder layer
 (hidden 2560, 32 query heads and 8 key/value heads of dimension 128, MLP 9728: q, k, v, o,
-gate, up, down at M = 512, where the down projection's K = 9728 exercises split-K), followed
+gate, up, down at M = 512, where the down projection's K = 9728 exercises split-K; q, k and v
+read the same input and run as one grouped launch, gate and up read the same input), followed
 by the vocabulary head (2560 -> 151936) applied to the last row only (logits_to_keep = 1,
 which dispatches to the matvec path).  These are the per-projection prefill shapes that
 tiny-llm's "Week 2 Day 6: SIMD-Matrix Prefill" benchmarks in Task 5 and its Benchmark
@@ -42,6 +43,8 @@ PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA
 M_PREFILL = 512
 LAYER = ["q", "k", "v", "o", "gate", "up", "down"]
 DOMINANT = ("gate", "up")     # largest projections: the roofline kernel
+INPUT_OF = {"k": "q", "v": "q", "up": "gate"}   # projections that read another's input
+GROUPED = ("q", "k", "v")     # one grouped launch in the step (same input)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qmm_prefill512_gate_up_traffic.json")
 KERNEL_SOURCES = ["w4a16_group_quantized_qmv_amd/csrc/qmm.hip", "w4a16_group_quantized_qmv_amd/csrc/device_common.h"]
 
@@ -96,14 +99,21 @@ def build_inputs(torch, copies):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
     projections = []
+    shared = {}
     for name in LAYER:
         idx = synth.shape_index(4, name)
         K, N = synth.LAYER_SHAPES[name]
         wq, s, b = synth.weights(4, idx, N, K)
-        x = synth.activations(4, idx, M_PREFILL, K)
+        # one input per group of projections that read the same activations in a layer: q, k and
+        # v read the attention input, gate and up the MLP input
+        src = INPUT_OF.get(name, name)
+        if src not in shared:
+            xs = synth.activations(4, synth.shape_index(4, src), M_PREFILL, K)
+            shared[src] = (xs, bf16(xs))
+        x, xd = shared[src]
         projections.append({"name": name, "M": M_PREFILL, "N": N, "K": K, "keep": 0,
                             "host": {"x": x, "wq": wq, "scales": s, "biases": b},
-                            "x": bf16(x), "w": [(torch.from_numpy(wq.view(np.int32)).to(dev), bf16(s), bf16(b))]})
+                            "x": xd, "w": [(torch.from_numpy(wq.view(np.int32)).to(dev), bf16(s), bf16(b))]})
     vidx = synth.shape_index(5, "vocab")
     K, N = synth.VOCAB_SHAPE
     wq, s, b = synth.weights(5, vidx, N, K)
@@ -286,23 +296,30 @@ def main():
     projections = build_inputs(torch, args.copies)
     print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
-    # prepared calls: one per (projection, weight copy); y buffers shared across copies
+    # launch units of the step: q, k and v in one grouped call, then one call per projection;
+    # prepared once per weight copy, outputs shared across copies
+    units = [[p for p in projections if p["name"] in GROUPED]] + [[p] for p in projections if p["name"] not in GROUPED]
     calls = []
     for c in range(args.copies):
         row = []
-        for p in projections:
-            x = p["x"][-p["keep"]:] if p["keep"] else p["x"]
-            wq, s, b = p["w"][c]
-            prev = calls[0][len(row)].y if calls else None
-            row.append(w4.PreparedLinear(x, wq, s, b, y=prev))
+        for u in units:
+            prev = calls[0][len(row)] if calls else None
+            if len(u) > 1:
+                row.append(w4.PreparedGrouped(u[0]["x"], [p["w"][c] for p in u], ys=prev.ys if prev else None))
+            else:
+                p = u[0]
+                x = p["x"][-p["keep"]:] if p["keep"] else p["x"]
+                wq, s, b = p["w"][c]
+                row.append(w4.PreparedLinear(x, wq, s, b, y=prev.y if prev else None))
         calls.append(row)
     plans = [call.plan for call in calls[0]]
+    unit_names = ["|".join(p["name"] for p in u) for u in units]
 
-    dom_idx = [j for j, p in enumerate(projections) if p["name"] in DOMINANT]
+    dom_idx = [j for j, u in enumerate(units) if len(u) == 1 and u[0]["name"] in DOMINANT]
     assert dom_idx == list(range(dom_idx[0], dom_idx[0] + len(dom_idx))), "dominant projections must be adjacent"
 
     def step(i, starts=None, ends=None):
-        """One pass over the eight projections.  ``starts`` / ``ends`` map a call's index to a HIP
+        """One pass over the step's launch units (q|k|v grouped, o, gate, up, down, vocab).  ``starts`` / ``ends`` map a call's index to a HIP
         event recorded just before / after it: every call in the breakdown pass; in the timed pass
         one event before the gate launch and one after the up launch that follows it, so that no
         event sits between the two dominant launches."""
@@ -330,7 +347,7 @@ def main():
         return [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
 
     # timed region: the steps back to back on one stream, events around each gate and up launch
-    n = len(projections)
+    n = len(units)
     dom_ev = [event_pair() for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -353,17 +370,21 @@ def main():
         step(i, {j: e[0] for j, e in ev[i].items()}, {j: e[1] for j, e in ev[i].items()})
     torch.cuda.synchronize()
     per = []
-    for j, p in enumerate(projections):
+    for j, u in enumerate(units):
         us = sorted(ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e3 for i in range(bsteps))
         avg = sum(us) / len(us)
-        f, by = flops(p["M"], p["N"], p["K"]), algo_bytes(p["M"], p["N"], p["K"])
+        M, K, N = u[0]["M"], u[0]["K"], sum(p["N"] for p in u)
+        f = sum(flops(p["M"], p["N"], p["K"]) for p in u)
+        # one x for the unit (grouped projections read it once)
+        by = sum(algo_bytes(p["M"], p["N"], p["K"]) for p in u) - 2.0 * M * K * (len(u) - 1)
         pl = plans[j]
-        per.append({"name": p["name"], "M": p["M"], "N": p["N"], "K": p["K"], "avg_us": round(avg, 3),
+        path = {1: "qmv", w4.PATH_GROUPED: "qmm grouped"}.get(pl["path"], "qmm")
+        per.append({"name": unit_names[j], "M": M, "N": N, "K": K, "avg_us": round(avg, 3),
                     "median_us": round(us[len(us) // 2], 3), "TFLOP/s": round(f / avg / 1e6, 2),
                     "GB/s": round(by / avg / 1e3, 1),
-                    "path": "qmv" if pl["path"] == 1 else "qmm", "variant": pl["variant"],
+                    "path": path, "variant": pl["variant"],
                     "tile": [pl["tile_m"], pl["tile_n"]], "split_k": pl["split_k"],
-                    **roof(p["M"], p["N"], p["K"], f / avg / 1e6)})
+                    **roof(M, N, K, f / avg / 1e6)})
     step_flops = sum(flops(p["M"], p["N"], p["K"]) for p in projections)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -380,7 +401,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "prefill512_layer_projections+vocab_last_row", "M": M_PREFILL,
                    "projections": {p["name"]: [p["K"], p["N"]] for p in projections}, "group": 128,
-                   "weight_copies": args.copies, "logits_to_keep": 1},
+                   "launches": unit_names, "weight_copies": args.copies, "logits_to_keep": 1},
         "roofline": {"bound": "mfma",
                      "kernel": f"qmm {dom[0]['tile'][0]}x{dom[0]['tile'][1]} tile (gate/up, M=512, K=2560, N=9728)",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -527,6 +548,7 @@ def next_rows(torch, w4, projections, copies, reps=20):
     stream from a HIP graph over a weight rotation of more than 512 MB:
       * the fused gate/up + SwiGLU pair at the step's 512 rows against the two projections and
         against gate, up, then a framework-style bf16 SiLU and product;
+      * q, k and v as one grouped launch against three launches (512 and 128 rows);
       * the skinny path (16 and 32 rows) against the 64-row tiles on the gate and down shapes;
       * W4A8 (int8 activations) against W4A16 on the step's seven projections;
       * the 4096-row prefill of gate / up / down and the vocabulary head over all rows;
@@ -567,6 +589,29 @@ def next_rows(torch, w4, projections, copies, reps=20):
         "speedup_vs_unfused": round(t_unfused / t_fused, 3), "TFLOP/s": round(f2 / t_fused / 1e6, 2),
         "frac_mfma": round(f2 / t_fused / 1e6 / PEAK_BF16_TFLOPS, 4)}
     del fused, sep_g, sep_u, rot_g, rot_u
+
+    # q, k and v (one input) as one grouped launch against three launches, at 512 and 128 rows
+    qkv = [by[n] for n in GROUPED]
+    rots = [rotation(p["w"][0]) for p in qkv]
+    n = min(len(r) for r in rots)
+    rows_out = []
+    for rows in (M_PREFILL, 128):
+        xq = qkv[0]["x"][:rows]
+        ys = [torch.empty((rows, p["N"]), dtype=torch.bfloat16, device=dev) for p in qkv]
+        grouped = [w4.PreparedGrouped(xq, [r[c] for r in rots], ys=ys) for c in range(n)]
+        sep = [[w4.PreparedLinear(xq, *r[c], y=y) for r, y in zip(rots, ys)] for c in range(n)]
+        t_grp = timed(grouped)
+        t_sep = timed([(lambda c=c: [f() for f in sep[c]]) for c in range(n)])
+        f3 = sum(flops(rows, p["N"], p["K"]) for p in qkv)
+        pl = grouped[0].plan
+        rows_out.append({"M": rows, "N": [p["N"] for p in qkv], "K": qkv[0]["K"],
+                         "plan": {k: pl[k] for k in ("tile_m", "tile_n", "split_k", "variant")},
+                         "grouped_us": round(t_grp, 3), "three_launches_us": round(t_sep, 3),
+                         "speedup": round(t_sep / t_grp, 3), "TFLOP/s": round(f3 / t_grp / 1e6, 2),
+                         **roof(rows, sum(p["N"] for p in qkv), qkv[0]["K"], f3 / t_grp / 1e6)})
+        del grouped, sep, ys
+    out["qkv_grouped"] = rows_out
+    del rots
 
     # skinny rows
     skinny = []

@@ -76,7 +76,11 @@ enum w4a16_path {
                                   "Feature Request: Metal prefill speedup (~68%) on M5 Max",
                                   Related work, names for skinny tiles + deterministic split-K)  */
     W4A16_PATH_GATE_UP = 4,    /* reported by w4a16_gate_up_plan only: the fused gate / up tiles  */
-    W4A16_PATH_W4A8 = 5        /* reported by w4a8_plan only: int8-activation tiles               */
+    W4A16_PATH_W4A8 = 5,       /* reported by w4a8_plan only: int8-activation tiles               */
+    W4A16_PATH_GROUPED = 6,    /* reported by w4a16_grouped_plan only: one tile launch over the
+                                  column tiles of every projection                                */
+    W4A16_PATH_PER_PROJECTION = 7 /* reported by w4a16_grouped_plan only: one w4a16_linear dispatch
+                                  per projection                                                  */
 };
 
 /* Launch plan chosen by the dispatch policy (filled by w4a16_plan). */
@@ -181,6 +185,49 @@ int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, 
 #define W4A16_NOALLOC_SCRATCH_BYTES (32u << 20)
 int w4a16_linear_noalloc(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                          uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, void* stream);
+
+/*
+ * Projections of one input in one call, for projections that read the same activations (the
+ * query, key and value projections of an attention layer):
+ *
+ *     y_p = x . dequant(Wq_p)^T,   p = 0 .. count - 1,   1 <= count <= W4A16_MAX_GROUPED,
+ *
+ * each with the layouts above: x [M, K] shared, wq[p] uint32 [N[p], K / 8], scales[p] and
+ * biases[p] bf16 [N[p], K / 128], y[p] bf16 [M, N[p]].  The pointer arrays and N are host
+ * memory; the buffers they point to are device memory owned by the caller.
+ *
+ * "Week 2 Day 6: SIMD-Matrix Prefill", Benchmark Analysis (Identify Under-Filled Prefill
+ * Shapes) and the paragraph before it: a short, narrow key / value projection has too few result
+ * tiles to occupy the GPU, and splitting K adds a temporary buffer and another launch.  Here,
+ * with more than 32 rows, the projections' 128-column tiles form one grid of one launch (the
+ * tile form the qmm policy takes for M rows and the summed tile columns, never split; a
+ * projection's last tile may be ragged), so the key and value tiles run beside the query tiles.
+ * With at most 32 rows, or count = 1, every projection runs its own w4a16_linear dispatch.
+ * Results equal those of w4a16_linear per projection within the tolerance stated at qmm_w4a16
+ * (bit for bit where both take the same tile form).
+ *
+ * Workspace: w4a16_grouped_plan().workspace_bytes (the exact-code form's group sums of x, shared
+ * by the projections; or the largest per-projection workspace); with too little the call drops
+ * the exact-code form (same result within the tolerance).  Errors as w4a16_linear for every
+ * projection, plus: count outside 1 .. W4A16_MAX_GROUPED -> W4A16_ERR_SHAPE; a null pointer
+ * array -> W4A16_ERR_NULL; an output sharing bytes with any input or another output ->
+ * W4A16_ERR_OVERLAP.  All validation happens before any launch.
+ */
+#define W4A16_MAX_GROUPED 4
+int w4a16_linear_grouped(const uint16_t* x, int32_t count, const uint32_t* const* wq,
+                         const uint16_t* const* scales, const uint16_t* const* biases, uint16_t* const* y,
+                         const int64_t* N, int64_t M, int64_t K, int32_t group, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * Plan of w4a16_linear_grouped: path W4A16_PATH_GROUPED with the one launch's tiles (grid_x =
+ * the summed column tiles, split_k = 1), or W4A16_PATH_PER_PROJECTION (the first projection's
+ * plan), or, for count = 1, w4a16_plan's plan; workspace_bytes as above.  num_cus as in
+ * w4a16_plan.  Pure host arithmetic.  Returns W4A16_OK, _ERR_NULL, _ERR_SHAPE, _ERR_GROUP or
+ * _ERR_DEVICE.
+ */
+int w4a16_grouped_plan(int32_t count, const int64_t* N, int64_t M, int64_t K, int32_t group, int32_t num_cus,
+                       w4a16_plan_t* out);
 
 /*
  * Fused gate / up projection pair with SwiGLU (the SwiGLU fused into the mat-mat, and gate / up

@@ -401,3 +401,69 @@ def test_exact_code_mode_plans():
     assert gate_up_plan(4096, 9728, 2560)["variant"] == 11 and gate_up_plan(1024, 9728, 2560)["variant"] == 11
     assert gate_up_plan(512, 9728, 2560)["variant"] == 3                 # 96-row dequantizing tiles
     assert gate_up_plan(32, 9728, 2560)["variant"] < 10
+
+
+# ------------------------------------------------------------------------------ grouped projections of one input
+
+def grouped_plan(N, M, K):
+    return w4.w4a16_grouped_plan(N, M, K, 128, CUS)
+
+
+def test_grouped_plan_one_launch_over_the_column_tiles():
+    # "Week 2 Day 6: SIMD-Matrix Prefill", Benchmark Analysis: the short key / value projections
+    # under-fill the GPU alone; grouped with the query projection their tiles share one grid
+    qkv = [4096, 1024, 1024]
+    for M in (33, 128, 509, 512, 1024, 4096):
+        p = grouped_plan(qkv, M, 2560)
+        alone = plan(M, 6144, 2560, split_k=1)        # the tile form of one 6144-column projection
+        assert p["path"] == w4.PATH_GROUPED and p["split_k"] == 1 and p["grid_z"] == 1
+        assert p["grid_x"] == 48 and p["grid_y"] == -(-M // p["tile_m"])
+        assert (p["tile_m"], p["tile_n"], p["variant"], p["block_threads"]) == \
+            (alone["tile_m"], alone["tile_n"], alone["variant"], alone["block_threads"])
+        assert p["workspace_bytes"] == alone["workspace_bytes"]
+    # ragged projections: each owns ceil(N / 128) column tiles
+    assert grouped_plan([200, 96, 1000], 509, 256)["grid_x"] == 2 + 1 + 8
+    # the exact-code form above 1024 rows: the group sums of the shared x, once
+    p = grouped_plan(qkv, 4096, 2560)
+    assert p["variant"] >= 10 and p["workspace_bytes"] == -(-4096 * w4.w4a8_xsum_cols(2560) * 2 // 256) * 256
+
+
+def test_grouped_plan_per_projection_for_few_rows():
+    # at most 32 rows (matvec and skinny paths) and for one projection: each projection's own dispatch
+    for M in (1, 8, 16, 32):
+        p = grouped_plan([4096, 1024, 1024], M, 2560)
+        assert p["path"] == w4.PATH_PER_PROJECTION
+        assert p["workspace_bytes"] == max(plan(M, n, 2560)["workspace_bytes"] for n in (4096, 1024, 1024))
+        first = plan(M, 4096, 2560)
+        assert p["variant"] == first["variant"] and p["tile_m"] == first["tile_m"]
+    assert grouped_plan([2560], 512, 9728) == plan(512, 2560, 9728)
+
+
+@pytest.mark.parametrize("N,err", [([], 2), ([64] * 5, 2), ([64, 0], 2), ([64, 64], 0)])
+def test_grouped_plan_counts(N, err, lib):
+    arr = (ctypes.c_int64 * max(1, len(N)))(*N)
+    assert lib.w4a16_grouped_plan(len(N), arr, 64, 256, 128, CUS, ctypes.byref(w4.Plan())) == err
+    assert lib.w4a16_grouped_plan(2, None, 64, 256, 128, CUS, ctypes.byref(w4.Plan())) == 1
+    assert lib.w4a16_grouped_plan(2, arr, 64, 256, 64, CUS, ctypes.byref(w4.Plan())) in (2, 3)
+
+
+def test_grouped_call_validates_before_launch(lib):
+    # two projections at fake addresses: x, then per projection wq / s / b / y (16 MiB apart)
+    P = ctypes.c_void_p * 2
+    wq2, s2, b2, y2 = (i << 24 for i in range(10, 14))
+
+    def call(x=X, wq=(WQ, wq2), s=(S, s2), b=(B, b2), y=(Y, y2), N=(64, 32), M=40, K=256, group=128, count=2):
+        arrs = [None if v is None else P(*v) for v in (wq, s, b, y)]
+        n = None if N is None else (ctypes.c_int64 * 2)(*N)
+        return lib.w4a16_linear_grouped(x, count, *arrs, n, M, K, group, None, 0, None)
+
+    assert call(wq=None) == 1 and call(y=None) == 1 and call(N=None) == 1
+    assert call(x=None) == 1 and call(wq=(WQ, None)) == 1 and call(y=(None, y2)) == 1
+    assert call(count=0) == 2 and call(count=5) == 2
+    assert call(N=(64, 0)) == 2 and call(K=100) == 2 and call(group=64) == 3
+    assert call(x=ODD) == 4 and call(s=(S, s2 + 1)) == 4
+    # an output may share no byte with an input of its own projection or another one, nor with
+    # another output (y0 is 40 x 64 bf16 = 5 KiB, y1 40 x 32 bf16 = 2.5 KiB)
+    assert call(y=(X, y2)) == 9
+    assert call(y=(Y, wq2)) == 9 and call(y=(Y, s2 + 2)) == 9 and call(y=(b2, y2)) == 9
+    assert call(y=(Y, Y + 4096)) == 9 and call(y=(Y + 2048, Y)) == 9

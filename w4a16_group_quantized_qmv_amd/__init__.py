@@ -34,11 +34,15 @@ __all__ = [
     "qmv_affine", "qmv_affine_plan", "QMV_POLICY", "QMV_AMORTIZED", "QMV_PER_ROW", "QMV_FAMILIES", "BITS",
     "PATH_W4A8", "w4a8_xsum_cols", "w4a8_quantize_rows", "w4a8_plan", "qmm_w4a8", "w4a8_linear_workspace_bytes",
     "w4a8_linear", "PreparedW4A8",
+    "PATH_GROUPED", "PATH_PER_PROJECTION", "MAX_GROUPED", "w4a16_grouped_plan", "w4a16_linear_grouped",
+    "PreparedGrouped",
 ]
 
 GROUP = 128
 W4A16_OK = 0
 PATH_AUTO, PATH_QMV, PATH_QMM, PATH_SKINNY, PATH_GATE_UP, PATH_W4A8 = 0, 1, 2, 3, 4, 5
+PATH_GROUPED, PATH_PER_PROJECTION = 6, 7
+MAX_GROUPED = 4
 QMV_POLICY, QMV_AMORTIZED, QMV_PER_ROW, QMV_FAMILIES = 0, 1, 2, 3
 BITS = (1, 2, 3, 4, 8)
 
@@ -111,6 +115,12 @@ def load():
     lib.w4a8_linear_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
     lib.w4a8_linear.restype = ctypes.c_int
     lib.w4a8_linear.argtypes = [u16p, u32p, u16p, u16p, u16p, i64, i64, i64, i32, vp, ctypes.c_size_t, vp]
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    lib.w4a16_grouped_plan.restype = ctypes.c_int
+    lib.w4a16_grouped_plan.argtypes = [i32, ctypes.POINTER(i64), i64, i64, i32, i32, ctypes.POINTER(Plan)]
+    lib.w4a16_linear_grouped.restype = ctypes.c_int
+    lib.w4a16_linear_grouped.argtypes = [u16p, i32, pp, pp, pp, pp, ctypes.POINTER(i64), i64, i64, i32, vp,
+                                         ctypes.c_size_t, vp]
     _LIB = lib
     return lib
 
@@ -448,6 +458,49 @@ def linear(x, wq, scales, biases, logits_to_keep: int = 0, path: str | None = No
     raise ValueError(f"unknown path {path!r}")
 
 
+def w4a16_grouped_plan(N, M: int, K: int, group: int = GROUP, num_cus: int = 0) -> dict:
+    """Plan of ``w4a16_linear_grouped`` for projections of ``N[p]`` columns (one list entry each)."""
+    arr = (ctypes.c_int64 * len(N))(*N)
+    plan = Plan()
+    st = load().w4a16_grouped_plan(len(N), arr, M, K, group, num_cus, ctypes.byref(plan))
+    _raise_for(st, "w4a16_grouped_plan")
+    return plan.as_dict()
+
+
+def _grouped_args(x, weights, ys):
+    if not 1 <= len(weights) <= MAX_GROUPED:
+        raise ValueError(f"{len(weights)} projections: 1 .. {MAX_GROUPED} are supported")
+    if ys is None:
+        ys = [None] * len(weights)
+    if len(ys) != len(weights):
+        raise ValueError("one output per projection")
+    out, Ns = [], []
+    for (wq, s, b), y in zip(weights, ys):
+        M, N, K, y = _operands(x, wq, s, b, y)
+        out.append(y)
+        Ns.append(N)
+    vp = ctypes.c_void_p
+    arrays = tuple((vp * len(weights))(*[t.data_ptr() for t in col])
+                   for col in ([w[0] for w in weights], [w[1] for w in weights], [w[2] for w in weights], out))
+    return M, K, out, Ns, arrays
+
+
+def w4a16_linear_grouped(x, weights, ys=None, workspace=None, stream=None):
+    """Projections of one input in one call: ``weights`` is a list of ``(wq, scales, biases)``
+    triples (1 .. MAX_GROUPED), e.g. the query, key and value projections; returns the list of
+    outputs ``y_p = x . dequant(wq_p)^T``."""
+    own_y, own_ws = ys is None, workspace is None
+    M, K, out, Ns, (wqa, sa, ba, ya) = _grouped_args(x, weights, ys)
+    need = w4a16_grouped_plan(Ns, M, K)["workspace_bytes"]
+    ws, ws_bytes = _workspace(workspace, need, x.device)
+    _keep_for_stream(stream, x.device, *(out if own_y else []), ws if own_ws else None)
+    st = load().w4a16_linear_grouped(x.data_ptr(), len(weights), wqa, sa, ba, ya, (ctypes.c_int64 * len(Ns))(*Ns),
+                                     M, K, GROUP, None if ws is None else ws.data_ptr(), ws_bytes,
+                                     _stream(stream, x.device))
+    _raise_for(st, "w4a16_linear_grouped")
+    return out
+
+
 class PreparedLinear:
     """One projection with fixed tensors, validated once; calling it only enqueues the kernels.
 
@@ -514,6 +567,29 @@ class PreparedGateUp:
         if st != W4A16_OK:
             _raise_for(st, "w4a16_gate_up_swiglu")
         return self.h
+
+
+class PreparedGrouped:
+    """Grouped projections of one input with fixed tensors, validated once (see PreparedLinear):
+    the outputs and any workspace are allocated here (or passed in); ``__call__`` issues one
+    C-ABI call (``w4a16_linear_grouped``) on the stream current at construction."""
+
+    def __init__(self, x, weights, ys=None, workspace=None):
+        M, K, out, Ns, arrays = _grouped_args(x, weights, ys)
+        self.M, self.K, self.N, self.ys = M, K, Ns, out
+        self.plan = w4a16_grouped_plan(Ns, M, K)
+        ws, ws_bytes = _workspace(workspace, self.plan["workspace_bytes"], x.device)
+        self.workspace = ws
+        self._keep = (arrays, (ctypes.c_int64 * len(Ns))(*Ns))
+        self._fn = load().w4a16_linear_grouped
+        self._args = (x.data_ptr(), len(weights), *arrays, self._keep[1], M, K, GROUP,
+                      None if ws is None else ws.data_ptr(), ws_bytes, _stream(None, x.device))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != W4A16_OK:
+            _raise_for(st, "w4a16_linear_grouped")
+        return self.ys
 
 
 class PreparedW4A8:

@@ -332,6 +332,107 @@ int run_qmm(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint
     return run_plan(p, x, wq, s, b, y, M, N, K, workspace, static_cast<hipStream_t>(stream));
 }
 
+// Grouped projections of one input.  With more than 32 rows the projections' 128-column tiles
+// form one grid (the tile form the qmm policy takes for M rows and the summed tile columns,
+// never split); with at most 32 rows, or one projection, each projection runs its own
+// w4a16_linear dispatch and the workspace is the largest of theirs.
+static_assert(W4A16_MAX_GROUPED == kMaxGroupedProjections, "one limit for the ABI and the kernel");
+int make_grouped_plan(int32_t count, const int64_t* N, int64_t M, int64_t K, int32_t group, int32_t num_cus,
+                      w4a16_plan_t* out, bool codes = true) {
+    if (!out || !N) return W4A16_ERR_NULL;
+    if (count < 1 || count > W4A16_MAX_GROUPED) return W4A16_ERR_SHAPE;
+    int64_t tiles_n = 0;
+    for (int32_t p = 0; p < count; ++p) {
+        const int st = check_shape(M, N[p], K, group);
+        if (st != W4A16_OK) return st;
+        tiles_n += ceil_div(N[p], kGroupedTileN);
+    }
+    if (tiles_n * kGroupedTileN > kMaxDim) return W4A16_ERR_SHAPE;
+    int32_t cus = num_cus;
+    if (cus <= 0) {
+        const int st = query_num_cus(&cus);
+        if (st != W4A16_OK) return st;
+    }
+    if (count == 1 || M <= kSkinnyMaxRows) {
+        uint64_t ws = 0;
+        for (int32_t p = count - 1; p >= 0; --p) {      // leaves the first projection's plan in *out
+            const int st = make_plan(M, N[p], K, group, W4A16_PATH_AUTO, 0, cus, out);
+            if (st != W4A16_OK) return st;
+            ws = std::max<uint64_t>(ws, out->workspace_bytes);
+        }
+        if (count > 1) out->path = W4A16_PATH_PER_PROJECTION;
+        out->workspace_bytes = ws;
+        return W4A16_OK;
+    }
+    plan_qmm(M, tiles_n * kGroupedTileN, K, 1, cus, out, false, codes);
+    out->path = W4A16_PATH_GROUPED;
+    out->num_cus = cus;
+    return W4A16_OK;
+}
+
+int run_grouped(const uint16_t* x, int32_t count, const uint32_t* const* wq, const uint16_t* const* s,
+                const uint16_t* const* b, uint16_t* const* y, const int64_t* N, int64_t M, int64_t K, int32_t group,
+                void* workspace, size_t ws_bytes, void* stream) {
+    if (!wq || !s || !b || !y || !N) return W4A16_ERR_NULL;
+    if (count < 1 || count > W4A16_MAX_GROUPED) return W4A16_ERR_SHAPE;
+    for (int32_t p = 0; p < count; ++p) {
+        int st = check_shape(M, N[p], K, group);
+        if (st != W4A16_OK) return st;
+        st = check_buffers(x, wq[p], s[p], b[p], y[p], M, N[p], K);
+        if (st != W4A16_OK) return st;
+    }
+    // an output may share no byte with another projection's output or inputs either
+    for (int32_t p = 0; p < count; ++p) {
+        const uint64_t ny = static_cast<uint64_t>(M) * N[p] * 2;
+        for (int32_t q = 0; q < count; ++q) {
+            if (q == p) continue;
+            const uint64_t sb = static_cast<uint64_t>(N[q]) * (K / W4A16_GROUP) * 2;
+            if (overlaps(y[p], ny, y[q], static_cast<uint64_t>(M) * N[q] * 2) ||
+                overlaps(y[p], ny, wq[q], static_cast<uint64_t>(N[q]) * K / 2) || overlaps(y[p], ny, s[q], sb) ||
+                overlaps(y[p], ny, b[q], sb))
+                return W4A16_ERR_OVERLAP;
+        }
+    }
+    w4a16_plan_t pl;
+    int st = make_grouped_plan(count, N, M, K, group, 0, &pl);
+    if (st != W4A16_OK) return st;
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (pl.path != W4A16_PATH_GROUPED) {
+        // stream order keeps the shared workspace of consecutive calls apart
+        for (int32_t p = 0; p < count; ++p) {
+            st = run_qmm(x, wq[p], s[p], b[p], y[p], M, N[p], K, group, W4A16_PATH_AUTO, 0, workspace, ws_bytes,
+                         stream);
+            if (st != W4A16_OK) return st;
+        }
+        return W4A16_OK;
+    }
+    const int32_t cus = pl.num_cus;
+    st = fit_workspace(pl, 1, workspace, ws_bytes, [&](int32_t, bool codes) {
+        make_grouped_plan(count, N, M, K, group, cus, &pl, codes);
+    });
+    if (st != W4A16_OK) return st;
+    QmmGroups g{};
+    g.count = count;
+    int tn = 0;
+    for (int32_t p = 0; p < count; ++p) {
+        g.wq[p] = wq[p];
+        g.s[p] = s[p];
+        g.b[p] = b[p];
+        g.y[p] = y[p];
+        g.n[p] = static_cast<int>(N[p]);
+        g.tn_first[p] = tn;
+        tn += static_cast<int>(ceil_div(N[p], kGroupedTileN));
+    }
+    const int m = static_cast<int>(M), k = static_cast<int>(K);
+    uint16_t* xsum = nullptr;
+    if (plan_codes(pl)) {
+        xsum = static_cast<uint16_t*>(workspace);
+        const hipError_t e0 = launch_act_group_sums(x, xsum, m, k, group_sum_cols(k), hs);
+        if (e0 != hipSuccess) return to_status(e0);
+    }
+    return to_status(launch_qmm_grouped(plan_tile_variant(pl), x, xsum, g, m, k, hs));
+}
+
 // Gate / up pair with SwiGLU: one tile kernel computes both projections of the same columns.
 // Tiles: 32 rows up to 32 rows; above, 64-row tiles in the exact-code mode (measured on MI355X
 // against the dequantizing 64- and 128-row tiles: 87 vs 98 us at 512 rows and 497 vs 560 us at
@@ -719,6 +820,17 @@ int w4a16_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, 
 int w4a16_linear_noalloc(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                          uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t split_k, void* stream) {
     return run_linear_noalloc(x, wq, scales, biases, y, M, N, K, group, split_k, stream);
+}
+
+int w4a16_grouped_plan(int32_t count, const int64_t* N, int64_t M, int64_t K, int32_t group, int32_t num_cus,
+                       w4a16_plan_t* out) {
+    return make_grouped_plan(count, N, M, K, group, num_cus, out);
+}
+
+int w4a16_linear_grouped(const uint16_t* x, int32_t count, const uint32_t* const* wq, const uint16_t* const* scales,
+                         const uint16_t* const* biases, uint16_t* const* y, const int64_t* N, int64_t M, int64_t K,
+                         int32_t group, void* workspace, size_t workspace_bytes, void* stream) {
+    return run_grouped(x, count, wq, scales, biases, y, N, M, K, group, workspace, workspace_bytes, stream);
 }
 
 int qmv_affine_plan(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, int32_t mode, int32_t num_cus,

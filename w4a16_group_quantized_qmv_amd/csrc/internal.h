@@ -93,6 +93,24 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, cons
                       const uint16_t* biases, uint16_t* y, float* ws, int M, int N, int K, int split,
                       hipStream_t stream);
 
+// Grouped projections of one input (at most kMaxGroupedProjections): y_p = x . dequant(wq_p)^T,
+// one launch over the concatenation of the projections' column tiles.  Projection p owns the
+// column tiles [tn_first[p], tn_first[p + 1]) of 128 columns each (its last tile may be ragged);
+// count = 0 marks an ordinary single-projection launch.  Unsplit only.
+constexpr int kMaxGroupedProjections = 4;
+constexpr int kGroupedTileN = 128;   // columns per tile of every qmm tile form
+struct QmmGroups {
+    const uint32_t* wq[kMaxGroupedProjections];
+    const uint16_t* s[kMaxGroupedProjections];
+    const uint16_t* b[kMaxGroupedProjections];
+    uint16_t* y[kMaxGroupedProjections];
+    int n[kMaxGroupedProjections];
+    int tn_first[kMaxGroupedProjections];
+    int count;
+};
+hipError_t launch_qmm_grouped(int variant, const uint16_t* x, const uint16_t* xsum, const QmmGroups& groups, int M,
+                              int K, hipStream_t stream);
+
 // Gate / up pair with SwiGLU: h = bf16(silu(x . gate^T) * (x . up^T)), one tile kernel for both
 // projections.  split > 1 writes fp32 partials ws[0][z][M][N] (gate) and ws[1][z][M][N] (up).
 // xsum != nullptr selects the exact-code mode, compiled for the 64-row tiles

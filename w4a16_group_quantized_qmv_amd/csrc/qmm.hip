@@ -66,12 +66,13 @@ __device__ __forceinline__ float silu_f32(float z) { return z / (1.f + expf(-z))
 // gate / up pair with h = silu(gate) * up formed from the fp32 accumulators in the epilogue
 // (the SwiGLU fused into the mat-mat of "Feature Request: Metal prefill speedup (~68%) on M5
 // Max").  Weight set p of column block cb is block j = p * NB + cb.
-template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES, int NP = 1, int CODES = 0, int SBQ = 1, int KS = 1>
+template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES, int NP = 1, int CODES = 0, int SBQ = 1, int KS = 1,
+          bool GRP = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD))) void qmm_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, const uint32_t* __restrict__ wq2, const uint16_t* __restrict__ scales2,
     const uint16_t* __restrict__ biases2, uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N, int K,
-    int split, int tiles_m, int tiles_n, const uint16_t* __restrict__ xsum, int KB) {
+    int split, int tiles_m, int tiles_n, const uint16_t* __restrict__ xsum, int KB, const QmmGroups grp) {
     // KS = 2: two waves share each column strip, one taking sub-steps 0..3 of every group and
     // the other 4..7; their partial accumulators are added through LDS at the end
     static_assert(KS == 1 || (KS == 2 && NP == 1), "K-split waves: single projections");
@@ -113,7 +114,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     const int g_end = SBQ * static_cast<int>(static_cast<int64_t>(z + 1) * g_units / split);
     const int groups = g_end - g_begin;
     const int m0 = tm * BM;
-    const int n0 = tn * BN;
+    int n0 = tn * BN;
+    // Grouped launch: the projection that owns column tile tn takes over the weight, scale,
+    // bias and output pointers and the column count (scalar selects with constant indices, so
+    // the argument block is never copied to be indexed).
+    if constexpr (GRP) {
+        // (readfirstlane: the tile index is uniform, and saying so keeps the selects scalar)
+        const int p = __builtin_amdgcn_readfirstlane(
+            (grp.count > 1 && tn >= grp.tn_first[1] ? 1 : 0) + (grp.count > 2 && tn >= grp.tn_first[2] ? 1 : 0) +
+            (grp.count > 3 && tn >= grp.tn_first[3] ? 1 : 0));
+        auto pick = [p](auto a0, auto a1, auto a2, auto a3) { return p == 0 ? a0 : p == 1 ? a1 : p == 2 ? a2 : a3; };
+        wq = pick(grp.wq[0], grp.wq[1], grp.wq[2], grp.wq[3]);
+        scales = pick(grp.s[0], grp.s[1], grp.s[2], grp.s[3]);
+        biases = pick(grp.b[0], grp.b[1], grp.b[2], grp.b[3]);
+        y = pick(grp.y[0], grp.y[1], grp.y[2], grp.y[3]);
+        N = pick(grp.n[0], grp.n[1], grp.n[2], grp.n[3]);
+        n0 = (tn - pick(grp.tn_first[0], grp.tn_first[1], grp.tn_first[2], grp.tn_first[3])) * BN;
+    }
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int kh = wave / WN, wn = wave % WN;     // K half (KS = 2) and column strip of this wave
@@ -688,19 +705,42 @@ static bool quad_scales(int K, int split, const uint16_t* s, const uint16_t* b) 
            reinterpret_cast<uintptr_t>(b) % 8 == 0;
 }
 
+// grp: a grouped launch (N is then the concatenated column tiles' width, and wq, s, b, y are
+// placeholders that the kernel replaces per tile), or null for one projection.
 template <int BM, int NB, int NW, int WAVES_PER_SIMD, int STAGES, int CM = 0, int CODES_WPS = WAVES_PER_SIMD,
-          int KS = 1>
+          int KS = 1, bool GROUPED_FORM = false>
 static hipError_t launch_qmm_t(const uint16_t* x, const uint16_t* xsum, int KB, const uint32_t* wq, const uint16_t* s,
                                const uint16_t* b, uint16_t* y, float* ws, int M, int N, int K, int split,
-                               hipStream_t stream) {
+                               hipStream_t stream, const QmmGroups* grp = nullptr) {
     constexpr int BN = NW / KS * NB * 32;
+    static_assert(BN == kGroupedTileN, "grouped launches assume 128-column tiles");
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
     const dim3 grid(tiles_m * tiles_n * split);
-    const bool quad = STAGES == 2 && quad_scales(K, split, s, b);
-#define W4A16_LAUNCH_QMM(WPS, CODES, SBQ, XS)                                                                  \
-    hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WPS, STAGES, 1, CODES, SBQ, KS>), grid, dim3(64 * NW), 0, stream, x, wq, \
-                       s, b, nullptr, nullptr, nullptr, y, ws, M, N, K, split, tiles_m, tiles_n, XS, KB)
+    bool quad = STAGES == 2;
+    if (grp) {
+        for (int p = 0; p < grp->count; ++p) quad = quad && quad_scales(K, split, grp->s[p], grp->b[p]);
+    } else {
+        quad = quad && quad_scales(K, split, s, b);
+    }
+    // only the tile forms a grouped plan can pick are compiled in the grouped form
+    if (grp && (!GROUPED_FORM || split != 1)) return hipErrorInvalidValue;
+    const QmmGroups none{};
+    const QmmGroups& g = grp ? *grp : none;
+#define W4A16_LAUNCH_QMM(WPS, CODES, SBQ, XS)                                                                        \
+    do {                                                                                                          \
+        if constexpr (GROUPED_FORM) {                                                                             \
+            if (grp) {                                                                                            \
+                hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WPS, STAGES, 1, CODES, SBQ, KS, true>), grid,         \
+                                   dim3(64 * NW), 0, stream, x, wq, s, b, nullptr, nullptr, nullptr, y, ws, M, N, K, \
+                                   split, tiles_m, tiles_n, XS, KB, g);                                           \
+                break;                                                                                            \
+            }                                                                                                     \
+        }                                                                                                         \
+        hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WPS, STAGES, 1, CODES, SBQ, KS>), grid, dim3(64 * NW), 0,       \
+                           stream, x, wq, s, b, nullptr, nullptr, nullptr, y, ws, M, N, K, split, tiles_m, tiles_n,  \
+                           XS, KB, g);                                                                            \
+    } while (0)
     if constexpr (CM > 0) {
         if (xsum) {
             if constexpr (STAGES == 2) {
@@ -736,7 +776,7 @@ static hipError_t launch_gate_up_t(const uint16_t* x, const uint16_t* xsum, int 
     const bool quad = STAGES == 2 && quad_scales(K, split, sg, bg) && quad_scales(K, split, su, bu);
 #define W4A16_LAUNCH_GU(WPS, CODES, SBQ, XS)                                                                       \
     hipLaunchKernelGGL((qmm_kernel<BM, 1, 4, WPS, STAGES, 2, CODES, SBQ>), grid, dim3(256), 0, stream, x, wg, sg, bg, \
-                       wu, su, bu, h, ws, M, N, K, split, tiles_m, tiles_n, XS, KB)
+                       wu, su, bu, h, ws, M, N, K, split, tiles_m, tiles_n, XS, KB, QmmGroups{})
     if constexpr (CM > 0) {
         if (xsum) {
             if constexpr (STAGES == 2) {
@@ -761,24 +801,45 @@ static hipError_t launch_gate_up_t(const uint16_t* x, const uint16_t* xsum, int 
     return hipGetLastError();
 }
 
-hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, const uint32_t* wq, const uint16_t* scales,
-                      const uint16_t* biases, uint16_t* y, float* ws, int M, int N, int K, int split,
-                      hipStream_t stream) {
+// One tile form; grp != null makes it a grouped launch (unsplit, N = the concatenated tiles' width).
+static hipError_t dispatch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, const uint32_t* wq,
+                               const uint16_t* scales, const uint16_t* biases, uint16_t* y, float* ws, int M, int N,
+                               int K, int split, hipStream_t stream, const QmmGroups* grp) {
     const int KB = group_sum_cols(K);
     // the exact-code mode is compiled for the 128-row tiles, where it measured faster
     if (xsum && variant != kQmmCodesTileVariant) return hipErrorInvalidValue;
     switch (variant) {
-        case 0: return launch_qmm_t<128, 1, 4, 2, 2, 1>(x, xsum, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 1: return launch_qmm_t<64, 1, 4, 3, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 2: return launch_qmm_t<64, 1, 4, 2, 3>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 3: return launch_qmm_t<32, 1, 4, 4, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 4: return launch_qmm_t<32, 1, 4, 3, 3>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream);
-        case 5: return launch_qmm_t<64, 1, 8, 6, 2, 0, 6, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split,
-                                                           stream);
-        case 6: return launch_qmm_t<96, 1, 8, 4, 2, 0, 4, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split,
-                                                           stream);
+        case 0: return launch_qmm_t<128, 1, 4, 2, 2, 1, 2, 1, true>(x, xsum, KB, wq, scales, biases, y, ws, M, N, K,
+                                                                    split, stream, grp);
+        case 1: return launch_qmm_t<64, 1, 4, 3, 2, 0, 3, 1, true>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K,
+                                                                   split, stream, grp);
+        case 2: return launch_qmm_t<64, 1, 4, 2, 3>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream,
+                                                     grp);
+        case 3: return launch_qmm_t<32, 1, 4, 4, 2>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream,
+                                                     grp);
+        case 4: return launch_qmm_t<32, 1, 4, 3, 3>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K, split, stream,
+                                                     grp);
+        case 5: return launch_qmm_t<64, 1, 8, 6, 2, 0, 6, 2, true>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K,
+                                                                   split, stream, grp);
+        case 6: return launch_qmm_t<96, 1, 8, 4, 2, 0, 4, 2, true>(x, nullptr, KB, wq, scales, biases, y, ws, M, N, K,
+                                                                   split, stream, grp);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, const uint32_t* wq, const uint16_t* scales,
+                      const uint16_t* biases, uint16_t* y, float* ws, int M, int N, int K, int split,
+                      hipStream_t stream) {
+    return dispatch_qmm(variant, x, xsum, wq, scales, biases, y, ws, M, N, K, split, stream, nullptr);
+}
+
+hipError_t launch_qmm_grouped(int variant, const uint16_t* x, const uint16_t* xsum, const QmmGroups& groups, int M,
+                              int K, hipStream_t stream) {
+    if (groups.count < 1 || groups.count > kMaxGroupedProjections) return hipErrorInvalidValue;
+    const int last = groups.count - 1;
+    const int tiles_n = groups.tn_first[last] + (groups.n[last] + kGroupedTileN - 1) / kGroupedTileN;
+    return dispatch_qmm(variant, x, xsum, groups.wq[0], groups.s[0], groups.b[0], groups.y[0], nullptr, M,
+                        tiles_n * kGroupedTileN, K, 1, stream, &groups);
 }
 
 const QmmShape kGateUpVariants[kNumGateUpVariants] = {
