@@ -3,8 +3,10 @@
 
 One step is one 512-token prefill pass through the projections of one decoder layer
 (hidden 2560, 32 query heads and 8 key/value heads of dimension 128, MLP 9728: q, k, v, o,
-gate, up, down at M = 512, where the down projection's K = 9728 exercises split-K; q, k and v
-read the same input and run as one grouped launch, gate and up read the same input), followed
+gate, up, down at M = 512, where the down projection's K = 9728 exercises split-K), in layer
+order and launched as a serving stack would: q, k and v read the same input and run as one
+grouped launch; gate and up read the same input and run as the fused gate / up + SwiGLU pair,
+whose output h = silu(gate) * up is the down projection's input), followed
 by the vocabulary head (2560 -> 151936) applied to the last row only (logits_to_keep = 1,
 which dispatches to the matvec path).  These are the per-projection prefill shapes that
 tiny-llm's "Week 2 Day 6: SIMD-Matrix Prefill" benchmarks in Task 5 and its Benchmark
@@ -17,8 +19,8 @@ device copies so that weight reads miss the 256 MB last-level cache.  Output: on
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu-baseline] [--no-next-rows]
 
-Besides the step's throughput the line carries: the dominant kernel's roofline (HIP events
-around each of its launches in the timed region), the same run's measured ceilings (torch's
+Besides the step's throughput the line carries: the dominant kernel's roofline (the fused
+gate / up pair; HIP events around each of its launches in the timed region), the same run's measured ceilings (torch's
 bf16 GEMM through hipBLASLt on the same shapes, and device copy / read rates), every timed
 shape's fraction of the roof that binds it (min(MFMA peak, arithmetic intensity x HBM
 bandwidth)), and the CPU oracle on a bounded sample of the step.
@@ -42,9 +44,10 @@ PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 MFMA
 M_PREFILL = 512
 LAYER = ["q", "k", "v", "o", "gate", "up", "down"]
-DOMINANT = ("gate", "up")     # largest projections: the roofline kernel
 INPUT_OF = {"k": "q", "v": "q", "up": "gate"}   # projections that read another's input
 GROUPED = ("q", "k", "v")     # one grouped launch in the step (same input)
+FUSED = ("gate", "up")        # one fused gate / up + SwiGLU launch; its h is down's input
+DOMINANT = "gate|up"          # the largest launch of the step: the roofline kernel
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qmm_prefill512_gate_up_traffic.json")
 KERNEL_SOURCES = ["w4a16_group_quantized_qmv_amd/csrc/qmm.hip", "w4a16_group_quantized_qmv_amd/csrc/device_common.h"]
 
@@ -296,26 +299,33 @@ def main():
     projections = build_inputs(torch, args.copies)
     print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
-    # launch units of the step: q, k and v in one grouped call, then one call per projection;
-    # prepared once per weight copy, outputs shared across copies
-    units = [[p for p in projections if p["name"] in GROUPED]] + [[p] for p in projections if p["name"] not in GROUPED]
+    # launch units of the step, in layer order: q|k|v (one grouped call), o, gate|up (the fused
+    # SwiGLU pair; its output h is the down projection's input), down, the vocabulary head's last
+    # row.  Prepared once per weight copy, outputs shared across copies.
+    by_name = {p["name"]: p for p in projections}
+    units = [[by_name[n] for n in GROUPED], [by_name["o"]], [by_name[n] for n in FUSED], [by_name["down"]],
+             [by_name["vocab_last_row"]]]
+    unit_names = ["|".join(p["name"] for p in u) for u in units]
     calls = []
     for c in range(args.copies):
         row = []
-        for u in units:
+        h = None
+        for u, name in zip(units, unit_names):
             prev = calls[0][len(row)] if calls else None
-            if len(u) > 1:
+            if name == "q|k|v":
                 row.append(w4.PreparedGrouped(u[0]["x"], [p["w"][c] for p in u], ys=prev.ys if prev else None))
+            elif name == "gate|up":
+                row.append(w4.PreparedGateUp(u[0]["x"], u[0]["w"][c], u[1]["w"][c], h=prev.h if prev else None))
+                h = row[-1].h
             else:
                 p = u[0]
-                x = p["x"][-p["keep"]:] if p["keep"] else p["x"]
+                x = h if name == "down" else (p["x"][-p["keep"]:] if p["keep"] else p["x"])
                 wq, s, b = p["w"][c]
                 row.append(w4.PreparedLinear(x, wq, s, b, y=prev.y if prev else None))
         calls.append(row)
     plans = [call.plan for call in calls[0]]
-    unit_names = ["|".join(p["name"] for p in u) for u in units]
 
-    dom_idx = [j for j, u in enumerate(units) if len(u) == 1 and u[0]["name"] in DOMINANT]
+    dom_idx = [unit_names.index(DOMINANT)]
     assert dom_idx == list(range(dom_idx[0], dom_idx[0] + len(dom_idx))), "dominant projections must be adjacent"
 
     def step(i, starts=None, ends=None):
@@ -378,7 +388,7 @@ def main():
         # one x for the unit (grouped projections read it once)
         by = sum(algo_bytes(p["M"], p["N"], p["K"]) for p in u) - 2.0 * M * K * (len(u) - 1)
         pl = plans[j]
-        path = {1: "qmv", w4.PATH_GROUPED: "qmm grouped"}.get(pl["path"], "qmm")
+        path = {1: "qmv", w4.PATH_GROUPED: "qmm grouped", w4.PATH_GATE_UP: "qmm gate/up + SwiGLU"}.get(pl["path"], "qmm")
         per.append({"name": unit_names[j], "M": M, "N": N, "K": K, "avg_us": round(avg, 3),
                     "median_us": round(us[len(us) // 2], 3), "TFLOP/s": round(f / avg / 1e6, 2),
                     "GB/s": round(by / avg / 1e3, 1),
@@ -389,7 +399,7 @@ def main():
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     dom = [per[j] for j in dom_idx]
-    dom_flops = flops(M_PREFILL, *synth_shape("gate"))
+    dom_flops = sum(flops(p["M"], p["N"], p["K"]) for p in units[dom_idx[0]])
     achieved = dom_flops / dom_us / 1e6
     traffic = load_traffic()
     vocab = per[-1]
@@ -403,16 +413,18 @@ def main():
                    "projections": {p["name"]: [p["K"], p["N"]] for p in projections}, "group": 128,
                    "launches": unit_names, "weight_copies": args.copies, "logits_to_keep": 1},
         "roofline": {"bound": "mfma",
-                     "kernel": f"qmm {dom[0]['tile'][0]}x{dom[0]['tile'][1]} tile (gate/up, M=512, K=2560, N=9728)",
+                     "kernel": f"qmm gate/up + SwiGLU pair, {dom[0]['tile'][0]}x{dom[0]['tile'][1]} tiles of h "
+                               "(M=512, K=2560, N=9728 per projection)",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": dom_flops, "avg_launch_us": round(dom_us, 3),
                      "launches": len(dom_launch_us) * len(dom_idx),
                      "frac_of_measured_bf16_gemm": (round(achieved / ceilings["bf16_gemm_M512_TFLOP/s"], 4)
                                                     if ceilings else None),
-                     "timing": "HIP events on the launch stream before each timed step's gate launch and after "
-                               "the up launch that follows it (no event between the two), elapsed / 2, mean over "
-                               "the timed steps"},
+                     "the_measured_bf16_gemm": "torch.nn.functional.linear on one of the pair's projections (same "
+                                               "per-projection shape)",
+                     "timing": "HIP events on the launch stream just before and after each timed step's fused "
+                               "gate/up launch, mean over the timed steps"},
         "measured_ceiling": ceilings,
         "breakdown_timing": "separate pass after the timed region: HIP events around every call",
         "qmv_vocab_last_row": {"GB/s": round(vocab_bytes / vocab["avg_us"] / 1e3, 1),
