@@ -706,8 +706,35 @@ def next_rows(torch, w4, projections, copies, reps=20):
                                **roof(rows, p["N"], p["K"], f / t / 1e6)})
             del rot, y, xs
         layer_flops = sum(flops(rows, r["N"], r["K"]) for r in short_rows)
+        # the same layer launched as the step launches it: q|k|v grouped, o, the fused gate|up pair
+        # (its h feeding down), down; weights rotated per call
+        xa = torch.from_numpy(synth.activations(cfg, synth.shape_index(cfg, "q"), rows, by["q"]["K"]).view("int16"))
+        xa = xa.view(torch.bfloat16).to(dev)
+        xo = torch.from_numpy(synth.activations(cfg, synth.shape_index(cfg, "o"), rows, by["o"]["K"]).view("int16"))
+        xo = xo.view(torch.bfloat16).to(dev)
+        xg = torch.from_numpy(synth.activations(cfg, synth.shape_index(cfg, "gate"), rows,
+                                                by["gate"]["K"]).view("int16")).view(torch.bfloat16).to(dev)
+        rots = {n: rotation(by[n]["w"][0]) for n in LAYER}
+        nrot = min(len(r) for r in rots.values())
+        ys = [torch.empty((rows, by[n]["N"]), dtype=torch.bfloat16, device=dev) for n in GROUPED]
+        yo = torch.empty((rows, by["o"]["N"]), dtype=torch.bfloat16, device=dev)
+        h = torch.empty((rows, by["gate"]["N"]), dtype=torch.bfloat16, device=dev)
+        yd = torch.empty((rows, by["down"]["N"]), dtype=torch.bfloat16, device=dev)
+        seq = []
+        for c in range(nrot):
+            fns = [w4.PreparedGrouped(xa, [rots[n][c] for n in GROUPED], ys=ys),
+                   w4.PreparedLinear(xo, *rots["o"][c], y=yo),
+                   w4.PreparedGateUp(xg, rots["gate"][c], rots["up"][c], h=h),
+                   w4.PreparedLinear(h, *rots["down"][c], y=yd)]
+            seq.append(lambda fns=fns: [f() for f in fns])
+        t_layer = timed(seq)
         out[key] = {"projections": short_rows,
-                    "layer_TFLOP/s": round(layer_flops / sum(r["avg_us"] for r in short_rows) / 1e6, 2)}
+                    "layer_TFLOP/s": round(layer_flops / sum(r["avg_us"] for r in short_rows) / 1e6, 2),
+                    "layer_as_launched_us": round(t_layer, 3),
+                    "layer_as_launched_TFLOP/s": round(layer_flops / t_layer / 1e6, 2),
+                    "layer_as_launched": "q|k|v grouped, o, gate|up fused with SwiGLU (h feeds down), down; "
+                                         "one graph of the four calls per weight copy"}
+        del seq, rots, ys, yo, h, yd, xa, xo, xg
 
     # decode rows on the four decode shapes
     decode = []
