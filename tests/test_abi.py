@@ -415,12 +415,15 @@ def test_grouped_plan_one_launch_over_the_column_tiles():
     qkv = [4096, 1024, 1024]
     for M in (33, 128, 509, 512, 1024, 4096):
         p = grouped_plan(qkv, M, 2560)
-        alone = plan(M, 6144, 2560, split_k=1)        # the tile form of one 6144-column projection
-        assert p["path"] == w4.PATH_GROUPED and p["split_k"] == 1 and p["grid_z"] == 1
+        alone = plan(M, 6144, 2560)        # the tile form and split of one 6144-column projection
+        assert p["path"] == w4.PATH_GROUPED and p["grid_z"] == p["split_k"]
         assert p["grid_x"] == 48 and p["grid_y"] == -(-M // p["tile_m"])
-        assert (p["tile_m"], p["tile_n"], p["variant"], p["block_threads"]) == \
-            (alone["tile_m"], alone["tile_n"], alone["variant"], alone["block_threads"])
+        assert (p["tile_m"], p["tile_n"], p["variant"], p["block_threads"], p["split_k"]) == \
+            (alone["tile_m"], alone["tile_n"], alone["variant"], alone["block_threads"], alone["split_k"])
+        # the partials of every projection in one [S][M][48 * 128] array
         assert p["workspace_bytes"] == alone["workspace_bytes"]
+    # an under-filled grid splits (96 tiles at 128 rows), a filled one does not
+    assert grouped_plan(qkv, 128, 2560)["split_k"] > 1 and grouped_plan(qkv, 512, 2560)["split_k"] == 1
     # ragged projections: each owns ceil(N / 128) column tiles
     assert grouped_plan([200, 96, 1000], 509, 256)["grid_x"] == 2 + 1 + 8
     # the exact-code form above 1024 rows: the group sums of the shared x, once

@@ -54,6 +54,43 @@ def test_qkv_prefill_matches_oracle(lib, M):
     _check_all(ys, problems, rows=rows)
 
 
+def test_qkv_128_rows_split_matches_oracle(lib):
+    """The 128-row q, k and v: an under-filled grid, split along K with one grouped slice sum."""
+    import torch
+    M = 128
+    problems = _shared_x([synth.problem(3, name) for name in ("q", "k", "v")])
+    plan = lib.w4a16_grouped_plan([p["N"] for p in problems], M, problems[0]["K"])
+    announce(f"grouped qkv M={M} plan {plan}")
+    assert plan["path"] == lib.PATH_GROUPED and plan["split_k"] > 1
+    x, w = _devices(problems)
+    ys = lib.w4a16_linear_grouped(x, w)
+    torch.cuda.synchronize()
+    _check_all(ys, problems)
+
+
+@pytest.mark.parametrize("kind", ["sums", "pow2"])
+def test_split_integer_cases_are_bit_exact_and_repeat(lib, kind):
+    """A split grouped launch on integer inputs: exact, and the same bits on a second call."""
+    import torch
+    M, K = 96, 2560
+    cases = [_exact_case(kind, M, n, K, seed=3000 + i + 10 * (kind == "pow2")) for i, n in enumerate((640, 256))]
+    x_bits = cases[0][0]["x"]
+    xi = synth.from_bf16_bits(x_bits).astype(np.float64)
+    problems = [dict(p, x=x_bits) for p, _ in cases]
+    plan = lib.w4a16_grouped_plan([p["N"] for p in problems], M, K)
+    announce(f"grouped split integer {kind} plan {plan}")
+    assert plan["split_k"] > 1
+    x, w = _devices(problems)
+    first = [bits(y) for y in lib.w4a16_linear_grouped(x, w)]
+    second = [bits(y) for y in lib.w4a16_linear_grouped(x, w)]
+    torch.cuda.synchronize()
+    for p, a, b in zip(problems, first, second):
+        q = np.stack([(p["wq"] >> (4 * i)) & 0xF for i in range(8)], axis=-1).reshape(p["N"], K).astype(np.float64)
+        wv = q if kind == "sums" else (q - 8) / 64.0
+        assert np.array_equal(a, synth.to_bf16_bits((xi @ wv.T).astype(np.float32))), f"N={p['N']}"
+        assert np.array_equal(a, b)
+
+
 def test_ragged_projections_and_rows(lib):
     """Projections whose column counts are not multiples of the 128-column tile, at a ragged M."""
     import torch
@@ -132,11 +169,13 @@ def test_one_and_four_projections(lib, count):
     _check_all(ys, problems)
 
 
-def test_no_write_outside_any_output(lib):
+@pytest.mark.parametrize("K", [256, 2560])
+def test_no_write_outside_any_output(lib, K):
     """The outputs are views into one buffer with poisoned gaps between and around them: every gap
-    keeps its bit pattern, and every output element is written."""
+    keeps its bit pattern, and every output element is written (unsplit at K = 256, split with
+    the grouped slice sum at K = 2560)."""
     import torch
-    M, K = 70, 256
+    M = 70
     problems = _shared_x([synth.random_problem(80 + i, M, n, K) for i, n in enumerate((136, 72, 260))])
     gap = 4096
     sizes = [M * p["N"] for p in problems]
@@ -149,7 +188,7 @@ def test_no_write_outside_any_output(lib):
         spans.append((off, off + n))
         off += n + gap
     x, w = _devices(problems)
-    announce("grouped poisoned gaps")
+    announce(f"grouped poisoned gaps K={K} plan {lib.w4a16_grouped_plan([p['N'] for p in problems], M, K)}")
     lib.w4a16_linear_grouped(x, w, ys=ys)
     torch.cuda.synchronize()
     host = buf.cpu().numpy().view(np.uint16)

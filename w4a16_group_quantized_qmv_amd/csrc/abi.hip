@@ -333,12 +333,13 @@ int run_qmm(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint
 }
 
 // Grouped projections of one input.  With more than 32 rows the projections' 128-column tiles
-// form one grid (the tile form the qmm policy takes for M rows and the summed tile columns,
-// never split); with at most 32 rows, or one projection, each projection runs its own
+// form one grid: the tile form and the split that the qmm policy takes for M rows and the summed
+// tile columns (a split's partials of every projection in one array, summed by one grouped
+// slice-sum launch); with at most 32 rows, or one projection, each projection runs its own
 // w4a16_linear dispatch and the workspace is the largest of theirs.
 static_assert(W4A16_MAX_GROUPED == kMaxGroupedProjections, "one limit for the ABI and the kernel");
 int make_grouped_plan(int32_t count, const int64_t* N, int64_t M, int64_t K, int32_t group, int32_t num_cus,
-                      w4a16_plan_t* out, bool codes = true) {
+                      w4a16_plan_t* out, bool codes = true, int32_t split_k = 0) {
     if (!out || !N) return W4A16_ERR_NULL;
     if (count < 1 || count > W4A16_MAX_GROUPED) return W4A16_ERR_SHAPE;
     int64_t tiles_n = 0;
@@ -364,7 +365,7 @@ int make_grouped_plan(int32_t count, const int64_t* N, int64_t M, int64_t K, int
         out->workspace_bytes = ws;
         return W4A16_OK;
     }
-    plan_qmm(M, tiles_n * kGroupedTileN, K, 1, cus, out, false, codes);
+    plan_qmm(M, tiles_n * kGroupedTileN, K, split_k, cus, out, false, codes);
     out->path = W4A16_PATH_GROUPED;
     out->num_cus = cus;
     return W4A16_OK;
@@ -407,8 +408,8 @@ int run_grouped(const uint16_t* x, int32_t count, const uint32_t* const* wq, con
         return W4A16_OK;
     }
     const int32_t cus = pl.num_cus;
-    st = fit_workspace(pl, 1, workspace, ws_bytes, [&](int32_t, bool codes) {
-        make_grouped_plan(count, N, M, K, group, cus, &pl, codes);
+    st = fit_workspace(pl, 0, workspace, ws_bytes, [&](int32_t S, bool codes) {
+        make_grouped_plan(count, N, M, K, group, cus, &pl, codes, S);
     });
     if (st != W4A16_OK) return st;
     QmmGroups g{};
@@ -424,13 +425,19 @@ int run_grouped(const uint16_t* x, int32_t count, const uint32_t* const* wq, con
         tn += static_cast<int>(ceil_div(N[p], kGroupedTileN));
     }
     const int m = static_cast<int>(M), k = static_cast<int>(K);
+    // workspace: [group sums (exact-code mode)][fp32 split-K partials of the concatenated columns]
     uint16_t* xsum = nullptr;
+    uint8_t* rest = static_cast<uint8_t*>(workspace);
     if (plan_codes(pl)) {
         xsum = static_cast<uint16_t*>(workspace);
+        rest += group_sum_bytes(M, K);
         const hipError_t e0 = launch_act_group_sums(x, xsum, m, k, group_sum_cols(k), hs);
         if (e0 != hipSuccess) return to_status(e0);
     }
-    return to_status(launch_qmm_grouped(plan_tile_variant(pl), x, xsum, g, m, k, hs));
+    float* ws = pl.split_k > 1 ? reinterpret_cast<float*>(rest) : nullptr;
+    hipError_t e = launch_qmm_grouped(plan_tile_variant(pl), x, xsum, g, ws, m, k, pl.split_k, hs);
+    if (e != hipSuccess || pl.split_k == 1) return to_status(e);
+    return to_status(launch_splitk_reduce_grouped(ws, g, m, pl.split_k, hs));
 }
 
 // Gate / up pair with SwiGLU: one tile kernel computes both projections of the same columns.

@@ -95,8 +95,7 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, cons
 
 // Grouped projections of one input (at most kMaxGroupedProjections): y_p = x . dequant(wq_p)^T,
 // one launch over the concatenation of the projections' column tiles.  Projection p owns the
-// column tiles [tn_first[p], tn_first[p + 1]) of 128 columns each (its last tile may be ragged);
-// count = 0 marks an ordinary single-projection launch.  Unsplit only.
+// column tiles [tn_first[p], tn_first[p + 1]) of 128 columns each (its last tile may be ragged).
 constexpr int kMaxGroupedProjections = 4;
 constexpr int kGroupedTileN = 128;   // columns per tile of every qmm tile form
 struct QmmGroups {
@@ -108,8 +107,14 @@ struct QmmGroups {
     int tn_first[kMaxGroupedProjections];
     int count;
 };
-hipError_t launch_qmm_grouped(int variant, const uint16_t* x, const uint16_t* xsum, const QmmGroups& groups, int M,
-                              int K, hipStream_t stream);
+// Columns of the concatenated tile grid (a multiple of 128).
+int grouped_columns(const QmmGroups& groups);
+// split > 1 writes fp32 partials ws[z][M][grouped_columns] (every projection's columns at its
+// tiles' place), summed into the outputs by launch_splitk_reduce_grouped.
+hipError_t launch_qmm_grouped(int variant, const uint16_t* x, const uint16_t* xsum, const QmmGroups& groups,
+                              float* ws, int M, int K, int split, hipStream_t stream);
+hipError_t launch_splitk_reduce_grouped(const float* ws, const QmmGroups& groups, int M, int split,
+                                        hipStream_t stream);
 
 // Gate / up pair with SwiGLU: h = bf16(silu(x . gate^T) * (x . up^T)), one tile kernel for both
 // projections.  split > 1 writes fp32 partials ws[0][z][M][N] (gate) and ws[1][z][M][N] (up).

@@ -115,6 +115,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     const int groups = g_end - g_begin;
     const int m0 = tm * BM;
     int n0 = tn * BN;
+    // grouped launches: the split-K partials of every projection share one [split][M][NG] array
+    // of the concatenated tile columns (NG = the launch's N, before a projection takes over)
+    const int NG = N, n0g = n0;
     // Grouped launch: the projection that owns column tile tn takes over the weight, scale,
     // bias and output pointers and the column count (scalar selects with constant indices, so
     // the argument block is never copied to be indexed).
@@ -604,10 +607,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
                 if (col >= N) continue;
                 const size_t idx = static_cast<size_t>(m) * N + col;
                 if constexpr (NP == 1) {
-                    if (split == 1)
+                    if (split == 1) {
                         y[idx] = f32_to_bf16_bits(acc[rb][cb][r]);
-                    else
+                    } else if constexpr (GRP) {
+                        ws[(static_cast<size_t>(z) * M + m) * NG + (n0g - n0) + col] = acc[rb][cb][r];
+                    } else {
                         ws[static_cast<size_t>(z) * M * N + idx] = acc[rb][cb][r];
+                    }
                 } else {
                     // gate partials in plane 0, up partials in plane 1 (each [split][M][N])
                     const float gv = acc[rb][cb][r], uv = acc[rb][NB + cb][r];
@@ -724,7 +730,7 @@ static hipError_t launch_qmm_t(const uint16_t* x, const uint16_t* xsum, int KB, 
         quad = quad && quad_scales(K, split, s, b);
     }
     // only the tile forms a grouped plan can pick are compiled in the grouped form
-    if (grp && (!GROUPED_FORM || split != 1)) return hipErrorInvalidValue;
+    if (grp && !GROUPED_FORM) return hipErrorInvalidValue;
     const QmmGroups none{};
     const QmmGroups& g = grp ? *grp : none;
 #define W4A16_LAUNCH_QMM(WPS, CODES, SBQ, XS)                                                                        \
@@ -833,13 +839,48 @@ hipError_t launch_qmm(int variant, const uint16_t* x, const uint16_t* xsum, cons
     return dispatch_qmm(variant, x, xsum, wq, scales, biases, y, ws, M, N, K, split, stream, nullptr);
 }
 
-hipError_t launch_qmm_grouped(int variant, const uint16_t* x, const uint16_t* xsum, const QmmGroups& groups, int M,
-                              int K, hipStream_t stream) {
-    if (groups.count < 1 || groups.count > kMaxGroupedProjections) return hipErrorInvalidValue;
+int grouped_columns(const QmmGroups& groups) {
     const int last = groups.count - 1;
-    const int tiles_n = groups.tn_first[last] + (groups.n[last] + kGroupedTileN - 1) / kGroupedTileN;
-    return dispatch_qmm(variant, x, xsum, groups.wq[0], groups.s[0], groups.b[0], groups.y[0], nullptr, M,
-                        tiles_n * kGroupedTileN, K, 1, stream, &groups);
+    return (groups.tn_first[last] + (groups.n[last] + kGroupedTileN - 1) / kGroupedTileN) * kGroupedTileN;
+}
+
+hipError_t launch_qmm_grouped(int variant, const uint16_t* x, const uint16_t* xsum, const QmmGroups& groups,
+                              float* ws, int M, int K, int split, hipStream_t stream) {
+    if (groups.count < 1 || groups.count > kMaxGroupedProjections || split < 1 || (split > 1 && !ws))
+        return hipErrorInvalidValue;
+    return dispatch_qmm(variant, x, xsum, groups.wq[0], groups.s[0], groups.b[0], groups.y[0], ws, M,
+                        grouped_columns(groups), K, split, stream, &groups);
+}
+
+// Slice sums of a grouped split launch: element (m, c) of the [M][NG] partial planes belongs to
+// the projection that owns column tile c / 128; y_p[m][c - 128 tn_first[p]] = bf16(sum_z), slices
+// in order.  Columns past a projection's last column (its ragged tile) are skipped.
+__global__ __launch_bounds__(256) void splitk_reduce_grouped_kernel(const float* __restrict__ ws, const QmmGroups g,
+                                                                    int M, int NG, int split) {
+    const int64_t MN = static_cast<int64_t>(M) * NG;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= MN) return;
+    const int m = static_cast<int>(i / NG), c = static_cast<int>(i - static_cast<int64_t>(m) * NG);
+    const int tn = c / kGroupedTileN;
+    const int p = (g.count > 1 && tn >= g.tn_first[1] ? 1 : 0) + (g.count > 2 && tn >= g.tn_first[2] ? 1 : 0) +
+                  (g.count > 3 && tn >= g.tn_first[3] ? 1 : 0);
+    auto pick = [p](auto a0, auto a1, auto a2, auto a3) { return p == 0 ? a0 : p == 1 ? a1 : p == 2 ? a2 : a3; };
+    const int n = pick(g.n[0], g.n[1], g.n[2], g.n[3]);
+    const int local = c - pick(g.tn_first[0], g.tn_first[1], g.tn_first[2], g.tn_first[3]) * kGroupedTileN;
+    if (local >= n) return;
+    float v = ws[i];
+    for (int z = 1; z < split; ++z) v += ws[z * MN + i];
+    uint16_t* y = pick(g.y[0], g.y[1], g.y[2], g.y[3]);
+    y[static_cast<size_t>(m) * n + local] = f32_to_bf16_bits(v);
+}
+
+hipError_t launch_splitk_reduce_grouped(const float* ws, const QmmGroups& groups, int M, int split,
+                                        hipStream_t stream) {
+    const int NG = grouped_columns(groups);
+    const int64_t MN = static_cast<int64_t>(M) * NG;
+    hipLaunchKernelGGL(splitk_reduce_grouped_kernel, dim3(static_cast<unsigned>((MN + 255) / 256)), dim3(256), 0,
+                       stream, ws, groups, M, NG, split);
+    return hipGetLastError();
 }
 
 const QmmShape kGateUpVariants[kNumGateUpVariants] = {
