@@ -181,11 +181,17 @@ def test_all_zero_codes(lib, path):
 # (N, K, M, kernel the policy picks): 0 = 16-column dequantizing workgroups splitting K four ways,
 # 1 = 64-column workgroups, 2 = persistent wide kernel (activations and their group sums staged
 # in LDS once, one wave per 16-column block), 3 = row-amortized 16-column workgroups (exact codes
-# on the matrix core, s * P + b * X per group)
+# on the matrix core, s * P + b * X per group), 4 = burst (up to 4 rows: every wave issues all
+# its loads at once)
 QMV_FAMILY_CASES = [
-    (4000, 256, 3, 3),       # ragged N
-    (6150, 384, 1, 3),       # odd group count, ragged N
-    (2600, 8192, 3, 0),      # 64 groups: the dequantizing K-split kernel
+    (4000, 256, 3, 4),       # burst, ragged N
+    (6150, 384, 1, 4),       # burst, odd group count, ragged N
+    (4000, 256, 6, 3),       # row-amortized, ragged N
+    (6150, 384, 5, 3),       # row-amortized, odd group count
+    (2600, 8192, 3, 4),      # 64 groups: burst, 4 groups in each of 16 waves
+    (2600, 8192, 5, 0),      # 64 groups above 4 rows: the dequantizing K-split kernel
+    (1000, 10240, 2, 4),     # 80 groups: the burst kernel's largest share (16 waves x 5)
+    (1000, 10368, 2, 0),     # 81 groups: past it
     (1000, 9728, 8, 0),      # long K, ragged N
     (16390, 384, 8, 1),      # 1025 blocks, odd group count
     (24600, 256, 1, 2),      # one group pair per block: every step ends a block
@@ -193,7 +199,8 @@ QMV_FAMILY_CASES = [
     (30010, 1024, 8, 2),     # eight rows
     (24600, 384, 2, 1),      # odd group count: the wide kernel does not apply
     (16400, 4096, 4, 2),     # wide from 1024 blocks once K >= 4096
-    (9728, 4096, 4, 3),      # 608 blocks at K = 4096: row-amortized
+    (9728, 4096, 4, 4),      # 608 blocks at K = 4096: burst, 3 groups per wave
+    (9728, 4096, 7, 3),      # the same above 4 rows: row-amortized
     (24600, 9728, 8, 1),     # activations too large for the wide kernel's LDS
 ]
 

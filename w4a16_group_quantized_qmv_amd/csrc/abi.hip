@@ -88,13 +88,19 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
     // 16-column dequantizing kernel whose four waves split K leads by 5-20%; around 16k columns
     // the 64-column kernel leads; from 24k columns (16k at 32 groups or more) the persistent wide
     // kernel, which streams whole blocks per wave, wins by 1.4x on the 151936-column head.
+    // Below 16k columns at up to 4 rows and 80 groups, the burst kernel (every load of a wave
+    // issued at once, 2..5 groups per wave) leads both: 4-14% at K = 2560 (N = 1024 .. 9728)
+    // and 4-10% at K = 9728.
     const int64_t blocks16 = ceil_div(N, 16);
     const int64_t G = K / W4A16_GROUP;
     int variant;
+    int burst_kw = 0, burst_gpw = 0;
     if (qmv_wide_fits(static_cast<int>(M), static_cast<int>(K)) && (blocks16 >= 1536 || (blocks16 >= 1024 && G >= 32)))
         variant = kQmvWideVariant;
     else if (blocks16 >= 1024)
         variant = 1;
+    else if (qmv_burst_shape(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), &burst_kw, &burst_gpw))
+        variant = kQmvBurstVariant;
     else if (G >= 64 && M <= kQmvMaxRows)
         variant = 0;
     else
@@ -111,6 +117,9 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
         waves = qmv_wide_waves(static_cast<int>(M));
         p->tile_n = 16;
         p->grid_x = static_cast<int32_t>(std::min<int64_t>(ceil_div(blocks16, waves), int64_t{32 / waves} * cus));
+    } else if (variant == kQmvBurstVariant) {
+        waves = burst_kw;
+        p->grid_x = static_cast<int32_t>(blocks16);
     } else {
         p->grid_x = static_cast<int32_t>(ceil_div(N, p->tile_n));
     }
@@ -118,7 +127,7 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
     p->grid_z = 1;
     p->block_threads = 64 * waves;
     p->split_k = 1;
-    p->k_waves = v.kw;
+    p->k_waves = variant == kQmvBurstVariant ? burst_kw : v.kw;
     p->variant = variant;
     p->workspace_bytes = 0;
 }

@@ -15,7 +15,7 @@ struct QmvShape {
 };
 
 // Kernel instances compiled for qmv (index = plan variant).
-constexpr int kNumQmvVariants = 4;
+constexpr int kNumQmvVariants = 5;
 extern const QmvShape kQmvVariants[kNumQmvVariants];
 
 // The wide (persistent) qmv instances: 16-column blocks, 2 LDS stages, workgroups of
@@ -24,6 +24,17 @@ constexpr int kQmvWideVariant = 2;
 // The row-amortized kernel of the width-generic matvec at 4 bits (16 columns, 4 waves split K):
 // exact integer codes on the matrix core and y += s * P + b * X per group.
 constexpr int kQmvAmortizedVariant = 3;
+// The burst kernel (4-bit, at most 4 rows): a workgroup of up to kQmvBurstMaxWaves waves on one
+// 16-column block, each wave owning at most kQmvBurstMaxGroups groups and issuing all their
+// loads before it computes; the wave count depends on the shape (qmv_burst_shape).
+constexpr int kQmvBurstVariant = 4;
+constexpr int kQmvBurstMaxWaves = 16;
+constexpr int kQmvBurstMaxGroups = 5;
+// The burst kernel's waves per workgroup and groups per wave for an M x N x K matvec; false
+// where it does not apply (more than 4 rows, or more than 16 * 5 groups).
+bool qmv_burst_shape(int M, int N, int K, int* kw, int* gpw);
+hipError_t launch_qmv_burst(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                            uint16_t* y, int M, int N, int K, hipStream_t stream);
 constexpr int kQmvWideStages = 2;
 // Its LDS: per wave and stage one 2 KB block of codes plus 512 bytes of scales and biases
 // (with 1 KB allowed for the kernel's small placeholder objects); dynamically the permuted

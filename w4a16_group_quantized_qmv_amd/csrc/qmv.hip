@@ -507,6 +507,7 @@ const QmvShape kQmvVariants[kNumQmvVariants] = {
     {2, 2, 2},   // 1: 64 columns per workgroup, 2 waves split K
     {1, 4, 1},   // 2: wide: persistent, 16-column blocks, 8-wave (M <= 4) or 4-wave workgroups, 2 LDS stages
     {1, 1, 4},   // 3: row-amortized (width-generic kernel at 4 bits), 16 columns, 4 waves split K
+    {1, 1, 0},   // 4: burst, 16 columns, 1..16 waves split K (the count depends on the shape)
 };
 
 template <int CB, int WN, int KW>
@@ -582,6 +583,7 @@ hipError_t launch_qmv(int variant, const uint16_t* x, const uint32_t* wq, const 
                        ? launch_qmv_wide_t<1, kQmvWideStages, 8>(x, wq, scales, biases, y, M, N, K, stream)
                        : launch_qmv_wide_t<1, kQmvWideStages, 4>(x, wq, scales, biases, y, M, N, K, stream);
         case kQmvAmortizedVariant: return launch_qmv_bits(4, kQmvBitsMatrix, x, wq, scales, biases, y, M, N, K, stream);
+        case kQmvBurstVariant: return launch_qmv_burst(x, wq, scales, biases, y, M, N, K, stream);
         default: return hipErrorInvalidValue;
     }
 }

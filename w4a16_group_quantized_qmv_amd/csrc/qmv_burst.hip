@@ -1,0 +1,232 @@
+// qmv_burst: the 4-bit affine matvec for up to four decode rows, one HBM round trip per wave.
+//
+// The operation is the one of the W4 layout ("Week 2 Day 6" and the qmv_wide pages): a
+// column's 4-bit codes packed eight per uint32, low nibble first; one bf16 scale and bias per
+// 128 reduction values, w = s * q + b; y[m, n] = sum_k x[m, k] * w[n, k] in fp32.
+//
+// Why a separate kernel: at decode widths a matvec over a few MB of codes is latency bound,
+// not bandwidth bound.  The loop kernels keep one group in flight per wave, so a wave waits
+// for HBM once per group pair.  Here a workgroup is KW waves on one 16-column block, wave w
+// owns at most GPW consecutive groups, and it issues every load of its share -- codes,
+// scales, biases and its slice of the activations -- before the first matrix-core
+// instruction, then waits once.  Many short waves (KW up to 16 per block, GPW 2..5 groups
+// each) put the whole matrix in flight within about one memory latency.
+//
+// Per group (lane l: column c = l % 16, reduction values kq*32 .. kq*32 + 31, kq = l / 16 --
+// the B operand of v_mfma_f32_16x16x32_bf16), the codes become exact bf16 integers in the
+// permuted order of codes_bf16_permuted(); the activations (rows 0..M-1 of the A operand,
+// zero beyond) are put in the same order once, into the wave's own LDS slice, and read back as
+// A operands.  P = sum x*q and X = sum x come from the matrix core and y += s*P + b*X, the
+// row-amortized form of the affine dequantization.  The waves' partial sums are added in wave
+// order through LDS, so a result does not depend on timing.  Every load goes through a buffer
+// resource: columns past N and rows past M read zeros.
+#include "device_common.h"
+#include "internal.h"
+
+#include <atomic>
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int kBurstRows = 4;        // rows one launch serves (the A operand holds 16; 4 keep LDS small)
+
+// LDS of a KW-wave workgroup: each wave's activation slice (GPW groups x 16 chunks of 16
+// bytes per row), then the partial sums of waves 1..KW-1 (4 fp32 per lane).
+constexpr size_t burst_x_bytes(int gpw) { return static_cast<size_t>(gpw) * 16 * kBurstRows * 16; }
+constexpr size_t burst_lds_bytes(int kw, int gpw) {
+    return static_cast<size_t>(kw) * burst_x_bytes(gpw) + static_cast<size_t>(kw - 1) * 4 * 64 * 4;
+}
+
+}  // namespace
+
+template <int GPW>
+__global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int N, int K) {
+    extern __shared__ __attribute__((aligned(16))) u32x4_t lds[];
+    const int KW = static_cast<int>(blockDim.x) >> 6;
+    const int G = K >> 7;
+    const int lane = threadIdx.x & 63;
+    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col0 = blockIdx.x * 16;
+    const int g0 = static_cast<int>(static_cast<int64_t>(wk) * G / KW);
+    const int g1 = static_cast<int>(static_cast<int64_t>(wk + 1) * G / KW);
+    const int ng = g1 - g0;   // at most GPW (the launcher checks ceil(G / KW) <= GPW)
+    const int c = lane & 15, kq = lane >> 4;
+    const int row_bytes = K / 2;
+    auto clamp_records = [](int64_t bytes) { return static_cast<int>(bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes); };
+    const int64_t cols = static_cast<int64_t>(N - col0);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + static_cast<size_t>(col0) * row_bytes), 0,
+        clamp_records(cols * row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(scales + static_cast<size_t>(col0) * G), 0, clamp_records(cols * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(biases + static_cast<size_t>(col0) * G), 0, clamp_records(cols * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x), 0, clamp_records(static_cast<int64_t>(M) * K * 2), 0x00020000);
+    // a zero-sized resource: loads of groups the wave does not own return zeros
+    const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, 0, 0x00020000);
+    const uint32_t wvoff = static_cast<uint32_t>(c * row_bytes + kq * 16);
+    const uint32_t sbvoff = static_cast<uint32_t>(c * G * 2);
+    u32x4_t* const xs = lds + static_cast<size_t>(wk) * GPW * 16 * kBurstRows;
+    float* const red = reinterpret_cast<float*>(lds + static_cast<size_t>(KW) * GPW * 16 * kBurstRows);
+
+    // 1. every load of the wave: codes (16 bytes per lane and group), scales, biases, then the
+    //    activation slice: chunk j = ((gl * 4 + t) * 4 + q) * M + m holds row m's 8 values
+    //    gl*128 + q*32 + t*8 .. +7 of the wave's group gl (q: the lanes' kq, t: the operand)
+    uint32_t w[GPW][4];
+    uint16_t sv[GPW], bv[GPW];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        const bool live = i < ng;
+        const int g = g0 + (live ? i : 0);
+        const u32x4_t v =
+            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(live ? wr : none, wvoff, g * 64, 0));
+        w[i][0] = v[0];
+        w[i][1] = v[1];
+        w[i][2] = v[2];
+        w[i][3] = v[3];
+    }
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        const bool live = i < ng;
+        const int g = g0 + (live ? i : 0);
+        sv[i] = __builtin_amdgcn_raw_buffer_load_b16(live ? sr : none, sbvoff, g * 2, 0);
+        bv[i] = __builtin_amdgcn_raw_buffer_load_b16(live ? br : none, sbvoff, g * 2, 0);
+    }
+    const int chunks = ng * 16 * M;
+    constexpr int XL = (GPW * 16 * kBurstRows + 63) / 64;
+    u32x4_t xv[XL];
+#pragma unroll
+    for (int j0 = 0; j0 < XL; ++j0) {
+        const int j = j0 * 64 + lane;
+        uint32_t voff = 0x80000000u;   // past the end: reads zero
+        if (j < chunks) {
+            const int m = j % M;
+            int r = j / M;
+            const int q = r & 3;
+            r >>= 2;
+            const int t = r & 3;
+            const int gl = r >> 2;
+            voff = static_cast<uint32_t>(m * K + (g0 + gl) * kGroup + q * 32 + t * 8) * 2u;
+        }
+        xv[j0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, voff, 0, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all loads issued before anything waits on one
+#pragma unroll
+    for (int j0 = 0; j0 < XL; ++j0) {
+        const int j = j0 * 64 + lane;
+        if (j < chunks) xs[j] = __builtin_bit_cast(u32x4_t, permute_like_codes(xv[j0]));
+    }
+    // the slice is the wave's own: LDS accesses of one wave complete in order, so only the
+    // compiler must keep the reads below after these writes
+    asm volatile("" ::: "memory");
+
+    // 2. every group: rows 4*kq + r of column c
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    const u32x4_t zu = {0u, 0u, 0u, 0u};
+    const bf16x8_t ones = {__bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f),
+                           __bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f)};
+    const int arow = lane & 15;
+    f32x4_t yacc = zero4;
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        if (i < ng) {
+            f32x4_t xsum = zero4, p = zero4;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const u32x4_t av = arow < M ? xs[((i * 4 + t) * 4 + kq) * M + arow] : zu;
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+                xsum = mfma16x16x32(a, ones, xsum);
+                p = mfma16x16x32(a, codes_bf16_permuted(w[i][t]), p);
+            }
+            const float s = bf16_bits_to_f32(sv[i]), b = bf16_bits_to_f32(bv[i]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, p[r], __builtin_fmaf(b, xsum[r], yacc[r]));
+        }
+    }
+
+    // 3. waves 1..KW-1 hand their sums to wave 0, which adds them in wave order
+    if (KW > 1) {
+        if (wk > 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[((wk - 1) * 4 + r) * 64 + lane] = yacc[r];
+        }
+        __syncthreads();
+        if (wk == 0) {
+            for (int j = 0; j < KW - 1; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yacc[r] += red[(j * 4 + r) * 64 + lane];
+        }
+    }
+    if (wk == 0) {
+        const int col = col0 + c;
+        if (col < N) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * kq + r;
+                if (m < M) y[static_cast<size_t>(m) * N + col] = f32_to_bf16_bits(yacc[r]);
+            }
+        }
+    }
+}
+
+bool qmv_burst_shape(int M, int N, int K, int* kw, int* gpw) {
+    const int G = K / kGroup;
+    if (M < 1 || M > kBurstRows || K % kGroup != 0 || G < 1 || N < 1) return false;
+    // Measured on MI355X (M = 1 and 4; K = 2560 and 9728; N = 1024 .. 9728; graph-replayed
+    // launches over rotating weights): the fewer groups a wave owns the better, as long as the
+    // launch has enough workgroups -- two groups per wave up to 256 column blocks, three from
+    // 512 blocks (9728 columns at K = 2560: 7.4 us against 7.8 with two, 8.6 for the
+    // row-amortized loop kernel); above 32 groups, as few as 16 waves allow (K = 9728: 5
+    // groups, 9.5 us against 10.5).
+    const int blocks = (N + 15) / 16;
+    int g = blocks >= 512 ? 3 : 2;
+    const int need = (G + kQmvBurstMaxWaves - 1) / kQmvBurstMaxWaves;
+    if (need > g) g = need;
+    if (g > kQmvBurstMaxGroups) return false;
+    *gpw = g;
+    *kw = (G + g - 1) / g;
+    return true;
+}
+
+template <int GPW>
+static hipError_t launch_burst_t(int kw, const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                                 uint16_t* y, int M, int N, int K, hipStream_t stream) {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<bool> ready[kMaxDevices];   // per instance and device: the LDS permission is set
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    auto kern = qmv_burst_kernel<GPW>;
+    if (!ready[dev].load(std::memory_order_acquire)) {
+        // the largest workgroup's LDS (16 waves) may pass the 64 KB a launch gets by default
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(burst_lds_bytes(kQmvBurstMaxWaves, GPW)));
+        if (e != hipSuccess) return e;
+        ready[dev].store(true, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(kern, dim3((N + 15) / 16), dim3(64 * kw), burst_lds_bytes(kw, GPW), stream, x, wq, s, b, y, M,
+                       N, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_qmv_burst(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
+                            uint16_t* y, int M, int N, int K, hipStream_t stream) {
+    int kw = 0, gpw = 0;
+    if (!qmv_burst_shape(M, N, K, &kw, &gpw)) return hipErrorInvalidValue;
+    // every wave's share fits its registers: ceil(G / kw) <= gpw, and kw <= the bound
+    if (kw < 1 || kw > kQmvBurstMaxWaves || (K / kGroup + kw - 1) / kw > gpw) return hipErrorInvalidValue;
+    switch (gpw) {
+        case 2: return launch_burst_t<2>(kw, x, wq, scales, biases, y, M, N, K, stream);
+        case 3: return launch_burst_t<3>(kw, x, wq, scales, biases, y, M, N, K, stream);
+        case 4: return launch_burst_t<4>(kw, x, wq, scales, biases, y, M, N, K, stream);
+        case 5: return launch_burst_t<5>(kw, x, wq, scales, biases, y, M, N, K, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace w4a16
