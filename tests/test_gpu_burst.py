@@ -19,11 +19,11 @@ BURST = 4   # the plan's instance index of the burst kernel
 # (N, K) and what the plan makes of it at 1..4 rows
 SHAPES = [
     (96, 128),      # one group: a single wave
-    (33, 640),      # five groups over three waves (1, 2, 2), ragged N
+    (33, 640),      # five groups over three waves (2, 2, 1), ragged N
     (160, 2560),    # 20 groups: ten waves of two
-    (9728, 2560),   # 608 column blocks: seven waves of two or three
+    (9728, 2560),   # 608 column blocks: seven waves of three (the last of two)
     (200, 8192),    # 64 groups: sixteen waves of four
-    (300, 9728),    # 76 groups: sixteen waves of four or five
+    (300, 9728),    # 76 groups: fifteen waves of five and one of one
     (50, 10240),    # 80 groups: sixteen waves of five, the largest share
 ]
 

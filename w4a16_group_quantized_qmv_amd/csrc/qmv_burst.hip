@@ -10,7 +10,9 @@
 // owns at most GPW consecutive groups, and it issues every load of its share -- codes,
 // scales, biases and its slice of the activations -- before the first matrix-core
 // instruction, then waits once.  Many short waves (KW up to 16 per block, GPW 2..5 groups
-// each) put the whole matrix in flight within about one memory latency.
+// each) put the whole matrix in flight within about one memory latency.  KW is a kernel
+// argument: read from the workgroup size, it costs a dependent load from the dispatch packet
+// before the first address (measured 0.2-0.3 us per launch).
 //
 // Per group (lane l: column c = l % 16, reduction values kq*32 .. kq*32 + 31, kq = l / 16 --
 // the B operand of v_mfma_f32_16x16x32_bf16), the codes become exact bf16 integers in the
@@ -30,9 +32,10 @@ namespace w4a16 {
 namespace {
 
 constexpr int kBurstRows = 4;        // rows one launch serves (the A operand holds 16; 4 keep LDS small)
+static_assert(kBurstRows == 4, "the activation chunk index below takes the row from its low two bits");
 
 // LDS of a KW-wave workgroup: each wave's activation slice (GPW groups x 16 chunks of 16
-// bytes per row), then the partial sums of waves 1..KW-1 (4 fp32 per lane).
+// bytes per row), then the partial sums of waves 1..KW-1 (4 fp32 per lane, one 16-byte slot).
 constexpr size_t burst_x_bytes(int gpw) { return static_cast<size_t>(gpw) * 16 * kBurstRows * 16; }
 constexpr size_t burst_lds_bytes(int kw, int gpw) {
     return static_cast<size_t>(kw) * burst_x_bytes(gpw) + static_cast<size_t>(kw - 1) * 4 * 64 * 4;
@@ -43,16 +46,15 @@ constexpr size_t burst_lds_bytes(int kw, int gpw) {
 template <int GPW>
 __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
-    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int N, int K) {
+    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int N, int K, int KW) {
     extern __shared__ __attribute__((aligned(16))) u32x4_t lds[];
-    const int KW = static_cast<int>(blockDim.x) >> 6;
     const int G = K >> 7;
     const int lane = threadIdx.x & 63;
     const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col0 = blockIdx.x * 16;
-    const int g0 = static_cast<int>(static_cast<int64_t>(wk) * G / KW);
-    const int g1 = static_cast<int>(static_cast<int64_t>(wk + 1) * G / KW);
-    const int ng = g1 - g0;   // at most GPW (the launcher checks ceil(G / KW) <= GPW)
+    // wave w owns groups w*GPW .. w*GPW + GPW - 1 (the last wave fewer: KW = ceil(G / GPW))
+    const int g0 = wk * GPW;
+    const int ng = min(GPW, G - g0);
     const int c = lane & 15, kq = lane >> 4;
     const int row_bytes = K / 2;
     auto clamp_records = [](int64_t bytes) { return static_cast<int>(bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes); };
@@ -71,19 +73,19 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_kernel(
     const uint32_t wvoff = static_cast<uint32_t>(c * row_bytes + kq * 16);
     const uint32_t sbvoff = static_cast<uint32_t>(c * G * 2);
     u32x4_t* const xs = lds + static_cast<size_t>(wk) * GPW * 16 * kBurstRows;
-    float* const red = reinterpret_cast<float*>(lds + static_cast<size_t>(KW) * GPW * 16 * kBurstRows);
+    f32x4_t* const red = reinterpret_cast<f32x4_t*>(lds + static_cast<size_t>(KW) * GPW * 16 * kBurstRows);
 
     // 1. every load of the wave: codes (16 bytes per lane and group), scales, biases, then the
-    //    activation slice: chunk j = ((gl * 4 + t) * 4 + q) * M + m holds row m's 8 values
-    //    gl*128 + q*32 + t*8 .. +7 of the wave's group gl (q: the lanes' kq, t: the operand)
+    //    activation slice: chunk j = ((gl * 4 + t) * 4 + q) * 4 + m holds row m's 8 values
+    //    gl*128 + q*32 + t*8 .. +7 of the wave's group gl (q: the lanes' kq, t: the operand).
+    //    Groups past the wave's share read through the zero-sized resource; every offset is
+    //    wave-uniform arithmetic, so no load needs a per-lane resource or offset loop.
     uint32_t w[GPW][4];
     uint16_t sv[GPW], bv[GPW];
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
-        const bool live = i < ng;
-        const int g = g0 + (live ? i : 0);
-        const u32x4_t v =
-            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(live ? wr : none, wvoff, g * 64, 0));
+        const u32x4_t v = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(i < ng ? wr : none, wvoff, (g0 + i) * 64, 0));
         w[i][0] = v[0];
         w[i][1] = v[1];
         w[i][2] = v[2];
@@ -91,40 +93,30 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_kernel(
     }
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
-        const bool live = i < ng;
-        const int g = g0 + (live ? i : 0);
-        sv[i] = __builtin_amdgcn_raw_buffer_load_b16(live ? sr : none, sbvoff, g * 2, 0);
-        bv[i] = __builtin_amdgcn_raw_buffer_load_b16(live ? br : none, sbvoff, g * 2, 0);
+        sv[i] = __builtin_amdgcn_raw_buffer_load_b16(i < ng ? sr : none, sbvoff, (g0 + i) * 2, 0);
+        bv[i] = __builtin_amdgcn_raw_buffer_load_b16(i < ng ? br : none, sbvoff, (g0 + i) * 2, 0);
     }
-    const int chunks = ng * 16 * M;
-    constexpr int XL = (GPW * 16 * kBurstRows + 63) / 64;
+    constexpr int XL = GPW * 16 * kBurstRows / 64;
     u32x4_t xv[XL];
 #pragma unroll
     for (int j0 = 0; j0 < XL; ++j0) {
         const int j = j0 * 64 + lane;
-        uint32_t voff = 0x80000000u;   // past the end: reads zero
-        if (j < chunks) {
-            const int m = j % M;
-            int r = j / M;
-            const int q = r & 3;
-            r >>= 2;
-            const int t = r & 3;
-            const int gl = r >> 2;
-            voff = static_cast<uint32_t>(m * K + (g0 + gl) * kGroup + q * 32 + t * 8) * 2u;
-        }
+        const int m = j & 3, q = (j >> 2) & 3, t = (j >> 4) & 3, gl = j >> 6;   // gl = j0
+        const uint32_t voff = m < M && gl < ng
+                                  ? static_cast<uint32_t>(m * K + (g0 + gl) * kGroup + q * 32 + t * 8) * 2u
+                                  : 0x80000000u;   // past the end: reads zero
         xv[j0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, voff, 0, 0));
     }
     __builtin_amdgcn_sched_barrier(0);   // all loads issued before anything waits on one
 #pragma unroll
-    for (int j0 = 0; j0 < XL; ++j0) {
-        const int j = j0 * 64 + lane;
-        if (j < chunks) xs[j] = __builtin_bit_cast(u32x4_t, permute_like_codes(xv[j0]));
-    }
+    for (int j0 = 0; j0 < XL; ++j0) xs[j0 * 64 + lane] = __builtin_bit_cast(u32x4_t, permute_like_codes(xv[j0]));
     // the slice is the wave's own: LDS accesses of one wave complete in order, so only the
     // compiler must keep the reads below after these writes
     asm volatile("" ::: "memory");
 
-    // 2. every group: rows 4*kq + r of column c
+    // 2. every group: rows 4*kq + r of column c.  A group past the wave's share has zero codes,
+    //    scale, bias and activations and adds exactly +0; computing it anyway keeps its loads
+    //    unconditional, so the compiler cannot sink them below the wait
     const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
     const u32x4_t zu = {0u, 0u, 0u, 0u};
     const bf16x8_t ones = {__bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f),
@@ -133,32 +125,41 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_kernel(
     f32x4_t yacc = zero4;
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
-        if (i < ng) {
-            f32x4_t xsum = zero4, p = zero4;
+        f32x4_t xsum = zero4, p = zero4;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const u32x4_t av = arow < M ? xs[((i * 4 + t) * 4 + kq) * M + arow] : zu;
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
-                xsum = mfma16x16x32(a, ones, xsum);
-                p = mfma16x16x32(a, codes_bf16_permuted(w[i][t]), p);
-            }
-            const float s = bf16_bits_to_f32(sv[i]), b = bf16_bits_to_f32(bv[i]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, p[r], __builtin_fmaf(b, xsum[r], yacc[r]));
+        for (int t = 0; t < 4; ++t) {
+            const u32x4_t av = arow < M ? xs[((i * 4 + t) * 4 + kq) * kBurstRows + arow] : zu;
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+            xsum = mfma16x16x32(a, ones, xsum);
+            p = mfma16x16x32(a, codes_bf16_permuted(w[i][t]), p);
         }
+        const float s = bf16_bits_to_f32(sv[i]), b = bf16_bits_to_f32(bv[i]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, p[r], __builtin_fmaf(b, xsum[r], yacc[r]));
     }
 
-    // 3. waves 1..KW-1 hand their sums to wave 0, which adds them in wave order
+    // 3. waves 1..KW-1 hand their sums to wave 0 (one 16-byte slot per lane), which adds them
+    //    in wave order, reading four waves' slots before it adds them: a read per wave and add
+    //    would wait out the LDS latency up to 15 times
     if (KW > 1) {
-        if (wk > 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) red[((wk - 1) * 4 + r) * 64 + lane] = yacc[r];
-        }
+        if (wk > 0) red[(wk - 1) * 64 + lane] = yacc;
         __syncthreads();
         if (wk == 0) {
-            for (int j = 0; j < KW - 1; ++j)
+            int j = 0;
+            for (; j + 4 <= KW - 1; j += 4) {
+                f32x4_t v[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) yacc[r] += red[(j * 4 + r) * 64 + lane];
+                for (int u = 0; u < 4; ++u) v[u] = red[(j + u) * 64 + lane];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) yacc[r] += v[u][r];
+            }
+            for (; j < KW - 1; ++j) {
+                const f32x4_t v = red[j * 64 + lane];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yacc[r] += v[r];
+            }
         }
     }
     if (wk == 0) {
@@ -210,7 +211,7 @@ static hipError_t launch_burst_t(int kw, const uint16_t* x, const uint32_t* wq, 
         ready[dev].store(true, std::memory_order_release);
     }
     hipLaunchKernelGGL(kern, dim3((N + 15) / 16), dim3(64 * kw), burst_lds_bytes(kw, GPW), stream, x, wq, s, b, y, M,
-                       N, K);
+                       N, K, kw);
     return hipGetLastError();
 }
 
@@ -218,8 +219,8 @@ hipError_t launch_qmv_burst(const uint16_t* x, const uint32_t* wq, const uint16_
                             uint16_t* y, int M, int N, int K, hipStream_t stream) {
     int kw = 0, gpw = 0;
     if (!qmv_burst_shape(M, N, K, &kw, &gpw)) return hipErrorInvalidValue;
-    // every wave's share fits its registers: ceil(G / kw) <= gpw, and kw <= the bound
-    if (kw < 1 || kw > kQmvBurstMaxWaves || (K / kGroup + kw - 1) / kw > gpw) return hipErrorInvalidValue;
+    // the waves' shares of gpw groups cover every group, within the workgroup bound
+    if (kw < 1 || kw > kQmvBurstMaxWaves || static_cast<int64_t>(kw) * gpw < K / kGroup) return hipErrorInvalidValue;
     switch (gpw) {
         case 2: return launch_burst_t<2>(kw, x, wq, scales, biases, y, M, N, K, stream);
         case 3: return launch_burst_t<3>(kw, x, wq, scales, biases, y, M, N, K, stream);
