@@ -132,7 +132,7 @@ uint64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, i
  * Decode-row matvec, 1 <= M <= 8 ("Week 2 Day 6", Task 1: the Day 3 matvec serves M <= 8;
  * "Route affine qmv_wide ...": a dequantized group is reused across the M rows).  Needs no
  * workspace.  M > 8 returns W4A16_ERR_UNSUPPORTED.  The kernel family follows w4a16_plan
- * (up to 4 rows, 80 groups and 16k columns: the burst kernel, whose waves issue all of their
+ * (up to 4 rows and 80 groups, below 16k columns or 32k under 32 groups: the burst kernel, whose waves issue all of their
  * loads at once; wider heads: the persistent wide kernel).
  */
 int qmv_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,

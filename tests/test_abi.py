@@ -102,23 +102,29 @@ def test_grid_covers_the_output():
 
 
 def test_burst_matvec_plans():
-    # up to 4 rows and 80 groups below 16k columns: the burst kernel, 16-column workgroups of
-    # ceil(G / g) waves with g = 2 groups per wave (3 from 512 column blocks), at least
-    # ceil(G / 16) so that no workgroup passes 16 waves
-    for M, N, K, waves, per_wave in [(1, 9728, 2560, 7, 3), (4, 9728, 2560, 7, 3), (1, 4096, 2560, 10, 2),
+    # up to 4 rows and 80 groups, below 1024 column blocks or below 2048 under 32 groups: the
+    # burst kernel, 16-column workgroups of ceil(G / g) waves with g = 2 groups per wave (3 from
+    # 1024 column blocks), at least ceil(G / 16) so that no workgroup passes 16 waves
+    for M, N, K, waves, per_wave in [(1, 9728, 2560, 10, 2), (4, 9728, 2560, 10, 2), (1, 4096, 2560, 10, 2),
                                      (1, 1024, 2560, 10, 2), (1, 2560, 9728, 16, 5), (3, 2600, 8192, 16, 4),
-                                     (2, 1000, 10240, 16, 5), (1, 96, 128, 1, 2), (4, 2560, 4096, 16, 2)]:
+                                     (2, 1000, 10240, 16, 5), (1, 96, 128, 1, 2), (4, 2560, 4096, 16, 2),
+                                     (1, 16400, 2560, 7, 3), (2, 24600, 384, 1, 3), (1, 32752, 2560, 7, 3),
+                                     (4, 16368, 4096, 16, 2)]:
         p = plan(M, N, K)
         G = K // 128
         assert p["variant"] == 4, (M, N, K)                  # the burst kernel's instance index
         assert (p["k_waves"], p["block_threads"]) == (waves, 64 * waves), (M, N, K)
         assert (p["tile_n"], p["grid_x"], p["workspace_bytes"]) == (16, -(-N // 16), 0)
-        assert -(-G // waves) <= per_wave <= 5 and waves <= 16
-    # 5..8 rows, more than 80 groups and wide grids keep the other families
+        assert waves * per_wave >= G and per_wave <= 5 and waves <= 16
+    # 5..8 rows, more than 80 groups, 2048 blocks or more and 1024 blocks at 32 groups or more
+    # keep the other families
     assert plan(5, 9728, 2560)["variant"] == 3
     assert plan(8, 2560, 9728)["variant"] == 0
     assert plan(1, 1000, 10368)["variant"] == 0          # 81 groups
-    assert plan(1, 16400, 384)["variant"] == 1
+    assert plan(5, 16400, 384)["variant"] == 1
+    assert plan(1, 32768, 2560)["variant"] == 2          # 2048 blocks
+    assert plan(4, 16400, 4096)["variant"] == 2          # 1025 blocks at 32 groups
+    assert plan(1, 24600, 9728)["variant"] == 2
     assert plan(1, 151936, 2560)["variant"] == 2
 
 

@@ -21,10 +21,12 @@ SHAPES = [
     (96, 128),      # one group: a single wave
     (33, 640),      # five groups over three waves (2, 2, 1), ragged N
     (160, 2560),    # 20 groups: ten waves of two
-    (9728, 2560),   # 608 column blocks: seven waves of three (the last of two)
+    (9728, 2560),   # 608 column blocks: ten waves of two
     (200, 8192),    # 64 groups: sixteen waves of four
     (300, 9728),    # 76 groups: fifteen waves of five and one of one
     (50, 10240),    # 80 groups: sixteen waves of five, the largest share
+    (24600, 384),   # 1538 column blocks: one wave of three groups
+    (32744, 1280),  # 2047 column blocks, the last ragged: four waves of three (the last of one)
 ]
 
 

@@ -194,12 +194,15 @@ QMV_FAMILY_CASES = [
     (1000, 10368, 2, 0),     # 81 groups: past it
     (1000, 9728, 8, 0),      # long K, ragged N
     (16390, 384, 8, 1),      # 1025 blocks, odd group count
-    (24600, 256, 1, 2),      # one group pair per block: every step ends a block
+    (33000, 256, 1, 2),      # one group pair per block: every step ends a block
     (24600, 512, 5, 2),      # ragged N and M
     (30010, 1024, 8, 2),     # eight rows
-    (24600, 384, 2, 1),      # odd group count: the wide kernel does not apply
-    (16400, 4096, 4, 2),     # wide from 1024 blocks once K >= 4096
-    (9728, 4096, 4, 4),      # 608 blocks at K = 4096: burst, 3 groups per wave
+    (24600, 384, 6, 1),      # odd group count: the wide kernel does not apply
+    (24600, 384, 2, 4),      # burst from 1024 blocks: three groups per wave, odd group count
+    (16400, 4096, 5, 2),     # wide from 1024 blocks once K >= 4096
+    (16400, 4096, 4, 2),     # the same at 4 rows (the burst kernel stops at 1024 blocks there)
+    (20000, 2560, 4, 4),     # burst at 1250 blocks under 32 groups: seven waves of three
+    (9728, 4096, 4, 4),      # 608 blocks at K = 4096: burst, 2 groups per wave
     (9728, 4096, 7, 3),      # the same above 4 rows: row-amortized
     (24600, 9728, 8, 1),     # activations too large for the wide kernel's LDS
 ]
@@ -398,14 +401,25 @@ def test_tile_scales_at_two_byte_offsets_match_aligned(lib):
 
 
 def test_wide_matvec_scales_at_two_byte_offsets(lib):
-    # 24576 columns route one row to the persistent wide kernel; offset scales take the 64-column
+    # 32768 columns route one row to the persistent wide kernel; offset scales take the 64-column
     # kernel instead; both within the tolerance
-    p = synth.random_problem(42, 1, 24576, 256)
-    assert lib.w4a16_plan(1, 24576, 256)["variant"] == 2
-    announce("wide qmv scales at 2-byte offsets M=1 N=24576 K=256")
+    p = synth.random_problem(42, 1, 32768, 256)
+    assert lib.w4a16_plan(1, 32768, 256)["variant"] == 2
+    announce("wide qmv scales at 2-byte offsets M=1 N=32768 K=256")
     x, wq, s, b = to_device(p)
     assert_parity(bits(lib.linear(x, wq, s, b)), p)
     assert_parity(bits(lib.linear(x, wq, offset_by_one(s), offset_by_one(b))), p)
+
+
+def test_burst_matvec_scales_at_two_byte_offsets(lib):
+    # the burst kernel loads each scale and bias on its own: offset arrays give the same bits
+    p = synth.random_problem(43, 3, 4000, 2560)
+    assert lib.w4a16_plan(3, 4000, 2560)["variant"] == 4
+    announce("burst qmv scales at 2-byte offsets M=3 N=4000 K=2560")
+    x, wq, s, b = to_device(p)
+    y_al = bits(lib.linear(x, wq, s, b))
+    assert np.array_equal(y_al, bits(lib.linear(x, wq, offset_by_one(s), offset_by_one(b))))
+    assert_parity(y_al, p)
 
 
 # ---------------------------------------------------------------------------------- memory safety

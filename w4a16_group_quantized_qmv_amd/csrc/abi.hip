@@ -88,19 +88,20 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
     // 16-column dequantizing kernel whose four waves split K leads by 5-20%; around 16k columns
     // the 64-column kernel leads; from 24k columns (16k at 32 groups or more) the persistent wide
     // kernel, which streams whole blocks per wave, wins by 1.4x on the 151936-column head.
-    // Below 16k columns at up to 4 rows and 80 groups, the burst kernel (every load of a wave
-    // issued at once, 2..5 groups per wave) leads both: 4-14% at K = 2560 (N = 1024 .. 9728)
-    // and 4-10% at K = 9728.
+    // Up to 4 rows and 80 groups, below 16k columns, and below 32k columns under 32 groups,
+    // the burst kernel (every load of a wave issued at once, 2..5 groups per wave) leads all of
+    // them: by 15-23% below 16k columns (K = 2560, 4096 and 9728) and by 10-22% against the
+    // wide kernel at 16400 and 24600 columns (K = 2560).
     const int64_t blocks16 = ceil_div(N, 16);
     const int64_t G = K / W4A16_GROUP;
     int variant;
     int burst_kw = 0, burst_gpw = 0;
-    if (qmv_wide_fits(static_cast<int>(M), static_cast<int>(K)) && (blocks16 >= 1536 || (blocks16 >= 1024 && G >= 32)))
+    if (qmv_burst_shape(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), &burst_kw, &burst_gpw))
+        variant = kQmvBurstVariant;
+    else if (qmv_wide_fits(static_cast<int>(M), static_cast<int>(K)) && (blocks16 >= 1536 || (blocks16 >= 1024 && G >= 32)))
         variant = kQmvWideVariant;
     else if (blocks16 >= 1024)
         variant = 1;
-    else if (qmv_burst_shape(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), &burst_kw, &burst_gpw))
-        variant = kQmvBurstVariant;
     else if (G >= 64 && M <= kQmvMaxRows)
         variant = 0;
     else

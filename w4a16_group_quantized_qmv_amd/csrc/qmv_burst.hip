@@ -177,14 +177,17 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_kernel(
 bool qmv_burst_shape(int M, int N, int K, int* kw, int* gpw) {
     const int G = K / kGroup;
     if (M < 1 || M > kBurstRows || K % kGroup != 0 || G < 1 || N < 1) return false;
-    // Measured on MI355X (M = 1 and 4; K = 2560 and 9728; N = 1024 .. 9728; graph-replayed
-    // launches over rotating weights): the fewer groups a wave owns the better, as long as the
-    // launch has enough workgroups -- two groups per wave up to 256 column blocks, three from
-    // 512 blocks (9728 columns at K = 2560: 7.4 us against 7.8 with two, 8.6 for the
-    // row-amortized loop kernel); above 32 groups, as few as 16 waves allow (K = 9728: 5
-    // groups, 9.5 us against 10.5).
+    // Measured on MI355X (M = 1 and 4, graph-replayed launches over rotating weights): the
+    // fewer groups a wave owns the better while the launch has fewer than 1024 column blocks
+    // (two per wave: 7.1 us on 9728 x 2560 against 7.1-7.4 with three to five, 8.6 for the
+    // row-amortized loop kernel; 6.2 us on 2560 x 4096 against 8.0); from 1024 blocks three
+    // per wave (16400 x 2560: 8.5 us, the wide kernel 10.9; 24600 x 2560: 11.5 against 12.8),
+    // but not from 32 groups (16400 x 4096: 18.2 us, the wide kernel 16.2).  From 2048 blocks
+    // the persistent wide kernel leads (the 151936-column head: 43 us against 50 at best).
+    // Above 32 groups, as few groups per wave as 16 waves allow.
     const int blocks = (N + 15) / 16;
-    int g = blocks >= 512 ? 3 : 2;
+    if (blocks >= 2048 || (blocks >= 1024 && G >= 32)) return false;
+    int g = blocks >= 1024 ? 3 : 2;
     const int need = (G + kQmvBurstMaxWaves - 1) / kQmvBurstMaxWaves;
     if (need > g) g = need;
     if (g > kQmvBurstMaxGroups) return false;
