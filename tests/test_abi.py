@@ -102,20 +102,24 @@ def test_grid_covers_the_output():
 
 
 def test_burst_matvec_plans():
-    # up to 4 rows and 80 groups, below 1024 column blocks or below 2048 under 32 groups: the
-    # burst kernel, 16-column workgroups of ceil(G / g) waves with g = 2 groups per wave (3 from
-    # 1024 column blocks), at least ceil(G / 16) so that no workgroup passes 16 waves
-    for M, N, K, waves, per_wave in [(1, 9728, 2560, 10, 2), (4, 9728, 2560, 10, 2), (1, 4096, 2560, 10, 2),
-                                     (1, 1024, 2560, 10, 2), (1, 2560, 9728, 16, 5), (3, 2600, 8192, 16, 4),
-                                     (2, 1000, 10240, 16, 5), (1, 96, 128, 1, 2), (4, 2560, 4096, 16, 2),
-                                     (1, 16400, 2560, 7, 3), (2, 24600, 384, 1, 3), (1, 32752, 2560, 7, 3),
-                                     (4, 16368, 4096, 16, 2)]:
+    # up to 4 rows and 80 groups, below 1024 column blocks of 16 or below 2048 under 32 groups:
+    # the burst kernel.  Packed form (4 columns per workgroup, steps of 4 groups, one step per
+    # wave up to 64 groups, two above) below 1024 blocks at 1 and 2 rows, and at 3 and 4 rows
+    # for at most 160 blocks and 64 groups; otherwise 16 columns per workgroup with g = 2
+    # groups per wave (3 from 1024 blocks), at least ceil(G / 16)
+    for M, N, K, cols, waves, per_wave in [
+            (1, 9728, 2560, 4, 5, 4), (2, 9728, 2560, 4, 5, 4), (4, 9728, 2560, 16, 10, 2),
+            (1, 4096, 2560, 4, 5, 4), (1, 1024, 2560, 4, 5, 4), (4, 1024, 2560, 4, 5, 4),
+            (1, 2560, 9728, 4, 10, 8), (3, 2560, 9728, 16, 16, 5), (3, 2600, 8192, 16, 16, 4),
+            (3, 2560, 8192, 4, 16, 4), (2, 1000, 10240, 4, 10, 8), (1, 96, 128, 4, 1, 4),
+            (4, 2560, 4096, 4, 8, 4), (1, 16400, 2560, 16, 7, 3), (2, 24600, 384, 16, 1, 3),
+            (1, 32752, 2560, 16, 7, 3), (4, 16368, 4096, 16, 16, 2)]:
         p = plan(M, N, K)
         G = K // 128
         assert p["variant"] == 4, (M, N, K)                  # the burst kernel's instance index
-        assert (p["k_waves"], p["block_threads"]) == (waves, 64 * waves), (M, N, K)
-        assert (p["tile_n"], p["grid_x"], p["workspace_bytes"]) == (16, -(-N // 16), 0)
-        assert waves * per_wave >= G and per_wave <= 5 and waves <= 16
+        assert (p["tile_n"], p["k_waves"], p["block_threads"]) == (cols, waves, 64 * waves), (M, N, K)
+        assert (p["grid_x"], p["workspace_bytes"]) == (-(-N // cols), 0)
+        assert waves * per_wave >= G and waves <= 16
     # 5..8 rows, more than 80 groups, 2048 blocks or more and 1024 blocks at 32 groups or more
     # keep the other families
     assert plan(5, 9728, 2560)["variant"] == 3

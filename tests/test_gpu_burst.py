@@ -1,7 +1,9 @@
 """GPU parity of the burst matvec (4-bit, up to four decode rows; every wave issues all of its
-loads at once) through the C ABI: each wave and group count the policy gives it (1 to 16 waves,
-1 to 5 groups each), integer inputs bit for bit, random inputs against the CPU oracle within the
-tolerance of ``O.check``, and sentinel rows around the output that no write may touch.
+loads at once) through the C ABI, in both of its forms: 16 columns per workgroup, and the packed
+form (4 K slices in the MFMA's spare rows, 4 columns per workgroup).  Each wave and group count
+the policy gives either form (1 to 16 waves; 1 to 5 groups, or steps of 4 groups, each), integer
+inputs bit for bit, random inputs against the CPU oracle within the tolerance of ``O.check``,
+and sentinel rows around the output that no write may touch.
 """
 
 import numpy as np
@@ -16,18 +18,31 @@ pytestmark = pytest.mark.gpu
 
 BURST = 4   # the plan's instance index of the burst kernel
 
-# (N, K) and what the plan makes of it at 1..4 rows
+# (N, K) and what the plan makes of it: packed (tile_n 4) at 1 and 2 rows below 1024 column
+# blocks, and at 3 and 4 rows up to 160 blocks and 64 groups; 16 columns otherwise
 SHAPES = [
-    (96, 128),      # one group: a single wave
-    (33, 640),      # five groups over three waves (2, 2, 1), ragged N
-    (160, 2560),    # 20 groups: ten waves of two
-    (9728, 2560),   # 608 column blocks: ten waves of two
-    (200, 8192),    # 64 groups: sixteen waves of four
-    (300, 9728),    # 76 groups: fifteen waves of five and one of one
-    (50, 10240),    # 80 groups: sixteen waves of five, the largest share
+    (96, 128),      # one group: a single wave (packed at every M)
+    (3, 1280),      # fewer columns than one packed workgroup covers
+    (33, 640),      # five groups: two packed waves (4 + 1 groups), ragged N
+    (160, 2560),    # 20 groups: five packed waves
+    (9728, 2560),   # packed at 1-2 rows (2432 workgroups); at 3-4 rows ten waves of two groups
+    (200, 8192),    # 64 groups: sixteen packed waves of one step
+    (300, 9728),    # 76 groups: ten packed waves of two steps at 1-2 rows; sixteen of five at 3-4
+    (50, 10240),    # 80 groups: packed at 1-2 rows; sixteen waves of five at 3-4
     (24600, 384),   # 1538 column blocks: one wave of three groups
     (32744, 1280),  # 2047 column blocks, the last ragged: four waves of three (the last of one)
 ]
+
+
+def _plan(lib, M, N, K):
+    p = lib.w4a16_plan(M, N, K, 128, lib.PATH_QMV)
+    assert p["variant"] == BURST and p["tile_n"] in (4, 16), p
+    return p
+
+
+def test_both_forms_are_covered(lib):
+    forms = {(M, _plan(lib, M, N, K)["tile_n"]) for N, K in SHAPES for M in (1, 2, 3, 4)}
+    assert {(M, 4) for M in (1, 2, 3, 4)} <= forms and {(M, 16) for M in (1, 2, 3, 4)} <= forms
 
 
 @pytest.mark.parametrize("kind", ["sums", "pow2"])
@@ -35,7 +50,7 @@ SHAPES = [
 def test_burst_integer_cases_are_bit_exact(lib, N, K, kind):
     """Inputs whose projection is exact in fp32 and bf16: every output bit for bit, at 1..4 rows."""
     for M in (1, 2, 3, 4):
-        assert lib.w4a16_plan(M, N, K, 128, lib.PATH_QMV)["variant"] == BURST
+        _plan(lib, M, N, K)
         p, expect = _exact_case(kind, M, N, K, seed=5000 + 7 * M + N + K + (kind == "pow2"))
         y = run(lib, p, "qmv")
         assert np.array_equal(y, expect), f"M={M}"
@@ -50,12 +65,13 @@ def test_burst_random_cases_match_oracle(lib, N, K):
         assert np.array_equal(run(lib, p, "qmv"), y), "repeat run differs"
 
 
-@pytest.mark.parametrize("M,N,K", [(4, 1000, 2560), (1, 40, 10240), (3, 17, 128)])
+@pytest.mark.parametrize("M,N,K", [(4, 1000, 2560), (1, 40, 10240), (3, 17, 128), (1, 1001, 2560), (2, 9728, 9728),
+                                   (4, 3000, 2560)])
 def test_burst_writes_only_its_output(lib, M, N, K):
     """A sentinel row above and below y: untouched, and every element of y written."""
     import torch
     p = synth.random_problem(M * 13 + N, M, N, K)
-    assert lib.w4a16_plan(M, N, K, 128, lib.PATH_QMV)["variant"] == BURST
+    _plan(lib, M, N, K)
     x, wq, s, b = to_device(p)
     big = bf16_from_bits(np.full((M + 2, N), SENTINEL, dtype=np.uint16))
     y = big[1:M + 1]

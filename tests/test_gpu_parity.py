@@ -190,7 +190,7 @@ QMV_FAMILY_CASES = [
     (6150, 384, 5, 3),       # row-amortized, odd group count
     (2600, 8192, 3, 4),      # 64 groups: burst, 4 groups in each of 16 waves
     (2600, 8192, 5, 0),      # 64 groups above 4 rows: the dequantizing K-split kernel
-    (1000, 10240, 2, 4),     # 80 groups: the burst kernel's largest share (16 waves x 5)
+    (1000, 10240, 2, 4),     # 80 groups: packed burst, ten waves of two steps of four groups
     (1000, 10368, 2, 0),     # 81 groups: past it
     (1000, 9728, 8, 0),      # long K, ragged N
     (16390, 384, 8, 1),      # 1025 blocks, odd group count

@@ -95,8 +95,8 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
     const int64_t blocks16 = ceil_div(N, 16);
     const int64_t G = K / W4A16_GROUP;
     int variant;
-    int burst_kw = 0, burst_gpw = 0;
-    if (qmv_burst_shape(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), &burst_kw, &burst_gpw))
+    QmvBurstShape burst{};
+    if (qmv_burst_shape(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), &burst))
         variant = kQmvBurstVariant;
     else if (qmv_wide_fits(static_cast<int>(M), static_cast<int>(K)) && (blocks16 >= 1536 || (blocks16 >= 1024 && G >= 32)))
         variant = kQmvWideVariant;
@@ -119,8 +119,9 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
         p->tile_n = 16;
         p->grid_x = static_cast<int32_t>(std::min<int64_t>(ceil_div(blocks16, waves), int64_t{32 / waves} * cus));
     } else if (variant == kQmvBurstVariant) {
-        waves = burst_kw;
-        p->grid_x = static_cast<int32_t>(blocks16);
+        waves = burst.kw;
+        p->tile_n = burst.cols;
+        p->grid_x = static_cast<int32_t>(ceil_div(N, burst.cols));
     } else {
         p->grid_x = static_cast<int32_t>(ceil_div(N, p->tile_n));
     }
@@ -128,7 +129,7 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
     p->grid_z = 1;
     p->block_threads = 64 * waves;
     p->split_k = 1;
-    p->k_waves = variant == kQmvBurstVariant ? burst_kw : v.kw;
+    p->k_waves = variant == kQmvBurstVariant ? burst.kw : v.kw;
     p->variant = variant;
     p->workspace_bytes = 0;
 }

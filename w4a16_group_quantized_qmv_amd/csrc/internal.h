@@ -30,10 +30,15 @@ constexpr int kQmvAmortizedVariant = 3;
 constexpr int kQmvBurstVariant = 4;
 constexpr int kQmvBurstMaxWaves = 16;
 constexpr int kQmvBurstMaxGroups = 5;
-// The burst kernel's waves per workgroup and groups per wave for an M x N x K matvec; false
-// where it does not apply (more than 4 rows, more than 16 * 5 groups, 2048 column blocks or
-// more, or 1024 blocks or more at 32 groups or more).
-bool qmv_burst_shape(int M, int N, int K, int* kw, int* gpw);
+// The burst kernel's form for an M x N x K matvec: packed (4 K slices in the MFMA's spare rows,
+// 4 columns per workgroup, gpw steps of 4 groups per wave, rows = activation row slots) or not
+// (16 columns per workgroup, gpw groups per wave); kw waves per workgroup.  False where it does
+// not apply (more than 4 rows, more than 16 * 5 groups, 2048 column blocks or more, or 1024
+// blocks or more at 32 groups or more).
+struct QmvBurstShape {
+    int packed, kw, gpw, rows, cols;
+};
+bool qmv_burst_shape(int M, int N, int K, QmvBurstShape* out);
 hipError_t launch_qmv_burst(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                             uint16_t* y, int M, int N, int K, hipStream_t stream);
 constexpr int kQmvWideStages = 2;

@@ -22,6 +22,15 @@
 // row-amortized form of the affine dequantization.  The waves' partial sums are added in wave
 // order through LDS, so a result does not depend on timing.  Every load goes through a buffer
 // resource: columns past N and rows past M read zeros.
+//
+// Packed form (qmv_burst_packed_kernel): with at most 4 rows, 12 of the A operand's 16 rows are
+// padding.  The packed form fills them with 4 K slices: A rows 4s + m hold row m of the
+// activations of slice s, and B columns 4s + j hold column j's codes of slice s, so one MFMA
+// works on 4 columns x 4 groups instead of 16 columns x 1 group (the same 1 KB of codes).  Of
+// its 16 x 16 result only the 4 diagonal 4 x 4 blocks (slice s of A against slice s of B) are
+// wanted; the others are computed and dropped, which costs nothing on a path that waits on
+// memory.  A workgroup then covers 4 columns, so a narrow matrix (1024 or 2560 columns) spreads
+// over 4x as many workgroups and fills the compute units the 16-column form leaves idle.
 #include "device_common.h"
 #include "internal.h"
 
@@ -174,7 +183,126 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_kernel(
     }
 }
 
-bool qmv_burst_shape(int M, int N, int K, int* kw, int* gpw) {
+template <int GPW, int MR>
+__global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_packed_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int N, int K, int KW) {
+    extern __shared__ __attribute__((aligned(16))) u32x4_t lds[];
+    constexpr int GW = 4 * GPW;   // groups per wave: GPW steps of 4 slices
+    const int G = K >> 7;
+    const int lane = threadIdx.x & 63;
+    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col0 = blockIdx.x * 4;
+    const int g0 = wk * GW;       // step i, slice s: group g0 + 4 i + s
+    const int c = lane & 15, kq = lane >> 4;
+    const int sl = c >> 2, j = c & 3;   // this lane's slice and column (B operand), or slice and row (A)
+    const int row_bytes = K / 2;
+    auto clamp_records = [](int64_t bytes) { return static_cast<int>(bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes); };
+    const int64_t cols = static_cast<int64_t>(N - col0);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + static_cast<size_t>(col0) * row_bytes), 0,
+        clamp_records(cols * row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(scales + static_cast<size_t>(col0) * G), 0, clamp_records(cols * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(biases + static_cast<size_t>(col0) * G), 0, clamp_records(cols * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x), 0, clamp_records(static_cast<int64_t>(M) * K * 2), 0x00020000);
+    u32x4_t* const xs = lds + static_cast<size_t>(wk) * GW * 16 * MR;
+    float* const red = reinterpret_cast<float*>(lds + static_cast<size_t>(KW) * GW * 16 * MR);
+
+    // 1. every load of the wave.  Codes and scales: lane (s, j, kq) takes column j's 16 bytes at
+    //    kq*16 of group g0 + 4 i + s (the four slices of a step are 256 contiguous bytes of the
+    //    column).  Activations: chunk jj = ((gl * 4 + t) * 4 + q) * MR + m holds row m's values
+    //    gl*128 + q*32 + t*8 .. +7 of the wave's group gl, MR row slots per chunk (1, 2 or 4).
+    //    Past the last group, column or row the per-lane offset passes the resource's end and
+    //    the load returns zeros.
+    uint32_t w[GPW][4];
+    uint16_t sv[GPW], bv[GPW];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        const int g = g0 + 4 * i + sl;
+        const uint32_t voff = g < G ? static_cast<uint32_t>(j * row_bytes + g * 64 + kq * 16) : 0x80000000u;
+        const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, 0, 0));
+        w[i][0] = v[0];
+        w[i][1] = v[1];
+        w[i][2] = v[2];
+        w[i][3] = v[3];
+    }
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        const int g = g0 + 4 * i + sl;
+        const uint32_t voff = g < G ? static_cast<uint32_t>((j * G + g) * 2) : 0x80000000u;
+        sv[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, voff, 0, 0);
+        bv[i] = __builtin_amdgcn_raw_buffer_load_b16(br, voff, 0, 0);
+    }
+    constexpr int XL = GW * 16 * MR / 64;
+    u32x4_t xv[XL];
+#pragma unroll
+    for (int j0 = 0; j0 < XL; ++j0) {
+        const int jj = j0 * 64 + lane;
+        const int m = jj % MR, rr = jj / MR;
+        const int q = rr & 3, t = (rr >> 2) & 3, gl = rr >> 4;
+        const uint32_t voff = m < M && g0 + gl < G
+                                  ? static_cast<uint32_t>(m * K + (g0 + gl) * kGroup + q * 32 + t * 8) * 2u
+                                  : 0x80000000u;
+        xv[j0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, voff, 0, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all loads issued before anything waits on one
+#pragma unroll
+    for (int j0 = 0; j0 < XL; ++j0) xs[j0 * 64 + lane] = __builtin_bit_cast(u32x4_t, permute_like_codes(xv[j0]));
+    asm volatile("" ::: "memory");   // the wave's own slice: only the compiler must keep the order
+
+    // 2. every step: A lane (row 4 s + m, kq) reads slice s's row m; the result lane (c, kq) holds
+    //    rows 4 kq .. 4 kq + 3 of column c, wanted where kq is column c's slice
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    const u32x4_t zu = {0u, 0u, 0u, 0u};
+    const bf16x8_t ones = {__bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f),
+                           __bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f)};
+    const int am = j < MR ? j : 0;
+    f32x4_t yacc = zero4;
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        f32x4_t xsum = zero4, p = zero4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const u32x4_t av = j < M && j < MR ? xs[(((4 * i + sl) * 4 + t) * 4 + kq) * MR + am] : zu;
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+            xsum = mfma16x16x32(a, ones, xsum);
+            p = mfma16x16x32(a, codes_bf16_permuted(w[i][t]), p);
+        }
+        const float s = bf16_bits_to_f32(sv[i]), b = bf16_bits_to_f32(bv[i]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, p[r], __builtin_fmaf(b, xsum[r], yacc[r]));
+    }
+
+    // 3. the wanted lanes (kq == slice) hand rows 0..3 of their column to LDS; wave 0, lane
+    //    16 s + 4 j + m, adds its (slice, column, row) over the waves in wave order, then the
+    //    four slices of each output in a fixed pattern
+    if (kq == sl) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wk * 64 + sl * 16 + j * 4 + r] = yacc[r];
+    }
+    __syncthreads();
+    if (wk == 0) {
+        float acc = 0.f;
+        int w2 = 0;
+        for (; w2 + 4 <= KW; w2 += 4) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = red[(w2 + u) * 64 + lane];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc += v[u];
+        }
+        for (; w2 < KW; ++w2) acc += red[w2 * 64 + lane];
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        const int jo = (lane >> 2) & 3, m = lane & 3;
+        if (lane < 16 && m < M && col0 + jo < N) y[static_cast<size_t>(m) * N + col0 + jo] = f32_to_bf16_bits(acc);
+    }
+}
+
+bool qmv_burst_shape(int M, int N, int K, QmvBurstShape* out) {
     const int G = K / kGroup;
     if (M < 1 || M > kBurstRows || K % kGroup != 0 || G < 1 || N < 1) return false;
     // Measured on MI355X (M = 1 and 4, graph-replayed launches over rotating weights): the
@@ -186,45 +314,107 @@ bool qmv_burst_shape(int M, int N, int K, int* kw, int* gpw) {
     // the persistent wide kernel leads (the 151936-column head: 43 us against 50 at best).
     // Above 32 groups, as few groups per wave as 16 waves allow.
     const int blocks = (N + 15) / 16;
-    if (blocks >= 2048 || (blocks >= 1024 && G >= 32)) return false;
+    if (blocks >= 2048 || (blocks >= 1024 && G >= 32) || G > kQmvBurstMaxWaves * kQmvBurstMaxGroups) return false;
+    // The packed form, below 1024 blocks: at 1 and 2 rows everywhere (M = 1: 2560 x 9728
+    // 7.5-7.7 us against 9.1, 1024 x 2560 3.3 against 4.1, 4096 x 2560 4.3 against 4.5, 9728 x
+    // 2560 6.7 against 7.6; M = 2 alike); at 3 and 4 rows, whose 4-row activation slots take 4x
+    // the LDS and loads, only for at most 160 blocks and 64 groups (M = 4: 1024 x 2560 3.8
+    // against 4.5, 2560 x 4096 6.7 against 6.9; 2560 x 9728 15.7 against 10.6).  One step per
+    // wave (4 groups) up to 64 groups, two above.
+    if (blocks < 1024 && (M <= 2 || (blocks <= 160 && G <= 64))) {
+        out->packed = 1;
+        out->gpw = G > 4 * kQmvBurstMaxWaves ? 2 : 1;
+        out->kw = (G + 4 * out->gpw - 1) / (4 * out->gpw);
+        out->rows = M == 1 ? 1 : (M == 2 ? 2 : 4);
+        out->cols = 4;
+        return true;
+    }
     int g = blocks >= 1024 ? 3 : 2;
     const int need = (G + kQmvBurstMaxWaves - 1) / kQmvBurstMaxWaves;
     if (need > g) g = need;
-    if (g > kQmvBurstMaxGroups) return false;
-    *gpw = g;
-    *kw = (G + g - 1) / g;
+    out->packed = 0;
+    out->gpw = g;
+    out->kw = (G + g - 1) / g;
+    out->rows = kBurstRows;
+    out->cols = 16;
     return true;
 }
 
-template <int GPW>
-static hipError_t launch_burst_t(int kw, const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
-                                 uint16_t* y, int M, int N, int K, hipStream_t stream) {
-    constexpr int kMaxDevices = 64;
-    static std::atomic<bool> ready[kMaxDevices];   // per instance and device: the LDS permission is set
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Once per kernel instance and device: permission for the largest dynamic LDS its launches
+// use (16 waves), which may pass the 64 KB a launch gets by default.
+template <typename Kern>
+hipError_t allow_lds(Kern kern, size_t bytes, std::atomic<bool> (&ready)[kMaxDevices]) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    auto kern = qmv_burst_kernel<GPW>;
     if (!ready[dev].load(std::memory_order_acquire)) {
-        // the largest workgroup's LDS (16 waves) may pass the 64 KB a launch gets by default
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                static_cast<int>(burst_lds_bytes(kQmvBurstMaxWaves, GPW)));
+                                static_cast<int>(bytes));
         if (e != hipSuccess) return e;
         ready[dev].store(true, std::memory_order_release);
     }
+    return hipSuccess;
+}
+
+// LDS of a KW-wave packed workgroup: each wave's activation slots (4 GPW groups x 16 chunks x
+// MR rows of 16 bytes), then 64 fp32 partial sums per wave.
+constexpr size_t packed_lds_bytes(int kw, int gpw, int mr) {
+    return static_cast<size_t>(kw) * 4 * gpw * 16 * mr * 16 + static_cast<size_t>(kw) * 64 * 4;
+}
+
+}  // namespace
+
+template <int GPW>
+static hipError_t launch_burst_t(int kw, const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                                 uint16_t* y, int M, int N, int K, hipStream_t stream) {
+    static std::atomic<bool> ready[kMaxDevices];
+    auto kern = qmv_burst_kernel<GPW>;
+    const hipError_t e = allow_lds(kern, burst_lds_bytes(kQmvBurstMaxWaves, GPW), ready);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((N + 15) / 16), dim3(64 * kw), burst_lds_bytes(kw, GPW), stream, x, wq, s, b, y, M,
                        N, K, kw);
     return hipGetLastError();
 }
 
+template <int GPW, int MR>
+static hipError_t launch_packed_t(int kw, const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                                  uint16_t* y, int M, int N, int K, hipStream_t stream) {
+    static std::atomic<bool> ready[kMaxDevices];
+    auto kern = qmv_burst_packed_kernel<GPW, MR>;
+    const hipError_t e = allow_lds(kern, packed_lds_bytes(kQmvBurstMaxWaves, GPW, MR), ready);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((N + 3) / 4), dim3(64 * kw), packed_lds_bytes(kw, GPW, MR), stream, x, wq, s, b, y,
+                       M, N, K, kw);
+    return hipGetLastError();
+}
+
 hipError_t launch_qmv_burst(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                             uint16_t* y, int M, int N, int K, hipStream_t stream) {
-    int kw = 0, gpw = 0;
-    if (!qmv_burst_shape(M, N, K, &kw, &gpw)) return hipErrorInvalidValue;
+    QmvBurstShape sh;
+    if (!qmv_burst_shape(M, N, K, &sh)) return hipErrorInvalidValue;
+    const int kw = sh.kw, G = K / kGroup;
+    if (sh.packed) {
+        // the waves' shares of 4 gpw groups cover every group; the row slots cover M
+        if (kw < 1 || kw > kQmvBurstMaxWaves || static_cast<int64_t>(kw) * 4 * sh.gpw < G || sh.rows < M)
+            return hipErrorInvalidValue;
+        const int key = sh.gpw * 10 + sh.rows;
+        switch (key) {
+            case 11: return launch_packed_t<1, 1>(kw, x, wq, scales, biases, y, M, N, K, stream);
+            case 12: return launch_packed_t<1, 2>(kw, x, wq, scales, biases, y, M, N, K, stream);
+            case 14: return launch_packed_t<1, 4>(kw, x, wq, scales, biases, y, M, N, K, stream);
+            case 21: return launch_packed_t<2, 1>(kw, x, wq, scales, biases, y, M, N, K, stream);
+            case 22: return launch_packed_t<2, 2>(kw, x, wq, scales, biases, y, M, N, K, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     // the waves' shares of gpw groups cover every group, within the workgroup bound
-    if (kw < 1 || kw > kQmvBurstMaxWaves || static_cast<int64_t>(kw) * gpw < K / kGroup) return hipErrorInvalidValue;
-    switch (gpw) {
+    if (kw < 1 || kw > kQmvBurstMaxWaves || static_cast<int64_t>(kw) * sh.gpw < G) return hipErrorInvalidValue;
+    switch (sh.gpw) {
         case 2: return launch_burst_t<2>(kw, x, wq, scales, biases, y, M, N, K, stream);
         case 3: return launch_burst_t<3>(kw, x, wq, scales, biases, y, M, N, K, stream);
         case 4: return launch_burst_t<4>(kw, x, wq, scales, biases, y, M, N, K, stream);
