@@ -270,22 +270,26 @@ enum w4a16_qmv_mode {
     W4A16_QMV_POLICY = 0,      /* route by (bits, M) as measured on MI355X                         */
     W4A16_QMV_AMORTIZED = 1,   /* row-amortized: one unpacked group feeds all M rows (matrix core)  */
     W4A16_QMV_PER_ROW = 2,     /* per-row dot products, M <= 2                                      */
-    W4A16_QMV_FAMILIES = 3     /* bits = 4 only: the kernel families and policy of qmv_w4a16        */
+    W4A16_QMV_FAMILIES = 3,    /* bits = 4 only: the kernel families and policy of qmv_w4a16        */
+    W4A16_QMV_BURST = 4        /* M <= 4: every wave issues all of its loads at once, 4 K slices in
+                                  the matrix core's spare rows (below 16k columns; beyond 160 blocks
+                                  of 16 columns or 64 groups only up to 2 rows; at most 128 groups) */
 };
 
 /*
  * Affine matvec for decode rows (1 <= M <= 8) at bits = 1, 2, 3, 4 or 8 per code, routed by
  * (bits, M) between a per-row kernel and a row-amortized one ("Route affine qmv_wide by
  * bit-width and batch size #5" routes 1-bit and small M per row and larger M row-amortized).
- * Measured on MI355X the row-amortized kernel leads at every width and M, so the policy takes
- * it, and at bits = 4 the policy is qmv_w4a16's.  Layouts as above with wq uint32 [N, K * bits / 32]:
+ * Measured on MI355X the row-amortized kernel leads the per-row one at every width and M, and
+ * the burst form leads both where it applies, so the policy takes the burst form there and the
+ * row-amortized kernel elsewhere; at bits = 4 the policy is qmv_w4a16's.  Layouts as above with wq uint32 [N, K * bits / 32]:
  * a row's words are one bit stream, lowest bits first (stream bit t = bit t % 32 of word t / 32),
  * element k in stream bits bits*k .. bits*k + bits - 1 -- at 1, 2, 4 and 8 bits element
  * (32/bits)*j + i in bits bits*i .. of word j, at 3 bits codes 10 and 21 of every 32 straddle a
  * word; scales and biases bf16 [N, K/128]; w = s * q + b.  mode: enum w4a16_qmv_mode.  Needs no
  * workspace.  Same preconditions, ownership and errors as qmv_w4a16; bits outside {1, 2, 3, 4, 8},
- * M > 8, an unknown mode, the per-row mode with M > 2, or W4A16_QMV_FAMILIES with bits != 4 return
- * W4A16_ERR_UNSUPPORTED.
+ * M > 8, an unknown mode, the per-row mode with M > 2, W4A16_QMV_FAMILIES with bits != 4, or
+ * W4A16_QMV_BURST outside its shapes return W4A16_ERR_UNSUPPORTED.
  */
 int qmv_affine(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
                uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits, int32_t mode,

@@ -304,21 +304,35 @@ def test_gate_up_validates_before_launch(lib):
 # ------------------------------------------------------------------------------ width-generic matvec
 
 def test_qmv_affine_plans():
-    # measured routing: the row-amortized kernel at 1, 2 and 8 bits; qmv_w4a16's policy at 4 bits
+    # measured routing: qmv_w4a16's policy at 4 bits; at 1, 2, 3 and 8 bits the burst form where
+    # it applies (at most 4 rows, below 1024 column blocks of 16 and 128 groups; beyond 160
+    # blocks or 64 groups only up to 2 rows), the row-amortized kernel elsewhere
     for bits in w4.BITS:
         for M in range(1, 9):
-            for N, K in [(4000, 2560), (151936, 2560), (2560, 9728)]:
+            for N, K in [(4000, 2560), (151936, 2560), (2560, 9728), (1000, 16384), (2000, 8192)]:
                 p = w4.qmv_affine_plan(M, N, K, bits, w4.QMV_POLICY, 128, CUS)
                 assert p["path"] == w4.PATH_QMV and p["workspace_bytes"] == 0
+                blocks, G = -(-N // 16), K // 128
+                burst = M <= 4 and blocks < 1024 and G <= 128 and (M <= 2 or (blocks <= 160 and G <= 64))
                 if bits == 4:
-                    q = plan(M, N, K, path=w4.PATH_QMV)
+                    q = plan(M, N, K, path=w4.PATH_QMV) if G <= 8192 else None
                     assert p["variant"] == w4.QMV_FAMILIES
                     assert (p["tile_n"], p["grid_x"], p["k_waves"]) == (q["tile_n"], q["grid_x"], q["k_waves"])
+                elif burst:
+                    steps = 2 if G > 64 else 1
+                    assert p["variant"] == w4.QMV_BURST, (bits, M, N, K)
+                    assert (p["tile_n"], p["grid_x"]) == (4, -(-N // 4))
+                    assert p["k_waves"] == -(-G // (4 * steps)) and p["block_threads"] == 64 * p["k_waves"]
+                    assert p["tile_m"] == (1 if M == 1 else 2 if M == 2 else 4)
                 else:
-                    assert p["variant"] == w4.QMV_AMORTIZED
+                    assert p["variant"] == w4.QMV_AMORTIZED, (bits, M, N, K)
                     assert p["tile_n"] == 16 and p["grid_x"] == -(-N // 16)
-        for mode in (w4.QMV_AMORTIZED, w4.QMV_PER_ROW):
+        for mode in (w4.QMV_AMORTIZED, w4.QMV_PER_ROW, w4.QMV_BURST):
             assert w4.qmv_affine_plan(2, 4000, 2560, bits, mode, 128, CUS)["variant"] == mode
+        # the forced burst form outside its shapes
+        for M, N, K in [(5, 4000, 2560), (1, 20000, 2560), (3, 4000, 2560), (1, 1000, 16512)]:
+            with pytest.raises(NotImplementedError):
+                w4.qmv_affine_plan(M, N, K, bits, w4.QMV_BURST, 128, CUS)
 
 
 @pytest.mark.parametrize("args", [
@@ -326,7 +340,8 @@ def test_qmv_affine_plans():
     (9, 16, 256, 4, 0),                                            # more than eight rows
     (3, 16, 256, 4, w4.QMV_PER_ROW),                               # per-row kernel: M <= 2
     (1, 16, 256, 2, w4.QMV_FAMILIES),                              # the 4-bit families: bits = 4
-    (1, 16, 256, 4, 4), (1, 16, 256, 4, -1),                       # unknown mode
+    (5, 16, 256, 2, w4.QMV_BURST),                                 # burst form: M <= 4
+    (1, 16, 256, 4, 5), (1, 16, 256, 4, -1),                       # unknown mode
 ])
 def test_qmv_affine_rejects_unsupported(lib, args):
     M, N, K, bits, mode = args

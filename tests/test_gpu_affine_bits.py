@@ -1,9 +1,9 @@
 """GPU parity of the width-generic affine matvec (``qmv_affine``: 1, 2, 3, 4 and 8 bits per code,
 M <= 8) against the oracle, through the C ABI.
 
-Both kernels (row-amortized and per-row) and the policy are checked at every width on ragged
-shapes (N not a multiple of the 16-column block, group counts not a multiple of the four waves
-that split K), with the same per-element tolerance as the 4-bit paths.  Closed-form cases are
+The kernels (row-amortized, per-row and the burst form) and the policy are checked at every width
+on ragged shapes (N not a multiple of the 16-column block, group counts not a multiple of the
+four waves that split K), with the same per-element tolerance as the 4-bit paths.  Closed-form cases are
 bit-exact: one-hot activations return the codes themselves (so the unpack order is pinned
 position by position), and integer or power-of-two affine sums are exact in fp32.
 """
@@ -21,7 +21,14 @@ from gpu_helpers import announce, bits as to_bits, to_device
 pytestmark = pytest.mark.gpu
 
 WIDTHS = (1, 2, 3, 4, 8)
-MODES = {"policy": 0, "amortized": 1, "per_row": 2}
+MODES = {"policy": 0, "amortized": 1, "per_row": 2, "burst": 4}
+
+
+def burst_applies(M, N, K):
+    """Shapes of the burst form: at most 4 rows, below 1024 column blocks of 16 and 128 groups;
+    beyond 160 blocks or 64 groups only up to 2 rows."""
+    blocks, G = -(-N // 16), K // 128
+    return M <= 4 and blocks < 1024 and G <= 128 and (M <= 2 or (blocks <= 160 and G <= 64))
 
 
 def run_affine(lib, p, nbits, mode, dev=None):
@@ -39,12 +46,17 @@ def assert_parity(y_bits, p, nbits):
     assert r.ok, str(r)
 
 
-AFFINE_CASES = [          # (M, N, K): ragged N; G = 2, 3, 20 groups over four waves
+AFFINE_CASES = [          # (M, N, K): ragged N; G = 2, 3, 20, 76, 128 groups
     (1, 1000, 256),
     (2, 4000, 2560),
     (1, 24600, 384),
     (5, 1000, 384),
     (8, 2056, 2560),
+    (4, 150, 2560),          # burst form with 4-row slots
+    (3, 1001, 8192),         # 64 groups at 3 rows: sixteen burst waves
+    (2, 2560, 9728),         # 76 groups: two burst steps per wave
+    (1, 502, 16384),         # 128 groups: the burst form's largest
+    (1, 3, 640),             # fewer columns than one burst workgroup
 ]
 
 
@@ -53,7 +65,7 @@ AFFINE_CASES = [          # (M, N, K): ragged N; G = 2, 3, 20 groups over four w
 def test_affine_matches_oracle(lib, nbits, M, N, K):
     p = synth.random_problem(40 + nbits, M, N, K, bits=nbits)
     dev = to_device(p)
-    modes = ["policy", "amortized"] + (["per_row"] if M <= 2 else [])
+    modes = ["policy", "amortized"] + (["per_row"] if M <= 2 else []) + (["burst"] if burst_applies(M, N, K) else [])
     for mode in modes:
         assert_parity(run_affine(lib, p, nbits, mode, dev), p, nbits)
 
@@ -68,7 +80,7 @@ def one_hot_problem(nbits, K=256, N=40, seed=11):
 
 
 @pytest.mark.parametrize("nbits", WIDTHS)
-@pytest.mark.parametrize("mode,rows", [("amortized", 8), ("per_row", 2)])
+@pytest.mark.parametrize("mode,rows", [("amortized", 8), ("per_row", 2), ("burst", 4)])
 def test_one_hot_rows_return_the_codes(lib, nbits, mode, rows):
     import torch
     q, p = one_hot_problem(nbits)
@@ -82,7 +94,8 @@ def test_one_hot_rows_return_the_codes(lib, nbits, mode, rows):
 
 
 @pytest.mark.parametrize("nbits", WIDTHS)
-@pytest.mark.parametrize("mode,M", [("amortized", 8), ("amortized", 3), ("per_row", 2), ("per_row", 1)])
+@pytest.mark.parametrize("mode,M", [("amortized", 8), ("amortized", 3), ("per_row", 2), ("per_row", 1), ("burst", 1),
+                                    ("burst", 2), ("burst", 4)])
 def test_integer_sums_are_exact(lib, nbits, mode, M):
     rng = np.random.default_rng(12 + nbits)
     N, K = 1000, 640
@@ -98,7 +111,7 @@ def test_integer_sums_are_exact(lib, nbits, mode, M):
 
 
 @pytest.mark.parametrize("nbits", WIDTHS)
-@pytest.mark.parametrize("mode,M", [("amortized", 6), ("per_row", 2)])
+@pytest.mark.parametrize("mode,M", [("amortized", 6), ("per_row", 2), ("burst", 3)])
 def test_power_of_two_affine_is_exact(lib, nbits, mode, M):
     rng = np.random.default_rng(20 + nbits)
     N, K = 520, 384
@@ -121,7 +134,7 @@ SENTINEL = 0x7FA5     # a NaN pattern the kernels never produce
 
 
 @pytest.mark.parametrize("nbits", WIDTHS)
-@pytest.mark.parametrize("mode,M", [("amortized", 3), ("per_row", 1)])
+@pytest.mark.parametrize("mode,M", [("amortized", 3), ("per_row", 1), ("burst", 1), ("burst", 4)])
 def test_writes_stay_inside_the_output(lib, nbits, mode, M):
     """y is the head of a larger poisoned buffer: the M x N outputs are written, nothing after."""
     import torch

@@ -31,7 +31,7 @@ __all__ = [
     "load", "lib_path", "w4a16_abi_version", "w4a16_status_string", "w4a16_plan", "w4a16_workspace_bytes",
     "qmv_w4a16", "qmm_w4a16", "w4a16_linear", "w4a16_linear_noalloc", "NOALLOC_SCRATCH_BYTES", "linear", "W4A16Error", "declared_symbols", "PreparedLinear",
     "w4a16_gate_up_plan", "w4a16_gate_up_swiglu", "PreparedGateUp",
-    "qmv_affine", "qmv_affine_plan", "QMV_POLICY", "QMV_AMORTIZED", "QMV_PER_ROW", "QMV_FAMILIES", "BITS",
+    "qmv_affine", "qmv_affine_plan", "QMV_POLICY", "QMV_AMORTIZED", "QMV_PER_ROW", "QMV_FAMILIES", "QMV_BURST", "BITS",
     "PATH_W4A8", "w4a8_xsum_cols", "w4a8_quantize_rows", "w4a8_plan", "qmm_w4a8", "w4a8_linear_workspace_bytes",
     "w4a8_linear", "PreparedW4A8",
     "PATH_GROUPED", "PATH_PER_PROJECTION", "MAX_GROUPED", "w4a16_grouped_plan", "w4a16_linear_grouped",
@@ -43,7 +43,7 @@ W4A16_OK = 0
 PATH_AUTO, PATH_QMV, PATH_QMM, PATH_SKINNY, PATH_GATE_UP, PATH_W4A8 = 0, 1, 2, 3, 4, 5
 PATH_GROUPED, PATH_PER_PROJECTION = 6, 7
 MAX_GROUPED = 4
-QMV_POLICY, QMV_AMORTIZED, QMV_PER_ROW, QMV_FAMILIES = 0, 1, 2, 3
+QMV_POLICY, QMV_AMORTIZED, QMV_PER_ROW, QMV_FAMILIES, QMV_BURST = 0, 1, 2, 3, 4
 BITS = (1, 2, 3, 4, 8)
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -290,7 +290,7 @@ def qmv_w4a16(x, wq, scales, biases, y=None, stream=None):
 def qmv_affine(x, wq, scales, biases, bits: int, y=None, mode: int = QMV_POLICY, stream=None):
     """Decode-row matvec (1 <= M <= 8) over ``bits``-bit affine codes (1, 2, 3, 4 or 8; ``wq`` int32
     ``[N, K * bits / 32]``, lowest bits first), routed by (bits, M) unless ``mode`` forces the
-    row-amortized or the per-row kernel.  Returns y."""
+    row-amortized, the per-row kernel or the burst form.  Returns y."""
     if bits not in BITS:
         raise ValueError(f"bits={bits} must be one of {BITS}")
     own_y = y is None

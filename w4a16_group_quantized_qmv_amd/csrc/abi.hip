@@ -559,20 +559,44 @@ int plan_qmv_affine(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits
     if (!p) return W4A16_ERR_NULL;
     int st = check_shape(M, N, K, group);
     if (st != W4A16_OK) return st;
-    if (!bits_ok(bits) || M > kQmvMaxRows || mode < W4A16_QMV_POLICY || mode > W4A16_QMV_FAMILIES)
+    if (!bits_ok(bits) || M > kQmvMaxRows || mode < W4A16_QMV_POLICY || mode > W4A16_QMV_BURST)
         return W4A16_ERR_UNSUPPORTED;
     if (mode == W4A16_QMV_PER_ROW && M > kQmvPerRowMaxRows) return W4A16_ERR_UNSUPPORTED;
     if (mode == W4A16_QMV_FAMILIES && bits != 4) return W4A16_ERR_UNSUPPORTED;
+    QmvBurstShape burst{};
+    const bool burst_fits = qmv_bits_burst_shape(static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), &burst);
+    if (mode == W4A16_QMV_BURST && !burst_fits) return W4A16_ERR_UNSUPPORTED;
     int32_t cus = num_cus;
     if (cus <= 0) {
         st = query_num_cus(&cus);
         if (st != W4A16_OK) return st;
     }
-    if (mode == W4A16_QMV_POLICY) mode = bits == 4 ? W4A16_QMV_FAMILIES : W4A16_QMV_AMORTIZED;
+    // Measured on MI355X (graph replay over rotating weights): the burst form leads the
+    // row-amortized kernel at every width where it applies -- at M = 1 by 10-25% on 2560 -> 9728
+    // (1, 2, 3, 8 bits: 6.5 / 6.6 / 7.3 / 7.7 us against 7.3 / 7.6 / 8.1 / 10.3), by 35-42% on
+    // 9728 -> 2560 and by 25-40% on 2560 -> 1024; at M = 4 on 2560 -> 1024 by 21-37%.
+    if (mode == W4A16_QMV_POLICY)
+        mode = bits == 4 ? W4A16_QMV_FAMILIES : (burst_fits ? W4A16_QMV_BURST : W4A16_QMV_AMORTIZED);
     if (mode == W4A16_QMV_FAMILIES) {
         plan_qmv(M, N, K, cus, p);
         p->num_cus = cus;
         p->variant = mode;
+        return W4A16_OK;
+    }
+    if (mode == W4A16_QMV_BURST) {
+        p->path = W4A16_PATH_QMV;
+        p->tile_m = burst.rows;
+        p->tile_n = burst.cols;
+        p->tile_k = W4A16_GROUP;
+        p->grid_x = static_cast<int32_t>(ceil_div(N, burst.cols));
+        p->grid_y = 1;
+        p->grid_z = 1;
+        p->block_threads = 64 * burst.kw;
+        p->split_k = 1;
+        p->k_waves = burst.kw;
+        p->num_cus = cus;
+        p->variant = mode;
+        p->workspace_bytes = 0;
         return W4A16_OK;
     }
     p->path = W4A16_PATH_QMV;
@@ -607,6 +631,7 @@ int run_qmv_affine(const uint16_t* x, const uint32_t* wq, const uint16_t* s, con
         plan_qmv(M, N, K, p.num_cus, &p);
         return to_status(launch_qmv(p.variant, x, wq, s, b, y, m, n, k, hs));
     }
+    if (p.variant == W4A16_QMV_BURST) return to_status(launch_qmv_bits_burst(bits, x, wq, s, b, y, m, n, k, hs));
     return to_status(launch_qmv_bits(bits, p.variant == W4A16_QMV_PER_ROW ? kQmvBitsRows : kQmvBitsMatrix, x, wq, s,
                                      b, y, m, n, k, hs));
 }

@@ -153,6 +153,12 @@ hipError_t launch_splitk_reduce_glu(const float* ws, uint16_t* h, int64_t MN, in
 // Width-generic affine matvec (1, 2, 3, 4 or 8 bits per code, M <= 8): row-amortized on the
 // matrix core (mode kQmvBitsMatrix) or per row with dot products (kQmvBitsRows, M <= 2).
 constexpr int kQmvBitsMatrix = 0, kQmvBitsRows = 1;
+// The burst form of the width-generic matvec (packed layout, at most 4 rows): its shape, false
+// where it does not apply (1024 column blocks or more, more than 128 groups, or more than 2
+// rows beyond 160 blocks or 64 groups); and its launch.
+bool qmv_bits_burst_shape(int M, int N, int K, QmvBurstShape* out);
+hipError_t launch_qmv_bits_burst(int bits, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                                 const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream);
 hipError_t launch_qmv_bits(int bits, int mode, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
                            const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream);
 

@@ -38,6 +38,8 @@
 #include "device_common.h"
 #include "internal.h"
 
+#include <atomic>
+
 namespace w4a16 {
 
 namespace {
@@ -360,6 +362,208 @@ static hipError_t launch_qmv_bits_t(const uint16_t* x, const uint32_t* wq, const
     hipLaunchKernelGGL((qmv_bits_kernel<BITS, KW, MODE>), dim3((N + 15) / 16), dim3(64 * KW), 0, stream, x, wq, s, b,
                        y, M, N, K);
     return hipGetLastError();
+}
+
+// Burst form of the width-generic matvec, at most 4 rows: the packed layout of the 4-bit burst
+// kernel (qmv_burst.hip) -- 4 K slices in the MFMA's spare rows, A rows 4s + m holding row m of
+// slice s, B columns 4s + j holding column j's codes of slice s, the 4 diagonal 4 x 4 blocks of
+// the result kept -- with the codes of any width.  A workgroup covers 4 columns with KW waves;
+// wave w takes GPW steps of 4 consecutive groups and issues every load of them (codes: 4*BITS
+// bytes per lane and group; scales, biases; its activation slots) before its first MFMA.  The
+// activations are staged in their natural order and put in the codes' order (CodeOrder) as they
+// are read back.  Wave 0 adds the waves' sums in wave order and the 4 slices in a fixed lane
+// pattern, so results do not depend on timing.
+template <int BITS, int GPW, int MR>
+__global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_bits_burst_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int N, int K, int KW) {
+    extern __shared__ __attribute__((aligned(16))) u32x4_t lds[];
+    constexpr int GW = 4 * GPW;   // groups per wave: GPW steps of 4 slices
+    const int G = K >> 7;
+    const int lane = threadIdx.x & 63;
+    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col0 = blockIdx.x * 4;
+    const int g0 = wk * GW;       // step i, slice s: group g0 + 4 i + s
+    const int c = lane & 15, kq = lane >> 4;
+    const int sl = c >> 2, j = c & 3;   // slice and column (B operand) or slice and row (A operand)
+    const int row_bytes = K / 8 * BITS;
+    auto clamp_records = [](int64_t bytes) { return static_cast<int>(bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes); };
+    const int64_t cols = static_cast<int64_t>(N - col0);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + static_cast<size_t>(col0) * row_bytes), 0,
+        clamp_records(cols * row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(scales + static_cast<size_t>(col0) * G), 0, clamp_records(cols * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(biases + static_cast<size_t>(col0) * G), 0, clamp_records(cols * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x), 0, clamp_records(static_cast<int64_t>(M) * K * 2), 0x00020000);
+    u32x4_t* const xs = lds + static_cast<size_t>(wk) * GW * 16 * MR;
+    float* const red = reinterpret_cast<float*>(lds + static_cast<size_t>(KW) * GW * 16 * MR);
+
+    // 1. every load of the wave (past the last group, column or row the per-lane offset passes
+    //    the resource's end and the load returns zeros)
+    uint32_t w[GPW][BITS];
+    uint16_t sv[GPW], bv[GPW];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        const int g = g0 + 4 * i + sl;
+        const uint32_t voff =
+            g < G ? static_cast<uint32_t>(j * row_bytes + g * 16 * BITS + kq * 4 * BITS) : 0x80000000u;
+        load_codes<BITS>(wr, voff, 0, w[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        const int g = g0 + 4 * i + sl;
+        const uint32_t voff = g < G ? static_cast<uint32_t>((j * G + g) * 2) : 0x80000000u;
+        sv[i] = __builtin_amdgcn_raw_buffer_load_b16(sr, voff, 0, 0);
+        bv[i] = __builtin_amdgcn_raw_buffer_load_b16(br, voff, 0, 0);
+    }
+    // activation chunk jj = ((gl * 4 + t) * 4 + q) * MR + m: row m's values gl*128 + q*32 + t*8 .. +7
+    constexpr int XL = GW * 16 * MR / 64;
+    u32x4_t xv[XL];
+#pragma unroll
+    for (int j0 = 0; j0 < XL; ++j0) {
+        const int jj = j0 * 64 + lane;
+        const int m = jj % MR, rr = jj / MR;
+        const int q = rr & 3, t = (rr >> 2) & 3, gl = rr >> 4;
+        const uint32_t voff = m < M && g0 + gl < G
+                                  ? static_cast<uint32_t>(m * K + (g0 + gl) * kGroup + q * 32 + t * 8) * 2u
+                                  : 0x80000000u;
+        xv[j0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, voff, 0, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all loads issued before anything waits on one
+#pragma unroll
+    for (int j0 = 0; j0 < XL; ++j0) xs[j0 * 64 + lane] = xv[j0];
+    asm volatile("" ::: "memory");   // the wave's own slots: only the compiler must keep the order
+
+    // 2. every step: the result lane (c, kq) holds rows 4 kq .. 4 kq + 3 of column c, wanted where
+    //    kq is column c's slice
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    const u32x4_t zu = {0u, 0u, 0u, 0u};
+    const bf16x8_t ones = {__bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f),
+                           __bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f)};
+    const bool arow = j < M && j < MR;
+    const int am = j < MR ? j : 0;
+    f32x4_t yacc = zero4;
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        u32x4_t xn[4], aop[4], bop[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) xn[t] = arow ? xs[(((4 * i + sl) * 4 + t) * 4 + kq) * MR + am] : zu;
+        acts_in_code_order<BITS>(xn, aop);
+        codes_to_bf16<BITS>(w[i], bop);
+        f32x4_t xsum = zero4, p = zero4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, aop[t]);
+            xsum = mfma16x16x32(a, ones, xsum);
+            p = mfma16x16x32(a, __builtin_bit_cast(bf16x8_t, bop[t]), p);
+        }
+        const float s = bf16_bits_to_f32(sv[i]), b = bf16_bits_to_f32(bv[i]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, p[r], __builtin_fmaf(b, xsum[r], yacc[r]));
+    }
+
+    // 3. the wanted lanes hand rows 0..3 of their column to LDS; wave 0, lane 16 s + 4 j + m, adds
+    //    its (slice, column, row) over the waves in wave order, then the 4 slices of each output
+    if (kq == sl) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wk * 64 + sl * 16 + j * 4 + r] = yacc[r];
+    }
+    __syncthreads();
+    if (wk == 0) {
+        float acc = 0.f;
+        int w2 = 0;
+        for (; w2 + 4 <= KW; w2 += 4) {
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = red[(w2 + u) * 64 + lane];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc += v[u];
+        }
+        for (; w2 < KW; ++w2) acc += red[w2 * 64 + lane];
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        const int jo = (lane >> 2) & 3, m = lane & 3;
+        if (lane < 16 && m < M && col0 + jo < N) y[static_cast<size_t>(m) * N + col0 + jo] = f32_to_bf16_bits(acc);
+    }
+}
+
+bool qmv_bits_burst_shape(int M, int N, int K, QmvBurstShape* out) {
+    const int G = K / kGroup;
+    if (M < 1 || M > 4 || K % kGroup != 0 || G < 1 || N < 1) return false;
+    // The 4-bit packed form's domain (below 1024 column blocks of 16; at 3 and 4 rows up to 160
+    // blocks and 64 groups) and its steps: one per wave up to 64 groups, two up to 128.
+    const int blocks = (N + 15) / 16;
+    if (blocks >= 1024 || G > 8 * kQmvBurstMaxWaves || (M > 2 && (blocks > 160 || G > 64))) return false;
+    out->packed = 1;
+    out->gpw = G > 4 * kQmvBurstMaxWaves ? 2 : 1;
+    out->kw = (G + 4 * out->gpw - 1) / (4 * out->gpw);
+    out->rows = M == 1 ? 1 : (M == 2 ? 2 : 4);
+    out->cols = 4;
+    return true;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+constexpr size_t bits_burst_lds_bytes(int kw, int gpw, int mr) {
+    return static_cast<size_t>(kw) * 4 * gpw * 16 * mr * 16 + static_cast<size_t>(kw) * 64 * 4;
+}
+
+template <int BITS, int GPW, int MR>
+hipError_t launch_bits_burst_t(int kw, const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                               uint16_t* y, int M, int N, int K, hipStream_t stream) {
+    static std::atomic<bool> ready[kMaxDevices];   // per instance and device: the LDS permission is set
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    auto kern = qmv_bits_burst_kernel<BITS, GPW, MR>;
+    if (!ready[dev].load(std::memory_order_acquire)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(bits_burst_lds_bytes(kQmvBurstMaxWaves, GPW, MR)));
+        if (e != hipSuccess) return e;
+        ready[dev].store(true, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(kern, dim3((N + 3) / 4), dim3(64 * kw), bits_burst_lds_bytes(kw, GPW, MR), stream, x, wq, s, b,
+                       y, M, N, K, kw);
+    return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_bits_burst_w(const QmvBurstShape& sh, const uint16_t* x, const uint32_t* wq, const uint16_t* s,
+                               const uint16_t* b, uint16_t* y, int M, int N, int K, hipStream_t stream) {
+    switch (sh.gpw * 10 + sh.rows) {
+        case 11: return launch_bits_burst_t<BITS, 1, 1>(sh.kw, x, wq, s, b, y, M, N, K, stream);
+        case 12: return launch_bits_burst_t<BITS, 1, 2>(sh.kw, x, wq, s, b, y, M, N, K, stream);
+        case 14: return launch_bits_burst_t<BITS, 1, 4>(sh.kw, x, wq, s, b, y, M, N, K, stream);
+        case 21: return launch_bits_burst_t<BITS, 2, 1>(sh.kw, x, wq, s, b, y, M, N, K, stream);
+        case 22: return launch_bits_burst_t<BITS, 2, 2>(sh.kw, x, wq, s, b, y, M, N, K, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_qmv_bits_burst(int bits, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                                 const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream) {
+    QmvBurstShape sh;
+    if (!qmv_bits_burst_shape(M, N, K, &sh)) return hipErrorInvalidValue;
+    // the waves' shares of 4 gpw groups cover every group; the row slots cover M
+    if (sh.kw < 1 || sh.kw > kQmvBurstMaxWaves || static_cast<int64_t>(sh.kw) * 4 * sh.gpw < K / kGroup ||
+        sh.rows < M)
+        return hipErrorInvalidValue;
+    switch (bits) {
+        case 1: return launch_bits_burst_w<1>(sh, x, wq, scales, biases, y, M, N, K, stream);
+        case 2: return launch_bits_burst_w<2>(sh, x, wq, scales, biases, y, M, N, K, stream);
+        case 3: return launch_bits_burst_w<3>(sh, x, wq, scales, biases, y, M, N, K, stream);
+        case 4: return launch_bits_burst_w<4>(sh, x, wq, scales, biases, y, M, N, K, stream);
+        case 8: return launch_bits_burst_w<8>(sh, x, wq, scales, biases, y, M, N, K, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 // four waves split K
