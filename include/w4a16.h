@@ -131,9 +131,9 @@ uint64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, i
 /*
  * Decode-row matvec, 1 <= M <= 8 ("Week 2 Day 6", Task 1: the Day 3 matvec serves M <= 8;
  * "Route affine qmv_wide ...": a dequantized group is reused across the M rows).  Needs no
- * workspace.  M > 8 returns W4A16_ERR_UNSUPPORTED.  The kernel family follows w4a16_plan
- * (up to 4 rows and 80 groups, below 16k columns or 32k under 32 groups: the burst kernel, whose waves issue all of their
- * loads at once; wider heads: the persistent wide kernel).
+ * workspace.  M > 8 returns W4A16_ERR_UNSUPPORTED.  The kernel family follows w4a16_plan: up
+ * to 4 rows below 32k columns (at 1 and 2 rows up to 128 groups, at 3 and 4 up to 80) the burst
+ * kernel, whose waves issue all of their loads at once; wider heads the persistent wide kernel.
  */
 int qmv_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
               uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, void* stream);
@@ -272,7 +272,7 @@ enum w4a16_qmv_mode {
     W4A16_QMV_PER_ROW = 2,     /* per-row dot products, M <= 2                                      */
     W4A16_QMV_FAMILIES = 3,    /* bits = 4 only: the kernel families and policy of qmv_w4a16        */
     W4A16_QMV_BURST = 4        /* M <= 4: every wave issues all of its loads at once, 4 K slices in
-                                  the matrix core's spare rows (below 16k columns; beyond 160 blocks
+                                  the matrix core's spare rows (below 32k columns; beyond 160 blocks
                                   of 16 columns or 64 groups only up to 2 rows; at most 128 groups) */
 };
 

@@ -102,33 +102,38 @@ def test_grid_covers_the_output():
 
 
 def test_burst_matvec_plans():
-    # up to 4 rows and 80 groups, below 1024 column blocks of 16 or below 2048 under 32 groups:
-    # the burst kernel.  Packed form (4 columns per workgroup, steps of 4 groups, one step per
-    # wave up to 64 groups, two above) below 1024 blocks at 1 and 2 rows, and at 3 and 4 rows
-    # for at most 160 blocks and 64 groups; otherwise 16 columns per workgroup with g = 2
-    # groups per wave (3 from 1024 blocks), at least ceil(G / 16)
+    # up to 4 rows below 2048 column blocks of 16: the burst kernel.  Packed form (4 columns per
+    # workgroup, steps of 4 groups: one per wave below 1024 blocks up to 64 groups, two
+    # otherwise) at 1 and 2 rows up to 128 groups, and at 3 and 4 rows up to 160 blocks and 64
+    # groups; otherwise, at 3 and 4 rows up to 80 groups and not from 1024 blocks at 32 groups,
+    # 16 columns per workgroup with g = 2 groups per wave (3 from 1024 blocks), at least
+    # ceil(G / 16)
     for M, N, K, cols, waves, per_wave in [
             (1, 9728, 2560, 4, 5, 4), (2, 9728, 2560, 4, 5, 4), (4, 9728, 2560, 16, 10, 2),
             (1, 4096, 2560, 4, 5, 4), (1, 1024, 2560, 4, 5, 4), (4, 1024, 2560, 4, 5, 4),
             (1, 2560, 9728, 4, 10, 8), (3, 2560, 9728, 16, 16, 5), (3, 2600, 8192, 16, 16, 4),
             (3, 2560, 8192, 4, 16, 4), (2, 1000, 10240, 4, 10, 8), (1, 96, 128, 4, 1, 4),
-            (4, 2560, 4096, 4, 8, 4), (1, 16400, 2560, 16, 7, 3), (2, 24600, 384, 16, 1, 3),
-            (1, 32752, 2560, 16, 7, 3), (4, 16368, 4096, 16, 16, 2)]:
+            (4, 2560, 4096, 4, 8, 4), (1, 16400, 2560, 4, 3, 8), (2, 24600, 384, 4, 1, 8),
+            (1, 26608, 2560, 4, 3, 8), (4, 16368, 4096, 16, 16, 2), (3, 16400, 2560, 16, 7, 3),
+            (1, 32752, 4096, 4, 4, 8), (1, 30000, 384, 4, 1, 8),
+            (1, 16400, 9728, 4, 10, 8), (2, 1000, 16384, 4, 16, 8), (1, 24600, 9728, 4, 10, 8)]:
         p = plan(M, N, K)
         G = K // 128
         assert p["variant"] == 4, (M, N, K)                  # the burst kernel's instance index
         assert (p["tile_n"], p["k_waves"], p["block_threads"]) == (cols, waves, 64 * waves), (M, N, K)
         assert (p["grid_x"], p["workspace_bytes"]) == (-(-N // cols), 0)
         assert waves * per_wave >= G and waves <= 16
-    # 5..8 rows, more than 80 groups, 2048 blocks or more and 1024 blocks at 32 groups or more
-    # keep the other families
+    # 5..8 rows, 2048 blocks or more, more groups than the forms take, and 1024 blocks at 32
+    # groups or more above 2 rows keep the other families
     assert plan(5, 9728, 2560)["variant"] == 3
     assert plan(8, 2560, 9728)["variant"] == 0
-    assert plan(1, 1000, 10368)["variant"] == 0          # 81 groups
+    assert plan(1, 1000, 16512)["variant"] == 0          # 129 groups
+    assert plan(3, 1000, 10368)["variant"] == 0          # 81 groups at 3 rows
     assert plan(5, 16400, 384)["variant"] == 1
     assert plan(1, 32768, 2560)["variant"] == 2          # 2048 blocks
-    assert plan(4, 16400, 4096)["variant"] == 2          # 1025 blocks at 32 groups
-    assert plan(1, 24600, 9728)["variant"] == 2
+    assert plan(1, 26624, 2560)["variant"] == 2          # 1664 blocks under 32 groups
+    assert plan(4, 16400, 4096)["variant"] == 2          # 1025 blocks at 32 groups, 4 rows
+    assert plan(3, 24600, 9728)["variant"] == 2
     assert plan(1, 151936, 2560)["variant"] == 2
 
 
@@ -305,21 +310,21 @@ def test_gate_up_validates_before_launch(lib):
 
 def test_qmv_affine_plans():
     # measured routing: qmv_w4a16's policy at 4 bits; at 1, 2, 3 and 8 bits the burst form where
-    # it applies (at most 4 rows, below 1024 column blocks of 16 and 128 groups; beyond 160
+    # it applies (at most 4 rows, below 2048 column blocks of 16 and 128 groups; beyond 160
     # blocks or 64 groups only up to 2 rows), the row-amortized kernel elsewhere
     for bits in w4.BITS:
         for M in range(1, 9):
-            for N, K in [(4000, 2560), (151936, 2560), (2560, 9728), (1000, 16384), (2000, 8192)]:
+            for N, K in [(4000, 2560), (151936, 2560), (2560, 9728), (1000, 16384), (2000, 8192), (20000, 4096)]:
                 p = w4.qmv_affine_plan(M, N, K, bits, w4.QMV_POLICY, 128, CUS)
                 assert p["path"] == w4.PATH_QMV and p["workspace_bytes"] == 0
                 blocks, G = -(-N // 16), K // 128
-                burst = M <= 4 and blocks < 1024 and G <= 128 and (M <= 2 or (blocks <= 160 and G <= 64))
+                burst = M <= 4 and blocks < 2048 and G <= 128 and (M <= 2 or (blocks <= 160 and G <= 64))
                 if bits == 4:
                     q = plan(M, N, K, path=w4.PATH_QMV) if G <= 8192 else None
                     assert p["variant"] == w4.QMV_FAMILIES
                     assert (p["tile_n"], p["grid_x"], p["k_waves"]) == (q["tile_n"], q["grid_x"], q["k_waves"])
                 elif burst:
-                    steps = 2 if G > 64 else 1
+                    steps = 2 if G > 64 or blocks >= 1024 else 1
                     assert p["variant"] == w4.QMV_BURST, (bits, M, N, K)
                     assert (p["tile_n"], p["grid_x"]) == (4, -(-N // 4))
                     assert p["k_waves"] == -(-G // (4 * steps)) and p["block_threads"] == 64 * p["k_waves"]
@@ -330,7 +335,7 @@ def test_qmv_affine_plans():
         for mode in (w4.QMV_AMORTIZED, w4.QMV_PER_ROW, w4.QMV_BURST):
             assert w4.qmv_affine_plan(2, 4000, 2560, bits, mode, 128, CUS)["variant"] == mode
         # the forced burst form outside its shapes
-        for M, N, K in [(5, 4000, 2560), (1, 20000, 2560), (3, 4000, 2560), (1, 1000, 16512)]:
+        for M, N, K in [(5, 4000, 2560), (1, 32768, 2560), (3, 4000, 2560), (1, 1000, 16512)]:
             with pytest.raises(NotImplementedError):
                 w4.qmv_affine_plan(M, N, K, bits, w4.QMV_BURST, 128, CUS)
 

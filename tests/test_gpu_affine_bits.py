@@ -25,10 +25,10 @@ MODES = {"policy": 0, "amortized": 1, "per_row": 2, "burst": 4}
 
 
 def burst_applies(M, N, K):
-    """Shapes of the burst form: at most 4 rows, below 1024 column blocks of 16 and 128 groups;
+    """Shapes of the burst form: at most 4 rows, below 2048 column blocks of 16 and 128 groups;
     beyond 160 blocks or 64 groups only up to 2 rows."""
     blocks, G = -(-N // 16), K // 128
-    return M <= 4 and blocks < 1024 and G <= 128 and (M <= 2 or (blocks <= 160 and G <= 64))
+    return M <= 4 and blocks < 2048 and G <= 128 and (M <= 2 or (blocks <= 160 and G <= 64))
 
 
 def run_affine(lib, p, nbits, mode, dev=None):

@@ -18,8 +18,9 @@ pytestmark = pytest.mark.gpu
 
 BURST = 4   # the plan's instance index of the burst kernel
 
-# (N, K) and what the plan makes of it: packed (tile_n 4) at 1 and 2 rows below 1024 column
-# blocks, and at 3 and 4 rows up to 160 blocks and 64 groups; 16 columns otherwise
+# (N, K) and what the plan makes of it: the packed form (tile_n 4) at 1 and 2 rows below 2048
+# column blocks (below 1664 under 32 groups where the wide kernel applies), and at 3 and 4 rows
+# up to 160 blocks and 64 groups; 16 columns otherwise
 SHAPES = [
     (96, 128),      # one group: a single wave (packed at every M)
     (3, 1280),      # fewer columns than one packed workgroup covers
@@ -29,20 +30,31 @@ SHAPES = [
     (200, 8192),    # 64 groups: sixteen packed waves of one step
     (300, 9728),    # 76 groups: ten packed waves of two steps at 1-2 rows; sixteen of five at 3-4
     (50, 10240),    # 80 groups: packed at 1-2 rows; sixteen waves of five at 3-4
-    (24600, 384),   # 1538 column blocks: one wave of three groups
-    (32744, 1280),  # 2047 column blocks, the last ragged: four waves of three (the last of one)
+    (40, 16384),    # 128 groups: sixteen packed waves of two steps at 1-2 rows (the others at 3-4)
+    (24600, 384),   # 1538 column blocks: packed, one wave of two steps, at 1-2 rows; one wave of three groups at 3-4
+    (32744, 1152),  # 2047 blocks, the last ragged, 9 groups (the wide kernel needs an even count):
+                    # packed at 1-2 rows; three waves of three groups at 3-4
 ]
 
 
 def _plan(lib, M, N, K):
+    """The plan, which is the burst kernel's except for more than 80 groups at 3 and 4 rows."""
     p = lib.w4a16_plan(M, N, K, 128, lib.PATH_QMV)
-    assert p["variant"] == BURST and p["tile_n"] in (4, 16), p
+    if M <= 2 or K // 128 <= 80:
+        assert p["variant"] == BURST and p["tile_n"] in (4, 16), p
     return p
 
 
+def _plan_any(lib, M, N, K):
+    return lib.w4a16_plan(M, N, K, 128, lib.PATH_QMV)
+
+
 def test_both_forms_are_covered(lib):
-    forms = {(M, _plan(lib, M, N, K)["tile_n"]) for N, K in SHAPES for M in (1, 2, 3, 4)}
-    assert {(M, 4) for M in (1, 2, 3, 4)} <= forms and {(M, 16) for M in (1, 2, 3, 4)} <= forms
+    """The packed form at every row count, the 16-column form at 3 and 4 rows (the only rows it
+    serves)."""
+    forms = {(M, _plan_any(lib, M, N, K)["variant"], _plan_any(lib, M, N, K)["tile_n"])
+             for N, K in SHAPES for M in (1, 2, 3, 4)}
+    assert {(M, BURST, 4) for M in (1, 2, 3, 4)} <= forms and {(M, BURST, 16) for M in (3, 4)} <= forms
 
 
 @pytest.mark.parametrize("kind", ["sums", "pow2"])

@@ -191,14 +191,17 @@ QMV_FAMILY_CASES = [
     (2600, 8192, 3, 4),      # 64 groups: burst, 4 groups in each of 16 waves
     (2600, 8192, 5, 0),      # 64 groups above 4 rows: the dequantizing K-split kernel
     (1000, 10240, 2, 4),     # 80 groups: packed burst, ten waves of two steps of four groups
-    (1000, 10368, 2, 0),     # 81 groups: past it
+    (1000, 16384, 1, 4),     # 128 groups at 1 row: packed burst, sixteen waves of two steps
+    (20000, 8192, 2, 4),     # 1250 blocks at 2 rows: packed burst instead of the wide kernel
+    (1000, 10368, 3, 0),     # 81 groups at 3 rows: past it
     (1000, 9728, 8, 0),      # long K, ragged N
     (16390, 384, 8, 1),      # 1025 blocks, odd group count
     (33000, 256, 1, 2),      # one group pair per block: every step ends a block
     (24600, 512, 5, 2),      # ragged N and M
     (30010, 1024, 8, 2),     # eight rows
     (24600, 384, 6, 1),      # odd group count: the wide kernel does not apply
-    (24600, 384, 2, 4),      # burst from 1024 blocks: three groups per wave, odd group count
+    (24600, 384, 2, 4),      # packed burst from 1024 blocks: two steps per wave, odd group count
+    (30000, 2560, 1, 2),     # 1875 blocks under 32 groups: the wide kernel
     (16400, 4096, 5, 2),     # wide from 1024 blocks once K >= 4096
     (16400, 4096, 4, 2),     # the same at 4 rows (the burst kernel stops at 1024 blocks there)
     (20000, 2560, 4, 4),     # burst at 1250 blocks under 32 groups: seven waves of three

@@ -33,8 +33,9 @@ constexpr int kQmvBurstMaxGroups = 5;
 // The burst kernel's form for an M x N x K matvec: packed (4 K slices in the MFMA's spare rows,
 // 4 columns per workgroup, gpw steps of 4 groups per wave, rows = activation row slots) or not
 // (16 columns per workgroup, gpw groups per wave); kw waves per workgroup.  False where it does
-// not apply (more than 4 rows, more than 16 * 5 groups, 2048 column blocks or more, or 1024
-// blocks or more at 32 groups or more).
+// not apply: more than 4 rows, 2048 column blocks or more, or 1664 blocks or more under 32
+// groups where the wide kernel applies; at 1 and 2 rows more than 128 groups; at 3 and 4 rows
+// more than 80 groups, or 1024 blocks or more at 32 groups or more.
 struct QmvBurstShape {
     int packed, kw, gpw, rows, cols;
 };
@@ -154,7 +155,7 @@ hipError_t launch_splitk_reduce_glu(const float* ws, uint16_t* h, int64_t MN, in
 // matrix core (mode kQmvBitsMatrix) or per row with dot products (kQmvBitsRows, M <= 2).
 constexpr int kQmvBitsMatrix = 0, kQmvBitsRows = 1;
 // The burst form of the width-generic matvec (packed layout, at most 4 rows): its shape, false
-// where it does not apply (1024 column blocks or more, more than 128 groups, or more than 2
+// where it does not apply (2048 column blocks or more, more than 128 groups, or more than 2
 // rows beyond 160 blocks or 64 groups); and its launch.
 bool qmv_bits_burst_shape(int M, int N, int K, QmvBurstShape* out);
 hipError_t launch_qmv_bits_burst(int bits, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,

@@ -493,12 +493,13 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_bits_burst_kernel(
 bool qmv_bits_burst_shape(int M, int N, int K, QmvBurstShape* out) {
     const int G = K / kGroup;
     if (M < 1 || M > 4 || K % kGroup != 0 || G < 1 || N < 1) return false;
-    // The 4-bit packed form's domain (below 1024 column blocks of 16; at 3 and 4 rows up to 160
-    // blocks and 64 groups) and its steps: one per wave up to 64 groups, two up to 128.
+    // The 4-bit packed form's domain (below 2048 column blocks of 16 and up to 128 groups; at 3
+    // and 4 rows up to 160 blocks and 64 groups) and its steps: one per wave below 1024 blocks
+    // up to 64 groups, two otherwise.
     const int blocks = (N + 15) / 16;
-    if (blocks >= 1024 || G > 8 * kQmvBurstMaxWaves || (M > 2 && (blocks > 160 || G > 64))) return false;
+    if (blocks >= 2048 || G > 8 * kQmvBurstMaxWaves || (M > 2 && (blocks > 160 || G > 64))) return false;
     out->packed = 1;
-    out->gpw = G > 4 * kQmvBurstMaxWaves ? 2 : 1;
+    out->gpw = blocks >= 1024 || G > 4 * kQmvBurstMaxWaves ? 2 : 1;
     out->kw = (G + 4 * out->gpw - 1) / (4 * out->gpw);
     out->rows = M == 1 ? 1 : (M == 2 ? 2 : 4);
     out->cols = 4;

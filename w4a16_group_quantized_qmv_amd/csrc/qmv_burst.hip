@@ -305,30 +305,35 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_packed_kerne
 bool qmv_burst_shape(int M, int N, int K, QmvBurstShape* out) {
     const int G = K / kGroup;
     if (M < 1 || M > kBurstRows || K % kGroup != 0 || G < 1 || N < 1) return false;
-    // Measured on MI355X (M = 1 and 4, graph-replayed launches over rotating weights): the
-    // fewer groups a wave owns the better while the launch has fewer than 1024 column blocks
-    // (two per wave: 7.1 us on 9728 x 2560 against 7.1-7.4 with three to five, 8.6 for the
-    // row-amortized loop kernel; 6.2 us on 2560 x 4096 against 8.0); from 1024 blocks three
-    // per wave (16400 x 2560: 8.5 us, the wide kernel 10.9; 24600 x 2560: 11.5 against 12.8),
-    // but not from 32 groups (16400 x 4096: 18.2 us, the wide kernel 16.2).  From 2048 blocks
-    // the persistent wide kernel leads (the 151936-column head: 43 us against 50 at best).
-    // Above 32 groups, as few groups per wave as 16 waves allow.
+    // From 2048 column blocks of 16 the persistent wide kernel leads both forms (151936 x 2560:
+    // 43 us against 50-55; 32768 and 65536 x 2560: 13.0 and 21.2 against 14.5 and 24.9), and
+    // from 1664 blocks under 32 groups where it applies (30000 x 2560: 12.9 against 13.6 us at
+    // M = 1, 13.1 against 15.4 at M = 2; 24600 x 2560: 12.9 against 12.0 and 13.2 against 13.3).
     const int blocks = (N + 15) / 16;
-    if (blocks >= 2048 || (blocks >= 1024 && G >= 32) || G > kQmvBurstMaxWaves * kQmvBurstMaxGroups) return false;
-    // The packed form, below 1024 blocks: at 1 and 2 rows everywhere (M = 1: 2560 x 9728
-    // 7.5-7.7 us against 9.1, 1024 x 2560 3.3 against 4.1, 4096 x 2560 4.3 against 4.5, 9728 x
-    // 2560 6.7 against 7.6; M = 2 alike); at 3 and 4 rows, whose 4-row activation slots take 4x
-    // the LDS and loads, only for at most 160 blocks and 64 groups (M = 4: 1024 x 2560 3.8
-    // against 4.5, 2560 x 4096 6.7 against 6.9; 2560 x 9728 15.7 against 10.6).  One step per
-    // wave (4 groups) up to 64 groups, two above.
-    if (blocks < 1024 && (M <= 2 || (blocks <= 160 && G <= 64))) {
+    if (blocks >= 2048 || (blocks >= 1664 && G < 32 && qmv_wide_fits(M, K))) return false;
+    // The packed form.  At 1 and 2 rows below 2048 blocks and up to 128 groups (graph-replayed,
+    // rotating weights, M = 1, N x K: 9728 x 2560 6.7 us against 7.1-7.6 for the 16-column
+    // form, 2560 x 9728 7.5-7.8 against 9.0, 1024 x 2560 3.3 against 4.1; from 1024 blocks, two steps
+    // per wave, against the wide kernel: 16400 x 9728 27.3 against 42.3 us, 20000 x 8192 23.4
+    // against 38.1, 16400 x 4096 11.6 against 16.1, 24600 x 4096 15.4 against 18.6; beyond 80
+    // groups against the K-split kernel: 1000 x 16384 5.5 against 17.4).  At 3 and
+    // 4 rows, whose 4-row activation slots take 4x the LDS and loads, only up to 160 blocks and
+    // 64 groups (M = 4: 1024 x 2560 3.8 against 4.5, 2560 x 4096 6.7 against 6.9; 2560 x 9728
+    // 15.7 against 10.6).  One step of 4 groups per wave below 1024 blocks up to 64 groups, two
+    // steps otherwise.
+    if ((M <= 2 && G <= 8 * kQmvBurstMaxWaves) || (blocks <= 160 && G <= 4 * kQmvBurstMaxWaves)) {
         out->packed = 1;
-        out->gpw = G > 4 * kQmvBurstMaxWaves ? 2 : 1;
+        out->gpw = blocks >= 1024 || G > 4 * kQmvBurstMaxWaves ? 2 : 1;
         out->kw = (G + 4 * out->gpw - 1) / (4 * out->gpw);
         out->rows = M == 1 ? 1 : (M == 2 ? 2 : 4);
         out->cols = 4;
         return true;
     }
+    // The 16-column form at 3 and 4 rows: the fewer groups a wave owns the better while the
+    // launch has fewer than 1024 blocks (two per wave), from 1024 blocks three (16400 x 2560:
+    // 8.5 us, the wide kernel 10.9), but not from 32 groups (16400 x 4096: 18.2 us, the wide
+    // kernel 16.2); above 32 groups, as few groups per wave as 16 waves allow, up to 80 groups.
+    if ((blocks >= 1024 && G >= 32) || G > kQmvBurstMaxWaves * kQmvBurstMaxGroups) return false;
     int g = blocks >= 1024 ? 3 : 2;
     const int need = (G + kQmvBurstMaxWaves - 1) / kQmvBurstMaxWaves;
     if (need > g) g = need;
