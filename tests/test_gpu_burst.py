@@ -94,3 +94,47 @@ def test_burst_writes_only_its_output(lib, M, N, K):
     assert np.all(out[0] == SENTINEL) and np.all(out[-1] == SENTINEL), "write outside [M, N]"
     assert not np.any(out[1:-1] == SENTINEL), "element of y left unwritten"
     assert_parity(out[1:-1], p)
+
+
+def test_burst_calls_in_a_graph_replay(lib):
+    """Captured burst calls (the packed form at one row, the 16-column form at four, the
+    width-generic form at 3 bits) replay like the eager calls; replays alternate with eager work
+    on the same outputs."""
+    import torch
+    cases = [(1, 2600, 2560, 4), (4, 4000, 2560, 4), (2, 1000, 2560, 3)]
+    probs = [synth.random_problem(700 + i, M, N, K, bits=nb) for i, (M, N, K, nb) in enumerate(cases)]
+    devs = [to_device(p) for p in probs]
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0") for M, N, _, _ in cases]
+    announce("burst graph replay")
+
+    def calls():
+        for (M, N, K, nb), d, y in zip(cases, devs, ys):
+            if nb == 4:
+                lib.qmv_w4a16(*d, y=y)
+            else:
+                lib.qmv_affine(*d, nb, y=y, mode=lib.QMV_BURST)
+
+    calls()
+    torch.cuda.synchronize()
+    refs = [bits(y) for y in ys]
+    assert lib.w4a16_plan(1, 2600, 2560, 128, lib.PATH_QMV)["tile_n"] == 4
+    assert lib.w4a16_plan(4, 4000, 2560, 128, lib.PATH_QMV)["tile_n"] == 16
+    for p, r in zip(probs[:2], refs[:2]):
+        assert_parity(r, p)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            calls()
+    torch.cuda.synchronize()
+    for i in range(3):
+        for y in ys:
+            y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        for y, r in zip(ys, refs):
+            assert np.array_equal(bits(y), r), f"replay {i}"
+        calls()                                            # eager, same outputs
+        torch.cuda.synchronize()
+        for y, r in zip(ys, refs):
+            assert np.array_equal(bits(y), r), f"eager call after replay {i}"
