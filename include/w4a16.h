@@ -132,8 +132,9 @@ uint64_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, i
  * Decode-row matvec, 1 <= M <= 8 ("Week 2 Day 6", Task 1: the Day 3 matvec serves M <= 8;
  * "Route affine qmv_wide ...": a dequantized group is reused across the M rows).  Needs no
  * workspace.  M > 8 returns W4A16_ERR_UNSUPPORTED.  The kernel family follows w4a16_plan: up
- * to 4 rows below 32k columns (at 1 and 2 rows up to 128 groups, at 3 and 4 up to 80) the burst
- * kernel, whose waves issue all of their loads at once; wider heads the persistent wide kernel.
+ * to 4 rows below 32k columns (at 1 and 2 rows up to 128 groups, at 3 and 4 up to 80) and 5 to
+ * 8 rows below 16k columns up to 64 groups the burst kernel, whose waves issue all of their
+ * loads at once; wider heads the persistent wide kernel.
  */
 int qmv_w4a16(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases,
               uint16_t* y, int64_t M, int64_t N, int64_t K, int32_t group, void* stream);

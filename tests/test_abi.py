@@ -102,7 +102,9 @@ def test_grid_covers_the_output():
 
 
 def test_burst_matvec_plans():
-    # up to 4 rows below 2048 column blocks of 16: the burst kernel.  Packed form (4 columns per
+    # up to 4 rows below 2048 column blocks of 16, and 5 to 8 rows below 1024 blocks up to 64
+    # groups (16 columns, 8 row slots, g = 2 groups per wave or ceil(G / 16)): the burst
+    # kernel.  Packed form (4 columns per
     # workgroup, steps of 4 groups: one per wave below 1024 blocks up to 64 groups, two
     # otherwise) at 1 and 2 rows up to 128 groups, and at 3 and 4 rows up to 160 blocks and 64
     # groups; otherwise, at 3 and 4 rows up to 80 groups and not from 1024 blocks at 32 groups,
@@ -116,17 +118,20 @@ def test_burst_matvec_plans():
             (4, 2560, 4096, 4, 8, 4), (1, 16400, 2560, 4, 3, 8), (2, 24600, 384, 4, 1, 8),
             (1, 26608, 2560, 4, 3, 8), (4, 16368, 4096, 16, 16, 2), (3, 16400, 2560, 16, 7, 3),
             (1, 32752, 4096, 4, 4, 8), (1, 30000, 384, 4, 1, 8),
-            (1, 16400, 9728, 4, 10, 8), (2, 1000, 16384, 4, 16, 8), (1, 24600, 9728, 4, 10, 8)]:
+            (1, 16400, 9728, 4, 10, 8), (2, 1000, 16384, 4, 16, 8), (1, 24600, 9728, 4, 10, 8),
+            (5, 9728, 2560, 16, 10, 2), (8, 4096, 2560, 16, 10, 2), (6, 2600, 8192, 16, 16, 4),
+            (8, 96, 128, 16, 1, 2), (7, 9728, 4096, 16, 16, 2)]:
         p = plan(M, N, K)
         G = K // 128
         assert p["variant"] == 4, (M, N, K)                  # the burst kernel's instance index
         assert (p["tile_n"], p["k_waves"], p["block_threads"]) == (cols, waves, 64 * waves), (M, N, K)
         assert (p["grid_x"], p["workspace_bytes"]) == (-(-N // cols), 0)
         assert waves * per_wave >= G and waves <= 16
-    # 5..8 rows, 2048 blocks or more, more groups than the forms take, and 1024 blocks at 32
-    # groups or more above 2 rows keep the other families
-    assert plan(5, 9728, 2560)["variant"] == 3
-    assert plan(8, 2560, 9728)["variant"] == 0
+    # more rows, 2048 blocks or more, more groups than the forms take, 1024 blocks at 32 groups
+    # or more above 2 rows, and 1024 blocks at 5 to 8 rows keep the other families
+    assert plan(8, 2560, 9728)["variant"] == 0          # 76 groups at 8 rows
+    assert plan(8, 16400, 384)["variant"] == 1
+    assert plan(9, 9728, 2560, path=w4.PATH_SKINNY)["variant"] == 3
     assert plan(1, 1000, 16512)["variant"] == 0          # 129 groups
     assert plan(3, 1000, 10368)["variant"] == 0          # 81 groups at 3 rows
     assert plan(5, 16400, 384)["variant"] == 1

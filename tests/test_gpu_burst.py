@@ -138,3 +138,24 @@ def test_burst_calls_in_a_graph_replay(lib):
         torch.cuda.synchronize()
         for y, r in zip(ys, refs):
             assert np.array_equal(bits(y), r), f"eager call after replay {i}"
+
+
+# 5 to 8 rows: the 16-column form with 8 row slots (below 1024 column blocks, up to 64 groups)
+ROWS8_SHAPES = [(96, 128), (33, 640), (9728, 2560), (200, 8192), (1000, 4096)]
+
+
+@pytest.mark.parametrize("kind", ["sums", "pow2"])
+@pytest.mark.parametrize("N,K", ROWS8_SHAPES)
+def test_burst_eight_row_slots_integer_cases_are_bit_exact(lib, N, K, kind):
+    for M in (5, 6, 7, 8):
+        p = lib.w4a16_plan(M, N, K, 128, lib.PATH_QMV)
+        assert p["variant"] == BURST and p["tile_n"] == 16, p
+        case, expect = _exact_case(kind, M, N, K, seed=5600 + 7 * M + N + K + (kind == "pow2"))
+        assert np.array_equal(run(lib, case, "qmv"), expect), f"M={M}"
+
+
+@pytest.mark.parametrize("N,K", ROWS8_SHAPES)
+def test_burst_eight_row_slots_match_oracle(lib, N, K):
+    for M in (5, 8):
+        p = synth.random_problem(640 + M + N % 89, M, N, K)
+        assert_parity(run(lib, p, "qmv"), p)

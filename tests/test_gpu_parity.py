@@ -90,10 +90,11 @@ def test_identity_unpack_is_bit_exact_qmv(lib, N):
         assert np.array_equal(y, expect[r0:r0 + 8]), f"rows {r0}..{r0 + 7}"
 
 
-@pytest.mark.parametrize("path,N,K", [("qmv", 160, 512), ("qmv", 6150, 512), ("qmv", 300, 8192), ("qmv", 16400, 512),
+@pytest.mark.parametrize("path,N,K", [("qmv", 160, 512), ("qmv", 6150, 512), ("qmv", 300, 9728), ("qmv", 16400, 512),
                                       ("qmv", 24600, 512), ("qmm", 160, 512)])
 def test_small_integer_sums_are_exact(lib, path, N, K):
-    # qmv cases cover the row-amortized, dequantizing K-split, 64-column and wide kernels
+    # qmv cases (8 rows) cover the burst kernel with 8 row slots, the dequantizing K-split, the
+    # 64-column and the wide kernels
     rng = np.random.default_rng(8)
     M = 8 if path == "qmv" else 40
     q = rng.integers(0, 16, (N, K))
@@ -181,15 +182,16 @@ def test_all_zero_codes(lib, path):
 # (N, K, M, kernel the policy picks): 0 = 16-column dequantizing workgroups splitting K four ways,
 # 1 = 64-column workgroups, 2 = persistent wide kernel (activations and their group sums staged
 # in LDS once, one wave per 16-column block), 3 = row-amortized 16-column workgroups (exact codes
-# on the matrix core, s * P + b * X per group), 4 = burst (up to 4 rows: every wave issues all
-# its loads at once)
+# on the matrix core, s * P + b * X per group; at 4 bits now only above 8 rows, on the skinny
+# path), 4 = burst (every wave issues all its loads at once)
 QMV_FAMILY_CASES = [
     (4000, 256, 3, 4),       # burst, ragged N
     (6150, 384, 1, 4),       # burst, odd group count, ragged N
-    (4000, 256, 6, 3),       # row-amortized, ragged N
-    (6150, 384, 5, 3),       # row-amortized, odd group count
+    (4000, 256, 6, 4),       # burst with 8 row slots, ragged N
+    (6150, 384, 5, 4),       # burst with 8 row slots, odd group count
     (2600, 8192, 3, 4),      # 64 groups: burst, 4 groups in each of 16 waves
-    (2600, 8192, 5, 0),      # 64 groups above 4 rows: the dequantizing K-split kernel
+    (2600, 8192, 5, 4),      # 64 groups at 5 rows: burst, 8 row slots, 16 waves of 4 groups
+    (2600, 8320, 5, 0),      # 65 groups at 5 rows: the dequantizing K-split kernel
     (1000, 10240, 2, 4),     # 80 groups: packed burst, ten waves of two steps of four groups
     (1000, 16384, 1, 4),     # 128 groups at 1 row: packed burst, sixteen waves of two steps
     (20000, 8192, 2, 4),     # 1250 blocks at 2 rows: packed burst instead of the wide kernel
@@ -206,7 +208,7 @@ QMV_FAMILY_CASES = [
     (16400, 4096, 4, 2),     # the same at 4 rows (the burst kernel stops at 1024 blocks there)
     (20000, 2560, 4, 4),     # burst at 1250 blocks under 32 groups: seven waves of three
     (9728, 4096, 4, 4),      # 608 blocks at K = 4096: burst, 2 groups per wave
-    (9728, 4096, 7, 3),      # the same above 4 rows: row-amortized
+    (9728, 4096, 7, 4),      # the same at 7 rows: burst with 8 row slots
     (24600, 9728, 8, 1),     # activations too large for the wide kernel's LDS
 ]
 

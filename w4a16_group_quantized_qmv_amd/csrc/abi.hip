@@ -88,10 +88,10 @@ void plan_qmv(int64_t M, int64_t N, int64_t K, int32_t cus, w4a16_plan_t* p) {
     // 16-column dequantizing kernel whose four waves split K leads by 5-20%; around 16k columns
     // the 64-column kernel leads; from 24k columns (16k at 32 groups or more) the persistent wide
     // kernel, which streams whole blocks per wave, wins by 1.4x on the 151936-column head.
-    // Up to 4 rows below 32k columns (qmv_burst_shape gives the row, group and width limits),
-    // the burst kernel (every load of a wave issued at once, in its packed or 16-column form)
-    // leads all of them: by 15-25% below 16k columns and by 7-39% against the wide kernel at
-    // 16k-32k columns.
+    // Up to 4 rows below 32k columns and 5 to 8 rows below 16k columns (qmv_burst_shape gives
+    // the row, group and width limits), the burst kernel (every load of a wave issued at once,
+    // in its packed or 16-column form) leads all of them: at up to 4 rows by 15-25% below 16k
+    // columns and by 7-39% against the wide kernel at 16k-32k columns; at 5 to 8 rows by 7-10%.
     const int64_t blocks16 = ceil_div(N, 16);
     const int64_t G = K / W4A16_GROUP;
     int variant;

@@ -24,18 +24,20 @@ constexpr int kQmvWideVariant = 2;
 // The row-amortized kernel of the width-generic matvec at 4 bits (16 columns, 4 waves split K):
 // exact integer codes on the matrix core and y += s * P + b * X per group.
 constexpr int kQmvAmortizedVariant = 3;
-// The burst kernel (4-bit, at most 4 rows): a workgroup of up to kQmvBurstMaxWaves waves on one
-// 16-column block, each wave owning at most kQmvBurstMaxGroups groups and issuing all their
-// loads before it computes; the wave count depends on the shape (qmv_burst_shape).
+// The burst kernel (4-bit, at most 8 rows): a workgroup of up to kQmvBurstMaxWaves waves on one
+// 16-column block (or 4 in the packed form), each wave owning at most kQmvBurstMaxGroups groups
+// (or steps of 4) and issuing all their loads before it computes; the wave count depends on the
+// shape (qmv_burst_shape).
 constexpr int kQmvBurstVariant = 4;
 constexpr int kQmvBurstMaxWaves = 16;
 constexpr int kQmvBurstMaxGroups = 5;
 // The burst kernel's form for an M x N x K matvec: packed (4 K slices in the MFMA's spare rows,
 // 4 columns per workgroup, gpw steps of 4 groups per wave, rows = activation row slots) or not
-// (16 columns per workgroup, gpw groups per wave); kw waves per workgroup.  False where it does
-// not apply: more than 4 rows, 2048 column blocks or more, or 1664 blocks or more under 32
-// groups where the wide kernel applies; at 1 and 2 rows more than 128 groups; at 3 and 4 rows
-// more than 80 groups, or 1024 blocks or more at 32 groups or more.
+// (16 columns per workgroup, gpw groups per wave, 4 or 8 row slots); kw waves per workgroup.
+// False where it does not apply: more than 8 rows, 2048 column blocks or more, or 1664 blocks
+// or more under 32 groups where the wide kernel applies; at 1 and 2 rows more than 128 groups;
+// at 3 and 4 rows more than 80 groups, or 1024 blocks or more at 32 groups or more; at 5 to 8
+// rows 1024 blocks or more, or more than 64 groups.
 struct QmvBurstShape {
     int packed, kw, gpw, rows, cols;
 };

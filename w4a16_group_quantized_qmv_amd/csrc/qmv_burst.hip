@@ -1,4 +1,4 @@
-// qmv_burst: the 4-bit affine matvec for up to four decode rows, one HBM round trip per wave.
+// qmv_burst: the 4-bit affine matvec for up to eight decode rows, one HBM round trip per wave.
 //
 // The operation is the one of the W4 layout ("Week 2 Day 6" and the qmv_wide pages): a
 // column's 4-bit codes packed eight per uint32, low nibble first; one bf16 scale and bias per
@@ -17,8 +17,8 @@
 // Per group (lane l: column c = l % 16, reduction values kq*32 .. kq*32 + 31, kq = l / 16 --
 // the B operand of v_mfma_f32_16x16x32_bf16), the codes become exact bf16 integers in the
 // permuted order of codes_bf16_permuted(); the activations (rows 0..M-1 of the A operand,
-// zero beyond) are put in the same order once, into the wave's own LDS slice, and read back as
-// A operands.  P = sum x*q and X = sum x come from the matrix core and y += s*P + b*X, the
+// zero beyond; 4 row slots per chunk up to 4 rows, 8 up to 8) are put in the same order once,
+// into the wave's own LDS slice, and read back as A operands.  P = sum x*q and X = sum x come from the matrix core and y += s*P + b*X, the
 // row-amortized form of the affine dequantization.  The waves' partial sums are added in wave
 // order through LDS, so a result does not depend on timing.  Every load goes through a buffer
 // resource: columns past N and rows past M read zeros.
@@ -40,19 +40,19 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int kBurstRows = 4;        // rows one launch serves (the A operand holds 16; 4 keep LDS small)
-static_assert(kBurstRows == 4, "the activation chunk index below takes the row from its low two bits");
+constexpr int kBurstRows = 4;        // rows the packed form serves (4 K slices of 4 rows fill the A operand)
+constexpr int kBurstMaxRows = 8;     // rows the 16-column form serves (8 row slots from 5 rows)
 
-// LDS of a KW-wave workgroup: each wave's activation slice (GPW groups x 16 chunks of 16
-// bytes per row), then the partial sums of waves 1..KW-1 (4 fp32 per lane, one 16-byte slot).
-constexpr size_t burst_x_bytes(int gpw) { return static_cast<size_t>(gpw) * 16 * kBurstRows * 16; }
-constexpr size_t burst_lds_bytes(int kw, int gpw) {
-    return static_cast<size_t>(kw) * burst_x_bytes(gpw) + static_cast<size_t>(kw - 1) * 4 * 64 * 4;
+// LDS of a KW-wave workgroup of the 16-column form: each wave's activation slice (GPW groups x
+// 16 chunks of 16 bytes x MR row slots), then the partial sums of waves 1..KW-1 (4 fp32 per
+// lane, one 16-byte slot).
+constexpr size_t burst_lds_bytes(int kw, int gpw, int mr) {
+    return static_cast<size_t>(kw) * gpw * 16 * mr * 16 + static_cast<size_t>(kw - 1) * 4 * 64 * 4;
 }
 
 }  // namespace
 
-template <int GPW>
+template <int GPW, int MR>
 __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int N, int K, int KW) {
@@ -81,12 +81,14 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_kernel(
     const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, 0, 0x00020000);
     const uint32_t wvoff = static_cast<uint32_t>(c * row_bytes + kq * 16);
     const uint32_t sbvoff = static_cast<uint32_t>(c * G * 2);
-    u32x4_t* const xs = lds + static_cast<size_t>(wk) * GPW * 16 * kBurstRows;
-    f32x4_t* const red = reinterpret_cast<f32x4_t*>(lds + static_cast<size_t>(KW) * GPW * 16 * kBurstRows);
+    static_assert(MR == 4 || MR == 8, "row slots: a power of two that divides the 64 lanes");
+    u32x4_t* const xs = lds + static_cast<size_t>(wk) * GPW * 16 * MR;
+    f32x4_t* const red = reinterpret_cast<f32x4_t*>(lds + static_cast<size_t>(KW) * GPW * 16 * MR);
 
     // 1. every load of the wave: codes (16 bytes per lane and group), scales, biases, then the
-    //    activation slice: chunk j = ((gl * 4 + t) * 4 + q) * 4 + m holds row m's 8 values
-    //    gl*128 + q*32 + t*8 .. +7 of the wave's group gl (q: the lanes' kq, t: the operand).
+    //    activation slice: chunk j = ((gl * 4 + t) * 4 + q) * MR + m holds row m's 8 values
+    //    gl*128 + q*32 + t*8 .. +7 of the wave's group gl (q: the lanes' kq, t: the operand), MR
+    //    row slots per chunk (4 or 8).
     //    Groups past the wave's share read through the zero-sized resource; every offset is
     //    wave-uniform arithmetic, so no load needs a per-lane resource or offset loop.
     uint32_t w[GPW][4];
@@ -105,12 +107,13 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_kernel(
         sv[i] = __builtin_amdgcn_raw_buffer_load_b16(i < ng ? sr : none, sbvoff, (g0 + i) * 2, 0);
         bv[i] = __builtin_amdgcn_raw_buffer_load_b16(i < ng ? br : none, sbvoff, (g0 + i) * 2, 0);
     }
-    constexpr int XL = GPW * 16 * kBurstRows / 64;
+    constexpr int XL = GPW * 16 * MR / 64;
     u32x4_t xv[XL];
 #pragma unroll
     for (int j0 = 0; j0 < XL; ++j0) {
         const int j = j0 * 64 + lane;
-        const int m = j & 3, q = (j >> 2) & 3, t = (j >> 4) & 3, gl = j >> 6;   // gl = j0
+        const int m = j % MR, r = j / MR;
+        const int q = r & 3, t = (r >> 2) & 3, gl = r >> 4;
         const uint32_t voff = m < M && gl < ng
                                   ? static_cast<uint32_t>(m * K + (g0 + gl) * kGroup + q * 32 + t * 8) * 2u
                                   : 0x80000000u;   // past the end: reads zero
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_kernel(
         f32x4_t xsum = zero4, p = zero4;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const u32x4_t av = arow < M ? xs[((i * 4 + t) * 4 + kq) * kBurstRows + arow] : zu;
+            const u32x4_t av = arow < M ? xs[((i * 4 + t) * 4 + kq) * MR + arow] : zu;
             const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
             xsum = mfma16x16x32(a, ones, xsum);
             p = mfma16x16x32(a, codes_bf16_permuted(w[i][t]), p);
@@ -304,12 +307,29 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_packed_kerne
 
 bool qmv_burst_shape(int M, int N, int K, QmvBurstShape* out) {
     const int G = K / kGroup;
-    if (M < 1 || M > kBurstRows || K % kGroup != 0 || G < 1 || N < 1) return false;
+    if (M < 1 || M > kBurstMaxRows || K % kGroup != 0 || G < 1 || N < 1) return false;
+    const int blocks = (N + 15) / 16;
+    if (M > kBurstRows) {
+        // 5..8 rows: the 16-column form with 8 row slots, below 1024 column blocks and up to 64
+        // groups (16 waves of at most 4; more would pass the LDS).  Measured on MI355X (graph
+        // replay, rotating weights): M = 8 on 9728 x 2560 9.5 us against 10.3 for the
+        // row-amortized loop kernel, 4096 x 2560 5.4 against 5.8, 1024 x 2560 5.1 against 5.5;
+        // M = 5 8.3 / 5.0 / 4.7 against 9.2 / 5.4 / 5.1; two groups per wave measured best.
+        if (blocks >= 1024 || G > 4 * kQmvBurstMaxWaves) return false;
+        int g = 2;
+        const int need = (G + kQmvBurstMaxWaves - 1) / kQmvBurstMaxWaves;
+        if (need > g) g = need;
+        out->packed = 0;
+        out->gpw = g;
+        out->kw = (G + g - 1) / g;
+        out->rows = 2 * kBurstRows;
+        out->cols = 16;
+        return true;
+    }
     // From 2048 column blocks of 16 the persistent wide kernel leads both forms (151936 x 2560:
     // 43 us against 50-55; 32768 and 65536 x 2560: 13.0 and 21.2 against 14.5 and 24.9), and
     // from 1664 blocks under 32 groups where it applies (30000 x 2560: 12.9 against 13.6 us at
     // M = 1, 13.1 against 15.4 at M = 2; 24600 x 2560: 12.9 against 12.0 and 13.2 against 13.3).
-    const int blocks = (N + 15) / 16;
     if (blocks >= 2048 || (blocks >= 1664 && G < 32 && qmv_wide_fits(M, K))) return false;
     // The packed form.  At 1 and 2 rows below 2048 blocks and up to 128 groups (graph-replayed,
     // rotating weights, M = 1, N x K: 9728 x 2560 6.7 us against 7.1-7.6 for the 16-column
@@ -374,15 +394,15 @@ constexpr size_t packed_lds_bytes(int kw, int gpw, int mr) {
 
 }  // namespace
 
-template <int GPW>
+template <int GPW, int MR>
 static hipError_t launch_burst_t(int kw, const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                                  uint16_t* y, int M, int N, int K, hipStream_t stream) {
     static std::atomic<bool> ready[kMaxDevices];
-    auto kern = qmv_burst_kernel<GPW>;
-    const hipError_t e = allow_lds(kern, burst_lds_bytes(kQmvBurstMaxWaves, GPW), ready);
+    auto kern = qmv_burst_kernel<GPW, MR>;
+    const hipError_t e = allow_lds(kern, burst_lds_bytes(kQmvBurstMaxWaves, GPW, MR), ready);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((N + 15) / 16), dim3(64 * kw), burst_lds_bytes(kw, GPW), stream, x, wq, s, b, y, M,
-                       N, K, kw);
+    hipLaunchKernelGGL(kern, dim3((N + 15) / 16), dim3(64 * kw), burst_lds_bytes(kw, GPW, MR), stream, x, wq, s, b, y,
+                       M, N, K, kw);
     return hipGetLastError();
 }
 
@@ -419,11 +439,15 @@ hipError_t launch_qmv_burst(const uint16_t* x, const uint32_t* wq, const uint16_
     }
     // the waves' shares of gpw groups cover every group, within the workgroup bound
     if (kw < 1 || kw > kQmvBurstMaxWaves || static_cast<int64_t>(kw) * sh.gpw < G) return hipErrorInvalidValue;
-    switch (sh.gpw) {
-        case 2: return launch_burst_t<2>(kw, x, wq, scales, biases, y, M, N, K, stream);
-        case 3: return launch_burst_t<3>(kw, x, wq, scales, biases, y, M, N, K, stream);
-        case 4: return launch_burst_t<4>(kw, x, wq, scales, biases, y, M, N, K, stream);
-        case 5: return launch_burst_t<5>(kw, x, wq, scales, biases, y, M, N, K, stream);
+    if (sh.rows < M) return hipErrorInvalidValue;
+    switch (sh.gpw * 100 + sh.rows) {
+        case 204: return launch_burst_t<2, 4>(kw, x, wq, scales, biases, y, M, N, K, stream);
+        case 304: return launch_burst_t<3, 4>(kw, x, wq, scales, biases, y, M, N, K, stream);
+        case 404: return launch_burst_t<4, 4>(kw, x, wq, scales, biases, y, M, N, K, stream);
+        case 504: return launch_burst_t<5, 4>(kw, x, wq, scales, biases, y, M, N, K, stream);
+        case 208: return launch_burst_t<2, 8>(kw, x, wq, scales, biases, y, M, N, K, stream);
+        case 308: return launch_burst_t<3, 8>(kw, x, wq, scales, biases, y, M, N, K, stream);
+        case 408: return launch_burst_t<4, 8>(kw, x, wq, scales, biases, y, M, N, K, stream);
         default: return hipErrorInvalidValue;
     }
 }
