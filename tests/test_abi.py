@@ -281,7 +281,7 @@ def test_gate_up_plan_tiles_and_workspace():
         p = gate_up_plan(M, 9728, 2560)
         assert p["path"] == w4.PATH_GATE_UP and p["tile_m"] == tile_m and p["tile_n"] == 128, M
         assert p["grid_x"] == -(-9728 // 128) and p["grid_y"] == -(-M // tile_m)
-        codes = M > 32 and tile_m == 64
+        codes = M > 32 and tile_m == 64 and p["grid_x"] * p["grid_y"] * p["split_k"] > CUS
         assert (p["variant"] >= 10) == codes
         # the workspace holds the group sums (exact-code form), then gate and up partials
         sums = r256(M * w4.w4a8_xsum_cols(2560) * 2) if codes else 0

@@ -633,7 +633,7 @@ def assert_swiglu_parity(h_bits, x, gate, up, rows=None):
 
 
 @pytest.mark.parametrize("M,N,K,split", [
-    (33, 96, 256, 0),          # ragged M and N, 64-row exact-code tiles
+    (33, 96, 256, 0),          # ragged M and N, 64-row dequantizing tiles (one round)
     (1, 1000, 2560, 0),        # one row: 32-row tiles, policy split
     (20, 1000, 2560, 0),       # skinny rows, ragged N
     (128, 9728, 2560, 0),      # the 128-row gate / up shape (152 tiles: unsplit)
@@ -659,12 +659,14 @@ def test_gate_up_swiglu_prefill512_sampled_rows(lib):
     assert_swiglu_parity(h, x, gate, up, rows=np.arange(0, 512, 37))
 
 
-@pytest.mark.parametrize("M", [3, 40])     # 32-row dequantizing tiles; 64-row exact-code tiles
-def test_gate_up_swiglu_saturation_closed_form(lib, M):
+@pytest.mark.parametrize("M,N", [(3, 96),        # 32-row dequantizing tiles
+                                 (40, 96),       # 64-row dequantizing tiles (one round)
+                                 (640, 5472)])   # 64-row exact-code tiles
+def test_gate_up_swiglu_saturation_closed_form(lib, M, N):
     # all-zero codes and x = 1: g[n] = 128 * sum_g b_gate[n, g], u[n] = 128 * sum_g b_up[n, g].
     # Gate sums of -256, 0 and +256 hit silu's exp overflow (silu -> -0), its zero and its
     # identity tail (silu(256) = 256 in fp32); every product is exact in bf16.
-    N, K = 96, 256
+    K = 256
     G = K // 128
     x = synth.const_bf16(1.0, (M, K))
     bg_vals = np.array([-1.0, 0.0, 1.0])[np.arange(N) % 3]
@@ -678,18 +680,21 @@ def test_gate_up_swiglu_saturation_closed_form(lib, M):
     expect = np.where(g > 0, g * G, 0.0)
     got = synth.from_bf16_bits(h)
     assert np.array_equal(got, np.broadcast_to(expect, (M, N)).astype(got.dtype)), got[0, :6]
-    assert_swiglu_parity(h, x, gate, up)
+    assert_swiglu_parity(h, x, gate, up, rows=np.r_[0:M:max(1, M // 16), M - 1])
 
 
 def test_gate_up_exact_code_and_dequantizing_forms(lib):
-    # above 32 rows the plan runs the exact-code form; a call without workspace (no room for the
-    # activations' group sums) runs the dequantizing tiles instead: both within the tolerance
-    x, gate, up = gate_up_problem(25, 200, 1100, 2560)
-    assert lib.w4a16_gate_up_plan(200, 1100, 2560, split_k=1)["variant"] >= 10
+    # above 32 rows, with more than one 64-row tile per compute unit and no 96-row plan, the plan
+    # runs the exact-code form; a call without workspace (no room for the activations' group
+    # sums) runs the dequantizing tiles instead: both within the tolerance
+    x, gate, up = gate_up_problem(25, 640, 5472, 512)
+    assert lib.w4a16_gate_up_plan(640, 5472, 512, split_k=1)["variant"] >= 10
+    assert lib.w4a16_gate_up_plan(128, 9728, 2560)["variant"] < 10          # one round: dequantizing
     h_codes = run_gate_up(lib, x, gate, up, split_k=1)
     h_deq = run_gate_up(lib, x, gate, up, split_k=1, workspace=None)
-    assert_swiglu_parity(h_codes, x, gate, up)
-    assert_swiglu_parity(h_deq, x, gate, up)
+    rows = np.r_[0:640:7, 639]
+    assert_swiglu_parity(h_codes, x, gate, up, rows=rows)
+    assert_swiglu_parity(h_deq, x, gate, up, rows=rows)
 
 
 def test_gate_up_long_prefill_sampled_rows(lib):

@@ -466,6 +466,13 @@ void plan_gate_up(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus,
     int64_t tile_n = kGateUpVariants[variant].tile_n();
     int64_t tiles = ceil_div(M, kGateUpVariants[variant].bm) * ceil_div(N, tile_n);
     const int64_t S = tile_split(tiles, M, N, K / W4A16_GROUP, split_k, cus, skinny);
+    // A grid of at most one work unit per compute unit does not repay the exact-code form's
+    // pre-pass: the dequantizing 64-row tiles (measured on MI355X at 128 rows, K = 2560, N = 9728,
+    // 152 tiles: 35.3 us against 38.3 us with the group sums).
+    if (codes && tiles * S <= cus) {
+        variant = 1;
+        codes = false;
+    }
     // Unsplit 64-row grids of more than one tile per compute unit: dequantizing 96-row tiles when
     // they need fewer rounds of tiles per compute unit, and at most two (measured on MI355X, K =
     // 2560, N = 9728: 512 rows 73.5-76.4 us against 86-87 us for the 64-row exact-code tiles,
