@@ -445,6 +445,15 @@ def main():
             for row in result["next_rows"]["decode"]:
                 floor = ceilings.get(read_floor_key(row["N"], row["K"]))
                 row["frac_of_measured_read"] = round(floor / row["avg_us"], 4) if floor else None
+        # the metric's qmv part: the decode matvec at M = 1 on the largest decode shape
+        m1 = [r for r in result["next_rows"]["decode"] if r["M"] == 1]
+        if m1:
+            top = max(m1, key=lambda r: (r["N"] * r["K"], r["N"]))
+            result["qmv_decode_M1"] = {
+                "shape": f"{top['K']}->{top['N']}", "GB/s": top["GB/s"], "frac_hbm": top["frac_hbm"],
+                "frac_of_measured_read": top.get("frac_of_measured_read"), "avg_us": top["avg_us"],
+                "all_M1": {f"{r['K']}->{r['N']}": r["GB/s"] for r in m1},
+                "timing": "graph-replayed launches over a weight rotation of more than 512 MB (next_rows.decode)"}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on one step", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(projections)
