@@ -24,6 +24,7 @@ BURST = 4   # the plan's instance index of the burst kernel
 SHAPES = [
     (96, 128),      # one group: a single wave (packed at every M)
     (3, 1280),      # fewer columns than one packed workgroup covers
+    (1, 640),       # a single column
     (33, 640),      # five groups: two packed waves (4 + 1 groups), ragged N
     (160, 2560),    # 20 groups: five packed waves
     (9728, 2560),   # packed at 1-2 rows (2432 workgroups); at 3-4 rows ten waves of two groups

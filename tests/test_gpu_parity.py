@@ -416,11 +416,12 @@ def test_wide_matvec_scales_at_two_byte_offsets(lib):
     assert_parity(bits(lib.linear(x, wq, offset_by_one(s), offset_by_one(b))), p)
 
 
-def test_burst_matvec_scales_at_two_byte_offsets(lib):
+@pytest.mark.parametrize("M", [1, 3, 6])   # packed form; 16-column form with 4 and 8 row slots
+def test_burst_matvec_scales_at_two_byte_offsets(lib, M):
     # the burst kernel loads each scale and bias on its own: offset arrays give the same bits
-    p = synth.random_problem(43, 3, 4000, 2560)
-    assert lib.w4a16_plan(3, 4000, 2560)["variant"] == 4
-    announce("burst qmv scales at 2-byte offsets M=3 N=4000 K=2560")
+    p = synth.random_problem(43, M, 4000, 2560)
+    assert lib.w4a16_plan(M, 4000, 2560)["variant"] == 4
+    announce(f"burst qmv scales at 2-byte offsets M={M} N=4000 K=2560")
     x, wq, s, b = to_device(p)
     y_al = bits(lib.linear(x, wq, s, b))
     assert np.array_equal(y_al, bits(lib.linear(x, wq, offset_by_one(s), offset_by_one(b))))
