@@ -272,9 +272,11 @@ enum w4a16_qmv_mode {
     W4A16_QMV_AMORTIZED = 1,   /* row-amortized: one unpacked group feeds all M rows (matrix core)  */
     W4A16_QMV_PER_ROW = 2,     /* per-row dot products, M <= 2                                      */
     W4A16_QMV_FAMILIES = 3,    /* bits = 4 only: the kernel families and policy of qmv_w4a16        */
-    W4A16_QMV_BURST = 4        /* M <= 4: every wave issues all of its loads at once, 4 K slices in
-                                  the matrix core's spare rows (below 32k columns; beyond 160 blocks
-                                  of 16 columns or 64 groups only up to 2 rows; at most 128 groups) */
+    W4A16_QMV_BURST = 4        /* M <= 8: every wave issues all of its loads at once; up to 4 rows
+                                  4 K slices in the matrix core's spare rows (below 32k columns, at
+                                  most 128 groups; beyond 160 blocks of 16 columns or 64 groups only
+                                  up to 2 rows), else 16-column blocks (3 to 8 rows below 16k
+                                  columns, at most 80 groups up to 4 rows and 64 beyond)          */
 };
 
 /*

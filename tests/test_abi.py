@@ -314,33 +314,41 @@ def test_gate_up_validates_before_launch(lib):
 # ------------------------------------------------------------------------------ width-generic matvec
 
 def test_qmv_affine_plans():
-    # measured routing: qmv_w4a16's policy at 4 bits; at 1, 2, 3 and 8 bits the burst form where
-    # it applies (at most 4 rows, below 2048 column blocks of 16 and 128 groups; beyond 160
-    # blocks or 64 groups only up to 2 rows), the row-amortized kernel elsewhere
+    # measured routing: qmv_w4a16's policy at 4 bits; at 1, 2, 3 and 8 bits the burst forms where
+    # they apply (packed: at most 4 rows, below 2048 column blocks of 16 and 128 groups, beyond
+    # 160 blocks or 64 groups only up to 2 rows; 16 columns: 3 to 8 rows below 1024 blocks, up
+    # to 80 groups at 3-4 rows and 64 at 5-8), the row-amortized kernel elsewhere
     for bits in w4.BITS:
         for M in range(1, 9):
             for N, K in [(4000, 2560), (151936, 2560), (2560, 9728), (1000, 16384), (2000, 8192), (20000, 4096)]:
                 p = w4.qmv_affine_plan(M, N, K, bits, w4.QMV_POLICY, 128, CUS)
                 assert p["path"] == w4.PATH_QMV and p["workspace_bytes"] == 0
                 blocks, G = -(-N // 16), K // 128
-                burst = M <= 4 and blocks < 2048 and G <= 128 and (M <= 2 or (blocks <= 160 and G <= 64))
+                packed = M <= 4 and blocks < 2048 and G <= 128 and (M <= 2 or (blocks <= 160 and G <= 64))
+                wide16 = not packed and 3 <= M <= 8 and blocks < 1024 and G <= (80 if M <= 4 else 64)
+                burst = packed or wide16
                 if bits == 4:
                     q = plan(M, N, K, path=w4.PATH_QMV) if G <= 8192 else None
                     assert p["variant"] == w4.QMV_FAMILIES
                     assert (p["tile_n"], p["grid_x"], p["k_waves"]) == (q["tile_n"], q["grid_x"], q["k_waves"])
-                elif burst:
+                elif packed:
                     steps = 2 if G > 64 or blocks >= 1024 else 1
                     assert p["variant"] == w4.QMV_BURST, (bits, M, N, K)
                     assert (p["tile_n"], p["grid_x"]) == (4, -(-N // 4))
                     assert p["k_waves"] == -(-G // (4 * steps)) and p["block_threads"] == 64 * p["k_waves"]
                     assert p["tile_m"] == (1 if M == 1 else 2 if M == 2 else 4)
+                elif wide16:
+                    per_wave = max(2, -(-G // 16))
+                    assert p["variant"] == w4.QMV_BURST, (bits, M, N, K)
+                    assert (p["tile_n"], p["grid_x"], p["tile_m"]) == (16, -(-N // 16), 4 if M <= 4 else 8)
+                    assert p["k_waves"] == -(-G // per_wave) and p["block_threads"] == 64 * p["k_waves"]
                 else:
                     assert p["variant"] == w4.QMV_AMORTIZED, (bits, M, N, K)
                     assert p["tile_n"] == 16 and p["grid_x"] == -(-N // 16)
         for mode in (w4.QMV_AMORTIZED, w4.QMV_PER_ROW, w4.QMV_BURST):
             assert w4.qmv_affine_plan(2, 4000, 2560, bits, mode, 128, CUS)["variant"] == mode
         # the forced burst form outside its shapes
-        for M, N, K in [(5, 4000, 2560), (1, 32768, 2560), (3, 4000, 2560), (1, 1000, 16512)]:
+        for M, N, K in [(5, 20000, 2560), (1, 32768, 2560), (3, 4000, 10368), (6, 1000, 8320), (1, 1000, 16512)]:
             with pytest.raises(NotImplementedError):
                 w4.qmv_affine_plan(M, N, K, bits, w4.QMV_BURST, 128, CUS)
 
@@ -350,7 +358,7 @@ def test_qmv_affine_plans():
     (9, 16, 256, 4, 0),                                            # more than eight rows
     (3, 16, 256, 4, w4.QMV_PER_ROW),                               # per-row kernel: M <= 2
     (1, 16, 256, 2, w4.QMV_FAMILIES),                              # the 4-bit families: bits = 4
-    (5, 16, 256, 2, w4.QMV_BURST),                                 # burst form: M <= 4
+    (3, 16, 10368, 2, w4.QMV_BURST),                               # burst forms: at most 80 groups at 3 rows
     (1, 16, 256, 4, 5), (1, 16, 256, 4, -1),                       # unknown mode
 ])
 def test_qmv_affine_rejects_unsupported(lib, args):

@@ -25,10 +25,12 @@ MODES = {"policy": 0, "amortized": 1, "per_row": 2, "burst": 4}
 
 
 def burst_applies(M, N, K):
-    """Shapes of the burst form: at most 4 rows, below 2048 column blocks of 16 and 128 groups;
-    beyond 160 blocks or 64 groups only up to 2 rows."""
+    """Shapes of the burst forms: packed at most 4 rows, below 2048 column blocks of 16 and 128
+    groups, beyond 160 blocks or 64 groups only up to 2 rows; 16 columns at 3 to 8 rows below
+    1024 blocks, up to 80 groups at 3-4 rows and 64 at 5-8."""
     blocks, G = -(-N // 16), K // 128
-    return M <= 4 and blocks < 2048 and G <= 128 and (M <= 2 or (blocks <= 160 and G <= 64))
+    packed = M <= 4 and blocks < 2048 and G <= 128 and (M <= 2 or (blocks <= 160 and G <= 64))
+    return packed or (3 <= M <= 8 and blocks < 1024 and G <= (80 if M <= 4 else 64))
 
 
 def run_affine(lib, p, nbits, mode, dev=None):
@@ -57,6 +59,8 @@ AFFINE_CASES = [          # (M, N, K): ragged N; G = 2, 3, 20, 76, 128 groups
     (2, 2560, 9728),         # 76 groups: two burst steps per wave
     (1, 502, 16384),         # 128 groups: the burst form's largest
     (1, 3, 640),             # fewer columns than one burst workgroup
+    (4, 3000, 2560),         # 16-column burst form, 4 row slots
+    (7, 2056, 8192),         # 16-column burst form, 8 row slots, 64 groups
 ]
 
 
@@ -80,7 +84,7 @@ def one_hot_problem(nbits, K=256, N=40, seed=11):
 
 
 @pytest.mark.parametrize("nbits", WIDTHS)
-@pytest.mark.parametrize("mode,rows", [("amortized", 8), ("per_row", 2), ("burst", 4)])
+@pytest.mark.parametrize("mode,rows", [("amortized", 8), ("per_row", 2), ("burst", 4), ("burst", 8)])
 def test_one_hot_rows_return_the_codes(lib, nbits, mode, rows):
     import torch
     q, p = one_hot_problem(nbits)
@@ -94,11 +98,12 @@ def test_one_hot_rows_return_the_codes(lib, nbits, mode, rows):
 
 
 @pytest.mark.parametrize("nbits", WIDTHS)
-@pytest.mark.parametrize("mode,M", [("amortized", 8), ("amortized", 3), ("per_row", 2), ("per_row", 1), ("burst", 1),
-                                    ("burst", 2), ("burst", 4)])
-def test_integer_sums_are_exact(lib, nbits, mode, M):
+@pytest.mark.parametrize("mode,M,N", [("amortized", 8, 1000), ("amortized", 3, 1000), ("per_row", 2, 1000),
+                                      ("per_row", 1, 1000), ("burst", 1, 1000), ("burst", 2, 1000), ("burst", 4, 1000),
+                                      ("burst", 4, 3000), ("burst", 7, 1000)])      # packed; 16 columns at 3000 / 7 rows
+def test_integer_sums_are_exact(lib, nbits, mode, M, N):
     rng = np.random.default_rng(12 + nbits)
-    N, K = 1000, 640
+    K = 640
     q = rng.integers(0, 2 ** nbits, (N, K))
     xi = np.zeros((M, K), dtype=np.int64)
     for m in range(M):
@@ -111,10 +116,11 @@ def test_integer_sums_are_exact(lib, nbits, mode, M):
 
 
 @pytest.mark.parametrize("nbits", WIDTHS)
-@pytest.mark.parametrize("mode,M", [("amortized", 6), ("per_row", 2), ("burst", 3)])
-def test_power_of_two_affine_is_exact(lib, nbits, mode, M):
+@pytest.mark.parametrize("mode,M,N", [("amortized", 6, 520), ("per_row", 2, 520), ("burst", 3, 520),
+                                      ("burst", 3, 4000), ("burst", 6, 520)])
+def test_power_of_two_affine_is_exact(lib, nbits, mode, M, N):
     rng = np.random.default_rng(20 + nbits)
-    N, K = 520, 384
+    K = 384
     half = 2 ** (nbits - 1)
     q = rng.integers(0, 2 ** nbits, (N, K))
     xi = np.zeros((M, K), dtype=np.int64)
@@ -134,7 +140,7 @@ SENTINEL = 0x7FA5     # a NaN pattern the kernels never produce
 
 
 @pytest.mark.parametrize("nbits", WIDTHS)
-@pytest.mark.parametrize("mode,M", [("amortized", 3), ("per_row", 1), ("burst", 1), ("burst", 4)])
+@pytest.mark.parametrize("mode,M", [("amortized", 3), ("per_row", 1), ("burst", 1), ("burst", 4), ("burst", 8)])
 def test_writes_stay_inside_the_output(lib, nbits, mode, M):
     """y is the head of a larger poisoned buffer: the M x N outputs are written, nothing after."""
     import torch

@@ -581,7 +581,9 @@ int plan_qmv_affine(int64_t M, int64_t N, int64_t K, int32_t group, int32_t bits
     // Measured on MI355X (graph replay over rotating weights): the burst form leads the
     // row-amortized kernel at every width where it applies -- at M = 1 by 10-25% on 2560 -> 9728
     // (1, 2, 3, 8 bits: 6.5 / 6.6 / 7.3 / 7.7 us against 7.3 / 7.6 / 8.1 / 10.3), by 35-42% on
-    // 9728 -> 2560 and by 25-40% on 2560 -> 1024; at M = 4 on 2560 -> 1024 by 21-37%.
+    // 9728 -> 2560 and by 25-40% on 2560 -> 1024; at M = 4 on 2560 -> 1024 by 21-37%; the
+    // 16-column form at M = 4 on 2560 -> 9728 and 4096 by 2-15% (8 bits: 9.9 against 11.6 us),
+    // at M = 8 by 0-11% (within 1% at 1 and 2 bits on 4096 columns).
     if (mode == W4A16_QMV_POLICY)
         mode = bits == 4 ? W4A16_QMV_FAMILIES : (burst_fits ? W4A16_QMV_BURST : W4A16_QMV_AMORTIZED);
     if (mode == W4A16_QMV_FAMILIES) {

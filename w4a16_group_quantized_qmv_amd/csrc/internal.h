@@ -156,9 +156,10 @@ hipError_t launch_splitk_reduce_glu(const float* ws, uint16_t* h, int64_t MN, in
 // Width-generic affine matvec (1, 2, 3, 4 or 8 bits per code, M <= 8): row-amortized on the
 // matrix core (mode kQmvBitsMatrix) or per row with dot products (kQmvBitsRows, M <= 2).
 constexpr int kQmvBitsMatrix = 0, kQmvBitsRows = 1;
-// The burst form of the width-generic matvec (packed layout, at most 4 rows): its shape, false
-// where it does not apply (2048 column blocks or more, more than 128 groups, or more than 2
-// rows beyond 160 blocks or 64 groups); and its launch.
+// The burst forms of the width-generic matvec (at most 8 rows; the packed layout up to 4 rows,
+// the 16-column one from 3 rows): its shape, false where neither applies (the 4-bit burst
+// domains: 2048 column blocks or more, more than 128 groups; beyond the packed domain 1024
+// blocks or more, more than 80 groups at 3 and 4 rows or 64 at 5 to 8); and its launch.
 bool qmv_bits_burst_shape(int M, int N, int K, QmvBurstShape* out);
 hipError_t launch_qmv_bits_burst(int bits, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
                                  const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream);

@@ -490,19 +490,160 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_bits_burst_kernel(
     }
 }
 
+// The 16-column burst form at any width (3 to 8 rows, where the packed form's 4-row slots would
+// take too much LDS): the layout of the 4-bit 16-column burst kernel (qmv_burst.hip) -- KW
+// waves on one 16-column block, wave w owning groups w*GPW .. w*GPW + GPW - 1 and issuing every
+// load of them before its first MFMA -- with the codes of any width and the activations staged
+// in natural order, put in the width's code order as they are read back.  MR row slots (4 or 8)
+// per activation chunk; wave 0 adds the waves' sums in wave order.
+template <int BITS, int GPW, int MR>
+__global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_bits_burst16_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ wq, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ biases, uint16_t* __restrict__ y, int M, int N, int K, int KW) {
+    static_assert(MR == 4 || MR == 8, "row slots: a power of two that divides the 64 lanes");
+    extern __shared__ __attribute__((aligned(16))) u32x4_t lds[];
+    const int G = K >> 7;
+    const int lane = threadIdx.x & 63;
+    const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col0 = blockIdx.x * 16;
+    const int g0 = wk * GPW;
+    const int ng = min(GPW, G - g0);
+    const int c = lane & 15, kq = lane >> 4;
+    const int row_bytes = K / 8 * BITS;
+    auto clamp_records = [](int64_t bytes) { return static_cast<int>(bytes > 0x7FFFFFFFll ? 0x7FFFFFFFll : bytes); };
+    const int64_t cols = static_cast<int64_t>(N - col0);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(wq) + static_cast<size_t>(col0) * row_bytes), 0,
+        clamp_records(cols * row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(scales + static_cast<size_t>(col0) * G), 0, clamp_records(cols * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(biases + static_cast<size_t>(col0) * G), 0, clamp_records(cols * G * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x), 0, clamp_records(static_cast<int64_t>(M) * K * 2), 0x00020000);
+    // a zero-sized resource: loads of groups the wave does not own return zeros
+    const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, 0, 0x00020000);
+    const uint32_t wvoff = static_cast<uint32_t>(c * row_bytes + kq * 4 * BITS);
+    const uint32_t sbvoff = static_cast<uint32_t>(c * G * 2);
+    u32x4_t* const xs = lds + static_cast<size_t>(wk) * GPW * 16 * MR;
+    f32x4_t* const red = reinterpret_cast<f32x4_t*>(lds + static_cast<size_t>(KW) * GPW * 16 * MR);
+
+    // 1. every load of the wave; slots past its share read through the zero-sized resource and
+    //    add exactly +0 below, which keeps every load unconditional
+    uint32_t w[GPW][BITS];
+    uint16_t sv[GPW], bv[GPW];
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) load_codes<BITS>(i < ng ? wr : none, wvoff, static_cast<uint32_t>((g0 + i) * 16 * BITS), w[i]);
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        sv[i] = __builtin_amdgcn_raw_buffer_load_b16(i < ng ? sr : none, sbvoff, (g0 + i) * 2, 0);
+        bv[i] = __builtin_amdgcn_raw_buffer_load_b16(i < ng ? br : none, sbvoff, (g0 + i) * 2, 0);
+    }
+    // activation chunk j = ((gl * 4 + t) * 4 + q) * MR + m: row m's values gl*128 + q*32 + t*8 .. +7
+    constexpr int XL = GPW * 16 * MR / 64;
+    u32x4_t xv[XL];
+#pragma unroll
+    for (int j0 = 0; j0 < XL; ++j0) {
+        const int j = j0 * 64 + lane;
+        const int m = j % MR, r = j / MR;
+        const int q = r & 3, t = (r >> 2) & 3, gl = r >> 4;
+        const uint32_t voff = m < M && gl < ng
+                                  ? static_cast<uint32_t>(m * K + (g0 + gl) * kGroup + q * 32 + t * 8) * 2u
+                                  : 0x80000000u;
+        xv[j0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, voff, 0, 0));
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all loads issued before anything waits on one
+#pragma unroll
+    for (int j0 = 0; j0 < XL; ++j0) xs[j0 * 64 + lane] = xv[j0];
+    asm volatile("" ::: "memory");   // the wave's own slice: only the compiler must keep the order
+
+    // 2. every group: rows 4*kq + r of column c
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    const u32x4_t zu = {0u, 0u, 0u, 0u};
+    const bf16x8_t ones = {__bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f),
+                           __bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f)};
+    const int arow = lane & 15;
+    f32x4_t yacc = zero4;
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+        u32x4_t xn[4], aop[4], bop[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) xn[t] = arow < M ? xs[((i * 4 + t) * 4 + kq) * MR + arow] : zu;
+        acts_in_code_order<BITS>(xn, aop);
+        codes_to_bf16<BITS>(w[i], bop);
+        f32x4_t xsum = zero4, p = zero4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, aop[t]);
+            xsum = mfma16x16x32(a, ones, xsum);
+            p = mfma16x16x32(a, __builtin_bit_cast(bf16x8_t, bop[t]), p);
+        }
+        const float s = bf16_bits_to_f32(sv[i]), b = bf16_bits_to_f32(bv[i]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yacc[r] = __builtin_fmaf(s, p[r], __builtin_fmaf(b, xsum[r], yacc[r]));
+    }
+
+    // 3. waves 1..KW-1 hand their sums to wave 0 (one 16-byte slot per lane), which adds them in
+    //    wave order, four waves' slots read before they are added
+    if (KW > 1) {
+        if (wk > 0) red[(wk - 1) * 64 + lane] = yacc;
+        __syncthreads();
+        if (wk == 0) {
+            int j = 0;
+            for (; j + 4 <= KW - 1; j += 4) {
+                f32x4_t v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) v[u] = red[(j + u) * 64 + lane];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) yacc[r] += v[u][r];
+            }
+            for (; j < KW - 1; ++j) {
+                const f32x4_t v = red[j * 64 + lane];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yacc[r] += v[r];
+            }
+        }
+    }
+    if (wk == 0) {
+        const int col = col0 + c;
+        if (col < N) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * kq + r;
+                if (m < M) y[static_cast<size_t>(m) * N + col] = f32_to_bf16_bits(yacc[r]);
+            }
+        }
+    }
+}
+
 bool qmv_bits_burst_shape(int M, int N, int K, QmvBurstShape* out) {
     const int G = K / kGroup;
-    if (M < 1 || M > 4 || K % kGroup != 0 || G < 1 || N < 1) return false;
-    // The 4-bit packed form's domain (below 2048 column blocks of 16 and up to 128 groups; at 3
-    // and 4 rows up to 160 blocks and 64 groups) and its steps: one per wave below 1024 blocks
-    // up to 64 groups, two otherwise.
+    if (M < 1 || M > 8 || K % kGroup != 0 || G < 1 || N < 1) return false;
+    // The 4-bit burst forms' domains.  Packed: below 2048 column blocks of 16 and up to 128
+    // groups, at 3 and 4 rows up to 160 blocks and 64 groups; one step per wave below 1024
+    // blocks up to 64 groups, two otherwise.  16 columns: the rest below 1024 blocks, up to 80
+    // groups at 3 and 4 rows (4 row slots) and 64 at 5 to 8 rows (8 slots), two groups per wave
+    // or as few as 16 waves allow.
     const int blocks = (N + 15) / 16;
-    if (blocks >= 2048 || G > 8 * kQmvBurstMaxWaves || (M > 2 && (blocks > 160 || G > 64))) return false;
-    out->packed = 1;
-    out->gpw = blocks >= 1024 || G > 4 * kQmvBurstMaxWaves ? 2 : 1;
-    out->kw = (G + 4 * out->gpw - 1) / (4 * out->gpw);
-    out->rows = M == 1 ? 1 : (M == 2 ? 2 : 4);
-    out->cols = 4;
+    if (M <= 4 && blocks < 2048 && G <= 8 * kQmvBurstMaxWaves && (M <= 2 || (blocks <= 160 && G <= 64))) {
+        out->packed = 1;
+        out->gpw = blocks >= 1024 || G > 4 * kQmvBurstMaxWaves ? 2 : 1;
+        out->kw = (G + 4 * out->gpw - 1) / (4 * out->gpw);
+        out->rows = M == 1 ? 1 : (M == 2 ? 2 : 4);
+        out->cols = 4;
+        return true;
+    }
+    if (M <= 2 || blocks >= 1024 || G > (M <= 4 ? kQmvBurstMaxGroups : 4) * kQmvBurstMaxWaves) return false;
+    int g = 2;
+    const int need = (G + kQmvBurstMaxWaves - 1) / kQmvBurstMaxWaves;
+    if (need > g) g = need;
+    out->packed = 0;
+    out->gpw = g;
+    out->kw = (G + g - 1) / g;
+    out->rows = M <= 4 ? 4 : 8;
+    out->cols = 16;
     return true;
 }
 
@@ -534,9 +675,45 @@ hipError_t launch_bits_burst_t(int kw, const uint16_t* x, const uint32_t* wq, co
     return hipGetLastError();
 }
 
+constexpr size_t bits_burst16_lds_bytes(int kw, int gpw, int mr) {
+    return static_cast<size_t>(kw) * gpw * 16 * mr * 16 + static_cast<size_t>(kw - 1) * 64 * 16;
+}
+
+template <int BITS, int GPW, int MR>
+hipError_t launch_bits_burst16_t(int kw, const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
+                                 uint16_t* y, int M, int N, int K, hipStream_t stream) {
+    static std::atomic<bool> ready[kMaxDevices];   // per instance and device: the LDS permission is set
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    auto kern = qmv_bits_burst16_kernel<BITS, GPW, MR>;
+    if (!ready[dev].load(std::memory_order_acquire)) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(bits_burst16_lds_bytes(kQmvBurstMaxWaves, GPW, MR)));
+        if (e != hipSuccess) return e;
+        ready[dev].store(true, std::memory_order_release);
+    }
+    hipLaunchKernelGGL(kern, dim3((N + 15) / 16), dim3(64 * kw), bits_burst16_lds_bytes(kw, GPW, MR), stream, x, wq,
+                       s, b, y, M, N, K, kw);
+    return hipGetLastError();
+}
+
 template <int BITS>
 hipError_t launch_bits_burst_w(const QmvBurstShape& sh, const uint16_t* x, const uint32_t* wq, const uint16_t* s,
                                const uint16_t* b, uint16_t* y, int M, int N, int K, hipStream_t stream) {
+    if (!sh.packed) {
+        switch (sh.gpw * 100 + sh.rows) {
+            case 204: return launch_bits_burst16_t<BITS, 2, 4>(sh.kw, x, wq, s, b, y, M, N, K, stream);
+            case 304: return launch_bits_burst16_t<BITS, 3, 4>(sh.kw, x, wq, s, b, y, M, N, K, stream);
+            case 404: return launch_bits_burst16_t<BITS, 4, 4>(sh.kw, x, wq, s, b, y, M, N, K, stream);
+            case 504: return launch_bits_burst16_t<BITS, 5, 4>(sh.kw, x, wq, s, b, y, M, N, K, stream);
+            case 208: return launch_bits_burst16_t<BITS, 2, 8>(sh.kw, x, wq, s, b, y, M, N, K, stream);
+            case 308: return launch_bits_burst16_t<BITS, 3, 8>(sh.kw, x, wq, s, b, y, M, N, K, stream);
+            case 408: return launch_bits_burst16_t<BITS, 4, 8>(sh.kw, x, wq, s, b, y, M, N, K, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (sh.gpw * 10 + sh.rows) {
         case 11: return launch_bits_burst_t<BITS, 1, 1>(sh.kw, x, wq, s, b, y, M, N, K, stream);
         case 12: return launch_bits_burst_t<BITS, 1, 2>(sh.kw, x, wq, s, b, y, M, N, K, stream);
@@ -553,9 +730,10 @@ hipError_t launch_qmv_bits_burst(int bits, const uint16_t* x, const uint32_t* wq
                                  const uint16_t* biases, uint16_t* y, int M, int N, int K, hipStream_t stream) {
     QmvBurstShape sh;
     if (!qmv_bits_burst_shape(M, N, K, &sh)) return hipErrorInvalidValue;
-    // the waves' shares of 4 gpw groups cover every group; the row slots cover M
-    if (sh.kw < 1 || sh.kw > kQmvBurstMaxWaves || static_cast<int64_t>(sh.kw) * 4 * sh.gpw < K / kGroup ||
-        sh.rows < M)
+    // the waves' shares (4 gpw groups packed, gpw groups otherwise) cover every group; the row
+    // slots cover M
+    const int64_t per_wave = sh.packed ? 4 * sh.gpw : sh.gpw;
+    if (sh.kw < 1 || sh.kw > kQmvBurstMaxWaves || static_cast<int64_t>(sh.kw) * per_wave < K / kGroup || sh.rows < M)
         return hipErrorInvalidValue;
     switch (bits) {
         case 1: return launch_bits_burst_w<1>(sh, x, wq, scales, biases, y, M, N, K, stream);
