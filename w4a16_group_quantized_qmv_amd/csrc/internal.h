@@ -6,6 +6,14 @@
 
 namespace w4a16 {
 
+// Cache policy of the weight loads of the persistent wide matvec, the 16-column K-split matvec
+// and the packed burst forms: non-temporal (the codes of a decode matvec are read once per
+// call; measured on MI355X: the 151936-column head 41.5 against 44.3 us alone and 40.6 against
+// 49.3 us inside the 512-row step, the 13 MB packed-burst shapes 3% faster; the K-split
+// matvec within 1%).  The 16-column burst forms measured 1-5% slower with it and the tile
+// kernels, whose M-tiles re-read the same codes from L2, keep the default policy.
+constexpr int kStreamedOnce = 2;
+
 // qmv: one workgroup covers wn * cb * 16 output columns; kw of its waves split the K groups
 // of those columns and are summed in wave order through LDS.
 struct QmvShape {

@@ -95,8 +95,8 @@ __global__ __launch_bounds__(64 * WN * KW) void qmv_kernel(
         for (int cb = 0; cb < CB; ++cb) {
             uint8_t* dst = (buf ? &wbuf1[wave][0] : &wbuf0[wave][0]) + cb * kPairBytes;
             const uint32_t step = static_cast<uint32_t>(pair) * 128u + static_cast<uint32_t>(cb * 16 * row_bytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst, 16, voff_lo + step, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst + 1024, 16, voff_hi + step, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst, 16, voff_lo + step, 0, 0, kStreamedOnce);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst + 1024, 16, voff_hi + step, 0, 0, kStreamedOnce);
         }
     };
     const int rd0 = pair_slot(c, 0, kq), rd1 = pair_slot(c, 1, kq);
@@ -346,8 +346,10 @@ __global__ __launch_bounds__(64 * W) void qmv_wide_kernel(
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             const uint32_t step = static_cast<uint32_t>(ip) * 128u + static_cast<uint32_t>(cb * 16 * row_bytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst + cb * kPairBytes, 16, voff_lo + step, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst + cb * kPairBytes + 1024, 16, voff_hi + step, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst + cb * kPairBytes, 16, voff_lo + step, 0, 0,
+                                                     kStreamedOnce);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst + cb * kPairBytes + 1024, 16, voff_hi + step, 0, 0,
+                                                     kStreamedOnce);
         }
         const uint32_t sbo = sb_voff + static_cast<uint32_t>(ip) * 4u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(srsrc, dst + kSbOff, 4, sbo, 0, 0, 0);

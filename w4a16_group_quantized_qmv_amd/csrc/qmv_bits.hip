@@ -168,24 +168,25 @@ __device__ __forceinline__ void acts_in_code_order(const u32x4_t (&xv)[4], u32x4
     }
 }
 
-template <int BITS>
+// AUX: the loads' cache policy (kStreamedOnce where the kernel measured faster with it).
+template <int BITS, int AUX = 0>
 __device__ __forceinline__ void load_codes(const __amdgpu_buffer_rsrc_t& r, uint32_t voff, uint32_t soff,
                                            uint32_t (&w)[BITS]) {
     if constexpr (BITS == 1) {
-        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX);
     } else if constexpr (BITS == 2) {
-        const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+        const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX));
         w[0] = v[0];
         w[1] = v[1];
     } else if constexpr (BITS == 3) {
-        const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+        const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, AUX);
         w[0] = v[0];
         w[1] = v[1];
         w[2] = v[2];
     } else {
 #pragma unroll
         for (int h = 0; h < BITS / 4; ++h) {
-            const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16 * h, 0));
+            const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + 16 * h, AUX));
 #pragma unroll
             for (int i = 0; i < 4; ++i) w[4 * h + i] = v[i];
         }
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_bits_burst_kernel(
         const int g = g0 + 4 * i + sl;
         const uint32_t voff =
             g < G ? static_cast<uint32_t>(j * row_bytes + g * 16 * BITS + kq * 4 * BITS) : 0x80000000u;
-        load_codes<BITS>(wr, voff, 0, w[i]);
+        load_codes<BITS, kStreamedOnce>(wr, voff, 0, w[i]);
     }
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {

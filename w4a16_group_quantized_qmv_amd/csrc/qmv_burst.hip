@@ -226,7 +226,8 @@ __global__ __launch_bounds__(64 * kQmvBurstMaxWaves) void qmv_burst_packed_kerne
     for (int i = 0; i < GPW; ++i) {
         const int g = g0 + 4 * i + sl;
         const uint32_t voff = g < G ? static_cast<uint32_t>(j * row_bytes + g * 64 + kq * 16) : 0x80000000u;
-        const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, 0, 0));
+        const u32x4_t v =
+            __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, voff, 0, kStreamedOnce));
         w[i][0] = v[0];
         w[i][1] = v[1];
         w[i][2] = v[2];
