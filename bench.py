@@ -20,7 +20,8 @@ device copies so that weight reads miss the 256 MB last-level cache.  Output: on
     python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--no-cpu-baseline] [--no-next-rows]
 
 Besides the step's throughput the line carries: the dominant kernel's roofline (the fused
-gate / up pair; HIP events around each of its launches in the timed region), the same run's measured ceilings (torch's
+gate / up pair's tile kernel, from its own start and end timestamps in every timed step), the
+same run's measured ceilings (torch's
 bf16 GEMM through hipBLASLt on the same shapes, and device copy / read rates), every timed
 shape's fraction of the roof that binds it (min(MFMA peak, arithmetic intensity x HBM
 bandwidth)), and the CPU oracle on a bounded sample of the step.
@@ -328,15 +329,18 @@ def main():
     dom_idx = [unit_names.index(DOMINANT)]
     assert dom_idx == list(range(dom_idx[0], dom_idx[0] + len(dom_idx))), "dominant projections must be adjacent"
 
-    def step(i, starts=None, ends=None):
-        """One pass over the step's launch units (q|k|v grouped, o, gate, up, down, vocab).  ``starts`` / ``ends`` map a call's index to a HIP
-        event recorded just before / after it: every call in the breakdown pass; in the timed pass
-        one event before the gate launch and one after the up launch that follows it, so that no
-        event sits between the two dominant launches."""
+    def step(i, starts=None, ends=None, kernel_events=None):
+        """One pass over the step's launch units (q|k|v grouped, o, gate|up, down, vocab).  ``starts`` /
+        ``ends`` map a call's index to a HIP event recorded on the stream just before / after it:
+        every call in the breakdown pass, the fused gate|up call in the timed pass.
+        ``kernel_events`` maps a call's index to an event pair that its tile kernel's own start and
+        end timestamps go to (w4a16_time_next_launch)."""
         row = calls[i % args.copies]
         for j, call in enumerate(row):
             if starts is not None and j in starts:
                 starts[j].record()
+            if kernel_events is not None and j in kernel_events:
+                w4.w4a16_time_next_launch(*kernel_events[j])
             call()
             if ends is not None and j in ends:
                 ends[j].record()
@@ -356,22 +360,30 @@ def main():
     def event_pair():
         return [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
 
-    # timed region: the steps back to back on one stream, events around each gate and up launch
+    # timed region: the steps back to back on one stream; in every step the fused gate|up call is
+    # bracketed by two events on the stream, and its tile kernel puts its own start and end
+    # timestamps on two more (the HIP handles exist once each event has been recorded)
     n = len(units)
     dom_ev = [event_pair() for _ in range(args.steps)]
+    dom_kev = [event_pair() for _ in range(args.steps)]
+    for e in dom_kev:
+        e[0].record()
+        e[1].record()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        step(i, {dom_idx[0]: dom_ev[i][0]}, {dom_idx[-1]: dom_ev[i][1]})
+        step(i, {dom_idx[0]: dom_ev[i][0]}, {dom_idx[-1]: dom_ev[i][1]}, {dom_idx[0]: dom_kev[i]})
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(end)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
-    dom_launch_us = [e[0].elapsed_time(e[1]) * 1e3 / len(dom_idx) for e in dom_ev]
-    dom_us = sum(dom_launch_us) / len(dom_launch_us)
+    dom_bracket_us = [e[0].elapsed_time(e[1]) * 1e3 for e in dom_ev]
+    dom_kernel_us = [e[0].elapsed_time(e[1]) * 1e3 for e in dom_kev]
+    dom_us = sum(dom_kernel_us) / len(dom_kernel_us)
+    dom_bracket = sum(dom_bracket_us) / len(dom_bracket_us)
 
     # breakdown pass (not timed as a whole): events around every call
     bsteps = max(3, min(args.steps, 10))
@@ -418,13 +430,16 @@ def main():
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": dom_flops, "avg_launch_us": round(dom_us, 3),
-                     "launches": len(dom_launch_us) * len(dom_idx),
+                     "launches": len(dom_kernel_us),
+                     "avg_call_bracket_us": round(dom_bracket, 3),
                      "frac_of_measured_bf16_gemm": (round(achieved / ceilings["bf16_gemm_M512_TFLOP/s"], 4)
                                                     if ceilings else None),
                      "the_measured_bf16_gemm": "torch.nn.functional.linear on one of the pair's projections (same "
                                                "per-projection shape)",
-                     "timing": "HIP events on the launch stream just before and after each timed step's fused "
-                               "gate/up launch, mean over the timed steps"},
+                     "timing": "the tile kernel's own start and end timestamps (hipExtLaunchKernel events, armed "
+                               "by w4a16_time_next_launch) in every timed step, mean over the timed steps; "
+                               "avg_call_bracket_us: events recorded on the stream just before and after the "
+                               "same calls, which also span the dispatch and the end-of-kernel cache flush"},
         "measured_ceiling": ceilings,
         "breakdown_timing": "separate pass after the timed region: HIP events around every call",
         "qmv_vocab_last_row": {"GB/s": round(vocab_bytes / vocab["avg_us"] / 1e3, 1),

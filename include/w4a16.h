@@ -111,6 +111,21 @@ int w4a16_abi_version(void);
 const char* w4a16_status_string(int status);
 
 /*
+ * Kernel timestamps for measurement (the per-launch device time that the roofline fraction of a
+ * projection is computed from).  Arms a request on the calling host thread: the next
+ * contraction kernel that this thread launches through any entry point below (a tile or matvec
+ * kernel; not the group-sum pre-pass of the exact-code form nor a split-K slice sum) is launched
+ * with hipExtLaunchKernel, which sets start_event / stop_event to that kernel's execution start
+ * and end (so hipEventElapsedTime over them gives the kernel's own duration, without the launch
+ * overhead and the end-of-kernel system-scope cache flush that events recorded on the stream
+ * around the call also span).  The launch consumes the request; an entry point that returns an
+ * error before launching leaves it armed.  start_event and stop_event are hipEvent_t handles
+ * created by the caller (either may be null); passing two nulls cancels the request.  Calls
+ * captured into a HIP graph must not be timed this way.  Returns W4A16_OK.
+ */
+int w4a16_time_next_launch(void* start_event, void* stop_event);
+
+/*
  * Dispatch policy ("Week 2 Day 6", Task 1 for the M threshold; Task 5 and "Benchmark Analysis:
  * Identify Under-Filled Prefill Shapes" for splitting K only when the tile grid under-fills the
  * GPU).  path: W4A16_PATH_AUTO / _QMV / _QMM / _SKINNY.  split_k: 0 = policy, 1 = never split, S > 1 =

@@ -108,6 +108,24 @@ def test_small_integer_sums_are_exact(lib, path, N, K):
     assert np.array_equal(y, synth.to_bf16_bits((xi @ q.T).astype(np.float32)))
 
 
+@pytest.mark.parametrize("M,N,split", [(35, 203, 2), (35, 203, 3), (40, 256, 2), (40, 256, 5), (33, 97, 4)])
+def test_split_slice_sums_are_exact_in_both_forms(lib, M, N, split):
+    # integer sums: every split gives the exact result, with M x N odd or even, ragged N and
+    # slices of one to four groups
+    rng = np.random.default_rng(14)
+    K = 1024
+    q = rng.integers(0, 16, (N, K))
+    xi = np.zeros((M, K), dtype=np.int64)
+    for m in range(M):                 # at most 17 ones per row keeps every sum <= 255
+        xi[m, rng.choice(K, size=rng.integers(0, 18), replace=False)] = 1
+    G = K // 128
+    p = {"x": synth.to_bf16_bits(xi.astype(np.float32)), "wq": synth.pack_codes(q),
+         "scales": synth.const_bf16(1.0, (N, G)), "biases": synth.const_bf16(0.0, (N, G)), "M": M, "N": N, "K": K}
+    assert lib.w4a16_plan(M, N, K, 128, lib.PATH_QMM, split)["split_k"] == split
+    y = run(lib, p, "qmm", split)
+    assert np.array_equal(y, synth.to_bf16_bits((xi @ q.T).astype(np.float32)))
+
+
 @pytest.mark.parametrize("path,N", [("qmv", 48), ("qmv", 24600), ("qmm", 48)])
 def test_power_of_two_affine_is_exact(lib, path, N):
     rng = np.random.default_rng(9)
@@ -642,6 +660,7 @@ def assert_swiglu_parity(h_bits, x, gate, up, rows=None):
     (128, 2000, 1024, 1),      # forced: unsplit
     (70, 1100, 1024, 2),       # forced: two slices
     (70, 1100, 1024, 5),       # forced: five slices of 1 or 2 groups
+    (35, 203, 1024, 3),        # forced: three slices, M x N odd
     (1500, 512, 384, 0),       # beyond 1024 rows, odd group count
     (250, 9728, 384, 0),       # 96-row dequantizing tiles (one round against two): ragged rows
     (90, 40000, 256, 0),       # 96-row tiles, ragged columns (40000 = 312 x 128 + 64)

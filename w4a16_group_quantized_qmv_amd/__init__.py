@@ -121,6 +121,8 @@ def load():
     lib.w4a16_linear_grouped.restype = ctypes.c_int
     lib.w4a16_linear_grouped.argtypes = [u16p, i32, pp, pp, pp, pp, ctypes.POINTER(i64), i64, i64, i32, vp,
                                          ctypes.c_size_t, vp]
+    lib.w4a16_time_next_launch.restype = ctypes.c_int
+    lib.w4a16_time_next_launch.argtypes = [vp, vp]
     _LIB = lib
     return lib
 
@@ -141,6 +143,23 @@ def w4a16_abi_version() -> int:
 
 def w4a16_status_string(status: int) -> str:
     return load().w4a16_status_string(status).decode()
+
+
+def _event_handle(event) -> int | None:
+    """The hipEvent_t of a torch.cuda.Event (created by its first record()), an int handle, or None."""
+    if event is None or isinstance(event, int):
+        return event or None
+    handle = int(event.cuda_event)
+    if handle == 0:
+        raise ValueError("the event has no HIP event yet: record() it once before passing it")
+    return handle
+
+
+def w4a16_time_next_launch(start_event=None, stop_event=None):
+    """Arm the calling thread's kernel-timestamp request: the next contraction kernel launched
+    through the library records its own execution start and end on the two events."""
+    _raise_for(load().w4a16_time_next_launch(_event_handle(start_event), _event_handle(stop_event)),
+               "w4a16_time_next_launch")
 
 
 def _raise_for(status: int, what: str):

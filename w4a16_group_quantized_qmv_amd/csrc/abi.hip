@@ -812,9 +812,24 @@ int run_linear_noalloc(const uint16_t* x, const uint32_t* wq, const uint16_t* s,
 
 }  // namespace
 
+namespace w4a16 {
+
+LaunchTiming& launch_timing() {
+    thread_local LaunchTiming t;
+    return t;
+}
+
+}  // namespace w4a16
+
 extern "C" {
 
 int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+int w4a16_time_next_launch(void* start_event, void* stop_event) {
+    w4a16::launch_timing() = w4a16::LaunchTiming{static_cast<hipEvent_t>(start_event),
+                                                  static_cast<hipEvent_t>(stop_event)};
+    return W4A16_OK;
+}
 
 const char* w4a16_status_string(int status) {
     switch (status) {

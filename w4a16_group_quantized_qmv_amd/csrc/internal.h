@@ -1,10 +1,42 @@
 // Host-side launchers shared between the C-ABI layer and the kernel translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace w4a16 {
+
+// Kernel-timestamp request (w4a16_time_next_launch), one per host thread: while armed, the next
+// contraction kernel this thread launches (a tile or matvec kernel; not a group-sum pre-pass or
+// a split-K slice sum) is launched through hipExtLaunchKernel with these events, which then hold
+// the kernel's execution start and end, and the request is cleared.
+struct LaunchTiming {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchTiming& launch_timing();
+
+// hipExtLaunchKernel packs the arguments by the types it is given, so each one is first
+// converted to the kernel's own parameter type.
+template <typename... P, typename... A>
+inline void launch_timed(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t lds, hipStream_t stream,
+                         A... args) {
+    const LaunchTiming t = launch_timing();
+    launch_timing() = LaunchTiming{};
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, t.start, t.stop, 0u, static_cast<P>(args)...);
+}
+
+// Every contraction kernel launch goes through this: a plain launch unless a timing request is
+// armed on the calling thread.
+#define W4A16_LAUNCH(kernel, grid, block, lds, stream, ...)                                            \
+    do {                                                                                               \
+        const ::w4a16::LaunchTiming& w4a16_lt_ = ::w4a16::launch_timing();                             \
+        if (w4a16_lt_.start != nullptr || w4a16_lt_.stop != nullptr)                                   \
+            ::w4a16::launch_timed(kernel, dim3(grid), dim3(block), static_cast<uint32_t>(lds), stream, \
+                                  __VA_ARGS__);                                                        \
+        else                                                                                           \
+            hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                          \
+    } while (0)
 
 // Cache policy of the weight loads of the persistent wide matvec, the 16-column K-split matvec
 // and the packed burst forms: non-temporal (the codes of a decode matvec are read once per

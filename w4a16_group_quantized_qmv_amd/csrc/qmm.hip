@@ -737,13 +737,13 @@ static hipError_t launch_qmm_t(const uint16_t* x, const uint16_t* xsum, int KB, 
     do {                                                                                                          \
         if constexpr (GROUPED_FORM) {                                                                             \
             if (grp) {                                                                                            \
-                hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WPS, STAGES, 1, CODES, SBQ, KS, true>), grid,         \
+                W4A16_LAUNCH((qmm_kernel<BM, NB, NW, WPS, STAGES, 1, CODES, SBQ, KS, true>), grid,               \
                                    dim3(64 * NW), 0, stream, x, wq, s, b, nullptr, nullptr, nullptr, y, ws, M, N, K, \
                                    split, tiles_m, tiles_n, XS, KB, g);                                           \
                 break;                                                                                            \
             }                                                                                                     \
         }                                                                                                         \
-        hipLaunchKernelGGL((qmm_kernel<BM, NB, NW, WPS, STAGES, 1, CODES, SBQ, KS>), grid, dim3(64 * NW), 0,       \
+        W4A16_LAUNCH((qmm_kernel<BM, NB, NW, WPS, STAGES, 1, CODES, SBQ, KS>), grid, dim3(64 * NW), 0,             \
                            stream, x, wq, s, b, nullptr, nullptr, nullptr, y, ws, M, N, K, split, tiles_m, tiles_n,  \
                            XS, KB, g);                                                                            \
     } while (0)
@@ -781,7 +781,7 @@ static hipError_t launch_gate_up_t(const uint16_t* x, const uint16_t* xsum, int 
     const dim3 grid(tiles_m * tiles_n * split);
     const bool quad = STAGES == 2 && quad_scales(K, split, sg, bg) && quad_scales(K, split, su, bu);
 #define W4A16_LAUNCH_GU(WPS, CODES, SBQ, XS)                                                                       \
-    hipLaunchKernelGGL((qmm_kernel<BM, 1, 4, WPS, STAGES, 2, CODES, SBQ>), grid, dim3(256), 0, stream, x, wg, sg, bg, \
+    W4A16_LAUNCH((qmm_kernel<BM, 1, 4, WPS, STAGES, 2, CODES, SBQ>), grid, dim3(256), 0, stream, x, wg, sg, bg,       \
                        wu, su, bu, h, ws, M, N, K, split, tiles_m, tiles_n, XS, KB, QmmGroups{})
     if constexpr (CM > 0) {
         if (xsum) {

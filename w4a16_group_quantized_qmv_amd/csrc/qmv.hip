@@ -517,7 +517,7 @@ static hipError_t launch_qmv_t(const uint16_t* x, const uint32_t* wq, const uint
                                uint16_t* y, int M, int N, int K, hipStream_t stream) {
     const int cols_per_block = CB * WN * 16;
     const dim3 grid((N + cols_per_block - 1) / cols_per_block);
-    hipLaunchKernelGGL((qmv_kernel<CB, WN, KW>), grid, dim3(64 * WN * KW), 0, stream, x, wq, s, b, y, M, N, K);
+    W4A16_LAUNCH((qmv_kernel<CB, WN, KW>), grid, dim3(64 * WN * KW), 0, stream, x, wq, s, b, y, M, N, K);
     return hipGetLastError();
 }
 
@@ -568,7 +568,7 @@ static hipError_t launch_qmv_wide_t(const uint16_t* x, const uint32_t* wq, const
                               std::memory_order_relaxed);
     }
     const int wgs = std::min(per_cu * cus, (blocks + W - 1) / W);
-    hipLaunchKernelGGL(kern, dim3(wgs), dim3(64 * W), xbytes, stream, x, wq, s, b, y, M, N, K);
+    W4A16_LAUNCH(kern, dim3(wgs), dim3(64 * W), xbytes, stream, x, wq, s, b, y, M, N, K);
     return hipGetLastError();
 }
 

@@ -360,7 +360,7 @@ template <int BITS, int KW, int MODE>
 static hipError_t launch_qmv_bits_t(const uint16_t* x, const uint32_t* wq, const uint16_t* s, const uint16_t* b,
                                     uint16_t* y, int M, int N, int K, hipStream_t stream) {
     if (M < 1 || M > (MODE == kRows ? 2 : 16)) return hipErrorInvalidValue;   // rows one operand holds
-    hipLaunchKernelGGL((qmv_bits_kernel<BITS, KW, MODE>), dim3((N + 15) / 16), dim3(64 * KW), 0, stream, x, wq, s, b,
+    W4A16_LAUNCH((qmv_bits_kernel<BITS, KW, MODE>), dim3((N + 15) / 16), dim3(64 * KW), 0, stream, x, wq, s, b,
                        y, M, N, K);
     return hipGetLastError();
 }
@@ -671,7 +671,7 @@ hipError_t launch_bits_burst_t(int kw, const uint16_t* x, const uint32_t* wq, co
         if (e != hipSuccess) return e;
         ready[dev].store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL(kern, dim3((N + 3) / 4), dim3(64 * kw), bits_burst_lds_bytes(kw, GPW, MR), stream, x, wq, s, b,
+    W4A16_LAUNCH(kern, dim3((N + 3) / 4), dim3(64 * kw), bits_burst_lds_bytes(kw, GPW, MR), stream, x, wq, s, b,
                        y, M, N, K, kw);
     return hipGetLastError();
 }
@@ -695,7 +695,7 @@ hipError_t launch_bits_burst16_t(int kw, const uint16_t* x, const uint32_t* wq, 
         if (e != hipSuccess) return e;
         ready[dev].store(true, std::memory_order_release);
     }
-    hipLaunchKernelGGL(kern, dim3((N + 15) / 16), dim3(64 * kw), bits_burst16_lds_bytes(kw, GPW, MR), stream, x, wq,
+    W4A16_LAUNCH(kern, dim3((N + 15) / 16), dim3(64 * kw), bits_burst16_lds_bytes(kw, GPW, MR), stream, x, wq,
                        s, b, y, M, N, K, kw);
     return hipGetLastError();
 }

@@ -402,7 +402,7 @@ static hipError_t launch_burst_t(int kw, const uint16_t* x, const uint32_t* wq, 
     auto kern = qmv_burst_kernel<GPW, MR>;
     const hipError_t e = allow_lds(kern, burst_lds_bytes(kQmvBurstMaxWaves, GPW, MR), ready);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((N + 15) / 16), dim3(64 * kw), burst_lds_bytes(kw, GPW, MR), stream, x, wq, s, b, y,
+    W4A16_LAUNCH(kern, dim3((N + 15) / 16), dim3(64 * kw), burst_lds_bytes(kw, GPW, MR), stream, x, wq, s, b, y,
                        M, N, K, kw);
     return hipGetLastError();
 }
@@ -414,7 +414,7 @@ static hipError_t launch_packed_t(int kw, const uint16_t* x, const uint32_t* wq,
     auto kern = qmv_burst_packed_kernel<GPW, MR>;
     const hipError_t e = allow_lds(kern, packed_lds_bytes(kQmvBurstMaxWaves, GPW, MR), ready);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((N + 3) / 4), dim3(64 * kw), packed_lds_bytes(kw, GPW, MR), stream, x, wq, s, b, y,
+    W4A16_LAUNCH(kern, dim3((N + 3) / 4), dim3(64 * kw), packed_lds_bytes(kw, GPW, MR), stream, x, wq, s, b, y,
                        M, N, K, kw);
     return hipGetLastError();
 }

@@ -456,7 +456,7 @@ static hipError_t launch_w4a8_t(const int8_t* xq, const float* sx, const uint16_
                                 int KB, int split, hipStream_t stream) {
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + 127) / 128;
-    hipLaunchKernelGGL((qmm_w4a8_kernel<BM, WPS, KS>), dim3(tiles_m * tiles_n * split), dim3(256 * KS), 0, stream,
+    W4A16_LAUNCH((qmm_w4a8_kernel<BM, WPS, KS>), dim3(tiles_m * tiles_n * split), dim3(256 * KS), 0, stream,
                        xq, sx, xsum, wq, s, b, y, ws, M, N, K, KB, split, tiles_m, tiles_n);
     return hipGetLastError();
 }
