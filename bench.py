@@ -337,10 +337,10 @@ def main():
         end timestamps go to (w4a16_time_next_launch)."""
         row = calls[i % args.copies]
         for j, call in enumerate(row):
-            if starts is not None and j in starts:
-                starts[j].record()
             if kernel_events is not None and j in kernel_events:
                 w4.w4a16_time_next_launch(*kernel_events[j])
+            if starts is not None and j in starts:
+                starts[j].record()
             call()
             if ends is not None and j in ends:
                 ends[j].record()
@@ -385,16 +385,27 @@ def main():
     dom_us = sum(dom_kernel_us) / len(dom_kernel_us)
     dom_bracket = sum(dom_bracket_us) / len(dom_bracket_us)
 
-    # breakdown pass (not timed as a whole): events around every call
+    # breakdown passes (not timed as a whole): events around every call; then, in a pass of its
+    # own (arming the request costs host time that would open gaps inside the brackets), every
+    # call's contraction kernel (the tile or matvec kernel; not a slice sum) timestamped by itself
     bsteps = max(3, min(args.steps, 10))
     ev = [{j: event_pair() for j in range(n)} for _ in range(bsteps)]
     for i in range(bsteps):
         step(i, {j: e[0] for j, e in ev[i].items()}, {j: e[1] for j, e in ev[i].items()})
     torch.cuda.synchronize()
+    kev = [{j: event_pair() for j in range(n)} for _ in range(bsteps)]
+    for e in (e for row in kev for pair in row.values() for e in pair):
+        e.record()
+    torch.cuda.synchronize()
+    for i in range(bsteps):
+        step(i, kernel_events=kev[i])
+    torch.cuda.synchronize()
     per = []
     for j, u in enumerate(units):
         us = sorted(ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e3 for i in range(bsteps))
+        kus = sorted(kev[i][j][0].elapsed_time(kev[i][j][1]) * 1e3 for i in range(bsteps))
         avg = sum(us) / len(us)
+        kavg = sum(kus) / len(kus)
         M, K, N = u[0]["M"], u[0]["K"], sum(p["N"] for p in u)
         f = sum(flops(p["M"], p["N"], p["K"]) for p in u)
         # one x for the unit (grouped projections read it once)
@@ -402,7 +413,8 @@ def main():
         pl = plans[j]
         path = {1: "qmv", w4.PATH_GROUPED: "qmm grouped", w4.PATH_GATE_UP: "qmm gate/up + SwiGLU"}.get(pl["path"], "qmm")
         per.append({"name": unit_names[j], "M": M, "N": N, "K": K, "avg_us": round(avg, 3),
-                    "median_us": round(us[len(us) // 2], 3), "TFLOP/s": round(f / avg / 1e6, 2),
+                    "median_us": round(us[len(us) // 2], 3), "kernel_us": round(kavg, 3),
+                    "TFLOP/s": round(f / avg / 1e6, 2),
                     "GB/s": round(by / avg / 1e3, 1),
                     "path": path, "variant": pl["variant"],
                     "tile": [pl["tile_m"], pl["tile_n"]], "split_k": pl["split_k"],
@@ -441,14 +453,19 @@ def main():
                                "avg_call_bracket_us: events recorded on the stream just before and after the "
                                "same calls, which also span the dispatch and the end-of-kernel cache flush"},
         "measured_ceiling": ceilings,
-        "breakdown_timing": "separate pass after the timed region: HIP events around every call",
-        "qmv_vocab_last_row": {"GB/s": round(vocab_bytes / vocab["avg_us"] / 1e3, 1),
+        "breakdown_timing": "separate pass after the timed region: HIP events around every call (avg_us, "
+                            "median_us, and the rates); kernel_us: the call's tile or matvec kernel alone, from "
+                            "its own timestamps",
+        "qmv_vocab_last_row": {"GB/s": round(vocab_bytes / vocab["kernel_us"] / 1e3, 1),
                                "frac_of_measured_read_floor": (round(ceilings[read_floor_key(vocab["N"], vocab["K"])]
-                                                                     / vocab["avg_us"], 4) if ceilings else None),
-                               "frac_hbm": round(vocab_bytes / vocab["avg_us"] / 1e3 / PEAK_HBM_GBPS, 4),
-                               "frac_of_measured_read": (round(vocab_bytes / vocab["avg_us"] / 1e3 /
+                                                                     / vocab["kernel_us"], 4) if ceilings else None),
+                               "frac_hbm": round(vocab_bytes / vocab["kernel_us"] / 1e3 / PEAK_HBM_GBPS, 4),
+                               "frac_of_measured_read": (round(vocab_bytes / vocab["kernel_us"] / 1e3 /
                                                                ceilings["read_GB/s"], 4) if ceilings else None),
-                               "avg_us": vocab["avg_us"], "bytes": vocab_bytes},
+                               "kernel_us": vocab["kernel_us"], "avg_call_us": vocab["avg_us"],
+                               "GB/s_call": round(vocab_bytes / vocab["avg_us"] / 1e3, 1), "bytes": vocab_bytes,
+                               "timing": "the matvec kernel's own timestamps in the breakdown pass (mean of its "
+                                         "calls); GB/s_call: events around the same calls"},
         "breakdown": per,
         "kernel_source_sha256_16": kernel_source_hash(),
     }

@@ -37,7 +37,9 @@
  * A case outside what an entry point serves is an error of its own (W4A16_ERR_UNSUPPORTED),
  * never a silently different computation: the convention of raising NotImplementedError for
  * unsupported cases in "MLX Metal Kernels v0.20.0", Known limitations (continuation prefill).
- * Thread safety: stateless apart from a per-device cache of the compute-unit count.
+ * Thread safety: stateless apart from a per-device cache of the compute-unit count, the
+ * per-device scratch of w4a16_linear_noalloc and the per-thread request of
+ * w4a16_time_next_launch.
  */
 #ifndef W4A16_H
 #define W4A16_H
@@ -380,6 +382,13 @@ uint64_t w4a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t gr
  * of the workspace for partials (a policy split without room falls back to S = 1).  Same
  * preconditions and errors as qmm_w4a16; a missing or short workspace returns
  * W4A16_ERR_WORKSPACE, a misaligned one W4A16_ERR_ALIGN.
+ *
+ * Nothing routes to this path by itself: the caller chooses it.  Measured on MI355X (each call
+ * alone, weights from HBM) against the W4A16 entry points on the same shapes: at 512 rows it is
+ * 3% faster on the 2560 -> 9728 gate and up projections and slower on the narrower ones (q
+ * 2560 -> 4096 by 21%, k and v 2560 -> 1024 by 28%, o 4096 -> 2560 by 16%, down 9728 -> 2560 by
+ * 6%): the per-group int32 -> fp32 conversion and scaling of the group products costs about as
+ * much vector-ALU time as the int8 matrix rate saves.  At 4096 rows it is slightly faster.
  */
 int w4a8_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, uint16_t* y,
                 int64_t M, int64_t N, int64_t K, int32_t group, void* workspace, size_t workspace_bytes, void* stream);
