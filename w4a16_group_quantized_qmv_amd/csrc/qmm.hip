@@ -405,6 +405,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
         }
     };
 
+    // Dequantizing mode: the MFMAs of a group's last sub-step are issued at the start of the
+    // next group, right after that group's LDS reads (code words and first activation
+    // fragments), so the matrix core works while those reads and the first dequantization
+    // complete instead of idling after the barrier.  Their operands wait in registers; they
+    // are zero before the first group (adding exact zeros) and issued after the last group.
+    // Each accumulator still takes its MFMAs in the same order, so results are unchanged.
+    bf16x8_t pend_a[RB], pend_b[J];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) pend_a[rb] = bf16x8_t{};
+#pragma unroll
+    for (int j = 0; j < J; ++j) pend_b[j] = bf16x8_t{};
     auto compute = [&](auto ic, const Slot& o, int r) {
         u32x4_t ow[J][WCH];
         read_codes(ic, ow);
@@ -419,6 +430,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) a[0][rb] = *reinterpret_cast<const bf16x8_t*>(xt + abase + rb * 32 * kGroup);
 #pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int j = 0; j < J; ++j) acc[rb][j] = mfma32x32x16(pend_a[rb], pend_b[j], acc[rb][j]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
         for (int j = 0; j < J; ++j) bw[0][j] = dequant_word(ow[j][0][0], s[j], b[j]);
 #pragma unroll
         for (int t = 0; t < TSUB; ++t) {
@@ -430,18 +446,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
 #pragma unroll
                 for (int j = 0; j < J; ++j)
                     bw[nxt][j] = dequant_word(ow[j][(t + 1) >> 2][(t + 1) & 3], s[j], b[j]);
-            }
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int j = 0; j < J; ++j) acc[rb][j] = mfma32x32x16(a[cur][rb], bw[cur][j], acc[rb][j]);
-            // interleave: each MFMA is followed by a share of the next sub-step's dequantization
-            // (VALU) and fragment reads, so the wave keeps issuing while the matrix core works
+                    for (int j = 0; j < J; ++j) acc[rb][j] = mfma32x32x16(a[cur][rb], bw[cur][j], acc[rb][j]);
+                // interleave: each MFMA is followed by a share of the next sub-step's
+                // dequantization (VALU) and fragment reads, so the wave keeps issuing while the
+                // matrix core works
 #pragma unroll
-            for (int i = 0; i < RB * J; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, (20 * J + RB * J - 1) / (RB * J), 0);  // VALU
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // LDS read
+                for (int i = 0; i < RB * J; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, (20 * J + RB * J - 1) / (RB * J), 0);  // VALU
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // LDS read
+                }
+            } else {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) pend_a[rb] = a[cur][rb];
+#pragma unroll
+                for (int j = 0; j < J; ++j) pend_b[j] = bw[cur][j];
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -505,6 +527,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
             }
         }
 #undef W4A16_QMM_STEP
+    }
+    if constexpr (CODES == 0) {
+        // the last group's deferred sub-step
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int j = 0; j < J; ++j) acc[rb][j] = mfma32x32x16(pend_a[rb], pend_b[j], acc[rb][j]);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no direct load may outlive the wave
 
