@@ -310,9 +310,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     // registers to two sub-steps' operands.
     // Exact-code mode (CODES > 0): the matrix core multiplies the raw codes (exact bf16
     // integers), giving the group's P = sum_k x q in fp32, which is scaled into the accumulators,
-    // acc += s * P.  CODES == 1 scales right after the group's last MFMA (one P set; other waves
-    // cover the wait); CODES == 2 spreads the scaling of group t over the MFMAs of group t + 1
-    // (a ring of STAGES P sets, one per pipeline position).  The bias term sum_g b X is added
+    // acc += s * P.  CODES == 1 scales group t at the start of group t + 1, before its first
+    // MFMA overwrites the one P set, while that group's LDS reads complete; CODES == 2 spreads
+    // the scaling of group t over the MFMAs of group t + 1 (a ring of STAGES P sets, one per
+    // pipeline position).  The bias term sum_g b X is added
     // once per tile from the group sums of the activations.
     constexpr int PSETS = CODES == 2 ? STAGES : 1;
     f32x16_t Pr[PSETS][RB][J];
@@ -353,6 +354,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
         bf16x8_t a[2][RB], bw[2][J];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) a[0][rb] = *reinterpret_cast<const bf16x8_t*>(xt + abase + rb * 32 * kGroup);
+        if constexpr (PSETS == 1) {
+            // the previous group's scaling (s_last = 0 before the first group), issued while this
+            // group's LDS reads complete and after the previous group's MFMAs have drained
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int j = 0; j < J; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[rb][j][r] = __builtin_fmaf(s_last[j], Pr[0][rb][j][r], acc[rb][j][r]);
+        }
 #pragma unroll
         for (int j = 0; j < J; ++j) bw[0][j] = codes_bf16_natural(ow[j][0][0]);
 #pragma unroll
@@ -390,19 +401,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (PSETS == 1) {
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int j = 0; j < J; ++j) {
-                    const float sj = bf16_bits_to_f32(sb_bits(o.s[j], r));
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[rb][j][r] = __builtin_fmaf(sj, Pr[0][rb][j][r], acc[rb][j][r]);
-                }
-        } else {
-#pragma unroll
-            for (int j = 0; j < J; ++j) s_last[j] = bf16_bits_to_f32(sb_bits(o.s[j], r));
-        }
+        for (int j = 0; j < J; ++j) s_last[j] = bf16_bits_to_f32(sb_bits(o.s[j], r));
     };
 
     // Dequantizing mode: the MFMAs of a group's last sub-step are issued at the start of the
@@ -538,16 +538,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no direct load may outlive the wave
 
     if constexpr (CODES > 0) {
-        if constexpr (PSETS > 1) {
-            // the last group computed sits in the P set of the body's last position
+        // the last group's scaling: its P sits in the P set of the body's last position
+        constexpr int PL = PSETS == 1 ? 0 : STAGES - 1;
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int j = 0; j < J; ++j)
+            for (int j = 0; j < J; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        acc[rb][j][r] = __builtin_fmaf(s_last[j], Pr[STAGES - 1][rb][j][r], acc[rb][j][r]);
-        }
+                for (int r = 0; r < 16; ++r) acc[rb][j][r] = __builtin_fmaf(s_last[j], Pr[PL][rb][j][r], acc[rb][j][r]);
         // bias term, once per output (slice 0, K half 0): acc += xsum . baug^T over KB / 16
         // sub-steps, with baug[n, k'] = b[n, k' / 2] (zero for k' / 2 >= G) against the hi / lo
         // halves of X
