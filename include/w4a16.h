@@ -122,8 +122,9 @@ const char* w4a16_status_string(int status);
  * overhead and the end-of-kernel system-scope cache flush that events recorded on the stream
  * around the call also span).  The launch consumes the request; an entry point that returns an
  * error before launching leaves it armed.  start_event and stop_event are hipEvent_t handles
- * created by the caller (either may be null); passing two nulls cancels the request.  Calls
- * captured into a HIP graph must not be timed this way.  Returns W4A16_OK.
+ * created by the caller (either may be null); passing two nulls cancels the request.  A launch
+ * into a stream under HIP graph capture consumes the request without timing (the kernel is
+ * captured as a plain launch and the events are left as they were).  Returns W4A16_OK.
  */
 int w4a16_time_next_launch(void* start_event, void* stop_event);
 

@@ -4,7 +4,8 @@ An armed request launches the next tile or matvec kernel through hipExtLaunchKer
 caller's events.  That launch packs the kernel arguments itself, so each case runs once plainly
 and once timed on the same inputs and requires the two outputs to be identical bit for bit
 (same kernel, same inputs).  The kernel span must be positive and no longer than events
-recorded on the stream around the same call.
+recorded on the stream around the same call.  A request met by a launch under HIP graph capture
+is consumed by a plain launch: the replays match the eager result and the events stay untouched.
 """
 
 import numpy as np
@@ -96,3 +97,30 @@ def test_request_is_consumed_and_can_be_cancelled(lib):
     lib.linear(x, wq, s, b)
     torch.cuda.synchronize()
     assert k0.elapsed_time(k1) == first
+
+
+def test_request_met_under_graph_capture_launches_plainly(lib):
+    import torch
+    x, wq, s, b = _dev(51, 40, 256, 512)
+    eager = bits(lib.linear(x, wq, s, b))
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record()
+    k1.record()
+    torch.cuda.synchronize()
+    before = k0.elapsed_time(k1)
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        y = lib.linear(x, wq, s, b)                  # warm-up on the capture stream
+        torch.cuda.synchronize()
+        lib.w4a16_time_next_launch(k0, k1)
+        with torch.cuda.graph(graph, stream=stream):
+            y = lib.linear(x, wq, s, b)
+    for _ in range(3):
+        y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(y), eager)
+        lib.linear(x, wq, s, b)                      # eager work between the replays
+        torch.cuda.synchronize()
+    assert k0.elapsed_time(k1) == before             # the captured launch did not take the events

@@ -18,11 +18,18 @@ LaunchTiming& launch_timing();
 
 // hipExtLaunchKernel packs the arguments by the types it is given, so each one is first
 // converted to the kernel's own parameter type.
+// A request met by a launch into a stream under graph capture is consumed without timing: the
+// kernel is captured as a plain launch.
 template <typename... P, typename... A>
 inline void launch_timed(void (*kernel)(P...), dim3 grid, dim3 block, uint32_t lds, hipStream_t stream,
                          A... args) {
     const LaunchTiming t = launch_timing();
     launch_timing() = LaunchTiming{};
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &capture) != hipSuccess || capture != hipStreamCaptureStatusNone) {
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, static_cast<P>(args)...);
+        return;
+    }
     hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, t.start, t.stop, 0u, static_cast<P>(args)...);
 }
 
