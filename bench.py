@@ -382,8 +382,11 @@ def main():
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
     dom_bracket_us = [e[0].elapsed_time(e[1]) * 1e3 for e in dom_ev]
     dom_kernel_us = [e[0].elapsed_time(e[1]) * 1e3 for e in dom_kev]
-    dom_us = sum(dom_kernel_us) / len(dom_kernel_us)
     dom_bracket = sum(dom_bracket_us) / len(dom_bracket_us)
+    # every kernel span must lie inside the events recorded around its call; otherwise the
+    # kernel timestamps were not taken and the bracket is reported instead
+    kernel_spans_ok = all(0.0 < k <= b for k, b in zip(dom_kernel_us, dom_bracket_us))
+    dom_us = sum(dom_kernel_us) / len(dom_kernel_us) if kernel_spans_ok else dom_bracket
 
     # breakdown passes (not timed as a whole): events around every call; then, in a pass of its
     # own (arming the request costs host time that would open gaps inside the brackets), every
@@ -428,6 +431,10 @@ def main():
     traffic = load_traffic()
     vocab = per[-1]
     vocab_bytes = algo_bytes(1, vocab["N"], vocab["K"])
+    # the matvec's kernel span (its own pass) must be positive and not longer than the calls'
+    # event brackets; otherwise the bracket is used
+    vocab_kernel_ok = 0.0 < vocab["kernel_us"] <= vocab["avg_us"] * 1.05
+    vocab_us = vocab["kernel_us"] if vocab_kernel_ok else vocab["avg_us"]
 
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -448,24 +455,30 @@ def main():
                                                     if ceilings else None),
                      "the_measured_bf16_gemm": "torch.nn.functional.linear on one of the pair's projections (same "
                                                "per-projection shape)",
-                     "timing": "the tile kernel's own start and end timestamps (hipExtLaunchKernel events, armed "
-                               "by w4a16_time_next_launch) in every timed step, mean over the timed steps; "
-                               "avg_call_bracket_us: events recorded on the stream just before and after the "
-                               "same calls, which also span the dispatch and the end-of-kernel cache flush"},
+                     "timing": ("the tile kernel's own start and end timestamps (hipExtLaunchKernel events, armed "
+                                "by w4a16_time_next_launch) in every timed step, mean over the timed steps; "
+                                "avg_call_bracket_us: events recorded on the stream just before and after the "
+                                "same calls, which also span the dispatch and the end-of-kernel cache flush"
+                                if kernel_spans_ok else
+                                "FALLBACK: a kernel timestamp span did not lie inside its call's events, so "
+                                "avg_launch_us is the mean of the events recorded on the stream around each "
+                                "timed call")},
         "measured_ceiling": ceilings,
         "breakdown_timing": "separate pass after the timed region: HIP events around every call (avg_us, "
                             "median_us, and the rates); kernel_us: the call's tile or matvec kernel alone, from "
                             "its own timestamps",
-        "qmv_vocab_last_row": {"GB/s": round(vocab_bytes / vocab["kernel_us"] / 1e3, 1),
+        "qmv_vocab_last_row": {"GB/s": round(vocab_bytes / vocab_us / 1e3, 1),
                                "frac_of_measured_read_floor": (round(ceilings[read_floor_key(vocab["N"], vocab["K"])]
-                                                                     / vocab["kernel_us"], 4) if ceilings else None),
-                               "frac_hbm": round(vocab_bytes / vocab["kernel_us"] / 1e3 / PEAK_HBM_GBPS, 4),
-                               "frac_of_measured_read": (round(vocab_bytes / vocab["kernel_us"] / 1e3 /
+                                                                     / vocab_us, 4) if ceilings else None),
+                               "frac_hbm": round(vocab_bytes / vocab_us / 1e3 / PEAK_HBM_GBPS, 4),
+                               "frac_of_measured_read": (round(vocab_bytes / vocab_us / 1e3 /
                                                                ceilings["read_GB/s"], 4) if ceilings else None),
                                "kernel_us": vocab["kernel_us"], "avg_call_us": vocab["avg_us"],
                                "GB/s_call": round(vocab_bytes / vocab["avg_us"] / 1e3, 1), "bytes": vocab_bytes,
-                               "timing": "the matvec kernel's own timestamps in the breakdown pass (mean of its "
-                                         "calls); GB/s_call: events around the same calls"},
+                               "timing": ("the matvec kernel's own timestamps in the breakdown pass (mean of its "
+                                          "calls); GB/s_call: events around the same calls" if vocab_kernel_ok else
+                                          "FALLBACK: the kernel span exceeded the calls' event brackets, so the rates "
+                                          "use the brackets")},
         "breakdown": per,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
