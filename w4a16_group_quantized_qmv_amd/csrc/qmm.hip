@@ -450,14 +450,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int j = 0; j < J; ++j) acc[rb][j] = mfma32x32x16(a[cur][rb], bw[cur][j], acc[rb][j]);
-                // interleave: each MFMA is followed by a share of the next sub-step's
-                // dequantization (VALU) and fragment reads, so the wave keeps issuing while the
-                // matrix core works
+                if constexpr (RB * J == 1) {
+                    // one MFMA per sub-step (32-row tiles): the next fragment read goes ahead of
+                    // it, then the next sub-step's dequantization (measured 5% faster on the
+                    // 24- and 32-row gate projection than the interleave below)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 21, 0);  // VALU
+                } else {
+                    // interleave: each MFMA is followed by a share of the next sub-step's
+                    // dequantization (VALU) and fragment reads, so the wave keeps issuing while
+                    // the matrix core works
 #pragma unroll
-                for (int i = 0; i < RB * J; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, (20 * J + RB * J - 1) / (RB * J), 0);  // VALU
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // LDS read
+                    for (int i = 0; i < RB * J; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x002, (20 * J + RB * J - 1) / (RB * J), 0);  // VALU
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // LDS read
+                    }
                 }
             } else {
 #pragma unroll
