@@ -393,11 +393,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
                         for (int r = 2 * KS * t; r < 2 * KS * (t + 1); ++r)
                             acc[rb][j][r] = __builtin_fmaf(s_last[j], Pr[PP][rb][j][r], acc[rb][j][r]);
             }
+            // the next sub-step's fragment reads first, then each MFMA followed by a share of the
+            // conversion and scaling VALU (measured 0.7-2.9% faster on the 1024- and 4096-row
+            // exact-code tiles than reads spread between the MFMAs)
+            __builtin_amdgcn_sched_group_barrier(0x100, RB, 0);                                 // LDS reads
 #pragma unroll
             for (int i = 0; i < RB * J; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                              // MFMA
                 __builtin_amdgcn_sched_group_barrier(0x002, (11 * J + 2 * RB * J + RB * J - 1) / (RB * J), 0);  // VALU
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                              // LDS read
             }
             __builtin_amdgcn_sched_barrier(0);
         }
