@@ -186,9 +186,9 @@ int64_t tile_split(int64_t tiles, int64_t M, int64_t N, int64_t G, int32_t split
 void plan_qmm(int64_t M, int64_t N, int64_t K, int32_t split_k, int32_t cus, w4a16_plan_t* p,
               bool skinny = false, bool codes = true) {
     const int64_t G = K / W4A16_GROUP;
-    // Measured on MI355X: 64 x 128 tiles (four waves per SIMD) lead up to about a thousand
+    // Measured on MI355X: 64 x 128 tiles (three waves per SIMD) lead up to about a thousand
     // rows, where the grid is small; 128 x 128 tiles (two waves per SIMD) lead beyond.  For at
-    // most 32 rows, 32 x 128 tiles (four waves per SIMD, three stages) lead on every layer shape
+    // most 32 rows, 32 x 128 tiles (three waves per SIMD, three stages) lead on every layer shape
     // and on the vocabulary head.
     int variant = skinny ? kQmmSkinnyVariant : (M <= 1024 ? 1 : 0);
     const int64_t tile_n = kQmmVariants[variant].tile_n();
