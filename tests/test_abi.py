@@ -34,6 +34,18 @@ def test_abi_version_and_status_strings():
     assert w4.w4a16_status_string(99) == "unknown"
 
 
+def test_time_next_launch_is_host_state_only(lib):
+    """Arming and cancelling set only the calling thread's request (no HIP call, no device)."""
+    import types
+    try:
+        assert lib.w4a16_time_next_launch(None, None) == w4.W4A16_OK
+        assert lib.w4a16_time_next_launch(ctypes.c_void_p(0x1000), None) == w4.W4A16_OK
+    finally:
+        assert lib.w4a16_time_next_launch(None, None) == w4.W4A16_OK   # cancelled: nothing stays armed
+    with pytest.raises(ValueError, match="record"):                     # an event never recorded has no handle
+        w4.w4a16_time_next_launch(types.SimpleNamespace(cuda_event=0), None)
+
+
 # ------------------------------------------------------------------------------ dispatch policy
 
 def plan(M, N, K, path=0, split_k=0):
