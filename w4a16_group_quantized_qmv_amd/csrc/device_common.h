@@ -31,6 +31,7 @@ constexpr int kWordsPerGroup = 16;   // 128 four-bit codes in sixteen 32-bit wor
 
 // Tile order of the tiled kernels (qmm and the int8 path).
 constexpr int kBandM = 8;               // M-tiles per band of the tile order
+constexpr int kBandM128 = 4;            // M-tiles per band for the 128-row W4A16 tiles
 
 // Linear workgroup index -> work index such that XCD c (= i % 8) receives the contiguous range
 // of work indices [start_c, start_c + count_c).
@@ -40,12 +41,13 @@ __device__ __forceinline__ int xcd_remap(int i, int total) {
     return c * per + (c < rem ? c : rem) + k;
 }
 
-// Tile index -> (tm, tn): bands of up to kBandM M-tiles, each band walked N-tile by N-tile.
+// Tile index -> (tm, tn): bands of up to BAND M-tiles, each band walked N-tile by N-tile.
+template <int BAND = kBandM>
 __device__ __forceinline__ void band_order(int tile, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int band = tile / (kBandM * tiles_n);
-    const int first = band * kBandM;
-    const int rows = min(kBandM, tiles_m - first);
-    const int in_band = tile - band * kBandM * tiles_n;
+    const int band = tile / (BAND * tiles_n);
+    const int first = band * BAND;
+    const int rows = min(BAND, tiles_m - first);
+    const int in_band = tile - band * BAND * tiles_n;
     tm = first + in_band % rows;
     tn = in_band / rows;
 }

@@ -45,9 +45,12 @@
 //    read by four lanes, the activation tile row-contiguously.  Scales and biases come as one
 //    bf16 per column and group, or (SBQ = 4) four consecutive groups in one 8-byte load.
 //  * Tile order: workgroup i runs on XCD i % 8; the remap below hands each XCD a contiguous run
-//    of work indices, and work indices walk the tile grid in bands of up to 8 M-tiles, N-tile by
-//    N-tile, so the workgroups resident on one XCD share activation rows and weight columns in
-//    its L2.
+//    of work indices, and work indices walk the tile grid in bands of up to 8 M-tiles (4 for
+//    128-row tiles), N-tile by N-tile, so the workgroups resident on one XCD share activation
+//    rows and weight columns in its L2.  With 128-row tiles the 64 workgroups resident on an XCD
+//    cover 4 x 16 tiles instead of 8 x 8, which reads fewer activation rows per round of tiles
+//    (measured at 4096 rows: L2 fetches of the gate tile 448 -> 274 MB, of down 520 -> 337 MB,
+//    1.5% and 0.5% faster, outputs bit-identical; 2-tile bands measured the same).
 //  * Split-K: the work index also selects one of S contiguous runs of groups (sizes differ by at
 //    most one).  Each slice writes fp32 partials; splitk_reduce sums them in slice order, so the
 //    result is deterministic.
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES_P
     const int work = xcd_remap(blockIdx.x, tiles * split);
     const int z = work / tiles;
     int tm, tn;
-    band_order(work - z * tiles, tiles_m, tiles_n, tm, tn);
+    band_order<(BM >= 128 ? kBandM128 : kBandM)>(work - z * tiles, tiles_m, tiles_n, tm, tn);
 
     const int G = K >> 7;
     const int row_bytes = K >> 1;
