@@ -386,9 +386,9 @@ uint64_t w4a8_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t gr
  *
  * Nothing routes to this path by itself: the caller chooses it.  Measured on MI355X (each call
  * alone, weights from HBM) against the W4A16 entry points on the same shapes: at 512 rows it is
- * 3% faster on the 2560 -> 9728 gate and up projections and slower on the narrower ones (q
- * 2560 -> 4096 by 21%, k and v 2560 -> 1024 by 28%, o 4096 -> 2560 by 16%, down 9728 -> 2560 by
- * 6%): the per-group int32 -> fp32 conversion and scaling of the group products costs about as
+ * within 3% of them on the 2560 -> 9728 gate and up projections (ahead or behind from run to
+ * run) and slower on the narrower ones (q 2560 -> 4096 by 21%, k and v 2560 -> 1024 by 28-30%,
+ * o 4096 -> 2560 by 16-19%, down 9728 -> 2560 by 6-7%): the per-group int32 -> fp32 conversion and scaling of the group products costs about as
  * much vector-ALU time as the int8 matrix rate saves.  At 4096 rows it is slightly faster.
  */
 int w4a8_linear(const uint16_t* x, const uint32_t* wq, const uint16_t* scales, const uint16_t* biases, uint16_t* y,
