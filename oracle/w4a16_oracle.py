@@ -23,7 +23,7 @@ Sources on the pages:
   affine quantized matvec in which a group of weights is dequantized
   (``scale * q + bias``) and reused across the input rows.
 
-Readings where the pages are silent (each one is also listed in the design doc):
+Readings where the pages are silent:
 
 * R1 nibble order: element ``8*j + i`` of a weight row sits in bits
   ``4*i .. 4*i+3`` of 32-bit word ``j`` (low nibble first).
