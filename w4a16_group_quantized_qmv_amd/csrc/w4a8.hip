@@ -146,7 +146,9 @@ qmm_w4a8_kernel(const int8_t* __restrict__ xq, const float* __restrict__ sx, con
     const int work = xcd_remap(blockIdx.x, tiles * split);
     const int z = work / tiles;
     int tm, tn;
-    band_order(work - z * tiles, tiles_m, tiles_n, tm, tn);
+    // 128-row tiles walk bands of 4 M-tiles, like the W4A16 tiles (measured at 4096 rows: down
+    // 0.8% faster, gate unchanged, outputs bit-identical)
+    band_order<(BM >= 128 ? kBandM128 : kBandM)>(work - z * tiles, tiles_m, tiles_n, tm, tn);
 
     const int G = K >> 7;
     const int row_bytes = K >> 1;
